@@ -1,0 +1,182 @@
+"""CPU oracle for the Q4_K weight-streaming decode GEMM - TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The product path (the HIP library and
+its binding) never does, and the two share no code: the arithmetic here lives
+in ``q4k_oracle.c`` (plain C, double precision, compiled with gcc) and in the
+few numpy lines below that only marshal arrays.
+
+What it computes, and where that comes from:
+
+* ``gemm``: ``y[m,n] = sum_k x[m,k] w[n,k]`` and ``S[m,n] = sum_k |x w|`` with
+  w the exact dequantized Q4_K weight (the OpenJet post, "RTX 3090 one card,
+  four coding agents", paragraph on how parallel decoding works: the stacked
+  rows all multiply the same weights, read once). Pinned by the hand-built
+  blocks, the constant-scale closed form and the numpy cross-checks in
+  ``tests/test_oracle_pins.py``.
+* ``decode_block`` / ``dequant_rows``: the Q4_K block (public GGUF layout;
+  the pages name only "Q4_K_M"). Pinned by hand-built bytes, single-nibble
+  unit vectors and exhaustive scale/min round trips.
+* ``standardize``: the row-wise transform used between dependent matrices of
+  the layer walk (mean 0, variance 1 per row). Pinned by its closed-form
+  moments. ``f64_to_f16`` is pinned to numpy's binary16 cast.
+* ``within_bound``: the acceptance rule ``|y - y_ref| <= tol * S``, and
+  ``y == 0`` exactly where ``S == 0``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+BLOCK_BYTES = 144
+QK = 256
+TOL = 1e-4
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so in place (gcc -O2, strict C11: no fp contraction,
+    no fast-math)."""
+    src = os.path.join(_HERE, "q4k_oracle.c")
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", src, "-o", tmp, "-lm"]
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.oracle_f16_to_f64.restype = ctypes.c_double
+        lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_f64_to_f16.restype = ctypes.c_uint16
+        lib.oracle_f64_to_f16.argtypes = [ctypes.c_double]
+        lib.oracle_f16_to_f64_array.restype = None
+        lib.oracle_f16_to_f64_array.argtypes = [vp, i64, vp]
+        lib.oracle_f64_to_f16_array.restype = None
+        lib.oracle_f64_to_f16_array.argtypes = [vp, i64, vp]
+        lib.oracle_unpack_scales.restype = None
+        lib.oracle_unpack_scales.argtypes = [vp, vp, vp]
+        lib.oracle_decode_block.restype = None
+        lib.oracle_decode_block.argtypes = [vp, vp, vp, vp, vp, vp]
+        lib.oracle_dequant_rows.restype = None
+        lib.oracle_dequant_rows.argtypes = [vp, i64, i64, vp]
+        lib.oracle_gemm.restype = ctypes.c_int
+        lib.oracle_gemm.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+        lib.oracle_standardize.restype = None
+        lib.oracle_standardize.argtypes = [vp, i64, i64, ctypes.c_double, vp]
+        _lib = lib
+    return _lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def f16_to_f64(bits) -> np.ndarray:
+    """Decode binary16 bit patterns (uint16 array, or float16 array) to float64."""
+    h = np.asarray(bits)
+    if h.dtype == np.float16:
+        h = h.view(np.uint16)
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, dtype=np.float64)
+    _load().oracle_f16_to_f64_array(h.ctypes.data, h.size, out.ctypes.data)
+    return out
+
+
+def f64_to_f16(v) -> np.ndarray:
+    """Round float64 values to binary16 (nearest, ties to even); returns uint16 bits."""
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().oracle_f64_to_f16_array(v.ctypes.data, v.size, out.ctypes.data)
+    return out
+
+
+def unpack_scales(s12) -> tuple[np.ndarray, np.ndarray]:
+    s = _c(np.frombuffer(bytes(s12), dtype=np.uint8), np.uint8)
+    if s.size != 12:
+        raise ValueError("need 12 bytes")
+    sc = np.zeros(8, dtype=np.int32)
+    mn = np.zeros(8, dtype=np.int32)
+    _load().oracle_unpack_scales(s.ctypes.data, sc.ctypes.data, mn.ctypes.data)
+    return sc, mn
+
+
+def decode_block(blk) -> tuple[float, float, np.ndarray, np.ndarray, np.ndarray]:
+    b = _c(np.frombuffer(bytes(blk), dtype=np.uint8), np.uint8)
+    if b.size != BLOCK_BYTES:
+        raise ValueError("a Q4_K block is 144 bytes")
+    d = np.zeros(1, dtype=np.float64)
+    dmin = np.zeros(1, dtype=np.float64)
+    sc = np.zeros(8, dtype=np.int32)
+    mn = np.zeros(8, dtype=np.int32)
+    q = np.zeros(256, dtype=np.int32)
+    _load().oracle_decode_block(b.ctypes.data, d.ctypes.data, dmin.ctypes.data, sc.ctypes.data,
+                                mn.ctypes.data, q.ctypes.data)
+    return float(d[0]), float(dmin[0]), sc, mn, q
+
+
+def dequant_rows(W: np.ndarray, K: int) -> np.ndarray:
+    """Exact float64 weights [nrows, K] of Q4_K rows W (uint8 [nrows, K/256*144])."""
+    W = _c(W, np.uint8)
+    nrows = W.size // (K // QK * BLOCK_BYTES)
+    out = np.empty((nrows, K), dtype=np.float64)
+    _load().oracle_dequant_rows(W.ctypes.data, nrows, K, out.ctypes.data)
+    return out
+
+
+def gemm(W: np.ndarray, X: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Reference (y, S), both float64 [M, ncols], for the Q4_K rows W of the
+    output columns to check and fp16 activations X [M, K]."""
+    X = np.asarray(X)
+    if X.dtype != np.float16:
+        raise TypeError("X must be float16")
+    M, K = X.shape
+    if K % QK:
+        raise ValueError("K must be a multiple of 256")
+    W = _c(W, np.uint8).reshape(-1, K // QK * BLOCK_BYTES)
+    ncols = W.shape[0]
+    xb = _c(X.view(np.uint16), np.uint16)
+    y = np.empty((M, ncols), dtype=np.float64)
+    S = np.empty((M, ncols), dtype=np.float64)
+    rc = _load().oracle_gemm(W.ctypes.data, xb.ctypes.data, M, ncols, K, y.ctypes.data,
+                             S.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm failed ({rc})")
+    return y, S
+
+
+def standardize(v: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """(v - row mean) / sqrt(row variance + eps), float64 [M, N]."""
+    v = _c(v, np.float64)
+    M, N = v.shape
+    out = np.empty_like(v)
+    _load().oracle_standardize(v.ctypes.data, M, N, eps, out.ctypes.data)
+    return out
+
+
+def within_bound(y: np.ndarray, y_ref: np.ndarray, S: np.ndarray, tol: float = TOL):
+    """Acceptance rule: |y - y_ref| <= tol * S per element, and y exactly 0 where
+    S is 0. Returns (ok, worst |err|/S over S>0, number of failing elements)."""
+    y = np.asarray(y, dtype=np.float64)
+    err = np.abs(y - y_ref)
+    zero = S == 0
+    bad = (err > tol * S) | (zero & (y != 0)) | ~np.isfinite(y)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(zero, 0.0, err / np.where(zero, 1.0, S))
+    worst = float(np.max(rel)) if rel.size else 0.0
+    return (not bool(bad.any())), worst, int(bad.sum())

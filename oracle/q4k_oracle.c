@@ -1,0 +1,215 @@
+/*
+ * q4k_oracle.c - plain, slow fp64 CPU reference of the Q4_K weight-streaming
+ * decode GEMM. TEST INFRASTRUCTURE ONLY: only the test suite, the smoke check
+ * and the CPU-baseline leg of the benchmark may load it. The product path
+ * never calls it and shares no code with it.
+ *
+ * What it computes (the multi-agent decode step of the OpenJet post, "RTX 3090
+ * one card, four coding agents", paragraph on how parallel decoding works:
+ * every agent's rows are stacked into one batch and each weight, read once,
+ * multiplies all of them):
+ *
+ *   y[m][n] = sum_k x[m][k] * w[n][k]          (Y = X * W^T)
+ *   S[m][n] = sum_k |x[m][k] * w[n][k]|        (the per-element error scale)
+ *
+ * with w the exact dequantized Q4_K weight. Every step is done in double
+ * precision with k in increasing order; no blocking, no reordering.
+ *
+ * Q4_K block (144 bytes per 256 weights, the public GGUF k-quant layout; the
+ * pages name the format only as "Q4_K_M"):
+ *   bytes 0-1   d      (binary16, little-endian)
+ *   bytes 2-3   dmin   (binary16, little-endian)
+ *   bytes 4-15  twelve bytes of packed 6-bit scales sc[0..7] and mins m[0..7]
+ *   bytes 16-143 128 bytes of 4-bit quants
+ *   weight t (0..255) of the block, in sub-block j = t/32:
+ *     w = d * sc[j] * q[t] - dmin * m[j]
+ *
+ * Every dequantized weight is exact in double: d has an 11-bit significand,
+ * sc[j]*q[t] <= 945 has 10 bits, dmin*m[j] has 17 bits, so both products and
+ * their difference fit in 53 bits.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#define ORACLE_BLOCK_BYTES 144
+#define ORACLE_QK 256
+
+/* binary16 -> double, decoded bit by bit:
+ *   exponent field 0   : subnormal, value = mantissa * 2^-24
+ *   exponent field 31  : infinity (mantissa 0) or NaN
+ *   otherwise          : (1024 + mantissa) * 2^(exponent - 25)           */
+double oracle_f16_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 31;
+  int mant = h & 1023;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)mant, -24);
+  } else if (e == 31) {
+    v = mant ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + mant), e - 25);
+  }
+  return sign ? -v : v;
+}
+
+/* double -> binary16 bits, round to nearest with ties to even; magnitudes
+ * that round beyond 65504 give infinity. The spacing of binary16 values at
+ * |v| is 2^-24 below 2^-14 and 2^(e-11) for |v| in [2^(e-1), 2^e) above it;
+ * the neighbour is picked from the exact remainder. */
+uint16_t oracle_f64_to_f16(double v) {
+  if (isnan(v)) return 0x7E00;
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  /* 65504 is the largest finite value; 65520, the midpoint to 65536, ties to
+   * the even side, which is the overflow. */
+  if (a >= 65520.0) return sign | 0x7C00;
+  double ulp;
+  if (a < 0x1p-14) {
+    ulp = 0x1p-24;
+  } else {
+    int e;
+    frexp(a, &e);
+    ulp = ldexp(1.0, e - 11);
+  }
+  double n = floor(a / ulp);   /* exact: division by a power of two */
+  double rem = a - n * ulp;    /* exact */
+  if (rem > 0.5 * ulp || (rem == 0.5 * ulp && fmod(n, 2.0) != 0.0)) n += 1.0;
+  double pick = n * ulp;
+  if (pick < 0x1p-14) return sign | (uint16_t)(pick * 0x1p24);
+  int e;
+  double m = frexp(pick, &e); /* pick = m * 2^e, m in [0.5, 1) */
+  int ef = e - 1 + 15;
+  int mant = (int)(ldexp(m, 11) - 1024.0);
+  return sign | (uint16_t)(ef << 10) | (uint16_t)mant;
+}
+
+/* Split the 12 packed bytes into the eight 6-bit scales and eight 6-bit mins.
+ * Sub-blocks 0..3 keep their scale in the low 6 bits of bytes 0..3 and their
+ * min in the low 6 bits of bytes 4..7. Sub-blocks 4..7 keep the low 4 bits of
+ * scale and min in the low and high nibble of bytes 8..11, and the top 2 bits
+ * in the top 2 bits of bytes 0..3 (scale) and 4..7 (min). */
+void oracle_unpack_scales(const uint8_t* s12, int sc[8], int mn[8]) {
+  for (int j = 0; j < 4; ++j) {
+    sc[j] = s12[j] & 63;
+    mn[j] = s12[j + 4] & 63;
+  }
+  for (int j = 4; j < 8; ++j) {
+    int low4_sc = s12[j + 4] & 15;
+    int low4_m = s12[j + 4] >> 4;
+    int top2_sc = s12[j - 4] >> 6;
+    int top2_m = s12[j] >> 6;
+    sc[j] = low4_sc | (top2_sc << 4);
+    mn[j] = low4_m | (top2_m << 4);
+  }
+}
+
+/* Quants: byte i (0..31) of 32-byte chunk c (0..3) holds weight 64c+i in its
+ * low nibble (sub-block 2c) and weight 64c+32+i in its high nibble
+ * (sub-block 2c+1). */
+void oracle_unpack_quants(const uint8_t* qs128, int q[256]) {
+  for (int c = 0; c < 4; ++c) {
+    for (int i = 0; i < 32; ++i) {
+      uint8_t b = qs128[32 * c + i];
+      q[64 * c + i] = b & 15;
+      q[64 * c + 32 + i] = b >> 4;
+    }
+  }
+}
+
+/* Decode one block into its fields. */
+void oracle_decode_block(const uint8_t* blk, double* d, double* dmin, int sc[8], int mn[8],
+                         int q[256]) {
+  uint16_t hd = (uint16_t)(blk[0] | (blk[1] << 8));
+  uint16_t hm = (uint16_t)(blk[2] | (blk[3] << 8));
+  *d = oracle_f16_to_f64(hd);
+  *dmin = oracle_f16_to_f64(hm);
+  oracle_unpack_scales(blk + 4, sc, mn);
+  oracle_unpack_quants(blk + 16, q);
+}
+
+/* Dequantize one weight row of K values (K/256 consecutive blocks). */
+void oracle_dequant_row(const uint8_t* row, int64_t K, double* w) {
+  int sc[8], mn[8], q[256];
+  double d, dmin;
+  for (int64_t kb = 0; kb < K / ORACLE_QK; ++kb) {
+    oracle_decode_block(row + kb * ORACLE_BLOCK_BYTES, &d, &dmin, sc, mn, q);
+    for (int t = 0; t < ORACLE_QK; ++t) {
+      int j = t / 32;
+      w[kb * ORACLE_QK + t] = d * (double)sc[j] * (double)q[t] - dmin * (double)mn[j];
+    }
+  }
+}
+
+void oracle_dequant_rows(const uint8_t* W, int64_t nrows, int64_t K, double* w) {
+  int64_t row_bytes = K / ORACLE_QK * ORACLE_BLOCK_BYTES;
+  for (int64_t n = 0; n < nrows; ++n) oracle_dequant_row(W + n * row_bytes, K, w + n * K);
+}
+
+/* Reference GEMM. W holds `ncols` weight rows (the output columns to check),
+ * X is fp16 [M][K] row-major (bits), outputs y and S are double [M][ncols].
+ * Threads split the columns; each column is dequantized once into a private
+ * double buffer, then every row m is a plain in-order dot product. */
+int oracle_gemm(const uint8_t* W, const uint16_t* X, int64_t M, int64_t ncols, int64_t K,
+                double* y, double* S) {
+  if (K % ORACLE_QK) return -1;
+  int64_t row_bytes = K / ORACLE_QK * ORACLE_BLOCK_BYTES;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
+  if (!xd) return -2;
+  for (int64_t i = 0; i < M * K; ++i) xd[i] = oracle_f16_to_f64(X[i]);
+  int err = 0;
+#pragma omp parallel
+  {
+    double* w = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!w) {
+#pragma omp atomic write
+      err = -2;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t n = 0; n < ncols; ++n) {
+      if (!w) continue;
+      oracle_dequant_row(W + n * row_bytes, K, w);
+      for (int64_t m = 0; m < M; ++m) {
+        const double* xm = xd + m * K;
+        double acc = 0.0, sabs = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+          double p = w[k] * xm[k];
+          acc += p;
+          sabs += fabs(p);
+        }
+        y[m * ncols + n] = acc;
+        S[m * ncols + n] = sabs;
+      }
+    }
+    free(w);
+  }
+  free(xd);
+  return err;
+}
+
+/* The row-wise transform between the dependent matrices of the layer walk:
+ *   t[m][n] = (v[m][n] - mean_m) / sqrt(var_m + eps)
+ * with mean and (population) variance over the row's N values, in double. */
+void oracle_standardize(const double* v, int64_t M, int64_t N, double eps, double* t) {
+  for (int64_t m = 0; m < M; ++m) {
+    const double* r = v + m * N;
+    double mean = 0.0;
+    for (int64_t n = 0; n < N; ++n) mean += r[n];
+    mean /= (double)N;
+    double var = 0.0;
+    for (int64_t n = 0; n < N; ++n) var += (r[n] - mean) * (r[n] - mean);
+    var /= (double)N;
+    double inv = 1.0 / sqrt(var + eps);
+    for (int64_t n = 0; n < N; ++n) t[m * N + n] = (r[n] - mean) * inv;
+  }
+}
+
+void oracle_f64_to_f16_array(const double* v, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_f16(v[i]);
+}
+
+void oracle_f16_to_f64_array(const uint16_t* h, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_to_f64(h[i]);
+}

@@ -1,0 +1,148 @@
+/*
+ * synth.c - seeded, seekable generator of synthetic Q4_K weight blocks and
+ * fp16 activation rows.
+ *
+ * This module produces INPUTS only. It holds none of the arithmetic of the
+ * method under test: it never decodes a block, never dequantizes and never
+ * multiplies. Both the GPU path's tests/bench and the CPU oracle consume the
+ * bytes it writes; neither imports the other.
+ *
+ * Distributions (the workload definition of the single-matrix decode GEMM):
+ *   d, dmin : binary16 of |z| * 1e-3, z ~ N(0,1), round-to-nearest-even
+ *   the 12 scale/min bytes and the 128 nibble bytes : independent uniform
+ *             bytes. Every 6-bit scale, 6-bit min and 4-bit quant field of the
+ *             Q4_K block is a disjoint set of bits of those bytes, so uniform
+ *             bytes give each field the uniform distribution over its range
+ *             (0..63 for scales/mins, 0..15 for quants), independently.
+ *   activations : binary16 of z, z ~ N(0,1), round-to-nearest-even.
+ *
+ * Random source: SplitMix64 (Steele, Lea & Flood, "Fast splittable
+ * pseudorandom number generators", OOPSLA 2014). Output i of the stream with
+ * key k is mix(k + (i+1)*0x9E3779B97F4A7C15), where mix is the published
+ * 64-bit finalizer. The stream is therefore counter-based: any block or
+ * element can be regenerated alone from (key, index).
+ *
+ * Normals: Box-Muller on one 64-bit draw: u1 = (hi32 + 1) / 2^32 in (0,1],
+ * u2 = lo32 / 2^32 in [0,1); r = sqrt(-2 ln u1); z0 = r cos(2 pi u2),
+ * z1 = r sin(2 pi u2), all in double precision.
+ *
+ * Block b of a weight stream uses draws 19b .. 19b+18: draw 0 gives (d, dmin)
+ * through Box-Muller, draws 1..18 give the 144 block bytes little-endian,
+ * whose first four bytes are then replaced by d and dmin (little-endian
+ * binary16). Activation element i uses the Box-Muller pair of draw i/2
+ * (z0 for even i, z1 for odd i).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#define SYNTH_GAMMA 0x9E3779B97F4A7C15ULL
+#define SYNTH_BLOCK_BYTES 144
+#define SYNTH_DRAWS_PER_BLOCK 19
+
+static uint64_t synth_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+/* Output number i (0-based) of the SplitMix64 stream seeded with key. */
+uint64_t synth_draw(uint64_t key, uint64_t i) {
+  return synth_mix(key + (i + 1) * SYNTH_GAMMA);
+}
+
+/* Key of a sub-stream: three nested draws so distinct (seed, a, b, c) give
+ * unrelated streams. */
+uint64_t synth_key(uint64_t seed, uint64_t a, uint64_t b, uint64_t c) {
+  uint64_t k = synth_draw(seed, a);
+  k = synth_draw(k, b);
+  return synth_draw(k, c);
+}
+
+/* binary16 encoding of a double, round to nearest, ties to even; overflow
+ * gives infinity. Used only to encode generated values. */
+static uint16_t synth_f64_to_f16(double v) {
+  uint16_t sign = 0;
+  if (signbit(v)) { sign = 0x8000; v = -v; }
+  if (isnan(v)) return (uint16_t)(sign | 0x7E00);
+  if (v >= 65520.0) return (uint16_t)(sign | 0x7C00); /* rounds to inf */
+  if (v < 0x1p-14) {
+    /* subnormal range: value = n * 2^-24, n in 0..1024 (1024 = smallest normal) */
+    double n = v * 0x1p24;
+    double fl = floor(n);
+    double frac = n - fl;
+    uint32_t r = (uint32_t)fl;
+    if (frac > 0.5 || (frac == 0.5 && (r & 1))) r++;
+    return (uint16_t)(sign | r); /* r == 1024 encodes 2^-14 exactly */
+  }
+  int e;
+  double m = frexp(v, &e);            /* v = m * 2^e, m in [0.5,1) */
+  double n = ldexp(m, 11);            /* 11 significant bits: n in [1024,2048) */
+  double fl = floor(n);
+  double frac = n - fl;
+  uint32_t r = (uint32_t)fl;
+  if (frac > 0.5 || (frac == 0.5 && (r & 1))) r++;
+  int exp16 = e - 1 + 15;             /* v in [2^(e-1), 2^e) */
+  if (r == 2048) { r = 1024; exp16++; }
+  if (exp16 >= 31) return (uint16_t)(sign | 0x7C00);
+  return (uint16_t)(sign | ((uint32_t)exp16 << 10) | (r - 1024));
+}
+
+static void synth_normal_pair(uint64_t w, double* z0, double* z1) {
+  double u1 = ((double)(w >> 32) + 1.0) * 0x1p-32;
+  double u2 = (double)(w & 0xFFFFFFFFULL) * 0x1p-32;
+  double r = sqrt(-2.0 * log(u1));
+  double a = 6.283185307179586476925286766559 * u2;
+  *z0 = r * cos(a);
+  *z1 = r * sin(a);
+}
+
+/* Write blocks [b0, b0+nb) of the weight stream `key` to out (nb*144 bytes). */
+void synth_q4k_blocks(uint64_t key, uint64_t b0, uint64_t nb, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < (int64_t)nb; ++i) {
+    uint64_t b = b0 + (uint64_t)i;
+    uint8_t* blk = out + (size_t)i * SYNTH_BLOCK_BYTES;
+    uint64_t base = b * SYNTH_DRAWS_PER_BLOCK;
+    for (int t = 0; t < 18; ++t) {
+      uint64_t w = synth_draw(key, base + 1 + (uint64_t)t);
+      for (int j = 0; j < 8; ++j) blk[8 * t + j] = (uint8_t)(w >> (8 * j));
+    }
+    double z0, z1;
+    synth_normal_pair(synth_draw(key, base), &z0, &z1);
+    uint16_t d = synth_f64_to_f16(fabs(z0) * 1e-3);
+    uint16_t dmin = synth_f64_to_f16(fabs(z1) * 1e-3);
+    blk[0] = (uint8_t)d; blk[1] = (uint8_t)(d >> 8);
+    blk[2] = (uint8_t)dmin; blk[3] = (uint8_t)(dmin >> 8);
+  }
+}
+
+/* Write the blocks of whole weight rows [n0, n0+nrows) of an (N, K) matrix
+ * whose row n holds K/256 consecutive blocks. */
+void synth_q4k_rows(uint64_t key, int64_t K, int64_t n0, int64_t nrows, uint8_t* out) {
+  uint64_t kb = (uint64_t)(K / 256);
+  synth_q4k_blocks(key, (uint64_t)n0 * kb, (uint64_t)nrows * kb, out);
+}
+
+/* Write activation elements [i0, i0+n) of stream `key` as binary16 bits. */
+void synth_f16_normal(uint64_t key, uint64_t i0, uint64_t n, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < (int64_t)n; ++j) {
+    uint64_t i = i0 + (uint64_t)j;
+    double z0, z1;
+    synth_normal_pair(synth_draw(key, i >> 1), &z0, &z1);
+    out[j] = synth_f64_to_f16((i & 1) ? z1 : z0);
+  }
+}
+
+/* The Box-Muller normals behind activation elements [i0, i0+n) of stream
+ * `key`, before the binary16 rounding (for testing the encoding). */
+void synth_normals(uint64_t key, uint64_t i0, uint64_t n, double* out) {
+  for (uint64_t j = 0; j < n; ++j) {
+    uint64_t i = i0 + j;
+    double z0, z1;
+    synth_normal_pair(synth_draw(key, i >> 1), &z0, &z1);
+    out[j] = (i & 1) ? z1 : z0;
+  }
+}

@@ -1,0 +1,338 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Every check here compares the oracle with something the pages, the public
+Q4_K block definition or plain mathematics fixes: hand-worked bytes and
+weights (tests/golden/), exhaustive round trips, unit vectors, closed forms,
+and library routines for the pieces that have one (numpy's binary16 decoding
+and rounding, numpy's float64/int64 matrix products). The pieces are chosen so
+that a dropped term, a wrong sign, a wrong nibble or bit index or a transposed
+operand fails at least one of them.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def make_block(d_bits=0, dmin_bits=0, scales=None, qs=None):
+    """Assemble 144 block bytes from raw fields (no arithmetic of the method)."""
+    b = bytearray(144)
+    b[0:2] = int(d_bits).to_bytes(2, "little")
+    b[2:4] = int(dmin_bits).to_bytes(2, "little")
+    if scales is not None:
+        b[4:16] = bytes(scales)
+    if qs is not None:
+        b[16:144] = bytes(qs)
+    return bytes(b)
+
+
+def pack_scales_from_spec(sc, mn):
+    """Inverse of the 12-byte scale/min packing, written from the layout rule:
+    sub-blocks 0..3 sit in the low 6 bits of bytes 0..3 (scale) and 4..7 (min);
+    sub-blocks 4..7 put their low 4 bits in bytes 8..11 (scale low nibble, min
+    high nibble) and their top 2 bits in bits 6..7 of bytes 0..3 (scale) and
+    4..7 (min)."""
+    s = [0] * 12
+    for j in range(4):
+        s[j] = sc[j] & 63
+        s[j + 4] = mn[j] & 63
+    for j in range(4, 8):
+        s[j + 4] = (sc[j] & 15) | ((mn[j] & 15) << 4)
+        s[j - 4] |= (sc[j] >> 4) << 6
+        s[j] |= (mn[j] >> 4) << 6
+    return bytes(s)
+
+
+# ---------------------------------------------------------------- binary16
+
+def test_f16_decode_exhaustive_vs_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.f16_to_f64(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # signed zeros and subnormal extremes by hand
+    assert ours[0x0001] == 2.0 ** -24
+    assert ours[0x03FF] == 1023 * 2.0 ** -24
+    assert ours[0x0400] == 2.0 ** -14
+    assert ours[0x3C00] == 1.0 and ours[0x7BFF] == 65504.0
+    assert np.isinf(ours[0x7C00]) and np.signbit(ours[0x8000])
+
+
+def test_f64_to_f16_vs_numpy():
+    rng = np.random.default_rng(1)
+    v = np.concatenate([
+        rng.standard_normal(200000),
+        rng.standard_normal(50000) * 1e-5,          # subnormal range
+        rng.standard_normal(50000) * 3e4,           # near overflow
+        np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, -65520.0, 1e9, 2.0 ** -25,
+                  3 * 2.0 ** -25, 2.0 ** -24 * 1.5, 2.0 ** -14 - 2.0 ** -26]),
+    ])
+    # exact ties: midpoints between consecutive binary16 values
+    h = np.arange(0x0000, 0x7BFF, 7, dtype=np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    v = np.concatenate([v, (lo + hi) / 2, -(lo + hi) / 2])
+    ours = oracle.f64_to_f16(v)
+    ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+# ------------------------------------------------------- scale/min packing
+
+def _golden_scale_lines():
+    with open(os.path.join(GOLDEN, "q4k_scale_bytes.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            b, sc, mn = (p.split() for p in line.split("|"))
+            yield bytes(int(x, 16) for x in b), [int(x) for x in sc], [int(x) for x in mn]
+
+
+def test_scale_bytes_golden():
+    n = 0
+    for b, sc, mn in _golden_scale_lines():
+        got_sc, got_mn = oracle.unpack_scales(b)
+        assert list(got_sc) == sc, b.hex()
+        assert list(got_mn) == mn, b.hex()
+        # the spec-side packer is the inverse on these hand-worked lines
+        assert pack_scales_from_spec(sc, mn) == b
+        n += 1
+    assert n >= 7
+
+
+def test_scale_roundtrip_exhaustive():
+    # every (sub-block j, scale, min) in 8 x 64 x 64, other sub-blocks zero
+    for j in range(8):
+        for s in range(64):
+            for m in range(0, 64, 1):
+                sc = [0] * 8
+                mn = [0] * 8
+                sc[j] = s
+                mn[j] = m
+                got_sc, got_mn = oracle.unpack_scales(pack_scales_from_spec(sc, mn))
+                if list(got_sc) != sc or list(got_mn) != mn:
+                    pytest.fail(f"j={j} sc={s} m={m}: {got_sc} {got_mn}")
+
+
+def test_scale_roundtrip_random_full():
+    rng = np.random.default_rng(7)
+    for _ in range(2000):
+        sc = [int(x) for x in rng.integers(0, 64, 8)]
+        mn = [int(x) for x in rng.integers(0, 64, 8)]
+        got_sc, got_mn = oracle.unpack_scales(pack_scales_from_spec(sc, mn))
+        assert list(got_sc) == sc and list(got_mn) == mn
+
+
+# ------------------------------------------------------------ nibble order
+
+def test_single_nibble_unit_vectors():
+    """d = 1, dmin = 0, every scale 1, exactly one quant set to 1: the block
+    dequantizes to the unit vector e_t. The nibble is placed by the layout
+    rule: weight t = 64c + 32h + i lives in quant byte 32c + i, low nibble for
+    h = 0 and high nibble for h = 1."""
+    ones = pack_scales_from_spec([1] * 8, [0] * 8)
+    rows = []
+    for t in range(256):
+        c, r = divmod(t, 64)
+        h, i = divmod(r, 32)
+        qs = bytearray(128)
+        qs[32 * c + i] = 0x01 if h == 0 else 0x10
+        rows.append(make_block(0x3C00, 0x0000, ones, qs))
+    W = np.frombuffer(b"".join(rows), dtype=np.uint8).reshape(256, 144)
+    w = oracle.dequant_rows(W, 256)
+    assert np.array_equal(w, np.eye(256))
+
+
+# ---------------------------------------------------------- dequant formula
+
+def test_all_zero_block():
+    W = np.zeros((3, 4 * 144), dtype=np.uint8)
+    w = oracle.dequant_rows(W, 1024)
+    assert np.all(w == 0)
+    X = synth.activations(0, 5, 1024)
+    y, S = oracle.gemm(W, X)
+    assert np.all(y == 0) and np.all(S == 0)
+
+
+def test_max_scale_block():
+    # d = dmin = 1, every scale and min 63, every quant 15: w = 63*15 - 63 = 882
+    blk = make_block(0x3C00, 0x3C00, pack_scales_from_spec([63] * 8, [63] * 8), [0xFF] * 128)
+    assert blk[4:16] == bytes([0xFF] * 12)
+    w = oracle.dequant_rows(np.frombuffer(blk, dtype=np.uint8), 256)
+    assert np.all(w == 882.0)
+
+
+def test_min_only_block():
+    # all quants 0: w = -dmin * m_j on every weight of sub-block j
+    mn = [3, 0, 63, 17, 1, 44, 9, 60]
+    blk = make_block(0x3C00, 0x3400, pack_scales_from_spec([5] * 8, mn), [0] * 128)  # dmin=0.25
+    w = oracle.dequant_rows(np.frombuffer(blk, dtype=np.uint8), 256)[0]
+    for j in range(8):
+        assert np.all(w[32 * j:32 * j + 32] == -0.25 * mn[j])
+
+
+def test_subnormal_d():
+    # d = 2^-24 (smallest subnormal), one weight with scale 63 and quant 15
+    blk = make_block(0x0001, 0x0000, pack_scales_from_spec([63] * 8, [0] * 8),
+                     [0x0F] + [0] * 127)
+    w = oracle.dequant_rows(np.frombuffer(blk, dtype=np.uint8), 256)[0]
+    assert w[0] == 63 * 15 * 2.0 ** -24
+    assert np.count_nonzero(w) == 1
+
+
+def test_handbuilt_block_golden():
+    fields = {"qs": []}
+    ws = []
+    with open(os.path.join(GOLDEN, "q4k_block_handbuilt.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            k, *rest = line.split()
+            if k == "qs":
+                fields["qs"].append((int(rest[0]), int(rest[1], 16)))
+            elif k == "w":
+                ws.append((int(rest[0]), float(rest[1])))
+            elif k == "scales":
+                fields[k] = bytes(int(x, 16) for x in rest)
+            else:
+                fields[k] = int(rest[0], 16)
+    qs = bytearray(128)
+    for off, val in fields["qs"]:
+        qs[off] = val
+    blk = make_block(fields["d"], fields["dmin"], fields["scales"], qs)
+    w = oracle.dequant_rows(np.frombuffer(blk, dtype=np.uint8), 256)[0]
+    assert len(ws) >= 9
+    for t, val in ws:
+        assert w[t] == val, (t, w[t], val)
+
+
+# ------------------------------------------------------------------- matmul
+
+def test_constant_scale_closed_form():
+    """With d, dmin, sc, m the same in every block, W = d*sc*Q - dmin*m*J, so
+    Y = d*sc*(X Q^T) - dmin*m*rowsum(X) 1^T with X Q^T an exact integer-weight
+    product (checked with int64 arithmetic on the scaled fp16 inputs). Rows
+    and columns differ in count so a transposed operand cannot pass."""
+    rng = np.random.default_rng(3)
+    M, N, K = 5, 37, 768
+    d_bits, dmin_bits = 0x1E00, 0x1A00          # 0.005859375 and 0.0029296875
+    sc, m = 41, 13
+    scales = pack_scales_from_spec([sc] * 8, [m] * 8)
+    Q = rng.integers(0, 16, size=(N, K))
+    rows = []
+    for n in range(N):
+        blocks = []
+        for kb in range(K // 256):
+            q = Q[n, 256 * kb:256 * kb + 256]
+            qs = bytearray(128)
+            for c in range(4):
+                for i in range(32):
+                    qs[32 * c + i] = int(q[64 * c + i]) | (int(q[64 * c + 32 + i]) << 4)
+            blocks.append(make_block(d_bits, dmin_bits, scales, qs))
+        rows.append(b"".join(blocks))
+    W = np.frombuffer(b"".join(rows), dtype=np.uint8).reshape(N, -1)
+    X = (rng.standard_normal((M, K))).astype(np.float16)
+    y, S = oracle.gemm(W, X)
+
+    d = float(np.array([d_bits], dtype=np.uint16).view(np.float16)[0])
+    dmin = float(np.array([dmin_bits], dtype=np.uint16).view(np.float16)[0])
+    # every fp16 value is an integer multiple of 2^-24: exact int64 products
+    xi = (X.astype(np.float64) * 2.0 ** 24).astype(np.int64)
+    xq = xi @ Q.T.astype(np.int64)               # exact
+    xs = xi.sum(axis=1, keepdims=True)           # exact
+    y_cf = d * sc * (xq.astype(np.float64) * 2.0 ** -24) - dmin * m * (xs * 2.0 ** -24)
+    assert np.allclose(y, y_cf, rtol=0, atol=1e-9 * np.abs(S).max())
+    # and tighter, per element, against the error scale
+    assert np.all(np.abs(y - y_cf) <= 1e-12 * S + 1e-300)
+
+
+def test_gemm_vs_numpy_matmul_and_abs():
+    rng = np.random.default_rng(11)
+    M, N, K = 7, 53, 1280
+    W = synth.q4k_matrix(synth.key(5, 9), N, K)
+    X = synth.f16_normal(synth.key(5, 10), M * K).reshape(M, K)
+    y, S = oracle.gemm(W, X)
+    w = oracle.dequant_rows(W, K)
+    x = X.astype(np.float64)
+    y_np = x @ w.T
+    S_np = np.abs(x) @ np.abs(w).T
+    assert np.all(np.abs(y - y_np) <= 1e-12 * S)
+    assert np.allclose(S, S_np, rtol=1e-12, atol=0)
+    # a transposed or row-swapped result would not match
+    assert y.shape == (M, N)
+    del rng
+
+
+def test_oracle_error_far_below_tolerance():
+    """The oracle's own rounding is ~K * 2^-53 * S, far below the 1e-4 * S bound:
+    compare against an exact rational evaluation on a small case."""
+    from fractions import Fraction
+    M, N, K = 2, 3, 512
+    W = synth.q4k_matrix(synth.key(8, 1), N, K)
+    X = synth.f16_normal(synth.key(8, 2), M * K).reshape(M, K)
+    y, S = oracle.gemm(W, X)
+    w = oracle.dequant_rows(W, K)              # exact values (checked above)
+    x = X.astype(np.float64)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x[m], w[n]))
+            assert abs(Fraction(float(y[m, n])) - exact) <= Fraction(1, 10 ** 12) * Fraction(float(S[m, n]))
+
+
+# ---------------------------------------------------- transform and bounds
+
+def test_standardize_moments_and_small_case():
+    v = np.array([[1.0, 2.0, 3.0, 4.0], [10.0, 10.0, 10.0, 10.0]])
+    t = oracle.standardize(v, eps=1e-6)
+    # row 0: mean 2.5, population variance 1.25
+    assert np.allclose(t[0], (v[0] - 2.5) / np.sqrt(1.25 + 1e-6), rtol=1e-15, atol=0)
+    # a constant row maps to exact zeros
+    assert np.all(t[1] == 0.0)
+    rng = np.random.default_rng(2)
+    v = rng.standard_normal((6, 5000)) * 30 + 7
+    t = oracle.standardize(v, eps=1e-6)
+    assert np.allclose(t.mean(axis=1), 0, atol=1e-12)
+    var = v.var(axis=1)
+    assert np.allclose(t.var(axis=1), var / (var + 1e-6), rtol=1e-12)
+
+
+def test_within_bound_rule():
+    y_ref = np.array([1.0, 0.0, -2.0])
+    S = np.array([10.0, 0.0, 4.0])
+    assert oracle.within_bound(np.array([1.0009, 0.0, -2.0004]), y_ref, S)[0]
+    assert not oracle.within_bound(np.array([1.0011, 0.0, -2.0]), y_ref, S)[0]
+    assert not oracle.within_bound(np.array([1.0, 1e-30, -2.0]), y_ref, S)[0]
+    assert not oracle.within_bound(np.array([np.nan, 0.0, -2.0]), y_ref, S)[0]
+
+
+def test_generated_fields_are_uniform():
+    """Decoded fields of generated blocks cover their whole range uniformly: a
+    decoder that drops the top scale bits or mixes up nibbles would not."""
+    W = synth.q4k_matrix(synth.key(0, 77), 64, 256 * 16)       # 1024 blocks
+    sc_all, mn_all, q_all, d_all = [], [], [], []
+    for blk in W.reshape(-1, 144):
+        d, dmin, sc, mn, q = oracle.decode_block(blk.tobytes())
+        sc_all.append(sc)
+        mn_all.append(mn)
+        q_all.append(q)
+        d_all += [d, dmin]
+    for vals, hi in ((np.concatenate(sc_all), 64), (np.concatenate(mn_all), 64),
+                     (np.concatenate(q_all), 16)):
+        counts = np.bincount(vals, minlength=hi)
+        assert counts.size == hi
+        exp = vals.size / hi
+        chi2 = float(((counts - exp) ** 2 / exp).sum())
+        assert chi2 < hi + 6 * np.sqrt(2 * hi), chi2
+    d_all = np.array(d_all)
+    assert np.all(d_all >= 0)
+    # E|z| * 1e-3 = sqrt(2/pi) * 1e-3
+    assert abs(d_all.mean() - np.sqrt(2 / np.pi) * 1e-3) < 5e-5
