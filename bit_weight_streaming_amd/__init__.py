@@ -1,0 +1,202 @@
+"""bit_weight_streaming_amd - Q4_K weight-streaming decode GEMM for AMD MI355X.
+
+A thin ctypes binding of ``libmkq4k.so`` (C ABI in ``include/mk_q4k.h``).
+PyTorch only allocates device memory and supplies the current HIP stream;
+every step of the computation runs in the library's gfx950 kernels. There is
+no CPU or PyTorch fallback: if the library is missing or the device is not a
+gfx950 GPU, calls raise.
+
+    Y = gemm(W, X)            # W uint8 [N, K/256*144] (Q4_K rows), X fp16 [M, K]
+    step(layers, io, x0, x_out, workspace)   # the persistent multi-layer walk
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(_HERE)
+LIB_PATH = os.path.join(_HERE, "libmkq4k.so")
+_SOURCES = ["q4k_gemm.hip", "q4k_step.hip", "mk_api.hip"]
+HIPCC_FLAGS = [
+    "-O3", "--offload-arch=gfx950", "-fPIC", "-shared", "-std=c++17",
+    # packed fp32 instructions stay off (see the build notes)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+QK = 256
+BLOCK_BYTES = 144
+MAX_M = 64
+
+MK_OK = 0
+MK_EINVAL = -1
+MK_EALIGN = -2
+MK_EWORKSPACE = -3
+MK_EOCCUPANCY = -4
+MK_EHIP = -5
+MK_ENODEV = -6
+MK_ETIMEOUT = -7
+MK_ERANGE = -8
+
+_lib = None
+
+
+class MkError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"mk error {code}: {msg}")
+        self.code = code
+
+
+def sources() -> list[str]:
+    return [os.path.join(_HERE, "csrc", s) for s in _SOURCES
+            if os.path.exists(os.path.join(_HERE, "csrc", s))]
+
+
+def build() -> str:
+    """Compile libmkq4k.so in place for gfx950 with hipcc (runs without a GPU)."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(_ROOT, "include"), *sources(), "-o", tmp]
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+class _Mat(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("N", ctypes.c_int), ("K", ctypes.c_int)]
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [(n, _Mat) for n in ("q", "k", "v", "o", "gate", "up", "down")]
+
+
+class _LayerIO(ctypes.Structure):
+    _fields_ = [("y", ctypes.c_void_p * 7), ("x", ctypes.c_void_p * 4)]
+
+
+MATRIX_NAMES = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MkError(MK_ENODEV, f"{LIB_PATH} is missing: run build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.mk_strerror.restype = ctypes.c_char_p
+        L.mk_strerror.argtypes = [i]
+        L.mk_device_info.restype = i
+        L.mk_device_info.argtypes = [ctypes.c_char_p, sz]
+        L.mk_q4k_gemm.restype = i
+        L.mk_q4k_gemm.argtypes = [vp, vp, vp, i, i, i, vp]
+        L.mk_q4k_gemm_workspace_bytes.restype = sz
+        L.mk_q4k_gemm_workspace_bytes.argtypes = [i, i, i]
+        L.mk_q4k_gemm_ws.restype = i
+        L.mk_q4k_gemm_ws.argtypes = [vp, vp, vp, i, i, i, vp, sz, vp]
+        if hasattr(L, "mk_q4k_step"):
+            L.mk_q4k_step_workspace_bytes.restype = sz
+            L.mk_q4k_step_workspace_bytes.argtypes = [ctypes.POINTER(_Layer), i, i]
+            L.mk_q4k_step.restype = i
+            L.mk_q4k_step.argtypes = [ctypes.POINTER(_Layer), ctypes.POINTER(_LayerIO), i, i,
+                                      vp, vp, vp, sz, vp]
+            L.mk_q4k_step_status.restype = i
+            L.mk_q4k_step_status.argtypes = [vp, ctypes.POINTER(i)]
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().mk_strerror(code).decode()
+
+
+def _check(rc: int) -> None:
+    if rc != MK_OK:
+        raise MkError(rc, strerror(rc))
+
+
+def device_info() -> str:
+    buf = ctypes.create_string_buffer(1024)
+    _check(lib().mk_device_info(buf, len(buf)))
+    return buf.value.decode()
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptr(t) -> int:
+    return int(t.data_ptr()) if t is not None else 0
+
+
+def gemm(W, X, out=None, stream=None, workspace=None):
+    """Y = X * W^T. W: uint8 [N, K/256*144] (or flat), X: float16 [M, K], both on
+    the GPU; returns float32 [M, N] (written into `out` if given)."""
+    import torch
+    if X.dim() != 2 or X.dtype != torch.float16:
+        raise MkError(MK_EINVAL, "X must be a 2-D float16 tensor")
+    M, K = X.shape
+    if K % QK:
+        raise MkError(MK_EINVAL, "K must be a multiple of 256")
+    if W.dtype != torch.uint8 or W.numel() % (K // QK * BLOCK_BYTES):
+        raise MkError(MK_EINVAL, "W must be uint8 Q4_K rows of K/256*144 bytes")
+    if not (X.is_contiguous() and W.is_contiguous()):
+        raise MkError(MK_EINVAL, "W and X must be contiguous")
+    N = W.numel() // (K // QK * BLOCK_BYTES)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    elif out.shape != (M, N) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise MkError(MK_EINVAL, "out must be a contiguous float32 [M, N] tensor")
+    if workspace is None:
+        rc = lib().mk_q4k_gemm(_ptr(W), _ptr(X), _ptr(out), M, N, K, _stream(stream))
+    else:
+        rc = lib().mk_q4k_gemm_ws(_ptr(W), _ptr(X), _ptr(out), M, N, K, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc)
+    return out
+
+
+def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().mk_q4k_gemm_workspace_bytes(M, N, K))
+
+
+# ---------------------------------------------------------------- the step
+
+def _layers_struct(layers):
+    arr = (_Layer * len(layers))()
+    for i, lay in enumerate(layers):
+        for name in MATRIX_NAMES:
+            w, n, k = lay[name]
+            setattr(arr[i], name, _Mat(_ptr(w) if not isinstance(w, int) else w, n, k))
+    return arr
+
+
+def step_workspace_bytes(layer0, n_layers: int, M: int) -> int:
+    arr = _layers_struct([layer0])
+    return int(lib().mk_q4k_step_workspace_bytes(arr, n_layers, M))
+
+
+def step(layers, io, x0, x_out, workspace, M: int, stream=None) -> None:
+    """Enqueue the persistent walk. layers: list of dicts name -> (W tensor,
+    N, K); io: list of dicts with 'y' (7 float32 tensors, matrix order) and
+    'x' (4 float16 tensors, phase inputs A..D)."""
+    larr = _layers_struct(layers)
+    ioarr = (_LayerIO * len(io))()
+    for i, d in enumerate(io):
+        for t in range(7):
+            ioarr[i].y[t] = _ptr(d["y"][t])
+        for p in range(4):
+            ioarr[i].x[p] = _ptr(d["x"][p])
+    rc = lib().mk_q4k_step(larr, ioarr, len(layers), M, _ptr(x0), _ptr(x_out), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc)
+
+
+def step_status(workspace) -> int:
+    st = ctypes.c_int(0)
+    _check(lib().mk_q4k_step_status(_ptr(workspace), ctypes.byref(st)))
+    return st.value

@@ -1,0 +1,163 @@
+// mk_api.hip - the C ABI (include/mk_q4k.h): argument validation, device
+// checks, workspace handling and dispatch to the kernels. Validation happens
+// before any HIP call, so every rejected call touches no device.
+#include <mutex>
+#include <stdio.h>
+#include <string.h>
+
+#include "mk_q4k.h"
+#include "q4k_host.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Per-device facts, filled on first use.
+struct DevInfo {
+  int checked = 0;
+  int ok = 0;
+  int cus = 0;
+  hipDeviceProp_t prop;
+};
+DevInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+// Library-owned GEMM workspace per device (mk_q4k_gemm only).
+struct OwnedWs {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+OwnedWs g_ws[kMaxDevices];
+std::mutex g_ws_mu;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int current_device(int* dev_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MK_ENODEV;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevInfo& d = g_dev[dev];
+  if (!d.checked) {
+    d.checked = 1;
+    if (hipGetDeviceProperties(&d.prop, dev) == hipSuccess &&
+        strncmp(d.prop.gcnArchName, "gfx950", 6) == 0) {
+      d.ok = 1;
+      d.cus = d.prop.multiProcessorCount;
+    }
+  }
+  if (!d.ok) return MK_ENODEV;
+  *dev_out = dev;
+  return MK_OK;
+}
+
+int check_gemm_args(const void* W, const uint16_t* X, const float* Y, int M, int N, int K) {
+  if (!W || !X || !Y) return MK_EINVAL;
+  if (M < 1 || M > MK_Q4K_MAX_M || N < 1 || K < MK_Q4K_QK || K % MK_Q4K_QK) return MK_EINVAL;
+  if ((long long)N * (K / MK_Q4K_QK) > (1LL << 40)) return MK_EINVAL;
+  if (!aligned16(W) || !aligned16(X) || !aligned16(Y)) return MK_EALIGN;
+  // Y must not overlap W or X
+  const char* y0 = reinterpret_cast<const char*>(Y);
+  const char* y1 = y0 + (size_t)M * N * sizeof(float);
+  const char* w0 = static_cast<const char*>(W);
+  const char* w1 = w0 + (size_t)N * (K / MK_Q4K_QK) * MK_Q4K_BLOCK_BYTES;
+  const char* x0 = reinterpret_cast<const char*>(X);
+  const char* x1 = x0 + (size_t)M * K * sizeof(uint16_t);
+  if (y0 < w1 && w0 < y1) return MK_EINVAL;
+  if (y0 < x1 && x0 < y1) return MK_EINVAL;
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mk_strerror(int code) {
+  switch (code) {
+    case MK_OK: return "ok";
+    case MK_EINVAL: return "invalid argument (shape, null pointer, overlap or layer chain)";
+    case MK_EALIGN: return "pointer not 16-byte aligned";
+    case MK_EWORKSPACE: return "workspace missing or too small";
+    case MK_EOCCUPANCY: return "persistent grid cannot be co-resident on this device";
+    case MK_EHIP: return "HIP runtime error";
+    case MK_ENODEV: return "current device is not a gfx950 GPU";
+    case MK_ETIMEOUT: return "device: grid barrier wait timed out";
+    case MK_ERANGE: return "device: row statistic out of representable range";
+    default: return "unknown error code";
+  }
+}
+
+int mk_device_info(char* buf, size_t len) {
+  if (!buf || len == 0) return MK_EINVAL;
+  int dev;
+  int rc = current_device(&dev);
+  if (rc != MK_OK) {
+    snprintf(buf, len, "no gfx950 device");
+    return rc;
+  }
+  const hipDeviceProp_t& p = g_dev[dev].prop;
+  snprintf(buf, len,
+           "{\"name\": \"%s\", \"arch\": \"%s\", \"cus\": %d, \"lds_per_block\": %zu, "
+           "\"clock_khz\": %d, \"mem_clock_khz\": %d, \"bus_bits\": %d, \"l2_bytes\": %d, "
+           "\"hbm_bytes\": %zu}",
+           p.name, p.gcnArchName, p.multiProcessorCount, (size_t)p.sharedMemPerBlock, p.clockRate,
+           p.memoryClockRate, p.memoryBusWidth, p.l2CacheSize, (size_t)p.totalGlobalMem);
+  return MK_OK;
+}
+
+size_t mk_q4k_gemm_workspace_bytes(int M, int N, int K) {
+  if (M < 1 || M > MK_Q4K_MAX_M || N < 1 || K < MK_Q4K_QK || K % MK_Q4K_QK) return 0;
+  return mk::gemm_plan(M, N, K).ws_bytes;
+}
+
+int mk_q4k_gemm_ws(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N,
+                   int K, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_gemm_args(W_blocks, X_fp16, Y_fp32, M, N, K);
+  if (rc != MK_OK) return rc;
+  const mk::GemmPlan p = mk::gemm_plan(M, N, K);
+  if (p.ws_bytes > 0) {
+    if (!workspace || ws_bytes < p.ws_bytes) return MK_EWORKSPACE;
+    if (!aligned16(workspace)) return MK_EALIGN;
+  }
+  int dev;
+  rc = current_device(&dev);
+  if (rc != MK_OK) return rc;
+  hipError_t e = mk::gemm_launch(p, W_blocks, X_fp16, Y_fp32, M, N, K, workspace,
+                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MK_OK : MK_EHIP;
+}
+
+int mk_q4k_gemm(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N, int K,
+                void* stream) {
+  int rc = check_gemm_args(W_blocks, X_fp16, Y_fp32, M, N, K);
+  if (rc != MK_OK) return rc;
+  const mk::GemmPlan p = mk::gemm_plan(M, N, K);
+  int dev;
+  rc = current_device(&dev);
+  if (rc != MK_OK) return rc;
+  void* ws = nullptr;
+  if (p.ws_bytes > 0) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    OwnedWs& o = g_ws[dev];
+    if (o.bytes < p.ws_bytes) {
+      if (o.ptr) {
+        // the old buffer may still be in use by queued work
+        if (hipDeviceSynchronize() != hipSuccess) return MK_EHIP;
+        (void)hipFree(o.ptr);
+        o.ptr = nullptr;
+        o.bytes = 0;
+      }
+      size_t want = p.ws_bytes < ((size_t)64 << 20) ? ((size_t)64 << 20) : p.ws_bytes;
+      if (hipMalloc(&o.ptr, want) != hipSuccess) {
+        o.ptr = nullptr;
+        return MK_EHIP;
+      }
+      o.bytes = want;
+    }
+    ws = o.ptr;
+  }
+  hipError_t e = mk::gemm_launch(p, W_blocks, X_fp16, Y_fp32, M, N, K, ws,
+                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MK_OK : MK_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,234 @@
+// q4k_device.h - device building blocks of the Q4_K weight-streaming GEMM
+// for gfx950 (CDNA4, wave64, MFMA).
+//
+// One wave multiplies a "tile" of 16 weight rows (16 output columns n) by up
+// to 16*MT stacked activation rows, one 256-weight super-block at a time. The
+// weight bytes are streamed from HBM once; the activations sit in LDS.
+//
+// Per super-block and wave:
+//   lane l = n + 16*g (n = l % 16 column of the tile, g = l / 16 in 0..3)
+//   loads the 16-byte block header (d, dmin, 12 scale bytes) and the 32 quant
+//   bytes of chunk g (quant byte i of chunk g holds weight 64g+i in its low
+//   nibble and weight 64g+32+i in its high nibble, i.e. sub-blocks 2g, 2g+1).
+//   Nibbles become binary16 operands sc_j * q exactly (sc_j * q <= 945 fits
+//   in 11 bits) through the 0x6400 exponent trick and one packed FMA; eight
+//   MFMA 16x16x32 f16 instructions contract them with the activations:
+//       C_main[m][n] = sum_{k in block} (sc_j(k) * q_k) * x[m][k]
+//   and one MFMA 16x16x16 f16 gives the min term
+//       C_min[m][n] = sum_j m_j * xsum[m][j]      (xsum split in hi+lo fp16)
+//   then acc[m][n] += d * C_main - dmin * C_min   in fp32.
+// This is the factored form of w = d*sc_j*q - dmin*m_j: every product inside
+// the MFMA is exact (11-bit * 11-bit significands), so the only roundings are
+// fp32 accumulations, far inside the 1e-4 * sum|w x| bound.
+//
+// The k order inside one MFMA is free as long as both operands use it; the
+// nibble extraction yields pairs (k, k+2) per 32-bit lane-half, so the
+// activations are stored in LDS already permuted into that order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mk {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int QK = 256;
+constexpr int BLOCK_BYTES = 144;
+// LDS bytes per activation row per super-block (256 binary16 values)
+constexpr int X_BYTES_PER_BLOCK = 512;
+// LDS bytes per activation row per super-block for the sub-block sums
+// (8 sub-blocks x {hi, lo} binary16)
+constexpr int XSUM_BYTES_PER_BLOCK = 32;
+// pad added to each LDS activation row so that the 16 rows read by one
+// ds_read_b128 land on distinct banks
+constexpr int X_ROW_PAD = 16;
+
+template <typename T, typename F>
+__device__ __forceinline__ T bit_cast_(F f) {
+  static_assert(sizeof(T) == sizeof(F), "size");
+  T t;
+  __builtin_memcpy(&t, &f, sizeof(T));
+  return t;
+}
+
+// The three 16-byte loads of one lane for one super-block.
+struct BlockRegs {
+  u32x4 h;   // d | dmin<<16, scale bytes 0-3, 4-7, 8-11
+  u32x4 q0;  // quant bytes 0..15 of chunk g
+  u32x4 q1;  // quant bytes 16..31 of chunk g
+};
+
+// Streaming loads (nontemporal: each weight byte is used exactly once).
+__device__ __forceinline__ void load_block(BlockRegs& r, const uint8_t* blk, int g) {
+  r.h = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(blk));
+  r.q0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(blk + 16 + 32 * g));
+  r.q1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(blk + 32 + 32 * g));
+}
+
+// binary16 pair (v, v) of a small non-negative integer v <= 63, exactly:
+// 0x6400 | v is 1024 + v, minus 1024.
+__device__ __forceinline__ half2v small_int_pair(uint32_t v) {
+  uint32_t u = (v * 0x00010001u) | 0x64006400u;
+  return bit_cast_<half2v>(u) - half2v{(_Float16)1024.0f, (_Float16)1024.0f};
+}
+
+// Per-lane scale data of one block for sub-blocks 2g (low nibbles) and 2g+1
+// (high nibbles).
+struct LaneScales {
+  half2v sl, nl;  // (sc_lo, sc_lo), (-1024*sc_lo, ...): maps 1024+q -> sc_lo*q
+  half2v sh, nh;  // (sc_hi/16, ...), (-64*sc_hi, ...): maps 1024+16q -> sc_hi*q
+  half4v bmin;    // (m_lo, m_lo, m_hi, m_hi): min-term MFMA operand
+  float d, dmin;
+};
+
+// Unpack the 6-bit scales and mins of sub-blocks 2g, 2g+1 from the header.
+// Sub-blocks 0..3: scale = low 6 bits of scale byte j, min = low 6 bits of
+// byte j+4. Sub-blocks 4..7: low 4 bits in the low/high nibble of byte j+4,
+// top 2 bits in bits 6-7 of byte j-4 (scale) and byte j (min).
+__device__ __forceinline__ LaneScales lane_scales(const u32x4& h, int g) {
+  const uint32_t sh = 16u * (uint32_t)(g & 1);
+  const uint32_t a = h.y >> sh;  // scale bytes 0-3
+  const uint32_t b = h.z >> sh;  // scale bytes 4-7
+  const uint32_t c = h.w >> sh;  // scale bytes 8-11
+  uint32_t scp, mnp;
+  if (g < 2) {
+    scp = a & 0x3F3Fu;
+    mnp = b & 0x3F3Fu;
+  } else {
+    scp = (c & 0x0F0Fu) | ((a >> 2) & 0x3030u);
+    mnp = ((c >> 4) & 0x0F0Fu) | ((b >> 2) & 0x3030u);
+  }
+  LaneScales s;
+  const half2v s_lo = small_int_pair(scp & 0xFFu);
+  const half2v s_hi = small_int_pair(scp >> 8);
+  s.sl = s_lo;
+  s.nl = s_lo * half2v{(_Float16)-1024.0f, (_Float16)-1024.0f};
+  s.sh = s_hi * half2v{(_Float16)0.0625f, (_Float16)0.0625f};
+  s.nh = s_hi * half2v{(_Float16)-64.0f, (_Float16)-64.0f};
+  const half2v m_lo = small_int_pair(mnp & 0xFFu);
+  const half2v m_hi = small_int_pair(mnp >> 8);
+  s.bmin = half4v{m_lo.x, m_lo.y, m_hi.x, m_hi.y};
+  const half2v dd = bit_cast_<half2v>(h.x);
+  s.d = (float)dd.x;
+  s.dmin = (float)dd.y;
+  return s;
+}
+
+// B operands of the two MFMAs fed by quant dwords v0, v1 (8 consecutive
+// weights of sub-block 2g in the low nibbles, of 2g+1 in the high nibbles),
+// k order (0,2,1,3,4,6,5,7).
+__device__ __forceinline__ void unpack_pair(uint32_t v0, uint32_t v1, const LaneScales& s,
+                                            half8v& b_lo, half8v& b_hi) {
+  const uint32_t t0 = v0 >> 8, t1 = v1 >> 8;
+  const half2v l0 = bit_cast_<half2v>((v0 & 0x000F000Fu) | 0x64006400u);
+  const half2v l1 = bit_cast_<half2v>((t0 & 0x000F000Fu) | 0x64006400u);
+  const half2v l2 = bit_cast_<half2v>((v1 & 0x000F000Fu) | 0x64006400u);
+  const half2v l3 = bit_cast_<half2v>((t1 & 0x000F000Fu) | 0x64006400u);
+  const half2v h0 = bit_cast_<half2v>((v0 & 0x00F000F0u) | 0x64006400u);
+  const half2v h1 = bit_cast_<half2v>((t0 & 0x00F000F0u) | 0x64006400u);
+  const half2v h2 = bit_cast_<half2v>((v1 & 0x00F000F0u) | 0x64006400u);
+  const half2v h3 = bit_cast_<half2v>((t1 & 0x00F000F0u) | 0x64006400u);
+  const half2v L0 = __builtin_elementwise_fma(l0, s.sl, s.nl);
+  const half2v L1 = __builtin_elementwise_fma(l1, s.sl, s.nl);
+  const half2v L2 = __builtin_elementwise_fma(l2, s.sl, s.nl);
+  const half2v L3 = __builtin_elementwise_fma(l3, s.sl, s.nl);
+  const half2v H0 = __builtin_elementwise_fma(h0, s.sh, s.nh);
+  const half2v H1 = __builtin_elementwise_fma(h1, s.sh, s.nh);
+  const half2v H2 = __builtin_elementwise_fma(h2, s.sh, s.nh);
+  const half2v H3 = __builtin_elementwise_fma(h3, s.sh, s.nh);
+  b_lo = half8v{L0.x, L0.y, L1.x, L1.y, L2.x, L2.y, L3.x, L3.y};
+  b_hi = half8v{H0.x, H0.y, H1.x, H1.y, H2.x, H2.y, H3.x, H3.y};
+}
+
+// Multiply one super-block (already in registers) against MT row tiles.
+// xa[rt] points at this lane's 128 LDS bytes of activations for the block
+// (row 16*rt + l%16, chunk g) or is null when that row does not exist;
+// xs[rt] points at its 4 sub-block-sum halves (hi/lo of sub-blocks 2g, 2g+1).
+template <int MT>
+__device__ __forceinline__ void mma_block(const BlockRegs& r, int g, const char* const* xa,
+                                          const char* const* xs, floatx4* acc) {
+  const LaneScales s = lane_scales(r.h, g);
+  half8v b[8];
+  unpack_pair(r.q0.x, r.q0.y, s, b[0], b[1]);
+  unpack_pair(r.q0.z, r.q0.w, s, b[2], b[3]);
+  unpack_pair(r.q1.x, r.q1.y, s, b[4], b[5]);
+  unpack_pair(r.q1.z, r.q1.w, s, b[6], b[7]);
+#pragma unroll
+  for (int rt = 0; rt < MT; ++rt) {
+    floatx4 cm = {0.f, 0.f, 0.f, 0.f};
+    floatx4 cn = {0.f, 0.f, 0.f, 0.f};
+    half4v am = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+    if (xs[rt]) am = *reinterpret_cast<const half4v*>(xs[rt]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      half8v a = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f,
+                  (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+      if (xa[rt]) a = *reinterpret_cast<const half8v*>(xa[rt] + 16 * t);
+      cm = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[t], cm, 0, 0, 0);
+    }
+    cn = __builtin_amdgcn_mfma_f32_16x16x16f16(am, s.bmin, cn, 0, 0, 0);
+    acc[rt] = __builtin_elementwise_fma(floatx4{s.d, s.d, s.d, s.d}, cm, acc[rt]);
+    acc[rt] = __builtin_elementwise_fma(floatx4{-s.dmin, -s.dmin, -s.dmin, -s.dmin}, cn, acc[rt]);
+  }
+}
+
+// Stage activations of super-blocks [kb0, kb0+nkb) of the M rows of X
+// ([M][K] binary16, row stride K) into LDS in the MFMA order above, plus the
+// fp32 sums of every 32-weight sub-block split into binary16 hi + lo.
+// x_lds row m starts at m * row_stride bytes; position of (block b, chunk g,
+// MFMA t, element e) is b*512 + g*128 + t*16 + 2*e and holds
+// x[m][(kb0+b)*256 + 64g + 32(t&1) + 8(t>>1) + perm(e)], perm = 0,2,1,3,4,6,5,7.
+__device__ __forceinline__ void stage_x(const uint16_t* __restrict__ X, int K, int M, int kb0,
+                                        int nkb, char* x_lds, int row_stride, char* xs_lds,
+                                        int tid, int nthreads) {
+  const int items = M * nkb * 32;
+  for (int it = tid; it < items; it += nthreads) {
+    const int t = it & 7;
+    const int g = (it >> 3) & 3;
+    const int rest = it >> 5;
+    const int b = rest % nkb;
+    const int m = rest / nkb;
+    const int k = (kb0 + b) * QK + 64 * g + 32 * (t & 1) + 8 * (t >> 1);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(X + (size_t)m * K + k);
+    // halves (0,1 | 2,3 | 4,5 | 6,7) -> (0,2 | 1,3 | 4,6 | 5,7)
+    u32x4 o;
+    o.x = (v.x & 0xFFFFu) | (v.y << 16);
+    o.y = (v.x >> 16) | (v.y & 0xFFFF0000u);
+    o.z = (v.z & 0xFFFFu) | (v.w << 16);
+    o.w = (v.z >> 16) | (v.w & 0xFFFF0000u);
+    *reinterpret_cast<u32x4*>(x_lds + (size_t)m * row_stride + b * X_BYTES_PER_BLOCK + g * 128 +
+                              t * 16) = o;
+  }
+  const int sitems = M * nkb * 8;
+  for (int it = tid; it < sitems; it += nthreads) {
+    const int j = it & 7;
+    const int rest = it >> 3;
+    const int b = rest % nkb;
+    const int m = rest / nkb;
+    const u32x4* src = reinterpret_cast<const u32x4*>(X + (size_t)m * K + (kb0 + b) * QK + 32 * j);
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = src[q];
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const half2v h = bit_cast_<half2v>(w4[i]);
+        sum += (float)h.x;
+        sum += (float)h.y;
+      }
+    }
+    const _Float16 hi = (_Float16)sum;
+    const _Float16 lo = (_Float16)(sum - (float)hi);
+    half2v p = {hi, lo};
+    *reinterpret_cast<half2v*>(xs_lds + ((size_t)m * nkb + b) * XSUM_BYTES_PER_BLOCK + 4 * j) = p;
+  }
+}
+
+}  // namespace mk

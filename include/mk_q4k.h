@@ -1,0 +1,158 @@
+/*
+ * mk_q4k.h - C ABI of the Q4_K weight-streaming decode GEMM for AMD MI355X
+ * (gfx950).
+ *
+ * The operation (the OpenJet post, "RTX 3090 one card, four coding agents",
+ * paragraph on how parallel decoding works): a decode step stacks the rows of
+ * every active agent (next token plus two draft tokens each, 12 rows for four
+ * agents) into one activation matrix X, streams every Q4_K weight of the model
+ * from memory exactly once, and multiplies each weight, while it is on chip,
+ * against all of the rows. The cost of a step is then about one weight read
+ * however many rows ride along. The same paragraph states that the whole step
+ * runs as one persistent kernel with no per-layer launches; mk_q4k_step is
+ * that walk.
+ *
+ *   Y[m][n] = sum_k X[m][k] * w[n][k],   0 <= m < M, 0 <= n < N, 0 <= k < K
+ *
+ * Weights: Q4_K super-blocks of 256 weights in 144 bytes (the public GGUF
+ * k-quant layout; the pages name the format "Q4_K_M"):
+ *   bytes 0-1 d (binary16), 2-3 dmin (binary16), 4-15 packed 6-bit scales
+ *   sc[8] and mins m[8], 16-143 4-bit quants q[256];
+ *   w = d * sc[j] * q - dmin * m[j] for a weight of sub-block j (32 weights).
+ * W holds N rows; row n is K/256 consecutive blocks, so block (n, kb) starts
+ * at byte (n * (K/256) + kb) * 144. Subnormal d and dmin are honoured.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers owned by the caller unless marked (host).
+ *     W, X and Y must be 16-byte aligned. Y must not overlap W or X.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Calls validate their arguments on the host (no device access), enqueue
+ *     their kernels on `stream` and return; they do not synchronise and never
+ *     print or abort. Errors are returned as negative codes.
+ *   - Results are deterministic run to run (no floating-point atomics), and
+ *     each output element is within 1e-4 * sum_k |w[n][k] * X[m][k]| of the
+ *     exact result.
+ */
+#ifndef MK_Q4K_H
+#define MK_Q4K_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MK_OK 0
+#define MK_EINVAL (-1)     /* bad shape, null pointer or broken layer chain   */
+#define MK_EALIGN (-2)     /* W, X, Y (or a step buffer) not 16-byte aligned  */
+#define MK_EWORKSPACE (-3) /* workspace missing or smaller than required      */
+#define MK_EOCCUPANCY (-4) /* the persistent grid cannot be co-resident       */
+#define MK_EHIP (-5)       /* a HIP runtime call failed (see mk_strerror)     */
+#define MK_ENODEV (-6)     /* the current device is not a gfx950 GPU          */
+#define MK_ETIMEOUT (-7)   /* device status: a grid-barrier wait timed out     */
+#define MK_ERANGE (-8)     /* device status: a row statistic left its range    */
+
+#define MK_Q4K_QK 256          /* weights per super-block                   */
+#define MK_Q4K_BLOCK_BYTES 144 /* bytes per super-block                     */
+#define MK_Q4K_MAX_M 64        /* most stacked rows one call accepts        */
+
+/*
+ * mk_q4k_gemm: Y = X * W^T for one Q4_K matrix.
+ *   W_blocks  N * (K/256) blocks of 144 bytes, layout above.
+ *   X_fp16    [M][K] binary16, row-major, row stride K.
+ *   Y_fp32    [M][N] float, row-major, row stride N; fully overwritten.
+ *   M         1..64 stacked rows; N >= 1; K >= 256 and K % 256 == 0.
+ * Returns MK_OK or MK_EINVAL / MK_EALIGN / MK_ENODEV / MK_EHIP. The library
+ * keeps a private device workspace per GPU for K-split partial sums; the first
+ * call on a device that needs more than it holds allocates it (hipMalloc,
+ * which may synchronise that device); later calls allocate nothing.
+ */
+int mk_q4k_gemm(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N, int K,
+                void* stream);
+
+/*
+ * mk_q4k_gemm_ws: as mk_q4k_gemm with a caller-provided workspace of at least
+ * mk_q4k_gemm_workspace_bytes(M, N, K) bytes (16-byte aligned device memory,
+ * used by one call at a time). It never allocates.
+ */
+size_t mk_q4k_gemm_workspace_bytes(int M, int N, int K);
+int mk_q4k_gemm_ws(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N,
+                   int K, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * The decode-step walk: one persistent kernel launch runs n_layers layers of
+ * seven Q4_K matrices each, in their data-dependency order, with grid-wide
+ * barriers between dependent phases:
+ *   phase A  x_l           -> q [M, Nq], k [M, Nk], v [M, Nv]
+ *   phase B  T(q)          -> o [M, H]
+ *   phase C  T(o)          -> gate [M, F], up [M, F]
+ *   phase D  T(gate * up)  -> down [M, H]          (product elementwise, fp32)
+ *   x_{l+1} = T(down)
+ * where T(v) = binary16_RNE((v - mean) / sqrt(var + 1e-6)), mean and
+ * population variance taken over each row's values. The layer input x_0 is
+ * given; every later input is produced on the device. k and v are written but
+ * feed nothing (in a model they would feed attention, which is not part of
+ * this walk).
+ *
+ * Chain rules (checked): q.K = k.K = v.K = gate.K = up.K = down.N = H (the
+ * hidden size), o.K = q.N, gate.N = up.N = down.K = F; every K % 256 == 0;
+ * every layer has the same shapes.
+ */
+typedef struct {
+  const void* w; /* device: N * (K/256) Q4_K blocks */
+  int N;         /* output columns (weight rows)    */
+  int K;         /* input width                     */
+} mk_q4k_mat;
+
+typedef struct {
+  mk_q4k_mat q, k, v, o, gate, up, down;
+} mk_q4k_layer;
+
+/* Per-layer outputs the step writes (device pointers, caller-owned). */
+typedef struct {
+  float* y[7];    /* fp32 [M][N_t] for t = q, k, v, o, gate, up, down          */
+  uint16_t* x[4]; /* binary16 phase inputs A..D: x_l [M][H], T(q) [M][q.N],
+                     T(o) [M][H], T(gate*up) [M][F]                            */
+} mk_q4k_layer_io;
+
+/* Bytes of device workspace mk_q4k_step needs for this shape. */
+size_t mk_q4k_step_workspace_bytes(const mk_q4k_layer* layer0 /* host */, int n_layers, int M);
+
+/*
+ * mk_q4k_step: run the walk.
+ *   layers    (host) n_layers layer descriptors, read before return.
+ *   io        (host) n_layers output descriptors, read before return.
+ *   x0        [M][H] binary16 input of layer 0.
+ *   x_out     [M][H] binary16 T(down) of the last layer.
+ *   workspace device memory of >= mk_q4k_step_workspace_bytes bytes, used by
+ *             one call at a time; it holds the barrier counter, the device
+ *             status word, row statistics, partial sums and the copied
+ *             descriptor tables.
+ * Returns MK_OK (enqueued) or a host-side error. Device-side failures (a
+ * barrier wait that times out, a statistic out of range) are recorded in the
+ * workspace status word; read it with mk_q4k_step_status after the stream
+ * has been synchronised.
+ */
+int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_layers, int M,
+                const uint16_t* x0, uint16_t* x_out, void* workspace, size_t ws_bytes,
+                void* stream);
+
+/* Copy the device status word of the last step run in `workspace` to
+ * *status_out (MK_OK, MK_ETIMEOUT or MK_ERANGE). Synchronous; call after the
+ * step's stream has completed. */
+int mk_q4k_step_status(const void* workspace, int* status_out);
+
+/* Static text for a return code (never NULL). */
+const char* mk_strerror(int code);
+
+/* Describe the current device (name, arch, CU count, LDS per block, clock)
+ * into buf; returns MK_OK or MK_ENODEV / MK_EINVAL. */
+int mk_device_info(char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MK_Q4K_H */

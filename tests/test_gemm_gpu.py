@@ -1,0 +1,210 @@
+"""GPU parity of mk_q4k_gemm against the fp64 oracle, plus the properties the
+kernel must keep (determinism, exact scaling, row permutation), edge cases and
+the single-matrix workloads at their full sizes. Every call goes through the
+C ABI (libmkq4k.so) via the ctypes binding."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import bit_weight_streaming_amd as mk  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def run_gpu(W_np, X_np):
+    W = torch.from_numpy(np.ascontiguousarray(W_np)).to(DEV)
+    X = torch.from_numpy(np.ascontiguousarray(X_np)).to(DEV)
+    Y = mk.gemm(W, X)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy()
+
+
+def check(W_np, X_np, cols=None, Y=None):
+    """Parity within |y - y_ref| <= 1e-4 * S on all columns or on `cols`."""
+    if Y is None:
+        Y = run_gpu(W_np, X_np)
+    Wc = W_np if cols is None else W_np[cols]
+    y_ref, S = oracle.gemm(Wc, X_np)
+    Yc = Y if cols is None else Y[:, cols]
+    ok, worst, nbad = oracle.within_bound(Yc, y_ref, S)
+    assert ok, f"{nbad} elements outside the bound, worst |err|/S = {worst:.3e}"
+    return Y, worst
+
+
+def inputs(N, K, M, seed=0, tag=0):
+    W = synth.q4k_matrix(synth.key(seed, synth.TAG_WEIGHT, tag, N * 100003 + K), N, K)
+    X = synth.activations(seed + tag, M, K)
+    return W, X
+
+
+def test_device_is_gfx950():
+    info = mk.device_info()
+    assert "gfx950" in info
+
+
+# --- the tiny workload: K=1024, N=256, M=1, seed 0, every column ----------------
+def test_tiny_all_columns():
+    W = synth.q4k_matrix(synth.weight_key(0, 0, 0), 256, 1024)
+    X = synth.activations(0, 1, 1024)
+    _, worst = check(W, X)
+    print(f"tiny worst |err|/S = {worst:.3e}")
+
+
+# --- shapes that span several tiles, a ragged tail and every row-tile count -----
+@pytest.mark.parametrize("M,N,K", [
+    (1, 257, 768), (5, 257, 1024), (12, 100, 2560), (16, 33, 512), (17, 48, 1280),
+    (31, 40, 256), (32, 17, 1536), (33, 64, 768), (48, 16, 512), (49, 31, 1024),
+    (64, 70, 2048), (12, 1, 256), (3, 15, 4096),
+])
+def test_parity_shapes(M, N, K):
+    W, X = inputs(N, K, M, tag=M)
+    check(W, X)
+
+
+# --- the single-projection workload: K=5120, N=17408, M=12, every column --------
+def test_gate_up_m12_full():
+    W, X = inputs(17408, 5120, 12, tag=2)
+    _, worst = check(W, X)
+    print(f"gate/up M=12 worst |err|/S = {worst:.3e}")
+
+
+# --- the down-projection sweep: K=17408, N=5120, M in {1,4,8,12,16} -------------
+@pytest.mark.parametrize("M", [1, 4, 8, 12, 16])
+def test_down_sweep_full(M):
+    W, X = inputs(5120, 17408, M, tag=3)
+    check(W, X)
+
+
+# --- 64 rows on both single-matrix shapes ---------------------------------------
+def test_m64_tiny_full():
+    W = synth.q4k_matrix(synth.weight_key(0, 0, 0), 256, 1024)
+    X = synth.activations(5, 64, 1024)
+    check(W, X)
+
+
+def test_m64_gate_up_sampled():
+    W, X = inputs(17408, 5120, 64, tag=5)
+    rng = np.random.default_rng(5)
+    cols = np.sort(rng.choice(17408, 3000, replace=False))
+    cols = np.unique(np.concatenate([cols, [0, 15, 16, 17407]]))
+    check(W, X, cols=cols)
+
+
+# --- edge cases -----------------------------------------------------------------
+def test_all_zero_weights_give_exact_zero():
+    W = np.zeros((40, 4 * 144), dtype=np.uint8)
+    X = synth.activations(1, 9, 1024)
+    Y = run_gpu(W, X)
+    assert np.all(Y == 0)
+
+
+def test_zero_activations_give_exact_zero():
+    W, _ = inputs(50, 1024, 3, tag=7)
+    X = np.zeros((3, 1024), dtype=np.float16)
+    Y = run_gpu(W, X)
+    assert np.all(Y == 0)
+
+
+def _blocks(d_bits, dmin_bits, scale_byte, q_byte, n_rows, kb):
+    blk = bytearray(144)
+    blk[0:2] = d_bits.to_bytes(2, "little")
+    blk[2:4] = dmin_bits.to_bytes(2, "little")
+    blk[4:16] = bytes([scale_byte] * 12)
+    blk[16:] = bytes([q_byte] * 128)
+    return np.frombuffer(bytes(blk) * (n_rows * kb), dtype=np.uint8).reshape(n_rows, kb * 144)
+
+
+def test_max_scale_blocks():
+    W = _blocks(0x3C00, 0x3C00, 0xFF, 0xFF, 20, 2)      # every w = 882
+    X = synth.activations(2, 4, 512)
+    check(W, X)
+
+
+def test_subnormal_d_and_dmin():
+    # d = 3 * 2^-24, dmin = 2^-24 on every block, random nibbles/scales
+    W, X = inputs(64, 1024, 6, tag=9)
+    W = W.copy().reshape(-1, 144)
+    W[:, 0:2] = np.frombuffer((3).to_bytes(2, "little"), dtype=np.uint8)
+    W[:, 2:4] = np.frombuffer((1).to_bytes(2, "little"), dtype=np.uint8)
+    W = W.reshape(64, -1)
+    Y, _ = check(W, X)
+    assert np.count_nonzero(Y) > 0
+
+
+def test_subnormal_activations():
+    W, _ = inputs(48, 768, 5, tag=10)
+    rng = np.random.default_rng(3)
+    bits = rng.integers(1, 1024, size=(5, 768)).astype(np.uint16)    # subnormal fp16
+    bits |= (rng.integers(0, 2, size=(5, 768)).astype(np.uint16) << 15)
+    X = bits.view(np.float16)
+    Y, _ = check(W, X)
+    assert np.count_nonzero(Y) > 0
+
+
+def test_min_only_blocks():
+    W = _blocks(0x3C00, 0x3800, 0x2A, 0x00, 30, 3)      # q = 0: w = -dmin * m
+    X = synth.activations(3, 7, 768)
+    check(W, X)
+
+
+def test_large_activation_values():
+    W, _ = inputs(32, 512, 4, tag=11)
+    X = (synth.activations(4, 4, 512).astype(np.float32) * 1000).astype(np.float16)
+    check(W, X)
+
+
+# --- properties -----------------------------------------------------------------
+def test_deterministic_run_to_run():
+    W, X = inputs(1000, 5120, 12, tag=12)
+    Wt = torch.from_numpy(W).to(DEV)
+    Xt = torch.from_numpy(X).to(DEV)
+    a = mk.gemm(Wt, Xt).cpu()
+    for _ in range(3):
+        assert torch.equal(a, mk.gemm(Wt, Xt).cpu())
+
+
+def test_power_of_two_scaling_exact():
+    W, X = inputs(300, 2048, 12, tag=13)
+    Wt = torch.from_numpy(W).to(DEV)
+    Xt = torch.from_numpy(X).to(DEV)
+    y1 = mk.gemm(Wt, Xt).cpu()
+    y2 = mk.gemm(Wt, (Xt.float() * 2).half()).cpu()
+    assert torch.equal(y2, 2 * y1)
+
+
+def test_row_permutation():
+    W, X = inputs(200, 3072, 12, tag=14)
+    perm = np.random.default_rng(1).permutation(12)
+    Wt = torch.from_numpy(W).to(DEV)
+    y = mk.gemm(Wt, torch.from_numpy(X).to(DEV)).cpu()
+    yp = mk.gemm(Wt, torch.from_numpy(np.ascontiguousarray(X[perm])).to(DEV)).cpu()
+    assert torch.equal(yp, y[perm])
+
+
+def test_explicit_workspace_matches_owned():
+    W, X = inputs(700, 17408 // 4, 12, tag=15)
+    Wt = torch.from_numpy(W).to(DEV)
+    Xt = torch.from_numpy(X).to(DEV)
+    nbytes = mk.gemm_workspace_bytes(12, 700, 17408 // 4)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    a = mk.gemm(Wt, Xt).cpu()
+    b = mk.gemm(Wt, Xt, workspace=ws).cpu()
+    assert torch.equal(a, b)
+
+
+def test_misaligned_pointer_rejected():
+    W, X = inputs(16, 256, 1, tag=16)
+    Wt = torch.from_numpy(W).to(DEV)
+    Xbig = torch.zeros(1, 256 + 1, dtype=torch.float16, device=DEV)
+    Xmis = Xbig.view(-1)[1:257].view(1, 256)      # 2-byte offset
+    with pytest.raises(mk.MkError) as e:
+        mk.gemm(Wt, Xmis)
+    assert e.value.code == mk.MK_EALIGN
