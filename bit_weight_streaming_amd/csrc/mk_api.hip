@@ -69,6 +69,15 @@ int check_gemm_args(const void* W, const uint16_t* X, const float* Y, int M, int
 
 }  // namespace
 
+namespace mk {
+int current_gfx950(int* cus) {
+  int dev;
+  int rc = current_device(&dev);
+  if (rc == MK_OK && cus) *cus = g_dev[dev].cus;
+  return rc;
+}
+}  // namespace mk
+
 extern "C" {
 
 const char* mk_strerror(int code) {

@@ -232,3 +232,52 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ X, int K, i
 }
 
 }  // namespace mk
+
+namespace mk {
+
+// One row tile (M <= 16) against NB weight blocks of the same super-block
+// position (e.g. the gate and up rows of one column tile): each group of 8
+// activation operands is read from LDS once and used for every block, and the
+// weights are unpacked one 8-weight group at a time to keep few registers live.
+template <int NB>
+__device__ __forceinline__ void mma_blocks_rt1(const BlockRegs* r, int g, const char* xa,
+                                               const char* xs, floatx4* acc) {
+  LaneScales s[NB];
+  floatx4 cm[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    s[nb] = lane_scales(r[nb].h, g);
+    cm[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  const half8v zero8 = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f,
+                        (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    half8v a_lo = zero8, a_hi = zero8;
+    if (xa) {
+      a_lo = *reinterpret_cast<const half8v*>(xa + 16 * (2 * u));
+      a_hi = *reinterpret_cast<const half8v*>(xa + 16 * (2 * u + 1));
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint32_t v0 = u == 0 ? r[nb].q0.x : u == 1 ? r[nb].q0.z : u == 2 ? r[nb].q1.x : r[nb].q1.z;
+      const uint32_t v1 = u == 0 ? r[nb].q0.y : u == 1 ? r[nb].q0.w : u == 2 ? r[nb].q1.y : r[nb].q1.w;
+      half8v b_lo, b_hi;
+      unpack_pair(v0, v1, s[nb], b_lo, b_hi);
+      cm[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, cm[nb], 0, 0, 0);
+      cm[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, cm[nb], 0, 0, 0);
+    }
+  }
+  half4v am = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+  if (xs) am = *reinterpret_cast<const half4v*>(xs);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    floatx4 cn = {0.f, 0.f, 0.f, 0.f};
+    cn = __builtin_amdgcn_mfma_f32_16x16x16f16(am, s[nb].bmin, cn, 0, 0, 0);
+    acc[nb] = __builtin_elementwise_fma(floatx4{s[nb].d, s[nb].d, s[nb].d, s[nb].d}, cm[nb], acc[nb]);
+    acc[nb] = __builtin_elementwise_fma(floatx4{-s[nb].dmin, -s[nb].dmin, -s[nb].dmin, -s[nb].dmin},
+                                        cn, acc[nb]);
+  }
+}
+
+}  // namespace mk

@@ -23,3 +23,9 @@ hipError_t gemm_launch(const GemmPlan& p, const void* W, const uint16_t* X, floa
                        int K, void* ws, hipStream_t st);
 
 }  // namespace mk
+
+namespace mk {
+// MK_OK and the CU count of the current device if it is a gfx950 GPU,
+// MK_ENODEV otherwise.
+int current_gfx950(int* cus);
+}  // namespace mk

@@ -1,0 +1,72 @@
+// q4k_step.h - host/device shared definitions of the persistent decode-step
+// walk (internal; the public interface is mk_q4k_step in mk_q4k.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mk {
+
+constexpr int STEP_WAVES = 8;
+constexpr int STEP_THREADS = 64 * STEP_WAVES;
+constexpr int STEP_PD = 8;       // weight blocks in flight per wave
+constexpr int STAT_SLOTS = 8;    // spread of the row-statistic atomics
+constexpr int STEP_MAX_M = 16;   // rows the walk supports (one MFMA row tile)
+constexpr int FLAG_STRIDE = 16;  // uints between barrier flags (64 bytes)
+
+// Fixed-point scales of the row statistics: sum(y) * 2^28, sum(y^2) * 2^20
+// accumulated with 64-bit integer atomics, so the totals do not depend on the
+// order in which workgroups add them.
+constexpr double STAT_SCALE_SUM = 268435456.0;
+constexpr double STAT_SCALE_SQ = 1048576.0;
+
+// One phase of a layer (the same for every layer).
+struct DevPhase {
+  int K;           // input width
+  int KB;          // K / 256
+  int nm;          // matrices per tile: 1, or 2 (gate and up paired)
+  int nseg;        // column segments (phase A: q | k | v)
+  int seg_n[3];    // columns of each segment
+  int seg_t0[4];   // first tile of each segment; seg_t0[nseg] = total tiles
+  int seg_c0[3];   // first column of each segment in the partial buffer
+  int mat0;        // index (0..6) of the first matrix of the phase
+  int nt;          // tiles (16 columns each)
+  int ncols;       // columns of the partial buffer (gate/up: 2F)
+  int sk;          // K slices
+  int nkb;         // super-blocks per slice (the last slice may be shorter)
+  int x_stride;    // LDS bytes per staged activation row
+  int stat_n;      // columns the consumer's statistics run over
+  int tw_max;      // most tiles one workgroup owns
+  size_t part_off; // workspace offset of the [sk][M][ncols] partial sums
+  size_t cons_off; // workspace offset of the consumer copies [layer][M][cons_ld]
+  int cons_ld;     // row stride (floats) of a consumer copy
+  size_t cons_layer_bytes;
+};
+
+// Device copy of one layer's pointers.
+struct DevLayer {
+  const uint8_t* w[7];
+  float* y[7];
+  uint16_t* x[4];
+};
+
+struct StepParams {
+  size_t phases_off;     // DevPhase[4] table in the workspace
+  int n_layers;
+  int M;
+  int G;                 // workgroups (one per CU)
+  int H;                 // hidden size (x width)
+  const uint16_t* x0;
+  uint16_t* x_out;
+  char* ws;              // workspace base
+  size_t layers_off;     // DevLayer table
+  size_t flags_off;      // G flags + go flag
+  size_t ctr_off;        // [4][max_nt] tile counters
+  int max_nt;
+  size_t stats_off;      // [n_layers][4][STAT_SLOTS][M][2] int64
+  size_t status_off;     // int status word
+  size_t lds_bytes;
+};
+
+}  // namespace mk

@@ -180,3 +180,10 @@ def within_bound(y: np.ndarray, y_ref: np.ndarray, S: np.ndarray, tol: float = T
         rel = np.where(zero, 0.0, err / np.where(zero, 1.0, S))
     worst = float(np.max(rel)) if rel.size else 0.0
     return (not bool(bad.any())), worst, int(bad.sum())
+
+
+def f16_spacing(t) -> np.ndarray:
+    """Distance between adjacent binary16 values around |t| (numpy's spacing of
+    the binary16 value nearest to t); the tolerance of the transform check."""
+    t = np.asarray(t, dtype=np.float64)
+    return np.spacing(np.abs(t).astype(np.float16)).astype(np.float64)

@@ -1,0 +1,84 @@
+"""Device-resident synthetic layer stacks for the decode-step walk.
+
+Input plumbing only (no arithmetic of the method): weights come from the
+seeded generator in ``synth.c`` (one stream per (seed, layer, matrix)), are
+written into pinned host buffers and copied to the GPU; output buffers are
+allocated empty. The real 27B-class shapes are hidden 5120, q 6144, k/v 1024,
+FFN 17408 over 64 layers; smaller shapes serve the full-oracle tests.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import LAYER_MATRICES, QK, BLOCK_BYTES, q4k_fill_ptr, weight_key, activations
+
+MATRIX_ORDER = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+def shapes(H=5120, Nq=6144, Nkv=1024, F=17408):
+    """(name -> (N, K)) for one layer."""
+    return {"q": (Nq, H), "k": (Nkv, H), "v": (Nkv, H), "o": (H, Nq),
+            "gate": (F, H), "up": (F, H), "down": (H, F)}
+
+
+MODEL_SHAPES = shapes()
+assert all(MODEL_SHAPES[n] == (N, K) for n, K, N in LAYER_MATRICES)
+
+
+def weight_bytes(shp, n_layers):
+    return n_layers * sum(N * (K // QK) * BLOCK_BYTES for N, K in shp.values())
+
+
+class Stack:
+    """n_layers of Q4_K matrices plus the per-layer output buffers on `device`."""
+
+    def __init__(self, n_layers, M, shp=None, seed=0, device="cuda:0"):
+        import torch
+        self.torch = torch
+        self.n_layers = n_layers
+        self.M = M
+        self.shp = dict(shp or MODEL_SHAPES)
+        self.seed = seed
+        self.device = device
+        self.H = self.shp["q"][1]
+        self.weights = []     # per layer: name -> uint8 tensor [N, K/256*144]
+        biggest = max(N * (K // QK) * BLOCK_BYTES for N, K in self.shp.values())
+        pinned = torch.empty(biggest, dtype=torch.uint8, pin_memory=True)
+        for l in range(n_layers):
+            lay = {}
+            for mi, name in enumerate(MATRIX_ORDER):
+                N, K = self.shp[name]
+                nbytes = N * (K // QK) * BLOCK_BYTES
+                q4k_fill_ptr(weight_key(seed, l, mi), K, 0, N, pinned.data_ptr())
+                t = torch.empty((N, K // QK * BLOCK_BYTES), dtype=torch.uint8, device=device)
+                t.view(-1).copy_(pinned[:nbytes], non_blocking=False)
+                lay[name] = t
+            self.weights.append(lay)
+        del pinned
+        self.x0 = torch.from_numpy(activations(seed, M, self.H)).to(device)
+        self.x_out = torch.empty((M, self.H), dtype=torch.float16, device=device)
+        self.io = []
+        F = self.shp["gate"][0]
+        Nq = self.shp["q"][0]
+        for l in range(n_layers):
+            ys = [torch.empty((M, self.shp[n][0]), dtype=torch.float32, device=device)
+                  for n in MATRIX_ORDER]
+            xs = [torch.empty((M, w), dtype=torch.float16, device=device)
+                  for w in (self.H, Nq, self.H, F)]
+            self.io.append({"y": ys, "x": xs})
+
+    def layer_descs(self):
+        return [{n: (lay[n], self.shp[n][0], self.shp[n][1]) for n in MATRIX_ORDER}
+                for lay in self.weights]
+
+    def host_rows(self, layer, name, rows):
+        """The Q4_K bytes of the given weight rows of one matrix (regenerated)."""
+        from . import q4k_rows
+        N, K = self.shp[name]
+        mi = MATRIX_ORDER.index(name)
+        full = q4k_rows(weight_key(self.seed, layer, mi), K, 0, N)
+        return full[np.asarray(rows)]
+
+    @property
+    def weight_bytes(self):
+        return weight_bytes(self.shp, self.n_layers)

@@ -1,0 +1,138 @@
+"""GPU parity of the persistent decode-step walk (mk_q4k_step).
+
+For every layer and matrix the oracle multiplies the GPU's own binary16 phase
+input (io.x) by the Q4_K weights of the checked columns and compares with the
+GPU output within |y - y_ref| <= 1e-4 * sum|w x|; every phase input is checked
+against the oracle's fp64 transform of the GPU's fp32 outputs to within one
+binary16 spacing. Checking each matrix against its own input keeps binary16
+rounding differences from compounding along the 4*L chained products."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.stack import Stack, shapes, MATRIX_ORDER
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import bit_weight_streaming_amd as mk  # noqa: E402
+
+DEV = "cuda:0"
+PHASE_OF = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3}
+
+
+def run_step(stack, reps=1):
+    descs = stack.layer_descs()
+    nbytes = mk.step_workspace_bytes(descs[0], stack.n_layers, stack.M)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    for _ in range(reps):
+        mk.step(descs, stack.io, stack.x0, stack.x_out, ws, stack.M)
+    torch.cuda.synchronize()
+    st = mk.step_status(ws)
+    assert st == 0, f"device status {st}: {mk.strerror(st)}"
+    return ws
+
+
+def check_transform(x_gpu, v64, what):
+    t = oracle.standardize(v64, eps=1e-6)
+    x = oracle.f16_to_f64(x_gpu)
+    err = np.abs(x - t)
+    tol = oracle.f16_spacing(t)
+    bad = err > tol
+    assert not bad.any(), f"{what}: {bad.sum()} values off by more than one binary16 spacing"
+    # invariants of a standardized row
+    assert np.all(np.isfinite(x))
+    assert np.allclose(x.mean(axis=1), 0, atol=1e-2), what
+    assert np.allclose(np.sqrt((x ** 2).mean(axis=1)), 1, atol=1e-2), what
+
+
+def check_stack(stack, layers=None, ncols=None, seed=0):
+    rng = np.random.default_rng(seed)
+    layers = range(stack.n_layers) if layers is None else layers
+    x0 = stack.x0.cpu().numpy()
+    worst = 0.0
+    for l in layers:
+        io = stack.io[l]
+        xs = [io["x"][p].cpu().numpy() for p in range(4)]
+        ys = [io["y"][t].cpu().numpy().astype(np.float64) for t in range(7)]
+        for t in range(7):
+            assert np.all(np.isfinite(ys[t])), (l, MATRIX_ORDER[t])
+        # phase inputs
+        if l == 0:
+            assert np.array_equal(xs[0].view(np.uint16), x0.view(np.uint16))
+        else:
+            prev_down = stack.io[l - 1]["y"][6].cpu().numpy().astype(np.float64)
+            check_transform(xs[0], prev_down, f"layer {l} input")
+        check_transform(xs[1], ys[0], f"layer {l} T(q)")
+        check_transform(xs[2], ys[3], f"layer {l} T(o)")
+        gu = ys[4].astype(np.float32) * ys[5].astype(np.float32)      # fp32 product
+        check_transform(xs[3], gu.astype(np.float64), f"layer {l} T(gate*up)")
+        # every matrix against its own input
+        for t, name in enumerate(MATRIX_ORDER):
+            N, K = stack.shp[name]
+            if ncols is None or ncols >= N:
+                cols = np.arange(N)
+            else:
+                cols = np.unique(np.concatenate([rng.choice(N, ncols, replace=False), [0, N - 1]]))
+            W = stack.host_rows(l, name, cols)
+            y_ref, S = oracle.gemm(W, xs[PHASE_OF[name]])
+            ok, w, nbad = oracle.within_bound(ys[t][:, cols], y_ref, S)
+            assert ok, f"layer {l} {name}: {nbad} outside the bound, worst {w:.3e}"
+            worst = max(worst, w)
+    return worst
+
+
+SMALL = shapes(H=512, Nq=768, Nkv=256, F=1280)
+RAGGED = shapes(H=768, Nq=512, Nkv=200, F=1024)
+
+
+@pytest.mark.parametrize("M", [12, 1, 5, 16])
+def test_small_stack_all_columns(M):
+    stack = Stack(3, M, SMALL, seed=M, device=DEV)
+    run_step(stack)
+    worst = check_stack(stack)
+    xo = stack.x_out.cpu().numpy()
+    last_down = stack.io[-1]["y"][6].cpu().numpy().astype(np.float64)
+    check_transform(xo, last_down, "x_out")
+    print(f"M={M} worst |err|/S = {worst:.3e}")
+
+
+def test_ragged_kv_stack():
+    stack = Stack(2, 12, RAGGED, seed=7, device=DEV)
+    run_step(stack)
+    check_stack(stack)
+
+
+def test_step_deterministic_and_repeatable():
+    stack = Stack(2, 12, SMALL, seed=3, device=DEV)
+    ws = run_step(stack)
+    first = [[y.clone() for y in io["y"]] for io in stack.io]
+    xo = stack.x_out.clone()
+    descs = stack.layer_descs()
+    for _ in range(3):
+        mk.step(descs, stack.io, stack.x0, stack.x_out, ws, stack.M)
+    torch.cuda.synchronize()
+    assert mk.step_status(ws) == 0
+    for l, io in enumerate(stack.io):
+        for t in range(7):
+            assert torch.equal(io["y"][t], first[l][t]), (l, t)
+    assert torch.equal(stack.x_out, xo)
+
+
+def test_step_rejects_bad_chain():
+    stack = Stack(1, 4, SMALL, seed=1, device=DEV)
+    descs = stack.layer_descs()
+    bad = [dict(descs[0])]
+    w, N, K = bad[0]["o"]
+    bad[0]["o"] = (w, N, K + 256)           # o.K != q.N
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+    with pytest.raises(mk.MkError) as e:
+        mk.step(bad, stack.io, stack.x0, stack.x_out, ws, 4)
+    assert e.value.code == mk.MK_EINVAL
+    with pytest.raises(mk.MkError) as e:
+        mk.step(descs, stack.io, stack.x0, stack.x_out, ws[:16], 4)
+    assert e.value.code == mk.MK_EWORKSPACE
