@@ -7,7 +7,8 @@ no CPU or PyTorch fallback: if the library is missing or the device is not a
 gfx950 GPU, calls raise.
 
     Y = gemm(W, X)            # W uint8 [N, K/256*144] (Q4_K rows), X fp16 [M, K]
-    step(layers, io, x0, x_out, workspace)   # the persistent multi-layer walk
+    Wt = repack(W, N, K)      # load-time tile-record form for the step
+    step(layers, io, x0, x_out, workspace, M)   # the persistent multi-layer walk
 """
 from __future__ import annotations
 
@@ -18,7 +19,7 @@ import subprocess
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 LIB_PATH = os.path.join(_HERE, "libmkq4k.so")
-_SOURCES = ["q4k_gemm.hip", "q4k_step.hip", "mk_api.hip"]
+_SOURCES = ["q4k_gemm.hip", "q4k_step.hip", "q4k_repack.hip", "mk_api.hip"]
 HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-fPIC", "-shared", "-std=c++17",
     # packed fp32 instructions stay off (see the build notes)
@@ -96,6 +97,10 @@ def lib():
         L.mk_q4k_gemm_workspace_bytes.argtypes = [i, i, i]
         L.mk_q4k_gemm_ws.restype = i
         L.mk_q4k_gemm_ws.argtypes = [vp, vp, vp, i, i, i, vp, sz, vp]
+        L.mk_q4k_tiles_bytes.restype = sz
+        L.mk_q4k_tiles_bytes.argtypes = [i, i]
+        L.mk_q4k_repack.restype = i
+        L.mk_q4k_repack.argtypes = [vp, vp, i, i, vp]
         if hasattr(L, "mk_q4k_step"):
             L.mk_q4k_step_workspace_bytes.restype = sz
             L.mk_q4k_step_workspace_bytes.argtypes = [ctypes.POINTER(_Layer), i, i]
@@ -162,6 +167,27 @@ def gemm(W, X, out=None, stream=None, workspace=None):
 
 def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(lib().mk_q4k_gemm_workspace_bytes(M, N, K))
+
+
+def tiles_bytes(N: int, K: int) -> int:
+    """Bytes of the tile-record form of an N x K Q4_K matrix."""
+    return int(lib().mk_q4k_tiles_bytes(N, K))
+
+
+def repack(W, N: int, K: int, out=None, stream=None):
+    """Tile-record form (uint8 device tensor) of the Q4_K rows W (device)."""
+    import torch
+    nbytes = tiles_bytes(N, K)
+    if nbytes == 0:
+        raise MkError(MK_EINVAL, "invalid shape")
+    if W.dtype != torch.uint8 or W.numel() != N * (K // QK) * BLOCK_BYTES or not W.is_contiguous():
+        raise MkError(MK_EINVAL, "W must be contiguous uint8 Q4_K rows")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    elif out.numel() * out.element_size() < nbytes or not out.is_contiguous():
+        raise MkError(MK_EINVAL, "out too small")
+    _check(lib().mk_q4k_repack(_ptr(W), _ptr(out), N, K, _stream(stream)))
+    return out
 
 
 # ---------------------------------------------------------------- the step

@@ -281,3 +281,101 @@ __device__ __forceinline__ void mma_blocks_rt1(const BlockRegs* r, int g, const 
 }
 
 }  // namespace mk
+
+namespace mk {
+
+// Bytes of one 16-row tile record of a super-block (see q4k_repack.hip).
+constexpr int TILE_REC = 16 * BLOCK_BYTES;
+
+// Lane l's three operands of one tile record: header of row l%16, quant bytes
+// [32g, 32g+16) and [32g+16, 32g+32) of that row (g = l/16). The three loads
+// of a wave read 256 (broadcast), 1024 and 1024 contiguous bytes.
+__device__ __forceinline__ void load_rec(BlockRegs& r, const uint8_t* rec, int lane) {
+  r.h = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + (lane & 15) * 16));
+  r.q0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + 256 + lane * 16));
+  r.q1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + 1280 + lane * 16));
+}
+
+// Nibble masks and the binary16 exponent pattern, materialised once in
+// VGPRs so that every (v & mask) | 0x64006400 is one v_and_or_b32 (gfx9 VOP3
+// takes no literal and one SGPR).
+struct UnpackConsts {
+  uint32_t mlo, mhi, orv;
+};
+
+__device__ __forceinline__ UnpackConsts unpack_consts() {
+  UnpackConsts k;
+  asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(k.mlo));
+  asm volatile("v_mov_b32 %0, 0x00F000F0" : "=v"(k.mhi));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.orv));
+  return k;
+}
+
+// As unpack_pair, with the masks in registers.
+__device__ __forceinline__ void unpack_pair_k(uint32_t v0, uint32_t v1, const LaneScales& s,
+                                              const UnpackConsts& k, half8v& b_lo,
+                                              half8v& b_hi) {
+  const uint32_t t0 = v0 >> 8, t1 = v1 >> 8;
+  const half2v l0 = bit_cast_<half2v>((v0 & k.mlo) | k.orv);
+  const half2v l1 = bit_cast_<half2v>((t0 & k.mlo) | k.orv);
+  const half2v l2 = bit_cast_<half2v>((v1 & k.mlo) | k.orv);
+  const half2v l3 = bit_cast_<half2v>((t1 & k.mlo) | k.orv);
+  const half2v h0 = bit_cast_<half2v>((v0 & k.mhi) | k.orv);
+  const half2v h1 = bit_cast_<half2v>((t0 & k.mhi) | k.orv);
+  const half2v h2 = bit_cast_<half2v>((v1 & k.mhi) | k.orv);
+  const half2v h3 = bit_cast_<half2v>((t1 & k.mhi) | k.orv);
+  const half2v L0 = __builtin_elementwise_fma(l0, s.sl, s.nl);
+  const half2v L1 = __builtin_elementwise_fma(l1, s.sl, s.nl);
+  const half2v L2 = __builtin_elementwise_fma(l2, s.sl, s.nl);
+  const half2v L3 = __builtin_elementwise_fma(l3, s.sl, s.nl);
+  const half2v H0 = __builtin_elementwise_fma(h0, s.sh, s.nh);
+  const half2v H1 = __builtin_elementwise_fma(h1, s.sh, s.nh);
+  const half2v H2 = __builtin_elementwise_fma(h2, s.sh, s.nh);
+  const half2v H3 = __builtin_elementwise_fma(h3, s.sh, s.nh);
+  b_lo = half8v{L0.x, L0.y, L1.x, L1.y, L2.x, L2.y, L3.x, L3.y};
+  b_hi = half8v{H0.x, H0.y, H1.x, H1.y, H2.x, H2.y, H3.x, H3.y};
+}
+
+// One 16-row tile of activations (xa: this lane's 128 LDS bytes of the
+// block, always valid - rows past M read a real row whose results are never
+// stored) against NB weight records of the same super-block; the main term
+// runs as two independent MFMA chains (even and odd 32-weight groups).
+template <int NB>
+__device__ __forceinline__ void mma_unit(const BlockRegs* r, int g, const char* xa,
+                                         const char* xs, const UnpackConsts& k, floatx4* acc) {
+  LaneScales s[NB];
+  floatx4 c0[NB], c1[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    s[nb] = lane_scales(r[nb].h, g);
+    c0[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    c1[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const half8v a_lo = *reinterpret_cast<const half8v*>(xa + 32 * u);
+    const half8v a_hi = *reinterpret_cast<const half8v*>(xa + 32 * u + 16);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint32_t v0 = u == 0 ? r[nb].q0.x : u == 1 ? r[nb].q0.z : u == 2 ? r[nb].q1.x : r[nb].q1.z;
+      const uint32_t v1 = u == 0 ? r[nb].q0.y : u == 1 ? r[nb].q0.w : u == 2 ? r[nb].q1.y : r[nb].q1.w;
+      half8v b_lo, b_hi;
+      unpack_pair_k(v0, v1, s[nb], k, b_lo, b_hi);
+      c0[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, c0[nb], 0, 0, 0);
+      c1[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, c1[nb], 0, 0, 0);
+    }
+  }
+  const half4v am = *reinterpret_cast<const half4v*>(xs);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    floatx4 cn = {0.f, 0.f, 0.f, 0.f};
+    cn = __builtin_amdgcn_mfma_f32_16x16x16f16(am, s[nb].bmin, cn, 0, 0, 0);
+    const floatx4 dd = {s[nb].d, s[nb].d, s[nb].d, s[nb].d};
+    acc[nb] = __builtin_elementwise_fma(dd, c0[nb], acc[nb]);
+    acc[nb] = __builtin_elementwise_fma(dd, c1[nb], acc[nb]);
+    acc[nb] = __builtin_elementwise_fma(
+        floatx4{-s[nb].dmin, -s[nb].dmin, -s[nb].dmin, -s[nb].dmin}, cn, acc[nb]);
+  }
+}
+
+}  // namespace mk

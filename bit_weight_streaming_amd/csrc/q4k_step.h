@@ -10,10 +10,13 @@ namespace mk {
 
 constexpr int STEP_WAVES = 8;
 constexpr int STEP_THREADS = 64 * STEP_WAVES;
-constexpr int STEP_PD = 8;       // weight blocks in flight per wave
-constexpr int STAT_SLOTS = 8;    // spread of the row-statistic atomics
+constexpr int STEP_PD = 8;       // weight records in flight per wave
+constexpr int STEP_PD_PRE = 4;   // of which issued before a phase's input is ready
+constexpr int STEP_MAX_LAYERS = 128;
+constexpr int STAT_SLOTS = 64;   // spread of the row-statistic atomics
+constexpr int DONE_CTRS = 64;    // spread of the finished-tile counters
+constexpr int CTR_STRIDE = 32;   // uints between counters (128 bytes)
 constexpr int STEP_MAX_M = 16;   // rows the walk supports (one MFMA row tile)
-constexpr int FLAG_STRIDE = 16;  // uints between barrier flags (64 bytes)
 
 // Fixed-point scales of the row statistics: sum(y) * 2^28, sum(y^2) * 2^20
 // accumulated with 64-bit integer atomics, so the totals do not depend on the
@@ -38,6 +41,9 @@ struct DevPhase {
   int x_stride;    // LDS bytes per staged activation row
   int stat_n;      // columns the consumer's statistics run over
   int tw_max;      // most tiles one workgroup owns
+  int cmax;        // most waves of one workgroup that share a tile
+  int lds_contrib; // LDS offset of the per-tile wave contributions
+  int lds_bytes;   // LDS this phase needs
   size_t part_off; // workspace offset of the [sk][M][ncols] partial sums
   size_t cons_off; // workspace offset of the consumer copies [layer][M][cons_ld]
   int cons_ld;     // row stride (floats) of a consumer copy
@@ -61,8 +67,8 @@ struct StepParams {
   uint16_t* x_out;
   char* ws;              // workspace base
   size_t layers_off;     // DevLayer table
-  size_t flags_off;      // G flags + go flag
-  size_t ctr_off;        // [4][max_nt] tile counters
+  size_t done_off;       // DONE_CTRS finished-tile counters
+  size_t ctr_off;        // [4][max_nt] per-tile slice-arrival counters
   int max_nt;
   size_t stats_off;      // [n_layers][4][STAT_SLOTS][M][2] int64
   size_t status_off;     // int status word

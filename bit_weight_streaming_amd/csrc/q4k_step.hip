@@ -9,27 +9,30 @@
 //   D: T(gate * up) -> down,     x_{l+1} = T(down)
 // with T(v) = binary16((v - mean) / sqrt(var + 1e-6)) per row.
 //
-// Work split (one workgroup of 8 waves per CU, G workgroups):
-//   Each phase's columns form 16-wide tiles (gate and up tiles travel as a
-//   pair that shares the activation operands). K is cut into sk slices;
-//   workgroup w takes slice w % sk and a contiguous run of tiles, stages the
-//   binary16 activations of its slice in LDS once, and its waves stream their
-//   tiles' Q4_K blocks through an 8-deep register ring (mma_blocks_rt1).
+// Work split (G workgroups of 8 waves, one per CU):
+//   A phase's columns form 16-wide tiles (gate and up tiles travel as a pair
+//   that shares the activation operands). K is cut into sk slices; workgroup
+//   w takes slice w % sk and a contiguous run of tiles. It stages the binary16
+//   activations of its slice in LDS once; its waves split the run's
+//   (tile, super-block) units into equal contiguous ranges and stream them
+//   from the tile-record weights through an 8-deep register ring. Waves that
+//   share a tile leave their part in LDS; the parts are added in wave order.
 //   Slice partial sums go to the workspace; the last slice to finish a tile
-//   (an integer counter says which) adds the sk partials in slice order, writes
-//   the outputs, the copy the next phase reads, and the tile's row statistics
-//   (sum y and sum y^2 as 64-bit fixed-point atomics, order independent).
-//   A flag barrier then separates the phases; the next phase's first weight
-//   blocks are already in flight when it starts.
+//   (an integer counter says which) adds the sk partials in slice order and
+//   writes the outputs, the fp32 copy the next phase stages from, and the
+//   tile's row statistics (sum y, sum y^2 as 64-bit fixed-point atomics,
+//   order independent), then counts the tile as finished.
+//   A phase starts when every tile of the previous one is counted finished;
+//   its first weight records are already in flight by then.
 //
 // Cross-workgroup memory protocol (no cache flushes or invalidates): data
-// another workgroup reads is written with device-coherent stores (sc1) and the
-// writer waits for them (s_waitcnt vmcnt(0)) before it raises a flag or adds
-// to a counter; readers poll with device-coherent loads and read shared data
+// another workgroup reads is written with device-coherent stores (sc1) and
+// the writer waits for them (s_waitcnt vmcnt(0)) before it adds to a counter;
+// readers poll counters with device-coherent loads and read shared data
 // either with device-coherent loads (partials, statistics) or, for the phase
-// input copies, with ordinary loads of addresses that no workgroup touched
-// before they were written (one fresh, 256-byte aligned buffer per layer and
-// phase), so no cache can hold a stale line of them.
+// input copies, with ordinary loads of addresses no workgroup touched before
+// they were written (one fresh, 256-byte aligned buffer per layer and phase),
+// so no cache can hold a stale line of them.
 #include <math.h>
 #include <string.h>
 
@@ -46,16 +49,14 @@ namespace mk {
 namespace {
 
 constexpr unsigned long long kTimeoutTicks = 500000000ull;  // 5 s at 100 MHz
+constexpr int kStageRound = 7;   // staging chunks a thread loads before using them
+constexpr int kFixRound = 4;     // fix-up elements a thread loads before using them
+// statistics slot values (STAT_SLOTS x M x 2) each thread reads when staging
+constexpr int kStatPer = (STAT_SLOTS * STEP_MAX_M * 2 + STEP_THREADS - 1) / STEP_THREADS;
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(unsigned* p, unsigned v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float ld_dev(const float* p) {
@@ -71,7 +72,15 @@ __device__ __forceinline__ long long ld_dev(const long long* p) {
   return __hip_atomic_load(const_cast<long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Which slice and tiles workgroup w owns in a phase.
+__device__ __forceinline__ void set_status(const StepParams& P, int code) {
+  int* status = reinterpret_cast<int*>(P.ws + P.status_off);
+  int expect = 0;
+  __hip_atomic_compare_exchange_strong(status, &expect, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Which slice and tiles workgroup w owns in a phase, and the split of its
+// (tile, super-block) units over the waves.
 struct Assign {
   int s;      // K slice
   int t0;     // first tile
@@ -79,6 +88,7 @@ struct Assign {
   int kb0;    // first super-block of the slice
   int nkb;    // super-blocks in the slice
   int j, gs;  // index among, and number of, workgroups sharing the slice
+  int U;      // units = tw * nkb
 };
 
 __device__ __forceinline__ Assign assign(const DevPhase& ph, int w, int G) {
@@ -90,235 +100,245 @@ __device__ __forceinline__ Assign assign(const DevPhase& ph, int w, int G) {
   a.tw = (int)((long long)ph.nt * (a.j + 1) / a.gs) - a.t0;
   a.kb0 = a.s * ph.nkb;
   a.nkb = min(ph.nkb, ph.KB - a.kb0);
+  a.U = a.tw * a.nkb;
   return a;
+}
+
+// First unit of wave v's range, and the wave whose range holds unit x.
+__device__ __forceinline__ int wave_begin(const Assign& a, int v) {
+  return (int)((long long)a.U * v / STEP_WAVES);
+}
+__device__ __forceinline__ int wave_of_unit(const Assign& a, int x) {
+  return min(STEP_WAVES - 1, (int)(((long long)STEP_WAVES * (x + 1) - 1) / a.U));
 }
 
 __device__ __forceinline__ int seg_of(const DevPhase& ph, int tg) {
   return (tg >= ph.seg_t0[1]) + (tg >= ph.seg_t0[2]);
 }
 
-// Walks one wave's weight blocks of a phase: tiles wave, wave+8, ... of the
-// workgroup's run; per tile the slice's super-blocks; per super-block the nm
-// matrices of the tile. Stops (stays on the last block) at the end.
+// Walks one wave's weight records of a phase: units ua..ub-1 of the
+// workgroup (unit u = tile u / nkb, super-block u % nkb), nm records per unit.
+// Past the end it keeps pointing at the last record (re-read, never used).
 struct Iter {
-  int q, b, ti, nti;
+  int u, ub, tl, b, q;
   const uint8_t* base[2];
 };
 
-__device__ __forceinline__ void iter_tile(Iter& it, const DevPhase& ph, const DevLayer* L,
-                                          const Assign& a, int wave, int c) {
-  const int tg = a.t0 + wave + STEP_WAVES * it.ti;
+// The 7 weight pointers of one layer (an LDS copy of the layer table).
+typedef const uint8_t* const* WPtrs;
+
+__device__ __forceinline__ void iter_tile(Iter& it, const DevPhase& ph, WPtrs L,
+                                          const Assign& a) {
+  const int tg = a.t0 + it.tl;
   const int seg = seg_of(ph, tg);
-  int row = (tg - ph.seg_t0[seg]) * 16 + c;
-  row = min(row, ph.seg_n[seg] - 1);
-  const size_t off = ((size_t)row * ph.KB + a.kb0) * BLOCK_BYTES;
-  it.base[0] = L->w[ph.mat0 + seg] + off;
-  it.base[1] = ph.nm == 2 ? L->w[ph.mat0 + seg + 1] + off : it.base[0];
+  const size_t off = (size_t)(tg - ph.seg_t0[seg]) * ph.KB * TILE_REC;
+  it.base[0] = L[ph.mat0 + seg] + off;
+  it.base[1] = ph.nm == 2 ? L[ph.mat0 + seg + 1] + off : it.base[0];
 }
 
-__device__ __forceinline__ void iter_init(Iter& it, const DevPhase& ph, const DevLayer* L,
-                                          const Assign& a, int wave, int c) {
+__device__ __forceinline__ void iter_init(Iter& it, const DevPhase& ph, WPtrs L,
+                                          const Assign& a, int wave) {
+  it.u = wave_begin(a, wave);
+  it.ub = wave_begin(a, wave + 1);
   it.q = 0;
-  it.b = 0;
-  it.ti = 0;
-  it.nti = wave < a.tw ? (a.tw - wave + STEP_WAVES - 1) / STEP_WAVES : 0;
+  it.tl = a.nkb > 0 ? it.u / a.nkb : 0;
+  it.b = a.nkb > 0 ? it.u - it.tl * a.nkb : 0;
   it.base[0] = it.base[1] = nullptr;
-  if (it.nti > 0) iter_tile(it, ph, L, a, wave, c);
+  if (it.u < it.ub) iter_tile(it, ph, L, a);
 }
 
-__device__ __forceinline__ const uint8_t* iter_addr(const Iter& it) {
-  return (it.q ? it.base[1] : it.base[0]) + (size_t)it.b * BLOCK_BYTES;
+__device__ __forceinline__ const uint8_t* iter_addr(const Iter& it, const Assign& a) {
+  return (it.q ? it.base[1] : it.base[0]) + (size_t)(a.kb0 + it.b) * TILE_REC;
 }
 
-__device__ __forceinline__ void iter_next(Iter& it, const DevPhase& ph, const DevLayer* L,
-                                          const Assign& a, int wave, int c) {
+__device__ __forceinline__ void iter_next(Iter& it, const DevPhase& ph, WPtrs L,
+                                          const Assign& a) {
   if (++it.q < ph.nm) return;
-  it.q = 0;
-  if (++it.b < a.nkb) return;
-  if (it.ti + 1 < it.nti) {
-    it.b = 0;
-    ++it.ti;
-    iter_tile(it, ph, L, a, wave, c);
-  } else {
-    it.b = a.nkb - 1;  // past the end: keep re-reading the last block
+  if (it.u + 1 >= it.ub) {  // stay on the last record
     it.q = ph.nm - 1;
+    return;
   }
+  it.q = 0;
+  ++it.u;
+  if (++it.b < a.nkb) return;
+  it.b = 0;
+  ++it.tl;
+  iter_tile(it, ph, L, a);
 }
 
-// Issue the first STEP_PD weight loads of a phase into the ring.
-__device__ __forceinline__ void ring_prologue(BlockRegs (&ring)[STEP_PD], Iter& it,
-                                              const DevPhase& ph, const DevLayer* L,
-                                              const Assign& a, int wave, int c, int g) {
-  if (it.nti == 0) return;
+// Issue ring slots [s0, s1) of a phase's first STEP_PD weight records.
+__device__ __forceinline__ void ring_fill(BlockRegs (&ring)[STEP_PD], Iter& it,
+                                          const DevPhase& ph, WPtrs L, const Assign& a, int lane,
+                                          int s0, int s1) {
+  if (it.u >= it.ub) return;
 #pragma unroll
   for (int s = 0; s < STEP_PD; ++s) {
-    load_block(ring[s], iter_addr(it), g);
-    iter_next(it, ph, L, a, wave, c);
+    if (s >= s0 && s < s1) {
+      load_rec(ring[s], iter_addr(it, a), lane);
+      iter_next(it, ph, L, a);
+    }
   }
 }
 
-// Stream the phase's blocks of this wave, multiply them against the staged
-// activations and leave each finished tile's slice partial (per lane one
-// floatx4: rows 4*(lane/16)+r, column lane%16) in the LDS partial area.
+// Stream the wave's units, multiply them against the staged activations and
+// leave each tile part in the LDS contribution slot (tile, wave - first wave
+// of the tile): per lane one floatx4 (rows 4*(lane/16)+r, column lane%16).
 template <int NM>
 __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& it,
-                                              const DevPhase& ph, const DevLayer* L,
+                                              const DevPhase& ph, WPtrs L,
                                               const Assign& a, int wave, int lane,
                                               const char* xa_lane, const char* xs_lane,
-                                              char* part_lds) {
-  const int c = lane & 15;
+                                              char* contrib, const UnpackConsts& k) {
   const int g = lane >> 4;
-  const int nti = it.nti;
-  const int U = nti * a.nkb * NM;
+  const int ua = wave_begin(a, wave), ub = wave_begin(a, wave + 1);
+  const int U = (ub - ua) * NM;  // records
+  if (U <= 0) return;
   floatx4 acc[NM];
 #pragma unroll
   for (int q = 0; q < NM; ++q) acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
-  int cb = 0, cti = 0;  // consumer position: block, tile counter
-  auto consume = [&](int s) {
-    const char* xa = xa_lane ? xa_lane + cb * X_BYTES_PER_BLOCK : nullptr;
-    const char* xs = xs_lane ? xs_lane + cb * XSUM_BYTES_PER_BLOCK : nullptr;
-    mma_blocks_rt1<NM>(&ring[s], g, xa, xs, acc);
-    if (++cb == a.nkb) {
-      const int slot = (wave + STEP_WAVES * cti) * NM;
+  int ctl = ua / a.nkb;
+  int cb = ua - ctl * a.nkb;
+  int cu = ua;
+  auto flush = [&]() {
+    const int first = wave_of_unit(a, ctl * a.nkb);
+    char* slot = contrib + ((size_t)(ctl * ph.cmax + (wave - first)) * NM) * 1024 + lane * 16;
 #pragma unroll
-      for (int q = 0; q < NM; ++q) {
-        *reinterpret_cast<floatx4*>(part_lds + (size_t)(slot + q) * 1024 + lane * 16) = acc[q];
-        acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
-      cb = 0;
-      ++cti;
+    for (int q = 0; q < NM; ++q) {
+      *reinterpret_cast<floatx4*>(slot + q * 1024) = acc[q];
+      acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
   };
-  int u = 0;
-  for (; u + STEP_PD <= U; u += STEP_PD) {
+  auto consume = [&](int s) {
+    mma_unit<NM>(&ring[s], g, xa_lane + cb * X_BYTES_PER_BLOCK, xs_lane + cb * XSUM_BYTES_PER_BLOCK,
+                 k, acc);
+    ++cu;
+    if (++cb == a.nkb || cu == ub) {
+      flush();
+      if (cb == a.nkb) {
+        cb = 0;
+        ++ctl;
+      }
+    }
+  };
+  int r = 0;
+  for (; r + STEP_PD <= U; r += STEP_PD) {
 #pragma unroll
     for (int s = 0; s < STEP_PD; s += NM) {
       consume(s);
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
-        load_block(ring[s + q], iter_addr(it), g);
-        iter_next(it, ph, L, a, wave, c);
+        load_rec(ring[s + q], iter_addr(it, a), lane);
+        iter_next(it, ph, L, a);
       }
     }
   }
 #pragma unroll
   for (int s = 0; s < STEP_PD; s += NM)
-    if (u + s < U) consume(s);
+    if (r + s < U) consume(s);
 }
-
-// Grid-wide barrier: every workgroup raises its flag (after its own stores
-// have completed), workgroup 0's first wave waits for all flags and raises the
-// release flag, everyone waits for it. Returns false when the walk must stop
-// (a timeout here or a failure elsewhere).
-__device__ bool grid_barrier(const StepParams& P, unsigned epoch, int* abort_s) {
-  unsigned* flags = reinterpret_cast<unsigned*>(P.ws + P.flags_off);
-  unsigned* go = flags + (size_t)P.G * FLAG_STRIDE;
-  int* status = reinterpret_cast<int*>(P.ws + P.status_off);
-  wait_vm0();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    *abort_s = 0;
-    st_dev(&flags[blockIdx.x * FLAG_STRIDE], epoch);
-  }
-  if (blockIdx.x == 0 && threadIdx.x < 64) {
-    bool bad = false;
-    const unsigned long long t0 = wall_clock64();
-    for (int w = threadIdx.x; w < P.G && !bad; w += 64) {
-      int n = 0;
-      while (ld_dev(&flags[(size_t)w * FLAG_STRIDE]) < epoch) {
-        __builtin_amdgcn_s_sleep(1);
-        if ((++n & 63) == 0 && (ld_dev(status) != 0 || wall_clock64() - t0 > kTimeoutTicks)) {
-          bad = true;
-          break;
-        }
-      }
-    }
-    if (bad) {
-      int expect = 0;
-      __hip_atomic_compare_exchange_strong(status, &expect, MK_ETIMEOUT, __ATOMIC_RELAXED,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (!__any(bad) && threadIdx.x == 0) st_dev(go, epoch);
-  }
-  if (threadIdx.x == 0) {
-    const unsigned long long t0 = wall_clock64();
-    int n = 0;
-    while (ld_dev(go) < epoch) {
-      __builtin_amdgcn_s_sleep(1);
-      if ((++n & 63) == 0) {
-        if (ld_dev(status) != 0) {
-          *abort_s = 1;
-          break;
-        }
-        if (wall_clock64() - t0 > kTimeoutTicks) {
-          int expect = 0;
-          __hip_atomic_compare_exchange_strong(status, &expect, MK_ETIMEOUT, __ATOMIC_RELAXED,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          *abort_s = 1;
-          break;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  return *abort_s == 0;
-}
-
-}  // namespace
-
-}  // namespace mk
-
-namespace mk {
-
-namespace {
 
 // Stage the activations of slice a into LDS in the MFMA order (see
 // q4k_device.h) and, from workgroup a.j of the slice group, the matching
 // chunks of the binary16 phase input io_x ([M][K], natural order).
 //   F16_SRC: src is binary16 [M][K] (the layer-0 input), copied as is.
 //   otherwise: src is fp32 [M][src_ld]; the value staged is
-//              binary16((y - mu[m]) * inv[m]) (round to nearest even).
+//              binary16((y - mean_m) / sqrt(var_m + 1e-6)) (round to nearest
+//              even), mean and variance from the integer statistics at st
+//              (STAT_SLOTS slots of [M][2]) over stat_n columns. The first
+//              round of activation loads and the statistics loads are issued
+//              together; the slot totals are added with integer LDS atomics,
+//              so their order does not matter.
+// Each thread loads up to kStageRound 8-wide chunks per round.
 template <bool F16_SRC>
 __device__ __forceinline__ void stage_slice(const void* src, int src_ld, int K, int M,
-                                            const Assign& a, const float* mu, const float* inv,
+                                            const Assign& a, const long long* st, int stat_n,
+                                            unsigned long long* tot_s, float* mu_s, float* inv_s,
                                             char* x_lds, int x_stride, uint16_t* io_x, int tid) {
   const int cpr = a.nkb * 32;  // 8-wide chunks per row
   const int items = M * cpr;
-  for (int it = tid; it < items; it += STEP_THREADS) {
-    const int m = it / cpr;
-    const int ch = it - m * cpr;
-    const int b = ch >> 5;
-    const int kk = (ch & 31) * 8;
-    const int k = (a.kb0 + b) * QK + kk;
-    u32x4 h;  // 8 binary16 values, natural order
-    if (F16_SRC) {
-      h = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + (size_t)m * K + k);
-    } else {
-      const float* s = static_cast<const float*>(src) + (size_t)m * src_ld + k;
-      const floatx4 v0 = *reinterpret_cast<const floatx4*>(s);
-      const floatx4 v1 = *reinterpret_cast<const floatx4*>(s + 4);
-      const float mm = mu[m], iv = inv[m];
-      half2v p0 = {(_Float16)((v0.x - mm) * iv), (_Float16)((v0.y - mm) * iv)};
-      half2v p1 = {(_Float16)((v0.z - mm) * iv), (_Float16)((v0.w - mm) * iv)};
-      half2v p2 = {(_Float16)((v1.x - mm) * iv), (_Float16)((v1.y - mm) * iv)};
-      half2v p3 = {(_Float16)((v1.z - mm) * iv), (_Float16)((v1.w - mm) * iv)};
-      h = u32x4{bit_cast_<uint32_t>(p0), bit_cast_<uint32_t>(p1), bit_cast_<uint32_t>(p2),
-                bit_cast_<uint32_t>(p3)};
+  if (!F16_SRC && tid < 2 * M) tot_s[tid] = 0ull;
+  for (int base = 0; base < items; base += STEP_THREADS * kStageRound) {
+    floatx4 v0[kStageRound], v1[kStageRound];
+    u32x4 hv[kStageRound];
+#pragma unroll
+    for (int i = 0; i < kStageRound; ++i) {
+      const int it = base + i * STEP_THREADS + tid;
+      if (it < items) {
+        const int m = it / cpr;
+        const int ch = it - m * cpr;
+        const int k = (a.kb0 + (ch >> 5)) * QK + (ch & 31) * 8;
+        if (F16_SRC) {
+          hv[i] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) +
+                                                  (size_t)m * K + k);
+        } else {
+          const float* s = static_cast<const float*>(src) + (size_t)m * src_ld + k;
+          v0[i] = *reinterpret_cast<const floatx4*>(s);
+          v1[i] = *reinterpret_cast<const floatx4*>(s + 4);
+        }
+      }
     }
-    if (io_x && (ch % a.gs) == a.j) *reinterpret_cast<u32x4*>(io_x + (size_t)m * K + k) = h;
-    u32x4 o;  // element order 0,2,1,3,4,6,5,7
-    o.x = (h.x & 0xFFFFu) | (h.y << 16);
-    o.y = (h.x >> 16) | (h.y & 0xFFFF0000u);
-    o.z = (h.z & 0xFFFFu) | (h.w << 16);
-    o.w = (h.z >> 16) | (h.w & 0xFFFF0000u);
-    const int gq = kk >> 6, hb = (kk >> 5) & 1, u = (kk >> 3) & 3;
-    *reinterpret_cast<u32x4*>(x_lds + (size_t)m * x_stride + b * X_BYTES_PER_BLOCK + gq * 128 +
-                              (2 * u + hb) * 16) = o;
+    if (!F16_SRC && base == 0) {
+      // statistics of the producer: up to kStatPer slot values per thread
+      const int nv = STAT_SLOTS * M * 2;
+      long long pv[kStatPer];
+#pragma unroll
+      for (int i = 0; i < kStatPer; ++i) {
+        const int e = tid + i * STEP_THREADS;
+        pv[i] = e < nv ? ld_dev(st + e) : 0;
+      }
+      __syncthreads();  // tot_s cleared
+#pragma unroll
+      for (int i = 0; i < kStatPer; ++i) {
+        const int e = tid + i * STEP_THREADS;
+        if (e < nv) atomicAdd(&tot_s[e % (2 * M)], (unsigned long long)pv[i]);
+      }
+      __syncthreads();
+      if (tid < M) {
+        const double mean = (double)(long long)tot_s[2 * tid] / STAT_SCALE_SUM / stat_n;
+        const double e2 = (double)(long long)tot_s[2 * tid + 1] / STAT_SCALE_SQ / stat_n;
+        double var = e2 - mean * mean;
+        if (var < 0.0) var = 0.0;
+        mu_s[tid] = (float)mean;
+        inv_s[tid] = (float)(1.0 / sqrt(var + 1e-6));
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < kStageRound; ++i) {
+      const int it = base + i * STEP_THREADS + tid;
+      if (it >= items) continue;
+      const int m = it / cpr;
+      const int ch = it - m * cpr;
+      const int b = ch >> 5;
+      const int kk = (ch & 31) * 8;
+      const int k = (a.kb0 + b) * QK + kk;
+      u32x4 h;
+      if (F16_SRC) {
+        h = hv[i];
+      } else {
+        const float mm = mu_s[m], iv = inv_s[m];
+        const half2v p0 = {(_Float16)((v0[i].x - mm) * iv), (_Float16)((v0[i].y - mm) * iv)};
+        const half2v p1 = {(_Float16)((v0[i].z - mm) * iv), (_Float16)((v0[i].w - mm) * iv)};
+        const half2v p2 = {(_Float16)((v1[i].x - mm) * iv), (_Float16)((v1[i].y - mm) * iv)};
+        const half2v p3 = {(_Float16)((v1[i].z - mm) * iv), (_Float16)((v1[i].w - mm) * iv)};
+        h = u32x4{bit_cast_<uint32_t>(p0), bit_cast_<uint32_t>(p1), bit_cast_<uint32_t>(p2),
+                  bit_cast_<uint32_t>(p3)};
+      }
+      if (io_x && (ch % a.gs) == a.j) *reinterpret_cast<u32x4*>(io_x + (size_t)m * K + k) = h;
+      u32x4 o;  // element order 0,2,1,3,4,6,5,7
+      o.x = (h.x & 0xFFFFu) | (h.y << 16);
+      o.y = (h.x >> 16) | (h.y & 0xFFFF0000u);
+      o.z = (h.z & 0xFFFFu) | (h.w << 16);
+      o.w = (h.z >> 16) | (h.w & 0xFFFF0000u);
+      const int gq = kk >> 6, hb = (kk >> 5) & 1, u = (kk >> 3) & 3;
+      *reinterpret_cast<u32x4*>(x_lds + (size_t)m * x_stride + b * X_BYTES_PER_BLOCK + gq * 128 +
+                                (2 * u + hb) * 16) = o;
+    }
   }
 }
 
 // Sub-block sums of the staged activations, split into binary16 hi + lo, for
-// the min-term MFMA. Row m, block b, sub-block j lands at
+// the min-term MFMA: row m, block b, sub-block j at
 // xs_lds + (m * nkb_stride + b) * 32 + 4 * j.
 __device__ __forceinline__ void stage_xsum(int M, int nkb, int nkb_stride, const char* x_lds,
                                            int x_stride, char* xs_lds, int tid) {
@@ -350,81 +370,157 @@ __device__ __forceinline__ void stage_xsum(int M, int nkb, int nkb_stride, const
 }
 
 // Row mean and 1/sqrt(var + 1e-6) of the statistics of (layer, phase) over
-// n columns, into LDS.
-__device__ __forceinline__ void load_stats(const StepParams& P, int l, int p, int n, float* mu_s,
-                                           float* inv_s, int tid) {
-  if (tid < P.M) {
-    const long long* st = reinterpret_cast<const long long*>(P.ws + P.stats_off) +
-                          (size_t)(l * 4 + p) * STAT_SLOTS * P.M * 2;
-    long long s1 = 0, s2 = 0;
-    for (int sl = 0; sl < STAT_SLOTS; ++sl) {
-      s1 += ld_dev(st + ((size_t)sl * P.M + tid) * 2);
-      s2 += ld_dev(st + ((size_t)sl * P.M + tid) * 2 + 1);
+// n columns, into mu_s / inv_s. The STAT_SLOTS slots are integer sums, so the
+// totals do not depend on the order they are added in.
+__device__ __forceinline__ void load_stats(const StepParams& P, int l, int p, int n,
+                                           unsigned long long* tot_s, float* mu_s, float* inv_s,
+                                           int tid) {
+  const int M = P.M;
+  if (tid < 2 * M) tot_s[tid] = 0ull;
+  __syncthreads();
+  const long long* st = reinterpret_cast<const long long*>(P.ws + P.stats_off) +
+                        (size_t)(l * 4 + p) * STAT_SLOTS * M * 2;
+  const int nv = STAT_SLOTS * M * 2;
+  long long part[2] = {0, 0};
+  int idx[2] = {-1, -1};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + i * STEP_THREADS;
+    if (e < nv) {
+      part[i] = ld_dev(st + e);
+      idx[i] = e % (2 * M);
     }
-    const double mean = (double)s1 / STAT_SCALE_SUM / n;
-    const double e2 = (double)s2 / STAT_SCALE_SQ / n;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    if (idx[i] >= 0) atomicAdd(&tot_s[idx[i]], (unsigned long long)part[i]);
+  for (int e = tid + 2 * STEP_THREADS; e < nv; e += STEP_THREADS)
+    atomicAdd(&tot_s[e % (2 * M)], (unsigned long long)ld_dev(st + e));
+  __syncthreads();
+  if (tid < M) {
+    const double mean = (double)(long long)tot_s[2 * tid] / STAT_SCALE_SUM / n;
+    const double e2 = (double)(long long)tot_s[2 * tid + 1] / STAT_SCALE_SQ / n;
     double var = e2 - mean * mean;
     if (var < 0.0) var = 0.0;
     mu_s[tid] = (float)mean;
     inv_s[tid] = (float)(1.0 / sqrt(var + 1e-6));
   }
+  __syncthreads();
 }
 
-__device__ __forceinline__ void set_status(const StepParams& P, int code) {
-  int* status = reinterpret_cast<int*>(P.ws + P.status_off);
-  int expect = 0;
-  __hip_atomic_compare_exchange_strong(status, &expect, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Finish one tile whose every K slice has arrived: add the slice partials in
-// slice order, write the outputs, the consumer copy and the row statistics.
-// Called by a whole wave; lane = column (lane % 16) x row group (lane / 16).
-__device__ __forceinline__ void fixup_tile(const StepParams& P, const DevPhase& ph, int p, int l,
-                                           const DevLayer* L, int tg, int lane) {
-  const int M = P.M;
-  const int seg = seg_of(ph, tg);
-  const int nseg = ph.seg_n[seg];
-  const int cs = (tg - ph.seg_t0[seg]) * 16 + (lane & 15);
-  const bool valid = cs < nseg;
-  const int rg = lane >> 4;
-  const float* part = reinterpret_cast<const float*>(P.ws + ph.part_off);
-  const bool has_cons = (p != 0) || (seg == 0);
-  float* cons = reinterpret_cast<float*>(P.ws + ph.cons_off + (size_t)l * ph.cons_layer_bytes);
-  long long* st = reinterpret_cast<long long*>(P.ws + P.stats_off) +
-                  ((size_t)(l * 4 + p) * STAT_SLOTS + (tg % STAT_SLOTS)) * M * 2;
-#pragma unroll
-  for (int jr = 0; jr < 4; ++jr) {
-    const int m = rg + 4 * jr;
-    float y0 = 0.f, y1 = 0.f;
-    if (m < M && valid) {
-      const size_t col0 = (size_t)ph.seg_c0[seg] + cs;
-      for (int sl = 0; sl < ph.sk; ++sl) y0 += ld_dev(&part[((size_t)sl * M + m) * ph.ncols + col0]);
-      L->y[ph.mat0 + seg][(size_t)m * nseg + cs] = y0;
-      if (ph.nm == 2) {
-        const size_t col1 = col0 + nseg;
-        for (int sl = 0; sl < ph.sk; ++sl)
-          y1 += ld_dev(&part[((size_t)sl * M + m) * ph.ncols + col1]);
-        L->y[ph.mat0 + seg + 1][(size_t)m * nseg + cs] = y1;
+// Wait until every tile of the phases up to (l, p) has been counted finished.
+__device__ __forceinline__ bool wait_done(const StepParams& P, const DevPhase* PH, int l, int p,
+                                          int* abort_s) {
+  if (threadIdx.x < 64) {
+    const unsigned* done = reinterpret_cast<const unsigned*>(P.ws + P.done_off);
+    const int* status = reinterpret_cast<const int*>(P.ws + P.status_off);
+    const int c = threadIdx.x;
+    unsigned per_layer = 0, upto = 0;
+    for (int q = 0; q < 4; ++q) {
+      const int nt = PH[q].nt;
+      const unsigned nc = (unsigned)(nt / DONE_CTRS + (c < nt % DONE_CTRS ? 1 : 0));
+      per_layer += nc;
+      if (q <= p) upto += nc;
+    }
+    const unsigned target = (unsigned)l * per_layer + upto;
+    const unsigned long long t0 = wall_clock64();
+    int n = 0;
+    bool bad = false;
+    while (ld_dev(done + (size_t)c * CTR_STRIDE) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if ((++n & 63) == 0) {
+        if (ld_dev(status) != 0) {
+          bad = true;
+          break;
+        }
+        if (wall_clock64() - t0 > kTimeoutTicks) {
+          set_status(P, MK_ETIMEOUT);
+          bad = true;
+          break;
+        }
       }
     }
-    if (has_cons) {
-      const float cv = ph.nm == 2 ? y0 * y1 : y0;
-      if (m < M && valid) st_dev(&cons[(size_t)m * ph.cons_ld + cs], cv);
+    const bool any_bad = __any(bad);
+    if (threadIdx.x == 0) *abort_s = any_bad ? 1 : 0;
+  }
+  __syncthreads();
+  return *abort_s == 0;
+}
+
+// Finish the tiles whose last K slice this workgroup contributed: add the sk
+// partials in slice order, write the outputs, the consumer copy and the row
+// statistics. Elements (tile, m, column) are spread over all threads; each
+// group of 16 lanes holds the 16 columns of one (tile, m).
+__device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase& ph, int p, int l,
+                                            const DevLayer* L, const Assign& a,
+                                            const int* last_list, int nlast, int tid) {
+  const int M = P.M;
+  const float* part = reinterpret_cast<const float*>(P.ws + ph.part_off);
+  float* consb = reinterpret_cast<float*>(P.ws + ph.cons_off + (size_t)l * ph.cons_layer_bytes);
+  long long* stl = reinterpret_cast<long long*>(P.ws + P.stats_off) +
+                   (size_t)(l * 4 + p) * STAT_SLOTS * M * 2;
+  const int items = nlast * M * 16;
+  for (int base = 0; base < items; base += STEP_THREADS * kFixRound) {
+    float y[kFixRound][2];
+#pragma unroll
+    for (int i = 0; i < kFixRound; ++i) {
+      y[i][0] = y[i][1] = 0.f;
+      const int e = base + i * STEP_THREADS + tid;
+      if (e >= items) continue;
+      const int c = e & 15;
+      const int rest = e >> 4;
+      const int li = rest / M;
+      const int m = rest - li * M;
+      const int tg = a.t0 + last_list[li];
+      const int seg = seg_of(ph, tg);
+      const int cs = (tg - ph.seg_t0[seg]) * 16 + c;
+      if (cs >= ph.seg_n[seg]) continue;
+      const size_t col0 = (size_t)ph.seg_c0[seg] + cs;
+      for (int sl = 0; sl < ph.sk; ++sl)
+        y[i][0] += ld_dev(&part[((size_t)sl * M + m) * ph.ncols + col0]);
+      if (ph.nm == 2) {
+        const size_t col1 = col0 + ph.seg_n[seg];
+        for (int sl = 0; sl < ph.sk; ++sl)
+          y[i][1] += ld_dev(&part[((size_t)sl * M + m) * ph.ncols + col1]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kFixRound; ++i) {
+      const int e0 = base + i * STEP_THREADS;
+      if (e0 >= items) break;  // uniform across the workgroup
+      const int e = e0 + tid;
+      const bool live = e < items;
+      const int c = e & 15;
+      const int rest = e >> 4;
+      const int li = live ? rest / M : 0;
+      const int m = live ? rest - li * M : 0;
+      const int tg = a.t0 + last_list[li];
+      const int seg = seg_of(ph, tg);
+      const int nseg = ph.seg_n[seg];
+      const int cs = (tg - ph.seg_t0[seg]) * 16 + c;
+      const bool valid = live && cs < nseg;
+      if (valid) {
+        L->y[ph.mat0 + seg][(size_t)m * nseg + cs] = y[i][0];
+        if (ph.nm == 2) L->y[ph.mat0 + seg + 1][(size_t)m * nseg + cs] = y[i][1];
+      }
+      const bool has_cons = live && ((p != 0) || (seg == 0));
+      const float cv = valid ? (ph.nm == 2 ? y[i][0] * y[i][1] : y[i][0]) : 0.f;
+      if (has_cons && valid) st_dev(&consb[(size_t)m * ph.cons_ld + cs], cv);
       double s1 = cv, s2 = (double)cv * (double)cv;
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) {
         s1 += __shfl_xor(s1, off, 16);
         s2 += __shfl_xor(s2, off, 16);
       }
-      if ((lane & 15) == 0 && m < M) {
+      if (has_cons && c == 0) {
         const double f1 = s1 * STAT_SCALE_SUM, f2 = s2 * STAT_SCALE_SQ;
+        long long* st = stl + ((size_t)(tg % STAT_SLOTS) * M + m) * 2;
         if (!(fabs(f1) < 4.0e18) || !(f2 < 4.0e18)) {
           set_status(P, MK_ERANGE);
         } else {
-          __hip_atomic_fetch_add(st + (size_t)m * 2, (long long)llrint(f1), __ATOMIC_RELAXED,
+          __hip_atomic_fetch_add(st, (long long)llrint(f1), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_fetch_add(st + (size_t)m * 2 + 1, (long long)llrint(f2), __ATOMIC_RELAXED,
+          __hip_atomic_fetch_add(st + 1, (long long)llrint(f2), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
         }
       }
@@ -432,11 +528,16 @@ __device__ __forceinline__ void fixup_tile(const StepParams& P, const DevPhase& 
   }
 }
 
-// End of a phase in one workgroup: publish the slice partials of its tiles,
-// count the arrivals per tile and finish the tiles whose last slice this is.
-__device__ __forceinline__ void phase_outputs(const StepParams& P, const DevPhase& ph, int p, int l,
-                                              const DevLayer* L, const Assign& a,
-                                              const char* part_lds, int* last_s, int tid) {
+// End of a phase in one workgroup: add the wave parts of each tile, publish
+// the slice partials and count them in; then, for the tiles this workgroup
+// finishes (tile t is finished by the workgroup of slice t % sk), wait until
+// every slice has arrived, add the partials in slice order, and count the
+// tiles as finished. Spreading the finishing over the slices keeps every
+// workgroup's share of it equal.
+__device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhase& ph, int p,
+                                              int l, const DevLayer* L, const Assign& a,
+                                              const char* contrib, int* fin_list, int* nfin_s,
+                                              int* abort_s, int tid) {
   const int M = P.M;
   float* part = reinterpret_cast<float*>(P.ws + ph.part_off);
   const int entries = a.tw * ph.nm * 64;
@@ -447,7 +548,17 @@ __device__ __forceinline__ void phase_outputs(const StepParams& P, const DevPhas
     const int seg = seg_of(ph, tg);
     const int cs = (tg - ph.seg_t0[seg]) * 16 + (ln & 15);
     if (cs >= ph.seg_n[seg]) continue;
-    const floatx4 v = *reinterpret_cast<const floatx4*>(part_lds + (size_t)slot * 1024 + ln * 16);
+    const int w0 = wave_of_unit(a, tl * a.nkb);
+    const int w1 = wave_of_unit(a, (tl + 1) * a.nkb - 1);
+    floatx4 v = *reinterpret_cast<const floatx4*>(
+        contrib + ((size_t)(tl * ph.cmax) * ph.nm + q) * 1024 + ln * 16);
+    for (int kk = 1; kk <= w1 - w0; ++kk) {
+      // waves with an empty range (fewer units than waves) wrote nothing
+      if (wave_begin(a, w0 + kk) == wave_begin(a, w0 + kk + 1)) continue;
+      const floatx4 u = *reinterpret_cast<const floatx4*>(
+          contrib + ((size_t)(tl * ph.cmax + kk) * ph.nm + q) * 1024 + ln * 16);
+      v += u;
+    }
     const size_t pc = (size_t)ph.seg_c0[seg] + (size_t)q * ph.seg_n[seg] + cs;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -458,93 +569,133 @@ __device__ __forceinline__ void phase_outputs(const StepParams& P, const DevPhas
   wait_vm0();
   __syncthreads();
   unsigned* ctr = reinterpret_cast<unsigned*>(P.ws + P.ctr_off) + (size_t)p * P.max_nt;
-  if (tid < a.tw) {
-    const unsigned old = __hip_atomic_fetch_add(&ctr[a.t0 + tid], 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    last_s[tid] = old == (unsigned)(ph.sk * (l + 1) - 1);
+  if (tid < a.tw)
+    __hip_atomic_fetch_add(&ctr[a.t0 + tid], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    int n = 0;
+    for (int i = 0; i < a.tw; ++i)
+      if ((a.t0 + i) % ph.sk == a.s) fin_list[n++] = i;
+    *nfin_s = n;
+    *abort_s = 0;
   }
   __syncthreads();
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int tl = wave; tl < a.tw; tl += STEP_WAVES)
-    if (last_s[tl]) fixup_tile(P, ph, p, l, L, a.t0 + tl, lane);
+  const int nfin = *nfin_s;
+  if (tid < nfin) {
+    const unsigned target = (unsigned)(ph.sk * (l + 1));
+    const unsigned* c = &ctr[a.t0 + fin_list[tid]];
+    const int* status = reinterpret_cast<const int*>(P.ws + P.status_off);
+    const unsigned long long t0 = wall_clock64();
+    int n = 0;
+    while (ld_dev(c) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if ((++n & 63) == 0) {
+        if (ld_dev(status) != 0) {
+          *abort_s = 1;
+          break;
+        }
+        if (wall_clock64() - t0 > kTimeoutTicks) {
+          set_status(P, MK_ETIMEOUT);
+          *abort_s = 1;
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (*abort_s) return false;
+  fixup_tiles(P, ph, p, l, L, a, fin_list, nfin, tid);
   wait_vm0();
   __syncthreads();
+  if (tid < nfin) {
+    unsigned* done = reinterpret_cast<unsigned*>(P.ws + P.done_off);
+    const int tg = a.t0 + fin_list[tid];
+    __hip_atomic_fetch_add(done + (size_t)(tg % DONE_CTRS) * CTR_STRIDE, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return true;
 }
 
 }  // namespace
 
 __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ DevPhase PH[4];
+  __shared__ const uint8_t* wtab[STEP_MAX_LAYERS][7];
   __shared__ float mu_s[STEP_MAX_M];
   __shared__ float inv_s[STEP_MAX_M];
-  __shared__ int abort_s;
+  __shared__ unsigned long long tot_s[2 * STEP_MAX_M];
+  __shared__ int abort_s, nfin_s;
   const int M = P.M;
   const int w = blockIdx.x;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int c = lane & 15, g = lane >> 4;
-
-  const DevPhase* PH = reinterpret_cast<const DevPhase*>(P.ws + P.phases_off);
-  // LDS: staged activations | sub-block sums | tile partials | arrival flags
-  int x_stride_max = 0, nkb_max = 0, part_max = 0;
-  for (int p = 0; p < 4; ++p) {
-    x_stride_max = max(x_stride_max, PH[p].x_stride);
-    nkb_max = max(nkb_max, PH[p].nkb);
-    part_max = max(part_max, PH[p].tw_max * PH[p].nm);
-  }
-  char* x_lds = smem;
-  char* xs_lds = x_lds + (size_t)M * x_stride_max;
-  char* part_lds = xs_lds + (size_t)M * nkb_max * XSUM_BYTES_PER_BLOCK;
-  int* last_s = reinterpret_cast<int*>(part_lds + (size_t)part_max * 1024);
-
   const DevLayer* layers = reinterpret_cast<const DevLayer*>(P.ws + P.layers_off);
+  {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(P.ws + P.phases_off);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(PH);
+    for (int i = tid; i < (int)(sizeof(PH) / 4); i += STEP_THREADS) dst[i] = src[i];
+    for (int i = tid; i < P.n_layers * 7; i += STEP_THREADS) wtab[i / 7][i % 7] = layers[i / 7].w[i % 7];
+  }
+  __syncthreads();
+  const UnpackConsts k = unpack_consts();
+  // Rows past M read row M-1 (their results are never stored), so every
+  // lane's activation reads are unconditional.
+  const int arow = c < M ? c : M - 1;
+
   BlockRegs ring[STEP_PD];
   Iter it;
   Assign a = assign(PH[0], w, P.G);
-  iter_init(it, PH[0], &layers[0], a, wave, c);
-  ring_prologue(ring, it, PH[0], &layers[0], a, wave, c, g);
+  iter_init(it, PH[0], wtab[0], a, wave);
+  ring_fill(ring, it, PH[0], wtab[0], a, lane, 0, STEP_PD_PRE);
 
-  unsigned epoch = 0;
   for (int l = 0; l < P.n_layers; ++l) {
     const DevLayer* L = &layers[l];
     for (int p = 0; p < 4; ++p) {
       const DevPhase& ph = PH[p];
-      // ---- stage this phase's input slice
+      char* x_lds = smem;
+      char* xs_lds = x_lds + (size_t)M * ph.x_stride;
+      char* contrib = smem + ph.lds_contrib;
+      int* fin_list = reinterpret_cast<int*>(contrib + (size_t)ph.tw_max * ph.cmax * ph.nm * 1024);
+      // ---- stage this phase's input slice, then the rest of the first
+      //      weight records
       if (l == 0 && p == 0) {
-        stage_slice<true>(P.x0, 0, ph.K, M, a, nullptr, nullptr, x_lds, ph.x_stride, L->x[0], tid);
+        stage_slice<true>(P.x0, 0, ph.K, M, a, nullptr, 0, tot_s, mu_s, inv_s, x_lds, ph.x_stride,
+                          L->x[0], tid);
       } else {
         const int ls = p ? l : l - 1, ps = p ? p - 1 : 3;
         const DevPhase& src = PH[ps];
-        load_stats(P, ls, ps, src.stat_n, mu_s, inv_s, tid);
-        __syncthreads();
+        const long long* st = reinterpret_cast<const long long*>(P.ws + P.stats_off) +
+                              (size_t)(ls * 4 + ps) * STAT_SLOTS * M * 2;
         const float* cons = reinterpret_cast<const float*>(P.ws + src.cons_off +
                                                            (size_t)ls * src.cons_layer_bytes);
-        stage_slice<false>(cons, src.cons_ld, ph.K, M, a, mu_s, inv_s, x_lds, ph.x_stride,
-                           L->x[p], tid);
+        stage_slice<false>(cons, src.cons_ld, ph.K, M, a, st, src.stat_n, tot_s, mu_s, inv_s,
+                           x_lds, ph.x_stride, L->x[p], tid);
       }
+      ring_fill(ring, it, ph, wtab[l], a, lane, STEP_PD_PRE, STEP_PD);
       __syncthreads();
       stage_xsum(M, a.nkb, ph.nkb, x_lds, ph.x_stride, xs_lds, tid);
       __syncthreads();
 
       // ---- stream the weights
-      const char* xa_lane = c < M ? x_lds + (size_t)c * ph.x_stride + g * 128 : nullptr;
-      const char* xs_lane =
-          c < M ? xs_lds + (size_t)c * ph.nkb * XSUM_BYTES_PER_BLOCK + 8 * g : nullptr;
+      const char* xa_lane = x_lds + (size_t)arow * ph.x_stride + g * 128;
+      const char* xs_lane = xs_lds + (size_t)arow * ph.nkb * XSUM_BYTES_PER_BLOCK + 8 * g;
       if (ph.nm == 2)
-        phase_compute<2>(ring, it, ph, L, a, wave, lane, xa_lane, xs_lane, part_lds);
+        phase_compute<2>(ring, it, ph, wtab[l], a, wave, lane, xa_lane, xs_lane, contrib, k);
       else
-        phase_compute<1>(ring, it, ph, L, a, wave, lane, xa_lane, xs_lane, part_lds);
+        phase_compute<1>(ring, it, ph, wtab[l], a, wave, lane, xa_lane, xs_lane, contrib, k);
       __syncthreads();
 
-      // ---- finish tiles, then start the next phase's weight stream
-      phase_outputs(P, ph, p, l, L, a, part_lds, last_s, tid);
+      // ---- finish tiles, start the next phase's weight stream, wait until
+      //      every tile of this phase is finished
+      if (!phase_outputs(P, ph, p, l, L, a, contrib, fin_list, &nfin_s, &abort_s, tid)) return;
       const int ln = p < 3 ? l : l + 1, pn = p < 3 ? p + 1 : 0;
       if (ln < P.n_layers) {
         a = assign(PH[pn], w, P.G);
-        iter_init(it, PH[pn], &layers[ln], a, wave, c);
-        ring_prologue(ring, it, PH[pn], &layers[ln], a, wave, c, g);
+        iter_init(it, PH[pn], wtab[ln], a, wave);
+        ring_fill(ring, it, PH[pn], wtab[ln], a, lane, 0, STEP_PD_PRE);
       }
-      if (!grid_barrier(P, ++epoch, &abort_s)) return;
+      if (!wait_done(P, PH, l, p, &abort_s)) return;
     }
   }
 
@@ -552,8 +703,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   {
     const int ls = P.n_layers - 1;
     const DevPhase& src = PH[3];
-    load_stats(P, ls, 3, src.stat_n, mu_s, inv_s, tid);
-    __syncthreads();
+    load_stats(P, ls, 3, src.stat_n, tot_s, mu_s, inv_s, tid);
     const float* cons =
         reinterpret_cast<const float*>(P.ws + src.cons_off + (size_t)ls * src.cons_layer_bytes);
     const int c0 = (int)((long long)P.H * w / P.G), c1 = (int)((long long)P.H * (w + 1) / P.G);
@@ -567,7 +717,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   }
 }
 
-// Zero the barrier flags, status word, tile counters and statistics.
+// Zero the counters, status word and statistics.
 __global__ void __launch_bounds__(256) q4k_step_clear(uint32_t* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
@@ -581,9 +731,11 @@ namespace mk {
 
 namespace {
 
-constexpr int kMaxG = 1024;                    // flags reserved for up to 1024 CUs
+constexpr int kMaxG = 1024;                    // most workgroups (CUs) planned for
 constexpr size_t kLdsLimit = 160 * 1024;
-constexpr size_t kStaticLds = 2 * STEP_MAX_M * sizeof(float) + 64;
+constexpr size_t kStaticLds = 4 * sizeof(DevPhase) + STEP_MAX_LAYERS * 7 * sizeof(void*) +
+                              2 * STEP_MAX_M * sizeof(float) +
+                              2 * STEP_MAX_M * sizeof(unsigned long long) + 64;
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -591,10 +743,25 @@ int tiles_of(int n) { return (n + 15) / 16; }
 
 struct StepPlan {
   DevPhase ph[4];
-  size_t phases_off, layers_off, flags_off, status_off, ctr_off, stats_off, sync_end;
+  size_t phases_off, layers_off, done_off, status_off, ctr_off, stats_off, sync_end;
   int max_nt;
   size_t total;
 };
+
+// Host mirror of the device work split (assign / wave_of_unit in the kernel).
+void host_assign(const DevPhase& ph, int w, int G, int* t0, int* tw, int* nkb) {
+  const int s = w % ph.sk, j = w / ph.sk;
+  const int gs = (G - s + ph.sk - 1) / ph.sk;
+  *t0 = (int)((long long)ph.nt * j / gs);
+  *tw = (int)((long long)ph.nt * (j + 1) / gs) - *t0;
+  const int kb0 = s * ph.nkb;
+  *nkb = ph.nkb < ph.KB - kb0 ? ph.nkb : ph.KB - kb0;
+}
+
+int host_wave_of_unit(int U, int x) {
+  int w = (int)(((long long)STEP_WAVES * (x + 1) - 1) / U);
+  return w < STEP_WAVES - 1 ? w : STEP_WAVES - 1;
+}
 
 // Fill the phase table for the shapes of layer 0; sk is chosen so that one
 // slice of staged activations fits the LDS budget. Offsets are relative to
@@ -649,15 +816,33 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
       ++sk;
     }
     ph.x_stride = ph.nkb * X_BYTES_PER_BLOCK + X_ROW_PAD;
-    const int gs_min = G / ph.sk;
-    ph.tw_max = (ph.nt + gs_min - 1) / gs_min;
+    ph.tw_max = 0;
+    ph.cmax = 1;
+    for (int w = 0; w < G; ++w) {
+      int t0, tw, nkb;
+      host_assign(ph, w, G, &t0, &tw, &nkb);
+      if (tw > ph.tw_max) ph.tw_max = tw;
+      const int U = tw * nkb;
+      for (int tl = 0; tl < tw; ++tl) {
+        const int c = host_wave_of_unit(U, (tl + 1) * nkb - 1) - host_wave_of_unit(U, tl * nkb) + 1;
+        if (c > ph.cmax) ph.cmax = c;
+      }
+    }
+    if (ph.tw_max < 1) ph.tw_max = 1;
+    {
+      const size_t xb = (size_t)M * ph.x_stride + (size_t)M * ph.nkb * XSUM_BYTES_PER_BLOCK;
+      const size_t c0 = (xb + 15) & ~(size_t)15;
+      ph.lds_contrib = (int)c0;
+      ph.lds_bytes = (int)(c0 + (size_t)ph.tw_max * ph.cmax * ph.nm * 1024 +
+                           2 * (size_t)ph.tw_max * sizeof(int));
+    }
     ph.cons_ld = ((ph.stat_n + 63) / 64) * 64;
     ph.cons_layer_bytes = align256((size_t)M * ph.cons_ld * sizeof(float));
   }
   // workspace layout
   size_t off = 0;
-  sp.flags_off = off;
-  off += align256((size_t)(kMaxG + 1) * FLAG_STRIDE * sizeof(unsigned));
+  sp.done_off = off;
+  off += align256((size_t)DONE_CTRS * CTR_STRIDE * sizeof(unsigned));
   sp.status_off = off;
   off += 256;
   sp.max_nt = 0;
@@ -682,17 +867,11 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
   sp.total = off;
 }
 
-size_t lds_bytes(const StepPlan& sp, int M) {
-  int x_stride_max = 0, nkb_max = 0, part_max = 0, tw_max = 0;
-  for (int p = 0; p < 4; ++p) {
-    const DevPhase& ph = sp.ph[p];
-    x_stride_max = ph.x_stride > x_stride_max ? ph.x_stride : x_stride_max;
-    nkb_max = ph.nkb > nkb_max ? ph.nkb : nkb_max;
-    part_max = ph.tw_max * ph.nm > part_max ? ph.tw_max * ph.nm : part_max;
-    tw_max = ph.tw_max > tw_max ? ph.tw_max : tw_max;
-  }
-  return (size_t)M * x_stride_max + (size_t)M * nkb_max * XSUM_BYTES_PER_BLOCK +
-         (size_t)part_max * 1024 + (size_t)tw_max * sizeof(int);
+size_t lds_bytes(const StepPlan& sp, int) {
+  size_t mx = 0;
+  for (int p = 0; p < 4; ++p)
+    if ((size_t)sp.ph[p].lds_bytes > mx) mx = (size_t)sp.ph[p].lds_bytes;
+  return mx;
 }
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -705,7 +884,8 @@ int check_mat(const mk_q4k_mat& m) {
 bool same_shape(const mk_q4k_mat& a, const mk_q4k_mat& b) { return a.N == b.N && a.K == b.K; }
 
 int check_step_shapes(const mk_q4k_layer* layers, int n_layers, int M) {
-  if (!layers || n_layers < 1 || M < 1 || M > STEP_MAX_M) return MK_EINVAL;
+  if (!layers || n_layers < 1 || n_layers > STEP_MAX_LAYERS || M < 1 || M > STEP_MAX_M)
+    return MK_EINVAL;
   const mk_q4k_layer& L = layers[0];
   const mk_q4k_mat* m[7] = {&L.q, &L.k, &L.v, &L.o, &L.gate, &L.up, &L.down};
   for (int i = 0; i < 7; ++i)
@@ -838,7 +1018,7 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
   P.x_out = x_out;
   P.ws = ws;
   P.layers_off = sp.layers_off;
-  P.flags_off = sp.flags_off;
+  P.done_off = sp.done_off;
   P.ctr_off = sp.ctr_off;
   P.max_nt = sp.max_nt;
   P.stats_off = sp.stats_off;
@@ -851,10 +1031,8 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
 
 int mk_q4k_step_status(const void* workspace, int* status_out) {
   if (!workspace || !status_out) return MK_EINVAL;
-  // the status word sits right after the barrier flags
-  mk::StepPlan sp;
-  memset(&sp, 0, sizeof(sp));
-  const size_t off = mk::align256((size_t)(mk::kMaxG + 1) * mk::FLAG_STRIDE * sizeof(unsigned));
+  // the status word sits right after the finished-tile counters
+  const size_t off = mk::align256((size_t)mk::DONE_CTRS * mk::CTR_STRIDE * sizeof(unsigned));
   int v = 0;
   if (hipMemcpy(&v, static_cast<const char*>(workspace) + off, sizeof(int),
                 hipMemcpyDeviceToHost) != hipSuccess)

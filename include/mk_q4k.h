@@ -51,7 +51,7 @@ extern "C" {
 #define MK_EOCCUPANCY (-4) /* the persistent grid cannot be co-resident       */
 #define MK_EHIP (-5)       /* a HIP runtime call failed (see mk_strerror)     */
 #define MK_ENODEV (-6)     /* the current device is not a gfx950 GPU          */
-#define MK_ETIMEOUT (-7)   /* device status: a grid-barrier wait timed out     */
+#define MK_ETIMEOUT (-7)   /* device status: a cross-workgroup wait timed out  */
 #define MK_ERANGE (-8)     /* device status: a row statistic left its range    */
 
 #define MK_Q4K_QK 256          /* weights per super-block                   */
@@ -82,9 +82,30 @@ int mk_q4k_gemm_ws(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, 
                    int K, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Tile records: a load-time reordering of a Q4_K matrix for the streaming
+ * kernels. Every block keeps its 144 bytes; rows are grouped in tiles of 16
+ * (rows past N are zero blocks) and for tile t and super-block kb the
+ * 2304-byte record at (t * (K/256) + kb) * 2304 holds the 16 block headers
+ * (bytes 0-15 of each block, row order), then for l = 0..63 (row i = l % 16,
+ * g = l / 16) quant bytes [32g, 32g+16) of row i, then for the same l quant
+ * bytes [32g+16, 32g+32). A wave then reads each operand with one contiguous
+ * 1 KiB load instead of sixteen 16-byte pieces 2.9 KB apart.
+ *
+ * mk_q4k_tiles_bytes: size of the record form of an N x K matrix
+ *   (ceil(N/16) * (K/256) * 2304), 0 for an invalid shape.
+ * mk_q4k_repack: write the record form of W_rows (layout above, N rows) to
+ *   W_tiles (device, mk_q4k_tiles_bytes bytes, must not overlap W_rows).
+ *   Asynchronous on `stream`; MK_OK, MK_EINVAL, MK_EALIGN or MK_EHIP.
+ */
+size_t mk_q4k_tiles_bytes(int N, int K);
+int mk_q4k_repack(const void* W_rows, void* W_tiles, int N, int K, void* stream);
+
+/*
  * The decode-step walk: one persistent kernel launch runs n_layers layers of
- * seven Q4_K matrices each, in their data-dependency order, with grid-wide
- * barriers between dependent phases:
+ * seven Q4_K matrices each, in their data-dependency order. No grid-wide
+ * barrier is used: a phase's outputs are counted into device counters and the
+ * next phase starts on every workgroup as soon as those counters show that its
+ * whole input exists:
  *   phase A  x_l           -> q [M, Nq], k [M, Nk], v [M, Nv]
  *   phase B  T(q)          -> o [M, H]
  *   phase C  T(o)          -> gate [M, F], up [M, F]
@@ -98,10 +119,13 @@ int mk_q4k_gemm_ws(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, 
  *
  * Chain rules (checked): q.K = k.K = v.K = gate.K = up.K = down.N = H (the
  * hidden size), o.K = q.N, gate.N = up.N = down.K = F; every K % 256 == 0;
- * every layer has the same shapes.
+ * every layer has the same shapes. Limits: 1 <= M <= 16 stacked rows,
+ * 1 <= n_layers <= 128. Each phase's K range is cut into slices whose input
+ * rows fit in on-chip memory; a shape whose plan still does not fit one
+ * workgroup per compute unit returns MK_EOCCUPANCY.
  */
 typedef struct {
-  const void* w; /* device: N * (K/256) Q4_K blocks */
+  const void* w; /* device: the tile-record form (mk_q4k_repack) of the matrix */
   int N;         /* output columns (weight rows)    */
   int K;         /* input width                     */
 } mk_q4k_mat;
@@ -127,11 +151,12 @@ size_t mk_q4k_step_workspace_bytes(const mk_q4k_layer* layer0 /* host */, int n_
  *   x0        [M][H] binary16 input of layer 0.
  *   x_out     [M][H] binary16 T(down) of the last layer.
  *   workspace device memory of >= mk_q4k_step_workspace_bytes bytes, used by
- *             one call at a time; it holds the barrier counter, the device
- *             status word, row statistics, partial sums and the copied
- *             descriptor tables.
+ *             one call at a time (calls that overlap on one workspace race);
+ *             it holds the phase counters, the device status word, row
+ *             statistics, partial sums and the copied descriptor tables.
+ *             The call clears what must start at zero itself.
  * Returns MK_OK (enqueued) or a host-side error. Device-side failures (a
- * barrier wait that times out, a statistic out of range) are recorded in the
+ * counter wait that times out, a statistic out of range) are recorded in the
  * workspace status word; read it with mk_q4k_step_status after the stream
  * has been synchronised.
  */

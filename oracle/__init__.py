@@ -77,6 +77,8 @@ def _load():
         lib.oracle_dequant_rows.argtypes = [vp, i64, i64, vp]
         lib.oracle_gemm.restype = ctypes.c_int
         lib.oracle_gemm.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
         lib.oracle_standardize.restype = None
         lib.oracle_standardize.argtypes = [vp, i64, i64, ctypes.c_double, vp]
         _lib = lib
@@ -187,3 +189,8 @@ def f16_spacing(t) -> np.ndarray:
     the binary16 value nearest to t); the tolerance of the transform check."""
     t = np.asarray(t, dtype=np.float64)
     return np.spacing(np.abs(t).astype(np.float16)).astype(np.float64)
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops run on."""
+    return int(_load().oracle_num_threads())

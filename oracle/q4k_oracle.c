@@ -213,3 +213,15 @@ void oracle_f64_to_f16_array(const double* v, int64_t n, uint16_t* out) {
 void oracle_f16_to_f64_array(const uint16_t* h, int64_t n, double* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_to_f64(h[i]);
 }
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+/* Threads the oracle's parallel loops use. */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -30,7 +30,11 @@ def weight_bytes(shp, n_layers):
 
 
 class Stack:
-    """n_layers of Q4_K matrices plus the per-layer output buffers on `device`."""
+    """n_layers of Q4_K matrices plus the per-layer output buffers on `device`.
+
+    The weights are kept on the device in the tile-record form the step walk
+    reads (made by the library's repack call from the generated rows); the
+    rows themselves can be regenerated on the host with host_rows()."""
 
     def __init__(self, n_layers, M, shp=None, seed=0, device="cuda:0"):
         import torch
@@ -41,20 +45,22 @@ class Stack:
         self.seed = seed
         self.device = device
         self.H = self.shp["q"][1]
-        self.weights = []     # per layer: name -> uint8 tensor [N, K/256*144]
+        import bit_weight_streaming_amd as mk
+        self.weights = []     # per layer: name -> uint8 tile-record tensor
         biggest = max(N * (K // QK) * BLOCK_BYTES for N, K in self.shp.values())
         pinned = torch.empty(biggest, dtype=torch.uint8, pin_memory=True)
+        rows = torch.empty(biggest, dtype=torch.uint8, device=device)
         for l in range(n_layers):
             lay = {}
             for mi, name in enumerate(MATRIX_ORDER):
                 N, K = self.shp[name]
                 nbytes = N * (K // QK) * BLOCK_BYTES
                 q4k_fill_ptr(weight_key(seed, l, mi), K, 0, N, pinned.data_ptr())
-                t = torch.empty((N, K // QK * BLOCK_BYTES), dtype=torch.uint8, device=device)
-                t.view(-1).copy_(pinned[:nbytes], non_blocking=False)
-                lay[name] = t
+                rows[:nbytes].copy_(pinned[:nbytes], non_blocking=False)
+                lay[name] = mk.repack(rows[:nbytes], N, K)
+                torch.cuda.synchronize()
             self.weights.append(lay)
-        del pinned
+        del pinned, rows
         self.x0 = torch.from_numpy(activations(seed, M, self.H)).to(device)
         self.x_out = torch.empty((M, self.H), dtype=torch.float16, device=device)
         self.io = []
