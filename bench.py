@@ -26,6 +26,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s (decimal)
+# HBM traffic of the step kernel as measured by rocprofv3 PMC runs; reported only
+# while the kernel sources still hash to the value recorded there.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4k_step_m12_64layers_traffic.md")
+KERNEL_SOURCES = ("q4k_step.hip", "q4k_step.h", "q4k_device.h")
+COPY_BYTES = 1 << 30
 METRIC = "weight-stream GB/s and % of HBM peak at M=12; rows*tokens/s per decode step"
 
 
@@ -46,45 +51,91 @@ def algorithmic_bytes(stack) -> dict:
     return {"weights": w, "y": y, "x": x, "io": io, "total": w + y + x + io}
 
 
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_weight_streaming_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(n_layers: int, M: int):
+    """HBM bytes per launch from the committed counter summary, or None when it
+    is absent, was taken on another workload or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(l.strip()[2:].split(" = ", 1) for l in fh if l.startswith("- ") and " = " in l)
+    except OSError:
+        return None
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    if int(kv.get("n_layers", -1)) != n_layers or int(kv.get("M", -1)) != M:
+        return None
+    return int(kv["hbm_bytes_per_launch"])
+
+
+def copy_calibration(steps: int) -> int:
+    """Plain device-to-device copies of COPY_BYTES each (the reference kernel the
+    PMC byte counters are scaled by)."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES,
+                      "launches": steps}), flush=True)
+    return 0
+
+
 def cpu_baseline(stack, budget_s: float = 20.0) -> dict:
-    """Time the fp64 oracle (as it stands) on layer 0 of the same workload:
-    all seven matrices, all M rows, a prefix of each matrix's columns sized so
-    the run stays near budget_s."""
+    """Time the fp64 oracle (as it stands) on the same decode step: layers
+    chained through T exactly as the GPU walks them, every column of every
+    matrix, as many leading layers as fit in about budget_s of oracle time.
+    Generating the weights on the host is input plumbing and is not timed."""
     import numpy as np
     import oracle
     import synth
     from synth.stack import MATRIX_ORDER
-    M = stack.M
+    M, shp = stack.M, stack.shp
+
+    def T(v):
+        return oracle.f64_to_f16(oracle.standardize(v)).view(np.float16)
+
+    def rows(l, name):
+        N, K = shp[name]
+        return synth.q4k_rows(synth.weight_key(stack.seed, l, MATRIX_ORDER.index(name)), K, 0, N)
+
     x = synth.activations(stack.seed, M, stack.H)
-    # probe the rate on a small slice, then size the sample
-    W = stack.host_rows(0, "q", np.arange(64))
-    t0 = time.perf_counter()
-    oracle.gemm(W, x)
-    probe = max(time.perf_counter() - t0, 1e-4)
-    weights_per_s = 64 * stack.shp["q"][1] / probe
-    layer_weights = sum(N * K for N, K in stack.shp.values())
-    frac = min(1.0, budget_s * weights_per_s / layer_weights)
-    xs = {"q": x, "k": x, "v": x, "o": None, "gate": x, "up": x, "down": None}
-    total_bytes = 0
-    elapsed = 0.0
-    for name in MATRIX_ORDER:
-        N, K = stack.shp[name]
-        n = max(16, int(N * frac))
-        W = stack.host_rows(0, name, np.arange(n))
-        xin = xs[name] if xs[name] is not None else synth.activations(stack.seed + 1, M, K)
+    elapsed, done_bytes, layers = 0.0, 0, 0
+    while layers < stack.n_layers:
+        W = {n: rows(layers, n) for n in MATRIX_ORDER}
         t0 = time.perf_counter()
-        oracle.gemm(W, xin)
-        elapsed += time.perf_counter() - t0
-        total_bytes += W.nbytes
-    gbs = total_bytes / elapsed / 1e9
+        yq = oracle.gemm(W["q"], x)[0]
+        oracle.gemm(W["k"], x)
+        oracle.gemm(W["v"], x)
+        yo = oracle.gemm(W["o"], T(yq))[0]
+        xc = T(yo)
+        gu = oracle.gemm(W["gate"], xc)[0] * oracle.gemm(W["up"], xc)[0]
+        x = T(oracle.gemm(W["down"], T(gu))[0])
+        dt = time.perf_counter() - t0
+        elapsed += dt
+        done_bytes += sum(w.nbytes for w in W.values())
+        layers += 1
+        if elapsed + dt > budget_s:
+            break
+    gbs = done_bytes / elapsed / 1e9
     return {
         "value": round(gbs, 4),
         "unit": "GB/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": (f"layer 0, all 7 matrices, first {frac * 100:.1f}% of each matrix's columns, "
-                   f"M={M}: {total_bytes / 1e6:.1f} MB of Q4_K weights in {elapsed:.2f} s "
-                   f"(fp64 dequantize + naive matmul); row-tokens/s at this rate "
+        "sample": (f"the first {layers} of {stack.n_layers} layers of the same step, chained through "
+                   f"T, all columns of all 7 matrices, M={M}: {done_bytes / 1e9:.3f} GB of Q4_K "
+                   f"weights in {elapsed:.2f} s (fp64 dequantize + naive matmul, OpenMP over "
+                   f"columns); row-tokens/s at this rate "
                    f"{M * gbs * 1e9 / stack.weight_bytes:.4f}"),
     }
 
@@ -98,6 +149,8 @@ def main() -> int:
     ap.add_argument("--M", type=int, default=12)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 1 GiB copies (scale for the PMC byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -106,6 +159,9 @@ def main() -> int:
               "run it with --gpus 1 (multi-GPU runs are not part of this build).",
               file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        return copy_calibration(args.steps)
 
     import torch
     import bit_weight_streaming_amd as mk
@@ -135,34 +191,40 @@ def main() -> int:
         return 1
     log("warmup done")
 
+    # the library launches on the stream it is given: the current torch stream,
+    # so the events below are recorded on the launch stream itself
     stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    for a, b in ev:
+        a.record(stream)
         step()
-    e1.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     st = mk.step_status(ws)
     if st != 0:
         log(f"device status {st}: {mk.strerror(st)}")
         return 1
-    ms = e0.elapsed_time(e1) / args.steps
+    per_launch = [a.elapsed_time(b) for a, b in ev]
+    ms = ev[0][0].elapsed_time(ev[-1][1]) / args.steps      # whole timed region
+    t_launch = sum(per_launch) / len(per_launch) * 1e-3        # average launch duration
     t = ms * 1e-3
     ab = algorithmic_bytes(stack)
     gbs = stack.weight_bytes / t / 1e9
-    log(f"{args.steps} steps: {ms:.3f} ms/step (events), wall {wall / args.steps * 1e3:.3f} ms/step, "
-        f"{gbs:.1f} GB/s weights")
+    log(f"{args.steps} steps: {ms:.3f} ms/step (events), launch avg {t_launch * 1e3:.3f} ms "
+        f"(min {min(per_launch):.3f}, max {max(per_launch):.3f}), wall {wall / args.steps * 1e3:.3f} "
+        f"ms/step, {gbs:.1f} GB/s weights")
 
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(stack)
 
-    achieved = ab["total"] / t / 1e9
+    achieved = ab["total"] / t_launch / 1e9
+    traffic = measured_traffic(args.layers, args.M)
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -193,8 +255,10 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "algorithmic_bytes_per_launch": ab["total"],
+            "launch_ms": round(t_launch * 1e3, 4),
+            "kernel": "q4k_step_kernel (one launch = one decode step, all layers)",
         },
         "cpu_baseline": cpu,
     }

@@ -10,7 +10,7 @@ namespace mk {
 
 constexpr int STEP_WAVES = 8;
 constexpr int STEP_THREADS = 64 * STEP_WAVES;
-constexpr int STEP_PD = 8;       // weight records in flight per wave
+constexpr int STEP_PD = 4;       // weight records in flight per wave (more spills registers)
 constexpr int STEP_PD_PRE = 4;   // of which issued before a phase's input is ready
 constexpr int STEP_MAX_LAYERS = 128;
 constexpr int STAT_SLOTS = 64;   // spread of the row-statistic atomics

@@ -136,3 +136,30 @@ def test_step_rejects_bad_chain():
     with pytest.raises(mk.MkError) as e:
         mk.step(descs, stack.io, stack.x0, stack.x_out, ws[:16], 4)
     assert e.value.code == mk.MK_EWORKSPACE
+
+
+def test_second_step_on_new_input_reads_fresh_values():
+    """Two steps over the same buffers and workspace with different layer-0
+    inputs: every value of the second must follow from its own input (a
+    cached line left over from the first step would fail the checks)."""
+    stack = Stack(3, 12, SMALL, seed=21, device=DEV)
+    ws = run_step(stack)
+    stack.x0.copy_(torch.from_numpy(synth.activations(99, 12, stack.H)).to(DEV))
+    mk.step(stack.layer_descs(), stack.io, stack.x0, stack.x_out, ws, stack.M)
+    torch.cuda.synchronize()
+    assert mk.step_status(ws) == 0
+    check_stack(stack)
+    xo = stack.x_out.cpu().numpy()
+    check_transform(xo, stack.io[-1]["y"][6].cpu().numpy().astype(np.float64), "x_out")
+
+
+def test_full_stack_sampled_columns():
+    """The 64-layer stack at M=12 (12.27 GB of weights), as the benchmark runs
+    it; every matrix checked on a seeded subset of 4096 columns (all columns
+    of k and v) against its own binary16 input, every transform in full."""
+    stack = Stack(64, 12, seed=0, device=DEV)
+    run_step(stack, reps=2)
+    worst = check_stack(stack, ncols=4096, seed=1234)
+    xo = stack.x_out.cpu().numpy()
+    check_transform(xo, stack.io[-1]["y"][6].cpu().numpy().astype(np.float64), "x_out")
+    print(f"full stack worst |err|/S = {worst:.3e}")
