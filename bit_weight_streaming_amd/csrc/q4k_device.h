@@ -290,10 +290,21 @@ constexpr int TILE_REC = 16 * BLOCK_BYTES;
 // Lane l's three operands of one tile record: header of row l%16, quant bytes
 // [32g, 32g+16) and [32g+16, 32g+32) of that row (g = l/16). The three loads
 // of a wave read 256 (broadcast), 1024 and 1024 contiguous bytes.
+// Global-address-space views of pointers that come out of LDS tables (which
+// the compiler otherwise treats as generic and accesses with flat
+// instructions; flat operations also count against the LDS wait counter).
+template <class T>
+using gptr = __attribute__((address_space(1))) T*;
+template <class T>
+__device__ __forceinline__ gptr<T> to_global(T* p) {
+  return (gptr<T>)p;
+}
+
 __device__ __forceinline__ void load_rec(BlockRegs& r, const uint8_t* rec, int lane) {
-  r.h = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + (lane & 15) * 16));
-  r.q0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + 256 + lane * 16));
-  r.q1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + 1280 + lane * 16));
+  const gptr<const u32x4> g = to_global(reinterpret_cast<const u32x4*>(rec));
+  r.h = __builtin_nontemporal_load(g + (lane & 15));
+  r.q0 = __builtin_nontemporal_load(g + 16 + lane);
+  r.q1 = __builtin_nontemporal_load(g + 80 + lane);
 }
 
 // Nibble masks and the binary16 exponent pattern, materialised once in

@@ -24,6 +24,10 @@ constexpr int STEP_MAX_M = 16;   // rows the walk supports (one MFMA row tile)
 constexpr double STAT_SCALE_SUM = 268435456.0;
 constexpr double STAT_SCALE_SQ = 1048576.0;
 
+// Bit pattern of a slice partial that has not arrived yet: a signalling NaN,
+// which floating-point arithmetic never produces (its NaN results are quiet).
+constexpr uint32_t PART_EMPTY = 0x7FBADBADu;
+
 // One phase of a layer (the same for every layer).
 struct DevPhase {
   int K;           // input width
@@ -44,7 +48,9 @@ struct DevPhase {
   int cmax;        // most waves of one workgroup that share a tile
   int lds_contrib; // LDS offset of the per-tile wave contributions
   int lds_bytes;   // LDS this phase needs
-  size_t part_off; // workspace offset of the [sk][M][ncols] partial sums
+  size_t part_off; // workspace offset of the slice partials: one 1 KiB block
+                   // (16 x 16 fp32 in MFMA lane order) per (tile, slice, matrix)
+  unsigned part_bytes;
   size_t cons_off; // workspace offset of the consumer copies [layer][M][cons_ld]
   int cons_ld;     // row stride (floats) of a consumer copy
   size_t cons_layer_bytes;
@@ -68,8 +74,6 @@ struct StepParams {
   char* ws;              // workspace base
   size_t layers_off;     // DevLayer table
   size_t done_off;       // DONE_CTRS finished-tile counters
-  size_t ctr_off;        // [4][max_nt] per-tile slice-arrival counters
-  int max_nt;
   size_t stats_off;      // [n_layers][4][STAT_SLOTS][M][2] int64
   size_t status_off;     // int status word
   size_t lds_bytes;

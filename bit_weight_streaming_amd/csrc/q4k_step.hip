@@ -72,6 +72,25 @@ __device__ __forceinline__ long long ld_dev(const long long* p) {
   return __hip_atomic_load(const_cast<long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16-byte device-coherent accesses through a buffer resource (cache policy
+// sc1: the agent-scope coherence level, as for relaxed agent-scope atomics).
+// Offsets past the resource's size read as zero and drop writes.
+constexpr int kCoherent = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ floatx4 ld4_dev(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
+}
+__device__ __forceinline__ void st4_dev(__amdgpu_buffer_rsrc_t r, unsigned off, floatx4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCoherent);
+}
+
+__device__ __forceinline__ bool arrived(const floatx4& v) {
+  const u32x4 b = __builtin_bit_cast(u32x4, v);
+  return b.x != PART_EMPTY && b.y != PART_EMPTY && b.z != PART_EMPTY && b.w != PART_EMPTY;
+}
+
 __device__ __forceinline__ void set_status(const StepParams& P, int code) {
   int* status = reinterpret_cast<int*>(P.ws + P.status_off);
   int expect = 0;
@@ -91,11 +110,21 @@ struct Assign {
   int U;      // units = tw * nkb
 };
 
+// First workgroup of slice s: the G workgroups are spread over the slices in
+// proportion to their super-blocks, so a short last slice gets fewer of them
+// and every workgroup owns about the same number of (tile, block) units.
+__host__ __device__ inline int slice_start(int s, int sk, int nkb, int KB, int G) {
+  return s >= sk ? G : (int)((long long)G * s * nkb / KB);
+}
+
 __device__ __forceinline__ Assign assign(const DevPhase& ph, int w, int G) {
   Assign a;
-  a.s = w % ph.sk;
-  a.j = w / ph.sk;
-  a.gs = (G - a.s + ph.sk - 1) / ph.sk;
+  int s = 0;
+  while (s + 1 < ph.sk && slice_start(s + 1, ph.sk, ph.nkb, ph.KB, G) <= w) ++s;
+  const int first = slice_start(s, ph.sk, ph.nkb, ph.KB, G);
+  a.s = s;
+  a.j = w - first;
+  a.gs = slice_start(s + 1, ph.sk, ph.nkb, ph.KB, G) - first;
   a.t0 = (int)((long long)ph.nt * a.j / a.gs);
   a.tw = (int)((long long)ph.nt * (a.j + 1) / a.gs) - a.t0;
   a.kb0 = a.s * ph.nkb;
@@ -104,12 +133,26 @@ __device__ __forceinline__ Assign assign(const DevPhase& ph, int w, int G) {
   return a;
 }
 
-// First unit of wave v's range, and the wave whose range holds unit x.
-__device__ __forceinline__ int wave_begin(const Assign& a, int v) {
-  return (int)((long long)a.U * v / STEP_WAVES);
-}
+// First unit of wave v's range, and the wave whose range holds unit x (the
+// last wave whose range starts at or before x: waves with an empty range are
+// skipped). No divisions: both run in the per-tile and per-element loops.
+static_assert(STEP_WAVES == 8, "wave ranges are computed with a shift by 3");
+__device__ __forceinline__ int wave_begin(const Assign& a, int v) { return (a.U * v) >> 3; }
 __device__ __forceinline__ int wave_of_unit(const Assign& a, int x) {
-  return min(STEP_WAVES - 1, (int)(((long long)STEP_WAVES * (x + 1) - 1) / a.U));
+  int w = 0;
+#pragma unroll
+  for (int v = 1; v < STEP_WAVES; ++v) w += ((a.U * v) >> 3) <= x;
+  return w;
+}
+
+// The tiles this workgroup finishes: local tile i with (t0 + i) % sk == s,
+// i.e. i = fin_first + j * sk for j < fin_count.
+__device__ __forceinline__ int fin_first(const Assign& a, int sk) {
+  return ((a.s - a.t0) % sk + sk) % sk;
+}
+__device__ __forceinline__ int fin_count(const Assign& a, int sk) {
+  const int i0 = fin_first(a, sk);
+  return i0 < a.tw ? (a.tw - 1 - i0) / sk + 1 : 0;
 }
 
 __device__ __forceinline__ int seg_of(const DevPhase& ph, int tg) {
@@ -180,15 +223,19 @@ __device__ __forceinline__ void ring_fill(BlockRegs (&ring)[STEP_PD], Iter& it,
   }
 }
 
-// Stream the wave's units, multiply them against the staged activations and
-// leave each tile part in the LDS contribution slot (tile, wave - first wave
-// of the tile): per lane one floatx4 (rows 4*(lane/16)+r, column lane%16).
+// Stream the wave's units and multiply them against the staged activations.
+// A tile the wave computes alone goes straight to its slice partial block in
+// the workspace (one 16-byte store per lane, issued while the stream goes
+// on); a tile shared with other waves leaves its part in the LDS contribution
+// slot (tile, wave - first wave of the tile). Per lane one floatx4: rows
+// 4*(lane/16)+r, column lane%16.
 template <int NM>
 __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& it,
                                               const DevPhase& ph, WPtrs L,
                                               const Assign& a, int wave, int lane,
                                               const char* xa_lane, const char* xs_lane,
-                                              char* contrib, const UnpackConsts& k) {
+                                              char* contrib, __amdgpu_buffer_rsrc_t pr,
+                                              const UnpackConsts& k) {
   const int g = lane >> 4;
   const int ua = wave_begin(a, wave), ub = wave_begin(a, wave + 1);
   const int U = (ub - ua) * NM;  // records
@@ -201,11 +248,21 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
   int cu = ua;
   auto flush = [&]() {
     const int first = wave_of_unit(a, ctl * a.nkb);
-    char* slot = contrib + ((size_t)(ctl * ph.cmax + (wave - first)) * NM) * 1024 + lane * 16;
+    const int last = wave_of_unit(a, (ctl + 1) * a.nkb - 1);
+    if (first == last) {
+      const unsigned off = ((unsigned)((a.t0 + ctl) * ph.sk + a.s) * NM) * 1024u + lane * 16;
 #pragma unroll
-    for (int q = 0; q < NM; ++q) {
-      *reinterpret_cast<floatx4*>(slot + q * 1024) = acc[q];
-      acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < NM; ++q) {
+        st4_dev(pr, off + q * 1024u, acc[q]);
+        acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    } else {
+      char* slot = contrib + ((size_t)(ctl * ph.cmax + (wave - first)) * NM) * 1024 + lane * 16;
+#pragma unroll
+      for (int q = 0; q < NM; ++q) {
+        *reinterpret_cast<floatx4*>(slot + q * 1024) = acc[q];
+        acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
     }
   };
   auto consume = [&](int s) {
@@ -324,7 +381,8 @@ __device__ __forceinline__ void stage_slice(const void* src, int src_ld, int K, 
         h = u32x4{bit_cast_<uint32_t>(p0), bit_cast_<uint32_t>(p1), bit_cast_<uint32_t>(p2),
                   bit_cast_<uint32_t>(p3)};
       }
-      if (io_x && (ch % a.gs) == a.j) *reinterpret_cast<u32x4*>(io_x + (size_t)m * K + k) = h;
+      if (io_x && (ch % a.gs) == a.j)
+        *to_global(reinterpret_cast<u32x4*>(io_x + (size_t)m * K + k)) = h;
       u32x4 o;  // element order 0,2,1,3,4,6,5,7
       o.x = (h.x & 0xFFFFu) | (h.y << 16);
       o.y = (h.x >> 16) | (h.y & 0xFFFF0000u);
@@ -447,168 +505,200 @@ __device__ __forceinline__ bool wait_done(const StepParams& P, const DevPhase* P
   return *abort_s == 0;
 }
 
-// Finish the tiles whose last K slice this workgroup contributed: add the sk
-// partials in slice order, write the outputs, the consumer copy and the row
-// statistics. Elements (tile, m, column) are spread over all threads; each
-// group of 16 lanes holds the 16 columns of one (tile, m).
-__device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase& ph, int p, int l,
-                                            const DevLayer* L, const Assign& a,
-                                            const int* last_list, int nlast, int tid) {
-  const int M = P.M;
-  const float* part = reinterpret_cast<const float*>(P.ws + ph.part_off);
-  float* consb = reinterpret_cast<float*>(P.ws + ph.cons_off + (size_t)l * ph.cons_layer_bytes);
-  long long* stl = reinterpret_cast<long long*>(P.ws + P.stats_off) +
-                   (size_t)(l * 4 + p) * STAT_SLOTS * M * 2;
-  const int items = nlast * M * 16;
-  for (int base = 0; base < items; base += STEP_THREADS * kFixRound) {
-    float y[kFixRound][2];
-#pragma unroll
-    for (int i = 0; i < kFixRound; ++i) {
-      y[i][0] = y[i][1] = 0.f;
-      const int e = base + i * STEP_THREADS + tid;
-      if (e >= items) continue;
-      const int c = e & 15;
-      const int rest = e >> 4;
-      const int li = rest / M;
-      const int m = rest - li * M;
-      const int tg = a.t0 + last_list[li];
-      const int seg = seg_of(ph, tg);
-      const int cs = (tg - ph.seg_t0[seg]) * 16 + c;
-      if (cs >= ph.seg_n[seg]) continue;
-      const size_t col0 = (size_t)ph.seg_c0[seg] + cs;
-      for (int sl = 0; sl < ph.sk; ++sl)
-        y[i][0] += ld_dev(&part[((size_t)sl * M + m) * ph.ncols + col0]);
-      if (ph.nm == 2) {
-        const size_t col1 = col0 + ph.seg_n[seg];
-        for (int sl = 0; sl < ph.sk; ++sl)
-          y[i][1] += ld_dev(&part[((size_t)sl * M + m) * ph.ncols + col1]);
+// Finish the tiles this workgroup is the finisher of: add the sk slice
+// partials of each tile in slice order, write the outputs, the consumer copy
+// and the row statistics. One task per (tile, lane): the lane's 4 rows of one
+// column, loaded as one 16-byte piece per slice and matrix. A thread takes two
+// tasks at a time with all their loads in flight together. The statistics of
+// each (tile, row) are summed over the tile's 16 columns in fp32 (fixed
+// order), rounded to fixed point, added in LDS as integers and sent with one
+// atomic per (row, sum).
+// Reload a slice partial piece until every one of its words has been written
+// (no word still holds PART_EMPTY; each word is written once, so a piece with
+// no empty word is complete). Gives up when another workgroup has recorded a
+// failure or the wall-clock limit passes.
+__device__ __forceinline__ floatx4 await_piece(const StepParams& P, __amdgpu_buffer_rsrc_t pr,
+                                               unsigned off, floatx4 v, unsigned long long t0,
+                                               int* abort_s) {
+  int n = 0;
+  while (!arrived(v)) {
+    __builtin_amdgcn_s_sleep(1);
+    v = ld4_dev(pr, off);
+    if ((++n & 63) == 0) {
+      if (ld_dev(reinterpret_cast<const int*>(P.ws + P.status_off)) != 0) {
+        *abort_s = 1;
+        break;
+      }
+      if (wall_clock64() - t0 > kTimeoutTicks) {
+        set_status(P, MK_ETIMEOUT);
+        *abort_s = 1;
+        break;
       }
     }
+  }
+  return v;
+}
+
+template <int NM>
+__device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase& ph, int p,
+                                             const DevLayer* L, int tg, int ln, const floatx4* y,
+                                             float* consb, unsigned long long* wst) {
+  const int M = P.M;
+  const int seg = __builtin_amdgcn_readfirstlane(seg_of(ph, tg));  // uniform per wave
+  const int nseg = ph.seg_n[seg];
+  const int cs = (tg - ph.seg_t0[seg]) * 16 + (ln & 15);
+  const int g = ln >> 4;
+  const bool has_cons = (p != 0) || (seg == 0);
+  float* yp[NM];
 #pragma unroll
-    for (int i = 0; i < kFixRound; ++i) {
-      const int e0 = base + i * STEP_THREADS;
-      if (e0 >= items) break;  // uniform across the workgroup
-      const int e = e0 + tid;
-      const bool live = e < items;
-      const int c = e & 15;
-      const int rest = e >> 4;
-      const int li = live ? rest / M : 0;
-      const int m = live ? rest - li * M : 0;
-      const int tg = a.t0 + last_list[li];
-      const int seg = seg_of(ph, tg);
-      const int nseg = ph.seg_n[seg];
-      const int cs = (tg - ph.seg_t0[seg]) * 16 + c;
-      const bool valid = live && cs < nseg;
-      if (valid) {
-        L->y[ph.mat0 + seg][(size_t)m * nseg + cs] = y[i][0];
-        if (ph.nm == 2) L->y[ph.mat0 + seg + 1][(size_t)m * nseg + cs] = y[i][1];
-      }
-      const bool has_cons = live && ((p != 0) || (seg == 0));
-      const float cv = valid ? (ph.nm == 2 ? y[i][0] * y[i][1] : y[i][0]) : 0.f;
-      if (has_cons && valid) st_dev(&consb[(size_t)m * ph.cons_ld + cs], cv);
-      double s1 = cv, s2 = (double)cv * (double)cv;
+  for (int q = 0; q < NM; ++q) yp[q] = L->y[ph.mat0 + seg + q];
+  float s1[4], s2[4];
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        s1 += __shfl_xor(s1, off, 16);
-        s2 += __shfl_xor(s2, off, 16);
-      }
-      if (has_cons && c == 0) {
-        const double f1 = s1 * STAT_SCALE_SUM, f2 = s2 * STAT_SCALE_SQ;
-        long long* st = stl + ((size_t)(tg % STAT_SLOTS) * M + m) * 2;
-        if (!(fabs(f1) < 4.0e18) || !(f2 < 4.0e18)) {
-          set_status(P, MK_ERANGE);
-        } else {
-          __hip_atomic_fetch_add(st, (long long)llrint(f1), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_fetch_add(st + 1, (long long)llrint(f2), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-        }
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * g + r;
+    const bool valid = m < M && cs < nseg;
+    const float cv = valid ? (NM == 2 ? y[0][r] * y[1][r] : y[0][r]) : 0.f;
+    if (valid) {
+#pragma unroll
+      for (int q = 0; q < NM; ++q) to_global(yp[q])[(size_t)m * nseg + cs] = y[q][r];
+      if (has_cons) st_dev(&consb[(size_t)m * ph.cons_ld + cs], cv);
+    }
+    s1[r] = cv;
+    s2[r] = cv * cv;
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s1[r] += __shfl_xor(s1[r], off, 16);
+      s2[r] += __shfl_xor(s2[r], off, 16);
+    }
+  if (has_cons && (ln & 15) == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * g + r;
+      if (m >= M) break;
+      const double f1 = (double)s1[r] * STAT_SCALE_SUM, f2 = (double)s2[r] * STAT_SCALE_SQ;
+      if (!(fabs(f1) < 4.0e18) || !(f2 < 4.0e18)) {
+        set_status(P, MK_ERANGE);
+      } else {
+        atomicAdd(&wst[2 * m], (unsigned long long)llrint(f1));
+        atomicAdd(&wst[2 * m + 1], (unsigned long long)llrint(f2));
       }
     }
   }
 }
 
-// End of a phase in one workgroup: add the wave parts of each tile, publish
-// the slice partials and count them in; then, for the tiles this workgroup
+template <int NM>
+__device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase& ph, int p, int l,
+                                            const DevLayer* L, const Assign& a, int nfin,
+                                            unsigned long long* wst, int* abort_s, int tid) {
+  const int M = P.M;
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
+  float* consb = reinterpret_cast<float*>(P.ws + ph.cons_off + (size_t)l * ph.cons_layer_bytes);
+  long long* stl = reinterpret_cast<long long*>(P.ws + P.stats_off) +
+                   (size_t)(l * 4 + p) * STAT_SLOTS * M * 2;
+  const int tasks = nfin * 64;
+  const floatx4 empty = __builtin_bit_cast(floatx4, u32x4{PART_EMPTY, PART_EMPTY, PART_EMPTY,
+                                                          PART_EMPTY});
+  const unsigned long long t0 = wall_clock64();
+  for (int t = tid; t < tasks; t += 2 * STEP_THREADS) {  // uniform per wave
+    const bool two = t + STEP_THREADS < tasks;            // uniform per wave
+    const int ln = t & 63;
+    const int f0 = a.t0 + fin_first(a, ph.sk);
+    const int tg0 = f0 + (t >> 6) * ph.sk;
+    const int tg1 = two ? f0 + ((t + STEP_THREADS) >> 6) * ph.sk : tg0;
+    const unsigned base0 = (unsigned)tg0 * ph.sk * NM * 1024u + ln * 16;
+    const unsigned base1 = (unsigned)tg1 * ph.sk * NM * 1024u + ln * 16;
+    floatx4 y0[NM], y1[NM];
+#pragma unroll
+    for (int q = 0; q < NM; ++q) y0[q] = y1[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ph.sk; s0 += 4) {
+      floatx4 v0[4][NM], v1[4][NM];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < NM; ++q)
+          if (s0 + i < ph.sk) {
+            v0[i][q] = ld4_dev(pr, base0 + ((s0 + i) * NM + q) * 1024u);
+            if (two) v1[i][q] = ld4_dev(pr, base1 + ((s0 + i) * NM + q) * 1024u);
+          }
+      // wait for late slices, add in slice order, mark the pieces empty again
+      // for the same phase of the next layer
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < NM; ++q)
+          if (s0 + i < ph.sk) {
+            const unsigned o = ((s0 + i) * NM + q) * 1024u;
+            y0[q] += await_piece(P, pr, base0 + o, v0[i][q], t0, abort_s);
+            st4_dev(pr, base0 + o, empty);
+            if (two) {
+              y1[q] += await_piece(P, pr, base1 + o, v1[i][q], t0, abort_s);
+              st4_dev(pr, base1 + o, empty);
+            }
+          }
+    }
+    fixup_finish<NM>(P, ph, p, L, tg0, ln, y0, consb, wst);
+    if (two) fixup_finish<NM>(P, ph, p, L, tg1, ln, y1, consb, wst);
+  }
+  __syncthreads();
+  if (tid < 2 * M) {
+    const long long v = (long long)wst[tid];
+    if (v != 0)
+      __hip_atomic_fetch_add(stl + (size_t)(blockIdx.x % STAT_SLOTS) * M * 2 + tid, v,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// End of a phase in one workgroup: add the wave parts of each tile shared
+// by several waves, publish those slice partials and count every tile in; then, for the tiles this workgroup
 // finishes (tile t is finished by the workgroup of slice t % sk), wait until
 // every slice has arrived, add the partials in slice order, and count the
 // tiles as finished. Spreading the finishing over the slices keeps every
 // workgroup's share of it equal.
+template <int NM>
 __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhase& ph, int p,
                                               int l, const DevLayer* L, const Assign& a,
-                                              const char* contrib, int* fin_list, int* nfin_s,
-                                              int* abort_s, int tid) {
-  const int M = P.M;
-  float* part = reinterpret_cast<float*>(P.ws + ph.part_off);
-  const int entries = a.tw * ph.nm * 64;
-  for (int e = tid; e < entries; e += STEP_THREADS) {
-    const int slot = e >> 6, ln = e & 63;
-    const int tl = slot / ph.nm, q = slot - tl * ph.nm;
+                                              const char* contrib, int* abort_s,
+                                              unsigned long long* wst, int tid) {
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
+  if (tid < 2 * STEP_MAX_M) wst[tid] = 0ull;
+  // Only a tile holding the start of some wave's range (other than at the
+  // tile's first unit) is shared; items (boundary v, matrix, lane), each
+  // shared tile taken at the first boundary inside it.
+  const int items = (STEP_WAVES - 1) * NM * 64;
+  for (int e = tid; e < items; e += STEP_THREADS) {
+    const int vb = 1 + (e >> 6) / NM, q = (e >> 6) % NM, ln = e & 63;
+    const int u = wave_begin(a, vb);
+    if (u >= a.U || u % a.nkb == 0) continue;
+    const int tl = u / a.nkb;
+    const int up = wave_begin(a, vb - 1);
+    if (vb > 1 && up % a.nkb != 0 && up / a.nkb == tl) continue;  // taken at boundary vb - 1
     const int tg = a.t0 + tl;
-    const int seg = seg_of(ph, tg);
-    const int cs = (tg - ph.seg_t0[seg]) * 16 + (ln & 15);
-    if (cs >= ph.seg_n[seg]) continue;
     const int w0 = wave_of_unit(a, tl * a.nkb);
     const int w1 = wave_of_unit(a, (tl + 1) * a.nkb - 1);
     floatx4 v = *reinterpret_cast<const floatx4*>(
-        contrib + ((size_t)(tl * ph.cmax) * ph.nm + q) * 1024 + ln * 16);
+        contrib + ((size_t)(tl * ph.cmax) * NM + q) * 1024 + ln * 16);
     for (int kk = 1; kk <= w1 - w0; ++kk) {
       // waves with an empty range (fewer units than waves) wrote nothing
       if (wave_begin(a, w0 + kk) == wave_begin(a, w0 + kk + 1)) continue;
       const floatx4 u = *reinterpret_cast<const floatx4*>(
-          contrib + ((size_t)(tl * ph.cmax + kk) * ph.nm + q) * 1024 + ln * 16);
+          contrib + ((size_t)(tl * ph.cmax + kk) * NM + q) * 1024 + ln * 16);
       v += u;
     }
-    const size_t pc = (size_t)ph.seg_c0[seg] + (size_t)q * ph.seg_n[seg] + cs;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * (ln >> 4) + r;
-      if (m < M) st_dev(&part[((size_t)a.s * M + m) * ph.ncols + pc], v[r]);
-    }
+    st4_dev(pr, ((unsigned)(tg * ph.sk + a.s) * NM + q) * 1024u + ln * 16, v);
   }
+  if (tid == 0) *abort_s = 0;
+  __syncthreads();
+  const int nfin = fin_count(a, ph.sk);
+  fixup_tiles<NM>(P, ph, p, l, L, a, nfin, wst, abort_s, tid);
   wait_vm0();
-  __syncthreads();
-  unsigned* ctr = reinterpret_cast<unsigned*>(P.ws + P.ctr_off) + (size_t)p * P.max_nt;
-  if (tid < a.tw)
-    __hip_atomic_fetch_add(&ctr[a.t0 + tid], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (tid == 0) {
-    int n = 0;
-    for (int i = 0; i < a.tw; ++i)
-      if ((a.t0 + i) % ph.sk == a.s) fin_list[n++] = i;
-    *nfin_s = n;
-    *abort_s = 0;
-  }
-  __syncthreads();
-  const int nfin = *nfin_s;
-  if (tid < nfin) {
-    const unsigned target = (unsigned)(ph.sk * (l + 1));
-    const unsigned* c = &ctr[a.t0 + fin_list[tid]];
-    const int* status = reinterpret_cast<const int*>(P.ws + P.status_off);
-    const unsigned long long t0 = wall_clock64();
-    int n = 0;
-    while (ld_dev(c) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if ((++n & 63) == 0) {
-        if (ld_dev(status) != 0) {
-          *abort_s = 1;
-          break;
-        }
-        if (wall_clock64() - t0 > kTimeoutTicks) {
-          set_status(P, MK_ETIMEOUT);
-          *abort_s = 1;
-          break;
-        }
-      }
-    }
-  }
   __syncthreads();
   if (*abort_s) return false;
-  fixup_tiles(P, ph, p, l, L, a, fin_list, nfin, tid);
-  wait_vm0();
-  __syncthreads();
   if (tid < nfin) {
     unsigned* done = reinterpret_cast<unsigned*>(P.ws + P.done_off);
-    const int tg = a.t0 + fin_list[tid];
+    const int tg = a.t0 + fin_first(a, ph.sk) + tid * ph.sk;
     __hip_atomic_fetch_add(done + (size_t)(tg % DONE_CTRS) * CTR_STRIDE, 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -620,11 +710,11 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
 __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ DevPhase PH[4];
-  __shared__ const uint8_t* wtab[STEP_MAX_LAYERS][7];
+  __shared__ DevLayer ltab[STEP_MAX_LAYERS];  // every layer's pointers, read from LDS
   __shared__ float mu_s[STEP_MAX_M];
   __shared__ float inv_s[STEP_MAX_M];
   __shared__ unsigned long long tot_s[2 * STEP_MAX_M];
-  __shared__ int abort_s, nfin_s;
+  __shared__ int abort_s;
   const int M = P.M;
   const int w = blockIdx.x;
   const int tid = threadIdx.x;
@@ -635,7 +725,10 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(P.ws + P.phases_off);
     uint32_t* dst = reinterpret_cast<uint32_t*>(PH);
     for (int i = tid; i < (int)(sizeof(PH) / 4); i += STEP_THREADS) dst[i] = src[i];
-    for (int i = tid; i < P.n_layers * 7; i += STEP_THREADS) wtab[i / 7][i % 7] = layers[i / 7].w[i % 7];
+    const uint32_t* lsrc = reinterpret_cast<const uint32_t*>(layers);
+    uint32_t* ldst = reinterpret_cast<uint32_t*>(ltab);
+    const int nw = P.n_layers * (int)(sizeof(DevLayer) / 4);
+    for (int i = tid; i < nw; i += STEP_THREADS) ldst[i] = lsrc[i];
   }
   __syncthreads();
   const UnpackConsts k = unpack_consts();
@@ -646,17 +739,16 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   BlockRegs ring[STEP_PD];
   Iter it;
   Assign a = assign(PH[0], w, P.G);
-  iter_init(it, PH[0], wtab[0], a, wave);
-  ring_fill(ring, it, PH[0], wtab[0], a, lane, 0, STEP_PD_PRE);
+  iter_init(it, PH[0], ltab[0].w, a, wave);
+  ring_fill(ring, it, PH[0], ltab[0].w, a, lane, 0, STEP_PD_PRE);
 
   for (int l = 0; l < P.n_layers; ++l) {
-    const DevLayer* L = &layers[l];
+    const DevLayer* L = &ltab[l];
     for (int p = 0; p < 4; ++p) {
       const DevPhase& ph = PH[p];
       char* x_lds = smem;
       char* xs_lds = x_lds + (size_t)M * ph.x_stride;
       char* contrib = smem + ph.lds_contrib;
-      int* fin_list = reinterpret_cast<int*>(contrib + (size_t)ph.tw_max * ph.cmax * ph.nm * 1024);
       // ---- stage this phase's input slice, then the rest of the first
       //      weight records
       if (l == 0 && p == 0) {
@@ -672,7 +764,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
         stage_slice<false>(cons, src.cons_ld, ph.K, M, a, st, src.stat_n, tot_s, mu_s, inv_s,
                            x_lds, ph.x_stride, L->x[p], tid);
       }
-      ring_fill(ring, it, ph, wtab[l], a, lane, STEP_PD_PRE, STEP_PD);
+      ring_fill(ring, it, ph, ltab[l].w, a, lane, STEP_PD_PRE, STEP_PD);
       __syncthreads();
       stage_xsum(M, a.nkb, ph.nkb, x_lds, ph.x_stride, xs_lds, tid);
       __syncthreads();
@@ -680,20 +772,25 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       // ---- stream the weights
       const char* xa_lane = x_lds + (size_t)arow * ph.x_stride + g * 128;
       const char* xs_lane = xs_lds + (size_t)arow * ph.nkb * XSUM_BYTES_PER_BLOCK + 8 * g;
+      const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
       if (ph.nm == 2)
-        phase_compute<2>(ring, it, ph, wtab[l], a, wave, lane, xa_lane, xs_lane, contrib, k);
+        phase_compute<2>(ring, it, ph, ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, pr, k);
       else
-        phase_compute<1>(ring, it, ph, wtab[l], a, wave, lane, xa_lane, xs_lane, contrib, k);
+        phase_compute<1>(ring, it, ph, ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, pr, k);
       __syncthreads();
 
       // ---- finish tiles, start the next phase's weight stream, wait until
       //      every tile of this phase is finished
-      if (!phase_outputs(P, ph, p, l, L, a, contrib, fin_list, &nfin_s, &abort_s, tid)) return;
+      const bool ok = ph.nm == 2 ? phase_outputs<2>(P, ph, p, l, L, a, contrib, &abort_s, tot_s,
+                                                    tid)
+                                 : phase_outputs<1>(P, ph, p, l, L, a, contrib, &abort_s, tot_s,
+                                                    tid);
+      if (!ok) return;
       const int ln = p < 3 ? l : l + 1, pn = p < 3 ? p + 1 : 0;
       if (ln < P.n_layers) {
         a = assign(PH[pn], w, P.G);
-        iter_init(it, PH[pn], wtab[ln], a, wave);
-        ring_fill(ring, it, PH[pn], wtab[ln], a, lane, 0, STEP_PD_PRE);
+        iter_init(it, PH[pn], ltab[ln].w, a, wave);
+        ring_fill(ring, it, PH[pn], ltab[ln].w, a, lane, 0, STEP_PD_PRE);
       }
       if (!wait_done(P, PH, l, p, &abort_s)) return;
     }
@@ -712,16 +809,21 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       const int m = i / nc, cc = c0 + (i - m * nc);
       const float y = cons[(size_t)m * src.cons_ld + cc];
       const _Float16 h = (_Float16)((y - mu_s[m]) * inv_s[m]);
-      P.x_out[(size_t)m * P.H + cc] = bit_cast_<uint16_t>(h);
+      to_global(P.x_out)[(size_t)m * P.H + cc] = bit_cast_<uint16_t>(h);
     }
   }
 }
 
-// Zero the counters, status word and statistics.
-__global__ void __launch_bounds__(256) q4k_step_clear(uint32_t* p, size_t n) {
+// Zero the counters, status word and statistics, and mark every slice
+// partial piece empty.
+__global__ void __launch_bounds__(256) q4k_step_clear(uint32_t* p, size_t n, uint32_t* part,
+                                                      size_t npart) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0u;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < npart;
+       i += (size_t)gridDim.x * blockDim.x)
+    part[i] = PART_EMPTY;
 }
 
 }  // namespace mk
@@ -733,7 +835,7 @@ namespace {
 
 constexpr int kMaxG = 1024;                    // most workgroups (CUs) planned for
 constexpr size_t kLdsLimit = 160 * 1024;
-constexpr size_t kStaticLds = 4 * sizeof(DevPhase) + STEP_MAX_LAYERS * 7 * sizeof(void*) +
+constexpr size_t kStaticLds = 4 * sizeof(DevPhase) + STEP_MAX_LAYERS * sizeof(DevLayer) +
                               2 * STEP_MAX_M * sizeof(float) +
                               2 * STEP_MAX_M * sizeof(unsigned long long) + 64;
 
@@ -743,15 +845,19 @@ int tiles_of(int n) { return (n + 15) / 16; }
 
 struct StepPlan {
   DevPhase ph[4];
-  size_t phases_off, layers_off, done_off, status_off, ctr_off, stats_off, sync_end;
-  int max_nt;
+  size_t phases_off, layers_off, done_off, status_off, stats_off, sync_end;
+  size_t part_begin, part_end;  // slice partial blocks of all phases
   size_t total;
+  bool ok = true;  // false: some K slice would get no workgroup
 };
 
 // Host mirror of the device work split (assign / wave_of_unit in the kernel).
 void host_assign(const DevPhase& ph, int w, int G, int* t0, int* tw, int* nkb) {
-  const int s = w % ph.sk, j = w / ph.sk;
-  const int gs = (G - s + ph.sk - 1) / ph.sk;
+  int s = 0;
+  while (s + 1 < ph.sk && slice_start(s + 1, ph.sk, ph.nkb, ph.KB, G) <= w) ++s;
+  const int first = slice_start(s, ph.sk, ph.nkb, ph.KB, G);
+  const int j = w - first;
+  const int gs = slice_start(s + 1, ph.sk, ph.nkb, ph.KB, G) - first;
   *t0 = (int)((long long)ph.nt * j / gs);
   *tw = (int)((long long)ph.nt * (j + 1) / gs) - *t0;
   const int kb0 = s * ph.nkb;
@@ -759,8 +865,9 @@ void host_assign(const DevPhase& ph, int w, int G, int* t0, int* tw, int* nkb) {
 }
 
 int host_wave_of_unit(int U, int x) {
-  int w = (int)(((long long)STEP_WAVES * (x + 1) - 1) / U);
-  return w < STEP_WAVES - 1 ? w : STEP_WAVES - 1;
+  int w = 0;
+  for (int v = 1; v < STEP_WAVES; ++v) w += ((U * v) >> 3) <= x;
+  return w;
 }
 
 // Fill the phase table for the shapes of layer 0; sk is chosen so that one
@@ -769,6 +876,7 @@ int host_wave_of_unit(int U, int x) {
 void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& sp) {
   const mk_q4k_mat* mats[7] = {&L0.q, &L0.k, &L0.v, &L0.o, &L0.gate, &L0.up, &L0.down};
   memset(&sp, 0, sizeof(sp));
+  sp.ok = true;
   for (int p = 0; p < 4; ++p) {
     DevPhase& ph = sp.ph[p];
     int first, nseg;
@@ -803,12 +911,14 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
     // columns the statistics of this phase's consumer copy run over
     ph.stat_n = ph.seg_n[0];
     // K slices: at least 4, more while one slice of activations exceeds 96 KiB
+    // of LDS or takes more than one round of loads to stage
     int sk = 4 < ph.KB ? 4 : ph.KB;
     for (;;) {
       int nkb = (ph.KB + sk - 1) / sk;
       size_t xb = (size_t)M * (nkb * X_BYTES_PER_BLOCK + X_ROW_PAD) +
                   (size_t)M * nkb * XSUM_BYTES_PER_BLOCK;
-      if (xb <= 96 * 1024 || nkb == 1) {
+      const bool one_round = M * nkb * 32 <= STEP_THREADS * kStageRound;
+      if ((xb <= 96 * 1024 && one_round) || nkb == 1) {
         ph.sk = (ph.KB + nkb - 1) / nkb;
         ph.nkb = nkb;
         break;
@@ -816,6 +926,9 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
       ++sk;
     }
     ph.x_stride = ph.nkb * X_BYTES_PER_BLOCK + X_ROW_PAD;
+    for (int q = 0; q < ph.sk; ++q)
+      if (slice_start(q + 1, ph.sk, ph.nkb, ph.KB, G) <= slice_start(q, ph.sk, ph.nkb, ph.KB, G))
+        sp.ok = false;
     ph.tw_max = 0;
     ph.cmax = 1;
     for (int w = 0; w < G; ++w) {
@@ -833,8 +946,7 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
       const size_t xb = (size_t)M * ph.x_stride + (size_t)M * ph.nkb * XSUM_BYTES_PER_BLOCK;
       const size_t c0 = (xb + 15) & ~(size_t)15;
       ph.lds_contrib = (int)c0;
-      ph.lds_bytes = (int)(c0 + (size_t)ph.tw_max * ph.cmax * ph.nm * 1024 +
-                           2 * (size_t)ph.tw_max * sizeof(int));
+      ph.lds_bytes = (int)(c0 + (size_t)ph.tw_max * ph.cmax * ph.nm * 1024);
     }
     ph.cons_ld = ((ph.stat_n + 63) / 64) * 64;
     ph.cons_layer_bytes = align256((size_t)M * ph.cons_ld * sizeof(float));
@@ -845,10 +957,6 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
   off += align256((size_t)DONE_CTRS * CTR_STRIDE * sizeof(unsigned));
   sp.status_off = off;
   off += 256;
-  sp.max_nt = 0;
-  for (int p = 0; p < 4; ++p) sp.max_nt = sp.ph[p].nt > sp.max_nt ? sp.ph[p].nt : sp.max_nt;
-  sp.ctr_off = off;
-  off += align256((size_t)4 * sp.max_nt * sizeof(unsigned));
   sp.stats_off = off;
   off += align256((size_t)n_layers * 4 * STAT_SLOTS * M * 2 * sizeof(long long));
   sp.sync_end = off;
@@ -856,10 +964,14 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
   off += align256(4 * sizeof(DevPhase));
   sp.layers_off = off;
   off += align256((size_t)n_layers * sizeof(DevLayer));
+  sp.part_begin = off;
   for (int p = 0; p < 4; ++p) {
     sp.ph[p].part_off = off;
-    off += align256((size_t)sp.ph[p].sk * M * sp.ph[p].ncols * sizeof(float));
+    const size_t pb = (size_t)sp.ph[p].nt * sp.ph[p].sk * sp.ph[p].nm * 1024;
+    sp.ph[p].part_bytes = (unsigned)pb;
+    off += align256(pb);
   }
+  sp.part_end = off;
   for (int p = 0; p < 4; ++p) {
     sp.ph[p].cons_off = off;
     off += (size_t)n_layers * sp.ph[p].cons_layer_bytes;
@@ -924,7 +1036,7 @@ size_t mk_q4k_step_workspace_bytes(const mk_q4k_layer* layer0, int n_layers, int
   if (mk::check_step_shapes(layer0, 1, M) != MK_OK || n_layers < 1) return 0;
   mk::StepPlan sp;
   mk::plan_phases(*layer0, n_layers, M, mk::kMaxG, sp);
-  return sp.total;
+  return sp.ok ? sp.total : 0;
 }
 
 int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_layers, int M,
@@ -953,9 +1065,13 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
   const int G = cus < kMaxG ? cus : kMaxG;
   StepPlan sp;
   plan_phases(layers[0], n_layers, M, G, sp);
+  if (!sp.ok) return MK_EINVAL;
   if (ws_bytes < sp.total) return MK_EWORKSPACE;
-  for (int p = 0; p < 4; ++p)
+  for (int p = 0; p < 4; ++p) {
     if (sp.ph[p].sk > G) return MK_EINVAL;
+    // partial blocks are addressed with 32-bit buffer offsets
+    if ((size_t)sp.ph[p].nt * sp.ph[p].sk * sp.ph[p].nm * 1024 >= (1ull << 32)) return MK_EINVAL;
+  }
   const size_t lds = lds_bytes(sp, M);
   if (lds + kStaticLds > kLdsLimit) return MK_EINVAL;
   hipError_t e = hipFuncSetAttribute((const void*)q4k_step_kernel,
@@ -1003,7 +1119,9 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
   // clear flags, status, counters and statistics
   const size_t nclear = sp.sync_end / sizeof(uint32_t);
   hipLaunchKernelGGL(q4k_step_clear, dim3(256), dim3(256), 0, st,
-                     reinterpret_cast<uint32_t*>(ws), nclear);
+                     reinterpret_cast<uint32_t*>(ws), nclear,
+                     reinterpret_cast<uint32_t*>(ws + sp.part_begin),
+                     (sp.part_end - sp.part_begin) / sizeof(uint32_t));
   e = hipGetLastError();
   if (e != hipSuccess) return MK_EHIP;
 
@@ -1019,8 +1137,6 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
   P.ws = ws;
   P.layers_off = sp.layers_off;
   P.done_off = sp.done_off;
-  P.ctr_off = sp.ctr_off;
-  P.max_nt = sp.max_nt;
   P.stats_off = sp.stats_off;
   P.status_off = sp.status_off;
   P.lds_bytes = lds;
