@@ -90,6 +90,76 @@ def copy_calibration(steps: int) -> int:
     return 0
 
 
+# Single-matrix GEMM configurations (mk_q4k_gemm on the plain row layout):
+# (label, M, N, K). Each weight matrix is 50 MB, inside the 256 MB Infinity
+# Cache, so timed launches rotate over GEMM_COPIES independent copies.
+GEMM_CONFIGS = (
+    ("tiny K=1024 N=256", 1, 256, 1024),
+    ("gate/up K=5120 N=17408", 12, 17408, 5120),
+    ("down K=17408 N=5120", 1, 5120, 17408),
+    ("down K=17408 N=5120", 4, 5120, 17408),
+    ("down K=17408 N=5120", 8, 5120, 17408),
+    ("down K=17408 N=5120", 12, 5120, 17408),
+    ("down K=17408 N=5120", 16, 5120, 17408),
+    ("tiny K=1024 N=256", 64, 256, 1024),
+    ("gate/up K=5120 N=17408", 64, 17408, 5120),
+)
+GEMM_COPIES = 12
+FP16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def gemm_bench(seed: int, reps: int = 60) -> list:
+    """Time the single-matrix GEMM on each configuration, on the plain row
+    layout (mk_q4k_gemm) and on the tile-record form (mk_q4k_gemm_tiled): HIP
+    events around `reps` back-to-back launches cycling over GEMM_COPIES weight
+    copies (>= 600 MB for the 50 MB matrices), after warm-up launches."""
+    import torch
+    import bit_weight_streaming_amd as mk
+    import synth
+    out = []
+    cache = {}
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        for i in range(n + 2):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    for label, M, N, K in GEMM_CONFIGS:
+        if (N, K) not in cache:
+            w = torch.from_numpy(synth.q4k_matrix(synth.key(seed, 7, N, K), N, K))
+            copies = GEMM_COPIES if N * K >= 1 << 24 else 1
+            rows = [w.to("cuda:0") for _ in range(copies)]
+            cache[(N, K)] = (rows, [mk.repack(r, N, K) for r in rows])
+        rows, tiles = cache[(N, K)]
+        X = torch.from_numpy(synth.activations(seed, M, K)).to("cuda:0")
+        Y = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+        wbytes = N * (K // 256) * 144
+        alg = wbytes + M * K * 2 + M * N * 4
+        line = {"config": label, "M": M, "weight_copies": len(rows)}
+        for name, fn in (("rows", lambda i: mk.gemm(rows[i % len(rows)], X, out=Y)),
+                         ("tiles", lambda i: mk.gemm_tiled(tiles[i % len(tiles)], X, N, out=Y))):
+            t = timed(fn, len(rows))
+            gbs = wbytes / t / 1e9
+            line[name] = {
+                "us": round(t * 1e6, 2), "weight_GBps": round(gbs, 1),
+                "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                "roofline_frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
+                "mfma_util": round(2.0 * M * N * K / t / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
+                "row_tokens_per_s": round(M / t, 1),
+            }
+            log(f"gemm {name:5s} {label} M={M}: {t * 1e6:.2f} us, {gbs:.1f} GB/s")
+        out.append(line)
+    return out
+
+
 def cpu_baseline(stack, budget_s: float = 20.0) -> dict:
     """Time the fp64 oracle (as it stands) on the same decode step: layers
     chained through T exactly as the GPU walks them, every column of every
@@ -149,6 +219,7 @@ def main() -> int:
     ap.add_argument("--M", type=int, default=12)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-gemm", action="store_true", help="skip the single-matrix GEMM lines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB copies (scale for the PMC byte counters)")
     args = ap.parse_args()
@@ -218,6 +289,10 @@ def main() -> int:
         f"(min {min(per_launch):.3f}, max {max(per_launch):.3f}), wall {wall / args.steps * 1e3:.3f} "
         f"ms/step, {gbs:.1f} GB/s weights")
 
+    gemm = None
+    if not args.no_gemm:
+        gemm = gemm_bench(args.seed)
+
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample")
@@ -261,6 +336,7 @@ def main() -> int:
             "kernel": "q4k_step_kernel (one launch = one decode step, all layers)",
         },
         "cpu_baseline": cpu,
+        "gemm": gemm,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -101,6 +101,8 @@ def lib():
         L.mk_q4k_tiles_bytes.argtypes = [i, i]
         L.mk_q4k_repack.restype = i
         L.mk_q4k_repack.argtypes = [vp, vp, i, i, vp]
+        L.mk_q4k_gemm_tiled.restype = i
+        L.mk_q4k_gemm_tiled.argtypes = [vp, vp, vp, i, i, i, vp]
         if hasattr(L, "mk_q4k_step"):
             L.mk_q4k_step_workspace_bytes.restype = sz
             L.mk_q4k_step_workspace_bytes.argtypes = [ctypes.POINTER(_Layer), i, i]
@@ -140,7 +142,9 @@ def _ptr(t) -> int:
 
 def gemm(W, X, out=None, stream=None, workspace=None):
     """Y = X * W^T. W: uint8 [N, K/256*144] (or flat), X: float16 [M, K], both on
-    the GPU; returns float32 [M, N] (written into `out` if given)."""
+    the GPU; returns float32 [M, N] (written into `out` if given). A
+    `workspace` (uint8 device tensor of gemm_workspace_bytes) must be
+    zero-filled before its first use; each call leaves it zero-filled."""
     import torch
     if X.dim() != 2 or X.dtype != torch.float16:
         raise MkError(MK_EINVAL, "X must be a 2-D float16 tensor")
@@ -162,6 +166,23 @@ def gemm(W, X, out=None, stream=None, workspace=None):
         rc = lib().mk_q4k_gemm_ws(_ptr(W), _ptr(X), _ptr(out), M, N, K, _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc)
+    return out
+
+
+def gemm_tiled(Wt, X, N: int, out=None, stream=None):
+    """Y = X * W^T with W in the tile-record form (repack()); N columns."""
+    import torch
+    if X.dim() != 2 or X.dtype != torch.float16 or not X.is_contiguous():
+        raise MkError(MK_EINVAL, "X must be a contiguous 2-D float16 tensor")
+    M, K = X.shape
+    nbytes = tiles_bytes(N, K)
+    if nbytes == 0 or Wt.dtype != torch.uint8 or Wt.numel() < nbytes or not Wt.is_contiguous():
+        raise MkError(MK_EINVAL, "Wt must be the contiguous tile-record form of an N x K matrix")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    elif out.shape != (M, N) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise MkError(MK_EINVAL, "out must be a contiguous float32 [M, N] tensor")
+    _check(lib().mk_q4k_gemm_tiled(_ptr(Wt), _ptr(X), _ptr(out), M, N, K, _stream(stream)))
     return out
 
 

@@ -50,7 +50,8 @@ int current_device(int* dev_out) {
   return MK_OK;
 }
 
-int check_gemm_args(const void* W, const uint16_t* X, const float* Y, int M, int N, int K) {
+int check_gemm_args(const void* W, const uint16_t* X, const float* Y, int M, int N, int K,
+                    bool tiled) {
   if (!W || !X || !Y) return MK_EINVAL;
   if (M < 1 || M > MK_Q4K_MAX_M || N < 1 || K < MK_Q4K_QK || K % MK_Q4K_QK) return MK_EINVAL;
   if ((long long)N * (K / MK_Q4K_QK) > (1LL << 40)) return MK_EINVAL;
@@ -59,7 +60,8 @@ int check_gemm_args(const void* W, const uint16_t* X, const float* Y, int M, int
   const char* y0 = reinterpret_cast<const char*>(Y);
   const char* y1 = y0 + (size_t)M * N * sizeof(float);
   const char* w0 = static_cast<const char*>(W);
-  const char* w1 = w0 + (size_t)N * (K / MK_Q4K_QK) * MK_Q4K_BLOCK_BYTES;
+  const char* w1 = w0 + (tiled ? (size_t)((N + 15) / 16) * (K / MK_Q4K_QK) * 16 * MK_Q4K_BLOCK_BYTES
+                               : (size_t)N * (K / MK_Q4K_QK) * MK_Q4K_BLOCK_BYTES);
   const char* x0 = reinterpret_cast<const char*>(X);
   const char* x1 = x0 + (size_t)M * K * sizeof(uint16_t);
   if (y0 < w1 && w0 < y1) return MK_EINVAL;
@@ -77,6 +79,66 @@ int current_gfx950(int* cus) {
   return rc;
 }
 }  // namespace mk
+
+namespace {
+
+// CU count assumed for workspace sizing when no gfx950 device is current.
+constexpr int kDefaultCus = 256;
+
+// Library-owned workspace of the current device with at least `bytes` bytes,
+// zero-filled when (re)allocated; the GEMM leaves it zeroed after every call.
+int owned_workspace(int dev, size_t bytes, void** out) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  OwnedWs& o = g_ws[dev];
+  if (o.bytes < bytes) {
+    if (o.ptr) {
+      // the old buffer may still be in use by queued work
+      if (hipDeviceSynchronize() != hipSuccess) return MK_EHIP;
+      (void)hipFree(o.ptr);
+      o.ptr = nullptr;
+      o.bytes = 0;
+    }
+    const size_t want = bytes < ((size_t)64 << 20) ? ((size_t)64 << 20) : bytes;
+    if (hipMalloc(&o.ptr, want) != hipSuccess) {
+      o.ptr = nullptr;
+      return MK_EHIP;
+    }
+    if (hipMemset(o.ptr, 0, want) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+      (void)hipFree(o.ptr);
+      o.ptr = nullptr;
+      return MK_EHIP;
+    }
+    o.bytes = want;
+  }
+  *out = o.ptr;
+  return MK_OK;
+}
+
+int run_gemm(bool tiled, const void* W, const uint16_t* X, float* Y, int M, int N, int K,
+             void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_gemm_args(W, X, Y, M, N, K, tiled);
+  if (rc != MK_OK) return rc;
+  // a caller workspace is validated before the device is looked at
+  int dev = -1;
+  const bool have_dev = current_device(&dev) == MK_OK;
+  const mk::GemmPlan p = mk::gemm_plan(M, N, K, have_dev ? g_dev[dev].cus : kDefaultCus);
+  if (!p.ok) return MK_EINVAL;
+  const bool caller_ws = workspace != nullptr || ws_bytes != 0;
+  if (caller_ws && p.ws_bytes > 0) {
+    if (!workspace || ws_bytes < p.ws_bytes) return MK_EWORKSPACE;
+    if (!aligned16(workspace)) return MK_EALIGN;
+  }
+  if (!have_dev) return MK_ENODEV;
+  void* ws = workspace;
+  if (!caller_ws && p.ws_bytes > 0) {
+    rc = owned_workspace(dev, p.ws_bytes, &ws);
+    if (rc != MK_OK) return rc;
+  }
+  hipError_t e = mk::gemm_launch(p, tiled, W, X, Y, M, N, K, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MK_OK : MK_EHIP;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -115,58 +177,24 @@ int mk_device_info(char* buf, size_t len) {
 
 size_t mk_q4k_gemm_workspace_bytes(int M, int N, int K) {
   if (M < 1 || M > MK_Q4K_MAX_M || N < 1 || K < MK_Q4K_QK || K % MK_Q4K_QK) return 0;
-  return mk::gemm_plan(M, N, K).ws_bytes;
+  int cus = 0;
+  if (mk::current_gfx950(&cus) != MK_OK) cus = kDefaultCus;
+  return mk::gemm_plan(M, N, K, cus).ws_bytes;
 }
 
 int mk_q4k_gemm_ws(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N,
                    int K, void* workspace, size_t ws_bytes, void* stream) {
-  int rc = check_gemm_args(W_blocks, X_fp16, Y_fp32, M, N, K);
-  if (rc != MK_OK) return rc;
-  const mk::GemmPlan p = mk::gemm_plan(M, N, K);
-  if (p.ws_bytes > 0) {
-    if (!workspace || ws_bytes < p.ws_bytes) return MK_EWORKSPACE;
-    if (!aligned16(workspace)) return MK_EALIGN;
-  }
-  int dev;
-  rc = current_device(&dev);
-  if (rc != MK_OK) return rc;
-  hipError_t e = mk::gemm_launch(p, W_blocks, X_fp16, Y_fp32, M, N, K, workspace,
-                                 static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? MK_OK : MK_EHIP;
+  return run_gemm(false, W_blocks, X_fp16, Y_fp32, M, N, K, workspace, ws_bytes, stream);
 }
 
 int mk_q4k_gemm(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N, int K,
                 void* stream) {
-  int rc = check_gemm_args(W_blocks, X_fp16, Y_fp32, M, N, K);
-  if (rc != MK_OK) return rc;
-  const mk::GemmPlan p = mk::gemm_plan(M, N, K);
-  int dev;
-  rc = current_device(&dev);
-  if (rc != MK_OK) return rc;
-  void* ws = nullptr;
-  if (p.ws_bytes > 0) {
-    std::lock_guard<std::mutex> lk(g_ws_mu);
-    OwnedWs& o = g_ws[dev];
-    if (o.bytes < p.ws_bytes) {
-      if (o.ptr) {
-        // the old buffer may still be in use by queued work
-        if (hipDeviceSynchronize() != hipSuccess) return MK_EHIP;
-        (void)hipFree(o.ptr);
-        o.ptr = nullptr;
-        o.bytes = 0;
-      }
-      size_t want = p.ws_bytes < ((size_t)64 << 20) ? ((size_t)64 << 20) : p.ws_bytes;
-      if (hipMalloc(&o.ptr, want) != hipSuccess) {
-        o.ptr = nullptr;
-        return MK_EHIP;
-      }
-      o.bytes = want;
-    }
-    ws = o.ptr;
-  }
-  hipError_t e = mk::gemm_launch(p, W_blocks, X_fp16, Y_fp32, M, N, K, ws,
-                                 static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? MK_OK : MK_EHIP;
+  return run_gemm(false, W_blocks, X_fp16, Y_fp32, M, N, K, nullptr, 0, stream);
+}
+
+int mk_q4k_gemm_tiled(const void* W_tiles, const uint16_t* X_fp16, float* Y_fp32, int M, int N,
+                      int K, void* stream) {
+  return run_gemm(true, W_tiles, X_fp16, Y_fp32, M, N, K, nullptr, 0, stream);
 }
 
 }  // extern "C"

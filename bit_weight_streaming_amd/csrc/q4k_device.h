@@ -120,73 +120,17 @@ __device__ __forceinline__ LaneScales lane_scales(const u32x4& h, int g) {
   return s;
 }
 
-// B operands of the two MFMAs fed by quant dwords v0, v1 (8 consecutive
-// weights of sub-block 2g in the low nibbles, of 2g+1 in the high nibbles),
-// k order (0,2,1,3,4,6,5,7).
-__device__ __forceinline__ void unpack_pair(uint32_t v0, uint32_t v1, const LaneScales& s,
-                                            half8v& b_lo, half8v& b_hi) {
-  const uint32_t t0 = v0 >> 8, t1 = v1 >> 8;
-  const half2v l0 = bit_cast_<half2v>((v0 & 0x000F000Fu) | 0x64006400u);
-  const half2v l1 = bit_cast_<half2v>((t0 & 0x000F000Fu) | 0x64006400u);
-  const half2v l2 = bit_cast_<half2v>((v1 & 0x000F000Fu) | 0x64006400u);
-  const half2v l3 = bit_cast_<half2v>((t1 & 0x000F000Fu) | 0x64006400u);
-  const half2v h0 = bit_cast_<half2v>((v0 & 0x00F000F0u) | 0x64006400u);
-  const half2v h1 = bit_cast_<half2v>((t0 & 0x00F000F0u) | 0x64006400u);
-  const half2v h2 = bit_cast_<half2v>((v1 & 0x00F000F0u) | 0x64006400u);
-  const half2v h3 = bit_cast_<half2v>((t1 & 0x00F000F0u) | 0x64006400u);
-  const half2v L0 = __builtin_elementwise_fma(l0, s.sl, s.nl);
-  const half2v L1 = __builtin_elementwise_fma(l1, s.sl, s.nl);
-  const half2v L2 = __builtin_elementwise_fma(l2, s.sl, s.nl);
-  const half2v L3 = __builtin_elementwise_fma(l3, s.sl, s.nl);
-  const half2v H0 = __builtin_elementwise_fma(h0, s.sh, s.nh);
-  const half2v H1 = __builtin_elementwise_fma(h1, s.sh, s.nh);
-  const half2v H2 = __builtin_elementwise_fma(h2, s.sh, s.nh);
-  const half2v H3 = __builtin_elementwise_fma(h3, s.sh, s.nh);
-  b_lo = half8v{L0.x, L0.y, L1.x, L1.y, L2.x, L2.y, L3.x, L3.y};
-  b_hi = half8v{H0.x, H0.y, H1.x, H1.y, H2.x, H2.y, H3.x, H3.y};
-}
 
-// Multiply one super-block (already in registers) against MT row tiles.
-// xa[rt] points at this lane's 128 LDS bytes of activations for the block
-// (row 16*rt + l%16, chunk g) or is null when that row does not exist;
-// xs[rt] points at its 4 sub-block-sum halves (hi/lo of sub-blocks 2g, 2g+1).
-template <int MT>
-__device__ __forceinline__ void mma_block(const BlockRegs& r, int g, const char* const* xa,
-                                          const char* const* xs, floatx4* acc) {
-  const LaneScales s = lane_scales(r.h, g);
-  half8v b[8];
-  unpack_pair(r.q0.x, r.q0.y, s, b[0], b[1]);
-  unpack_pair(r.q0.z, r.q0.w, s, b[2], b[3]);
-  unpack_pair(r.q1.x, r.q1.y, s, b[4], b[5]);
-  unpack_pair(r.q1.z, r.q1.w, s, b[6], b[7]);
-#pragma unroll
-  for (int rt = 0; rt < MT; ++rt) {
-    floatx4 cm = {0.f, 0.f, 0.f, 0.f};
-    floatx4 cn = {0.f, 0.f, 0.f, 0.f};
-    half4v am = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
-    if (xs[rt]) am = *reinterpret_cast<const half4v*>(xs[rt]);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      half8v a = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f,
-                  (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
-      if (xa[rt]) a = *reinterpret_cast<const half8v*>(xa[rt] + 16 * t);
-      cm = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[t], cm, 0, 0, 0);
-    }
-    cn = __builtin_amdgcn_mfma_f32_16x16x16f16(am, s.bmin, cn, 0, 0, 0);
-    acc[rt] = __builtin_elementwise_fma(floatx4{s.d, s.d, s.d, s.d}, cm, acc[rt]);
-    acc[rt] = __builtin_elementwise_fma(floatx4{-s.dmin, -s.dmin, -s.dmin, -s.dmin}, cn, acc[rt]);
-  }
-}
 
 // Stage activations of super-blocks [kb0, kb0+nkb) of the M rows of X
-// ([M][K] binary16, row stride K) into LDS in the MFMA order above, plus the
-// fp32 sums of every 32-weight sub-block split into binary16 hi + lo.
+// ([M][K] binary16, row stride K) into LDS in the MFMA order above (the
+// sub-block sums follow from the staged copy: stage_xsum, after a barrier).
 // x_lds row m starts at m * row_stride bytes; position of (block b, chunk g,
 // MFMA t, element e) is b*512 + g*128 + t*16 + 2*e and holds
 // x[m][(kb0+b)*256 + 64g + 32(t&1) + 8(t>>1) + perm(e)], perm = 0,2,1,3,4,6,5,7.
 __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ X, int K, int M, int kb0,
-                                        int nkb, char* x_lds, int row_stride, char* xs_lds,
-                                        int tid, int nthreads) {
+                                        int nkb, char* x_lds, int row_stride, int tid,
+                                        int nthreads) {
   const int items = M * nkb * 32;
   for (int it = tid; it < items; it += nthreads) {
     const int t = it & 7;
@@ -205,80 +149,12 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ X, int K, i
     *reinterpret_cast<u32x4*>(x_lds + (size_t)m * row_stride + b * X_BYTES_PER_BLOCK + g * 128 +
                               t * 16) = o;
   }
-  const int sitems = M * nkb * 8;
-  for (int it = tid; it < sitems; it += nthreads) {
-    const int j = it & 7;
-    const int rest = it >> 3;
-    const int b = rest % nkb;
-    const int m = rest / nkb;
-    const u32x4* src = reinterpret_cast<const u32x4*>(X + (size_t)m * K + (kb0 + b) * QK + 32 * j);
-    float sum = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4 v = src[q];
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const half2v h = bit_cast_<half2v>(w4[i]);
-        sum += (float)h.x;
-        sum += (float)h.y;
-      }
-    }
-    const _Float16 hi = (_Float16)sum;
-    const _Float16 lo = (_Float16)(sum - (float)hi);
-    half2v p = {hi, lo};
-    *reinterpret_cast<half2v*>(xs_lds + ((size_t)m * nkb + b) * XSUM_BYTES_PER_BLOCK + 4 * j) = p;
-  }
 }
 
 }  // namespace mk
 
 namespace mk {
 
-// One row tile (M <= 16) against NB weight blocks of the same super-block
-// position (e.g. the gate and up rows of one column tile): each group of 8
-// activation operands is read from LDS once and used for every block, and the
-// weights are unpacked one 8-weight group at a time to keep few registers live.
-template <int NB>
-__device__ __forceinline__ void mma_blocks_rt1(const BlockRegs* r, int g, const char* xa,
-                                               const char* xs, floatx4* acc) {
-  LaneScales s[NB];
-  floatx4 cm[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    s[nb] = lane_scales(r[nb].h, g);
-    cm[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-  const half8v zero8 = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f,
-                        (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    half8v a_lo = zero8, a_hi = zero8;
-    if (xa) {
-      a_lo = *reinterpret_cast<const half8v*>(xa + 16 * (2 * u));
-      a_hi = *reinterpret_cast<const half8v*>(xa + 16 * (2 * u + 1));
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const uint32_t v0 = u == 0 ? r[nb].q0.x : u == 1 ? r[nb].q0.z : u == 2 ? r[nb].q1.x : r[nb].q1.z;
-      const uint32_t v1 = u == 0 ? r[nb].q0.y : u == 1 ? r[nb].q0.w : u == 2 ? r[nb].q1.y : r[nb].q1.w;
-      half8v b_lo, b_hi;
-      unpack_pair(v0, v1, s[nb], b_lo, b_hi);
-      cm[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, cm[nb], 0, 0, 0);
-      cm[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, cm[nb], 0, 0, 0);
-    }
-  }
-  half4v am = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
-  if (xs) am = *reinterpret_cast<const half4v*>(xs);
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    floatx4 cn = {0.f, 0.f, 0.f, 0.f};
-    cn = __builtin_amdgcn_mfma_f32_16x16x16f16(am, s[nb].bmin, cn, 0, 0, 0);
-    acc[nb] = __builtin_elementwise_fma(floatx4{s[nb].d, s[nb].d, s[nb].d, s[nb].d}, cm[nb], acc[nb]);
-    acc[nb] = __builtin_elementwise_fma(floatx4{-s[nb].dmin, -s[nb].dmin, -s[nb].dmin, -s[nb].dmin},
-                                        cn, acc[nb]);
-  }
-}
 
 }  // namespace mk
 
@@ -322,7 +198,13 @@ __device__ __forceinline__ UnpackConsts unpack_consts() {
   return k;
 }
 
-// As unpack_pair, with the masks in registers.
+// B operands of the two MFMAs fed by quant dwords v0, v1 (8 consecutive
+// weights of sub-block 2g in the low nibbles, of 2g+1 in the high nibbles),
+// k order (0,2,1,3,4,6,5,7): each nibble q becomes the binary16 1024 + q (or
+// 1024 + 16 q for a high nibble) by OR-ing in the exponent pattern, and one
+// packed FMA with (scale, -1024 * scale) (or (scale / 16, -64 * scale))
+// leaves exactly scale * q: every operand and result is exact in binary16.
+// Masks come in registers.
 __device__ __forceinline__ void unpack_pair_k(uint32_t v0, uint32_t v1, const LaneScales& s,
                                               const UnpackConsts& k, half8v& b_lo,
                                               half8v& b_hi) {
@@ -386,6 +268,162 @@ __device__ __forceinline__ void mma_unit(const BlockRegs* r, int g, const char* 
     acc[nb] = __builtin_elementwise_fma(dd, c1[nb], acc[nb]);
     acc[nb] = __builtin_elementwise_fma(
         floatx4{-s[nb].dmin, -s[nb].dmin, -s[nb].dmin, -s[nb].dmin}, cn, acc[nb]);
+  }
+}
+
+}  // namespace mk
+
+namespace mk {
+
+// ---- pieces shared by the persistent streaming kernels (decode step, GEMM)
+
+// Waves per workgroup of the streaming kernels; unit ranges are split over
+// them with a shift.
+constexpr int SPLIT_WAVES = 8;
+
+// 16-byte device-coherent accesses through a buffer resource (cache policy
+// sc1: the agent-scope coherence level, as for relaxed agent-scope atomics).
+// Offsets past the resource's size read as zero and drop writes.
+constexpr int kCoherent = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ floatx4 ld4_dev(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
+}
+__device__ __forceinline__ void st4_dev(__amdgpu_buffer_rsrc_t r, unsigned off, floatx4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCoherent);
+}
+
+// Values the compiler cannot see are the same in every lane (read from LDS)
+// but are: forcing them into scalar registers keeps the work split and the
+// weight-record walk on the scalar unit and out of the vector registers.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <class T>
+__device__ __forceinline__ T* uni(T* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return reinterpret_cast<T*>(((unsigned long long)hi << 32) | lo);
+}
+
+// Work split of one matrix pass over G workgroups: the K range is cut into sk
+// slices of nkb super-blocks (the last may be shorter); the workgroups are
+// spread over the slices in proportion to their super-blocks, and the nt
+// 16-column tiles are split evenly among the workgroups of a slice. Inside a
+// workgroup the tw * nkb (tile, super-block) units are split over the waves.
+struct Assign {
+  int s;      // K slice
+  int t0;     // first tile
+  int tw;     // tiles
+  int kb0;    // first super-block of the slice
+  int nkb;    // super-blocks in the slice
+  int j, gs;  // index among, and number of, workgroups sharing the slice
+  int U;      // units = tw * nkb
+};
+
+// First workgroup of slice s.
+__host__ __device__ inline int slice_start(int s, int sk, int nkb, int KB, int G) {
+  return s >= sk ? G : (int)((long long)G * s * nkb / KB);
+}
+
+__host__ __device__ inline Assign assign_split(int nt, int sk, int nkb, int KB, int w, int G) {
+  Assign a;
+  int s = 0;
+  while (s + 1 < sk && slice_start(s + 1, sk, nkb, KB, G) <= w) ++s;
+  const int first = slice_start(s, sk, nkb, KB, G);
+  a.s = s;
+  a.j = w - first;
+  a.gs = slice_start(s + 1, sk, nkb, KB, G) - first;
+  a.t0 = (int)((long long)nt * a.j / a.gs);
+  a.tw = (int)((long long)nt * (a.j + 1) / a.gs) - a.t0;
+  a.kb0 = a.s * nkb;
+  a.nkb = nkb < KB - a.kb0 ? nkb : KB - a.kb0;
+  a.U = a.tw * a.nkb;
+  return a;
+}
+
+// First unit of wave v's range, and the wave whose range holds unit x (the
+// last wave whose range starts at or before x: waves with an empty range are
+// skipped). No divisions: both run in the per-tile and per-element loops.
+static_assert(SPLIT_WAVES == 8, "wave ranges are computed with a shift by 3");
+__host__ __device__ inline int wave_begin(const Assign& a, int v) { return (a.U * v) >> 3; }
+__host__ __device__ inline int wave_of_unit(const Assign& a, int x) {
+  int w = 0;
+#pragma unroll
+  for (int v = 1; v < SPLIT_WAVES; ++v) w += ((a.U * v) >> 3) <= x;
+  return w;
+}
+
+// Sub-block sums of the staged activations, split into binary16 hi + lo, for
+// the min-term MFMA: row m, block b, sub-block j at
+// xs_lds + (m * nkb_stride + b) * 32 + 4 * j.
+__device__ __forceinline__ void stage_xsum(int M, int nkb, int nkb_stride, const char* x_lds,
+                                           int x_stride, char* xs_lds, int tid,
+                                           int nthreads) {
+  const int items = M * nkb * 8;
+  for (int it = tid; it < items; it += nthreads) {
+    const int j = it & 7;
+    const int rest = it >> 3;
+    const int m = rest / nkb;
+    const int b = rest - m * nkb;
+    const int gq = j >> 1, hb = j & 1;
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(
+          x_lds + (size_t)m * x_stride + b * X_BYTES_PER_BLOCK + gq * 128 + (2 * u + hb) * 16);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const half2v hh = bit_cast_<half2v>(w4[i]);
+        sum += (float)hh.x;
+        sum += (float)hh.y;
+      }
+    }
+    const _Float16 hi = (_Float16)sum;
+    const _Float16 lo = (_Float16)(sum - (float)hi);
+    *reinterpret_cast<half2v*>(xs_lds + ((size_t)m * nkb_stride + b) * XSUM_BYTES_PER_BLOCK +
+                               4 * j) = half2v{hi, lo};
+  }
+}
+
+// Activations of MT 16-row tiles (xa[rt]: this lane's 128 LDS bytes of the
+// block, always valid - rows past M read a real row whose results are never
+// stored) against one weight record; the main term runs as two independent
+// MFMA chains per row tile, the weights are unpacked once for all row tiles.
+template <int MT>
+__device__ __forceinline__ void mma_unit_mt(const BlockRegs& r, int g, const char* const* xa,
+                                            const char* const* xs, const UnpackConsts& k,
+                                            floatx4* acc) {
+  const LaneScales s = lane_scales(r.h, g);
+  floatx4 c0[MT], c1[MT];
+#pragma unroll
+  for (int rt = 0; rt < MT; ++rt) c0[rt] = c1[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t v0 = u == 0 ? r.q0.x : u == 1 ? r.q0.z : u == 2 ? r.q1.x : r.q1.z;
+    const uint32_t v1 = u == 0 ? r.q0.y : u == 1 ? r.q0.w : u == 2 ? r.q1.y : r.q1.w;
+    half8v b_lo, b_hi;
+    unpack_pair_k(v0, v1, s, k, b_lo, b_hi);
+#pragma unroll
+    for (int rt = 0; rt < MT; ++rt) {
+      const half8v a_lo = *reinterpret_cast<const half8v*>(xa[rt] + 32 * u);
+      const half8v a_hi = *reinterpret_cast<const half8v*>(xa[rt] + 32 * u + 16);
+      c0[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, c0[rt], 0, 0, 0);
+      c1[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, c1[rt], 0, 0, 0);
+    }
+  }
+  const floatx4 dd = {s.d, s.d, s.d, s.d};
+  const floatx4 nm = {-s.dmin, -s.dmin, -s.dmin, -s.dmin};
+#pragma unroll
+  for (int rt = 0; rt < MT; ++rt) {
+    const half4v am = *reinterpret_cast<const half4v*>(xs[rt]);
+    floatx4 cn = {0.f, 0.f, 0.f, 0.f};
+    cn = __builtin_amdgcn_mfma_f32_16x16x16f16(am, s.bmin, cn, 0, 0, 0);
+    acc[rt] = __builtin_elementwise_fma(dd, c0[rt], acc[rt]);
+    acc[rt] = __builtin_elementwise_fma(dd, c1[rt], acc[rt]);
+    acc[rt] = __builtin_elementwise_fma(nm, cn, acc[rt]);
   }
 }
 

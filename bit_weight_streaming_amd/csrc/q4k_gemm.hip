@@ -1,160 +1,357 @@
 // q4k_gemm.hip - single-matrix Q4_K weight-streaming GEMM, Y = X * W^T.
 //
-// Grid: x = groups of WAVES column tiles (16 columns per wave), y = K slices.
-// Each workgroup stages the activations of its K slice into LDS once, then
-// every wave streams the Q4_K blocks of its 16 weight rows over that slice
-// through a register ring of PD blocks in flight, multiplying each block
-// against all M rows (mma_block). With one slice the result goes straight to
-// Y; with several, each slice writes fp32 partials and a second kernel adds
-// them in slice order (deterministic; no floating-point atomics).
+// One persistent pass over the weights (the multi-row decode step of the
+// OpenJet post, "RTX 3090 one card, four coding agents", paragraph on how
+// parallel decoding works: each weight is read once and multiplied against
+// every stacked row while on chip).
+//
+// Grid: one workgroup per CU, 8 waves. The K range is cut into sk slices; the
+// workgroups are spread over the slices (assign_split) and each stages the M
+// activation rows of its slice into LDS once. The workgroup's (16-column
+// tile, super-block) units are split over its waves; every wave streams its
+// units through a register ring of GEMM_PD records and multiplies each
+// record against all M rows (MT 16-row MFMA tiles). A tile that one wave
+// computes alone is written straight out: to Y when there is one K slice, as
+// a slice partial otherwise. Tiles shared by waves meet in LDS (two slots per
+// wave) and are added at the end. With several slices, every workgroup then
+// counts its tiles in with an atomic that returns the previous count; the
+// workgroup that brings a tile's count to sk adds the sk partials in slice
+// order, writes Y and resets the counter to zero. No workgroup ever waits for
+// another one, and no floating-point atomics are used.
+//
+// TILED selects the load-time tile-record layout (mk_q4k_repack: every wave
+// load is one contiguous 1 KiB piece); otherwise the plain row layout is read
+// in place.
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "q4k_device.h"
 #include "q4k_host.h"
 
 namespace mk {
 
-constexpr int GEMM_WAVES = 4;
-constexpr int GEMM_THREADS = 64 * GEMM_WAVES;
+constexpr int GEMM_THREADS = 64 * SPLIT_WAVES;
+constexpr size_t kGemmLdsLimit = 160 * 1024;
+constexpr size_t GEMM_CTR_REGION = 256 * 1024;  // counters of up to 65536 column tiles
 
-template <int MT, int PD>
-__global__ void __launch_bounds__(GEMM_THREADS)
-    q4k_gemm_kernel(const uint8_t* __restrict__ W, const uint16_t* __restrict__ X,
-                    float* __restrict__ out, int M, int N, int K, int nkb_slice) {
+struct GemmArgs {
+  const uint8_t* w;    // weights: tile records (TILED) or row blocks
+  const uint16_t* x;   // [M][K] binary16
+  float* y;            // [M][N]
+  unsigned* ctr;       // per-tile arrival counters (zero between calls)
+  char* part;          // slice partials
+  unsigned part_bytes; // bytes of slice partials
+  int M, N, K, KB, nt, sk, nkb, G, x_stride, lds_contrib;
+};
+
+template <int MT>
+struct GemmRing {  // records in flight per wave (what the registers allow)
+  static constexpr int PD = MT == 1 ? 6 : MT == 2 ? 4 : MT == 3 ? 3 : 2;
+};
+
+template <int MT, bool TILED>
+__global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
+  constexpr int PD = GemmRing<MT>::PD;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int KB = K / QK;
-  const int slice = blockIdx.y;
-  const int kb0 = slice * nkb_slice;
-  const int nkb = min(nkb_slice, KB - kb0);
-  const int row_stride = nkb_slice * X_BYTES_PER_BLOCK + X_ROW_PAD;
+  __shared__ int nlast_s;
+  const int tid = threadIdx.x;
+  const int wave = uni(tid >> 6), lane = tid & 63, c = lane & 15, g = lane >> 4;
+  const Assign a = assign_split(A.nt, A.sk, A.nkb, A.KB, blockIdx.x, A.G);
   char* x_lds = smem;
-  char* xs_lds = smem + (size_t)M * row_stride;
+  char* xs_lds = smem + (size_t)A.M * A.x_stride;
+  char* contrib = smem + A.lds_contrib;
+  int* last_list = reinterpret_cast<int*>(contrib + SPLIT_WAVES * 2 * MT * 1024);
 
-  stage_x(X, K, M, kb0, nkb, x_lds, row_stride, xs_lds, threadIdx.x, GEMM_THREADS);
-  __syncthreads();
-
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int c = lane & 15;   // B/C column within the tile; also the A-operand row
-  const int g = lane >> 4;   // quant chunk / k group
-  const int col0 = (blockIdx.x * GEMM_WAVES + wave) * 16;
-  if (col0 >= N) return;
-  // rows past N (ragged last tile) read the last valid row; never stored
-  const int col = min(col0 + c, N - 1);
-  const uint8_t* wrow = W + ((size_t)col * KB + kb0) * BLOCK_BYTES;
-
-  const char* xa0[MT];
-  const char* xs0[MT];
+  // this lane's activations of each row tile (rows past M read row M-1; their
+  // results are never stored, so every read is unconditional)
+  const char* xa[MT];
+  const char* xs[MT];
 #pragma unroll
   for (int rt = 0; rt < MT; ++rt) {
-    const int m = 16 * rt + c;
-    xa0[rt] = m < M ? x_lds + (size_t)m * row_stride + g * 128 : nullptr;
-    xs0[rt] = m < M ? xs_lds + (size_t)m * nkb * XSUM_BYTES_PER_BLOCK + 8 * g : nullptr;
+    const int row = min(16 * rt + c, A.M - 1);
+    xa[rt] = x_lds + (size_t)row * A.x_stride + g * 128;
+    xs[rt] = xs_lds + (size_t)row * a.nkb * XSUM_BYTES_PER_BLOCK + 8 * g;
   }
-  floatx4 acc[MT];
-#pragma unroll
-  for (int rt = 0; rt < MT; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const UnpackConsts k = unpack_consts();
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(A.part, A.part_bytes);
 
-  // Register ring of PD blocks in flight. The steady-state loop issues its
-  // loads unconditionally (past the end it re-reads the last block, which is
-  // never consumed) so the compiler can wait for exactly the oldest block.
-  BlockRegs ring[PD];
+  // the result of tile tg, row tile rt, lane ln: to Y, or as this slice's partial
+  auto put = [&](int tg, int ln, const floatx4& v, int rt) {
+    if (A.sk == 1) {
+      const int col = 16 * tg + (ln & 15);
+      if (col < A.N) {
 #pragma unroll
-  for (int s = 0; s < PD; ++s) load_block(ring[s], wrow + (size_t)min(s, nkb - 1) * BLOCK_BYTES, g);
-
-  auto consume = [&](const BlockRegs& r, int b) {
-    const char* xa[MT];
-    const char* xs[MT];
-#pragma unroll
-    for (int rt = 0; rt < MT; ++rt) {
-      xa[rt] = xa0[rt] ? xa0[rt] + b * X_BYTES_PER_BLOCK : nullptr;
-      xs[rt] = xs0[rt] ? xs0[rt] + b * XSUM_BYTES_PER_BLOCK : nullptr;
+        for (int r = 0; r < 4; ++r) {
+          const int m = 16 * rt + 4 * (ln >> 4) + r;
+          if (m < A.M) A.y[(size_t)m * A.N + col] = v[r];
+        }
+      }
+    } else {
+      st4_dev(pr, ((unsigned)(tg * A.sk + a.s) * MT + rt) * 1024u + ln * 16, v);
     }
-    mma_block<MT>(r, g, xa, xs, acc);
   };
-  int b = 0;
-  for (; b + PD <= nkb; b += PD) {
-#pragma unroll
-    for (int s = 0; s < PD; ++s) {
-      consume(ring[s], b + s);
-      load_block(ring[s], wrow + (size_t)min(b + s + PD, nkb - 1) * BLOCK_BYTES, g);
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < PD; ++s)
-    if (b + s < nkb) consume(ring[s], b + s);
+  // LDS slot of wave v: 0 = a tile that began before its range, 1 = a tile
+  // that goes on after it
+  auto slot = [&](int v, int ab, int rt) -> char* {
+    return contrib + ((size_t)(v * 2 + ab) * MT + rt) * 1024;
+  };
 
-  if (col0 + c < N) {
-    float* o = out + (size_t)slice * M * N + col0 + c;
-#pragma unroll
-    for (int rt = 0; rt < MT; ++rt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 16 * rt + 4 * g + r;
-        if (m < M) o[(size_t)m * N] = acc[rt][r];
+  const int ua = wave_begin(a, wave), ub = wave_begin(a, wave + 1);
+  // next unit to load; past the end the last unit is re-read (never used),
+  // so the steady-state loads are unconditional
+  int ltl = ua / a.nkb, lb = ua - ltl * a.nkb, lu = ua;
+  auto load_next = [&](BlockRegs& r) {
+    const int tg = a.t0 + ltl;
+    if (TILED) {
+      load_rec(r, A.w + ((size_t)tg * A.KB + a.kb0 + lb) * TILE_REC, lane);
+    } else {
+      const int col = min(16 * tg + c, A.N - 1);
+      load_block(r, A.w + ((size_t)col * A.KB + a.kb0 + lb) * BLOCK_BYTES, g);
+    }
+    if (lu + 1 < ub) {
+      ++lu;
+      if (++lb == a.nkb) {
+        lb = 0;
+        ++ltl;
       }
     }
+  };
+  // the first weight records are in flight while the activations are staged
+  BlockRegs ring[PD];
+  if (ua < ub) {
+#pragma unroll
+    for (int s = 0; s < PD; ++s) load_next(ring[s]);
+  }
+  if (a.U > 0) stage_x(A.x, A.K, A.M, a.kb0, a.nkb, x_lds, A.x_stride, tid, GEMM_THREADS);
+  if (tid == 0) nlast_s = 0;
+  __syncthreads();
+  if (a.U > 0) stage_xsum(A.M, a.nkb, a.nkb, x_lds, A.x_stride, xs_lds, tid, GEMM_THREADS);
+  __syncthreads();
+
+  if (ua < ub) {
+
+    floatx4 acc[MT];
+#pragma unroll
+    for (int rt = 0; rt < MT; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    int ctl = ua / a.nkb, cb = ua - ctl * a.nkb, cu = ua;
+    auto flush = [&]() {
+      const int first = wave_of_unit(a, ctl * a.nkb);
+      const int last = wave_of_unit(a, (ctl + 1) * a.nkb - 1);
+      if (first == last) {
+#pragma unroll
+        for (int rt = 0; rt < MT; ++rt) put(a.t0 + ctl, lane, acc[rt], rt);
+      } else {
+        const int ab = ctl * a.nkb < ua ? 0 : 1;
+#pragma unroll
+        for (int rt = 0; rt < MT; ++rt)
+          *reinterpret_cast<floatx4*>(slot(wave, ab, rt) + lane * 16) = acc[rt];
+      }
+#pragma unroll
+      for (int rt = 0; rt < MT; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto consume = [&](const BlockRegs& r) {
+      const char* xab[MT];
+      const char* xsb[MT];
+#pragma unroll
+      for (int rt = 0; rt < MT; ++rt) {
+        xab[rt] = xa[rt] + cb * X_BYTES_PER_BLOCK;
+        xsb[rt] = xs[rt] + cb * XSUM_BYTES_PER_BLOCK;
+      }
+      mma_unit_mt<MT>(r, g, xab, xsb, k, acc);
+      ++cu;
+      if (++cb == a.nkb || cu == ub) {
+        flush();
+        if (cb == a.nkb) {
+          cb = 0;
+          ++ctl;
+        }
+      }
+    };
+    const int U = ub - ua;
+    int r = 0;
+    for (; r + PD <= U; r += PD) {
+#pragma unroll
+      for (int s = 0; s < PD; ++s) {
+        consume(ring[s]);
+        load_next(ring[s]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < PD; ++s)
+      if (r + s < U) consume(ring[s]);
+  }
+  __syncthreads();
+
+  // Tiles shared by waves: each holds the start of some wave's range other
+  // than at its first unit; taken once, at the first such boundary. The
+  // tile's first wave left its part in slot 1, every later wave in slot 0.
+  for (int e = tid; e < (SPLIT_WAVES - 1) * MT * 64; e += GEMM_THREADS) {
+    const int vb = 1 + (e >> 6) / MT, rt = (e >> 6) % MT, ln = e & 63;
+    const int u = wave_begin(a, vb);
+    if (u >= a.U || u % a.nkb == 0) continue;
+    const int tl = u / a.nkb;
+    const int up = wave_begin(a, vb - 1);
+    if (vb > 1 && up % a.nkb != 0 && up / a.nkb == tl) continue;
+    const int w0 = wave_of_unit(a, tl * a.nkb);
+    const int w1 = wave_of_unit(a, (tl + 1) * a.nkb - 1);
+    floatx4 v = *reinterpret_cast<const floatx4*>(slot(w0, 1, rt) + ln * 16);
+    for (int vv = w0 + 1; vv <= w1; ++vv) {
+      if (wave_begin(a, vv) == wave_begin(a, vv + 1)) continue;  // empty range: wrote nothing
+      v += *reinterpret_cast<const floatx4*>(slot(vv, 0, rt) + ln * 16);
+    }
+    put(a.t0 + tl, ln, v, rt);
+  }
+  if (A.sk == 1) return;
+
+  // count the tiles in; the workgroup that completes a tile finishes it
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // our partials are stored
+  __syncthreads();
+  unsigned* ctr = A.ctr;
+  for (int i = tid; i < a.tw; i += GEMM_THREADS) {
+    const unsigned old =
+        __hip_atomic_fetch_add(&ctr[a.t0 + i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == (unsigned)(A.sk - 1)) last_list[atomicAdd(&nlast_s, 1)] = a.t0 + i;
+  }
+  __syncthreads();
+  const int nl = nlast_s;
+  for (int t = tid; t < nl * MT * 64; t += GEMM_THREADS) {
+    const int li = t / (MT * 64), rt = (t >> 6) % MT, ln = t & 63;
+    const int tg = last_list[li];
+    const unsigned base = ((unsigned)tg * A.sk * MT + rt) * 1024u + ln * 16;
+    floatx4 y = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < A.sk; s0 += 4) {
+      floatx4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (s0 + i < A.sk) v[i] = ld4_dev(pr, base + (unsigned)(s0 + i) * MT * 1024u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (s0 + i < A.sk) y += v[i];
+    }
+    const int col = 16 * tg + (ln & 15);
+    if (col < A.N) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * rt + 4 * (ln >> 4) + r;
+        if (m < A.M) A.y[(size_t)m * A.N + col] = y[r];
+      }
+    }
+    if (rt == 0 && ln == 0)
+      __hip_atomic_store(&ctr[tg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Y[i] = sum_s P[s][i] in slice order.
-__global__ void __launch_bounds__(256)
-    q4k_reduce_slices(const float* __restrict__ P, float* __restrict__ Y, long long n, int ks) {
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (long long)gridDim.x * blockDim.x) {
-    float s = P[i];
-    for (int k = 1; k < ks; ++k) s += P[(size_t)k * n + i];
-    Y[i] = s;
-  }
-}
+namespace {
 
-GemmPlan gemm_plan(int M, int N, int K) {
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+GemmPlan make_plan(int M, int N, int K, int G) {
   GemmPlan p;
-  const int KB = K / QK;
   p.mt = (M + 15) / 16;
-  // LDS budget for the staged activations of one slice
-  const size_t budget = p.mt >= 4 ? 120 * 1024 : 48 * 1024;
-  const size_t per_block = (size_t)M * (X_BYTES_PER_BLOCK + XSUM_BYTES_PER_BLOCK);
-  int nkb = (int)((budget - (size_t)M * X_ROW_PAD) / per_block);
-  if (nkb < 1) nkb = 1;
-  if (nkb > KB) nkb = KB;
-  p.ks = (KB + nkb - 1) / nkb;
-  p.nkb = (KB + p.ks - 1) / p.ks;  // even out the slices
-  p.lds = (size_t)M * (p.nkb * X_BYTES_PER_BLOCK + X_ROW_PAD) +
-          (size_t)M * p.nkb * XSUM_BYTES_PER_BLOCK;
-  p.groups = ((N + 15) / 16 + GEMM_WAVES - 1) / GEMM_WAVES;
-  p.ws_bytes = p.ks > 1 ? (size_t)p.ks * M * N * sizeof(float) : 0;
+  p.KB = K / QK;
+  p.nt = (N + 15) / 16;
+  p.G = G < p.nt * p.KB ? G : p.nt * p.KB;  // no more workgroups than units
+  G = p.G;
+  const size_t contrib = (size_t)SPLIT_WAVES * 2 * p.mt * 1024;
+  const double avg = (double)p.nt * p.KB / G;
+  int prev_nkb = -1;
+  for (int sk = 1; sk <= p.KB; ++sk) {
+    const int nkb = (p.KB + sk - 1) / sk;
+    if (nkb == prev_nkb) continue;
+    prev_nkb = nkb;
+    const int skr = (p.KB + nkb - 1) / nkb;
+    const size_t xb = (size_t)M * (nkb * X_BYTES_PER_BLOCK + X_ROW_PAD) +
+                      (size_t)M * nkb * XSUM_BYTES_PER_BLOCK;
+    const size_t c0 = (xb + 15) & ~(size_t)15;
+    int tw_max = 1, umax = 0;
+    for (int w = 0; w < G; ++w) {
+      const Assign a = assign_split(p.nt, skr, nkb, p.KB, w, G);
+      if (a.tw > tw_max) tw_max = a.tw;
+      if (a.U > umax) umax = a.U;
+    }
+    const size_t lds = c0 + contrib + (size_t)tw_max * sizeof(int);
+    const bool fits = lds + 256 <= kGemmLdsLimit;
+    // accept the first split that fits and keeps the busiest workgroup
+    // within ~8% of the mean (or cannot be split further)
+    const bool balanced = umax <= avg * 1.08 + 1.0;
+    if ((fits && balanced) || nkb == 1) {
+      p.sk = skr;
+      p.nkb = nkb;
+      p.x_stride = nkb * X_BYTES_PER_BLOCK + X_ROW_PAD;
+      p.lds_contrib = (int)c0;
+      p.lds = lds;
+      p.ok = fits;
+      break;
+    }
+  }
+  // workspace: the per-tile counters in a fixed region at the start (every
+  // call leaves them zero, and no call of any shape writes anything else
+  // there), then the slice partials
+  p.part_bytes = p.sk > 1 ? (size_t)p.nt * p.sk * p.mt * 1024 : 0;
+  p.part_off = GEMM_CTR_REGION;
+  p.ws_bytes = p.sk > 1 ? p.part_off + p.part_bytes : 0;
+  if (p.part_bytes >= (1ull << 32) || (size_t)p.nt * sizeof(unsigned) > GEMM_CTR_REGION)
+    p.ok = false;
   return p;
 }
 
-template <int MT>
-static hipError_t launch_mt(const GemmPlan& p, const uint8_t* W, const uint16_t* X, float* out,
-                            int M, int N, int K, hipStream_t st) {
-  constexpr int PD = 4;
-  auto kern = q4k_gemm_kernel<MT, PD>;
+std::mutex g_plan_mu;
+std::map<std::tuple<int, int, int, int>, GemmPlan> g_plans;
+
+template <int MT, bool TILED>
+hipError_t launch(const GemmPlan& p, const GemmArgs& A, hipStream_t st) {
+  auto kern = q4k_gemm_kernel<MT, TILED>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(p.groups, p.ks), dim3(GEMM_THREADS), p.lds, st, W, X, out, M, N,
-                     K, p.nkb);
+  hipLaunchKernelGGL(kern, dim3(p.G), dim3(GEMM_THREADS), p.lds, st, A);
   return hipGetLastError();
 }
 
-hipError_t gemm_launch(const GemmPlan& p, const void* W, const uint16_t* X, float* Y, int M, int N,
-                       int K, void* ws, hipStream_t st) {
-  float* out = p.ks > 1 ? static_cast<float*>(ws) : Y;
-  const uint8_t* w = static_cast<const uint8_t*>(W);
-  hipError_t e;
+template <bool TILED>
+hipError_t launch_mt(const GemmPlan& p, const GemmArgs& A, hipStream_t st) {
   switch (p.mt) {
-    case 1: e = launch_mt<1>(p, w, X, out, M, N, K, st); break;
-    case 2: e = launch_mt<2>(p, w, X, out, M, N, K, st); break;
-    case 3: e = launch_mt<3>(p, w, X, out, M, N, K, st); break;
-    default: e = launch_mt<4>(p, w, X, out, M, N, K, st); break;
+    case 1: return launch<1, TILED>(p, A, st);
+    case 2: return launch<2, TILED>(p, A, st);
+    case 3: return launch<3, TILED>(p, A, st);
+    default: return launch<4, TILED>(p, A, st);
   }
-  if (e != hipSuccess || p.ks == 1) return e;
-  const long long n = (long long)M * N;
-  int blocks = (int)((n + 255) / 256);
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(q4k_reduce_slices, dim3(blocks), dim3(256), 0, st, out, Y, n, p.ks);
-  return hipGetLastError();
+}
+
+}  // namespace
+
+GemmPlan gemm_plan(int M, int N, int K, int G) {
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  const auto key = std::make_tuple(M, N, K, G);
+  auto it = g_plans.find(key);
+  if (it != g_plans.end()) return it->second;
+  const GemmPlan p = make_plan(M, N, K, G);
+  if (g_plans.size() > 4096) g_plans.clear();
+  g_plans.emplace(key, p);
+  return p;
+}
+
+hipError_t gemm_launch(const GemmPlan& p, bool tiled, const void* W, const uint16_t* X, float* Y,
+                       int M, int N, int K, void* ws, hipStream_t st) {
+  GemmArgs A;
+  A.w = static_cast<const uint8_t*>(W);
+  A.x = X;
+  A.y = Y;
+  A.ctr = static_cast<unsigned*>(ws);
+  A.part = static_cast<char*>(ws) + p.part_off;
+  A.part_bytes = (unsigned)p.part_bytes;
+  A.M = M;
+  A.N = N;
+  A.K = K;
+  A.KB = p.KB;
+  A.nt = p.nt;
+  A.sk = p.sk;
+  A.nkb = p.nkb;
+  A.G = p.G;
+  A.x_stride = p.x_stride;
+  A.lds_contrib = p.lds_contrib;
+  return tiled ? launch_mt<true>(p, A, st) : launch_mt<false>(p, A, st);
 }
 
 }  // namespace mk

@@ -8,19 +8,26 @@
 
 namespace mk {
 
-// Launch plan of the single-matrix GEMM for one (M, N, K).
+// Launch plan of the single-matrix GEMM for one (M, N, K) on G workgroups.
 struct GemmPlan {
-  int mt = 1;          // 16-row MFMA tiles covering M
-  int ks = 1;          // K slices (workgroup rows of the grid)
-  int nkb = 1;         // super-blocks per slice
-  int groups = 1;      // workgroups per slice (4 column tiles each)
-  size_t lds = 0;      // dynamic LDS bytes
-  size_t ws_bytes = 0; // partial-sum workspace (0 when ks == 1)
+  int mt = 1;            // 16-row MFMA tiles covering M
+  int KB = 1;            // K / 256
+  int nt = 1;            // 16-column tiles covering N
+  int G = 1;             // workgroups (one per CU)
+  int sk = 1;            // K slices
+  int nkb = 1;           // super-blocks per slice (the last may be shorter)
+  int x_stride = 0;      // LDS bytes per staged activation row
+  int lds_contrib = 0;   // LDS offset of the per-wave contribution slots
+  size_t lds = 0;        // dynamic LDS bytes
+  size_t part_bytes = 0; // slice partials (0 when sk == 1)
+  size_t part_off = 0;   // offset of the slice partials in the workspace (after the counters)
+  size_t ws_bytes = 0;   // workspace bytes (0 when sk == 1)
+  bool ok = false;       // the plan fits the device
 };
 
-GemmPlan gemm_plan(int M, int N, int K);
-hipError_t gemm_launch(const GemmPlan& p, const void* W, const uint16_t* X, float* Y, int M, int N,
-                       int K, void* ws, hipStream_t st);
+GemmPlan gemm_plan(int M, int N, int K, int G);
+hipError_t gemm_launch(const GemmPlan& p, bool tiled, const void* W, const uint16_t* X, float* Y,
+                       int M, int N, int K, void* ws, hipStream_t st);
 
 }  // namespace mk
 

@@ -72,19 +72,7 @@ __device__ __forceinline__ long long ld_dev(const long long* p) {
   return __hip_atomic_load(const_cast<long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// 16-byte device-coherent accesses through a buffer resource (cache policy
-// sc1: the agent-scope coherence level, as for relaxed agent-scope atomics).
-// Offsets past the resource's size read as zero and drop writes.
-constexpr int kCoherent = 16;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-__device__ __forceinline__ floatx4 ld4_dev(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
-}
-__device__ __forceinline__ void st4_dev(__amdgpu_buffer_rsrc_t r, unsigned off, floatx4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCoherent);
-}
+static_assert(STEP_WAVES == SPLIT_WAVES, "the step splits units like the other streaming kernels");
 
 __device__ __forceinline__ bool arrived(const floatx4& v) {
   const u32x4 b = __builtin_bit_cast(u32x4, v);
@@ -98,51 +86,8 @@ __device__ __forceinline__ void set_status(const StepParams& P, int code) {
                                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Which slice and tiles workgroup w owns in a phase, and the split of its
-// (tile, super-block) units over the waves.
-struct Assign {
-  int s;      // K slice
-  int t0;     // first tile
-  int tw;     // tiles
-  int kb0;    // first super-block of the slice
-  int nkb;    // super-blocks in the slice
-  int j, gs;  // index among, and number of, workgroups sharing the slice
-  int U;      // units = tw * nkb
-};
-
-// First workgroup of slice s: the G workgroups are spread over the slices in
-// proportion to their super-blocks, so a short last slice gets fewer of them
-// and every workgroup owns about the same number of (tile, block) units.
-__host__ __device__ inline int slice_start(int s, int sk, int nkb, int KB, int G) {
-  return s >= sk ? G : (int)((long long)G * s * nkb / KB);
-}
-
 __device__ __forceinline__ Assign assign(const DevPhase& ph, int w, int G) {
-  Assign a;
-  int s = 0;
-  while (s + 1 < ph.sk && slice_start(s + 1, ph.sk, ph.nkb, ph.KB, G) <= w) ++s;
-  const int first = slice_start(s, ph.sk, ph.nkb, ph.KB, G);
-  a.s = s;
-  a.j = w - first;
-  a.gs = slice_start(s + 1, ph.sk, ph.nkb, ph.KB, G) - first;
-  a.t0 = (int)((long long)ph.nt * a.j / a.gs);
-  a.tw = (int)((long long)ph.nt * (a.j + 1) / a.gs) - a.t0;
-  a.kb0 = a.s * ph.nkb;
-  a.nkb = min(ph.nkb, ph.KB - a.kb0);
-  a.U = a.tw * a.nkb;
-  return a;
-}
-
-// First unit of wave v's range, and the wave whose range holds unit x (the
-// last wave whose range starts at or before x: waves with an empty range are
-// skipped). No divisions: both run in the per-tile and per-element loops.
-static_assert(STEP_WAVES == 8, "wave ranges are computed with a shift by 3");
-__device__ __forceinline__ int wave_begin(const Assign& a, int v) { return (a.U * v) >> 3; }
-__device__ __forceinline__ int wave_of_unit(const Assign& a, int x) {
-  int w = 0;
-#pragma unroll
-  for (int v = 1; v < STEP_WAVES; ++v) w += ((a.U * v) >> 3) <= x;
-  return w;
+  return assign_split(uni(ph.nt), uni(ph.sk), uni(ph.nkb), uni(ph.KB), w, G);
 }
 
 // The tiles this workgroup finishes: local tile i with (t0 + i) % sk == s,
@@ -156,7 +101,7 @@ __device__ __forceinline__ int fin_count(const Assign& a, int sk) {
 }
 
 __device__ __forceinline__ int seg_of(const DevPhase& ph, int tg) {
-  return (tg >= ph.seg_t0[1]) + (tg >= ph.seg_t0[2]);
+  return (tg >= uni(ph.seg_t0[1])) + (tg >= uni(ph.seg_t0[2]));
 }
 
 // Walks one wave's weight records of a phase: units ua..ub-1 of the
@@ -174,9 +119,10 @@ __device__ __forceinline__ void iter_tile(Iter& it, const DevPhase& ph, WPtrs L,
                                           const Assign& a) {
   const int tg = a.t0 + it.tl;
   const int seg = seg_of(ph, tg);
-  const size_t off = (size_t)(tg - ph.seg_t0[seg]) * ph.KB * TILE_REC;
-  it.base[0] = L[ph.mat0 + seg] + off;
-  it.base[1] = ph.nm == 2 ? L[ph.mat0 + seg + 1] + off : it.base[0];
+  const size_t off = (size_t)(tg - uni(ph.seg_t0[seg])) * uni(ph.KB) * TILE_REC;
+  const int mi = uni(ph.mat0) + seg;
+  it.base[0] = uni(L[mi]) + off;
+  it.base[1] = uni(ph.nm) == 2 ? uni(L[mi + 1]) + off : it.base[0];
 }
 
 __device__ __forceinline__ void iter_init(Iter& it, const DevPhase& ph, WPtrs L,
@@ -196,9 +142,10 @@ __device__ __forceinline__ const uint8_t* iter_addr(const Iter& it, const Assign
 
 __device__ __forceinline__ void iter_next(Iter& it, const DevPhase& ph, WPtrs L,
                                           const Assign& a) {
-  if (++it.q < ph.nm) return;
+  const int nm = uni(ph.nm);
+  if (++it.q < nm) return;
   if (it.u + 1 >= it.ub) {  // stay on the last record
-    it.q = ph.nm - 1;
+    it.q = nm - 1;
     return;
   }
   it.q = 0;
@@ -395,37 +342,6 @@ __device__ __forceinline__ void stage_slice(const void* src, int src_ld, int K, 
   }
 }
 
-// Sub-block sums of the staged activations, split into binary16 hi + lo, for
-// the min-term MFMA: row m, block b, sub-block j at
-// xs_lds + (m * nkb_stride + b) * 32 + 4 * j.
-__device__ __forceinline__ void stage_xsum(int M, int nkb, int nkb_stride, const char* x_lds,
-                                           int x_stride, char* xs_lds, int tid) {
-  const int items = M * nkb * 8;
-  for (int it = tid; it < items; it += STEP_THREADS) {
-    const int j = it & 7;
-    const int rest = it >> 3;
-    const int m = rest / nkb;
-    const int b = rest - m * nkb;
-    const int gq = j >> 1, hb = j & 1;
-    float sum = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(
-          x_lds + (size_t)m * x_stride + b * X_BYTES_PER_BLOCK + gq * 128 + (2 * u + hb) * 16);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const half2v hh = bit_cast_<half2v>(w4[i]);
-        sum += (float)hh.x;
-        sum += (float)hh.y;
-      }
-    }
-    const _Float16 hi = (_Float16)sum;
-    const _Float16 lo = (_Float16)(sum - (float)hi);
-    *reinterpret_cast<half2v*>(xs_lds + ((size_t)m * nkb_stride + b) * XSUM_BYTES_PER_BLOCK +
-                               4 * j) = half2v{hi, lo};
-  }
-}
 
 // Row mean and 1/sqrt(var + 1e-6) of the statistics of (layer, phase) over
 // n columns, into mu_s / inv_s. The STAT_SLOTS slots are integer sums, so the
@@ -718,7 +634,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   const int M = P.M;
   const int w = blockIdx.x;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = uni(tid >> 6), lane = tid & 63;
   const int c = lane & 15, g = lane >> 4;
   const DevLayer* layers = reinterpret_cast<const DevLayer*>(P.ws + P.layers_off);
   {
@@ -766,7 +682,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       }
       ring_fill(ring, it, ph, ltab[l].w, a, lane, STEP_PD_PRE, STEP_PD);
       __syncthreads();
-      stage_xsum(M, a.nkb, ph.nkb, x_lds, ph.x_stride, xs_lds, tid);
+      stage_xsum(M, a.nkb, ph.nkb, x_lds, ph.x_stride, xs_lds, tid, STEP_THREADS);
       __syncthreads();
 
       // ---- stream the weights
@@ -851,23 +767,18 @@ struct StepPlan {
   bool ok = true;  // false: some K slice would get no workgroup
 };
 
-// Host mirror of the device work split (assign / wave_of_unit in the kernel).
+// Host mirror of the device work split (the same shared functions).
 void host_assign(const DevPhase& ph, int w, int G, int* t0, int* tw, int* nkb) {
-  int s = 0;
-  while (s + 1 < ph.sk && slice_start(s + 1, ph.sk, ph.nkb, ph.KB, G) <= w) ++s;
-  const int first = slice_start(s, ph.sk, ph.nkb, ph.KB, G);
-  const int j = w - first;
-  const int gs = slice_start(s + 1, ph.sk, ph.nkb, ph.KB, G) - first;
-  *t0 = (int)((long long)ph.nt * j / gs);
-  *tw = (int)((long long)ph.nt * (j + 1) / gs) - *t0;
-  const int kb0 = s * ph.nkb;
-  *nkb = ph.nkb < ph.KB - kb0 ? ph.nkb : ph.KB - kb0;
+  const Assign a = assign_split(ph.nt, ph.sk, ph.nkb, ph.KB, w, G);
+  *t0 = a.t0;
+  *tw = a.tw;
+  *nkb = a.nkb;
 }
 
 int host_wave_of_unit(int U, int x) {
-  int w = 0;
-  for (int v = 1; v < STEP_WAVES; ++v) w += ((U * v) >> 3) <= x;
-  return w;
+  Assign a = {};
+  a.U = U;
+  return wave_of_unit(a, x);
 }
 
 // Fill the phase table for the shapes of layer 0; sk is chosen so that one

@@ -64,10 +64,15 @@ extern "C" {
  *   X_fp16    [M][K] binary16, row-major, row stride K.
  *   Y_fp32    [M][N] float, row-major, row stride N; fully overwritten.
  *   M         1..64 stacked rows; N >= 1; K >= 256 and K % 256 == 0.
+ * One launch of one workgroup per compute unit; when K is cut into several
+ * slices, the slice partial sums meet in a device workspace and are added in
+ * slice order by whichever workgroup finishes a tile last.
  * Returns MK_OK or MK_EINVAL / MK_EALIGN / MK_ENODEV / MK_EHIP. The library
- * keeps a private device workspace per GPU for K-split partial sums; the first
- * call on a device that needs more than it holds allocates it (hipMalloc,
- * which may synchronise that device); later calls allocate nothing.
+ * keeps a private device workspace per GPU for the K-split partial sums; the
+ * first call on a device that needs more than it holds allocates and zeroes
+ * it (hipMalloc + hipMemset, which synchronise that device); later calls
+ * allocate nothing. Calls that share the library workspace on one GPU must
+ * be ordered (one stream, or synchronised).
  */
 int mk_q4k_gemm(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N, int K,
                 void* stream);
@@ -75,7 +80,10 @@ int mk_q4k_gemm(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int
 /*
  * mk_q4k_gemm_ws: as mk_q4k_gemm with a caller-provided workspace of at least
  * mk_q4k_gemm_workspace_bytes(M, N, K) bytes (16-byte aligned device memory,
- * used by one call at a time). It never allocates.
+ * used by one call at a time, ZERO-FILLED before its first use; every call
+ * leaves its counter region zero-filled again, whatever the shape). It never
+ * allocates. The size depends on the current device's compute-unit count
+ * (256 is assumed when there is none). N may be at most 1048576.
  */
 size_t mk_q4k_gemm_workspace_bytes(int M, int N, int K);
 int mk_q4k_gemm_ws(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N,
@@ -99,6 +107,16 @@ int mk_q4k_gemm_ws(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, 
  */
 size_t mk_q4k_tiles_bytes(int N, int K);
 int mk_q4k_repack(const void* W_rows, void* W_tiles, int N, int K, void* stream);
+
+/*
+ * mk_q4k_gemm_tiled: mk_q4k_gemm on the tile-record form of W (W_tiles, made
+ * once by mk_q4k_repack at load time). Same arguments, results (bit for bit:
+ * the same kernel and arithmetic order), errors and workspace behaviour; the
+ * weight stream reads whole 1 KiB pieces instead of 16-byte pieces of 16
+ * rows.
+ */
+int mk_q4k_gemm_tiled(const void* W_tiles, const uint16_t* X_fp16, float* Y_fp32, int M, int N,
+                      int K, void* stream);
 
 /*
  * The decode-step walk: one persistent kernel launch runs n_layers layers of

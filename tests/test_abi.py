@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("mk_q4k_gemm", "mk_q4k_gemm_ws", "mk_q4k_gemm_workspace_bytes", "mk_q4k_step",
-              "mk_q4k_repack", "mk_q4k_tiles_bytes",
+              "mk_q4k_repack", "mk_q4k_tiles_bytes", "mk_q4k_gemm_tiled",
               "mk_q4k_step_workspace_bytes", "mk_q4k_step_status", "mk_strerror",
               "mk_device_info"):
         assert f in names

@@ -194,7 +194,7 @@ def test_explicit_workspace_matches_owned():
     Wt = torch.from_numpy(W).to(DEV)
     Xt = torch.from_numpy(X).to(DEV)
     nbytes = mk.gemm_workspace_bytes(12, 700, 17408 // 4)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=DEV)
     a = mk.gemm(Wt, Xt).cpu()
     b = mk.gemm(Wt, Xt, workspace=ws).cpu()
     assert torch.equal(a, b)
@@ -208,3 +208,56 @@ def test_misaligned_pointer_rejected():
     with pytest.raises(mk.MkError) as e:
         mk.gemm(Wt, Xmis)
     assert e.value.code == mk.MK_EALIGN
+
+
+# --- the tile-record path (mk_q4k_gemm_tiled) ------------------------------------
+def tiled_pair(W_np, X_np, N):
+    W = torch.from_numpy(np.ascontiguousarray(W_np)).to(DEV)
+    X = torch.from_numpy(np.ascontiguousarray(X_np)).to(DEV)
+    Wt = mk.repack(W, N, X_np.shape[1])
+    y_rows = mk.gemm(W, X)
+    y_tiles = mk.gemm_tiled(Wt, X, N)
+    torch.cuda.synchronize()
+    return y_rows.cpu().numpy(), y_tiles.cpu().numpy()
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 256, 1024), (12, 333, 2048), (16, 17408 // 8, 5120), (33, 100, 1536), (64, 257, 1024),
+    (5, 5120 // 4, 17408),
+])
+def test_tiled_bitwise_equal_to_rows_and_in_bound(M, N, K):
+    W, X = inputs(N, K, M, tag=40 + M)
+    y_rows, y_tiles = tiled_pair(W, X, N)
+    assert np.array_equal(y_rows.view(np.uint32), y_tiles.view(np.uint32))
+    check(W, X, Y=y_tiles)
+
+
+def test_tiled_gate_up_m12_sampled():
+    N, K, M = 17408, 5120, 12
+    W, X = inputs(N, K, M, tag=50)
+    _, y = tiled_pair(W, X, N)
+    cols = np.unique(np.random.default_rng(5).choice(N, 2048, replace=False))
+    check(W, X, cols=cols, Y=y)
+
+
+def test_tiled_down_m16_sampled():
+    N, K, M = 5120, 17408, 16
+    W, X = inputs(N, K, M, tag=51)
+    _, y = tiled_pair(W, X, N)
+    cols = np.unique(np.concatenate([np.random.default_rng(6).choice(N, 1024, replace=False),
+                                     [0, N - 1]]))
+    check(W, X, cols=cols, Y=y)
+
+
+def test_interleaved_shapes_keep_the_workspace_consistent():
+    """Calls of different shapes (each splitting K) share the library
+    workspace; every call must leave its counters ready for the next one."""
+    a = inputs(300, 17408, 12, tag=60)
+    b = inputs(500, 8192, 4, tag=61)
+    ya = run_gpu(*a)
+    yb = run_gpu(*b)
+    ya2 = run_gpu(*a)
+    yb2 = run_gpu(*b)
+    assert np.array_equal(ya, ya2) and np.array_equal(yb, yb2)
+    check(*a, Y=ya)
+    check(*b, Y=yb)
