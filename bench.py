@@ -222,6 +222,8 @@ def main() -> int:
     ap.add_argument("--no-gemm", action="store_true", help="skip the single-matrix GEMM lines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB copies (scale for the PMC byte counters)")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="only the single-matrix GEMM lines (no 64-layer stack)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -237,6 +239,11 @@ def main() -> int:
     import torch
     import bit_weight_streaming_amd as mk
     from synth.stack import Stack
+
+    if args.gemm_only:
+        torch.cuda.set_device(0)
+        print(json.dumps({"gemm": gemm_bench(args.seed)}), flush=True)
+        return 0
 
     dev = "cuda:0"
     torch.cuda.set_device(0)

@@ -24,9 +24,15 @@ constexpr int STEP_MAX_M = 16;   // rows the walk supports (one MFMA row tile)
 constexpr double STAT_SCALE_SUM = 268435456.0;
 constexpr double STAT_SCALE_SQ = 1048576.0;
 
-// Bit pattern of a slice partial that has not arrived yet: a signalling NaN,
-// which floating-point arithmetic never produces (its NaN results are quiet).
-constexpr uint32_t PART_EMPTY = 0x7FBADBADu;
+// A slice partial carries the parity of its layer in the lowest bit of each
+// word: the producer sets it, the finisher waits until every word of a piece
+// shows the layer's parity and clears the bit before adding (a change of at
+// most one unit in the last place of a partial; a zero partial stays zero).
+// Every piece of a phase is rewritten in every layer, so a piece still
+// holding the previous layer's value always shows the other parity. Before a
+// step all pieces are filled with PART_FILL, whose parity is 1 (layer 0
+// expects 0).
+constexpr uint32_t PART_FILL = 1u;
 
 // One phase of a layer (the same for every layer).
 struct DevPhase {

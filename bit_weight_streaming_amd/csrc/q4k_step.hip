@@ -74,9 +74,20 @@ __device__ __forceinline__ long long ld_dev(const long long* p) {
 
 static_assert(STEP_WAVES == SPLIT_WAVES, "the step splits units like the other streaming kernels");
 
-__device__ __forceinline__ bool arrived(const floatx4& v) {
+// Slice-partial words tagged with a layer parity (see PART_FILL).
+__device__ __forceinline__ floatx4 tag_parity(const floatx4& v, unsigned par) {
   const u32x4 b = __builtin_bit_cast(u32x4, v);
-  return b.x != PART_EMPTY && b.y != PART_EMPTY && b.z != PART_EMPTY && b.w != PART_EMPTY;
+  return __builtin_bit_cast(floatx4, u32x4{(b.x & ~1u) | par, (b.y & ~1u) | par,
+                                           (b.z & ~1u) | par, (b.w & ~1u) | par});
+}
+__device__ __forceinline__ floatx4 untag(const floatx4& v) {
+  const u32x4 b = __builtin_bit_cast(u32x4, v);
+  return __builtin_bit_cast(floatx4, u32x4{b.x & ~1u, b.y & ~1u, b.z & ~1u, b.w & ~1u});
+}
+__device__ __forceinline__ bool arrived(const floatx4& v, unsigned par) {
+  const u32x4 b = __builtin_bit_cast(u32x4, v);
+  return ((b.x & 1u) == par) && ((b.y & 1u) == par) && ((b.z & 1u) == par) &&
+         ((b.w & 1u) == par);
 }
 
 __device__ __forceinline__ void set_status(const StepParams& P, int code) {
@@ -182,6 +193,7 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
                                               const Assign& a, int wave, int lane,
                                               const char* xa_lane, const char* xs_lane,
                                               char* contrib, __amdgpu_buffer_rsrc_t pr,
+                                              unsigned par, bool rows_ok,
                                               const UnpackConsts& k) {
   const int g = lane >> 4;
   const int ua = wave_begin(a, wave), ub = wave_begin(a, wave + 1);
@@ -200,7 +212,7 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
       const unsigned off = ((unsigned)((a.t0 + ctl) * ph.sk + a.s) * NM) * 1024u + lane * 16;
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
-        st4_dev(pr, off + q * 1024u, acc[q]);
+        if (rows_ok) st4_dev(pr, off + q * 1024u, tag_parity(acc[q], par));
         acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
     } else {
@@ -429,15 +441,15 @@ __device__ __forceinline__ bool wait_done(const StepParams& P, const DevPhase* P
 // each (tile, row) are summed over the tile's 16 columns in fp32 (fixed
 // order), rounded to fixed point, added in LDS as integers and sent with one
 // atomic per (row, sum).
-// Reload a slice partial piece until every one of its words has been written
-// (no word still holds PART_EMPTY; each word is written once, so a piece with
-// no empty word is complete). Gives up when another workgroup has recorded a
-// failure or the wall-clock limit passes.
+// Reload a slice partial piece until every one of its words carries this
+// layer's parity (each word is written once per layer, so such a piece is
+// complete). Gives up when another workgroup has recorded a failure or the
+// wall-clock limit passes.
 __device__ __forceinline__ floatx4 await_piece(const StepParams& P, __amdgpu_buffer_rsrc_t pr,
-                                               unsigned off, floatx4 v, unsigned long long t0,
-                                               int* abort_s) {
+                                               unsigned off, floatx4 v, unsigned par,
+                                               unsigned long long t0, int* abort_s) {
   int n = 0;
-  while (!arrived(v)) {
+  while (!arrived(v, par)) {
     __builtin_amdgcn_s_sleep(1);
     v = ld4_dev(pr, off);
     if ((++n & 63) == 0) {
@@ -515,8 +527,7 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
   long long* stl = reinterpret_cast<long long*>(P.ws + P.stats_off) +
                    (size_t)(l * 4 + p) * STAT_SLOTS * M * 2;
   const int tasks = nfin * 64;
-  const floatx4 empty = __builtin_bit_cast(floatx4, u32x4{PART_EMPTY, PART_EMPTY, PART_EMPTY,
-                                                          PART_EMPTY});
+  const unsigned par = (unsigned)l & 1u;
   const unsigned long long t0 = wall_clock64();
   for (int t = tid; t < tasks; t += 2 * STEP_THREADS) {  // uniform per wave
     const bool two = t + STEP_THREADS < tasks;            // uniform per wave
@@ -526,6 +537,7 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
     const int tg1 = two ? f0 + ((t + STEP_THREADS) >> 6) * ph.sk : tg0;
     const unsigned base0 = (unsigned)tg0 * ph.sk * NM * 1024u + ln * 16;
     const unsigned base1 = (unsigned)tg1 * ph.sk * NM * 1024u + ln * 16;
+    const bool rows_ok = 4 * (ln >> 4) < M;  // lanes holding only rows past M skip
     floatx4 y0[NM], y1[NM];
 #pragma unroll
     for (int q = 0; q < NM; ++q) y0[q] = y1[q] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -535,24 +547,19 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < NM; ++q)
-          if (s0 + i < ph.sk) {
+          if (s0 + i < ph.sk && rows_ok) {
             v0[i][q] = ld4_dev(pr, base0 + ((s0 + i) * NM + q) * 1024u);
             if (two) v1[i][q] = ld4_dev(pr, base1 + ((s0 + i) * NM + q) * 1024u);
           }
-      // wait for late slices, add in slice order, mark the pieces empty again
-      // for the same phase of the next layer
+      // wait for late slices and add in slice order
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < NM; ++q)
-          if (s0 + i < ph.sk) {
+          if (s0 + i < ph.sk && rows_ok) {
             const unsigned o = ((s0 + i) * NM + q) * 1024u;
-            y0[q] += await_piece(P, pr, base0 + o, v0[i][q], t0, abort_s);
-            st4_dev(pr, base0 + o, empty);
-            if (two) {
-              y1[q] += await_piece(P, pr, base1 + o, v1[i][q], t0, abort_s);
-              st4_dev(pr, base1 + o, empty);
-            }
+            y0[q] += untag(await_piece(P, pr, base0 + o, v0[i][q], par, t0, abort_s));
+            if (two) y1[q] += untag(await_piece(P, pr, base1 + o, v1[i][q], par, t0, abort_s));
           }
     }
     fixup_finish<NM>(P, ph, p, L, tg0, ln, y0, consb, wst);
@@ -603,7 +610,9 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
           contrib + ((size_t)(tl * ph.cmax + kk) * NM + q) * 1024 + ln * 16);
       v += u;
     }
-    st4_dev(pr, ((unsigned)(tg * ph.sk + a.s) * NM + q) * 1024u + ln * 16, v);
+    if (4 * (ln >> 4) < P.M)
+      st4_dev(pr, ((unsigned)(tg * ph.sk + a.s) * NM + q) * 1024u + ln * 16,
+              tag_parity(v, (unsigned)l & 1u));
   }
   if (tid == 0) *abort_s = 0;
   __syncthreads();
@@ -690,9 +699,11 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       const char* xs_lane = xs_lds + (size_t)arow * ph.nkb * XSUM_BYTES_PER_BLOCK + 8 * g;
       const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
       if (ph.nm == 2)
-        phase_compute<2>(ring, it, ph, ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, pr, k);
+        phase_compute<2>(ring, it, ph, ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, pr,
+                         (unsigned)l & 1u, 4 * g < M, k);
       else
-        phase_compute<1>(ring, it, ph, ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, pr, k);
+        phase_compute<1>(ring, it, ph, ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, pr,
+                         (unsigned)l & 1u, 4 * g < M, k);
       __syncthreads();
 
       // ---- finish tiles, start the next phase's weight stream, wait until
@@ -730,8 +741,8 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   }
 }
 
-// Zero the counters, status word and statistics, and mark every slice
-// partial piece empty.
+// Zero the counters, status word and statistics, and fill every slice
+// partial piece with words of parity 1 (not yet written in layer 0).
 __global__ void __launch_bounds__(256) q4k_step_clear(uint32_t* p, size_t n, uint32_t* part,
                                                       size_t npart) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -739,7 +750,7 @@ __global__ void __launch_bounds__(256) q4k_step_clear(uint32_t* p, size_t n, uin
     p[i] = 0u;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < npart;
        i += (size_t)gridDim.x * blockDim.x)
-    part[i] = PART_EMPTY;
+    part[i] = PART_FILL;
 }
 
 }  // namespace mk
