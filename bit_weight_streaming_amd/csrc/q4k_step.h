@@ -11,7 +11,6 @@ namespace mk {
 constexpr int STEP_WAVES = 8;
 constexpr int STEP_THREADS = 64 * STEP_WAVES;
 constexpr int STEP_PD = 4;       // weight records in flight per wave (more spills registers)
-constexpr int STEP_PD_PRE = 4;   // of which issued before a phase's input is ready
 constexpr int STEP_MAX_LAYERS = 128;
 constexpr int STAT_SLOTS = 64;   // spread of the row-statistic atomics
 constexpr int DONE_CTRS = 64;    // spread of the finished-tile counters
@@ -70,7 +69,7 @@ struct DevLayer {
 };
 
 struct StepParams {
-  size_t phases_off;     // DevPhase[4] table in the workspace
+  DevPhase ph[4];        // the four phases (kernel arguments: read through the scalar cache)
   int n_layers;
   int M;
   int G;                 // workgroups (one per CU)

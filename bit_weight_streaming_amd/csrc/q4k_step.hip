@@ -73,6 +73,29 @@ __device__ __forceinline__ long long ld_dev(const long long* p) {
 }
 
 static_assert(STEP_WAVES == SPLIT_WAVES, "the step splits units like the other streaming kernels");
+static_assert(STEP_PD % 2 == 0, "gate and up records take ring slots in pairs");
+
+// The value of another lane of the same 16-lane row (DPP control CTRL: a
+// quad permutation, or a rotation of the row).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                            0xF, 0xF, false));
+}
+constexpr int kQuadSwap1 = 0xB1;  // quad lanes 1,0,3,2
+constexpr int kQuadSwap2 = 0x4E;  // quad lanes 2,3,0,1
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
+
+// Sum over the 16 lanes of a row, the same in every lane of it (each step
+// adds the same two operands in every lane, in either order).
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_mov<kRowRor8>(v);
+  v += dpp_mov<kRowRor4>(v);
+  v += dpp_mov<kQuadSwap2>(v);
+  v += dpp_mov<kQuadSwap1>(v);
+  return v;
+}
 
 // Slice-partial words tagged with a layer parity (see PART_FILL).
 __device__ __forceinline__ floatx4 tag_parity(const floatx4& v, unsigned par) {
@@ -97,19 +120,20 @@ __device__ __forceinline__ void set_status(const StepParams& P, int code) {
                                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ Assign assign(const DevPhase& ph, int w, int G) {
-  return assign_split(uni(ph.nt), uni(ph.sk), uni(ph.nkb), uni(ph.KB), w, G);
+// A work split held in LDS, read into wave-uniform registers.
+__device__ __forceinline__ Assign lds_assign(const Assign& x) {
+  Assign a;
+  a.s = uni(x.s);
+  a.t0 = uni(x.t0);
+  a.tw = uni(x.tw);
+  a.kb0 = uni(x.kb0);
+  a.nkb = uni(x.nkb);
+  a.j = uni(x.j);
+  a.gs = uni(x.gs);
+  a.U = uni(x.U);
+  return a;
 }
 
-// The tiles this workgroup finishes: local tile i with (t0 + i) % sk == s,
-// i.e. i = fin_first + j * sk for j < fin_count.
-__device__ __forceinline__ int fin_first(const Assign& a, int sk) {
-  return ((a.s - a.t0) % sk + sk) % sk;
-}
-__device__ __forceinline__ int fin_count(const Assign& a, int sk) {
-  const int i0 = fin_first(a, sk);
-  return i0 < a.tw ? (a.tw - 1 - i0) / sk + 1 : 0;
-}
 
 __device__ __forceinline__ int seg_of(const DevPhase& ph, int tg) {
   return (tg >= uni(ph.seg_t0[1])) + (tg >= uni(ph.seg_t0[2]));
@@ -118,9 +142,14 @@ __device__ __forceinline__ int seg_of(const DevPhase& ph, int tg) {
 // Walks one wave's weight records of a phase: units ua..ub-1 of the
 // workgroup (unit u = tile u / nkb, super-block u % nkb), nm records per unit.
 // Past the end it keeps pointing at the last record (re-read, never used).
+// Moving to the next tile of the same matrix adds a stride; only crossing
+// into the next column segment (phase A: q -> k -> v) looks the pointers up.
 struct Iter {
-  int u, ub, tl, b, q;
-  const uint8_t* base[2];
+  int u, ub, b, q;
+  int tg;       // tile (phase numbering)
+  int seg_end;  // first tile of the next segment
+  unsigned stride;  // bytes from one tile's records to the next
+  const uint8_t* base[2];  // record (tg, super-block a.kb0) of each matrix
 };
 
 // The 7 weight pointers of one layer (an LDS copy of the layer table).
@@ -128,27 +157,35 @@ typedef const uint8_t* const* WPtrs;
 
 __device__ __forceinline__ void iter_tile(Iter& it, const DevPhase& ph, WPtrs L,
                                           const Assign& a) {
-  const int tg = a.t0 + it.tl;
-  const int seg = seg_of(ph, tg);
-  const size_t off = (size_t)(tg - uni(ph.seg_t0[seg])) * uni(ph.KB) * TILE_REC;
+  const int seg = seg_of(ph, it.tg);
+  const size_t off = (size_t)(it.tg - uni(ph.seg_t0[seg])) * it.stride +
+                     (size_t)a.kb0 * TILE_REC;
   const int mi = uni(ph.mat0) + seg;
+  it.seg_end = uni(ph.seg_t0[seg + 1]);
   it.base[0] = uni(L[mi]) + off;
   it.base[1] = uni(ph.nm) == 2 ? uni(L[mi + 1]) + off : it.base[0];
 }
 
+// Start of a wave's walk from st = (first unit, end unit, tile, super-block)
+// and sp = (matrix of that tile, record offset, first tile of the next
+// segment), all computed once per launch.
 __device__ __forceinline__ void iter_init(Iter& it, const DevPhase& ph, WPtrs L,
-                                          const Assign& a, int wave) {
-  it.u = wave_begin(a, wave);
-  it.ub = wave_begin(a, wave + 1);
+                                          const int4& st, const int4& sp) {
+  it.u = uni(st.x);
+  it.ub = uni(st.y);
   it.q = 0;
-  it.tl = a.nkb > 0 ? it.u / a.nkb : 0;
-  it.b = a.nkb > 0 ? it.u - it.tl * a.nkb : 0;
-  it.base[0] = it.base[1] = nullptr;
-  if (it.u < it.ub) iter_tile(it, ph, L, a);
+  it.tg = uni(st.z);
+  it.b = uni(st.w);
+  it.stride = (unsigned)uni(ph.KB) * TILE_REC;
+  it.seg_end = uni(sp.z);
+  const int mi = uni(sp.x);
+  const unsigned off = (unsigned)uni(sp.y);
+  it.base[0] = uni(L[mi]) + off;
+  it.base[1] = uni(ph.nm) == 2 ? uni(L[mi + 1]) + off : it.base[0];
 }
 
-__device__ __forceinline__ const uint8_t* iter_addr(const Iter& it, const Assign& a) {
-  return (it.q ? it.base[1] : it.base[0]) + (size_t)(a.kb0 + it.b) * TILE_REC;
+__device__ __forceinline__ const uint8_t* iter_addr(const Iter& it) {
+  return (it.q ? it.base[1] : it.base[0]) + (unsigned)it.b * TILE_REC;
 }
 
 __device__ __forceinline__ void iter_next(Iter& it, const DevPhase& ph, WPtrs L,
@@ -163,19 +200,24 @@ __device__ __forceinline__ void iter_next(Iter& it, const DevPhase& ph, WPtrs L,
   ++it.u;
   if (++it.b < a.nkb) return;
   it.b = 0;
-  ++it.tl;
-  iter_tile(it, ph, L, a);
+  if (++it.tg < it.seg_end) {
+    it.base[0] += it.stride;
+    it.base[1] += it.stride;
+  } else {
+    iter_tile(it, ph, L, a);
+  }
 }
 
-// Issue ring slots [s0, s1) of a phase's first STEP_PD weight records.
+// Issue a phase's first STEP_PD weight records of the wave (fewer if the
+// wave has fewer) into ring slots 0.., before the phase's input is ready.
 __device__ __forceinline__ void ring_fill(BlockRegs (&ring)[STEP_PD], Iter& it,
-                                          const DevPhase& ph, WPtrs L, const Assign& a, int lane,
-                                          int s0, int s1) {
-  if (it.u >= it.ub) return;
+                                          const DevPhase& ph, WPtrs L, const Assign& a,
+                                          int lane) {
+  const int nrec = (it.ub - it.u) * uni(ph.nm);
 #pragma unroll
   for (int s = 0; s < STEP_PD; ++s) {
-    if (s >= s0 && s < s1) {
-      load_rec(ring[s], iter_addr(it, a), lane);
+    if (s < nrec) {
+      load_rec(ring[s], iter_addr(it), lane);
       iter_next(it, ph, L, a);
     }
   }
@@ -236,124 +278,172 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
       }
     }
   };
-  int r = 0;
-  for (; r + STEP_PD <= U; r += STEP_PD) {
+  // record r sits in ring slot r % STEP_PD; once consumed, its slot takes
+  // record r + STEP_PD, if the wave has one (no load past the range)
+  for (int r0 = 0; r0 < U; r0 += STEP_PD) {
 #pragma unroll
     for (int s = 0; s < STEP_PD; s += NM) {
+      if (r0 + s >= U) break;
       consume(s);
+      if (r0 + s + STEP_PD < U) {
 #pragma unroll
-      for (int q = 0; q < NM; ++q) {
-        load_rec(ring[s + q], iter_addr(it, a), lane);
-        iter_next(it, ph, L, a);
+        for (int q = 0; q < NM; ++q) {
+          load_rec(ring[s + q], iter_addr(it), lane);
+          iter_next(it, ph, L, a);
+        }
       }
     }
   }
-#pragma unroll
-  for (int s = 0; s < STEP_PD; s += NM)
-    if (r + s < U) consume(s);
 }
 
 // Stage the activations of slice a into LDS in the MFMA order (see
-// q4k_device.h) and, from workgroup a.j of the slice group, the matching
-// chunks of the binary16 phase input io_x ([M][K], natural order).
+// q4k_device.h), with the sub-block sums the min term multiplies (each split
+// into binary16 hi + lo), and, from workgroup a.j of the slice group, the
+// matching chunks of the binary16 phase input io_x ([M][K], natural order).
 //   F16_SRC: src is binary16 [M][K] (the layer-0 input), copied as is.
 //   otherwise: src is fp32 [M][src_ld]; the value staged is
 //              binary16((y - mean_m) / sqrt(var_m + 1e-6)) (round to nearest
 //              even), mean and variance from the integer statistics at st
-//              (STAT_SLOTS slots of [M][2]) over stat_n columns. The first
-//              round of activation loads and the statistics loads are issued
-//              together; the slot totals are added with integer LDS atomics,
-//              so their order does not matter.
-// Each thread loads up to kStageRound 8-wide chunks per round.
-template <bool F16_SRC>
-__device__ __forceinline__ void stage_slice(const void* src, int src_ld, int K, int M,
+//              (STAT_SLOTS slots of [M][2]) over stat_n columns. The
+//              statistics loads are issued before the activation loads, so
+//              their reduction (integer LDS atomics into tot_s, which the
+//              caller has cleared: the order of the additions does not
+//              matter) runs while the activations are still in flight.
+// Each thread loads up to kStageRound 8-wide chunks, all in one round. The
+// four chunks of one 32-value sub-block sit in four consecutive lanes, which
+// add their fp32 chunk sums with two lane exchanges.
+template <bool F16_SRC, int R>
+__device__ __forceinline__ void stage_rounds(const void* src, int src_ld, int K, int M,
                                             const Assign& a, const long long* st, int stat_n,
                                             unsigned long long* tot_s, float* mu_s, float* inv_s,
-                                            char* x_lds, int x_stride, uint16_t* io_x, int tid) {
+                                            char* x_lds, int x_stride, char* xs_lds,
+                                            int xs_stride, uint16_t* io_x, int tid) {
   const int cpr = a.nkb * 32;  // 8-wide chunks per row
-  const int items = M * cpr;
-  if (!F16_SRC && tid < 2 * M) tot_s[tid] = 0ull;
-  for (int base = 0; base < items; base += STEP_THREADS * kStageRound) {
-    floatx4 v0[kStageRound], v1[kStageRound];
-    u32x4 hv[kStageRound];
+  const int items = M * cpr;   // at most STEP_THREADS * R
+  const int nv = STAT_SLOTS * M * 2;  // a multiple of 64
+  // row of chunk index x < 2^16: x * magic / 2^32 (cpr < 2^16)
+  const unsigned magic = 0xFFFFFFFFu / (unsigned)cpr + 1u;
+  // chunks of each row this workgroup writes to io_x: [io_lo, io_hi)
+  const int io_lo = cpr * a.j / a.gs, io_hi = cpr * (a.j + 1) / a.gs;
+  // Every load is unconditional (indices clamped to the last valid one), so
+  // they issue back to back and the wait for the statistics, issued first,
+  // leaves the activation loads in flight.
+  long long pv[kStatPer];
+  if (!F16_SRC) {
 #pragma unroll
-    for (int i = 0; i < kStageRound; ++i) {
-      const int it = base + i * STEP_THREADS + tid;
-      if (it < items) {
-        const int m = it / cpr;
-        const int ch = it - m * cpr;
-        const int k = (a.kb0 + (ch >> 5)) * QK + (ch & 31) * 8;
-        if (F16_SRC) {
-          hv[i] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) +
-                                                  (size_t)m * K + k);
-        } else {
-          const float* s = static_cast<const float*>(src) + (size_t)m * src_ld + k;
-          v0[i] = *reinterpret_cast<const floatx4*>(s);
-          v1[i] = *reinterpret_cast<const floatx4*>(s + 4);
-        }
-      }
+    for (int i = 0; i < kStatPer; ++i) pv[i] = ld_dev(st + min(i * STEP_THREADS + tid, nv - 1));
+  }
+  floatx4 v0[R], v1[R];
+  u32x4 hv[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int it = min(i * STEP_THREADS + tid, items - 1);
+    const int m = __umulhi((unsigned)it, magic);
+    const int ch = it - m * cpr;
+    const int k = (a.kb0 + (ch >> 5)) * QK + (ch & 31) * 8;
+    if (F16_SRC) {
+      hv[i] = *to_global(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) +
+                                                        (size_t)m * K + k));
+    } else {
+      const float* s = static_cast<const float*>(src) + (size_t)m * src_ld + k;
+      v0[i] = *to_global(reinterpret_cast<const floatx4*>(s));
+      v1[i] = *to_global(reinterpret_cast<const floatx4*>(s + 4));
     }
-    if (!F16_SRC && base == 0) {
-      // statistics of the producer: up to kStatPer slot values per thread
-      const int nv = STAT_SLOTS * M * 2;
-      long long pv[kStatPer];
+  }
+  if (!F16_SRC) {
 #pragma unroll
-      for (int i = 0; i < kStatPer; ++i) {
-        const int e = tid + i * STEP_THREADS;
-        pv[i] = e < nv ? ld_dev(st + e) : 0;
-      }
-      __syncthreads();  // tot_s cleared
-#pragma unroll
-      for (int i = 0; i < kStatPer; ++i) {
-        const int e = tid + i * STEP_THREADS;
-        if (e < nv) atomicAdd(&tot_s[e % (2 * M)], (unsigned long long)pv[i]);
-      }
-      __syncthreads();
-      if (tid < M) {
-        const double mean = (double)(long long)tot_s[2 * tid] / STAT_SCALE_SUM / stat_n;
-        const double e2 = (double)(long long)tot_s[2 * tid + 1] / STAT_SCALE_SQ / stat_n;
-        double var = e2 - mean * mean;
-        if (var < 0.0) var = 0.0;
-        mu_s[tid] = (float)mean;
-        inv_s[tid] = (float)(1.0 / sqrt(var + 1e-6));
-      }
-      __syncthreads();
+    for (int i = 0; i < kStatPer; ++i)
+      if (i * STEP_THREADS + uni(tid & ~63) < nv)
+        atomicAdd(&tot_s[(i * STEP_THREADS + tid) % (2 * M)], (unsigned long long)pv[i]);
+    __syncthreads();
+    if (tid < M) {
+      const double mean = (double)(long long)tot_s[2 * tid] / STAT_SCALE_SUM / stat_n;
+      const double e2 = (double)(long long)tot_s[2 * tid + 1] / STAT_SCALE_SQ / stat_n;
+      double var = e2 - mean * mean;
+      if (var < 0.0) var = 0.0;
+      mu_s[tid] = (float)mean;
+      inv_s[tid] = (float)(1.0 / sqrt(var + 1e-6));
     }
+    __syncthreads();
+  }
+  const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int i = 0; i < kStageRound; ++i) {
-      const int it = base + i * STEP_THREADS + tid;
-      if (it >= items) continue;
-      const int m = it / cpr;
-      const int ch = it - m * cpr;
-      const int b = ch >> 5;
-      const int kk = (ch & 31) * 8;
-      const int k = (a.kb0 + b) * QK + kk;
-      u32x4 h;
-      if (F16_SRC) {
-        h = hv[i];
-      } else {
-        const float mm = mu_s[m], iv = inv_s[m];
-        const half2v p0 = {(_Float16)((v0[i].x - mm) * iv), (_Float16)((v0[i].y - mm) * iv)};
-        const half2v p1 = {(_Float16)((v0[i].z - mm) * iv), (_Float16)((v0[i].w - mm) * iv)};
-        const half2v p2 = {(_Float16)((v1[i].x - mm) * iv), (_Float16)((v1[i].y - mm) * iv)};
-        const half2v p3 = {(_Float16)((v1[i].z - mm) * iv), (_Float16)((v1[i].w - mm) * iv)};
-        h = u32x4{bit_cast_<uint32_t>(p0), bit_cast_<uint32_t>(p1), bit_cast_<uint32_t>(p2),
-                  bit_cast_<uint32_t>(p3)};
-      }
-      if (io_x && (ch % a.gs) == a.j)
-        *to_global(reinterpret_cast<u32x4*>(io_x + (size_t)m * K + k)) = h;
-      u32x4 o;  // element order 0,2,1,3,4,6,5,7
-      o.x = (h.x & 0xFFFFu) | (h.y << 16);
-      o.y = (h.x >> 16) | (h.y & 0xFFFF0000u);
-      o.z = (h.z & 0xFFFFu) | (h.w << 16);
-      o.w = (h.z >> 16) | (h.w & 0xFFFF0000u);
-      const int gq = kk >> 6, hb = (kk >> 5) & 1, u = (kk >> 3) & 3;
-      *reinterpret_cast<u32x4*>(x_lds + (size_t)m * x_stride + b * X_BYTES_PER_BLOCK + gq * 128 +
-                                (2 * u + hb) * 16) = o;
+  for (int i = 0; i < R; ++i) {
+    if (i * STEP_THREADS + uni(tid & ~63) >= items) continue;
+    const int it = i * STEP_THREADS + tid;
+    const bool ok = it < items;  // the same for the four lanes of a sub-block
+    const int m = __umulhi((unsigned)(ok ? it : items - 1), magic);
+    const int ch = (ok ? it : items - 1) - m * cpr;
+    const int b = ch >> 5;
+    const int kk = (ch & 31) * 8;
+    u32x4 h;
+    if (F16_SRC) {
+      h = hv[i];
+    } else {
+      // (y - mean) * inv as one fused step: y * inv + (-mean * inv)
+      const float iv = inv_s[m], nb = -mu_s[m] * iv;
+      const half2v p0 = {(_Float16)__builtin_fmaf(v0[i].x, iv, nb),
+                         (_Float16)__builtin_fmaf(v0[i].y, iv, nb)};
+      const half2v p1 = {(_Float16)__builtin_fmaf(v0[i].z, iv, nb),
+                         (_Float16)__builtin_fmaf(v0[i].w, iv, nb)};
+      const half2v p2 = {(_Float16)__builtin_fmaf(v1[i].x, iv, nb),
+                         (_Float16)__builtin_fmaf(v1[i].y, iv, nb)};
+      const half2v p3 = {(_Float16)__builtin_fmaf(v1[i].z, iv, nb),
+                         (_Float16)__builtin_fmaf(v1[i].w, iv, nb)};
+      h = u32x4{bit_cast_<uint32_t>(p0), bit_cast_<uint32_t>(p1), bit_cast_<uint32_t>(p2),
+                bit_cast_<uint32_t>(p3)};
+    }
+    // fp32 sum of the chunk's 8 values (pairwise dot products with 1), then
+    // of the sub-block's 4 chunks
+    float sum = __builtin_amdgcn_fdot2(bit_cast_<half2v>(h.x), one2, 0.f, false);
+    sum = __builtin_amdgcn_fdot2(bit_cast_<half2v>(h.y), one2, sum, false);
+    sum = __builtin_amdgcn_fdot2(bit_cast_<half2v>(h.z), one2, sum, false);
+    sum = __builtin_amdgcn_fdot2(bit_cast_<half2v>(h.w), one2, sum, false);
+    sum += dpp_mov<kQuadSwap1>(sum);
+    sum += dpp_mov<kQuadSwap2>(sum);
+    if (!ok) continue;
+    if (io_x && ch >= io_lo && ch < io_hi)
+      *to_global(reinterpret_cast<u32x4*>(io_x + (size_t)m * K + (a.kb0 + b) * QK + kk)) = h;
+    u32x4 o;  // element order 0,2,1,3,4,6,5,7
+    o.x = (h.x & 0xFFFFu) | (h.y << 16);
+    o.y = (h.x >> 16) | (h.y & 0xFFFF0000u);
+    o.z = (h.z & 0xFFFFu) | (h.w << 16);
+    o.w = (h.z >> 16) | (h.w & 0xFFFF0000u);
+    const int gq = kk >> 6, hb = (kk >> 5) & 1, u = (kk >> 3) & 3;
+    *reinterpret_cast<u32x4*>(x_lds + (size_t)m * x_stride + b * X_BYTES_PER_BLOCK + gq * 128 +
+                              (2 * u + hb) * 16) = o;
+    if ((ch & 3) == 0) {
+      const _Float16 hi = (_Float16)sum;
+      const _Float16 lo = (_Float16)(sum - (float)hi);
+      *reinterpret_cast<half2v*>(xs_lds + ((size_t)m * xs_stride + b) * XSUM_BYTES_PER_BLOCK +
+                                 4 * (kk >> 5)) = half2v{hi, lo};
     }
   }
 }
 
+
+// Staging with the number of load rounds the slice needs (one per
+// STEP_THREADS chunks; the host plan keeps it at most kStageRound), so that
+// every issued load is a useful one.
+template <bool F16_SRC>
+__device__ __forceinline__ void stage_slice(const void* src, int src_ld, int K, int M,
+                                            const Assign& a, const long long* st, int stat_n,
+                                            unsigned long long* tot_s, float* mu_s, float* inv_s,
+                                            char* x_lds, int x_stride, char* xs_lds,
+                                            int xs_stride, uint16_t* io_x, int tid) {
+  static_assert(kStageRound == 7, "one instantiation per round count");
+  const int r = uni((M * a.nkb * 32 + STEP_THREADS - 1) / STEP_THREADS);
+#define MK_STAGE(RR)                                                                         \
+  stage_rounds<F16_SRC, RR>(src, src_ld, K, M, a, st, stat_n, tot_s, mu_s, inv_s, x_lds,    \
+                            x_stride, xs_lds, xs_stride, io_x, tid)
+  if (F16_SRC || r > 5) MK_STAGE(7);
+  else if (r > 4) MK_STAGE(5);
+  else if (r > 3) MK_STAGE(4);
+  else if (r > 2) MK_STAGE(3);
+  else if (r > 1) MK_STAGE(2);
+  else MK_STAGE(1);
+#undef MK_STAGE
+}
 
 // Row mean and 1/sqrt(var + 1e-6) of the statistics of (layer, phase) over
 // n columns, into mu_s / inv_s. The STAT_SLOTS slots are integer sums, so the
@@ -495,12 +585,10 @@ __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase
     s2[r] = cv * cv;
   }
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s1[r] += __shfl_xor(s1[r], off, 16);
-      s2[r] += __shfl_xor(s2[r], off, 16);
-    }
+  for (int r = 0; r < 4; ++r) {
+    s1[r] = row_sum16(s1[r]);
+    s2[r] = row_sum16(s2[r]);
+  }
   if (has_cons && (ln & 15) == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -519,8 +607,9 @@ __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase
 
 template <int NM>
 __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase& ph, int p, int l,
-                                            const DevLayer* L, const Assign& a, int nfin,
-                                            unsigned long long* wst, int* abort_s, int tid) {
+                                            const DevLayer* L, const Assign& a, int ffirst,
+                                            int nfin, unsigned long long* wst, int* abort_s,
+                                            int tid) {
   const int M = P.M;
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
   float* consb = reinterpret_cast<float*>(P.ws + ph.cons_off + (size_t)l * ph.cons_layer_bytes);
@@ -532,7 +621,7 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
   for (int t = tid; t < tasks; t += 2 * STEP_THREADS) {  // uniform per wave
     const bool two = t + STEP_THREADS < tasks;            // uniform per wave
     const int ln = t & 63;
-    const int f0 = a.t0 + fin_first(a, ph.sk);
+    const int f0 = a.t0 + ffirst;
     const int tg0 = f0 + (t >> 6) * ph.sk;
     const int tg1 = two ? f0 + ((t + STEP_THREADS) >> 6) * ph.sk : tg0;
     const unsigned base0 = (unsigned)tg0 * ph.sk * NM * 1024u + ln * 16;
@@ -582,7 +671,7 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
 // workgroup's share of it equal.
 template <int NM>
 __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhase& ph, int p,
-                                              int l, const DevLayer* L, const Assign& a,
+                                              int l, const DevLayer* L, const Assign& a, int ffirst, int nfin,
                                               const char* contrib, int* abort_s,
                                               unsigned long long* wst, int tid) {
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
@@ -616,14 +705,13 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
   }
   if (tid == 0) *abort_s = 0;
   __syncthreads();
-  const int nfin = fin_count(a, ph.sk);
-  fixup_tiles<NM>(P, ph, p, l, L, a, nfin, wst, abort_s, tid);
+  fixup_tiles<NM>(P, ph, p, l, L, a, ffirst, nfin, wst, abort_s, tid);
   wait_vm0();
   __syncthreads();
   if (*abort_s) return false;
   if (tid < nfin) {
     unsigned* done = reinterpret_cast<unsigned*>(P.ws + P.done_off);
-    const int tg = a.t0 + fin_first(a, ph.sk) + tid * ph.sk;
+    const int tg = a.t0 + ffirst + tid * ph.sk;
     __hip_atomic_fetch_add(done + (size_t)(tg % DONE_CTRS) * CTR_STRIDE, 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -634,8 +722,14 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
 
 __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ DevPhase PH[4];
   __shared__ DevLayer ltab[STEP_MAX_LAYERS];  // every layer's pointers, read from LDS
+  // this workgroup's split of each phase (the same in every layer), each
+  // wave's first unit, end unit, tile and super-block, and the first and
+  // number of the tiles it finishes
+  __shared__ Assign asg[4];
+  __shared__ int4 wstart[4][STEP_WAVES];
+  __shared__ int4 wseg[4][STEP_WAVES];
+  __shared__ int2 fin_s[4];
   __shared__ float mu_s[STEP_MAX_M];
   __shared__ float inv_s[STEP_MAX_M];
   __shared__ unsigned long long tot_s[2 * STEP_MAX_M];
@@ -645,15 +739,37 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6), lane = tid & 63;
   const int c = lane & 15, g = lane >> 4;
+  const DevPhase* PH = P.ph;
   const DevLayer* layers = reinterpret_cast<const DevLayer*>(P.ws + P.layers_off);
+  if (tid < 4) {
+    const DevPhase& q = PH[tid];
+    const Assign x = assign_split(q.nt, q.sk, q.nkb, q.KB, w, P.G);
+    asg[tid] = x;
+    const int ff = ((x.s - x.t0) % q.sk + q.sk) % q.sk;
+    fin_s[tid] = int2{ff, ff < x.tw ? (x.tw - 1 - ff) / q.sk + 1 : 0};
+  }
   {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(P.ws + P.phases_off);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(PH);
-    for (int i = tid; i < (int)(sizeof(PH) / 4); i += STEP_THREADS) dst[i] = src[i];
     const uint32_t* lsrc = reinterpret_cast<const uint32_t*>(layers);
     uint32_t* ldst = reinterpret_cast<uint32_t*>(ltab);
     const int nw = P.n_layers * (int)(sizeof(DevLayer) / 4);
     for (int i = tid; i < nw; i += STEP_THREADS) ldst[i] = lsrc[i];
+  }
+  __syncthreads();
+  if (tid < 4 * STEP_WAVES) {
+    const int q = tid / STEP_WAVES, v = tid % STEP_WAVES;
+    const Assign& x = asg[q];
+    const DevPhase& ph = PH[q];
+    const int u = wave_begin(x, v), ub = wave_begin(x, v + 1);
+    const int tl = x.nkb > 0 ? u / x.nkb : 0;
+    const int tg = x.t0 + tl;
+    const int seg = (tg >= ph.seg_t0[1]) + (tg >= ph.seg_t0[2]);
+    wstart[q][v] = int4{u, ub, tg, u - tl * x.nkb};
+    // a wave with no units keeps the phase's first matrix (never read)
+    wseg[q][v] = u < ub ? int4{ph.mat0 + seg,
+                               (int)((unsigned)(tg - ph.seg_t0[seg]) * (unsigned)ph.KB * TILE_REC +
+                                     (unsigned)x.kb0 * TILE_REC),
+                               ph.seg_t0[seg + 1], 0}
+                        : int4{ph.mat0, 0, ph.nt, 0};
   }
   __syncthreads();
   const UnpackConsts k = unpack_consts();
@@ -663,9 +779,9 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
 
   BlockRegs ring[STEP_PD];
   Iter it;
-  Assign a = assign(PH[0], w, P.G);
-  iter_init(it, PH[0], ltab[0].w, a, wave);
-  ring_fill(ring, it, PH[0], ltab[0].w, a, lane, 0, STEP_PD_PRE);
+  Assign a = lds_assign(asg[0]);
+  iter_init(it, PH[0], ltab[0].w, wstart[0][wave], wseg[0][wave]);
+  ring_fill(ring, it, PH[0], ltab[0].w, a, lane);
 
   for (int l = 0; l < P.n_layers; ++l) {
     const DevLayer* L = &ltab[l];
@@ -674,11 +790,11 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       char* x_lds = smem;
       char* xs_lds = x_lds + (size_t)M * ph.x_stride;
       char* contrib = smem + ph.lds_contrib;
-      // ---- stage this phase's input slice, then the rest of the first
-      //      weight records
+      // ---- stage this phase's input slice (the first weight records are
+      //      already in flight)
       if (l == 0 && p == 0) {
         stage_slice<true>(P.x0, 0, ph.K, M, a, nullptr, 0, tot_s, mu_s, inv_s, x_lds, ph.x_stride,
-                          L->x[0], tid);
+                          xs_lds, ph.nkb, L->x[0], tid);
       } else {
         const int ls = p ? l : l - 1, ps = p ? p - 1 : 3;
         const DevPhase& src = PH[ps];
@@ -687,11 +803,8 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
         const float* cons = reinterpret_cast<const float*>(P.ws + src.cons_off +
                                                            (size_t)ls * src.cons_layer_bytes);
         stage_slice<false>(cons, src.cons_ld, ph.K, M, a, st, src.stat_n, tot_s, mu_s, inv_s,
-                           x_lds, ph.x_stride, L->x[p], tid);
+                           x_lds, ph.x_stride, xs_lds, ph.nkb, L->x[p], tid);
       }
-      ring_fill(ring, it, ph, ltab[l].w, a, lane, STEP_PD_PRE, STEP_PD);
-      __syncthreads();
-      stage_xsum(M, a.nkb, ph.nkb, x_lds, ph.x_stride, xs_lds, tid, STEP_THREADS);
       __syncthreads();
 
       // ---- stream the weights
@@ -708,16 +821,22 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
 
       // ---- finish tiles, start the next phase's weight stream, wait until
       //      every tile of this phase is finished
-      const bool ok = ph.nm == 2 ? phase_outputs<2>(P, ph, p, l, L, a, contrib, &abort_s, tot_s,
+      const int ffirst = uni(fin_s[p].x), nfin = uni(fin_s[p].y);
+      const bool ok = ph.nm == 2 ? phase_outputs<2>(P, ph, p, l, L, a, ffirst, nfin, contrib,
+                                                    &abort_s, tot_s,
                                                     tid)
-                                 : phase_outputs<1>(P, ph, p, l, L, a, contrib, &abort_s, tot_s,
+                                 : phase_outputs<1>(P, ph, p, l, L, a, ffirst, nfin, contrib,
+                                                    &abort_s, tot_s,
                                                     tid);
       if (!ok) return;
+      // the statistics totals of the next staging start from zero (ordered
+      // before its atomics by the barrier that ends wait_done)
+      if (tid < 2 * STEP_MAX_M) tot_s[tid] = 0ull;
       const int ln = p < 3 ? l : l + 1, pn = p < 3 ? p + 1 : 0;
       if (ln < P.n_layers) {
-        a = assign(PH[pn], w, P.G);
-        iter_init(it, PH[pn], ltab[ln].w, a, wave);
-        ring_fill(ring, it, PH[pn], ltab[ln].w, a, lane, 0, STEP_PD_PRE);
+        a = lds_assign(asg[pn]);
+        iter_init(it, PH[pn], ltab[ln].w, wstart[pn][wave], wseg[pn][wave]);
+        ring_fill(ring, it, PH[pn], ltab[ln].w, a, lane);
       }
       if (!wait_done(P, PH, l, p, &abort_s)) return;
     }
@@ -762,7 +881,8 @@ namespace {
 
 constexpr int kMaxG = 1024;                    // most workgroups (CUs) planned for
 constexpr size_t kLdsLimit = 160 * 1024;
-constexpr size_t kStaticLds = 4 * sizeof(DevPhase) + STEP_MAX_LAYERS * sizeof(DevLayer) +
+constexpr size_t kStaticLds = 4 * sizeof(Assign) + 2 * 4 * STEP_WAVES * 16 + 4 * 8 +
+                              STEP_MAX_LAYERS * sizeof(DevLayer) +
                               2 * STEP_MAX_M * sizeof(float) +
                               2 * STEP_MAX_M * sizeof(unsigned long long) + 64;
 
@@ -772,7 +892,7 @@ int tiles_of(int n) { return (n + 15) / 16; }
 
 struct StepPlan {
   DevPhase ph[4];
-  size_t phases_off, layers_off, done_off, status_off, stats_off, sync_end;
+  size_t layers_off, done_off, status_off, stats_off, sync_end;
   size_t part_begin, part_end;  // slice partial blocks of all phases
   size_t total;
   bool ok = true;  // false: some K slice would get no workgroup
@@ -848,6 +968,7 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
       ++sk;
     }
     ph.x_stride = ph.nkb * X_BYTES_PER_BLOCK + X_ROW_PAD;
+    if (M * ph.nkb * 32 > STEP_THREADS * kStageRound) sp.ok = false;  // staging is one round
     for (int q = 0; q < ph.sk; ++q)
       if (slice_start(q + 1, ph.sk, ph.nkb, ph.KB, G) <= slice_start(q, ph.sk, ph.nkb, ph.KB, G))
         sp.ok = false;
@@ -882,8 +1003,6 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
   sp.stats_off = off;
   off += align256((size_t)n_layers * 4 * STAT_SLOTS * M * 2 * sizeof(long long));
   sp.sync_end = off;
-  sp.phases_off = off;
-  off += align256(4 * sizeof(DevPhase));
   sp.layers_off = off;
   off += align256((size_t)n_layers * sizeof(DevLayer));
   sp.part_begin = off;
@@ -912,6 +1031,8 @@ bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_mat(const mk_q4k_mat& m) {
   if (m.N < 1 || m.K < QK || m.K % QK) return MK_EINVAL;
+  // record offsets within one matrix are 32-bit
+  if ((size_t)tiles_of(m.N) * (size_t)(m.K / QK) * TILE_REC >= ((size_t)1 << 32)) return MK_EINVAL;
   return MK_OK;
 }
 
@@ -1028,8 +1149,6 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
                       memcmp(tc.phases, sp.ph, sizeof(sp.ph)) == 0;
     if (!same) {
       // pageable sources: the calls return once the host buffers have been read
-      e = hipMemcpyAsync(ws + sp.phases_off, sp.ph, sizeof(sp.ph), hipMemcpyHostToDevice, st);
-      if (e != hipSuccess) return MK_EHIP;
       e = hipMemcpyAsync(ws + sp.layers_off, table.data(), table.size() * sizeof(DevLayer),
                          hipMemcpyHostToDevice, st);
       if (e != hipSuccess) return MK_EHIP;
@@ -1049,7 +1168,7 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
 
   StepParams P;
   memset(&P, 0, sizeof(P));
-  P.phases_off = sp.phases_off;
+  memcpy(P.ph, sp.ph, sizeof(sp.ph));
   P.n_layers = n_layers;
   P.M = M;
   P.G = G;

@@ -138,7 +138,8 @@ int mk_q4k_gemm_tiled(const void* W_tiles, const uint16_t* X_fp16, float* Y_fp32
  * Chain rules (checked): q.K = k.K = v.K = gate.K = up.K = down.N = H (the
  * hidden size), o.K = q.N, gate.N = up.N = down.K = F; every K % 256 == 0;
  * every layer has the same shapes. Limits: 1 <= M <= 16 stacked rows,
- * 1 <= n_layers <= 128. Each phase's K range is cut into slices whose input
+ * 1 <= n_layers <= 128, each matrix's tile-record form under 4 GiB
+ * (otherwise MK_EINVAL). Each phase's K range is cut into slices whose input
  * rows fit in on-chip memory; a shape whose plan still does not fit one
  * workgroup per compute unit returns MK_EOCCUPANCY.
  */
