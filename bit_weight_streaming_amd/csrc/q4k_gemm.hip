@@ -98,8 +98,7 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
   };
 
   const int ua = wave_begin(a, wave), ub = wave_begin(a, wave + 1);
-  // next unit to load; past the end the last unit is re-read (never used),
-  // so the steady-state loads are unconditional
+  // next unit to load (the loop below never asks for one past ub)
   int ltl = ua / a.nkb, lb = ua - ltl * a.nkb, lu = ua;
   auto load_next = [&](BlockRegs& r) {
     const int tg = a.t0 + ltl;
@@ -119,10 +118,9 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
   };
   // the first weight records are in flight while the activations are staged
   BlockRegs ring[PD];
-  if (ua < ub) {
 #pragma unroll
-    for (int s = 0; s < PD; ++s) load_next(ring[s]);
-  }
+  for (int s = 0; s < PD; ++s)
+    if (s < ub - ua) load_next(ring[s]);
   if (a.U > 0) stage_x(A.x, A.K, A.M, a.kb0, a.nkb, x_lds, A.x_stride, tid, GEMM_THREADS);
   if (tid == 0) nlast_s = 0;
   __syncthreads();
@@ -168,18 +166,17 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
         }
       }
     };
+    // unit r sits in ring slot r % PD; once consumed, its slot takes unit
+    // r + PD, if the wave has one
     const int U = ub - ua;
-    int r = 0;
-    for (; r + PD <= U; r += PD) {
+    for (int r0 = 0; r0 < U; r0 += PD) {
 #pragma unroll
       for (int s = 0; s < PD; ++s) {
+        if (r0 + s >= U) break;
         consume(ring[s]);
-        load_next(ring[s]);
+        if (r0 + s + PD < U) load_next(ring[s]);
       }
     }
-#pragma unroll
-    for (int s = 0; s < PD; ++s)
-      if (r + s < U) consume(ring[s]);
   }
   __syncthreads();
 

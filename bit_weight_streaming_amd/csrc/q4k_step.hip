@@ -234,9 +234,7 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
                                               const DevPhase& ph, WPtrs L,
                                               const Assign& a, int wave, int lane,
                                               const char* xa_lane, const char* xs_lane,
-                                              char* contrib, __amdgpu_buffer_rsrc_t pr,
-                                              unsigned par, bool rows_ok,
-                                              const UnpackConsts& k) {
+                                              char* contrib, const UnpackConsts& k) {
   const int g = lane >> 4;
   const int ua = wave_begin(a, wave), ub = wave_begin(a, wave + 1);
   const int U = (ub - ua) * NM;  // records
@@ -249,21 +247,11 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
   int cu = ua;
   auto flush = [&]() {
     const int first = wave_of_unit(a, ctl * a.nkb);
-    const int last = wave_of_unit(a, (ctl + 1) * a.nkb - 1);
-    if (first == last) {
-      const unsigned off = ((unsigned)((a.t0 + ctl) * ph.sk + a.s) * NM) * 1024u + lane * 16;
+    char* slot = contrib + ((size_t)(ctl * ph.cmax + (wave - first)) * NM) * 1024 + lane * 16;
 #pragma unroll
-      for (int q = 0; q < NM; ++q) {
-        if (rows_ok) st4_dev(pr, off + q * 1024u, tag_parity(acc[q], par));
-        acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
-    } else {
-      char* slot = contrib + ((size_t)(ctl * ph.cmax + (wave - first)) * NM) * 1024 + lane * 16;
-#pragma unroll
-      for (int q = 0; q < NM; ++q) {
-        *reinterpret_cast<floatx4*>(slot + q * 1024) = acc[q];
-        acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
+    for (int q = 0; q < NM; ++q) {
+      *reinterpret_cast<floatx4*>(slot + q * 1024) = acc[q];
+      acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
   };
   auto consume = [&](int s) {
@@ -663,8 +651,8 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
   }
 }
 
-// End of a phase in one workgroup: add the wave parts of each tile shared
-// by several waves, publish those slice partials and count every tile in; then, for the tiles this workgroup
+// End of a phase in one workgroup: add the wave parts of each tile and
+// publish the tile's slice partial; then, for the tiles this workgroup
 // finishes (tile t is finished by the workgroup of slice t % sk), wait until
 // every slice has arrived, add the partials in slice order, and count the
 // tiles as finished. Spreading the finishing over the slices keeps every
@@ -676,17 +664,13 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
                                               unsigned long long* wst, int tid) {
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
   if (tid < 2 * STEP_MAX_M) wst[tid] = 0ull;
-  // Only a tile holding the start of some wave's range (other than at the
-  // tile's first unit) is shared; items (boundary v, matrix, lane), each
-  // shared tile taken at the first boundary inside it.
-  const int items = (STEP_WAVES - 1) * NM * 64;
+  // Every tile's wave parts sit in LDS (slot: tile, wave - first wave of the
+  // tile); add them and publish the tile's slice partial. Items (tile,
+  // matrix, lane); lanes that hold only rows past M have nothing to publish.
+  const int items = a.tw * NM * 64;
   for (int e = tid; e < items; e += STEP_THREADS) {
-    const int vb = 1 + (e >> 6) / NM, q = (e >> 6) % NM, ln = e & 63;
-    const int u = wave_begin(a, vb);
-    if (u >= a.U || u % a.nkb == 0) continue;
-    const int tl = u / a.nkb;
-    const int up = wave_begin(a, vb - 1);
-    if (vb > 1 && up % a.nkb != 0 && up / a.nkb == tl) continue;  // taken at boundary vb - 1
+    const int tl = e / (NM * 64), q = (e >> 6) % NM, ln = e & 63;
+    if (4 * (ln >> 4) >= P.M) continue;
     const int tg = a.t0 + tl;
     const int w0 = wave_of_unit(a, tl * a.nkb);
     const int w1 = wave_of_unit(a, (tl + 1) * a.nkb - 1);
@@ -699,9 +683,8 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
           contrib + ((size_t)(tl * ph.cmax + kk) * NM + q) * 1024 + ln * 16);
       v += u;
     }
-    if (4 * (ln >> 4) < P.M)
-      st4_dev(pr, ((unsigned)(tg * ph.sk + a.s) * NM + q) * 1024u + ln * 16,
-              tag_parity(v, (unsigned)l & 1u));
+    st4_dev(pr, ((unsigned)(tg * ph.sk + a.s) * NM + q) * 1024u + ln * 16,
+            tag_parity(v, (unsigned)l & 1u));
   }
   if (tid == 0) *abort_s = 0;
   __syncthreads();
@@ -810,13 +793,10 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       // ---- stream the weights
       const char* xa_lane = x_lds + (size_t)arow * ph.x_stride + g * 128;
       const char* xs_lane = xs_lds + (size_t)arow * ph.nkb * XSUM_BYTES_PER_BLOCK + 8 * g;
-      const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
       if (ph.nm == 2)
-        phase_compute<2>(ring, it, ph, ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, pr,
-                         (unsigned)l & 1u, 4 * g < M, k);
+        phase_compute<2>(ring, it, ph, ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, k);
       else
-        phase_compute<1>(ring, it, ph, ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, pr,
-                         (unsigned)l & 1u, 4 * g < M, k);
+        phase_compute<1>(ring, it, ph, ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, k);
       __syncthreads();
 
       // ---- finish tiles, start the next phase's weight stream, wait until
