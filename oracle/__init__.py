@@ -17,9 +17,13 @@ What it computes, and where that comes from:
 * ``decode_block`` / ``dequant_rows``: the Q4_K block (public GGUF layout;
   the pages name only "Q4_K_M"). Pinned by hand-built bytes, single-nibble
   unit vectors and exhaustive scale/min round trips.
-* ``standardize``: the row-wise transform used between dependent matrices of
-  the layer walk (mean 0, variance 1 per row). Pinned by its closed-form
-  moments. ``f64_to_f16`` is pinned to numpy's binary16 cast.
+* ``standardize`` / ``gemm_std``: every matrix of the layer walk multiplies
+  the row-wise standardized form (mean 0, variance 1 per row, exact in
+  float64) of its binary16 input; the phase inputs themselves are plain
+  binary16 casts of the previous outputs. Pinned by closed-form moments, by
+  invariance of ``gemm_std`` to a per-row shift and power-of-two scale of the
+  input, by constant rows (output exactly 0) and by a numpy cross-check.
+  ``f64_to_f16`` is pinned to numpy's binary16 cast.
 * ``within_bound``: the acceptance rule ``|y - y_ref| <= tol * S``, and
   ``y == 0`` exactly where ``S == 0``.
 """
@@ -77,6 +81,8 @@ def _load():
         lib.oracle_dequant_rows.argtypes = [vp, i64, i64, vp]
         lib.oracle_gemm.restype = ctypes.c_int
         lib.oracle_gemm.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+        lib.oracle_gemm_std.restype = ctypes.c_int
+        lib.oracle_gemm_std.argtypes = [vp, vp, i64, i64, i64, ctypes.c_double, vp, vp]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_standardize.restype = None
@@ -159,6 +165,28 @@ def gemm(W: np.ndarray, X: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
                              S.ctypes.data)
     if rc != 0:
         raise RuntimeError(f"oracle_gemm failed ({rc})")
+    return y, S
+
+
+def gemm_std(W: np.ndarray, X: np.ndarray, eps: float = 1e-6) -> tuple[np.ndarray, np.ndarray]:
+    """Reference (y, S) of one matrix of the layer walk: the Q4_K rows W times
+    the row-wise standardized fp16 activations X [M, K] (mean 0, variance 1
+    per row, computed exactly in float64, never rounded to binary16)."""
+    X = np.asarray(X)
+    if X.dtype != np.float16:
+        raise TypeError("X must be float16")
+    M, K = X.shape
+    if K % QK:
+        raise ValueError("K must be a multiple of 256")
+    W = _c(W, np.uint8).reshape(-1, K // QK * BLOCK_BYTES)
+    ncols = W.shape[0]
+    xb = _c(X.view(np.uint16), np.uint16)
+    y = np.empty((M, ncols), dtype=np.float64)
+    S = np.empty((M, ncols), dtype=np.float64)
+    rc = _load().oracle_gemm_std(W.ctypes.data, xb.ctypes.data, M, ncols, K, eps,
+                                 y.ctypes.data, S.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_std failed ({rc})")
     return y, S
 
 

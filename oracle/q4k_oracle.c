@@ -148,17 +148,15 @@ void oracle_dequant_rows(const uint8_t* W, int64_t nrows, int64_t K, double* w) 
   for (int64_t n = 0; n < nrows; ++n) oracle_dequant_row(W + n * row_bytes, K, w + n * K);
 }
 
-/* Reference GEMM. W holds `ncols` weight rows (the output columns to check),
- * X is fp16 [M][K] row-major (bits), outputs y and S are double [M][ncols].
- * Threads split the columns; each column is dequantized once into a private
- * double buffer, then every row m is a plain in-order dot product. */
-int oracle_gemm(const uint8_t* W, const uint16_t* X, int64_t M, int64_t ncols, int64_t K,
-                double* y, double* S) {
-  if (K % ORACLE_QK) return -1;
+void oracle_standardize(const double* v, int64_t M, int64_t N, double eps, double* t);
+
+/* y = xd * W^T and S = |xd| * |W|^T for double activations xd [M][K]: the
+ * product both references below share. Threads split the columns; each
+ * column is dequantized once into a private double buffer, then every row m
+ * is a plain in-order dot product. */
+static int gemm_f64(const uint8_t* W, const double* xd, int64_t M, int64_t ncols, int64_t K,
+                    double* y, double* S) {
   int64_t row_bytes = K / ORACLE_QK * ORACLE_BLOCK_BYTES;
-  double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
-  if (!xd) return -2;
-  for (int64_t i = 0; i < M * K; ++i) xd[i] = oracle_f16_to_f64(X[i]);
   int err = 0;
 #pragma omp parallel
   {
@@ -185,11 +183,48 @@ int oracle_gemm(const uint8_t* W, const uint16_t* X, int64_t M, int64_t ncols, i
     }
     free(w);
   }
+  return err;
+}
+
+/* Reference GEMM. W holds `ncols` weight rows (the output columns to check),
+ * X is fp16 [M][K] row-major (bits), outputs y and S are double [M][ncols]. */
+int oracle_gemm(const uint8_t* W, const uint16_t* X, int64_t M, int64_t ncols, int64_t K,
+                double* y, double* S) {
+  if (K % ORACLE_QK) return -1;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
+  if (!xd) return -2;
+  for (int64_t i = 0; i < M * K; ++i) xd[i] = oracle_f16_to_f64(X[i]);
+  int err = gemm_f64(W, xd, M, ncols, K, y, S);
   free(xd);
   return err;
 }
 
-/* The row-wise transform between the dependent matrices of the layer walk:
+/* Reference for one matrix of the layer walk: the product of the row-wise
+ * standardized binary16 input with the weights,
+ *   y[m][n] = sum_k t[m][k] * w[n][k],   S[m][n] = sum_k |t[m][k] * w[n][k]|,
+ *   t[m][k] = (x[m][k] - mean_m) / sqrt(var_m + eps),
+ * mean and (population) variance over the K values of row m of x, all in
+ * double: the standardization is exact, never rounded to binary16. */
+int oracle_gemm_std(const uint8_t* W, const uint16_t* X, int64_t M, int64_t ncols, int64_t K,
+                    double eps, double* y, double* S) {
+  if (K % ORACLE_QK) return -1;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
+  double* t = (double*)malloc(sizeof(double) * (size_t)(M * K));
+  if (!xd || !t) {
+    free(xd);
+    free(t);
+    return -2;
+  }
+  for (int64_t i = 0; i < M * K; ++i) xd[i] = oracle_f16_to_f64(X[i]);
+  oracle_standardize(xd, M, K, eps, t);
+  int err = gemm_f64(W, t, M, ncols, K, y, S);
+  free(xd);
+  free(t);
+  return err;
+}
+
+/* The row-wise standardization every matrix of the layer walk applies to its
+ * input:
  *   t[m][n] = (v[m][n] - mean_m) / sqrt(var_m + eps)
  * with mean and (population) variance over the row's N values, in double. */
 void oracle_standardize(const double* v, int64_t M, int64_t N, double eps, double* t) {

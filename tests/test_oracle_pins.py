@@ -305,6 +305,65 @@ def test_standardize_moments_and_small_case():
     assert np.allclose(t.var(axis=1), var / (var + 1e-6), rtol=1e-12)
 
 
+def test_gemm_std_shift_and_scale_invariance():
+    """Standardizing the input makes the product independent of a per-row
+    offset and of a per-row positive scale (exactly, up to the eps term). The
+    inputs sit on a coarse grid so that shifted and doubled copies are exact
+    in binary16; a dropped mean, a wrong sign or a missing 1/sigma breaks it."""
+    M, N, K = 3, 17, 768
+    W = synth.q4k_matrix(synth.key(12, 1), N, K)
+    rng = np.random.default_rng(12)
+    base = rng.integers(-64, 65, size=(M, K)).astype(np.float64) / 16.0
+    X = base.astype(np.float16)
+    y, S = oracle.gemm_std(W, X)
+    for shift, scale in ((3.0, 1.0), (-5.5, 1.0), (0.0, 2.0), (1.25, 4.0)):
+        X2 = ((base + shift) * scale).astype(np.float16)
+        assert np.array_equal(X2.astype(np.float64), (base + shift) * scale)  # exact
+        y2, S2 = oracle.gemm_std(W, X2)
+        var = base.var(axis=1, keepdims=True)
+        # eps breaks exact scale invariance by a factor sqrt((var + eps) / (s^2 var + eps))
+        f = np.sqrt((var + 1e-6) / (scale * scale * var + 1e-6)) * scale
+        assert np.all(np.abs(y2 - y * f) <= 1e-12 * S2), (shift, scale)
+        assert np.allclose(S2, S * f, rtol=1e-12), (shift, scale)
+
+
+def test_gemm_std_constant_row_is_zero_and_matches_numpy():
+    M, N, K = 4, 29, 1024
+    W = synth.q4k_matrix(synth.key(13, 1), N, K)
+    X = synth.f16_normal(synth.key(13, 2), M * K).reshape(M, K).copy()
+    X[2, :] = np.float16(3.5)                      # constant row: variance 0
+    y, S = oracle.gemm_std(W, X)
+    assert np.all(y[2] == 0.0) and np.all(S[2] == 0.0)
+    # numpy: standardize the decoded input, then a float64 matmul with the
+    # dequantized weights
+    x = X.astype(np.float64)
+    mu = x.mean(axis=1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=1, keepdims=True)
+    t = (x - mu) / np.sqrt(var + 1e-6)
+    w = oracle.dequant_rows(W, K)
+    y_np = t @ w.T
+    S_np = np.abs(t) @ np.abs(w).T
+    assert np.all(np.abs(y - y_np) <= 1e-12 * S_np + 1e-300)
+    assert np.allclose(S, S_np, rtol=1e-12, atol=1e-300)
+
+
+def test_gemm_std_alternating_row_closed_form():
+    """A row of +s, -s, +s, ... has mean 0 and variance s^2: the standardized
+    product is s / sqrt(s^2 + eps) times the plain product of the +-1 row
+    (the plain oracle GEMM, pinned above)."""
+    M, N, K = 2, 11, 512
+    W = synth.q4k_matrix(synth.key(14, 1), N, K)
+    z = np.where(np.arange(K) % 2 == 0, 1.0, -1.0)
+    for s in (0.5, 3.0, 1e-3):
+        X = np.stack([z * s, -z * s]).astype(np.float16)
+        sv = float(X.astype(np.float64)[0, 0])
+        y, S = oracle.gemm_std(W, X)
+        yz, Sz = oracle.gemm(W, np.stack([z, -z]).astype(np.float16))
+        f = abs(sv) / np.sqrt(sv * sv + 1e-6)
+        assert np.all(np.abs(y - f * yz) <= 1e-12 * S + 1e-300), s
+        assert np.allclose(S, f * Sz, rtol=1e-12), s
+
+
 def test_within_bound_rule():
     y_ref = np.array([1.0, 0.0, -2.0])
     S = np.array([10.0, 0.0, 4.0])
