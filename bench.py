@@ -162,17 +162,18 @@ def gemm_bench(seed: int, reps: int = 60) -> list:
 
 def cpu_baseline(stack, budget_s: float = 20.0) -> dict:
     """Time the fp64 oracle (as it stands) on the same decode step: layers
-    chained through T exactly as the GPU walks them, every column of every
-    matrix, as many leading layers as fit in about budget_s of oracle time.
-    Generating the weights on the host is input plumbing and is not timed."""
+    chained through binary16 casts as the GPU walks them, each matrix applied
+    to its row-standardized input, every column of every matrix, as many
+    leading layers as fit in about budget_s of oracle time. Generating the
+    weights on the host is input plumbing and is not timed."""
     import numpy as np
     import oracle
     import synth
     from synth.stack import MATRIX_ORDER
     M, shp = stack.M, stack.shp
 
-    def T(v):
-        return oracle.f64_to_f16(oracle.standardize(v)).view(np.float16)
+    def cast(v):
+        return oracle.f64_to_f16(v).view(np.float16)
 
     def rows(l, name):
         N, K = shp[name]
@@ -183,13 +184,13 @@ def cpu_baseline(stack, budget_s: float = 20.0) -> dict:
     while layers < stack.n_layers:
         W = {n: rows(layers, n) for n in MATRIX_ORDER}
         t0 = time.perf_counter()
-        yq = oracle.gemm(W["q"], x)[0]
-        oracle.gemm(W["k"], x)
-        oracle.gemm(W["v"], x)
-        yo = oracle.gemm(W["o"], T(yq))[0]
-        xc = T(yo)
-        gu = oracle.gemm(W["gate"], xc)[0] * oracle.gemm(W["up"], xc)[0]
-        x = T(oracle.gemm(W["down"], T(gu))[0])
+        yq = oracle.gemm_std(W["q"], x)[0]
+        oracle.gemm_std(W["k"], x)
+        oracle.gemm_std(W["v"], x)
+        yo = oracle.gemm_std(W["o"], cast(yq))[0]
+        xc = cast(yo)
+        gu = oracle.gemm_std(W["gate"], xc)[0] * oracle.gemm_std(W["up"], xc)[0]
+        x = cast(oracle.gemm_std(W["down"], cast(gu))[0])
         dt = time.perf_counter() - t0
         elapsed += dt
         done_bytes += sum(w.nbytes for w in W.values())
@@ -203,7 +204,7 @@ def cpu_baseline(stack, budget_s: float = 20.0) -> dict:
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": (f"the first {layers} of {stack.n_layers} layers of the same step, chained through "
-                   f"T, all columns of all 7 matrices, M={M}: {done_bytes / 1e9:.3f} GB of Q4_K "
+                   f"binary16 casts, all columns of all 7 matrices, M={M}: {done_bytes / 1e9:.3f} GB of Q4_K "
                    f"weights in {elapsed:.2f} s (fp64 dequantize + naive matmul, OpenMP over "
                    f"columns); row-tokens/s at this rate "
                    f"{M * gbs * 1e9 / stack.weight_bytes:.4f}"),

@@ -17,11 +17,14 @@ constexpr int DONE_CTRS = 64;    // spread of the finished-tile counters
 constexpr int CTR_STRIDE = 32;   // uints between counters (128 bytes)
 constexpr int STEP_MAX_M = 16;   // rows the walk supports (one MFMA row tile)
 
-// Fixed-point scales of the row statistics: sum(y) * 2^28, sum(y^2) * 2^20
-// accumulated with 64-bit integer atomics, so the totals do not depend on the
-// order in which workgroups add them.
-constexpr double STAT_SCALE_SUM = 268435456.0;
+// Fixed-point scales of the row statistics of a phase input: sum(x) * 2^24
+// (exact for binary16 values) and sum(x^2) * 2^20, accumulated with 64-bit
+// integer atomics, so the totals do not depend on the order in which
+// workgroups add them. One contribution (a tile row) must stay below 2^50 in
+// magnitude, which keeps any total of up to 8192 tiles inside 63 bits.
+constexpr double STAT_SCALE_SUM = 16777216.0;
 constexpr double STAT_SCALE_SQ = 1048576.0;
+constexpr double STAT_TERM_MAX = 1125899906842624.0;  // 2^50
 
 // A slice partial carries the parity of its layer in the lowest bit of each
 // word: the producer sets it, the finisher waits until every word of a piece
@@ -48,7 +51,6 @@ struct DevPhase {
   int sk;          // K slices
   int nkb;         // super-blocks per slice (the last slice may be shorter)
   int x_stride;    // LDS bytes per staged activation row
-  int stat_n;      // columns the consumer's statistics run over
   int tw_max;      // most tiles one workgroup owns
   int cmax;        // most waves of one workgroup that share a tile
   int lds_contrib; // LDS offset of the per-tile wave contributions
@@ -56,9 +58,8 @@ struct DevPhase {
   size_t part_off; // workspace offset of the slice partials: one 1 KiB block
                    // (16 x 16 fp32 in MFMA lane order) per (tile, slice, matrix)
   unsigned part_bytes;
-  size_t cons_off; // workspace offset of the consumer copies [layer][M][cons_ld]
-  int cons_ld;     // row stride (floats) of a consumer copy
-  size_t cons_layer_bytes;
+  unsigned cs_off[3];  // byte offset of each segment matrix's column sums
+                       // in its tile-record buffer (after the records)
 };
 
 // Device copy of one layer's pointers.
@@ -79,7 +80,9 @@ struct StepParams {
   char* ws;              // workspace base
   size_t layers_off;     // DevLayer table
   size_t done_off;       // DONE_CTRS finished-tile counters
-  size_t stats_off;      // [n_layers][4][STAT_SLOTS][M][2] int64
+  size_t start_off;      // workgroups done with the layer-0 input statistics
+  size_t stats_off;      // [n_layers][4][STAT_SLOTS][M][2] int64: row sums of
+                         // the input of phase p of layer l
   size_t status_off;     // int status word
   size_t lds_bytes;
 };

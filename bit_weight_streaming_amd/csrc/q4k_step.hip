@@ -51,8 +51,6 @@ namespace {
 constexpr unsigned long long kTimeoutTicks = 500000000ull;  // 5 s at 100 MHz
 constexpr int kStageRound = 7;   // staging chunks a thread loads before using them
 constexpr int kFixRound = 4;     // fix-up elements a thread loads before using them
-// statistics slot values (STAT_SLOTS x M x 2) each thread reads when staging
-constexpr int kStatPer = (STAT_SLOTS * STEP_MAX_M * 2 + STEP_THREADS - 1) / STEP_THREADS;
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -284,44 +282,22 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
   }
 }
 
-// Stage the activations of slice a into LDS in the MFMA order (see
-// q4k_device.h), with the sub-block sums the min term multiplies (each split
-// into binary16 hi + lo), and, from workgroup a.j of the slice group, the
-// matching chunks of the binary16 phase input io_x ([M][K], natural order).
-//   F16_SRC: src is binary16 [M][K] (the layer-0 input), copied as is.
-//   otherwise: src is fp32 [M][src_ld]; the value staged is
-//              binary16((y - mean_m) / sqrt(var_m + 1e-6)) (round to nearest
-//              even), mean and variance from the integer statistics at st
-//              (STAT_SLOTS slots of [M][2]) over stat_n columns. The
-//              statistics loads are issued before the activation loads, so
-//              their reduction (integer LDS atomics into tot_s, which the
-//              caller has cleared: the order of the additions does not
-//              matter) runs while the activations are still in flight.
-// Each thread loads up to kStageRound 8-wide chunks, all in one round. The
-// four chunks of one 32-value sub-block sit in four consecutive lanes, which
-// add their fp32 chunk sums with two lane exchanges.
-template <bool F16_SRC, int R>
-__device__ __forceinline__ void stage_rounds(const void* src, int src_ld, int K, int M,
-                                            const Assign& a, const long long* st, int stat_n,
-                                            unsigned long long* tot_s, float* mu_s, float* inv_s,
+// Stage the binary16 activations of slice a ([M][K] at src, natural order)
+// into LDS in the MFMA order (see q4k_device.h), with the sub-block sums the
+// min term multiplies (each split into binary16 hi + lo). Each thread loads
+// up to R 8-wide chunks, all in one round; the four chunks of one 32-value
+// sub-block sit in four consecutive lanes, which add their fp32 chunk sums
+// with two lane exchanges.
+template <int R>
+__device__ __forceinline__ void stage_rounds(const uint16_t* src, int K, int M, const Assign& a,
                                             char* x_lds, int x_stride, char* xs_lds,
-                                            int xs_stride, uint16_t* io_x, int tid) {
+                                            int xs_stride, int tid) {
   const int cpr = a.nkb * 32;  // 8-wide chunks per row
   const int items = M * cpr;   // at most STEP_THREADS * R
-  const int nv = STAT_SLOTS * M * 2;  // a multiple of 64
   // row of chunk index x < 2^16: x * magic / 2^32 (cpr < 2^16)
   const unsigned magic = 0xFFFFFFFFu / (unsigned)cpr + 1u;
-  // chunks of each row this workgroup writes to io_x: [io_lo, io_hi)
-  const int io_lo = cpr * a.j / a.gs, io_hi = cpr * (a.j + 1) / a.gs;
-  // Every load is unconditional (indices clamped to the last valid one), so
-  // they issue back to back and the wait for the statistics, issued first,
-  // leaves the activation loads in flight.
-  long long pv[kStatPer];
-  if (!F16_SRC) {
-#pragma unroll
-    for (int i = 0; i < kStatPer; ++i) pv[i] = ld_dev(st + min(i * STEP_THREADS + tid, nv - 1));
-  }
-  floatx4 v0[R], v1[R];
+  // every load is unconditional (indices clamped to the last valid one), so
+  // they issue back to back
   u32x4 hv[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
@@ -329,30 +305,7 @@ __device__ __forceinline__ void stage_rounds(const void* src, int src_ld, int K,
     const int m = __umulhi((unsigned)it, magic);
     const int ch = it - m * cpr;
     const int k = (a.kb0 + (ch >> 5)) * QK + (ch & 31) * 8;
-    if (F16_SRC) {
-      hv[i] = *to_global(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) +
-                                                        (size_t)m * K + k));
-    } else {
-      const float* s = static_cast<const float*>(src) + (size_t)m * src_ld + k;
-      v0[i] = *to_global(reinterpret_cast<const floatx4*>(s));
-      v1[i] = *to_global(reinterpret_cast<const floatx4*>(s + 4));
-    }
-  }
-  if (!F16_SRC) {
-#pragma unroll
-    for (int i = 0; i < kStatPer; ++i)
-      if (i * STEP_THREADS + uni(tid & ~63) < nv)
-        atomicAdd(&tot_s[(i * STEP_THREADS + tid) % (2 * M)], (unsigned long long)pv[i]);
-    __syncthreads();
-    if (tid < M) {
-      const double mean = (double)(long long)tot_s[2 * tid] / STAT_SCALE_SUM / stat_n;
-      const double e2 = (double)(long long)tot_s[2 * tid + 1] / STAT_SCALE_SQ / stat_n;
-      double var = e2 - mean * mean;
-      if (var < 0.0) var = 0.0;
-      mu_s[tid] = (float)mean;
-      inv_s[tid] = (float)(1.0 / sqrt(var + 1e-6));
-    }
-    __syncthreads();
+    hv[i] = *to_global(reinterpret_cast<const u32x4*>(src + (size_t)m * K + k));
   }
   const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
@@ -364,23 +317,7 @@ __device__ __forceinline__ void stage_rounds(const void* src, int src_ld, int K,
     const int ch = (ok ? it : items - 1) - m * cpr;
     const int b = ch >> 5;
     const int kk = (ch & 31) * 8;
-    u32x4 h;
-    if (F16_SRC) {
-      h = hv[i];
-    } else {
-      // (y - mean) * inv as one fused step: y * inv + (-mean * inv)
-      const float iv = inv_s[m], nb = -mu_s[m] * iv;
-      const half2v p0 = {(_Float16)__builtin_fmaf(v0[i].x, iv, nb),
-                         (_Float16)__builtin_fmaf(v0[i].y, iv, nb)};
-      const half2v p1 = {(_Float16)__builtin_fmaf(v0[i].z, iv, nb),
-                         (_Float16)__builtin_fmaf(v0[i].w, iv, nb)};
-      const half2v p2 = {(_Float16)__builtin_fmaf(v1[i].x, iv, nb),
-                         (_Float16)__builtin_fmaf(v1[i].y, iv, nb)};
-      const half2v p3 = {(_Float16)__builtin_fmaf(v1[i].z, iv, nb),
-                         (_Float16)__builtin_fmaf(v1[i].w, iv, nb)};
-      h = u32x4{bit_cast_<uint32_t>(p0), bit_cast_<uint32_t>(p1), bit_cast_<uint32_t>(p2),
-                bit_cast_<uint32_t>(p3)};
-    }
+    const u32x4 h = hv[i];
     // fp32 sum of the chunk's 8 values (pairwise dot products with 1), then
     // of the sub-block's 4 chunks
     float sum = __builtin_amdgcn_fdot2(bit_cast_<half2v>(h.x), one2, 0.f, false);
@@ -390,8 +327,6 @@ __device__ __forceinline__ void stage_rounds(const void* src, int src_ld, int K,
     sum += dpp_mov<kQuadSwap1>(sum);
     sum += dpp_mov<kQuadSwap2>(sum);
     if (!ok) continue;
-    if (io_x && ch >= io_lo && ch < io_hi)
-      *to_global(reinterpret_cast<u32x4*>(io_x + (size_t)m * K + (a.kb0 + b) * QK + kk)) = h;
     u32x4 o;  // element order 0,2,1,3,4,6,5,7
     o.x = (h.x & 0xFFFFu) | (h.y << 16);
     o.y = (h.x >> 16) | (h.y & 0xFFFF0000u);
@@ -409,22 +344,16 @@ __device__ __forceinline__ void stage_rounds(const void* src, int src_ld, int K,
   }
 }
 
-
 // Staging with the number of load rounds the slice needs (one per
 // STEP_THREADS chunks; the host plan keeps it at most kStageRound), so that
 // every issued load is a useful one.
-template <bool F16_SRC>
-__device__ __forceinline__ void stage_slice(const void* src, int src_ld, int K, int M,
-                                            const Assign& a, const long long* st, int stat_n,
-                                            unsigned long long* tot_s, float* mu_s, float* inv_s,
+__device__ __forceinline__ void stage_slice(const uint16_t* src, int K, int M, const Assign& a,
                                             char* x_lds, int x_stride, char* xs_lds,
-                                            int xs_stride, uint16_t* io_x, int tid) {
+                                            int xs_stride, int tid) {
   static_assert(kStageRound == 7, "one instantiation per round count");
   const int r = uni((M * a.nkb * 32 + STEP_THREADS - 1) / STEP_THREADS);
-#define MK_STAGE(RR)                                                                         \
-  stage_rounds<F16_SRC, RR>(src, src_ld, K, M, a, st, stat_n, tot_s, mu_s, inv_s, x_lds,    \
-                            x_stride, xs_lds, xs_stride, io_x, tid)
-  if (F16_SRC || r > 5) MK_STAGE(7);
+#define MK_STAGE(RR) stage_rounds<RR>(src, K, M, a, x_lds, x_stride, xs_lds, xs_stride, tid)
+  if (r > 5) MK_STAGE(7);
   else if (r > 4) MK_STAGE(5);
   else if (r > 3) MK_STAGE(4);
   else if (r > 2) MK_STAGE(3);
@@ -545,46 +474,82 @@ __device__ __forceinline__ floatx4 await_piece(const StepParams& P, __amdgpu_buf
   return v;
 }
 
+// One finished tile column (lane ln: column ln % 16, rows 4(ln/16)..+3) of
+// the phase: z holds the products with the binary16 input x of the phase.
+// The matrix output is the product with the row-standardized input,
+//   y[m][n] = inv_m * (z[m][n] - mean_m * colsum[n]),
+// written to the layer outputs. For the matrices that feed the next phase,
+// the next phase's input is the binary16 cast of y (of y_gate * y_up, taken
+// in fp32, for the paired phase), written as pairs of columns with
+// device-coherent 32-bit stores, and its row sums over the tile's columns
+// go into the workgroup's statistics (fixed point, LDS integer atomics).
 template <int NM>
-__device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase& ph, int p,
-                                             const DevLayer* L, int tg, int ln, const floatx4* y,
-                                             float* consb, unsigned long long* wst) {
+__device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase& ph,
+                                             const DevLayer* L, uint16_t* xn, bool stats,
+                                             int tg, int ln, const floatx4* z, const float* mu_s,
+                                             const float* inv_s, unsigned long long* wst) {
   const int M = P.M;
   const int seg = __builtin_amdgcn_readfirstlane(seg_of(ph, tg));  // uniform per wave
   const int nseg = ph.seg_n[seg];
   const int cs = (tg - ph.seg_t0[seg]) * 16 + (ln & 15);
   const int g = ln >> 4;
-  const bool has_cons = (p != 0) || (seg == 0);
+  const bool feeds = xn != nullptr && seg == 0;  // k and v feed nothing
   float* yp[NM];
+  float csum[NM];
 #pragma unroll
-  for (int q = 0; q < NM; ++q) yp[q] = L->y[ph.mat0 + seg + q];
+  for (int q = 0; q < NM; ++q) {
+    const int mi = ph.mat0 + seg + q;
+    yp[q] = L->y[mi];
+    // column sums follow the tile records (cs < tiles * 16: always inside)
+    csum[q] = to_global(reinterpret_cast<const float*>(L->w[mi] + ph.cs_off[seg]))[cs];
+  }
+  const int Kn = ph.seg_n[0];  // width of the next phase's input
   float s1[4], s2[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * g + r;
     const bool valid = m < M && cs < nseg;
-    const float cv = valid ? (NM == 2 ? y[0][r] * y[1][r] : y[0][r]) : 0.f;
+    const float mu = mu_s[m], iv = inv_s[m];
+    float y[NM];
+#pragma unroll
+    for (int q = 0; q < NM; ++q) y[q] = __builtin_fmaf(-mu, csum[q], z[q][r]) * iv;
     if (valid) {
 #pragma unroll
-      for (int q = 0; q < NM; ++q) to_global(yp[q])[(size_t)m * nseg + cs] = y[q][r];
-      if (has_cons) st_dev(&consb[(size_t)m * ph.cons_ld + cs], cv);
+      for (int q = 0; q < NM; ++q) to_global(yp[q])[(size_t)m * nseg + cs] = y[q];
     }
-    s1[r] = cv;
-    s2[r] = cv * cv;
+    float hv = 0.f;
+    if (feeds) {
+      // the value cast is the fp32 one (y, or the fp32 product of y_gate and
+      // y_up): the empty asm keeps the compiler from fusing the last multiply
+      // into a mixed-precision op that rounds once, straight to binary16
+      float v = NM == 2 ? y[0] * y[1] : y[0];
+      asm volatile("" : "+v"(v));
+      const _Float16 h = (_Float16)v;
+      const int hb = bit_cast_<uint16_t>(h);
+      const int hp = __builtin_amdgcn_mov_dpp(hb, kQuadSwap1, 0xF, 0xF, false);  // column cs ^ 1
+      if (valid && (cs & 1) == 0)
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(xn + (size_t)m * Kn + cs),
+                           (uint32_t)(hb & 0xFFFF) | ((uint32_t)hp << 16), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      hv = valid ? (float)h : 0.f;
+    }
+    s1[r] = hv;
+    s2[r] = hv * hv;
   }
+  if (!feeds || !stats) return;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     s1[r] = row_sum16(s1[r]);
     s2[r] = row_sum16(s2[r]);
   }
-  if (has_cons && (ln & 15) == 0) {
+  if ((ln & 15) == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * g + r;
       if (m >= M) break;
       const double f1 = (double)s1[r] * STAT_SCALE_SUM, f2 = (double)s2[r] * STAT_SCALE_SQ;
-      if (!(fabs(f1) < 4.0e18) || !(f2 < 4.0e18)) {
-        set_status(P, MK_ERANGE);
+      if (!(fabs(f1) < STAT_TERM_MAX) || !(f2 < STAT_TERM_MAX)) {
+        set_status(P, MK_ERANGE);  // an overflowed cast or values too large to sum
       } else {
         atomicAdd(&wst[2 * m], (unsigned long long)llrint(f1));
         atomicAdd(&wst[2 * m + 1], (unsigned long long)llrint(f2));
@@ -593,16 +558,29 @@ __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase
   }
 }
 
+// The next phase's input buffer (binary16 [M][Kn]) and the statistics slots
+// of it, after phase p of layer l; the last layer's down projection writes
+// x_out and no statistics.
+__device__ __forceinline__ uint16_t* next_input(const StepParams& P, const DevLayer* ltab, int l,
+                                                int p) {
+  if (p < 3) return ltab[l].x[p + 1];
+  return l + 1 < P.n_layers ? ltab[l + 1].x[0] : P.x_out;
+}
+
 template <int NM>
 __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase& ph, int p, int l,
-                                            const DevLayer* L, const Assign& a, int ffirst,
-                                            int nfin, unsigned long long* wst, int* abort_s,
+                                            const DevLayer* ltab, const Assign& a, int ffirst,
+                                            int nfin, unsigned long long* wst,
+                                            const float* mu_s, const float* inv_s, int* abort_s,
                                             int tid) {
   const int M = P.M;
+  const DevLayer* L = &ltab[l];
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
-  float* consb = reinterpret_cast<float*>(P.ws + ph.cons_off + (size_t)l * ph.cons_layer_bytes);
+  uint16_t* xn = next_input(P, ltab, l, p);
+  const bool stats = p < 3 || l + 1 < P.n_layers;
+  const int ln_ = p < 3 ? l : l + 1, pn = p < 3 ? p + 1 : 0;
   long long* stl = reinterpret_cast<long long*>(P.ws + P.stats_off) +
-                   (size_t)(l * 4 + p) * STAT_SLOTS * M * 2;
+                   (size_t)(ln_ * 4 + pn) * STAT_SLOTS * M * 2;
   const int tasks = nfin * 64;
   const unsigned par = (unsigned)l & 1u;
   const unsigned long long t0 = wall_clock64();
@@ -639,11 +617,11 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
             if (two) y1[q] += untag(await_piece(P, pr, base1 + o, v1[i][q], par, t0, abort_s));
           }
     }
-    fixup_finish<NM>(P, ph, p, L, tg0, ln, y0, consb, wst);
-    if (two) fixup_finish<NM>(P, ph, p, L, tg1, ln, y1, consb, wst);
+    fixup_finish<NM>(P, ph, L, xn, stats, tg0, ln, y0, mu_s, inv_s, wst);
+    if (two) fixup_finish<NM>(P, ph, L, xn, stats, tg1, ln, y1, mu_s, inv_s, wst);
   }
   __syncthreads();
-  if (tid < 2 * M) {
+  if (stats && tid < 2 * M) {
     const long long v = (long long)wst[tid];
     if (v != 0)
       __hip_atomic_fetch_add(stl + (size_t)(blockIdx.x % STAT_SLOTS) * M * 2 + tid, v,
@@ -651,17 +629,48 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
   }
 }
 
+// Wait until every workgroup has added its share of the layer-0 input
+// statistics (once per launch, before the first phase's finishing).
+__device__ __forceinline__ bool wait_start(const StepParams& P, int* abort_s) {
+  if (threadIdx.x == 0) {
+    const unsigned* ctr = reinterpret_cast<const unsigned*>(P.ws + P.start_off);
+    const int* status = reinterpret_cast<const int*>(P.ws + P.status_off);
+    const unsigned long long t0 = wall_clock64();
+    int n = 0, bad = 0;
+    while (ld_dev(ctr) < (unsigned)P.G) {
+      __builtin_amdgcn_s_sleep(1);
+      if ((++n & 63) == 0) {
+        if (ld_dev(status) != 0) {
+          bad = 1;
+          break;
+        }
+        if (wall_clock64() - t0 > kTimeoutTicks) {
+          set_status(P, MK_ETIMEOUT);
+          bad = 1;
+          break;
+        }
+      }
+    }
+    *abort_s = bad;
+  }
+  __syncthreads();
+  return *abort_s == 0;
+}
+
 // End of a phase in one workgroup: add the wave parts of each tile and
 // publish the tile's slice partial; then, for the tiles this workgroup
 // finishes (tile t is finished by the workgroup of slice t % sk), wait until
-// every slice has arrived, add the partials in slice order, and count the
-// tiles as finished. Spreading the finishing over the slices keeps every
-// workgroup's share of it equal.
+// every slice has arrived, add the partials in slice order, apply the
+// standardization of the phase input (its row statistics are read while the
+// partials travel) and count the tiles as finished. Spreading the finishing
+// over the slices keeps every workgroup's share of it equal.
 template <int NM>
 __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhase& ph, int p,
-                                              int l, const DevLayer* L, const Assign& a, int ffirst, int nfin,
-                                              const char* contrib, int* abort_s,
-                                              unsigned long long* wst, int tid) {
+                                              int l, const DevLayer* ltab, const Assign& a,
+                                              int ffirst, int nfin, const char* contrib,
+                                              int* abort_s, unsigned long long* wst,
+                                              unsigned long long* tot_s, float* mu_s,
+                                              float* inv_s, int tid) {
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
   if (tid < 2 * STEP_MAX_M) wst[tid] = 0ull;
   // Every tile's wave parts sit in LDS (slot: tile, wave - first wave of the
@@ -687,8 +696,10 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
             tag_parity(v, (unsigned)l & 1u));
   }
   if (tid == 0) *abort_s = 0;
-  __syncthreads();
-  fixup_tiles<NM>(P, ph, p, l, L, a, ffirst, nfin, wst, abort_s, tid);
+  if (l == 0 && p == 0 && !wait_start(P, abort_s)) return false;
+  // mean and 1/sqrt(var + 1e-6) of the rows of this phase's input
+  load_stats(P, l, p, ph.K, tot_s, mu_s, inv_s, tid);
+  fixup_tiles<NM>(P, ph, p, l, ltab, a, ffirst, nfin, wst, mu_s, inv_s, abort_s, tid);
   wait_vm0();
   __syncthreads();
   if (*abort_s) return false;
@@ -715,7 +726,8 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   __shared__ int2 fin_s[4];
   __shared__ float mu_s[STEP_MAX_M];
   __shared__ float inv_s[STEP_MAX_M];
-  __shared__ unsigned long long tot_s[2 * STEP_MAX_M];
+  __shared__ unsigned long long tot_s[2 * STEP_MAX_M];  // input statistics, being read
+  __shared__ unsigned long long wst_s[2 * STEP_MAX_M];  // next input's statistics, being added
   __shared__ int abort_s;
   const int M = P.M;
   const int w = blockIdx.x;
@@ -754,6 +766,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
                                ph.seg_t0[seg + 1], 0}
                         : int4{ph.mat0, 0, ph.nt, 0};
   }
+  if (tid < 2 * STEP_MAX_M) wst_s[tid] = 0ull;
   __syncthreads();
   const UnpackConsts k = unpack_consts();
   // Rows past M read row M-1 (their results are never stored), so every
@@ -766,6 +779,35 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   iter_init(it, PH[0], ltab[0].w, wstart[0][wave], wseg[0][wave]);
   ring_fill(ring, it, PH[0], ltab[0].w, a, lane);
 
+  // ---- layer-0 input: copy this workgroup's columns of x0 to the layer-0
+  //      phase input and add their row sums to its statistics
+  {
+    const int c0 = (int)((long long)P.H * w / P.G), c1 = (int)((long long)P.H * (w + 1) / P.G);
+    const int nc = c1 - c0;
+    for (int i = tid; i < M * nc; i += STEP_THREADS) {
+      const int m = i / nc, cc = c0 + (i - m * nc);
+      const uint16_t hb = to_global(P.x0)[(size_t)m * P.H + cc];
+      to_global(ltab[0].x[0])[(size_t)m * P.H + cc] = hb;
+      const float h = (float)bit_cast_<_Float16>(hb);
+      atomicAdd(&wst_s[2 * m], (unsigned long long)llrint((double)h * STAT_SCALE_SUM));
+      atomicAdd(&wst_s[2 * m + 1], (unsigned long long)llrint((double)(h * h) * STAT_SCALE_SQ));
+    }
+    __syncthreads();
+    if (tid < 2 * M) {
+      long long* st0 = reinterpret_cast<long long*>(P.ws + P.stats_off);
+      const long long v = (long long)wst_s[tid];
+      if (!(fabs((double)v) < STAT_TERM_MAX)) set_status(P, MK_ERANGE);
+      if (v != 0)
+        __hip_atomic_fetch_add(st0 + (size_t)(w % STAT_SLOTS) * M * 2 + tid, v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_vm0();
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_fetch_add(reinterpret_cast<unsigned*>(P.ws + P.start_off), 1u,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
   for (int l = 0; l < P.n_layers; ++l) {
     const DevLayer* L = &ltab[l];
     for (int p = 0; p < 4; ++p) {
@@ -773,21 +815,10 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       char* x_lds = smem;
       char* xs_lds = x_lds + (size_t)M * ph.x_stride;
       char* contrib = smem + ph.lds_contrib;
-      // ---- stage this phase's input slice (the first weight records are
-      //      already in flight)
-      if (l == 0 && p == 0) {
-        stage_slice<true>(P.x0, 0, ph.K, M, a, nullptr, 0, tot_s, mu_s, inv_s, x_lds, ph.x_stride,
-                          xs_lds, ph.nkb, L->x[0], tid);
-      } else {
-        const int ls = p ? l : l - 1, ps = p ? p - 1 : 3;
-        const DevPhase& src = PH[ps];
-        const long long* st = reinterpret_cast<const long long*>(P.ws + P.stats_off) +
-                              (size_t)(ls * 4 + ps) * STAT_SLOTS * M * 2;
-        const float* cons = reinterpret_cast<const float*>(P.ws + src.cons_off +
-                                                           (size_t)ls * src.cons_layer_bytes);
-        stage_slice<false>(cons, src.cons_ld, ph.K, M, a, st, src.stat_n, tot_s, mu_s, inv_s,
-                           x_lds, ph.x_stride, xs_lds, ph.nkb, L->x[p], tid);
-      }
+      // ---- stage this phase's binary16 input slice (the first weight
+      //      records are already in flight); layer 0 reads x0 itself
+      stage_slice(l == 0 && p == 0 ? P.x0 : L->x[p], ph.K, M, a, x_lds, ph.x_stride, xs_lds,
+                  ph.nkb, tid);
       __syncthreads();
 
       // ---- stream the weights
@@ -802,16 +833,12 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       // ---- finish tiles, start the next phase's weight stream, wait until
       //      every tile of this phase is finished
       const int ffirst = uni(fin_s[p].x), nfin = uni(fin_s[p].y);
-      const bool ok = ph.nm == 2 ? phase_outputs<2>(P, ph, p, l, L, a, ffirst, nfin, contrib,
-                                                    &abort_s, tot_s,
-                                                    tid)
-                                 : phase_outputs<1>(P, ph, p, l, L, a, ffirst, nfin, contrib,
-                                                    &abort_s, tot_s,
-                                                    tid);
+      const bool ok = ph.nm == 2
+                          ? phase_outputs<2>(P, ph, p, l, ltab, a, ffirst, nfin, contrib, &abort_s,
+                                             wst_s, tot_s, mu_s, inv_s, tid)
+                          : phase_outputs<1>(P, ph, p, l, ltab, a, ffirst, nfin, contrib, &abort_s,
+                                             wst_s, tot_s, mu_s, inv_s, tid);
       if (!ok) return;
-      // the statistics totals of the next staging start from zero (ordered
-      // before its atomics by the barrier that ends wait_done)
-      if (tid < 2 * STEP_MAX_M) tot_s[tid] = 0ull;
       const int ln = p < 3 ? l : l + 1, pn = p < 3 ? p + 1 : 0;
       if (ln < P.n_layers) {
         a = lds_assign(asg[pn]);
@@ -822,22 +849,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
     }
   }
 
-  // ---- x_out = T(down of the last layer), columns split over workgroups
-  {
-    const int ls = P.n_layers - 1;
-    const DevPhase& src = PH[3];
-    load_stats(P, ls, 3, src.stat_n, tot_s, mu_s, inv_s, tid);
-    const float* cons =
-        reinterpret_cast<const float*>(P.ws + src.cons_off + (size_t)ls * src.cons_layer_bytes);
-    const int c0 = (int)((long long)P.H * w / P.G), c1 = (int)((long long)P.H * (w + 1) / P.G);
-    const int nc = c1 - c0;
-    for (int i = tid; i < M * nc; i += STEP_THREADS) {
-      const int m = i / nc, cc = c0 + (i - m * nc);
-      const float y = cons[(size_t)m * src.cons_ld + cc];
-      const _Float16 h = (_Float16)((y - mu_s[m]) * inv_s[m]);
-      to_global(P.x_out)[(size_t)m * P.H + cc] = bit_cast_<uint16_t>(h);
-    }
-  }
+  // x_out was written by the finishers of the last layer's down projection
 }
 
 // Zero the counters, status word and statistics, and fill every slice
@@ -872,7 +884,7 @@ int tiles_of(int n) { return (n + 15) / 16; }
 
 struct StepPlan {
   DevPhase ph[4];
-  size_t layers_off, done_off, status_off, stats_off, sync_end;
+  size_t layers_off, done_off, status_off, start_off, stats_off, sync_end;
   size_t part_begin, part_end;  // slice partial blocks of all phases
   size_t total;
   bool ok = true;  // false: some K slice would get no workgroup
@@ -930,8 +942,9 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
     for (int s = nseg; s < 3; ++s) ph.seg_t0[s] = t;
     ph.nt = t;
     ph.ncols = c;
-    // columns the statistics of this phase's consumer copy run over
-    ph.stat_n = ph.seg_n[0];
+    // column sums of segment s's matrix: after its tile records
+    for (int s = 0; s < 3; ++s)
+      ph.cs_off[s] = s < nseg ? (unsigned)((size_t)tiles_of(ph.seg_n[s]) * ph.KB * TILE_REC) : 0u;
     // K slices: at least 4, more while one slice of activations exceeds 96 KiB
     // of LDS or takes more than one round of loads to stage
     int sk = 4 < ph.KB ? 4 : ph.KB;
@@ -971,14 +984,14 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
       ph.lds_contrib = (int)c0;
       ph.lds_bytes = (int)(c0 + (size_t)ph.tw_max * ph.cmax * ph.nm * 1024);
     }
-    ph.cons_ld = ((ph.stat_n + 63) / 64) * 64;
-    ph.cons_layer_bytes = align256((size_t)M * ph.cons_ld * sizeof(float));
   }
   // workspace layout
   size_t off = 0;
   sp.done_off = off;
   off += align256((size_t)DONE_CTRS * CTR_STRIDE * sizeof(unsigned));
   sp.status_off = off;
+  off += 256;
+  sp.start_off = off;
   off += 256;
   sp.stats_off = off;
   off += align256((size_t)n_layers * 4 * STAT_SLOTS * M * 2 * sizeof(long long));
@@ -993,10 +1006,6 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
     off += align256(pb);
   }
   sp.part_end = off;
-  for (int p = 0; p < 4; ++p) {
-    sp.ph[p].cons_off = off;
-    off += (size_t)n_layers * sp.ph[p].cons_layer_bytes;
-  }
   sp.total = off;
 }
 
@@ -1159,6 +1168,7 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
   P.layers_off = sp.layers_off;
   P.done_off = sp.done_off;
   P.stats_off = sp.stats_off;
+  P.start_off = sp.start_off;
   P.status_off = sp.status_off;
   P.lds_bytes = lds;
   hipLaunchKernelGGL(q4k_step_kernel, dim3(G), dim3(STEP_THREADS), lds, st, P);

@@ -99,8 +99,13 @@ int mk_q4k_gemm_ws(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, 
  * bytes [32g+16, 32g+32). A wave then reads each operand with one contiguous
  * 1 KiB load instead of sixteen 16-byte pieces 2.9 KB apart.
  *
+ * The records are followed by ceil(N/16)*16 fp32 column sums: entry n is
+ * sum_k w[n][k] over the exact dequantized weights of row n (0 for padding
+ * rows), rounded once to fp32. The decode-step walk uses them to apply the
+ * row standardization of its inputs after the product (see mk_q4k_step).
+ *
  * mk_q4k_tiles_bytes: size of the record form of an N x K matrix
- *   (ceil(N/16) * (K/256) * 2304), 0 for an invalid shape.
+ *   (ceil(N/16) * ((K/256) * 2304 + 64)), 0 for an invalid shape.
  * mk_q4k_repack: write the record form of W_rows (layout above, N rows) to
  *   W_tiles (device, mk_q4k_tiles_bytes bytes, must not overlap W_rows).
  *   Asynchronous on `stream`; MK_OK, MK_EINVAL, MK_EALIGN or MK_EHIP.
