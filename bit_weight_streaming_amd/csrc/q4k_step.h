@@ -60,6 +60,7 @@ struct DevPhase {
   unsigned part_bytes;
   unsigned cs_off[3];  // byte offset of each segment matrix's column sums
                        // in its tile-record buffer (after the records)
+  double inv_k;        // 1 / K (the row statistics of the input run over K)
 };
 
 // Device copy of one layer's pointers.

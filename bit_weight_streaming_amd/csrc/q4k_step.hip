@@ -51,6 +51,8 @@ namespace {
 constexpr unsigned long long kTimeoutTicks = 500000000ull;  // 5 s at 100 MHz
 constexpr int kStageRound = 7;   // staging chunks a thread loads before using them
 constexpr int kFixRound = 4;     // fix-up elements a thread loads before using them
+// statistics slot values (STAT_SLOTS x M x 2) each thread reads when staging
+constexpr int kStatPer = (STAT_SLOTS * STEP_MAX_M * 2 + STEP_THREADS - 1) / STEP_THREADS;
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -287,9 +289,13 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
 // min term multiplies (each split into binary16 hi + lo). Each thread loads
 // up to R 8-wide chunks, all in one round; the four chunks of one 32-value
 // sub-block sit in four consecutive lanes, which add their fp32 chunk sums
-// with two lane exchanges.
+// with two lane exchanges. The row statistics of the whole input (STAT_SLOTS
+// slots of [M][2] integer sums at st, complete before the phase starts) are
+// loaded in the same round and added into tot_s (cleared by the caller) with
+// LDS integer atomics; the finishing of the phase reads the totals.
 template <int R>
 __device__ __forceinline__ void stage_rounds(const uint16_t* src, int K, int M, const Assign& a,
+                                            const long long* st, unsigned long long* tot_s,
                                             char* x_lds, int x_stride, char* xs_lds,
                                             int xs_stride, int tid) {
   const int cpr = a.nkb * 32;  // 8-wide chunks per row
@@ -297,7 +303,11 @@ __device__ __forceinline__ void stage_rounds(const uint16_t* src, int K, int M, 
   // row of chunk index x < 2^16: x * magic / 2^32 (cpr < 2^16)
   const unsigned magic = 0xFFFFFFFFu / (unsigned)cpr + 1u;
   // every load is unconditional (indices clamped to the last valid one), so
-  // they issue back to back
+  // they issue back to back; the statistics first
+  const int nv = STAT_SLOTS * M * 2;  // a multiple of 64
+  long long pv[kStatPer];
+#pragma unroll
+  for (int i = 0; i < kStatPer; ++i) pv[i] = ld_dev(st + min(i * STEP_THREADS + tid, nv - 1));
   u32x4 hv[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
@@ -342,17 +352,23 @@ __device__ __forceinline__ void stage_rounds(const uint16_t* src, int K, int M, 
                                  4 * (kk >> 5)) = half2v{hi, lo};
     }
   }
+#pragma unroll
+  for (int i = 0; i < kStatPer; ++i)
+    if (i * STEP_THREADS + uni(tid & ~63) < nv)
+      atomicAdd(&tot_s[(i * STEP_THREADS + tid) % (2 * M)], (unsigned long long)pv[i]);
 }
 
 // Staging with the number of load rounds the slice needs (one per
 // STEP_THREADS chunks; the host plan keeps it at most kStageRound), so that
 // every issued load is a useful one.
 __device__ __forceinline__ void stage_slice(const uint16_t* src, int K, int M, const Assign& a,
+                                            const long long* st, unsigned long long* tot_s,
                                             char* x_lds, int x_stride, char* xs_lds,
                                             int xs_stride, int tid) {
   static_assert(kStageRound == 7, "one instantiation per round count");
   const int r = uni((M * a.nkb * 32 + STEP_THREADS - 1) / STEP_THREADS);
-#define MK_STAGE(RR) stage_rounds<RR>(src, K, M, a, x_lds, x_stride, xs_lds, xs_stride, tid)
+#define MK_STAGE(RR) \
+  stage_rounds<RR>(src, K, M, a, st, tot_s, x_lds, x_stride, xs_lds, xs_stride, tid)
   if (r > 5) MK_STAGE(7);
   else if (r > 4) MK_STAGE(5);
   else if (r > 3) MK_STAGE(4);
@@ -362,43 +378,15 @@ __device__ __forceinline__ void stage_slice(const uint16_t* src, int K, int M, c
 #undef MK_STAGE
 }
 
-// Row mean and 1/sqrt(var + 1e-6) of the statistics of (layer, phase) over
-// n columns, into mu_s / inv_s. The STAT_SLOTS slots are integer sums, so the
-// totals do not depend on the order they are added in.
-__device__ __forceinline__ void load_stats(const StepParams& P, int l, int p, int n,
-                                           unsigned long long* tot_s, float* mu_s, float* inv_s,
-                                           int tid) {
-  const int M = P.M;
-  if (tid < 2 * M) tot_s[tid] = 0ull;
-  __syncthreads();
-  const long long* st = reinterpret_cast<const long long*>(P.ws + P.stats_off) +
-                        (size_t)(l * 4 + p) * STAT_SLOTS * M * 2;
-  const int nv = STAT_SLOTS * M * 2;
-  long long part[2] = {0, 0};
-  int idx[2] = {-1, -1};
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int e = tid + i * STEP_THREADS;
-    if (e < nv) {
-      part[i] = ld_dev(st + e);
-      idx[i] = e % (2 * M);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    if (idx[i] >= 0) atomicAdd(&tot_s[idx[i]], (unsigned long long)part[i]);
-  for (int e = tid + 2 * STEP_THREADS; e < nv; e += STEP_THREADS)
-    atomicAdd(&tot_s[e % (2 * M)], (unsigned long long)ld_dev(st + e));
-  __syncthreads();
-  if (tid < M) {
-    const double mean = (double)(long long)tot_s[2 * tid] / STAT_SCALE_SUM / n;
-    const double e2 = (double)(long long)tot_s[2 * tid + 1] / STAT_SCALE_SQ / n;
-    double var = e2 - mean * mean;
-    if (var < 0.0) var = 0.0;
-    mu_s[tid] = (float)mean;
-    inv_s[tid] = (float)(1.0 / sqrt(var + 1e-6));
-  }
-  __syncthreads();
+// Mean and 1/sqrt(var + 1e-6) of row m of a phase input from its integer
+// statistics totals (sum x * 2^24, sum x^2 * 2^20 over K values): the
+// totals and products in double, the reciprocal square root in fp32.
+__device__ __forceinline__ float2 row_moments(const unsigned long long* tot_s, int m,
+                                              double inv_k) {
+  const double mean = (double)(long long)tot_s[2 * m] * (inv_k * (1.0 / STAT_SCALE_SUM));
+  const double e2 = (double)(long long)tot_s[2 * m + 1] * (inv_k * (1.0 / STAT_SCALE_SQ));
+  const double var = fmax(__builtin_fma(-mean, mean, e2), 0.0);
+  return float2{(float)mean, __builtin_amdgcn_rsqf((float)(var + 1e-6))};
 }
 
 // Wait until every tile of the phases up to (l, p) has been counted finished.
@@ -486,8 +474,9 @@ __device__ __forceinline__ floatx4 await_piece(const StepParams& P, __amdgpu_buf
 template <int NM>
 __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase& ph,
                                              const DevLayer* L, uint16_t* xn, bool stats,
-                                             int tg, int ln, const floatx4* z, const float* mu_s,
-                                             const float* inv_s, unsigned long long* wst) {
+                                             int tg, int ln, const floatx4* z, const float* csum,
+                                             const unsigned long long* tot_s,
+                                             unsigned long long* wst) {
   const int M = P.M;
   const int seg = __builtin_amdgcn_readfirstlane(seg_of(ph, tg));  // uniform per wave
   const int nseg = ph.seg_n[seg];
@@ -495,21 +484,16 @@ __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase
   const int g = ln >> 4;
   const bool feeds = xn != nullptr && seg == 0;  // k and v feed nothing
   float* yp[NM];
-  float csum[NM];
 #pragma unroll
-  for (int q = 0; q < NM; ++q) {
-    const int mi = ph.mat0 + seg + q;
-    yp[q] = L->y[mi];
-    // column sums follow the tile records (cs < tiles * 16: always inside)
-    csum[q] = to_global(reinterpret_cast<const float*>(L->w[mi] + ph.cs_off[seg]))[cs];
-  }
+  for (int q = 0; q < NM; ++q) yp[q] = L->y[ph.mat0 + seg + q];
   const int Kn = ph.seg_n[0];  // width of the next phase's input
   float s1[4], s2[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * g + r;
     const bool valid = m < M && cs < nseg;
-    const float mu = mu_s[m], iv = inv_s[m];
+    const float2 mv = row_moments(tot_s, m < M ? m : 0, ph.inv_k);
+    const float mu = mv.x, iv = mv.y;
     float y[NM];
 #pragma unroll
     for (int q = 0; q < NM; ++q) y[q] = __builtin_fmaf(-mu, csum[q], z[q][r]) * iv;
@@ -558,6 +542,19 @@ __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase
   }
 }
 
+// Column sums of the matrices of tile tg at lane ln's column (they follow
+// the tile records; the column is always inside the padded tile range).
+template <int NM>
+__device__ __forceinline__ void load_colsum(const DevPhase& ph, const DevLayer* L, int tg, int ln,
+                                            float* csum) {
+  const int seg = __builtin_amdgcn_readfirstlane(seg_of(ph, tg));
+  const int cs = (tg - ph.seg_t0[seg]) * 16 + (ln & 15);
+#pragma unroll
+  for (int q = 0; q < NM; ++q)
+    csum[q] = to_global(reinterpret_cast<const float*>(L->w[ph.mat0 + seg + q] +
+                                                       ph.cs_off[seg]))[cs];
+}
+
 // The next phase's input buffer (binary16 [M][Kn]) and the statistics slots
 // of it, after phase p of layer l; the last layer's down projection writes
 // x_out and no statistics.
@@ -571,7 +568,7 @@ template <int NM>
 __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase& ph, int p, int l,
                                             const DevLayer* ltab, const Assign& a, int ffirst,
                                             int nfin, unsigned long long* wst,
-                                            const float* mu_s, const float* inv_s, int* abort_s,
+                                            const unsigned long long* tot_s, int* abort_s,
                                             int tid) {
   const int M = P.M;
   const DevLayer* L = &ltab[l];
@@ -593,6 +590,10 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
     const unsigned base0 = (unsigned)tg0 * ph.sk * NM * 1024u + ln * 16;
     const unsigned base1 = (unsigned)tg1 * ph.sk * NM * 1024u + ln * 16;
     const bool rows_ok = 4 * (ln >> 4) < M;  // lanes holding only rows past M skip
+    // column sums, loaded while the partials travel
+    float cs0[NM], cs1[NM];
+    load_colsum<NM>(ph, L, tg0, ln, cs0);
+    load_colsum<NM>(ph, L, tg1, ln, cs1);
     floatx4 y0[NM], y1[NM];
 #pragma unroll
     for (int q = 0; q < NM; ++q) y0[q] = y1[q] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -617,8 +618,8 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
             if (two) y1[q] += untag(await_piece(P, pr, base1 + o, v1[i][q], par, t0, abort_s));
           }
     }
-    fixup_finish<NM>(P, ph, L, xn, stats, tg0, ln, y0, mu_s, inv_s, wst);
-    if (two) fixup_finish<NM>(P, ph, L, xn, stats, tg1, ln, y1, mu_s, inv_s, wst);
+    fixup_finish<NM>(P, ph, L, xn, stats, tg0, ln, y0, cs0, tot_s, wst);
+    if (two) fixup_finish<NM>(P, ph, L, xn, stats, tg1, ln, y1, cs1, tot_s, wst);
   }
   __syncthreads();
   if (stats && tid < 2 * M) {
@@ -661,16 +662,15 @@ __device__ __forceinline__ bool wait_start(const StepParams& P, int* abort_s) {
 // publish the tile's slice partial; then, for the tiles this workgroup
 // finishes (tile t is finished by the workgroup of slice t % sk), wait until
 // every slice has arrived, add the partials in slice order, apply the
-// standardization of the phase input (its row statistics are read while the
-// partials travel) and count the tiles as finished. Spreading the finishing
+// standardization of the phase input (its row statistics were added up while
+// the input was staged) and count the tiles as finished. Spreading the finishing
 // over the slices keeps every workgroup's share of it equal.
 template <int NM>
 __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhase& ph, int p,
                                               int l, const DevLayer* ltab, const Assign& a,
                                               int ffirst, int nfin, const char* contrib,
                                               int* abort_s, unsigned long long* wst,
-                                              unsigned long long* tot_s, float* mu_s,
-                                              float* inv_s, int tid) {
+                                              const unsigned long long* tot_s, int tid) {
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
   if (tid < 2 * STEP_MAX_M) wst[tid] = 0ull;
   // Every tile's wave parts sit in LDS (slot: tile, wave - first wave of the
@@ -696,10 +696,8 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
             tag_parity(v, (unsigned)l & 1u));
   }
   if (tid == 0) *abort_s = 0;
-  if (l == 0 && p == 0 && !wait_start(P, abort_s)) return false;
-  // mean and 1/sqrt(var + 1e-6) of the rows of this phase's input
-  load_stats(P, l, p, ph.K, tot_s, mu_s, inv_s, tid);
-  fixup_tiles<NM>(P, ph, p, l, ltab, a, ffirst, nfin, wst, mu_s, inv_s, abort_s, tid);
+  __syncthreads();
+  fixup_tiles<NM>(P, ph, p, l, ltab, a, ffirst, nfin, wst, tot_s, abort_s, tid);
   wait_vm0();
   __syncthreads();
   if (*abort_s) return false;
@@ -724,9 +722,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   __shared__ int4 wstart[4][STEP_WAVES];
   __shared__ int4 wseg[4][STEP_WAVES];
   __shared__ int2 fin_s[4];
-  __shared__ float mu_s[STEP_MAX_M];
-  __shared__ float inv_s[STEP_MAX_M];
-  __shared__ unsigned long long tot_s[2 * STEP_MAX_M];  // input statistics, being read
+  __shared__ unsigned long long tot_s[2 * STEP_MAX_M];  // statistics of the phase input
   __shared__ unsigned long long wst_s[2 * STEP_MAX_M];  // next input's statistics, being added
   __shared__ int abort_s;
   const int M = P.M;
@@ -766,7 +762,10 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
                                ph.seg_t0[seg + 1], 0}
                         : int4{ph.mat0, 0, ph.nt, 0};
   }
-  if (tid < 2 * STEP_MAX_M) wst_s[tid] = 0ull;
+  if (tid < 2 * STEP_MAX_M) {
+    wst_s[tid] = 0ull;
+    tot_s[tid] = 0ull;
+  }
   __syncthreads();
   const UnpackConsts k = unpack_consts();
   // Rows past M read row M-1 (their results are never stored), so every
@@ -806,6 +805,10 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
     if (tid == 0)
       __hip_atomic_fetch_add(reinterpret_cast<unsigned*>(P.ws + P.start_off), 1u,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // every workgroup's share must be in before the first staging reads the
+    // statistics
+    if (tid == 0) abort_s = 0;
+    if (!wait_start(P, &abort_s)) return;
   }
 
   for (int l = 0; l < P.n_layers; ++l) {
@@ -817,8 +820,10 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       char* contrib = smem + ph.lds_contrib;
       // ---- stage this phase's binary16 input slice (the first weight
       //      records are already in flight); layer 0 reads x0 itself
-      stage_slice(l == 0 && p == 0 ? P.x0 : L->x[p], ph.K, M, a, x_lds, ph.x_stride, xs_lds,
-                  ph.nkb, tid);
+      stage_slice(l == 0 && p == 0 ? P.x0 : L->x[p], ph.K, M, a,
+                  reinterpret_cast<const long long*>(P.ws + P.stats_off) +
+                      (size_t)(l * 4 + p) * STAT_SLOTS * M * 2,
+                  tot_s, x_lds, ph.x_stride, xs_lds, ph.nkb, tid);
       __syncthreads();
 
       // ---- stream the weights
@@ -835,10 +840,13 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       const int ffirst = uni(fin_s[p].x), nfin = uni(fin_s[p].y);
       const bool ok = ph.nm == 2
                           ? phase_outputs<2>(P, ph, p, l, ltab, a, ffirst, nfin, contrib, &abort_s,
-                                             wst_s, tot_s, mu_s, inv_s, tid)
+                                             wst_s, tot_s, tid)
                           : phase_outputs<1>(P, ph, p, l, ltab, a, ffirst, nfin, contrib, &abort_s,
-                                             wst_s, tot_s, mu_s, inv_s, tid);
+                                             wst_s, tot_s, tid);
       if (!ok) return;
+      // the next staging adds the next input's statistics from zero (ordered
+      // before its atomics by the barrier that ends wait_done)
+      if (tid < 2 * STEP_MAX_M) tot_s[tid] = 0ull;
       const int ln = p < 3 ? l : l + 1, pn = p < 3 ? p + 1 : 0;
       if (ln < P.n_layers) {
         a = lds_assign(asg[pn]);
@@ -924,6 +932,7 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
     ph.nseg = nseg;
     ph.K = mats[first]->K;
     ph.KB = ph.K / QK;
+    ph.inv_k = 1.0 / ph.K;
     int t = 0, c = 0;
     for (int s = 0; s < 3; ++s) {
       if (s < nseg) {
