@@ -50,26 +50,19 @@ namespace {
 
 constexpr unsigned long long kTimeoutTicks = 500000000ull;  // 5 s at 100 MHz
 constexpr int kStageRound = 7;   // staging chunks a thread loads before using them
-constexpr int kFixRound = 4;     // fix-up elements a thread loads before using them
 // statistics slot values (STAT_SLOTS x M x 2) each thread reads when staging
 constexpr int kStatPer = (STAT_SLOTS * STEP_MAX_M * 2 + STEP_THREADS - 1) / STEP_THREADS;
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned ld_dev(const unsigned* p) {
-  return __hip_atomic_load(const_cast<unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int ld_dev(const int* p) {
-  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ long long ld_dev(const long long* p) {
-  return __hip_atomic_load(const_cast<long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Device-coherent (agent-scope) loads of values other workgroups write.
+// The pointers are taken as global-address-space ones: through a generic
+// pointer the access would be a flat one, which also counts against the LDS
+// wait counter and so makes unrelated LDS accesses wait for memory.
+template <class T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load((gptr<T>)(const_cast<T*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 static_assert(STEP_WAVES == SPLIT_WAVES, "the step splits units like the other streaming kernels");
@@ -487,6 +480,7 @@ __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase
 #pragma unroll
   for (int q = 0; q < NM; ++q) yp[q] = L->y[ph.mat0 + seg + q];
   const int Kn = ph.seg_n[0];  // width of the next phase's input
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(xn, (unsigned)(M * Kn * 2));
   float s1[4], s2[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -512,9 +506,8 @@ __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase
       const int hb = bit_cast_<uint16_t>(h);
       const int hp = __builtin_amdgcn_mov_dpp(hb, kQuadSwap1, 0xF, 0xF, false);  // column cs ^ 1
       if (valid && (cs & 1) == 0)
-        __hip_atomic_store(reinterpret_cast<uint32_t*>(xn + (size_t)m * Kn + cs),
-                           (uint32_t)(hb & 0xFFFF) | ((uint32_t)hp << 16), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(hb & 0xFFFF) | ((uint32_t)hp << 16), xr,
+                                              (unsigned)((m * Kn + cs) * 2), 0, kCoherent);
       hv = valid ? (float)h : 0.f;
     }
     s1[r] = hv;
@@ -560,8 +553,12 @@ __device__ __forceinline__ void load_colsum(const DevPhase& ph, const DevLayer* 
 // x_out and no statistics.
 __device__ __forceinline__ uint16_t* next_input(const StepParams& P, const DevLayer* ltab, int l,
                                                 int p) {
-  if (p < 3) return ltab[l].x[p + 1];
-  return l + 1 < P.n_layers ? ltab[l + 1].x[0] : P.x_out;
+  // both candidates are read and the value selected (a selected address
+  // would make the compiler read it with a flat load)
+  const int ln = l + 1 < P.n_layers ? l + 1 : l;
+  uint16_t* nx = uni(p < 3 ? ltab[l].x[p + 1] : ltab[ln].x[0]);
+  uint16_t* xo = uni(P.x_out);
+  return (p == 3 && l + 1 >= P.n_layers) ? xo : nx;
 }
 
 template <int NM>
@@ -581,45 +578,40 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
   const int tasks = nfin * 64;
   const unsigned par = (unsigned)l & 1u;
   const unsigned long long t0 = wall_clock64();
-  for (int t = tid; t < tasks; t += 2 * STEP_THREADS) {  // uniform per wave
-    const bool two = t + STEP_THREADS < tasks;            // uniform per wave
+  // pieces loaded per round: every load of a round is issued, unconditionally
+  // (slices past sk re-read the last one), before any is waited for
+  constexpr int PR = 8 / NM;
+  for (int t = tid; t < tasks; t += STEP_THREADS) {  // uniform per wave
     const int ln = t & 63;
-    const int f0 = a.t0 + ffirst;
-    const int tg0 = f0 + (t >> 6) * ph.sk;
-    const int tg1 = two ? f0 + ((t + STEP_THREADS) >> 6) * ph.sk : tg0;
-    const unsigned base0 = (unsigned)tg0 * ph.sk * NM * 1024u + ln * 16;
-    const unsigned base1 = (unsigned)tg1 * ph.sk * NM * 1024u + ln * 16;
-    const bool rows_ok = 4 * (ln >> 4) < M;  // lanes holding only rows past M skip
-    // column sums, loaded while the partials travel
-    float cs0[NM], cs1[NM];
-    load_colsum<NM>(ph, L, tg0, ln, cs0);
-    load_colsum<NM>(ph, L, tg1, ln, cs1);
-    floatx4 y0[NM], y1[NM];
+    const int tg = a.t0 + ffirst + (t >> 6) * ph.sk;
+    const unsigned base = (unsigned)tg * ph.sk * NM * 1024u + ln * 16;
+    const bool rows_ok = 4 * (ln >> 4) < M;  // lanes holding only rows past M do not wait
+    float csum[NM];
+    load_colsum<NM>(ph, L, tg, ln, csum);
+    floatx4 y[NM];
 #pragma unroll
-    for (int q = 0; q < NM; ++q) y0[q] = y1[q] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < ph.sk; s0 += 4) {
-      floatx4 v0[4][NM], v1[4][NM];
+    for (int q = 0; q < NM; ++q) y[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ph.sk; s0 += PR) {
+      floatx4 v[PR][NM];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < PR; ++i)
 #pragma unroll
         for (int q = 0; q < NM; ++q)
-          if (s0 + i < ph.sk && rows_ok) {
-            v0[i][q] = ld4_dev(pr, base0 + ((s0 + i) * NM + q) * 1024u);
-            if (two) v1[i][q] = ld4_dev(pr, base1 + ((s0 + i) * NM + q) * 1024u);
-          }
+          v[i][q] = ld4_dev(pr, base + ((unsigned)min(s0 + i, ph.sk - 1) * NM + q) * 1024u);
       // wait for late slices and add in slice order
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < PR; ++i) {
+        if (s0 + i >= ph.sk) break;
 #pragma unroll
-        for (int q = 0; q < NM; ++q)
-          if (s0 + i < ph.sk && rows_ok) {
-            const unsigned o = ((s0 + i) * NM + q) * 1024u;
-            y0[q] += untag(await_piece(P, pr, base0 + o, v0[i][q], par, t0, abort_s));
-            if (two) y1[q] += untag(await_piece(P, pr, base1 + o, v1[i][q], par, t0, abort_s));
-          }
+        for (int q = 0; q < NM; ++q) {
+          floatx4 u = v[i][q];
+          if (rows_ok && !arrived(u, par))
+            u = await_piece(P, pr, base + ((s0 + i) * NM + q) * 1024u, u, par, t0, abort_s);
+          y[q] += untag(u);
+        }
+      }
     }
-    fixup_finish<NM>(P, ph, L, xn, stats, tg0, ln, y0, cs0, tot_s, wst);
-    if (two) fixup_finish<NM>(P, ph, L, xn, stats, tg1, ln, y1, cs1, tot_s, wst);
+    fixup_finish<NM>(P, ph, L, xn, stats, tg, ln, y, csum, tot_s, wst);
   }
   __syncthreads();
   if (stats && tid < 2 * M) {
