@@ -371,6 +371,13 @@ __device__ __forceinline__ void stage_slice(const uint16_t* src, int K, int M, c
 #undef MK_STAGE
 }
 
+// round(v) as a 64-bit integer for |v| < 2^51: adding 1.5 * 2^52 leaves the
+// rounded value (ties to even) in the low mantissa bits.
+__device__ __forceinline__ long long round_i64(double v) {
+  const double t = v + 6755399441055744.0;  // 1.5 * 2^52
+  return __builtin_bit_cast(long long, t) - 0x4338000000000000ll;
+}
+
 // Mean and 1/sqrt(var + 1e-6) of row m of a phase input from its integer
 // statistics totals (sum x * 2^24, sum x^2 * 2^20 over K values): the
 // totals and products in double, the reciprocal square root in fp32.
@@ -468,8 +475,7 @@ template <int NM>
 __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase& ph,
                                              const DevLayer* L, uint16_t* xn, bool stats,
                                              int tg, int ln, const floatx4* z, const float* csum,
-                                             const unsigned long long* tot_s,
-                                             unsigned long long* wst) {
+                                             const float2* mom_s, unsigned long long* wst) {
   const int M = P.M;
   const int seg = __builtin_amdgcn_readfirstlane(seg_of(ph, tg));  // uniform per wave
   const int nseg = ph.seg_n[seg];
@@ -486,7 +492,7 @@ __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * g + r;
     const bool valid = m < M && cs < nseg;
-    const float2 mv = row_moments(tot_s, m < M ? m : 0, ph.inv_k);
+    const float2 mv = mom_s[m];  // rows past M hold zeros (never stored)
     const float mu = mv.x, iv = mv.y;
     float y[NM];
 #pragma unroll
@@ -528,8 +534,8 @@ __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase
       if (!(fabs(f1) < STAT_TERM_MAX) || !(f2 < STAT_TERM_MAX)) {
         set_status(P, MK_ERANGE);  // an overflowed cast or values too large to sum
       } else {
-        atomicAdd(&wst[2 * m], (unsigned long long)llrint(f1));
-        atomicAdd(&wst[2 * m + 1], (unsigned long long)llrint(f2));
+        atomicAdd(&wst[2 * m], (unsigned long long)round_i64(f1));
+        atomicAdd(&wst[2 * m + 1], (unsigned long long)round_i64(f2));
       }
     }
   }
@@ -565,8 +571,7 @@ template <int NM>
 __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase& ph, int p, int l,
                                             const DevLayer* ltab, const Assign& a, int ffirst,
                                             int nfin, unsigned long long* wst,
-                                            const unsigned long long* tot_s, int* abort_s,
-                                            int tid) {
+                                            const float2* mom_s, int* abort_s, int tid) {
   const int M = P.M;
   const DevLayer* L = &ltab[l];
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
@@ -611,7 +616,7 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
         }
       }
     }
-    fixup_finish<NM>(P, ph, L, xn, stats, tg, ln, y, csum, tot_s, wst);
+    fixup_finish<NM>(P, ph, L, xn, stats, tg, ln, y, csum, mom_s, wst);
   }
   __syncthreads();
   if (stats && tid < 2 * M) {
@@ -662,7 +667,8 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
                                               int l, const DevLayer* ltab, const Assign& a,
                                               int ffirst, int nfin, const char* contrib,
                                               int* abort_s, unsigned long long* wst,
-                                              const unsigned long long* tot_s, int tid) {
+                                              const unsigned long long* tot_s, float2* mom_s,
+                                              int tid) {
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
   if (tid < 2 * STEP_MAX_M) wst[tid] = 0ull;
   // Every tile's wave parts sit in LDS (slot: tile, wave - first wave of the
@@ -688,8 +694,11 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
             tag_parity(v, (unsigned)l & 1u));
   }
   if (tid == 0) *abort_s = 0;
+  // each row's mean and 1/sqrt(var + 1e-6), once (rows past M: zeros)
+  if (tid < STEP_MAX_M)
+    mom_s[tid] = tid < P.M ? row_moments(tot_s, tid, ph.inv_k) : float2{0.f, 0.f};
   __syncthreads();
-  fixup_tiles<NM>(P, ph, p, l, ltab, a, ffirst, nfin, wst, tot_s, abort_s, tid);
+  fixup_tiles<NM>(P, ph, p, l, ltab, a, ffirst, nfin, wst, mom_s, abort_s, tid);
   wait_vm0();
   __syncthreads();
   if (*abort_s) return false;
@@ -715,6 +724,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   __shared__ int4 wseg[4][STEP_WAVES];
   __shared__ int2 fin_s[4];
   __shared__ unsigned long long tot_s[2 * STEP_MAX_M];  // statistics of the phase input
+  __shared__ float2 mom_s[STEP_MAX_M];                  // its rows' mean and 1/sigma
   __shared__ unsigned long long wst_s[2 * STEP_MAX_M];  // next input's statistics, being added
   __shared__ int abort_s;
   const int M = P.M;
@@ -780,8 +790,8 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       const uint16_t hb = to_global(P.x0)[(size_t)m * P.H + cc];
       to_global(ltab[0].x[0])[(size_t)m * P.H + cc] = hb;
       const float h = (float)bit_cast_<_Float16>(hb);
-      atomicAdd(&wst_s[2 * m], (unsigned long long)llrint((double)h * STAT_SCALE_SUM));
-      atomicAdd(&wst_s[2 * m + 1], (unsigned long long)llrint((double)(h * h) * STAT_SCALE_SQ));
+      atomicAdd(&wst_s[2 * m], (unsigned long long)round_i64((double)h * STAT_SCALE_SUM));
+      atomicAdd(&wst_s[2 * m + 1], (unsigned long long)round_i64((double)(h * h) * STAT_SCALE_SQ));
     }
     __syncthreads();
     if (tid < 2 * M) {
@@ -832,9 +842,9 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       const int ffirst = uni(fin_s[p].x), nfin = uni(fin_s[p].y);
       const bool ok = ph.nm == 2
                           ? phase_outputs<2>(P, ph, p, l, ltab, a, ffirst, nfin, contrib, &abort_s,
-                                             wst_s, tot_s, tid)
+                                             wst_s, tot_s, mom_s, tid)
                           : phase_outputs<1>(P, ph, p, l, ltab, a, ffirst, nfin, contrib, &abort_s,
-                                             wst_s, tot_s, tid);
+                                             wst_s, tot_s, mom_s, tid);
       if (!ok) return;
       // the next staging adds the next input's statistics from zero (ordered
       // before its atomics by the barrier that ends wait_done)
