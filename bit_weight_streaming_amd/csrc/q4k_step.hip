@@ -259,9 +259,23 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
       }
     }
   };
-  // record r sits in ring slot r % STEP_PD; once consumed, its slot takes
-  // record r + STEP_PD, if the wave has one (no load past the range)
-  for (int r0 = 0; r0 < U; r0 += STEP_PD) {
+  // Record r sits in ring slot r % STEP_PD; once consumed, its slot takes
+  // record r + STEP_PD, if the wave has one (no load past the range). In the
+  // steady-state loop every refill exists, so each use waits only for its own
+  // slot's loads; the last groups refill conditionally.
+  int r0 = 0;
+  for (; r0 + 2 * STEP_PD <= U; r0 += STEP_PD) {
+#pragma unroll
+    for (int s = 0; s < STEP_PD; s += NM) {
+      consume(s);
+#pragma unroll
+      for (int q = 0; q < NM; ++q) {
+        load_rec(ring[s + q], iter_addr(it), lane);
+        iter_next(it, ph, L, a);
+      }
+    }
+  }
+  for (; r0 < U; r0 += STEP_PD) {
 #pragma unroll
     for (int s = 0; s < STEP_PD; s += NM) {
       if (r0 + s >= U) break;
@@ -720,6 +734,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   // wave's first unit, end unit, tile and super-block, and the first and
   // number of the tiles it finishes
   __shared__ Assign asg[4];
+  __shared__ DevPhase ph_s[4];  // LDS copy of the phase table (read with variable indices)
   __shared__ int4 wstart[4][STEP_WAVES];
   __shared__ int4 wseg[4][STEP_WAVES];
   __shared__ int2 fin_s[4];
@@ -734,6 +749,11 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   const int c = lane & 15, g = lane >> 4;
   const DevPhase* PH = P.ph;
   const DevLayer* layers = reinterpret_cast<const DevLayer*>(P.ws + P.layers_off);
+  {
+    const int nw = (int)(sizeof(ph_s) / 4);
+    for (int i = tid; i < nw; i += STEP_THREADS)
+      reinterpret_cast<uint32_t*>(ph_s)[i] = reinterpret_cast<const uint32_t*>(PH)[i];
+  }
   if (tid < 4) {
     const DevPhase& q = PH[tid];
     const Assign x = assign_split(q.nt, q.sk, q.nkb, q.KB, w, P.G);
@@ -777,8 +797,8 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   BlockRegs ring[STEP_PD];
   Iter it;
   Assign a = lds_assign(asg[0]);
-  iter_init(it, PH[0], ltab[0].w, wstart[0][wave], wseg[0][wave]);
-  ring_fill(ring, it, PH[0], ltab[0].w, a, lane);
+  iter_init(it, ph_s[0], ltab[0].w, wstart[0][wave], wseg[0][wave]);
+  ring_fill(ring, it, ph_s[0], ltab[0].w, a, lane);
 
   // ---- layer-0 input: copy this workgroup's columns of x0 to the layer-0
   //      phase input and add their row sums to its statistics
@@ -832,9 +852,9 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       const char* xa_lane = x_lds + (size_t)arow * ph.x_stride + g * 128;
       const char* xs_lane = xs_lds + (size_t)arow * ph.nkb * XSUM_BYTES_PER_BLOCK + 8 * g;
       if (ph.nm == 2)
-        phase_compute<2>(ring, it, ph, ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, k);
+        phase_compute<2>(ring, it, ph_s[p], ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, k);
       else
-        phase_compute<1>(ring, it, ph, ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, k);
+        phase_compute<1>(ring, it, ph_s[p], ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, k);
       __syncthreads();
 
       // ---- finish tiles, start the next phase's weight stream, wait until
@@ -852,8 +872,8 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       const int ln = p < 3 ? l : l + 1, pn = p < 3 ? p + 1 : 0;
       if (ln < P.n_layers) {
         a = lds_assign(asg[pn]);
-        iter_init(it, PH[pn], ltab[ln].w, wstart[pn][wave], wseg[pn][wave]);
-        ring_fill(ring, it, PH[pn], ltab[ln].w, a, lane);
+        iter_init(it, ph_s[pn], ltab[ln].w, wstart[pn][wave], wseg[pn][wave]);
+        ring_fill(ring, it, ph_s[pn], ltab[ln].w, a, lane);
       }
       if (!wait_done(P, PH, l, p, &abort_s)) return;
     }
@@ -883,10 +903,13 @@ namespace {
 
 constexpr int kMaxG = 1024;                    // most workgroups (CUs) planned for
 constexpr size_t kLdsLimit = 160 * 1024;
-constexpr size_t kStaticLds = 4 * sizeof(Assign) + 2 * 4 * STEP_WAVES * 16 + 4 * 8 +
+// the kernel's static LDS arrays (layer and phase tables, work splits,
+// statistics), with room for alignment
+constexpr size_t kStaticLds = 4 * sizeof(Assign) + 4 * sizeof(DevPhase) +
+                              2 * 4 * STEP_WAVES * 16 + 4 * 8 +
                               STEP_MAX_LAYERS * sizeof(DevLayer) +
-                              2 * STEP_MAX_M * sizeof(float) +
-                              2 * STEP_MAX_M * sizeof(unsigned long long) + 64;
+                              STEP_MAX_M * sizeof(float) * 2 +
+                              2 * 2 * STEP_MAX_M * sizeof(unsigned long long) + 256;
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
