@@ -129,16 +129,23 @@ int mk_q4k_gemm_tiled(const void* W_tiles, const uint16_t* X_fp16, float* Y_fp32
  * barrier is used: a phase's outputs are counted into device counters and the
  * next phase starts on every workgroup as soon as those counters show that its
  * whole input exists:
- *   phase A  x_l           -> q [M, Nq], k [M, Nk], v [M, Nv]
- *   phase B  T(q)          -> o [M, H]
- *   phase C  T(o)          -> gate [M, F], up [M, F]
- *   phase D  T(gate * up)  -> down [M, H]          (product elementwise, fp32)
- *   x_{l+1} = T(down)
- * where T(v) = binary16_RNE((v - mean) / sqrt(var + 1e-6)), mean and
- * population variance taken over each row's values. The layer input x_0 is
- * given; every later input is produced on the device. k and v are written but
- * feed nothing (in a model they would feed attention, which is not part of
- * this walk).
+ *   phase A  x_l                -> q [M, Nq], k [M, Nk], v [M, Nv]
+ *   phase B  c(q)               -> o [M, H]
+ *   phase C  c(o)               -> gate [M, F], up [M, F]
+ *   phase D  c(gate * up)       -> down [M, H]     (product elementwise, fp32)
+ *   x_{l+1} = c(down)
+ * where c is the binary16 round-to-nearest-even cast (the workload's "fp32 to
+ * fp16 cast" between layers). Every matrix multiplies the row-standardized
+ * form of its binary16 input x:
+ *   y[m][n] = sum_k (x[m][k] - mean_m) / sqrt(var_m + 1e-6) * w[n][k],
+ * mean and population variance over the K values of row m of x, applied
+ * exactly (never rounded to binary16): the kernel computes
+ * (sum_k x*w - mean_m * colsum_n) / sqrt(var_m + 1e-6) with the column sums
+ * mk_q4k_repack stores after the records. Without the standardization the
+ * chained products leave the binary16 range within one layer. The layer input
+ * x_0 is given; every later input is produced on the device. k and v are
+ * written but feed nothing (in a model they would feed attention, which is
+ * not part of this walk).
  *
  * Chain rules (checked): q.K = k.K = v.K = gate.K = up.K = down.N = H (the
  * hidden size), o.K = q.N, gate.N = up.N = down.K = F; every K % 256 == 0;
@@ -161,8 +168,8 @@ typedef struct {
 /* Per-layer outputs the step writes (device pointers, caller-owned). */
 typedef struct {
   float* y[7];    /* fp32 [M][N_t] for t = q, k, v, o, gate, up, down          */
-  uint16_t* x[4]; /* binary16 phase inputs A..D: x_l [M][H], T(q) [M][q.N],
-                     T(o) [M][H], T(gate*up) [M][F]                            */
+  uint16_t* x[4]; /* binary16 phase inputs A..D: x_l [M][H], c(q) [M][q.N],
+                     c(o) [M][H], c(gate*up) [M][F]                            */
 } mk_q4k_layer_io;
 
 /* Bytes of device workspace mk_q4k_step needs for this shape. */
@@ -173,7 +180,7 @@ size_t mk_q4k_step_workspace_bytes(const mk_q4k_layer* layer0 /* host */, int n_
  *   layers    (host) n_layers layer descriptors, read before return.
  *   io        (host) n_layers output descriptors, read before return.
  *   x0        [M][H] binary16 input of layer 0.
- *   x_out     [M][H] binary16 T(down) of the last layer.
+ *   x_out     [M][H] binary16 c(down) of the last layer.
  *   workspace device memory of >= mk_q4k_step_workspace_bytes bytes, used by
  *             one call at a time (calls that overlap on one workspace race);
  *             it holds the phase counters, the device status word, row
@@ -182,7 +189,8 @@ size_t mk_q4k_step_workspace_bytes(const mk_q4k_layer* layer0 /* host */, int n_
  * Returns MK_OK (enqueued) or a host-side error. Device-side failures (a
  * counter wait that times out, a statistic out of range) are recorded in the
  * workspace status word; read it with mk_q4k_step_status after the stream
- * has been synchronised.
+ * has been synchronised. MK_ERANGE there means a cast overflowed binary16 or
+ * a row sum left the fixed-point range of the statistics (a term of 2^50).
  */
 int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_layers, int M,
                 const uint16_t* x0, uint16_t* x_out, void* workspace, size_t ws_bytes,
