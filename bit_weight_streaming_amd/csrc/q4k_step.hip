@@ -5,25 +5,29 @@
 // works: the whole step is one persistent kernel with no per-layer launches,
 // and every weight read once multiplies all stacked rows). Per layer there are
 // four dependent phases:
-//   A: x_l -> q, k, v     B: T(q) -> o     C: T(o) -> gate, up
-//   D: T(gate * up) -> down,     x_{l+1} = T(down)
-// with T(v) = binary16((v - mean) / sqrt(var + 1e-6)) per row.
+//   A: x_l -> q, k, v     B: c(q) -> o     C: c(o) -> gate, up
+//   D: c(gate * up) -> down,     x_{l+1} = c(down)
+// with c the binary16 round-to-nearest-even cast. Every matrix multiplies the
+// row-standardized form of its binary16 input, applied exactly after the
+// product: y = (sum x*w - mean * colsum) / sqrt(var + 1e-6).
 //
 // Work split (G workgroups of 8 waves, one per CU):
 //   A phase's columns form 16-wide tiles (gate and up tiles travel as a pair
 //   that shares the activation operands). K is cut into sk slices; workgroup
 //   w takes slice w % sk and a contiguous run of tiles. It stages the binary16
-//   activations of its slice in LDS once; its waves split the run's
-//   (tile, super-block) units into equal contiguous ranges and stream them
-//   from the tile-record weights through an 8-deep register ring. Waves that
-//   share a tile leave their part in LDS; the parts are added in wave order.
-//   Slice partial sums go to the workspace; the last slice to finish a tile
-//   (an integer counter says which) adds the sk partials in slice order and
-//   writes the outputs, the fp32 copy the next phase stages from, and the
-//   tile's row statistics (sum y, sum y^2 as 64-bit fixed-point atomics,
-//   order independent), then counts the tile as finished.
-//   A phase starts when every tile of the previous one is counted finished;
-//   its first weight records are already in flight by then.
+//   activations of its slice in LDS once (and adds the input's row statistics
+//   while doing so); its waves split the run's (tile, super-block) units into
+//   equal contiguous ranges and stream them from the tile-record weights
+//   through a register ring. Every tile's wave parts stay in LDS until the
+//   stream ends and are added in wave order.
+//   Slice partials go to the workspace, each word tagged with the layer's
+//   parity. Tile t is finished by the workgroup of slice t % sk: it waits
+//   until every slice's piece shows the right parity, adds the pieces in
+//   slice order, applies the standardization, writes the outputs and the
+//   binary16 input of the next phase, adds the tile's row statistics of that
+//   input (64-bit fixed-point atomics, order independent) and counts the tile
+//   as finished. The next phase starts when every tile of this one is counted
+//   finished; its first weight records are in flight by then.
 //
 // Cross-workgroup memory protocol (no cache flushes or invalidates): data
 // another workgroup reads is written with device-coherent stores (sc1) and

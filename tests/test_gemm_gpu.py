@@ -249,6 +249,25 @@ def test_tiled_down_m16_sampled():
     check(W, X, cols=cols, Y=y)
 
 
+@pytest.mark.parametrize("N,K", [(1, 256), (333, 2048), (5120, 17408)])
+def test_repack_column_sums(N, K):
+    """The fp32 sums of every output column's dequantized weights that follow
+    the tile records: each within one fp32 rounding of the exact float64 sum,
+    and zero on the padding columns of the last tile."""
+    W, _ = inputs(N, K, 1, tag=70 + N % 7)
+    Wt = mk.repack(torch.from_numpy(np.ascontiguousarray(W)).to(DEV), N, K)
+    torch.cuda.synchronize()
+    nt = (N + 15) // 16
+    raw = Wt.cpu().numpy()
+    cs = raw[raw.size - nt * 16 * 4:].view(np.float32).astype(np.float64)
+    deq = oracle.dequant_rows(W, K)
+    ref = deq.sum(axis=1)
+    # one fp32 rounding, plus the float64 summation-order slack of both sides
+    tol = np.spacing(np.abs(ref).astype(np.float32)) + 1e-13 * np.abs(deq).sum(axis=1)
+    assert np.all(np.abs(cs[:N] - ref) <= tol)
+    assert np.all(cs[N:] == 0.0)
+
+
 def test_interleaved_shapes_keep_the_workspace_consistent():
     """Calls of different shapes (each splitting K) share the library
     workspace; every call must leave its counters ready for the next one."""
