@@ -143,8 +143,8 @@ def _ptr(t) -> int:
 def gemm(W, X, out=None, stream=None, workspace=None):
     """Y = X * W^T. W: uint8 [N, K/256*144] (or flat), X: float16 [M, K], both on
     the GPU; returns float32 [M, N] (written into `out` if given). A
-    `workspace` (uint8 device tensor of gemm_workspace_bytes) must be
-    zero-filled before its first use; each call leaves it zero-filled."""
+    `workspace` (uint8 device tensor of gemm_workspace_bytes) needs no
+    initial contents; each call overwrites what it uses."""
     import torch
     if X.dim() != 2 or X.dtype != torch.float16:
         raise MkError(MK_EINVAL, "X must be a 2-D float16 tensor")

@@ -85,8 +85,7 @@ namespace {
 // CU count assumed for workspace sizing when no gfx950 device is current.
 constexpr int kDefaultCus = 256;
 
-// Library-owned workspace of the current device with at least `bytes` bytes,
-// zero-filled when (re)allocated; the GEMM leaves it zeroed after every call.
+// Library-owned workspace of the current device with at least `bytes` bytes.
 int owned_workspace(int dev, size_t bytes, void** out) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
   OwnedWs& o = g_ws[dev];
@@ -100,11 +99,6 @@ int owned_workspace(int dev, size_t bytes, void** out) {
     }
     const size_t want = bytes < ((size_t)64 << 20) ? ((size_t)64 << 20) : bytes;
     if (hipMalloc(&o.ptr, want) != hipSuccess) {
-      o.ptr = nullptr;
-      return MK_EHIP;
-    }
-    if (hipMemset(o.ptr, 0, want) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-      (void)hipFree(o.ptr);
       o.ptr = nullptr;
       return MK_EHIP;
     }

@@ -9,15 +9,16 @@
 // workgroups are spread over the slices (assign_split) and each stages the M
 // activation rows of its slice into LDS once. The workgroup's (16-column
 // tile, super-block) units are split over its waves; every wave streams its
-// units through a register ring of GEMM_PD records and multiplies each
-// record against all M rows (MT 16-row MFMA tiles). A tile that one wave
-// computes alone is written straight out: to Y when there is one K slice, as
-// a slice partial otherwise. Tiles shared by waves meet in LDS (two slots per
-// wave) and are added at the end. With several slices, every workgroup then
-// counts its tiles in with an atomic that returns the previous count; the
-// workgroup that brings a tile's count to sk adds the sk partials in slice
-// order, writes Y and resets the counter to zero. No workgroup ever waits for
-// another one, and no floating-point atomics are used.
+// units through a register ring (GemmRing) and multiplies each record
+// against all M rows (MT 16-row MFMA tiles). A tile that one wave computes
+// alone is written straight out: to Y when there is one K slice, as a slice
+// partial otherwise. A wave keeps its parts of the (at most two) tiles it
+// shares with other waves in registers until the stream ends; they are then
+// written to LDS over the staged activations and added in wave order. With
+// several slices a second kernel on the same stream adds each tile's sk
+// partials in slice order and writes Y: no workgroup ever waits for another
+// one, no counters are kept between calls, and no floating-point atomics are
+// used.
 //
 // TILED selects the load-time tile-record layout (mk_q4k_repack: every wave
 // load is one contiguous 1 KiB piece); otherwise the plain row layout is read
@@ -25,6 +26,7 @@
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <utility>
 
 #include "q4k_device.h"
 #include "q4k_host.h"
@@ -33,35 +35,33 @@ namespace mk {
 
 constexpr int GEMM_THREADS = 64 * SPLIT_WAVES;
 constexpr size_t kGemmLdsLimit = 160 * 1024;
-constexpr size_t GEMM_CTR_REGION = 256 * 1024;  // counters of up to 65536 column tiles
 
 struct GemmArgs {
   const uint8_t* w;    // weights: tile records (TILED) or row blocks
   const uint16_t* x;   // [M][K] binary16
   float* y;            // [M][N]
-  unsigned* ctr;       // per-tile arrival counters (zero between calls)
   char* part;          // slice partials
   unsigned part_bytes; // bytes of slice partials
-  int M, N, K, KB, nt, sk, nkb, G, x_stride, lds_contrib;
+  int M, N, K, KB, nt, sk, nkb, G, x_stride;
 };
 
 template <int MT>
 struct GemmRing {  // records in flight per wave (what the registers allow)
-  static constexpr int PD = MT == 1 ? 6 : MT == 2 ? 4 : MT == 3 ? 3 : 2;
+  static constexpr int PD = MT == 1 ? 6 : 4;
 };
 
 template <int MT, bool TILED>
 __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
   constexpr int PD = GemmRing<MT>::PD;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ int nlast_s;
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6), lane = tid & 63, c = lane & 15, g = lane >> 4;
   const Assign a = assign_split(A.nt, A.sk, A.nkb, A.KB, blockIdx.x, A.G);
   char* x_lds = smem;
   char* xs_lds = smem + (size_t)A.M * A.x_stride;
-  char* contrib = smem + A.lds_contrib;
-  int* last_list = reinterpret_cast<int*>(contrib + SPLIT_WAVES * 2 * MT * 1024);
+  // the wave parts of shared tiles are written once the stream has ended,
+  // over the staged activations
+  char* contrib = smem;
 
   // this lane's activations of each row tile (rows past M read row M-1; their
   // results are never stored, so every read is unconditional)
@@ -91,8 +91,8 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
       st4_dev(pr, ((unsigned)(tg * A.sk + a.s) * MT + rt) * 1024u + ln * 16, v);
     }
   };
-  // LDS slot of wave v: 0 = a tile that began before its range, 1 = a tile
-  // that goes on after it
+  // LDS slot of wave v: 0 = the tile that began before its range, 1 = the
+  // tile that goes on after it
   auto slot = [&](int v, int ab, int rt) -> char* {
     return contrib + ((size_t)(v * 2 + ab) * MT + rt) * 1024;
   };
@@ -122,11 +122,14 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
   for (int s = 0; s < PD; ++s)
     if (s < ub - ua) load_next(ring[s]);
   if (a.U > 0) stage_x(A.x, A.K, A.M, a.kb0, a.nkb, x_lds, A.x_stride, tid, GEMM_THREADS);
-  if (tid == 0) nlast_s = 0;
   __syncthreads();
   if (a.U > 0) stage_xsum(A.M, a.nkb, a.nkb, x_lds, A.x_stride, xs_lds, tid, GEMM_THREADS);
   __syncthreads();
 
+  // this wave's parts of the tiles it shares (slot 0, slot 1), held until the
+  // stream ends
+  floatx4 part0[MT], part1[MT];
+  bool has0 = false, has1 = false;
   if (ua < ub) {
 
     floatx4 acc[MT];
@@ -139,11 +142,14 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
       if (first == last) {
 #pragma unroll
         for (int rt = 0; rt < MT; ++rt) put(a.t0 + ctl, lane, acc[rt], rt);
-      } else {
-        const int ab = ctl * a.nkb < ua ? 0 : 1;
+      } else if (ctl * a.nkb < ua) {
 #pragma unroll
-        for (int rt = 0; rt < MT; ++rt)
-          *reinterpret_cast<floatx4*>(slot(wave, ab, rt) + lane * 16) = acc[rt];
+        for (int rt = 0; rt < MT; ++rt) part0[rt] = acc[rt];
+        has0 = true;
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < MT; ++rt) part1[rt] = acc[rt];
+        has1 = true;
       }
 #pragma unroll
       for (int rt = 0; rt < MT; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -178,6 +184,17 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
       }
     }
   }
+  __syncthreads();  // every wave is done with the staged activations
+  if (has0) {
+#pragma unroll
+    for (int rt = 0; rt < MT; ++rt)
+      *reinterpret_cast<floatx4*>(slot(wave, 0, rt) + lane * 16) = part0[rt];
+  }
+  if (has1) {
+#pragma unroll
+    for (int rt = 0; rt < MT; ++rt)
+      *reinterpret_cast<floatx4*>(slot(wave, 1, rt) + lane * 16) = part1[rt];
+  }
   __syncthreads();
 
   // Tiles shared by waves: each holds the start of some wave's range other
@@ -199,43 +216,39 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
     }
     put(a.t0 + tl, ln, v, rt);
   }
-  if (A.sk == 1) return;
+}
 
-  // count the tiles in; the workgroup that completes a tile finishes it
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // our partials are stored
-  __syncthreads();
-  unsigned* ctr = A.ctr;
-  for (int i = tid; i < a.tw; i += GEMM_THREADS) {
-    const unsigned old =
-        __hip_atomic_fetch_add(&ctr[a.t0 + i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == (unsigned)(A.sk - 1)) last_list[atomicAdd(&nlast_s, 1)] = a.t0 + i;
+// The second kernel of a K-split call: one wave per (column tile, row tile)
+// adds the tile's sk slice partials in slice order and writes Y. It runs
+// after the streaming kernel on the same stream, so every partial is in
+// memory; no counters are needed.
+constexpr int REDUCE_THREADS = 256;
+__global__ void __launch_bounds__(REDUCE_THREADS)
+    q4k_gemm_reduce(const char* __restrict__ part, float* __restrict__ y, int M, int N, int nt,
+                    int sk, int mt) {
+  const int task = blockIdx.x * (REDUCE_THREADS / 64) + (threadIdx.x >> 6);
+  if (task >= nt * mt) return;
+  const int tg = task / mt, rt = task - tg * mt, ln = threadIdx.x & 63;
+  const char* base = part + ((size_t)tg * sk * mt + rt) * 1024 + ln * 16;
+  const size_t stride = (size_t)mt * 1024;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int SB = 8;  // pieces loaded before any is added
+  for (int s0 = 0; s0 < sk; s0 += SB) {
+    floatx4 v[SB];
+#pragma unroll
+    for (int i = 0; i < SB; ++i)
+      v[i] = *reinterpret_cast<const floatx4*>(base + (size_t)min(s0 + i, sk - 1) * stride);
+#pragma unroll
+    for (int i = 0; i < SB; ++i)
+      if (s0 + i < sk) acc += v[i];
   }
-  __syncthreads();
-  const int nl = nlast_s;
-  for (int t = tid; t < nl * MT * 64; t += GEMM_THREADS) {
-    const int li = t / (MT * 64), rt = (t >> 6) % MT, ln = t & 63;
-    const int tg = last_list[li];
-    const unsigned base = ((unsigned)tg * A.sk * MT + rt) * 1024u + ln * 16;
-    floatx4 y = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < A.sk; s0 += 4) {
-      floatx4 v[4];
+  const int col = 16 * tg + (ln & 15);
+  if (col < N) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (s0 + i < A.sk) v[i] = ld4_dev(pr, base + (unsigned)(s0 + i) * MT * 1024u);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (s0 + i < A.sk) y += v[i];
+    for (int r = 0; r < 4; ++r) {
+      const int m = 16 * rt + 4 * (ln >> 4) + r;
+      if (m < M) y[(size_t)m * N + col] = acc[r];
     }
-    const int col = 16 * tg + (ln & 15);
-    if (col < A.N) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 16 * rt + 4 * (ln >> 4) + r;
-        if (m < A.M) A.y[(size_t)m * A.N + col] = y[r];
-      }
-    }
-    if (rt == 0 && ln == 0)
-      __hip_atomic_store(&ctr[tg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -251,7 +264,14 @@ GemmPlan make_plan(int M, int N, int K, int G) {
   p.G = G < p.nt * p.KB ? G : p.nt * p.KB;  // no more workgroups than units
   G = p.G;
   const size_t contrib = (size_t)SPLIT_WAVES * 2 * p.mt * 1024;
-  const double avg = (double)p.nt * p.KB / G;
+  // Among the splits that fit in LDS, take the one that moves the fewest
+  // bytes through the busiest workgroup (a compute unit's load path is the
+  // bottleneck): its weight records, its staged activations and the slice
+  // partials it stores; with K slices, also one compute unit's share of the
+  // partials the reduction reads, 12 KiB for each of its rounds of eight
+  // loads (a round trip takes about as long as 12 KiB on that path) and
+  // 24 KiB for the second launch. nkb = 1 is taken when nothing else fits.
+  double best = -1.0;
   int prev_nkb = -1;
   for (int sk = 1; sk <= p.KB; ++sk) {
     const int nkb = (p.KB + sk - 1) / sk;
@@ -267,42 +287,63 @@ GemmPlan make_plan(int M, int N, int K, int G) {
       if (a.tw > tw_max) tw_max = a.tw;
       if (a.U > umax) umax = a.U;
     }
-    const size_t lds = c0 + contrib + (size_t)tw_max * sizeof(int);
+    // the contribution slots reuse the activation region after the stream
+    const size_t c1 = c0 > contrib ? c0 : contrib;
+    const size_t lds = c1;
     const bool fits = lds + 256 <= kGemmLdsLimit;
-    // accept the first split that fits and keeps the busiest workgroup
-    // within ~8% of the mean (or cannot be split further)
-    const bool balanced = umax <= avg * 1.08 + 1.0;
-    if ((fits && balanced) || nkb == 1) {
+    const double part = (double)p.mt * 1024;
+    const double bytes = (double)umax * TILE_REC + (double)M * nkb * X_BYTES_PER_BLOCK +
+                         (skr > 1 ? tw_max * part + (double)p.nt * skr * part / G +
+                                        (skr + 7) / 8 * 12288.0 + 24576.0
+                                  : 0.0);
+    if ((fits && (best < 0 || bytes < best)) || (nkb == 1 && best < 0)) {
+      best = bytes;
       p.sk = skr;
       p.nkb = nkb;
       p.x_stride = nkb * X_BYTES_PER_BLOCK + X_ROW_PAD;
-      p.lds_contrib = (int)c0;
       p.lds = lds;
       p.ok = fits;
-      break;
     }
   }
-  // workspace: the per-tile counters in a fixed region at the start (every
-  // call leaves them zero, and no call of any shape writes anything else
-  // there), then the slice partials
+  // workspace: the slice partials (no initial contents needed)
   p.part_bytes = p.sk > 1 ? (size_t)p.nt * p.sk * p.mt * 1024 : 0;
-  p.part_off = GEMM_CTR_REGION;
-  p.ws_bytes = p.sk > 1 ? p.part_off + p.part_bytes : 0;
-  if (p.part_bytes >= (1ull << 32) || (size_t)p.nt * sizeof(unsigned) > GEMM_CTR_REGION)
-    p.ok = false;
+  p.part_off = 0;
+  p.ws_bytes = p.part_bytes;
+  if (p.part_bytes >= (1ull << 32)) p.ok = false;
   return p;
 }
 
 std::mutex g_plan_mu;
 std::map<std::tuple<int, int, int, int>, GemmPlan> g_plans;
 
+// Dynamic LDS each kernel instantiation has been allowed on each device
+// (the attribute is raised only when a plan needs more).
+std::mutex g_attr_mu;
+std::map<std::pair<const void*, int>, size_t> g_attr_lds;
+
+hipError_t allow_lds(const void* kern, size_t lds) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_attr_mu);
+  size_t& have = g_attr_lds[std::make_pair(kern, dev)];
+  if (have >= lds) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) have = lds;
+  return e;
+}
+
 template <int MT, bool TILED>
 hipError_t launch(const GemmPlan& p, const GemmArgs& A, hipStream_t st) {
   auto kern = q4k_gemm_kernel<MT, TILED>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+  hipError_t e = allow_lds((const void*)kern, p.lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(p.G), dim3(GEMM_THREADS), p.lds, st, A);
+  e = hipGetLastError();
+  if (e != hipSuccess || p.sk == 1) return e;
+  const int waves = p.nt * MT;
+  hipLaunchKernelGGL(q4k_gemm_reduce, dim3((waves + REDUCE_THREADS / 64 - 1) / (REDUCE_THREADS / 64)),
+                     dim3(REDUCE_THREADS), 0, st, A.part, A.y, A.M, A.N, p.nt, p.sk, MT);
   return hipGetLastError();
 }
 
@@ -335,7 +376,6 @@ hipError_t gemm_launch(const GemmPlan& p, bool tiled, const void* W, const uint1
   A.w = static_cast<const uint8_t*>(W);
   A.x = X;
   A.y = Y;
-  A.ctr = static_cast<unsigned*>(ws);
   A.part = static_cast<char*>(ws) + p.part_off;
   A.part_bytes = (unsigned)p.part_bytes;
   A.M = M;
@@ -347,7 +387,6 @@ hipError_t gemm_launch(const GemmPlan& p, bool tiled, const void* W, const uint1
   A.nkb = p.nkb;
   A.G = p.G;
   A.x_stride = p.x_stride;
-  A.lds_contrib = p.lds_contrib;
   return tiled ? launch_mt<true>(p, A, st) : launch_mt<false>(p, A, st);
 }
 

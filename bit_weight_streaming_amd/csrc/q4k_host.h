@@ -17,10 +17,9 @@ struct GemmPlan {
   int sk = 1;            // K slices
   int nkb = 1;           // super-blocks per slice (the last may be shorter)
   int x_stride = 0;      // LDS bytes per staged activation row
-  int lds_contrib = 0;   // LDS offset of the per-wave contribution slots
   size_t lds = 0;        // dynamic LDS bytes
   size_t part_bytes = 0; // slice partials (0 when sk == 1)
-  size_t part_off = 0;   // offset of the slice partials in the workspace (after the counters)
+  size_t part_off = 0;   // offset of the slice partials in the workspace
   size_t ws_bytes = 0;   // workspace bytes (0 when sk == 1)
   bool ok = false;       // the plan fits the device
 };

@@ -65,13 +65,13 @@ extern "C" {
  *   Y_fp32    [M][N] float, row-major, row stride N; fully overwritten.
  *   M         1..64 stacked rows; N >= 1; K >= 256 and K % 256 == 0.
  * One launch of one workgroup per compute unit; when K is cut into several
- * slices, the slice partial sums meet in a device workspace and are added in
- * slice order by whichever workgroup finishes a tile last.
+ * slices, the slice partial sums go to a device workspace and a second
+ * kernel, enqueued on the same stream, adds them in slice order.
  * Returns MK_OK or MK_EINVAL / MK_EALIGN / MK_ENODEV / MK_EHIP. The library
  * keeps a private device workspace per GPU for the K-split partial sums; the
- * first call on a device that needs more than it holds allocates and zeroes
- * it (hipMalloc + hipMemset, which synchronise that device); later calls
- * allocate nothing. Calls that share the library workspace on one GPU must
+ * first call on a device that needs more than it holds allocates it
+ * (hipMalloc, after synchronising that device when an older, smaller one is
+ * freed); later calls allocate nothing. Calls that share the library workspace on one GPU must
  * be ordered (one stream, or synchronised).
  */
 int mk_q4k_gemm(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N, int K,
@@ -80,10 +80,10 @@ int mk_q4k_gemm(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int
 /*
  * mk_q4k_gemm_ws: as mk_q4k_gemm with a caller-provided workspace of at least
  * mk_q4k_gemm_workspace_bytes(M, N, K) bytes (16-byte aligned device memory,
- * used by one call at a time, ZERO-FILLED before its first use; every call
- * leaves its counter region zero-filled again, whatever the shape). It never
- * allocates. The size depends on the current device's compute-unit count
- * (256 is assumed when there is none). N may be at most 1048576.
+ * used by one call at a time; its contents need no initialisation and are
+ * overwritten by every call). It never allocates. The size depends on the current device's compute-unit count
+ * (256 is assumed when there is none). A shape whose slice partials would
+ * take 4 GiB or more returns MK_EINVAL.
  */
 size_t mk_q4k_gemm_workspace_bytes(int M, int N, int K);
 int mk_q4k_gemm_ws(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N,
