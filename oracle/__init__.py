@@ -24,6 +24,13 @@ What it computes, and where that comes from:
   invariance of ``gemm_std`` to a per-row shift and power-of-two scale of the
   input, by constant rows (output exactly 0) and by a numpy cross-check.
   ``f64_to_f16`` is pinned to numpy's binary16 cast.
+* ``rms_inv`` / ``gemm_rms`` / ``silu``: the residual walk (real-layer
+  epilogues around the same products): each normed matrix multiplies the
+  binary16 cast of the residual times the norm weight, scaled per row by
+  1 / sqrt(mean(h^2) + eps) of the fp32 residual h; the feed-forward input
+  is SiLU(gate) * up. Pinned by constant rows, exact power-of-two scaling,
+  the reduction of ``gemm_rms`` to ``gemm`` at unit scale, the SiLU
+  identity silu(v) - silu(-v) = v and its limits, and numpy cross-checks.
 * ``within_bound``: the acceptance rule ``|y - y_ref| <= tol * S``, and
   ``y == 0`` exactly where ``S == 0``.
 """
@@ -87,6 +94,12 @@ def _load():
         lib.oracle_num_threads.argtypes = []
         lib.oracle_standardize.restype = None
         lib.oracle_standardize.argtypes = [vp, i64, i64, ctypes.c_double, vp]
+        lib.oracle_rms_inv.restype = None
+        lib.oracle_rms_inv.argtypes = [vp, i64, i64, ctypes.c_double, vp]
+        lib.oracle_gemm_rms.restype = ctypes.c_int
+        lib.oracle_gemm_rms.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
+        lib.oracle_silu.restype = None
+        lib.oracle_silu.argtypes = [vp, i64, vp]
         _lib = lib
     return _lib
 
@@ -188,6 +201,47 @@ def gemm_std(W: np.ndarray, X: np.ndarray, eps: float = 1e-6) -> tuple[np.ndarra
     if rc != 0:
         raise RuntimeError(f"oracle_gemm_std failed ({rc})")
     return y, S
+
+
+def rms_inv(h: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """1 / sqrt(mean(h^2) + eps) per row of h [M, N], float64 [M]."""
+    h = _c(h, np.float64)
+    M, N = h.shape
+    out = np.empty(M, dtype=np.float64)
+    _load().oracle_rms_inv(h.ctypes.data, M, N, eps, out.ctypes.data)
+    return out
+
+
+def gemm_rms(W: np.ndarray, X: np.ndarray, r: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Reference (y, S) of a normed matrix of the residual walk: the Q4_K rows
+    W times the binary16 input X [M, K] scaled per row by r [M]."""
+    X = np.asarray(X)
+    if X.dtype != np.float16:
+        raise TypeError("X must be float16")
+    M, K = X.shape
+    if K % QK:
+        raise ValueError("K must be a multiple of 256")
+    W = _c(W, np.uint8).reshape(-1, K // QK * BLOCK_BYTES)
+    ncols = W.shape[0]
+    xb = _c(X.view(np.uint16), np.uint16)
+    r = _c(r, np.float64)
+    if r.shape != (M,):
+        raise ValueError("r must have one value per row")
+    y = np.empty((M, ncols), dtype=np.float64)
+    S = np.empty((M, ncols), dtype=np.float64)
+    rc = _load().oracle_gemm_rms(W.ctypes.data, xb.ctypes.data, M, ncols, K, r.ctypes.data,
+                                 y.ctypes.data, S.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_rms failed ({rc})")
+    return y, S
+
+
+def silu(v: np.ndarray) -> np.ndarray:
+    """v / (1 + exp(-v)) in float64."""
+    v = _c(v, np.float64)
+    out = np.empty_like(v)
+    _load().oracle_silu(v.ctypes.data, v.size, out.ctypes.data)
+    return out
 
 
 def standardize(v: np.ndarray, eps: float = 1e-6) -> np.ndarray:

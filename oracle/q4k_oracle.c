@@ -241,6 +241,39 @@ void oracle_standardize(const double* v, int64_t M, int64_t N, double eps, doubl
   }
 }
 
+/* The residual layer walk: the RMSNorm scale of each row of the fp32
+ * residual h [M][N], r[m] = 1 / sqrt(sum_n h[m][n]^2 / N + eps) (the norm's
+ * per-column weight is applied before the binary16 cast of the input, the
+ * row scale after the product). */
+void oracle_rms_inv(const double* h, int64_t M, int64_t N, double eps, double* r) {
+  for (int64_t m = 0; m < M; ++m) {
+    double ss = 0.0;
+    for (int64_t n = 0; n < N; ++n) ss += h[m * N + n] * h[m * N + n];
+    r[m] = 1.0 / sqrt(ss / (double)N + eps);
+  }
+}
+
+/* Reference for a normed matrix of the residual walk: y = r[m] * x * W^T
+ * and S = r[m] * |x| * |W|^T, with x the binary16 input [M][K] and r the
+ * RMSNorm scale of the residual row (oracle_rms_inv). The product is taken
+ * on the row-scaled input, r[m] * x[m][k]. */
+int oracle_gemm_rms(const uint8_t* W, const uint16_t* X, int64_t M, int64_t ncols, int64_t K,
+                    const double* r, double* y, double* S) {
+  if (K % ORACLE_QK) return -1;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
+  if (!xd) return -2;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t k = 0; k < K; ++k) xd[m * K + k] = r[m] * oracle_f16_to_f64(X[m * K + k]);
+  int err = gemm_f64(W, xd, M, ncols, K, y, S);
+  free(xd);
+  return err;
+}
+
+/* SiLU of the SwiGLU feed-forward: v * sigmoid(v) = v / (1 + exp(-v)). */
+void oracle_silu(const double* v, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = v[i] / (1.0 + exp(-v[i]));
+}
+
 void oracle_f64_to_f16_array(const double* v, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_f16(v[i]);
 }

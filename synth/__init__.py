@@ -36,6 +36,8 @@ QK = 256
 TAG_WEIGHT = 1
 TAG_X = 2
 TAG_COPY = 3   # independent weight copies used to defeat on-chip caches
+TAG_NORM = 4   # RMSNorm weights of the residual walk: (seed, TAG_NORM, layer, 0|1)
+TAG_H0 = 5     # fp32 residual input of the residual walk: (seed, TAG_H0, M, H)
 
 # Layer stack: (name, K, N) in the order the step walks them.
 LAYER_MATRICES = (
@@ -79,6 +81,9 @@ def _load():
         lib.synth_q4k_rows.restype = None
         lib.synth_q4k_rows.argtypes = [u64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_void_p]
+        lib.synth_q4k_rows_centered.restype = None
+        lib.synth_q4k_rows_centered.argtypes = [u64, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int64, ctypes.c_void_p]
         lib.synth_f16_normal.restype = None
         lib.synth_f16_normal.argtypes = [u64, u64, u64, ctypes.c_void_p]
         lib.synth_normals.restype = None
@@ -120,6 +125,20 @@ def q4k_matrix(k: int, N: int, K: int) -> np.ndarray:
     return q4k_rows(k, K, 0, N)
 
 
+def q4k_rows_centered(k: int, K: int, n0: int, nrows: int) -> np.ndarray:
+    """Rows [n0, n0+nrows) of the centred Q4_K matrix of stream k (scales 1..4,
+    mins 15*scale, dmin ~ d/2: weights of about zero mean), uint8 [nrows, K/256*144]."""
+    if K % QK:
+        raise ValueError("K must be a multiple of 256")
+    out = np.empty((nrows, K // QK * BLOCK_BYTES), dtype=np.uint8)
+    _load().synth_q4k_rows_centered(k, K, n0, nrows, out.ctypes.data)
+    return out
+
+
+def q4k_fill_ptr_centered(k: int, K: int, n0: int, nrows: int, ptr: int) -> None:
+    _load().synth_q4k_rows_centered(k, K, n0, nrows, ptr)
+
+
 def q4k_fill_ptr(k: int, K: int, n0: int, nrows: int, ptr: int) -> None:
     """Write rows [n0, n0+nrows) to host memory at ptr (e.g. a pinned buffer)."""
     _load().synth_q4k_rows(k, K, n0, nrows, ptr)
@@ -136,6 +155,11 @@ def normals(k: int, n: int, i0: int = 0) -> np.ndarray:
     out = np.empty(n, dtype=np.float64)
     _load().synth_normals(k, i0, n, out.ctypes.data)
     return out
+
+
+def f32_normal(k: int, n: int, i0: int = 0) -> np.ndarray:
+    """float32 of the normals of stream k (round to nearest)."""
+    return normals(k, n, i0).astype(np.float32)
 
 
 def activations(seed: int, M: int, K: int) -> np.ndarray:

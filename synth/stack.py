@@ -10,7 +10,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import LAYER_MATRICES, QK, BLOCK_BYTES, q4k_fill_ptr, weight_key, activations
+from . import (LAYER_MATRICES, QK, BLOCK_BYTES, TAG_H0, TAG_NORM, activations, f32_normal, key,
+               q4k_fill_ptr, q4k_fill_ptr_centered, weight_key)
 
 MATRIX_ORDER = ("q", "k", "v", "o", "gate", "up", "down")
 
@@ -36,6 +37,8 @@ class Stack:
     reads (made by the library's repack call from the generated rows); the
     rows themselves can be regenerated on the host with host_rows()."""
 
+    centered = False  # weight generator: the workload's, or centred (ResStack)
+
     def __init__(self, n_layers, M, shp=None, seed=0, device="cuda:0"):
         import torch
         self.torch = torch
@@ -55,7 +58,8 @@ class Stack:
             for mi, name in enumerate(MATRIX_ORDER):
                 N, K = self.shp[name]
                 nbytes = N * (K // QK) * BLOCK_BYTES
-                q4k_fill_ptr(weight_key(seed, l, mi), K, 0, N, pinned.data_ptr())
+                fill = q4k_fill_ptr_centered if self.centered else q4k_fill_ptr
+                fill(weight_key(seed, l, mi), K, 0, N, pinned.data_ptr())
                 rows[:nbytes].copy_(pinned[:nbytes], non_blocking=False)
                 lay[name] = mk.repack(rows[:nbytes], N, K)
                 torch.cuda.synchronize()
@@ -79,12 +83,44 @@ class Stack:
 
     def host_rows(self, layer, name, rows):
         """The Q4_K bytes of the given weight rows of one matrix (regenerated)."""
-        from . import q4k_rows
+        from . import q4k_rows, q4k_rows_centered
         N, K = self.shp[name]
         mi = MATRIX_ORDER.index(name)
-        full = q4k_rows(weight_key(self.seed, layer, mi), K, 0, N)
+        gen = q4k_rows_centered if self.centered else q4k_rows
+        full = gen(weight_key(self.seed, layer, mi), K, 0, N)
         return full[np.asarray(rows)]
 
     @property
     def weight_bytes(self):
         return weight_bytes(self.shp, self.n_layers)
+
+
+def norm_weights(seed, layer, which, H):
+    """fp32 RMSNorm weight [H] of one layer (which: 0 before q/k/v, 1 before
+    gate/up): 1 + 0.25 z, z ~ N(0,1)."""
+    return (1.0 + 0.25 * f32_normal(key(seed, TAG_NORM, layer, which), H).astype(np.float64)
+            ).astype(np.float32)
+
+
+def residual_input(seed, M, H):
+    """fp32 [M, H] residual stream entering layer 0: N(0,1) values."""
+    return f32_normal(key(seed, TAG_H0, M, H), M * H).reshape(M, H)
+
+
+class ResStack(Stack):
+    """A Stack for the residual walk: centred weights (about zero mean, so
+    the stream stays in range without a mean-removing norm), per-layer fp32
+    RMSNorm weights, the fp32 residual input h0, and per-layer fp32 residual
+    outputs h_mid (after o) and h_out (after down) next to the usual ones."""
+
+    centered = True
+
+    def __init__(self, n_layers, M, shp=None, seed=0, device="cuda:0"):
+        super().__init__(n_layers, M, shp, seed, device)
+        torch = self.torch
+        H = self.H
+        self.norms = [[torch.from_numpy(norm_weights(seed, l, j, H)).to(device) for j in (0, 1)]
+                      for l in range(n_layers)]
+        self.h0 = torch.from_numpy(residual_input(seed, M, H)).to(device)
+        for io in self.io:
+            io["h"] = [torch.empty((M, H), dtype=torch.float32, device=device) for _ in range(2)]

@@ -16,6 +16,17 @@
  *             (0..63 for scales/mins, 0..15 for quants), independently.
  *   activations : binary16 of z, z ~ N(0,1), round-to-nearest-even.
  *
+ * Centred blocks (synth_q4k_blocks_centered, for the residual layer walk,
+ * whose norms do not remove a common offset): the same draws, then every
+ * sub-block gets scale sc = 1 + (2 bits of the original scale bytes) in
+ * 1..4 and min m = 15 * sc, and dmin = binary16(|z| * 0.5e-3) from the same
+ * normal z as d, so that a weight d*sc*q - dmin*m = d*sc*(q - 7.5) (up to
+ * the roundings of d and dmin) has mean about zero over the uniform quants. The 12 scale bytes are packed in the
+ * Q4_K layout: bytes 0-3 hold the 6-bit scales of sub-blocks 0-3 and, in
+ * bits 6-7, the top bits of the scales of 4-7; bytes 4-7 the same for the
+ * mins; bytes 8-11 the low 4 bits of the scale (low nibble) and min (high
+ * nibble) of sub-blocks 4-7.
+ *
  * Random source: SplitMix64 (Steele, Lea & Flood, "Fast splittable
  * pseudorandom number generators", OOPSLA 2014). Output i of the stream with
  * key k is mix(k + (i+1)*0x9E3779B97F4A7C15), where mix is the published
@@ -116,6 +127,40 @@ void synth_q4k_blocks(uint64_t key, uint64_t b0, uint64_t nb, uint8_t* out) {
     blk[0] = (uint8_t)d; blk[1] = (uint8_t)(d >> 8);
     blk[2] = (uint8_t)dmin; blk[3] = (uint8_t)(dmin >> 8);
   }
+}
+
+/* As synth_q4k_blocks, with centred scales and mins (see the header). */
+void synth_q4k_blocks_centered(uint64_t key, uint64_t b0, uint64_t nb, uint8_t* out) {
+  synth_q4k_blocks(key, b0, nb, out);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < (int64_t)nb; ++i) {
+    uint8_t* blk = out + (size_t)i * SYNTH_BLOCK_BYTES;
+    /* dmin from the same normal as d, halved before the rounding */
+    double z0, z1;
+    synth_normal_pair(synth_draw(key, (b0 + (uint64_t)i) * SYNTH_DRAWS_PER_BLOCK), &z0, &z1);
+    const uint16_t dmin = synth_f64_to_f16(fabs(z0) * 0.5e-3);
+    blk[2] = (uint8_t)dmin;
+    blk[3] = (uint8_t)(dmin >> 8);
+    /* two random bits per sub-block from the (uniform) original scale bytes */
+    uint8_t* s12 = blk + 4;
+    const unsigned r = (unsigned)s12[0] | ((unsigned)s12[1] << 8);
+    int sc[8], mn[8];
+    for (int j = 0; j < 8; ++j) {
+      sc[j] = 1 + (int)((r >> (2 * j)) & 3u);
+      mn[j] = 15 * sc[j];
+    }
+    for (int j = 0; j < 4; ++j) {
+      s12[j] = (uint8_t)((sc[j] & 63) | ((sc[j + 4] >> 4) << 6));
+      s12[j + 4] = (uint8_t)((mn[j] & 63) | ((mn[j + 4] >> 4) << 6));
+      s12[j + 8] = (uint8_t)((sc[j + 4] & 15) | ((mn[j + 4] & 15) << 4));
+    }
+  }
+}
+
+/* Rows [n0, n0+nrows) of a centred (N, K) matrix. */
+void synth_q4k_rows_centered(uint64_t key, int64_t K, int64_t n0, int64_t nrows, uint8_t* out) {
+  uint64_t kb = (uint64_t)(K / 256);
+  synth_q4k_blocks_centered(key, (uint64_t)n0 * kb, (uint64_t)nrows * kb, out);
 }
 
 /* Write the blocks of whole weight rows [n0, n0+nrows) of an (N, K) matrix

@@ -364,6 +364,78 @@ def test_gemm_std_alternating_row_closed_form():
         assert np.allclose(S, f * Sz, rtol=1e-12), s
 
 
+# --- the residual walk: RMSNorm scale, scaled product, SiLU --------------------
+def test_rms_inv_closed_forms():
+    """Constant rows c: 1/sqrt(c^2 + eps); alternating +-a: 1/sqrt(a^2 + eps);
+    a (3, 4, 3, 4, ...) row: mean square 12.5. A dropped square, a missing
+    1/N or eps outside the root breaks one of them."""
+    h = np.array([[2.0] * 8, [-3.0] * 8, [1.5, -1.5] * 4, [3.0, 4.0] * 4, [0.0] * 8])
+    for eps in (0.0, 1e-6, 0.25):
+        r = oracle.rms_inv(h, eps)
+        want = 1.0 / np.sqrt(np.array([4.0, 9.0, 2.25, 12.5, 0.0]) + eps)
+        if eps == 0.0:
+            assert np.allclose(r[:4], want[:4], rtol=1e-15) and np.isinf(r[4])
+        else:
+            assert np.allclose(r, want, rtol=1e-15)
+
+
+def test_rms_inv_matches_numpy_and_scales():
+    h = synth.normals(synth.key(20, 1), 6 * 1000).reshape(6, 1000) * 7.0
+    r = oracle.rms_inv(h, 1e-6)
+    assert np.allclose(r, 1.0 / np.sqrt((h * h).mean(axis=1) + 1e-6), rtol=1e-13)
+    # without eps the scale is exactly inverse-proportional to a power-of-two factor
+    assert np.array_equal(oracle.rms_inv(h * 8.0, 0.0) * 8.0, oracle.rms_inv(h, 0.0))
+
+
+def test_gemm_rms_reduces_to_gemm_and_scales_exactly():
+    """At unit scale the normed product is the plain oracle GEMM bit for bit;
+    a power-of-two row scale scales y and S exactly; a general scale agrees
+    with r * gemm to rounding."""
+    M, N, K = 3, 23, 768
+    W = synth.q4k_matrix(synth.key(21, 1), N, K)
+    X = synth.f16_normal(synth.key(21, 2), M * K).reshape(M, K)
+    y0, S0 = oracle.gemm(W, X)
+    y1, S1 = oracle.gemm_rms(W, X, np.ones(M))
+    assert np.array_equal(y1, y0) and np.array_equal(S1, S0)
+    r2 = np.array([0.125, 4.0, 2.0 ** -20])
+    y2, S2 = oracle.gemm_rms(W, X, r2)
+    assert np.array_equal(y2, y0 * r2[:, None]) and np.array_equal(S2, S0 * r2[:, None])
+    r3 = np.array([0.3, 1.7, 0.05])
+    y3, S3 = oracle.gemm_rms(W, X, r3)
+    assert np.all(np.abs(y3 - y0 * r3[:, None]) <= 1e-13 * S3)
+    # numpy: scale the decoded input, float64 matmul with the dequantized weights
+    t = X.astype(np.float64) * r3[:, None]
+    w = oracle.dequant_rows(W, K)
+    assert np.all(np.abs(y3 - t @ w.T) <= 1e-12 * S3)
+
+
+def test_silu_identities_and_values():
+    """silu(v) - silu(-v) = v; silu(0) = 0; silu(1) = e / (1 + e); silu(v) -> v
+    for large v and -> 0 for very negative v; numpy's v / (1 + exp(-v))."""
+    v = synth.normals(synth.key(22, 1), 2000) * 6.0
+    a, b = oracle.silu(v), oracle.silu(-v)
+    assert np.allclose(a - b, v, rtol=1e-14, atol=1e-15)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    e = np.e
+    assert abs(oracle.silu(np.array([1.0]))[0] - e / (1.0 + e)) <= 1e-16
+    big = oracle.silu(np.array([40.0, -40.0]))
+    assert big[0] == 40.0 and 0.0 > big[1] > -1e-15
+    assert np.allclose(a, v / (1.0 + np.exp(-v)), rtol=1e-15, atol=1e-300)
+
+
+def test_centered_generator_gives_zero_mean_weights():
+    """The centred blocks of the residual walk: scales 1..4, mins 15*scale,
+    dmin about d/2, so each sub-block is d*sc*(q - 7.5) up to the rounding of
+    dmin (checked through the pinned block decoder)."""
+    W = synth.q4k_rows_centered(synth.key(23, 1), 1024, 0, 32)
+    for row in W.reshape(-1, 144)[:64]:
+        d, dmin, sc, mn, q = oracle.decode_block(row)
+        assert np.all((sc >= 1) & (sc <= 4)) and np.array_equal(mn, 15 * sc)
+        assert abs(dmin - d / 2) <= 2.0 ** -11 * d + 2.0 ** -24  # two binary16 roundings
+    w = oracle.dequant_rows(W, 1024)
+    assert abs(w.mean()) < 0.01 * w.std()
+
+
 def test_within_bound_rule():
     y_ref = np.array([1.0, 0.0, -2.0])
     S = np.array([10.0, 0.0, 4.0])
