@@ -76,6 +76,15 @@ class _LayerIO(ctypes.Structure):
     _fields_ = [("y", ctypes.c_void_p * 7), ("x", ctypes.c_void_p * 4)]
 
 
+class _LayerResIO(ctypes.Structure):
+    _fields_ = [("y", ctypes.c_void_p * 7), ("x", ctypes.c_void_p * 4),
+                ("h_mid", ctypes.c_void_p), ("h_out", ctypes.c_void_p)]
+
+
+class _LayerNorm(ctypes.Structure):
+    _fields_ = [("attn", ctypes.c_void_p), ("ffn", ctypes.c_void_p)]
+
+
 MATRIX_NAMES = ("q", "k", "v", "o", "gate", "up", "down")
 
 
@@ -111,6 +120,10 @@ def lib():
                                       vp, vp, vp, sz, vp]
             L.mk_q4k_step_status.restype = i
             L.mk_q4k_step_status.argtypes = [vp, ctypes.POINTER(i)]
+        if hasattr(L, "mk_q4k_step_res"):
+            L.mk_q4k_step_res.restype = i
+            L.mk_q4k_step_res.argtypes = [ctypes.POINTER(_Layer), ctypes.POINTER(_LayerNorm),
+                                          ctypes.POINTER(_LayerResIO), i, i, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -240,6 +253,29 @@ def step(layers, io, x0, x_out, workspace, M: int, stream=None) -> None:
             ioarr[i].x[p] = _ptr(d["x"][p])
     rc = lib().mk_q4k_step(larr, ioarr, len(layers), M, _ptr(x0), _ptr(x_out), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc)
+
+
+def step_res(layers, io, norms, h0, workspace, M: int, stream=None) -> None:
+    """Enqueue the residual walk. layers as for step(); io: list of dicts with
+    'y' (7 float32 tensors), 'x' (4 float16 tensors) and 'h' (2 float32 [M, H]
+    tensors: the residual after o and after down); norms: list of pairs of
+    float32 [H] tensors (before q/k/v, before gate/up); h0: float32 [M, H]."""
+    larr = _layers_struct(layers)
+    ioarr = (_LayerResIO * len(io))()
+    narr = (_LayerNorm * len(norms))()
+    for i, d in enumerate(io):
+        for t in range(7):
+            ioarr[i].y[t] = _ptr(d["y"][t])
+        for p in range(4):
+            ioarr[i].x[p] = _ptr(d["x"][p])
+        ioarr[i].h_mid = _ptr(d["h"][0])
+        ioarr[i].h_out = _ptr(d["h"][1])
+    for i, (a, f) in enumerate(norms):
+        narr[i].attn = _ptr(a)
+        narr[i].ffn = _ptr(f)
+    rc = lib().mk_q4k_step_res(larr, narr, ioarr, len(layers), M, _ptr(h0), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc)
 
 

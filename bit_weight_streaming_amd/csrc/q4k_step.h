@@ -61,13 +61,31 @@ struct DevPhase {
   unsigned cs_off[3];  // byte offset of each segment matrix's column sums
                        // in its tile-record buffer (after the records)
   double inv_k;        // 1 / K (the row statistics of the input run over K)
+  int norm;            // what the products of the phase are scaled by per row:
+                       // NORM_STD, NORM_RMS or NORM_NONE
 };
+
+// Row scaling of a phase's products. NORM_STD: the standardization of the
+// binary16 input, (z - mean * colsum) / sqrt(var + 1e-6), from the sums of x
+// and x^2. NORM_RMS (residual walk): z / sqrt(mean(h^2) + 1e-6) of the fp32
+// residual h whose normed cast is the input, from the sum of h^2 held as two
+// integer words (see RMS_SCALE). NORM_NONE: z itself.
+constexpr int NORM_STD = 0, NORM_RMS = 1, NORM_NONE = 2;
+
+// Sum of h^2 in the residual walk: each term (a tile row's fp32 sum of
+// squares) is rounded to an integer at scale 2^40 and split at 2^32 into a
+// high and a low word, added separately (order independent); the total is
+// hi * 2^32 + lo at the same scale. A term must stay below 2^42 (unscaled).
+constexpr double RMS_SCALE = 1099511627776.0;     // 2^40
+constexpr double RMS_TERM_MAX = 4398046511104.0;  // 2^42
 
 // Device copy of one layer's pointers.
 struct DevLayer {
   const uint8_t* w[7];
   float* y[7];
   uint16_t* x[4];
+  float* h[2];        // residual walk: fp32 residual after o (h[0]) and after down (h[1])
+  const float* g[2];  // residual walk: RMSNorm weights before q/k/v (g[0]) and gate/up (g[1])
 };
 
 struct StepParams {
@@ -78,6 +96,7 @@ struct StepParams {
   int H;                 // hidden size (x width)
   const uint16_t* x0;
   uint16_t* x_out;
+  const float* h0;       // residual walk: fp32 residual entering layer 0
   char* ws;              // workspace base
   size_t layers_off;     // DevLayer table
   size_t done_off;       // DONE_CTRS finished-tile counters

@@ -407,6 +407,17 @@ __device__ __forceinline__ float2 row_moments(const unsigned long long* tot_s, i
   return float2{(float)mean, __builtin_amdgcn_rsqf((float)(var + 1e-6))};
 }
 
+// Row m's (mean, scale) pair of a phase: the products become
+// (z - mean * colsum) * scale (see NORM_STD, NORM_RMS, NORM_NONE).
+__device__ __forceinline__ float2 phase_moments(const unsigned long long* tot_s, int m,
+                                                const DevPhase& ph) {
+  if (ph.norm == NORM_STD) return row_moments(tot_s, m, ph.inv_k);
+  if (ph.norm == NORM_NONE) return float2{0.f, 1.f};
+  const double ss = (double)(long long)tot_s[2 * m] * 4294967296.0 + (double)(long long)tot_s[2 * m + 1];
+  const double ms = ss * (ph.inv_k * (1.0 / RMS_SCALE));
+  return float2{0.f, __builtin_amdgcn_rsqf((float)(ms + 1e-6))};
+}
+
 // Wait until every tile of the phases up to (l, p) has been counted finished.
 __device__ __forceinline__ bool wait_done(const StepParams& P, const DevPhase* PH, int l, int p,
                                           int* abort_s) {
@@ -480,19 +491,34 @@ __device__ __forceinline__ floatx4 await_piece(const StepParams& P, __amdgpu_buf
   return v;
 }
 
+// Residual-walk operands of one finished tile column, loaded with the
+// partial pieces: the four rows of the residual entering the add (hin) and
+// the norm weight of the next input at the column (gv).
+struct ResCol {
+  float hin[4];
+  float gv;
+};
+
 // One finished tile column (lane ln: column ln % 16, rows 4(ln/16)..+3) of
 // the phase: z holds the products with the binary16 input x of the phase.
-// The matrix output is the product with the row-standardized input,
-//   y[m][n] = inv_m * (z[m][n] - mean_m * colsum[n]),
-// written to the layer outputs. For the matrices that feed the next phase,
-// the next phase's input is the binary16 cast of y (of y_gate * y_up, taken
-// in fp32, for the paired phase), written as pairs of columns with
-// device-coherent 32-bit stores, and its row sums over the tile's columns
-// go into the workgroup's statistics (fixed point, LDS integer atomics).
-template <int NM>
-__device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase& ph,
+// The matrix output is the product with the row-normed input,
+//   y[m][n] = scale_m * (z[m][n] - mean_m * colsum[n]),
+// written to the layer outputs (mean 0 and no column sums outside the
+// standardization). For the matrices that feed the next phase, the next
+// phase's input is a binary16 cast, written as pairs of columns with
+// device-coherent 32-bit stores:
+//   MODE 0: of y (of y_gate * y_up, taken in fp32, for the paired phase);
+//           the row sums of the cast values go into the statistics;
+//   MODE 1 (residual walk), by phase: A: of y (q); B and D: the residual
+//           add h_new = h_in + y is written, and the cast is of h_new times
+//           the next norm weight, the statistics summing h_new^2; C: of
+//           silu(y_gate) * y_up in fp32.
+// Statistics go into the workgroup's LDS integer sums (fixed point).
+template <int NM, int MODE>
+__device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase& ph, int p,
                                              const DevLayer* L, uint16_t* xn, bool stats,
-                                             int tg, int ln, const floatx4* z, const float* csum,
+                                             float* h_new, const ResCol& rc, int tg, int ln,
+                                             const floatx4* z, const float* csum,
                                              const float2* mom_s, unsigned long long* wst) {
   const int M = P.M;
   const int seg = __builtin_amdgcn_readfirstlane(seg_of(ph, tg));  // uniform per wave
@@ -500,11 +526,13 @@ __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase
   const int cs = (tg - ph.seg_t0[seg]) * 16 + (ln & 15);
   const int g = ln >> 4;
   const bool feeds = xn != nullptr && seg == 0;  // k and v feed nothing
+  const bool res = MODE == 1 && (p == 1 || p == 3);
   float* yp[NM];
 #pragma unroll
   for (int q = 0; q < NM; ++q) yp[q] = L->y[ph.mat0 + seg + q];
   const int Kn = ph.seg_n[0];  // width of the next phase's input
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(xn, (unsigned)(M * Kn * 2));
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(h_new, (unsigned)(M * nseg * 4));
   float s1[4], s2[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -519,12 +547,26 @@ __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase
 #pragma unroll
       for (int q = 0; q < NM; ++q) to_global(yp[q])[(size_t)m * nseg + cs] = y[q];
     }
-    float hv = 0.f;
+    float hv = 0.f, hs = 0.f;
+    if (res) {
+      // read in a later phase by other workgroups: device-coherent store
+      const float hn = rc.hin[r] + y[0];
+      if (valid)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, hn), hr,
+                                              (unsigned)((m * nseg + cs) * 4), 0, kCoherent);
+      hs = valid ? hn : 0.f;
+    }
     if (feeds) {
-      // the value cast is the fp32 one (y, or the fp32 product of y_gate and
-      // y_up): the empty asm keeps the compiler from fusing the last multiply
-      // into a mixed-precision op that rounds once, straight to binary16
-      float v = NM == 2 ? y[0] * y[1] : y[0];
+      // the value cast is the fp32 one (see above): the empty asm keeps the
+      // compiler from fusing the last multiply into a mixed-precision op
+      // that rounds once, straight to binary16
+      float v;
+      if (MODE == 1 && res)
+        v = (rc.hin[r] + y[0]) * rc.gv;
+      else if (MODE == 1 && NM == 2)
+        v = y[0] / (1.f + expf(-y[0])) * y[NM - 1];
+      else
+        v = NM == 2 ? y[0] * y[NM - 1] : y[0];
       asm volatile("" : "+v"(v));
       const _Float16 h = (_Float16)v;
       const int hb = bit_cast_<uint16_t>(h);
@@ -532,15 +574,18 @@ __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase
       if (valid && (cs & 1) == 0)
         __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(hb & 0xFFFF) | ((uint32_t)hp << 16), xr,
                                               (unsigned)((m * Kn + cs) * 2), 0, kCoherent);
+      if (MODE == 1 && valid && (hb & 0x7C00) == 0x7C00)
+        set_status(P, MK_ERANGE);  // the cast overflowed (or met a NaN)
       hv = valid ? (float)h : 0.f;
     }
-    s1[r] = hv;
-    s2[r] = hv * hv;
+    s1[r] = MODE == 0 ? hv : 0.f;
+    s2[r] = MODE == 0 ? hv * hv : hs * hs;
   }
-  if (!feeds || !stats) return;
+  if (!stats) return;
+  if (MODE == 0 && !feeds) return;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    s1[r] = row_sum16(s1[r]);
+    if (MODE == 0) s1[r] = row_sum16(s1[r]);
     s2[r] = row_sum16(s2[r]);
   }
   if ((ln & 15) == 0) {
@@ -548,12 +593,25 @@ __device__ __forceinline__ void fixup_finish(const StepParams& P, const DevPhase
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * g + r;
       if (m >= M) break;
-      const double f1 = (double)s1[r] * STAT_SCALE_SUM, f2 = (double)s2[r] * STAT_SCALE_SQ;
-      if (!(fabs(f1) < STAT_TERM_MAX) || !(f2 < STAT_TERM_MAX)) {
-        set_status(P, MK_ERANGE);  // an overflowed cast or values too large to sum
+      if (MODE == 0) {
+        const double f1 = (double)s1[r] * STAT_SCALE_SUM, f2 = (double)s2[r] * STAT_SCALE_SQ;
+        if (!(fabs(f1) < STAT_TERM_MAX) || !(f2 < STAT_TERM_MAX)) {
+          set_status(P, MK_ERANGE);  // an overflowed cast or values too large to sum
+        } else {
+          atomicAdd(&wst[2 * m], (unsigned long long)round_i64(f1));
+          atomicAdd(&wst[2 * m + 1], (unsigned long long)round_i64(f2));
+        }
       } else {
-        atomicAdd(&wst[2 * m], (unsigned long long)round_i64(f1));
-        atomicAdd(&wst[2 * m + 1], (unsigned long long)round_i64(f2));
+        const double sq = (double)s2[r];
+        if (!(sq < RMS_TERM_MAX)) {
+          set_status(P, MK_ERANGE);  // a residual too large to sum (or not finite)
+        } else {
+          const double t = __builtin_rint(sq * RMS_SCALE);
+          const double hi = __builtin_floor(t * (1.0 / 4294967296.0));
+          const double lo = __builtin_fma(-hi, 4294967296.0, t);
+          atomicAdd(&wst[2 * m], (unsigned long long)(long long)hi);
+          atomicAdd(&wst[2 * m + 1], (unsigned long long)(long long)lo);
+        }
       }
     }
   }
@@ -575,17 +633,18 @@ __device__ __forceinline__ void load_colsum(const DevPhase& ph, const DevLayer* 
 // The next phase's input buffer (binary16 [M][Kn]) and the statistics slots
 // of it, after phase p of layer l; the last layer's down projection writes
 // x_out and no statistics.
+template <int MODE>
 __device__ __forceinline__ uint16_t* next_input(const StepParams& P, const DevLayer* ltab, int l,
                                                 int p) {
   // both candidates are read and the value selected (a selected address
   // would make the compiler read it with a flat load)
   const int ln = l + 1 < P.n_layers ? l + 1 : l;
   uint16_t* nx = uni(p < 3 ? ltab[l].x[p + 1] : ltab[ln].x[0]);
-  uint16_t* xo = uni(P.x_out);
+  uint16_t* xo = MODE == 0 ? uni(P.x_out) : nullptr;  // the residual walk ends in h
   return (p == 3 && l + 1 >= P.n_layers) ? xo : nx;
 }
 
-template <int NM>
+template <int NM, int MODE>
 __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase& ph, int p, int l,
                                             const DevLayer* ltab, const Assign& a, int ffirst,
                                             int nfin, unsigned long long* wst,
@@ -593,8 +652,26 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
   const int M = P.M;
   const DevLayer* L = &ltab[l];
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
-  uint16_t* xn = next_input(P, ltab, l, p);
-  const bool stats = p < 3 || l + 1 < P.n_layers;
+  uint16_t* xn = next_input<MODE>(P, ltab, l, p);
+  // MODE 0: every next input but x_out has statistics; MODE 1: the normed
+  // ones (after B: gate/up's input; after D: the next layer's q/k/v input)
+  const bool stats = MODE == 0 ? (p < 3 || l + 1 < P.n_layers)
+                               : (p == 1 || (p == 3 && l + 1 < P.n_layers));
+  // residual walk, B and D: the residual entering the add, its output and
+  // the next input's norm weight (all [M][H] / [H], read at the tile's columns)
+  const bool res = MODE == 1 && (p == 1 || p == 3);
+  const float* h_in = nullptr;
+  float* h_new = nullptr;
+  const float* gn = nullptr;
+  if (res) {
+    const int lg = l + 1 < P.n_layers ? l + 1 : l;
+    h_in = p == 1 ? (l == 0 ? P.h0 : ltab[l > 0 ? l - 1 : 0].h[1]) : L->h[0];
+    h_new = p == 1 ? L->h[0] : L->h[1];
+    gn = p == 1 ? L->g[1] : ltab[lg].g[0];  // unused after the last layer
+    h_in = uni(h_in);
+    h_new = uni(h_new);
+    gn = uni(gn);
+  }
   const int ln_ = p < 3 ? l : l + 1, pn = p < 3 ? p + 1 : 0;
   long long* stl = reinterpret_cast<long long*>(P.ws + P.stats_off) +
                    (size_t)(ln_ * 4 + pn) * STAT_SLOTS * M * 2;
@@ -610,7 +687,27 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
     const unsigned base = (unsigned)tg * ph.sk * NM * 1024u + ln * 16;
     const bool rows_ok = 4 * (ln >> 4) < M;  // lanes holding only rows past M do not wait
     float csum[NM];
-    load_colsum<NM>(ph, L, tg, ln, csum);
+    ResCol rc = {};
+    if (MODE == 0) {
+      load_colsum<NM>(ph, L, tg, ln, csum);
+    } else {
+#pragma unroll
+      for (int q = 0; q < NM; ++q) csum[q] = 0.f;  // no mean term
+      if (res) {
+        // clamped, so every lane loads (rows past M and columns past N are
+        // never stored)
+        // h_in was written by other workgroups (device-coherent loads)
+        const int cs = min((tg - ph.seg_t0[0]) * 16 + (ln & 15), ph.seg_n[0] - 1);
+        const __amdgpu_buffer_rsrc_t hir = make_rsrc(h_in, (unsigned)(M * ph.seg_n[0] * 4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          rc.hin[r] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(
+                         hir, (unsigned)((min(4 * (ln >> 4) + r, M - 1) * ph.seg_n[0] + cs) * 4), 0,
+                         kCoherent));
+        rc.gv = to_global(gn)[cs];
+      }
+    }
     floatx4 y[NM];
 #pragma unroll
     for (int q = 0; q < NM; ++q) y[q] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -634,7 +731,7 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
         }
       }
     }
-    fixup_finish<NM>(P, ph, L, xn, stats, tg, ln, y, csum, mom_s, wst);
+    fixup_finish<NM, MODE>(P, ph, p, L, xn, stats, h_new, rc, tg, ln, y, csum, mom_s, wst);
   }
   __syncthreads();
   if (stats && tid < 2 * M) {
@@ -680,7 +777,7 @@ __device__ __forceinline__ bool wait_start(const StepParams& P, int* abort_s) {
 // standardization of the phase input (its row statistics were added up while
 // the input was staged) and count the tiles as finished. Spreading the finishing
 // over the slices keeps every workgroup's share of it equal.
-template <int NM>
+template <int NM, int MODE>
 __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhase& ph, int p,
                                               int l, const DevLayer* ltab, const Assign& a,
                                               int ffirst, int nfin, const char* contrib,
@@ -714,9 +811,9 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
   if (tid == 0) *abort_s = 0;
   // each row's mean and 1/sqrt(var + 1e-6), once (rows past M: zeros)
   if (tid < STEP_MAX_M)
-    mom_s[tid] = tid < P.M ? row_moments(tot_s, tid, ph.inv_k) : float2{0.f, 0.f};
+    mom_s[tid] = tid < P.M ? phase_moments(tot_s, tid, ph) : float2{0.f, 0.f};
   __syncthreads();
-  fixup_tiles<NM>(P, ph, p, l, ltab, a, ffirst, nfin, wst, mom_s, abort_s, tid);
+  fixup_tiles<NM, MODE>(P, ph, p, l, ltab, a, ffirst, nfin, wst, mom_s, abort_s, tid);
   wait_vm0();
   __syncthreads();
   if (*abort_s) return false;
@@ -731,6 +828,9 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
 
 }  // namespace
 
+// MODE 0: the walk of standardized products between binary16 casts; MODE 1:
+// the residual walk (RMSNorm with weights, residual adds, SiLU * up).
+template <int MODE>
 __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ DevLayer ltab[STEP_MAX_LAYERS];  // every layer's pointers, read from LDS
@@ -804,24 +904,47 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   iter_init(it, ph_s[0], ltab[0].w, wstart[0][wave], wseg[0][wave]);
   ring_fill(ring, it, ph_s[0], ltab[0].w, a, lane);
 
-  // ---- layer-0 input: copy this workgroup's columns of x0 to the layer-0
-  //      phase input and add their row sums to its statistics
+  // ---- layer-0 input: this workgroup's columns of it (MODE 0: a copy of
+  //      x0; MODE 1: the cast of h0 times the first norm weight) and their
+  //      row sums, added to its statistics
   {
     const int c0 = (int)((long long)P.H * w / P.G), c1 = (int)((long long)P.H * (w + 1) / P.G);
     const int nc = c1 - c0;
+    const __amdgpu_buffer_rsrc_t x0r = make_rsrc(ltab[0].x[0], (unsigned)(M * P.H * 2));
     for (int i = tid; i < M * nc; i += STEP_THREADS) {
       const int m = i / nc, cc = c0 + (i - m * nc);
-      const uint16_t hb = to_global(P.x0)[(size_t)m * P.H + cc];
-      to_global(ltab[0].x[0])[(size_t)m * P.H + cc] = hb;
-      const float h = (float)bit_cast_<_Float16>(hb);
-      atomicAdd(&wst_s[2 * m], (unsigned long long)round_i64((double)h * STAT_SCALE_SUM));
-      atomicAdd(&wst_s[2 * m + 1], (unsigned long long)round_i64((double)(h * h) * STAT_SCALE_SQ));
+      if (MODE == 0) {
+        const uint16_t hb = to_global(P.x0)[(size_t)m * P.H + cc];
+        to_global(ltab[0].x[0])[(size_t)m * P.H + cc] = hb;
+        const float h = (float)bit_cast_<_Float16>(hb);
+        atomicAdd(&wst_s[2 * m], (unsigned long long)round_i64((double)h * STAT_SCALE_SUM));
+        atomicAdd(&wst_s[2 * m + 1],
+                  (unsigned long long)round_i64((double)(h * h) * STAT_SCALE_SQ));
+      } else {
+        const float hv = to_global(P.h0)[(size_t)m * P.H + cc];
+        float v = hv * to_global(ltab[0].g[0])[cc];
+        asm volatile("" : "+v"(v));
+        const uint16_t hb = bit_cast_<uint16_t>((_Float16)v);
+        // read by other workgroups after the start barrier: device-coherent
+        __builtin_amdgcn_raw_buffer_store_b16(hb, x0r, (unsigned)((m * P.H + cc) * 2), 0,
+                                              kCoherent);
+        const double sq = (double)hv * (double)hv;
+        if ((hb & 0x7C00) == 0x7C00 || !(sq < RMS_TERM_MAX)) {
+          set_status(P, MK_ERANGE);
+        } else {
+          const double t = __builtin_rint(sq * RMS_SCALE);
+          const double hi = __builtin_floor(t * (1.0 / 4294967296.0));
+          atomicAdd(&wst_s[2 * m], (unsigned long long)(long long)hi);
+          atomicAdd(&wst_s[2 * m + 1],
+                    (unsigned long long)(long long)__builtin_fma(-hi, 4294967296.0, t));
+        }
+      }
     }
     __syncthreads();
     if (tid < 2 * M) {
       long long* st0 = reinterpret_cast<long long*>(P.ws + P.stats_off);
       const long long v = (long long)wst_s[tid];
-      if (!(fabs((double)v) < STAT_TERM_MAX)) set_status(P, MK_ERANGE);
+      if (MODE == 0 && !(fabs((double)v) < STAT_TERM_MAX)) set_status(P, MK_ERANGE);
       if (v != 0)
         __hip_atomic_fetch_add(st0 + (size_t)(w % STAT_SLOTS) * M * 2 + tid, v, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
@@ -845,8 +968,8 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       char* xs_lds = x_lds + (size_t)M * ph.x_stride;
       char* contrib = smem + ph.lds_contrib;
       // ---- stage this phase's binary16 input slice (the first weight
-      //      records are already in flight); layer 0 reads x0 itself
-      stage_slice(l == 0 && p == 0 ? P.x0 : L->x[p], ph.K, M, a,
+      //      records are already in flight); MODE 0 reads layer 0's from x0
+      stage_slice(MODE == 0 && l == 0 && p == 0 ? P.x0 : L->x[p], ph.K, M, a,
                   reinterpret_cast<const long long*>(P.ws + P.stats_off) +
                       (size_t)(l * 4 + p) * STAT_SLOTS * M * 2,
                   tot_s, x_lds, ph.x_stride, xs_lds, ph.nkb, tid);
@@ -865,9 +988,9 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       //      every tile of this phase is finished
       const int ffirst = uni(fin_s[p].x), nfin = uni(fin_s[p].y);
       const bool ok = ph.nm == 2
-                          ? phase_outputs<2>(P, ph, p, l, ltab, a, ffirst, nfin, contrib, &abort_s,
+                          ? phase_outputs<2, MODE>(P, ph, p, l, ltab, a, ffirst, nfin, contrib, &abort_s,
                                              wst_s, tot_s, mom_s, tid)
-                          : phase_outputs<1>(P, ph, p, l, ltab, a, ffirst, nfin, contrib, &abort_s,
+                          : phase_outputs<1, MODE>(P, ph, p, l, ltab, a, ffirst, nfin, contrib, &abort_s,
                                              wst_s, tot_s, mom_s, tid);
       if (!ok) return;
       // the next staging adds the next input's statistics from zero (ordered
@@ -1096,39 +1219,13 @@ struct TableCache {
 TableCache g_table_cache[64];
 std::mutex g_table_mu;
 
-}  // namespace
-
-}  // namespace mk
-
-extern "C" {
-
-size_t mk_q4k_step_workspace_bytes(const mk_q4k_layer* layer0, int n_layers, int M) {
-  if (mk::check_step_shapes(layer0, 1, M) != MK_OK || n_layers < 1) return 0;
-  mk::StepPlan sp;
-  mk::plan_phases(*layer0, n_layers, M, mk::kMaxG, sp);
-  return sp.ok ? sp.total : 0;
-}
-
-int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_layers, int M,
-                const uint16_t* x0, uint16_t* x_out, void* workspace, size_t ws_bytes,
-                void* stream) {
-  using namespace mk;
-  int rc = check_step_shapes(layers, n_layers, M);
-  if (rc != MK_OK) return rc;
-  if (!io || !x0 || !x_out || !workspace) return MK_EINVAL;
-  if (!al16(x0) || !al16(x_out) || !al16(workspace)) return MK_EALIGN;
-  for (int l = 0; l < n_layers; ++l) {
-    const mk_q4k_layer& L = layers[l];
-    const void* w[7] = {L.q.w, L.k.w, L.v.w, L.o.w, L.gate.w, L.up.w, L.down.w};
-    for (int i = 0; i < 7; ++i) {
-      if (!w[i] || !io[l].y[i]) return MK_EINVAL;
-      if (!al16(w[i]) || !al16(io[l].y[i])) return MK_EALIGN;
-    }
-    for (int i = 0; i < 4; ++i) {
-      if (!io[l].x[i]) return MK_EINVAL;
-      if (!al16(io[l].x[i])) return MK_EALIGN;
-    }
-  }
+// The part of a step call both walks share: plan, checks, the device layer
+// table (re-sent only when it changed), the clear kernel and the launch.
+template <int MODE>
+int launch_walk(const mk_q4k_layer* layers, const std::vector<DevLayer>& table, int n_layers,
+                int M, const uint16_t* x0, uint16_t* x_out, const float* h0, void* workspace,
+                size_t ws_bytes, void* stream) {
+  int rc;
   int cus = 0;
   rc = current_gfx950(&cus);
   if (rc != MK_OK) return rc;
@@ -1136,6 +1233,8 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
   StepPlan sp;
   plan_phases(layers[0], n_layers, M, G, sp);
   if (!sp.ok) return MK_EINVAL;
+  for (int p = 0; p < 4; ++p)
+    sp.ph[p].norm = MODE == 0 ? NORM_STD : (p == 0 || p == 2 ? NORM_RMS : NORM_NONE);
   if (ws_bytes < sp.total) return MK_EWORKSPACE;
   for (int p = 0; p < 4; ++p) {
     if (sp.ph[p].sk > G) return MK_EINVAL;
@@ -1144,11 +1243,11 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
   }
   const size_t lds = lds_bytes(sp, M);
   if (lds + kStaticLds > kLdsLimit) return MK_EINVAL;
-  hipError_t e = hipFuncSetAttribute((const void*)q4k_step_kernel,
+  hipError_t e = hipFuncSetAttribute((const void*)q4k_step_kernel<MODE>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return MK_EHIP;
   int occ = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)q4k_step_kernel,
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)q4k_step_kernel<MODE>,
                                                    STEP_THREADS, lds);
   if (e != hipSuccess) return MK_EHIP;
   if (occ < 1) return MK_EOCCUPANCY;
@@ -1157,16 +1256,6 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
   char* ws = static_cast<char*>(workspace);
   // layer table
   {
-    std::vector<DevLayer> table(n_layers);
-    for (int l = 0; l < n_layers; ++l) {
-      const mk_q4k_layer& L = layers[l];
-      const mk_q4k_mat* m[7] = {&L.q, &L.k, &L.v, &L.o, &L.gate, &L.up, &L.down};
-      for (int i = 0; i < 7; ++i) {
-        table[l].w[i] = static_cast<const uint8_t*>(m[i]->w);
-        table[l].y[i] = io[l].y[i];
-      }
-      for (int i = 0; i < 4; ++i) table[l].x[i] = io[l].x[i];
-    }
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MK_EHIP;
     std::lock_guard<std::mutex> lk(g_table_mu);
@@ -1202,6 +1291,7 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
   P.H = layers[0].q.K;
   P.x0 = x0;
   P.x_out = x_out;
+  P.h0 = h0;
   P.ws = ws;
   P.layers_off = sp.layers_off;
   P.done_off = sp.done_off;
@@ -1209,9 +1299,93 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
   P.start_off = sp.start_off;
   P.status_off = sp.status_off;
   P.lds_bytes = lds;
-  hipLaunchKernelGGL(q4k_step_kernel, dim3(G), dim3(STEP_THREADS), lds, st, P);
+  hipLaunchKernelGGL(q4k_step_kernel<MODE>, dim3(G), dim3(STEP_THREADS), lds, st, P);
   e = hipGetLastError();
   return e == hipSuccess ? MK_OK : MK_EHIP;
+}
+
+// Host-side checks of the per-layer weights and outputs both walks share.
+int check_layer_io(const mk_q4k_layer* layers, float* const* y, uint16_t* const* x, int l) {
+  const mk_q4k_layer& L = layers[l];
+  const void* w[7] = {L.q.w, L.k.w, L.v.w, L.o.w, L.gate.w, L.up.w, L.down.w};
+  for (int i = 0; i < 7; ++i) {
+    if (!w[i] || !y[i]) return MK_EINVAL;
+    if (!al16(w[i]) || !al16(y[i])) return MK_EALIGN;
+  }
+  for (int i = 0; i < 4; ++i) {
+    if (!x[i]) return MK_EINVAL;
+    if (!al16(x[i])) return MK_EALIGN;
+  }
+  return MK_OK;
+}
+
+void fill_table(const mk_q4k_layer& L, float* const* y, uint16_t* const* x, DevLayer& t) {
+  const mk_q4k_mat* m[7] = {&L.q, &L.k, &L.v, &L.o, &L.gate, &L.up, &L.down};
+  memset(&t, 0, sizeof(t));
+  for (int i = 0; i < 7; ++i) {
+    t.w[i] = static_cast<const uint8_t*>(m[i]->w);
+    t.y[i] = y[i];
+  }
+  for (int i = 0; i < 4; ++i) t.x[i] = x[i];
+}
+
+
+}  // namespace
+
+}  // namespace mk
+
+extern "C" {
+
+size_t mk_q4k_step_workspace_bytes(const mk_q4k_layer* layer0, int n_layers, int M) {
+  if (mk::check_step_shapes(layer0, 1, M) != MK_OK || n_layers < 1) return 0;
+  mk::StepPlan sp;
+  mk::plan_phases(*layer0, n_layers, M, mk::kMaxG, sp);
+  return sp.ok ? sp.total : 0;
+}
+
+
+int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_layers, int M,
+                const uint16_t* x0, uint16_t* x_out, void* workspace, size_t ws_bytes,
+                void* stream) {
+  using namespace mk;
+  int rc = check_step_shapes(layers, n_layers, M);
+  if (rc != MK_OK) return rc;
+  if (!io || !x0 || !x_out || !workspace) return MK_EINVAL;
+  if (!al16(x0) || !al16(x_out) || !al16(workspace)) return MK_EALIGN;
+  std::vector<DevLayer> table(n_layers);
+  for (int l = 0; l < n_layers; ++l) {
+    rc = check_layer_io(layers, io[l].y, io[l].x, l);
+    if (rc != MK_OK) return rc;
+    fill_table(layers[l], io[l].y, io[l].x, table[l]);
+  }
+  return launch_walk<0>(layers, table, n_layers, M, x0, x_out, nullptr, workspace, ws_bytes,
+                        stream);
+}
+
+int mk_q4k_step_res(const mk_q4k_layer* layers, const mk_q4k_layer_norm* norms,
+                    const mk_q4k_layer_res_io* io, int n_layers, int M, const float* h0,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  using namespace mk;
+  int rc = check_step_shapes(layers, n_layers, M);
+  if (rc != MK_OK) return rc;
+  if (!io || !norms || !h0 || !workspace) return MK_EINVAL;
+  if (!al16(h0) || !al16(workspace)) return MK_EALIGN;
+  std::vector<DevLayer> table(n_layers);
+  for (int l = 0; l < n_layers; ++l) {
+    rc = check_layer_io(layers, io[l].y, io[l].x, l);
+    if (rc != MK_OK) return rc;
+    if (!io[l].h_mid || !io[l].h_out || !norms[l].attn || !norms[l].ffn) return MK_EINVAL;
+    if (!al16(io[l].h_mid) || !al16(io[l].h_out) || !al16(norms[l].attn) ||
+        !al16(norms[l].ffn))
+      return MK_EALIGN;
+    fill_table(layers[l], io[l].y, io[l].x, table[l]);
+    table[l].h[0] = io[l].h_mid;
+    table[l].h[1] = io[l].h_out;
+    table[l].g[0] = norms[l].attn;
+    table[l].g[1] = norms[l].ffn;
+  }
+  return launch_walk<1>(layers, table, n_layers, M, nullptr, nullptr, h0, workspace, ws_bytes,
+                        stream);
 }
 
 int mk_q4k_step_status(const void* workspace, int* status_out) {

@@ -196,6 +196,53 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
                 const uint16_t* x0, uint16_t* x_out, void* workspace, size_t ws_bytes,
                 void* stream);
 
+/*
+ * The residual walk: the same persistent kernel and products, with the
+ * epilogues of a real decoder layer around them in place of the
+ * standardization (the OpenJet post, "RTX 3090 one card, four coding
+ * agents", paragraph on how parallel decoding works: the one-kernel step
+ * includes the work on either side of each product). With h the fp32
+ * residual stream entering layer l and g_attn, g_ffn its fp32 RMSNorm
+ * weights [H]:
+ *   phase A  x_l = c(h * g_attn)        -> q, k, v = r(h) * (x_l . W)
+ *   phase B  c(q)                       -> o;    h_mid = h + o
+ *   phase C  c(h_mid * g_ffn)           -> gate, up = r(h_mid) * (x . W)
+ *   phase D  c(silu(gate) * up)         -> down; h_out = h_mid + down
+ * where c is the binary16 round-to-nearest-even cast of the fp32 value
+ * (products, sums and silu(v) = v / (1 + exp(-v)) in fp32), and
+ * r(h) = 1 / sqrt(mean_k h^2 + 1e-6) per row, applied exactly after the
+ * product (so the cast is of h * g, not of the normalised value). The
+ * attention between B and o is not part of the walk: o multiplies c(q).
+ * h_out of layer l is the residual entering layer l + 1; h0 enters layer 0.
+ * Shapes, limits, the workspace (mk_q4k_step_workspace_bytes) and the
+ * status word are those of mk_q4k_step; MK_ERANGE there also means a cast
+ * overflowed binary16 or a row's sum of squares left its range (a tile
+ * row's sum of h^2 of 2^42).
+ */
+typedef struct {
+  float* y[7];    /* fp32 [M][N_t] for t = q, k, v, o, gate, up, down          */
+  uint16_t* x[4]; /* binary16 phase inputs A..D: c(h*g_attn) [M][H], c(q) [M][q.N],
+                     c(h_mid*g_ffn) [M][H], c(silu(gate)*up) [M][F]            */
+  float* h_mid;   /* fp32 [M][H] residual after o                              */
+  float* h_out;   /* fp32 [M][H] residual after down                           */
+} mk_q4k_layer_res_io;
+
+typedef struct {
+  const float* attn; /* fp32 [H] RMSNorm weight of the q/k/v input (device)      */
+  const float* ffn;  /* fp32 [H] RMSNorm weight of the gate/up input (device)    */
+} mk_q4k_layer_norm;
+
+/*
+ * mk_q4k_step_res: run the residual walk. layers, norms and io are host
+ * arrays of n_layers entries, read before return; h0 is the device fp32
+ * [M][H] residual entering layer 0. Every device pointer is 16-byte aligned
+ * (MK_EALIGN otherwise); the output buffers must not overlap one another or
+ * the inputs.
+ */
+int mk_q4k_step_res(const mk_q4k_layer* layers, const mk_q4k_layer_norm* norms,
+                    const mk_q4k_layer_res_io* io, int n_layers, int M, const float* h0,
+                    void* workspace, size_t ws_bytes, void* stream);
+
 /* Copy the device status word of the last step run in `workspace` to
  * *status_out (MK_OK, MK_ETIMEOUT or MK_ERANGE). Synchronous; call after the
  * step's stream has completed. */
