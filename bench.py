@@ -225,6 +225,9 @@ def main() -> int:
                     help="only run plain 1 GiB copies (scale for the PMC byte counters)")
     ap.add_argument("--gemm-only", action="store_true",
                     help="only the single-matrix GEMM lines (no 64-layer stack)")
+    ap.add_argument("--walk", choices=("std", "res"), default="std",
+                    help="std: the standardized walk (the benchmark); res: the residual walk "
+                         "(RMSNorm, residual adds, SiLU*up) on centred weights, timed alone")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -239,7 +242,7 @@ def main() -> int:
 
     import torch
     import bit_weight_streaming_amd as mk
-    from synth.stack import Stack
+    from synth.stack import ResStack, Stack
 
     if args.gemm_only:
         torch.cuda.set_device(0)
@@ -250,7 +253,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     log(f"device: {mk.device_info()}")
     t0 = time.time()
-    stack = Stack(args.layers, args.M, seed=args.seed, device=dev)
+    res = args.walk == "res"
+    stack = (ResStack if res else Stack)(args.layers, args.M, seed=args.seed, device=dev)
     torch.cuda.synchronize()
     log(f"stack ready: {args.layers} layers, {stack.weight_bytes / 1e9:.3f} GB of Q4_K weights "
         f"in {time.time() - t0:.1f} s")
@@ -259,7 +263,10 @@ def main() -> int:
                      device=dev)
 
     def step():
-        mk.step(descs, stack.io, stack.x0, stack.x_out, ws, args.M)
+        if res:
+            mk.step_res(descs, stack.io, stack.norms, stack.h0, ws, args.M)
+        else:
+            mk.step(descs, stack.io, stack.x0, stack.x_out, ws, args.M)
 
     for _ in range(args.warmup):
         step()
@@ -298,6 +305,10 @@ def main() -> int:
         f"ms/step, {gbs:.1f} GB/s weights")
 
     gemm = None
+    if res:
+        # the residual walk is timed alone: no GEMM lines, no CPU leg, no
+        # committed counter record for it
+        args.no_gemm = args.no_cpu = True
     if not args.no_gemm:
         gemm = gemm_bench(args.seed)
 
@@ -306,8 +317,12 @@ def main() -> int:
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(stack)
 
+    if res:
+        # fp32 residual: h read and written twice per layer, h0, norm weights
+        H = stack.H
+        ab["total"] += args.layers * (4 * args.M * H * 4 + 2 * H * 4) + args.M * H * 4
     achieved = ab["total"] / t_launch / 1e9
-    traffic = measured_traffic(args.layers, args.M)
+    traffic = None if res else measured_traffic(args.layers, args.M)
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -324,7 +339,9 @@ def main() -> int:
         "config": {
             "workload": (f"decode step: {args.layers} layers x Q4_K q/k/v/o/gate/up/down "
                          f"(H=5120, q=6144, kv=1024, ffn=17408), M={args.M} stacked rows, "
-                         f"one persistent launch"),
+                         f"one persistent launch"
+                         + (", residual walk (RMSNorm, residual adds, SiLU*up; centred weights)"
+                            if res else "")),
             "n_layers": args.layers,
             "M": args.M,
             "weight_bytes": stack.weight_bytes,
@@ -341,7 +358,8 @@ def main() -> int:
             "traffic": traffic,
             "algorithmic_bytes_per_launch": ab["total"],
             "launch_ms": round(t_launch * 1e3, 4),
-            "kernel": "q4k_step_kernel (one launch = one decode step, all layers)",
+            "kernel": ("q4k_step_kernel<1>" if res else "q4k_step_kernel<0>")
+                      + " (one launch = one decode step, all layers)",
         },
         "cpu_baseline": cpu,
         "gemm": gemm,
