@@ -28,6 +28,7 @@
 #include <tuple>
 #include <utility>
 
+#include "mk_q4k.h"
 #include "q4k_device.h"
 #include "q4k_host.h"
 
@@ -271,6 +272,18 @@ GemmPlan make_plan(int M, int N, int K, int G) {
   // partials the reduction reads, 12 KiB for each of its rounds of eight
   // loads (a round trip takes about as long as 12 KiB on that path) and
   // 24 KiB for the second launch. nkb = 1 is taken when nothing else fits.
+  //
+  // The split is chosen for the largest row count a call takes (MK_Q4K_MAX_M),
+  // whatever M is: the K slices, and so the order in which every output is
+  // summed, depend on N, K and the device only. A row's result is then the
+  // same, bit for bit, whether it is multiplied alone or stacked with others.
+  const int Mp = MK_Q4K_MAX_M, mtp = (Mp + 15) / 16;
+  const size_t contrib_p = (size_t)SPLIT_WAVES * 2 * mtp * 1024;
+  auto x_bytes = [](int rows, int nkb) {
+    const size_t b = (size_t)rows * (nkb * X_BYTES_PER_BLOCK + X_ROW_PAD) +
+                     (size_t)rows * nkb * XSUM_BYTES_PER_BLOCK;
+    return (b + 15) & ~(size_t)15;
+  };
   double best = -1.0;
   int prev_nkb = -1;
   for (int sk = 1; sk <= p.KB; ++sk) {
@@ -278,9 +291,7 @@ GemmPlan make_plan(int M, int N, int K, int G) {
     if (nkb == prev_nkb) continue;
     prev_nkb = nkb;
     const int skr = (p.KB + nkb - 1) / nkb;
-    const size_t xb = (size_t)M * (nkb * X_BYTES_PER_BLOCK + X_ROW_PAD) +
-                      (size_t)M * nkb * XSUM_BYTES_PER_BLOCK;
-    const size_t c0 = (xb + 15) & ~(size_t)15;
+    const size_t c0 = x_bytes(Mp, nkb);
     int tw_max = 1, umax = 0;
     for (int w = 0; w < G; ++w) {
       const Assign a = assign_split(p.nt, skr, nkb, p.KB, w, G);
@@ -288,11 +299,10 @@ GemmPlan make_plan(int M, int N, int K, int G) {
       if (a.U > umax) umax = a.U;
     }
     // the contribution slots reuse the activation region after the stream
-    const size_t c1 = c0 > contrib ? c0 : contrib;
-    const size_t lds = c1;
-    const bool fits = lds + 256 <= kGemmLdsLimit;
-    const double part = (double)p.mt * 1024;
-    const double bytes = (double)umax * TILE_REC + (double)M * nkb * X_BYTES_PER_BLOCK +
+    const size_t c1 = c0 > contrib_p ? c0 : contrib_p;
+    const bool fits = c1 + 256 <= kGemmLdsLimit;
+    const double part = (double)mtp * 1024;
+    const double bytes = (double)umax * TILE_REC + (double)Mp * nkb * X_BYTES_PER_BLOCK +
                          (skr > 1 ? tw_max * part + (double)p.nt * skr * part / G +
                                         (skr + 7) / 8 * 12288.0 + 24576.0
                                   : 0.0);
@@ -301,9 +311,13 @@ GemmPlan make_plan(int M, int N, int K, int G) {
       p.sk = skr;
       p.nkb = nkb;
       p.x_stride = nkb * X_BYTES_PER_BLOCK + X_ROW_PAD;
-      p.lds = lds;
       p.ok = fits;
     }
+  }
+  // LDS for the actual rows: their slice of activations, or the slots
+  {
+    const size_t c0 = x_bytes(M, p.nkb);
+    p.lds = c0 > contrib ? c0 : contrib;
   }
   // workspace: the slice partials (no initial contents needed)
   p.part_bytes = p.sk > 1 ? (size_t)p.nt * p.sk * p.mt * 1024 : 0;

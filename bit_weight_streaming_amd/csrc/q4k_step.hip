@@ -1106,14 +1106,18 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
     // column sums of segment s's matrix: after its tile records
     for (int s = 0; s < 3; ++s)
       ph.cs_off[s] = s < nseg ? (unsigned)((size_t)tiles_of(ph.seg_n[s]) * ph.KB * TILE_REC) : 0u;
-    // K slices: at least 4, more while one slice of activations exceeds 96 KiB
-    // of LDS or takes more than one round of loads to stage
+    // K slices: at least 4, more while one slice of activations of the most
+    // rows the walk takes (STEP_MAX_M, whatever M is: the slices, and so every
+    // summation order, do not depend on the row count, and a row's results
+    // are the same, bit for bit, alone or stacked) exceeds 96 KiB of LDS or
+    // takes more than one round of loads to stage
+    const int Mp = STEP_MAX_M;
     int sk = 4 < ph.KB ? 4 : ph.KB;
     for (;;) {
       int nkb = (ph.KB + sk - 1) / sk;
-      size_t xb = (size_t)M * (nkb * X_BYTES_PER_BLOCK + X_ROW_PAD) +
-                  (size_t)M * nkb * XSUM_BYTES_PER_BLOCK;
-      const bool one_round = M * nkb * 32 <= STEP_THREADS * kStageRound;
+      size_t xb = (size_t)Mp * (nkb * X_BYTES_PER_BLOCK + X_ROW_PAD) +
+                  (size_t)Mp * nkb * XSUM_BYTES_PER_BLOCK;
+      const bool one_round = Mp * nkb * 32 <= STEP_THREADS * kStageRound;
       if ((xb <= 96 * 1024 && one_round) || nkb == 1) {
         ph.sk = (ph.KB + nkb - 1) / nkb;
         ph.nkb = nkb;

@@ -67,6 +67,11 @@ extern "C" {
  * One launch of one workgroup per compute unit; when K is cut into several
  * slices, the slice partial sums go to a device workspace and a second
  * kernel, enqueued on the same stream, adds them in slice order.
+ * Batch invariance: the K slices are chosen for MK_Q4K_MAX_M rows whatever
+ * M is, so each output is summed in an order that depends on N, K and the
+ * device only: a row of Y is the same, bit for bit, whether X holds it alone
+ * or stacked with any other rows (the same holds for mk_q4k_gemm_tiled, and
+ * the two agree bit for bit).
  * Returns MK_OK or MK_EINVAL / MK_EALIGN / MK_ENODEV / MK_EHIP. The library
  * keeps a private device workspace per GPU for the K-split partial sums; the
  * first call on a device that needs more than it holds allocates it
@@ -146,6 +151,11 @@ int mk_q4k_gemm_tiled(const void* W_tiles, const uint16_t* X_fp16, float* Y_fp32
  * x_0 is given; every later input is produced on the device. k and v are
  * written but feed nothing (in a model they would feed attention, which is
  * not part of this walk).
+ *
+ * Batch invariance: every phase's K slices are chosen for 16 rows whatever
+ * M is, and a row's statistics are exact integer sums of its own values, so
+ * each row's outputs and phase inputs are the same, bit for bit, whether it
+ * is walked alone or stacked with other rows (mk_q4k_step_res likewise).
  *
  * Chain rules (checked): q.K = k.K = v.K = gate.K = up.K = down.N = H (the
  * hidden size), o.K = q.N, gate.N = up.N = down.K = F; every K % 256 == 0;

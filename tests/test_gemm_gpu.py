@@ -280,3 +280,24 @@ def test_interleaved_shapes_keep_the_workspace_consistent():
     assert np.array_equal(ya, ya2) and np.array_equal(yb, yb2)
     check(*a, Y=ya)
     check(*b, Y=yb)
+
+
+# --- batch invariance: a row's result does not depend on the rows beside it ----
+@pytest.mark.parametrize("N,K", [(333, 2048), (17408 // 8, 5120), (5120 // 4, 17408)])
+def test_rows_bit_identical_alone_or_stacked(N, K):
+    """The K split is chosen for 64 rows whatever M is, so every output is
+    summed in the same order: the first M' rows of a 64-row call, and single
+    rows called alone, match it bit for bit (row and tile-record layouts)."""
+    W, X = inputs(N, K, 64, tag=80)
+    Wd = torch.from_numpy(W).to(DEV)
+    Xd = torch.from_numpy(X).to(DEV)
+    Wt = mk.repack(Wd, N, K)
+    full = mk.gemm(Wd, Xd)
+    full_t = mk.gemm_tiled(Wt, Xd, N)
+    torch.cuda.synchronize()
+    assert torch.equal(full, full_t)
+    for m in (1, 5, 12, 16, 33):
+        assert torch.equal(mk.gemm(Wd, Xd[:m].contiguous()), full[:m]), m
+        assert torch.equal(mk.gemm_tiled(Wt, Xd[:m].contiguous(), N), full[:m]), m
+    for r in (0, 13, 40, 63):
+        assert torch.equal(mk.gemm(Wd, Xd[r:r + 1].contiguous()), full[r:r + 1]), r

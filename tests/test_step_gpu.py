@@ -150,6 +150,23 @@ def test_second_step_on_new_input_reads_fresh_values():
     check_out(stack)
 
 
+def test_rows_bit_identical_alone_or_stacked():
+    """The K slices of every phase are chosen for 16 rows whatever M is, each
+    row's statistics are exact integer sums of its own values, and nothing
+    else mixes rows: a row walked alone gives every output and every cast of
+    the 12-row walk bit for bit."""
+    stack = Stack(2, 12, SMALL, seed=51, device=DEV)
+    run_step(stack)
+    for r in (0, 7, 11):
+        one = Stack(2, 1, SMALL, seed=51, device=DEV)
+        one.x0.copy_(stack.x0[r:r + 1])
+        run_step(one)
+        for l in range(2):
+            for a, b in zip(one.io[l]["y"] + one.io[l]["x"], stack.io[l]["y"] + stack.io[l]["x"]):
+                assert torch.equal(a[0], b[r]), (r, l)
+        assert torch.equal(one.x_out[0], stack.x_out[r])
+
+
 def test_full_stack_sampled_columns():
     """The 64-layer stack at M=12 (12.27 GB of weights), as the benchmark runs
     it; every matrix checked on a seeded subset of 4096 columns (all columns

@@ -133,6 +133,19 @@ def test_res_deterministic_and_repeatable():
             assert torch.equal(u, v)
 
 
+def test_res_rows_bit_identical_alone_or_stacked():
+    stack = ResStack(2, 12, SMALL, seed=45, device=DEV)
+    run_res(stack)
+    for r in (0, 11):
+        one = ResStack(2, 1, SMALL, seed=45, device=DEV)
+        one.h0.copy_(stack.h0[r:r + 1])
+        run_res(one)
+        for l in range(2):
+            for a, b in zip(one.io[l]["y"] + one.io[l]["x"] + one.io[l]["h"],
+                            stack.io[l]["y"] + stack.io[l]["x"] + stack.io[l]["h"]):
+                assert torch.equal(a[0], b[r]), (r, l)
+
+
 def test_res_rejects_missing_norm():
     stack = ResStack(1, 4, SMALL, seed=43, device=DEV)
     descs = stack.layer_descs()
