@@ -31,6 +31,12 @@ What it computes, and where that comes from:
   is SiLU(gate) * up. Pinned by constant rows, exact power-of-two scaling,
   the reduction of ``gemm_rms`` to ``gemm`` at unit scale, the SiLU
   identity silu(v) - silu(-v) = v and its limits, and numpy cross-checks.
+* ``q8_page`` / ``attn_decode``: decode attention of stacked rows over a
+  paged q8_0 KV pool (each row attends to its agent's first row_len tokens;
+  softmax of q.k / sqrt(128), weighted sum of v), in float64. Pinned by
+  hand-built pages, a single token (O = v), equal keys (O = mean v), two
+  tokens in closed form, shift invariance of the scores and a numpy
+  cross-check.
 * ``within_bound``: the acceptance rule ``|y - y_ref| <= tol * S``, and
   ``y == 0`` exactly where ``S == 0``.
 """
@@ -98,6 +104,10 @@ def _load():
         lib.oracle_rms_inv.argtypes = [vp, i64, i64, ctypes.c_double, vp]
         lib.oracle_gemm_rms.restype = ctypes.c_int
         lib.oracle_gemm_rms.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
+        lib.oracle_q8_page.restype = None
+        lib.oracle_q8_page.argtypes = [vp, vp, vp]
+        lib.oracle_q8_attn.restype = ctypes.c_int
+        lib.oracle_q8_attn.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp]
         lib.oracle_silu.restype = None
         lib.oracle_silu.argtypes = [vp, i64, vp]
         _lib = lib
@@ -242,6 +252,39 @@ def silu(v: np.ndarray) -> np.ndarray:
     out = np.empty_like(v)
     _load().oracle_silu(v.ctypes.data, v.size, out.ctypes.data)
     return out
+
+
+def q8_page(ph) -> tuple[np.ndarray, np.ndarray]:
+    """K, V (float64 [16, 128] each) of one 4352-byte page-head of the pool."""
+    b = _c(np.frombuffer(bytes(ph), dtype=np.uint8), np.uint8)
+    if b.size != 4352:
+        raise ValueError("a page-head is 4352 bytes")
+    k = np.empty((16, 128), dtype=np.float64)
+    v = np.empty((16, 128), dtype=np.float64)
+    _load().oracle_q8_page(b.ctypes.data, k.ctypes.data, v.ctypes.data)
+    return k, v
+
+
+def attn_decode(Q, pool, block_table, row_agent, row_len, n_kv: int):
+    """Reference (O, S), float64 [M, n_heads, 128], of decode attention over the
+    paged q8_0 pool for binary16 queries Q [M, n_heads, 128]."""
+    Q = np.asarray(Q)
+    if Q.dtype != np.float16 or Q.ndim != 3 or Q.shape[2] != 128:
+        raise TypeError("Q must be float16 [M, n_heads, 128]")
+    M, H, _ = Q.shape
+    qb = _c(Q.view(np.uint16), np.uint16)
+    pool = _c(pool, np.uint8)
+    bt = _c(block_table, np.int32)
+    ra = _c(row_agent, np.int32)
+    rl = _c(row_len, np.int32)
+    O = np.empty((M, H, 128), dtype=np.float64)
+    S = np.empty((M, H, 128), dtype=np.float64)
+    rc = _load().oracle_q8_attn(qb.ctypes.data, pool.ctypes.data, bt.ctypes.data, ra.ctypes.data,
+                                rl.ctypes.data, M, bt.shape[1], H, n_kv, O.ctypes.data,
+                                S.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_q8_attn failed ({rc})")
+    return O, S
 
 
 def standardize(v: np.ndarray, eps: float = 1e-6) -> np.ndarray:

@@ -274,6 +274,100 @@ void oracle_silu(const double* v, int64_t n, double* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = v[i] / (1.0 + exp(-v[i]));
 }
 
+/* ---- decode attention over a paged q8_0 KV pool ----------------------------
+ * A page holds 16 tokens; page p, KV head h is 4352 bytes at (p*n_kv + h)*4352:
+ * K quants [16][128] int8, K scales [16][4] binary16 (token t, dims 32b..32b+31
+ * share scale b), V quants [128][16] int8 (dim-major), V scales [16][4]. A
+ * value is scale * quant (q8_0). */
+#define ORACLE_PAGE_TOKENS 16
+#define ORACLE_HEAD_DIM 128
+#define ORACLE_PAGE_HEAD_BYTES 4352
+
+/* K and V of one page-head as doubles, [16][128] each. */
+void oracle_q8_page(const uint8_t* ph, double* k, double* v) {
+  for (int t = 0; t < ORACLE_PAGE_TOKENS; ++t)
+    for (int d = 0; d < ORACLE_HEAD_DIM; ++d) {
+      const int b = d / 32;
+      const uint16_t ks = (uint16_t)(ph[2048 + 2 * (4 * t + b)] | (ph[2048 + 2 * (4 * t + b) + 1] << 8));
+      const uint16_t vs = (uint16_t)(ph[4224 + 2 * (4 * t + b)] | (ph[4224 + 2 * (4 * t + b) + 1] << 8));
+      k[t * ORACLE_HEAD_DIM + d] = oracle_f16_to_f64(ks) * (double)(int8_t)ph[t * 128 + d];
+      v[t * ORACLE_HEAD_DIM + d] =
+          oracle_f16_to_f64(vs) * (double)(int8_t)ph[2176 + d * ORACLE_PAGE_TOKENS + t];
+    }
+}
+
+/* Reference decode attention. Row r of Q [M][n_heads][128] (binary16) belongs
+ * to agent row_agent[r] and attends to that agent's first row_len[r] tokens,
+ * token i living in page block_table[agent][i / 16], slot i % 16. Head h reads
+ * KV head h / (n_heads / n_kv). In double precision:
+ *   s_i = (q . k_i) / sqrt(128),  p = softmax(s),  O = sum_i p_i v_i,
+ * and S = sum_i p_i |v_i| (per output element, for the error bound). */
+int oracle_q8_attn(const uint16_t* Q, const uint8_t* pool, const int32_t* block_table,
+                   const int32_t* row_agent, const int32_t* row_len, int64_t M,
+                   int64_t max_pages, int64_t n_heads, int64_t n_kv, double* O, double* S) {
+  if (n_kv < 1 || n_heads % n_kv) return -1;
+  const int64_t group = n_heads / n_kv;
+  const double scale = 1.0 / sqrt((double)ORACLE_HEAD_DIM);
+  int err = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int64_t r = 0; r < M; ++r)
+    for (int64_t h = 0; h < n_heads; ++h) {
+      const int64_t n = row_len[r];
+      const int64_t a = row_agent[r];
+      const int64_t kvh = h / group;
+      double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+      double* k = (double*)malloc(sizeof(double) * ORACLE_PAGE_TOKENS * ORACLE_HEAD_DIM);
+      double* v = (double*)malloc(sizeof(double) * ORACLE_PAGE_TOKENS * ORACLE_HEAD_DIM);
+      double q[ORACLE_HEAD_DIM];
+      double* o = O + (r * n_heads + h) * ORACLE_HEAD_DIM;
+      double* sa = S + (r * n_heads + h) * ORACLE_HEAD_DIM;
+      if (!s || !k || !v || n < 1) {
+#pragma omp atomic write
+        err = n < 1 ? -1 : -2;
+        free(s);
+        free(k);
+        free(v);
+        continue;
+      }
+      for (int d = 0; d < ORACLE_HEAD_DIM; ++d)
+        q[d] = oracle_f16_to_f64(Q[(r * n_heads + h) * ORACLE_HEAD_DIM + d]);
+      /* scores */
+      double mx = -INFINITY;
+      for (int64_t i = 0; i < n; ++i) {
+        const int64_t page = block_table[a * max_pages + i / ORACLE_PAGE_TOKENS];
+        if (i % ORACLE_PAGE_TOKENS == 0)
+          oracle_q8_page(pool + (size_t)(page * n_kv + kvh) * ORACLE_PAGE_HEAD_BYTES, k, v);
+        const double* ki = k + (i % ORACLE_PAGE_TOKENS) * ORACLE_HEAD_DIM;
+        double dot = 0.0;
+        for (int d = 0; d < ORACLE_HEAD_DIM; ++d) dot += q[d] * ki[d];
+        s[i] = dot * scale;
+        if (s[i] > mx) mx = s[i];
+      }
+      /* softmax weights and the weighted sum of values */
+      double z = 0.0;
+      for (int64_t i = 0; i < n; ++i) {
+        s[i] = exp(s[i] - mx);
+        z += s[i];
+      }
+      for (int d = 0; d < ORACLE_HEAD_DIM; ++d) o[d] = sa[d] = 0.0;
+      for (int64_t i = 0; i < n; ++i) {
+        const int64_t page = block_table[a * max_pages + i / ORACLE_PAGE_TOKENS];
+        if (i % ORACLE_PAGE_TOKENS == 0)
+          oracle_q8_page(pool + (size_t)(page * n_kv + kvh) * ORACLE_PAGE_HEAD_BYTES, k, v);
+        const double p = s[i] / z;
+        const double* vi = v + (i % ORACLE_PAGE_TOKENS) * ORACLE_HEAD_DIM;
+        for (int d = 0; d < ORACLE_HEAD_DIM; ++d) {
+          o[d] += p * vi[d];
+          sa[d] += p * fabs(vi[d]);
+        }
+      }
+      free(s);
+      free(k);
+      free(v);
+    }
+  return err;
+}
+
 void oracle_f64_to_f16_array(const double* v, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_f16(v[i]);
 }

@@ -84,6 +84,8 @@ def _load():
         lib.synth_q4k_rows_centered.restype = None
         lib.synth_q4k_rows_centered.argtypes = [u64, ctypes.c_int64, ctypes.c_int64,
                                                 ctypes.c_int64, ctypes.c_void_p]
+        lib.synth_q8_pool.restype = None
+        lib.synth_q8_pool.argtypes = [u64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         lib.synth_f16_normal.restype = None
         lib.synth_f16_normal.argtypes = [u64, u64, u64, ctypes.c_void_p]
         lib.synth_normals.restype = None
@@ -160,6 +162,46 @@ def normals(k: int, n: int, i0: int = 0) -> np.ndarray:
 def f32_normal(k: int, n: int, i0: int = 0) -> np.ndarray:
     """float32 of the normals of stream k (round to nearest)."""
     return normals(k, n, i0).astype(np.float32)
+
+
+# ---- paged q8_0 KV pool for decode attention ----------------------------------
+KV_PAGE_TOKENS = 16
+KV_HEAD_DIM = 128
+KV_PAGE_HEAD_BYTES = 4352
+TAG_KV = 6     # (seed, TAG_KV, n_pages, n_kv)
+
+
+def q8_pool(seed: int, n_pages: int, n_kv: int) -> np.ndarray:
+    """uint8 [n_pages, n_kv, 4352]: K quants [16][128] int8, K scales [16][4]
+    binary16, V quants [128][16] int8, V scales [16][4] binary16 per page-head."""
+    out = np.empty((n_pages, n_kv, KV_PAGE_HEAD_BYTES), dtype=np.uint8)
+    _load().synth_q8_pool(key(seed, TAG_KV, n_pages, n_kv), n_pages, n_kv, out.ctypes.data)
+    return out
+
+
+def attn_layout(seed: int, lengths, rows_per_agent: int, n_pages: int):
+    """Block tables and rows of a decode step over a shared pool: agent a owns
+    ceil(lengths[a] / 16) pages drawn without replacement from a seeded
+    permutation of the pool; its rows r = rows_per_agent*a + j attend to the
+    first lengths[a] - rows_per_agent + 1 + j tokens (the new tokens are the
+    agent's last ones, each row seeing itself and the rows before it).
+    Returns (block_table int32 [A, max_pages], row_agent int32 [M],
+    row_len int32 [M])."""
+    lengths = [int(v) for v in lengths]
+    pages = [(n + KV_PAGE_TOKENS - 1) // KV_PAGE_TOKENS for n in lengths]
+    if sum(pages) > n_pages:
+        raise ValueError("pool too small")
+    perm = np.argsort(normals(key(seed, TAG_KV, 1, n_pages), n_pages), kind="stable")
+    A = len(lengths)
+    table = np.full((A, max(pages)), -1, dtype=np.int32)
+    o = 0
+    for a in range(A):
+        table[a, :pages[a]] = perm[o:o + pages[a]]
+        o += pages[a]
+    row_agent = np.repeat(np.arange(A, dtype=np.int32), rows_per_agent)
+    row_len = np.array([lengths[a] - rows_per_agent + 1 + j for a in range(A)
+                        for j in range(rows_per_agent)], dtype=np.int32)
+    return table, row_agent, row_len
 
 
 def activations(seed: int, M: int, K: int) -> np.ndarray:

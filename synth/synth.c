@@ -27,6 +27,18 @@
  * mins; bytes 8-11 the low 4 bits of the scale (low nibble) and min (high
  * nibble) of sub-blocks 4-7.
  *
+ * Paged q8_0 KV pool (decode attention): page p, KV head h occupies 4352
+ * bytes at (p * n_kv + h) * 4352: K quants [16 tokens][128] int8, K scales
+ * [16 tokens][4] binary16, V quants [128 dims][16 tokens] int8 (dim-major),
+ * V scales [16 tokens][4] binary16 (one scale per token and 32-dim block, as
+ * in q8_0; the quants are stored apart from their scales so that every
+ * load is aligned). Quants are uniform bytes; scales are binary16 of
+ * |z| * 0.03, z ~ N(0,1). Page-head j (= page * n_kv + head) takes its 4096
+ * quant bytes from draws j*512 .. j*512+511 of the stream keyed k ^ A5..A5
+ * (8 bytes each, K quants first) and its 128 scales from the Box-Muller
+ * pairs of draws j*64 .. j*64+63 of the stream keyed k ^ 5A..5A (K scales
+ * first).
+ *
  * Random source: SplitMix64 (Steele, Lea & Flood, "Fast splittable
  * pseudorandom number generators", OOPSLA 2014). Output i of the stream with
  * key k is mix(k + (i+1)*0x9E3779B97F4A7C15), where mix is the published
@@ -189,5 +201,27 @@ void synth_normals(uint64_t key, uint64_t i0, uint64_t n, double* out) {
     double z0, z1;
     synth_normal_pair(synth_draw(key, i >> 1), &z0, &z1);
     out[j] = (i & 1) ? z1 : z0;
+  }
+}
+
+/* Fill n_pages pages of a paged q8_0 KV pool with n_kv heads (layout above). */
+void synth_q8_pool(uint64_t key, int64_t n_pages, int64_t n_kv, uint8_t* out) {
+  const uint64_t kq = key ^ 0xA5A5A5A5A5A5A5A5ULL, ks = key ^ 0x5A5A5A5A5A5A5A5AULL;
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < n_pages * n_kv; ++j) {
+    uint8_t* ph = out + (size_t)j * 4352;
+    for (int i = 0; i < 512; ++i) {  /* 2048 K quant bytes, then 2048 V quant bytes */
+      const uint64_t w = synth_draw(kq, (uint64_t)j * 512 + (uint64_t)i);
+      uint8_t* dst = i < 256 ? ph + 8 * i : ph + 2176 + 8 * (i - 256);
+      for (int b = 0; b < 8; ++b) dst[b] = (uint8_t)(w >> (8 * b));
+    }
+    for (int i = 0; i < 128; ++i) {  /* 64 K scales, then 64 V scales */
+      double z0, z1;
+      synth_normal_pair(synth_draw(ks, (uint64_t)j * 64 + (uint64_t)(i >> 1)), &z0, &z1);
+      const uint16_t sc = synth_f64_to_f16(fabs((i & 1) ? z1 : z0) * 0.03);
+      uint8_t* dst = i < 64 ? ph + 2048 + 2 * i : ph + 4224 + 2 * (i - 64);
+      dst[0] = (uint8_t)sc;
+      dst[1] = (uint8_t)(sc >> 8);
+    }
   }
 }

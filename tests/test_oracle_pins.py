@@ -467,3 +467,109 @@ def test_generated_fields_are_uniform():
     assert np.all(d_all >= 0)
     # E|z| * 1e-3 = sqrt(2/pi) * 1e-3
     assert abs(d_all.mean() - np.sqrt(2 / np.pi) * 1e-3) < 5e-5
+
+
+# --- decode attention over the paged q8_0 pool ---------------------------------
+def _page(kq=None, ks=None, vq=None, vs=None):
+    """Assemble a 4352-byte page-head from fields (no arithmetic)."""
+    b = np.zeros(4352, dtype=np.uint8)
+    if kq is not None:
+        b[0:2048] = np.asarray(kq, dtype=np.int8).reshape(16, 128).view(np.uint8).ravel()
+    if ks is not None:
+        b[2048:2176] = np.asarray(ks, dtype=np.float16).reshape(16, 4).view(np.uint8).ravel()
+    if vq is not None:   # given [16 tokens][128 dims], stored dim-major
+        b[2176:4224] = np.asarray(vq, dtype=np.int8).reshape(16, 128).T.copy().view(np.uint8).ravel()
+    if vs is not None:
+        b[4224:4352] = np.asarray(vs, dtype=np.float16).reshape(16, 4).view(np.uint8).ravel()
+    return b
+
+
+def test_q8_page_decodes_by_hand():
+    """Token t, dim d: K = ks[t][d // 32] * kq[t][d]; V likewise, V quants
+    stored dim-major. A transposed V or a wrong scale block fails."""
+    kq = np.zeros((16, 128), dtype=np.int64)
+    kq[3, 40] = -7          # token 3, dim 40: block 1
+    kq[15, 127] = 127
+    ks = np.zeros((16, 4))
+    ks[3, 1] = 0.5
+    ks[15, 3] = 2.0 ** -10
+    vq = np.zeros((16, 128), dtype=np.int64)
+    vq[2, 5] = -128
+    vs = np.zeros((16, 4))
+    vs[2, 0] = 0.25
+    k, v = oracle.q8_page(_page(kq, ks, vq, vs))
+    want_k = np.zeros((16, 128))
+    want_k[3, 40] = -3.5
+    want_k[15, 127] = 127 * 2.0 ** -10
+    want_v = np.zeros((16, 128))
+    want_v[2, 5] = -32.0
+    assert np.array_equal(k, want_k) and np.array_equal(v, want_v)
+
+
+def _one_page_pool(kq, ks, vq, vs):
+    return _page(kq, ks, vq, vs).reshape(1, 1, 4352)
+
+
+def test_attn_single_token_and_equal_keys():
+    """One token: O = v_0 exactly. n tokens with equal keys: uniform weights,
+    O = mean of v (closed form), whatever the query."""
+    rng = np.random.default_rng(30)
+    vq = rng.integers(-128, 128, size=(16, 128))
+    vs = np.full((16, 4), 0.125)
+    kq = np.tile(rng.integers(-128, 128, size=(1, 128)), (16, 1))   # all keys equal
+    ks = np.full((16, 4), 0.03125)
+    pool = _one_page_pool(kq, ks, vq, vs)
+    Q = rng.standard_normal((5, 1, 128)).astype(np.float16)
+    table = np.zeros((1, 1), dtype=np.int32)
+    lens = np.array([1, 2, 7, 16, 16], dtype=np.int32)
+    O, S = oracle.attn_decode(Q, pool, table, np.zeros(5, np.int32), lens, 1)
+    v = vq * 0.125
+    for r, n in enumerate(lens):
+        assert np.allclose(O[r, 0], v[:n].mean(axis=0), rtol=1e-14, atol=1e-14)
+        assert np.allclose(S[r, 0], np.abs(v[:n]).mean(axis=0), rtol=1e-14, atol=1e-14)
+    assert np.array_equal(O[0, 0], v[0])
+
+
+def test_attn_two_tokens_closed_form():
+    """Two tokens whose scores differ by delta: p_1 = 1 / (1 + exp(-delta))."""
+    kq = np.zeros((16, 128), dtype=np.int64)
+    kq[0, 0], kq[1, 0] = 10, 30
+    ks = np.zeros((16, 4))
+    ks[0, 0] = ks[1, 0] = 0.0625
+    vq = np.zeros((16, 128), dtype=np.int64)
+    vq[0, :] = 8
+    vq[1, :] = -24
+    vs = np.full((16, 4), 0.5)
+    pool = _one_page_pool(kq, ks, vq, vs)
+    Q = np.zeros((1, 1, 128), dtype=np.float16)
+    Q[0, 0, 0] = 2.0
+    O, _ = oracle.attn_decode(Q, pool, np.zeros((1, 1), np.int32), np.zeros(1, np.int32),
+                              np.array([2], np.int32), 1)
+    delta = 2.0 * (30 - 10) * 0.0625 / np.sqrt(128.0)
+    p1 = 1.0 / (1.0 + np.exp(-delta))
+    assert np.allclose(O[0, 0], (1 - p1) * 4.0 + p1 * (-12.0), rtol=1e-14)
+
+
+def test_attn_matches_numpy_with_paging_and_gqa():
+    """A shared pool, per-agent page lists, causal row lengths and two query
+    heads per KV head, against numpy (dequantized pool, explicit softmax)."""
+    n_kv, H = 2, 4
+    pool = synth.q8_pool(31, 24, n_kv)
+    table, ra, rl = synth.attn_layout(31, [70, 33, 150], 3, 24)
+    Q = synth.f16_normal(synth.key(31, 9), 9 * H * 128).reshape(9, H, 128)
+    O, S = oracle.attn_decode(Q, pool, table, ra, rl, n_kv)
+    for r in range(9):
+        a = ra[r]
+        for h in range(H):
+            kvh = h // (H // n_kv)
+            ks, vs = [], []
+            for i in range(rl[r]):
+                k, v = oracle.q8_page(pool[table[a, i // 16], kvh])
+                ks.append(k[i % 16])
+                vs.append(v[i % 16])
+            K, V = np.array(ks), np.array(vs)
+            s = K @ Q[r, h].astype(np.float64) / np.sqrt(128.0)
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            assert np.allclose(O[r, h], p @ V, rtol=1e-12, atol=1e-14), (r, h)
+            assert np.allclose(S[r, h], p @ np.abs(V), rtol=1e-12, atol=1e-14), (r, h)
