@@ -19,7 +19,7 @@ import subprocess
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 LIB_PATH = os.path.join(_HERE, "libmkq4k.so")
-_SOURCES = ["q4k_gemm.hip", "q4k_step.hip", "q4k_repack.hip", "mk_api.hip"]
+_SOURCES = ["q4k_gemm.hip", "q4k_step.hip", "q4k_repack.hip", "q8_attn.hip", "mk_api.hip"]
 HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-fPIC", "-shared", "-std=c++17",
     # packed fp32 instructions stay off (see the build notes)
@@ -120,6 +120,11 @@ def lib():
                                       vp, vp, vp, sz, vp]
             L.mk_q4k_step_status.restype = i
             L.mk_q4k_step_status.argtypes = [vp, ctypes.POINTER(i)]
+        if hasattr(L, "mk_q8_attn_decode"):
+            L.mk_q8_attn_workspace_bytes.restype = sz
+            L.mk_q8_attn_workspace_bytes.argtypes = [i, i, i]
+            L.mk_q8_attn_decode.restype = i
+            L.mk_q8_attn_decode.argtypes = [vp, vp, i, vp, vp, i, i, i, i, i, vp, vp, sz, vp]
         if hasattr(L, "mk_q4k_step_res"):
             L.mk_q4k_step_res.restype = i
             L.mk_q4k_step_res.argtypes = [ctypes.POINTER(_Layer), ctypes.POINTER(_LayerNorm),
@@ -277,6 +282,40 @@ def step_res(layers, io, norms, h0, workspace, M: int, stream=None) -> None:
     rc = lib().mk_q4k_step_res(larr, narr, ioarr, len(layers), M, _ptr(h0), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc)
+
+
+def attn_workspace_bytes(n_agents: int, max_pages: int, n_kv: int) -> int:
+    return int(lib().mk_q8_attn_workspace_bytes(n_agents, max_pages, n_kv))
+
+
+def attn_decode(Q, pool, block_table, row_len, rows_per_agent: int, n_kv: int, workspace=None,
+                out=None, stream=None):
+    """Decode attention over the paged q8_0 pool. Q: float16 [M, n_heads, 128];
+    pool: uint8 [n_pages, n_kv, 4352]; block_table: int32 [n_agents, max_pages];
+    row_len: int32 [M] (all device tensors). Returns float32 [M, n_heads, 128]."""
+    import torch
+    M, H, D = Q.shape
+    A, P = block_table.shape
+    if D != 128 or Q.dtype != torch.float16 or M != A * rows_per_agent:
+        raise MkError(MK_EINVAL, "Q must be float16 [n_agents * rows_per_agent, n_heads, 128]")
+    if pool.dtype != torch.uint8 or pool.numel() % (n_kv * 4352):
+        raise MkError(MK_EINVAL, "pool must be uint8 pages of n_kv * 4352 bytes")
+    if block_table.dtype != torch.int32 or row_len.dtype != torch.int32 or row_len.numel() != M:
+        raise MkError(MK_EINVAL, "block_table and row_len must be int32")
+    for t in (Q, pool, block_table, row_len):
+        if not t.is_contiguous():
+            raise MkError(MK_EINVAL, "inputs must be contiguous")
+    if out is None:
+        out = torch.empty((M, H, 128), dtype=torch.float32, device=Q.device)
+    if workspace is None:
+        workspace = torch.empty(max(attn_workspace_bytes(A, P, n_kv), 16), dtype=torch.uint8,
+                                device=Q.device)
+    rc = lib().mk_q8_attn_decode(_ptr(Q), _ptr(pool), pool.numel() // (n_kv * 4352),
+                                 _ptr(block_table), _ptr(row_len), A, rows_per_agent, P, H, n_kv,
+                                 _ptr(out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc)
+    return out
 
 
 def step_status(workspace) -> int:

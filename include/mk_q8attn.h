@@ -1,0 +1,69 @@
+/*
+ * mk_q8attn.h - decode attention of stacked rows over a paged q8_0 KV pool
+ * (part of libmkq4k.so; error codes are those of mk_q4k.h).
+ *
+ * The other growing cost of the multi-agent decode step (the OpenJet post,
+ * "RTX 3090 one card, four coding agents", paragraph on how parallel
+ * decoding works: once the weights are read once per step, what grows with
+ * the agents is attention over their caches). n_agents agents each stack
+ * rows_per_agent rows (next token + drafts): row r = a * rows_per_agent + j.
+ *
+ * KV pool (device, caller-owned): 16-token pages; page p, KV head h is 4352
+ * bytes at (p * n_kv + h) * 4352:
+ *   K quants [16 tokens][128 dims] int8          bytes    0..2047
+ *   K scales [16 tokens][4 blocks] binary16      bytes 2048..2175
+ *   V quants [128 dims][16 tokens] int8          bytes 2176..4223
+ *   V scales [16 tokens][4 blocks] binary16      bytes 4224..4351
+ * Token t's value in dim d is scale[t][d / 32] * quant (q8_0: one binary16
+ * scale per 32 values; the quants are kept apart from their scales, and V
+ * dim-major, so that every load is aligned and the value product needs no
+ * transpose).
+ *
+ * Row r attends to the first row_len[r] tokens of its agent's sequence;
+ * token i of agent a lives in page block_table[a * max_pages + i / 16], slot
+ * i % 16. Head h reads KV head h / (n_heads / n_kv). Head dimension 128.
+ *   s_i = (q . k_i) / sqrt(128),   O = sum_i softmax(s)_i v_i
+ * Precision: the int8 quants and binary16 queries enter the products
+ * exactly; scores, softmax and sums in fp32; the weights times V scales go
+ * to the value product as binary16 hi + lo parts. Deterministic, and each
+ * row's result does not depend on the other rows.
+ */
+#ifndef MK_Q8ATTN_H
+#define MK_Q8ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Bytes of device workspace mk_q8_attn_decode needs (0 for invalid sizes). */
+size_t mk_q8_attn_workspace_bytes(int n_agents, int max_pages, int n_kv);
+
+/*
+ * mk_q8_attn_decode: enqueue decode attention on `stream`.
+ *   Q            device binary16 [M][n_heads][128], M = n_agents * rows_per_agent
+ *   pool         device KV pool (layout above) of n_pages pages
+ *   block_table  device int32 [n_agents][max_pages] page indices
+ *   row_len      device int32 [M]; 1 <= row_len[r] <= 16 * (pages listed for its agent)
+ *   O            device fp32 [M][n_heads][128], fully overwritten
+ *   workspace    device, >= mk_q8_attn_workspace_bytes(n_agents, max_pages, n_kv),
+ *                one call at a time
+ * Requires n_kv >= 1, n_heads % n_kv == 0 and rows_per_agent * n_heads / n_kv
+ * <= 32 (MK_EINVAL otherwise); Q, pool, O and workspace 16-byte aligned
+ * (MK_EALIGN). Device arrays are not read on the host: the kernels clamp
+ * lengths to 16 * max_pages and page indices into [0, n_pages), so values
+ * outside the limits above give unspecified results but never an access
+ * outside the pool.
+ */
+int mk_q8_attn_decode(const uint16_t* Q, const void* pool, int n_pages,
+                      const int32_t* block_table, const int32_t* row_len, int n_agents,
+                      int rows_per_agent, int max_pages, int n_heads, int n_kv, float* O,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MK_Q8ATTN_H */

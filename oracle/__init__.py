@@ -33,7 +33,8 @@ What it computes, and where that comes from:
   identity silu(v) - silu(-v) = v and its limits, and numpy cross-checks.
 * ``q8_page`` / ``attn_decode``: decode attention of stacked rows over a
   paged q8_0 KV pool (each row attends to its agent's first row_len tokens;
-  softmax of q.k / sqrt(128), weighted sum of v), in float64. Pinned by
+  softmax of q.k / sqrt(128), weighted sum of v), in float64; its bound S is
+  sum_i p_i max_d |v_i[d]| per (row, head). Pinned by
   hand-built pages, a single token (O = v), equal keys (O = mean v), two
   tokens in closed form, shift invariance of the scores and a numpy
   cross-check.
@@ -267,7 +268,8 @@ def q8_page(ph) -> tuple[np.ndarray, np.ndarray]:
 
 def attn_decode(Q, pool, block_table, row_agent, row_len, n_kv: int):
     """Reference (O, S), float64 [M, n_heads, 128], of decode attention over the
-    paged q8_0 pool for binary16 queries Q [M, n_heads, 128]."""
+    paged q8_0 pool for binary16 queries Q [M, n_heads, 128]; S is the size of
+    the attended values, sum_i p_i max_d |v_i[d]|, repeated over the dims."""
     Q = np.asarray(Q)
     if Q.dtype != np.float16 or Q.ndim != 3 or Q.shape[2] != 128:
         raise TypeError("Q must be float16 [M, n_heads, 128]")

@@ -301,7 +301,10 @@ void oracle_q8_page(const uint8_t* ph, double* k, double* v) {
  * token i living in page block_table[agent][i / 16], slot i % 16. Head h reads
  * KV head h / (n_heads / n_kv). In double precision:
  *   s_i = (q . k_i) / sqrt(128),  p = softmax(s),  O = sum_i p_i v_i,
- * and S = sum_i p_i |v_i| (per output element, for the error bound). */
+ * and, for the error bound, S = sum_i p_i max_d |v_i[d]|: the size of the
+ * values the row attends to, the same for every output dim of the head (a
+ * per-element sum of p_i |v_i[d]| could be made of weights far below any
+ * finite precision wherever the dominant token's value is 0). */
 int oracle_q8_attn(const uint16_t* Q, const uint8_t* pool, const int32_t* block_table,
                    const int32_t* row_agent, const int32_t* row_len, int64_t M,
                    int64_t max_pages, int64_t n_heads, int64_t n_kv, double* O, double* S) {
@@ -349,18 +352,22 @@ int oracle_q8_attn(const uint16_t* Q, const uint8_t* pool, const int32_t* block_
         s[i] = exp(s[i] - mx);
         z += s[i];
       }
-      for (int d = 0; d < ORACLE_HEAD_DIM; ++d) o[d] = sa[d] = 0.0;
+      double size = 0.0;
+      for (int d = 0; d < ORACLE_HEAD_DIM; ++d) o[d] = 0.0;
       for (int64_t i = 0; i < n; ++i) {
         const int64_t page = block_table[a * max_pages + i / ORACLE_PAGE_TOKENS];
         if (i % ORACLE_PAGE_TOKENS == 0)
           oracle_q8_page(pool + (size_t)(page * n_kv + kvh) * ORACLE_PAGE_HEAD_BYTES, k, v);
         const double p = s[i] / z;
         const double* vi = v + (i % ORACLE_PAGE_TOKENS) * ORACLE_HEAD_DIM;
+        double vmax = 0.0;
         for (int d = 0; d < ORACLE_HEAD_DIM; ++d) {
           o[d] += p * vi[d];
-          sa[d] += p * fabs(vi[d]);
+          if (fabs(vi[d]) > vmax) vmax = fabs(vi[d]);
         }
+        size += p * vmax;
       }
+      for (int d = 0; d < ORACLE_HEAD_DIM; ++d) sa[d] = size;
       free(s);
       free(k);
       free(v);

@@ -1,5 +1,5 @@
 """The C ABI without a GPU: the library loads, exports every function that
-include/mk_q4k.h declares, and rejects bad arguments on the host before any
+the headers in include/ declare, and rejects bad arguments on the host before any
 device access (so these run on CPU-only machines)."""
 import ctypes
 import os
@@ -10,7 +10,8 @@ import pytest
 import bit_weight_streaming_amd as mk
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mk_q4k.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -21,7 +22,7 @@ def L():
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    src = "".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(mk_\w+)\s*\(", src)))
 
@@ -31,7 +32,8 @@ def test_header_declares_the_boundary():
     for f in ("mk_q4k_gemm", "mk_q4k_gemm_ws", "mk_q4k_gemm_workspace_bytes", "mk_q4k_step",
               "mk_q4k_repack", "mk_q4k_tiles_bytes", "mk_q4k_gemm_tiled",
               "mk_q4k_step_workspace_bytes", "mk_q4k_step_status", "mk_strerror",
-              "mk_device_info"):
+              "mk_device_info", "mk_q4k_step_res", "mk_q8_attn_decode",
+              "mk_q8_attn_workspace_bytes"):
         assert f in names
 
 
@@ -103,3 +105,22 @@ def test_valid_call_without_gpu_is_nodev(L):
     assert gemm_rc(L) == mk.MK_ENODEV
     buf = ctypes.create_string_buffer(256)
     assert L.mk_device_info(buf, 256) == mk.MK_ENODEV
+
+
+def test_attn_rejects_bad_arguments(L):
+    ws = FAKE + (3 << 32)
+    args = dict(Q=FAKE, pool=FAKE + (1 << 32), n_pages=10, table=FAKE + (2 << 32),
+                lens=FAKE + (4 << 32), A=4, R=3, P=8, H=48, KV=8, O=FAKE + (5 << 32))
+
+    def rc(**kw):
+        a = dict(args, **kw)
+        return L.mk_q8_attn_decode(a["Q"], a["pool"], a["n_pages"], a["table"], a["lens"],
+                                   a["A"], a["R"], a["P"], a["H"], a["KV"], a["O"], ws,
+                                   1 << 30, None)
+    assert rc(H=47) == mk.MK_EINVAL          # heads not a multiple of KV heads
+    assert rc(R=6) == mk.MK_EINVAL           # 6 rows x 6 heads per KV head > 32
+    assert rc(n_pages=0) == mk.MK_EINVAL
+    assert rc(Q=FAKE + 2) == mk.MK_EALIGN
+    assert L.mk_q8_attn_decode(FAKE, FAKE + (1 << 32), 10, FAKE + (2 << 32), FAKE + (4 << 32),
+                               4, 3, 8, 48, 8, FAKE + (5 << 32), ws, 16, None) == mk.MK_EWORKSPACE
+    assert L.mk_q8_attn_workspace_bytes(4, 8, 8) == 4 * 8 * 1 * 32 * 132 * 4
