@@ -160,6 +160,68 @@ def gemm_bench(seed: int, reps: int = 60) -> list:
     return out
 
 
+ATTN_CONFIGS = (
+    # (label, per-agent cache lengths, rows per agent); 48 query heads over 8
+    # KV heads of 128 dims, a shared pool of 8,256 pages (132k tokens)
+    ("4 agents x 3 rows, 9k/27k/41k/55k tokens (132k pool full)", (9000, 27000, 41000, 55000), 3),
+    ("1 agent x 3 rows, 131k tokens", (131072,), 3),
+    ("4 agents x 3 rows, 2k tokens each", (2048,) * 4, 3),
+)
+ATTN_POOL_PAGES = 8256
+ATTN_POOL_COPIES = 3
+
+
+def attn_bench(seed: int, reps: int = 30) -> list:
+    """Time one layer's decode attention (mk_q8_attn_decode: the split kernel
+    and the merge) over the 132k-token q8_0 pool, with HIP events around
+    `reps` back-to-back calls cycling over ATTN_POOL_COPIES copies of the pool
+    (861 MB, beyond the last-level cache). Algorithmic bytes per call: every
+    page-head a call reads (4352 B each) plus Q, O and the block table."""
+    import torch
+    import bit_weight_streaming_amd as mk
+    import synth
+    dev = "cuda:0"
+    H, KV = 48, 8
+    pool_np = synth.q8_pool(seed, ATTN_POOL_PAGES, KV)
+    pools = [torch.from_numpy(pool_np).to(dev) for _ in range(ATTN_POOL_COPIES)]
+    del pool_np
+    stream = torch.cuda.current_stream()
+    out = []
+    for label, lengths, rows in ATTN_CONFIGS:
+        table, _, row_len = synth.attn_layout(seed, lengths, rows, ATTN_POOL_PAGES)
+        M = len(lengths) * rows
+        Q = torch.from_numpy(synth.f16_normal(synth.key(seed, 77, M, H), M * H * 128)
+                             .reshape(M, H, 128)).to(dev)
+        tb, rl = torch.from_numpy(table).to(dev), torch.from_numpy(row_len).to(dev)
+        ws = torch.empty(mk.attn_workspace_bytes(table.shape[0], table.shape[1], KV),
+                         dtype=torch.uint8, device=dev)
+        O = torch.empty((M, H, 128), dtype=torch.float32, device=dev)
+
+        def call(i):
+            mk.attn_decode(Q, pools[i % len(pools)], tb, rl, rows, KV, workspace=ws, out=O)
+
+        for i in range(2 * len(pools)):
+            call(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            call(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps * 1e-3
+        pages = sum((n + 15) // 16 for n in lengths)
+        kv_bytes = pages * KV * 4352
+        alg = kv_bytes + M * H * 128 * (2 + 4) + table.size * 4 + M * 4
+        gbs = alg / t / 1e9
+        log(f"attn {label}: {t * 1e6:.2f} us, {gbs:.1f} GB/s")
+        out.append({"config": label, "M": M, "heads": f"{H}/{KV}", "kv_bytes": kv_bytes,
+                    "us": round(t * 1e6, 2), "GBps": round(gbs, 1),
+                    "roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "kernels": "q8_attn_kernel + q8_attn_merge"})
+    return out
+
+
 def cpu_baseline(stack, budget_s: float = 20.0) -> dict:
     """Time the fp64 oracle (as it stands) on the same decode step: layers
     chained through binary16 casts as the GPU walks them, each matrix applied
@@ -225,6 +287,9 @@ def main() -> int:
                     help="only run plain 1 GiB copies (scale for the PMC byte counters)")
     ap.add_argument("--gemm-only", action="store_true",
                     help="only the single-matrix GEMM lines (no 64-layer stack)")
+    ap.add_argument("--no-attn", action="store_true", help="skip the decode-attention lines")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="only time decode attention over the 132k-token q8_0 pool")
     ap.add_argument("--walk", choices=("std", "res"), default="std",
                     help="std: the standardized walk (the benchmark); res: the residual walk "
                          "(RMSNorm, residual adds, SiLU*up) on centred weights, timed alone")
@@ -247,6 +312,10 @@ def main() -> int:
     if args.gemm_only:
         torch.cuda.set_device(0)
         print(json.dumps({"gemm": gemm_bench(args.seed)}), flush=True)
+        return 0
+    if args.attn_only:
+        torch.cuda.set_device(0)
+        print(json.dumps({"attn": attn_bench(args.seed)}), flush=True)
         return 0
 
     dev = "cuda:0"
@@ -308,9 +377,12 @@ def main() -> int:
     if res:
         # the residual walk is timed alone: no GEMM lines, no CPU leg, no
         # committed counter record for it
-        args.no_gemm = args.no_cpu = True
+        args.no_gemm = args.no_cpu = args.no_attn = True
     if not args.no_gemm:
         gemm = gemm_bench(args.seed)
+    attn = None
+    if not args.no_attn:
+        attn = attn_bench(args.seed)
 
     cpu = None
     if not args.no_cpu:
@@ -363,6 +435,7 @@ def main() -> int:
         },
         "cpu_baseline": cpu,
         "gemm": gemm,
+        "attn": attn,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -80,10 +80,63 @@ __device__ __forceinline__ int agent_len(const AttnArgs& A, int a) {
   return n;
 }
 
-__global__ void __launch_bounds__(ATT_THREADS) q8_attn_kernel(AttnArgs A) {
-  __shared__ float st_s[ATT_WAVES][2][64][2];             // per wave: (max, sum) per lane
-  __shared__ floatx4 acc_s[ATT_WAVES][2][8][64];          // per wave: the 16 output tiles
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+// One page-head's bytes as lane (c, g) holds them: K quants of token c, dims
+// 32u + 8g .. +7 (u = 0..3); K scales of tokens 4g .. 4g+3 (4 blocks each);
+// V quants of dims 16 dt + c, tokens 4g .. 4g+3 (dt = 0..7); V scales of
+// tokens 4g .. 4g+3.
+struct PageRaw {
+  u32x2 kq[4];
+  u32x4 ks[2];
+  uint32_t vq[8];
+  u32x4 vs[2];
+};
+
+__device__ __forceinline__ void load_page(PageRaw& R, const uint8_t* ph, int c, int g) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    R.kq[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(ph + c * 128 + 32 * u + 8 * g));
+  R.ks[0] = *reinterpret_cast<const u32x4*>(ph + 2048 + 32 * g);
+  R.ks[1] = *reinterpret_cast<const u32x4*>(ph + 2048 + 32 * g + 16);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    R.vq[dt] = __builtin_nontemporal_load(
+        reinterpret_cast<const uint32_t*>(ph + 2176 + (16 * dt + c) * 16 + 4 * g));
+  R.vs[0] = *reinterpret_cast<const u32x4*>(ph + 4224 + 32 * g);
+  R.vs[1] = *reinterpret_cast<const u32x4*>(ph + 4224 + 32 * g + 16);
+}
+
+// binary16 number i (0..15) of a 32-byte scale group
+__device__ __forceinline__ float half_at(const u32x4 (&w)[2], int i) {
+  const uint32_t x = w[i >> 3][(i >> 1) & 3];
+  return (float)bit_cast_<_Float16>((uint16_t)(x >> (16 * (i & 1))));
+}
+
+// Four int8 numbers (a little-endian word) as exact binary16: each byte,
+// offset by 128, becomes the low mantissa byte of 1024 (binary16 0x6400), and
+// 1152 = 1024 + 128 is then subtracted in binary16, exactly.
+__device__ __forceinline__ half4v i8x4_to_h4(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  const u32x2 b = {__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u),
+                   __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)};
+  const _Float16 k = (_Float16)1152.f;
+  return __builtin_bit_cast(half4v, b) - half4v{k, k, k, k};
+}
+
+// v0, v1 as binary16 hi + lo: hi rounded toward zero, lo = the exact fp32
+// rest, itself rounded toward zero, so |v - hi - lo| < 2^-20 |v| wherever
+// binary16 is normal.
+__device__ __forceinline__ void split2(float v0, float v1, uint32_t& hi, uint32_t& lo) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(v0, v1);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v0 - (float)h[0], v1 - (float)h[1]));
+}
+
+template <int NQT>
+__global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
+  __shared__ floatx4 acc_s[ATT_WAVES][8][64];    // one query tile of every wave
+  __shared__ float st_s[ATT_WAVES][NQT][64][2];  // per wave and tile: (max, sum) per lane
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int c = lane & 15, g = lane >> 4;
   const int grp = blockIdx.x % A.max_groups;
   const int kvh = (blockIdx.x / A.max_groups) % A.n_kv;
@@ -95,16 +148,19 @@ __global__ void __launch_bounds__(ATT_THREADS) q8_attn_kernel(AttnArgs A) {
   const int p1 = min(p0 + PAGES_PER_WAVE, npages);
 
   // query operands (B of the score MFMA): query vector 16 qt + c, dims
-  // 32 u + 8 g .. +7; past the agent's query vectors: zeros, length 0
-  half8v qop[2][4];
-  int qlen[2];
+  // 32 u + 8 g .. +7; columns past the agent's query vectors hold zeros and
+  // are never written out
+  half8v qop[NQT][4];
+  int qlen[NQT];
+  int lmin = 0x7FFFFFFF;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < NQT; ++qt) {
     const int qv = 16 * qt + c;
     const bool live = qv < A.nqv;
     const int j = live ? qv / A.group : 0, hh = live ? qv % A.group : 0;
     const int row = a * A.rows + j, head = kvh * A.group + hh;
-    qlen[qt] = live ? row_tokens(A, row) : 0;
+    qlen[qt] = live ? row_tokens(A, row) : 0x7FFFFFFF;
+    lmin = min(lmin, qlen[qt]);
     const uint16_t* qp = A.q + ((size_t)row * A.n_heads + head) * HEAD_DIM;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -112,170 +168,198 @@ __global__ void __launch_bounds__(ATT_THREADS) q8_attn_kernel(AttnArgs A) {
       qop[qt][u] = __builtin_bit_cast(half8v, v);
     }
   }
-
-  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
-  floatx4 acc[2][8];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+  for (int o = 1; o < 64; o <<= 1) lmin = min(lmin, __shfl_xor(lmin, o, 64));
+  // the wave's page list, one entry per lane, clamped into the pool
+  const int32_t* tab = A.table + (size_t)a * A.max_pages;
+  int pg_l = 0;
+  if (lane < PAGES_PER_WAVE && p0 + lane < p1) pg_l = min(max(tab[p0 + lane], 0), A.n_pages - 1);
+  auto page_ptr = [&](int p) {
+    const int pg = __builtin_amdgcn_readlane(pg_l, p - p0);
+    return A.pool + ((size_t)pg * A.n_kv + kvh) * PAGE_HEAD_BYTES;
+  };
+
+  // running state: per query column the max (log2 units) and this lane's
+  // share of the sum; the outputs in units of 2^12 / sig_run, sig_run the
+  // largest page bound so far
+  float m[NQT], lsum[NQT];
+  floatx4 acc[NQT][8];
+  float sig_run = 0.f;
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    m[qt] = -INFINITY;
+    lsum[qt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[qt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  const int32_t* tab = A.table + (size_t)a * A.max_pages;
-  for (int p = p0; p < p1; ++p) {
-    const int page = min(max(tab[p], 0), A.n_pages - 1);  // in range whatever the table holds
-    const uint8_t* ph = A.pool + ((size_t)page * A.n_kv + kvh) * PAGE_HEAD_BYTES;
-    // K quants of token c, dims 32u + 8g .. +7; scales of tokens 4g..4g+3
-    // (all four blocks); V quants of dims 16 dt + c, tokens 4g .. 4g+3; V
-    // scales of tokens 4g .. 4g+3
-    u32x2 kq[4];
+  auto page_step = [&](const PageRaw& R, int p) {
+    const int tok0 = p * PAGE_TOKENS + 4 * g;  // this lane's first token
+    const bool full = (p + 1) * PAGE_TOKENS <= lmin;
+    float pv[NQT][4], alpha[NQT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      kq[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(ph + c * 128 + 32 * u + 8 * g));
-    const u32x4 ks0 = *reinterpret_cast<const u32x4*>(ph + 2048 + 32 * g);
-    const u32x4 ks1 = *reinterpret_cast<const u32x4*>(ph + 2048 + 32 * g + 16);
-    uint32_t vq[8];
+    for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      vq[dt] = __builtin_nontemporal_load(
-          reinterpret_cast<const uint32_t*>(ph + 2176 + (16 * dt + c) * 16 + 4 * g));
-    const u32x4 vs0 = *reinterpret_cast<const u32x4*>(ph + 4224 + 32 * g);
-    const u32x4 vs1 = *reinterpret_cast<const u32x4*>(ph + 4224 + 32 * g + 16);
-    // ks[r][u]: token 4g + r, block u
-    float ks[4][4], vs[4][4];
-    {
-      const uint32_t kw[8] = {ks0.x, ks0.y, ks0.z, ks0.w, ks1.x, ks1.y, ks1.z, ks1.w};
-      const uint32_t vw[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = 4 * r + u;
-          ks[r][u] = (float)bit_cast_<_Float16>((uint16_t)(kw[i >> 1] >> (16 * (i & 1))));
-          vs[r][u] = (float)bit_cast_<_Float16>((uint16_t)(vw[i >> 1] >> (16 * (i & 1))));
-        }
-    }
-    // K quants as exact binary16 (A operand of the score MFMA)
-    half8v ka[4];
+      for (int r = 0; r < 4; ++r) pv[qt][r] = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint32_t w[2] = {kq[u].x, kq[u].y};
+      const half4v x = i8x4_to_h4(R.kq[u].x), y = i8x4_to_h4(R.kq[u].y);
+      const half8v ka = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        ka[u][e] = (_Float16)(float)(int8_t)(w[e >> 2] >> (8 * (e & 3)));
-    }
-    // the page's V scale bound: a power of two >= every scale of the page
-    float vmax = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) vmax = fmaxf(vmax, vs[r][u]);
-    vmax = xor_max(xor_max(vmax, 16), 32);  // the page's 16 tokens: lane groups g = 0..3
-    const uint32_t vb = __builtin_bit_cast(uint32_t, vmax);
-    const float sigma = vmax > 0.f ? __builtin_bit_cast(float, (vb + 0x007FFFFFu) & 0xFF800000u) : 1.f;
-    const float bscale = P_SCALE / sigma;
-
-    const int tok0 = p * PAGE_TOKENS + 4 * g;  // this lane's first token
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      floatx4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int qt = 0; qt < NQT; ++qt) {
         const floatx4 su =
-            __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u], qop[qt][u], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qop[qt][u], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] = __builtin_fmaf(ks[r][u], su[r], s[r]);
+        for (int r = 0; r < 4; ++r) pv[qt][r] = __builtin_fmaf(half_at(R.ks, 4 * r + u), su[r], pv[qt][r]);
       }
-      float pv[4];
+    }
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
       float mp = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pv[r] = tok0 + r < qlen[qt] ? s[r] * A.qk_scale : -INFINITY;
-        mp = fmaxf(mp, pv[r]);
+        pv[qt][r] = full || tok0 + r < qlen[qt] ? pv[qt][r] * A.qk_scale : -INFINITY;
+        mp = fmaxf(mp, pv[qt][r]);
       }
       mp = xor_max(xor_max(mp, 16), 32);
       const float mn = fmaxf(m[qt], mp);
-      float alpha = 1.f, ps = 0.f;
-      if (mn != -INFINITY) {
-        alpha = exp2f(m[qt] - mn);
+      const float ms = mn == -INFINITY ? 0.f : mn;
+      alpha[qt] = exp2f(m[qt] - ms);
+      float ps = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pv[r] = exp2f(pv[r] - mn);
-          ps += pv[r];
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pv[r] = 0.f;
+      for (int r = 0; r < 4; ++r) {
+        pv[qt][r] = exp2f(pv[qt][r] - ms);
+        ps += pv[qt][r];
       }
-      ps = xor_sum(xor_sum(ps, 16), 32);
-      lsum[qt] = __builtin_fmaf(lsum[qt], alpha, ps);
+      lsum[qt] = __builtin_fmaf(lsum[qt], alpha[qt], ps);
       m[qt] = mn;
+    }
+    // the page's V bound: a power of two >= every |scale| of its 16 tokens
+    // (on the binary16 bits: |x| orders as its magnitude bits)
+    uint32_t vbits = 0;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int b = dt >> 1;
-        half4v bh, bl;
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w = R.vs[i >> 2][i & 3] & 0x7FFF7FFFu;
+      vbits = max(vbits, max(w & 0xFFFFu, w >> 16));
+    }
+    vbits = max(vbits, (uint32_t)__shfl_xor((int)vbits, 16, 64));
+    vbits = max(vbits, (uint32_t)__shfl_xor((int)vbits, 32, 64));
+    const float vmax = (float)bit_cast_<_Float16>((uint16_t)vbits);
+    const uint32_t vb = __builtin_bit_cast(uint32_t, vmax);
+    const float sig_p = vmax > 0.f ? __builtin_bit_cast(float, (vb + 0x007FFFFFu) & 0xFF800000u) : 0.f;
+    const float sig_new = fmaxf(sig_run, sig_p);
+    bool change = sig_new != sig_run;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = pv[r] * vs[r][b] * bscale;
-          const _Float16 h = (_Float16)v;
-          bh[r] = h;
-          bl[r] = (_Float16)(v - (float)h);
-        }
-        half4v av;
+    for (int qt = 0; qt < NQT; ++qt) change |= alpha[qt] != 1.f;
+    if (__builtin_amdgcn_ballot_w64(change) != 0) {  // uniform branch
+      const float ratio = sig_new > 0.f ? sig_run / sig_new : 1.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) av[r] = (_Float16)(float)(int8_t)(vq[dt] >> (8 * r));
-        floatx4 t = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bh, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bl, t, 0, 0, 0);
-        const floatx4 al = {alpha, alpha, alpha, alpha};
-        const floatx4 sg = {sigma, sigma, sigma, sigma};
-        acc[qt][dt] = __builtin_elementwise_fma(sg, t, acc[qt][dt] * al);
+      for (int qt = 0; qt < NQT; ++qt) {
+        const float f = alpha[qt] * ratio;
+        const floatx4 ff = {f, f, f, f};
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[qt][dt] *= ff;
       }
+      sig_run = sig_new;
+    }
+    const float bscale = sig_run > 0.f ? P_SCALE / sig_run : 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float vsb[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vsb[r] = half_at(R.vs, 4 * r + b) * bscale;
+      half4v bh[NQT], bl[NQT];
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) {
+        uint32_t h0, h1, l0, l1;
+        split2(pv[qt][0] * vsb[0], pv[qt][1] * vsb[1], h0, l0);
+        split2(pv[qt][2] * vsb[2], pv[qt][3] * vsb[3], h1, l1);
+        bh[qt] = __builtin_bit_cast(half4v, u32x2{h0, h1});
+        bl[qt] = __builtin_bit_cast(half4v, u32x2{l0, l1});
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int dt = 2 * b + e;
+        const half4v av = i8x4_to_h4(R.vq[dt]);
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+          acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bh[qt], acc[qt][dt], 0, 0, 0);
+          acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bl[qt], acc[qt][dt], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // two page buffers in registers: the next page's loads are in flight while
+  // this one is computed. The loads are unconditional (past the wave's last
+  // page they read that page again, just read and still in cache) so that
+  // each wait covers exactly the older buffer.
+  if (p0 < p1) {
+    PageRaw R0, R1;
+    load_page(R0, page_ptr(p0), c, g);
+    for (int p = p0; p < p1; p += 2) {
+      load_page(R1, page_ptr(min(p + 1, p1 - 1)), c, g);
+      __builtin_amdgcn_sched_barrier(0);  // the loads go out before the compute
+      page_step(R0, p);
+      load_page(R0, page_ptr(min(p + 2, p1 - 1)), c, g);
+      __builtin_amdgcn_sched_barrier(0);
+      if (p + 1 < p1) page_step(R1, p + 1);
     }
   }
 
-  // merge the four waves in LDS (fixed order), then one partial per workgroup
+  // merge the four waves in LDS (fixed order), one query tile at a time,
+  // then one partial per workgroup: (max, sum, 128 outputs x 2^12)
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < NQT; ++qt) {
     st_s[wave][qt][lane][0] = m[qt];
-    st_s[wave][qt][lane][1] = lsum[qt];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc_s[wave][qt][dt][lane] = acc[qt][dt];
+    st_s[wave][qt][lane][1] = xor_sum(xor_sum(lsum[qt], 16), 32);
   }
-  __syncthreads();
-  // thread: (query tile qt = wave >> 1, half of the d tiles = wave & 1), lane
-  const int qt = wave >> 1, dh = wave & 1;
-  float mx = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < ATT_WAVES; ++w) mx = fmaxf(mx, st_s[w][qt][lane][0]);
-  float L = 0.f;
-  floatx4 o[4];
+  for (int qt = 0; qt < NQT; ++qt) {
+    const floatx4 sg = {sig_run, sig_run, sig_run, sig_run};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < 8; ++dt) acc_s[wave][dt][lane] = acc[qt][dt] * sg;
+    __syncthreads();
+    float mx = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < ATT_WAVES; ++w) {
-    const float mw = st_s[w][qt][lane][0];
-    const float f = mx == -INFINITY ? 0.f : exp2f(mw - mx);
-    L = __builtin_fmaf(st_s[w][qt][lane][1], f, L);
-    const floatx4 ff = {f, f, f, f};
+    for (int w = 0; w < ATT_WAVES; ++w) mx = fmaxf(mx, st_s[w][qt][lane][0]);
+    float L = 0.f;
+    floatx4 o[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = __builtin_elementwise_fma(ff, acc_s[w][qt][4 * dh + i][lane], o[i]);
-  }
-  const int qv = 16 * qt + c;
-  if (qv < A.nqv) {
-    float* dst = A.part + ((((size_t)a * A.n_kv + kvh) * A.max_groups + grp) * MAX_QV + qv) * PART_FLOATS;
-    if (dh == 0 && g == 0) {
-      dst[0] = mx;
-      dst[1] = L;
+    for (int w = 0; w < ATT_WAVES; ++w) {
+      const float f = mx == -INFINITY ? 0.f : exp2f(st_s[w][qt][lane][0] - mx);
+      L = __builtin_fmaf(st_s[w][qt][lane][1], f, L);
+      const floatx4 ff = {f, f, f, f};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) o[i] = __builtin_elementwise_fma(ff, acc_s[w][2 * wave + i][lane], o[i]);
     }
-    // tile dt holds dims 16 dt + 4 g .. +3 of query qv (scaled by 2^12)
+    const int qv = 16 * qt + c;
+    if (qv < A.nqv) {
+      float* dst =
+          A.part + ((((size_t)a * A.n_kv + kvh) * A.max_groups + grp) * MAX_QV + qv) * PART_FLOATS;
+      if (wave == 0 && g == 0) {
+        dst[0] = mx;
+        dst[1] = L;
+      }
+      // tile dt holds dims 16 dt + 4 g .. +3 of query qv
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<floatx4*>(dst + 4 + 16 * (4 * dh + i) + 4 * g) = o[i];
+      for (int i = 0; i < 2; ++i)
+        *reinterpret_cast<floatx4*>(dst + 4 + 16 * (2 * wave + i) + 4 * g) = o[i];
+    }
+    __syncthreads();
   }
 }
 
+constexpr int MERGE_CHUNK = HEAD_DIM;
+
 // One block per (row, head), one thread per output dim: add the partials of
-// the row's agent and KV head in group order.
+// the row's agent and KV head in group order. Each thread first takes the
+// maxima and weights of every 128th group; the weights go through LDS in
+// chunks of 128 groups, and the output sums read a chunk's partials with
+// many loads in flight.
 __global__ void __launch_bounds__(HEAD_DIM) q8_attn_merge(AttnArgs A) {
+  __shared__ float red[2];
+  __shared__ float fw[MERGE_CHUNK];
   const int r = blockIdx.x / A.n_heads, h = blockIdx.x % A.n_heads, d = threadIdx.x;
   const int a = r / A.rows, j = r % A.rows;
   const int kvh = h / A.group, qv = j * A.group + h % A.group;
@@ -284,14 +368,33 @@ __global__ void __launch_bounds__(HEAD_DIM) q8_attn_merge(AttnArgs A) {
   const float* src = A.part + (((size_t)a * A.n_kv + kvh) * A.max_groups * MAX_QV + qv) * PART_FLOATS;
   const size_t stride = (size_t)MAX_QV * PART_FLOATS;
   float mx = -INFINITY;
-  for (int s = 0; s < ng; ++s) mx = fmaxf(mx, src[s * stride]);
+  for (int s = d; s < ng; s += MERGE_CHUNK) mx = fmaxf(mx, src[s * stride]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = xor_max(mx, o);
+  if ((d & 63) == 0) red[d >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(red[0], red[1]);
   float L = 0.f, o = 0.f;
-  for (int s = 0; s < ng; ++s) {
-    const float* ps = src + s * stride;
-    const float f = mx == -INFINITY ? 0.f : exp2f(ps[0] - mx);
-    L = __builtin_fmaf(ps[1], f, L);
-    o = __builtin_fmaf(ps[4 + d], f, o);
+  for (int s0 = 0; s0 < ng; s0 += MERGE_CHUNK) {
+    __syncthreads();  // red and the previous chunk's weights are consumed
+    if (s0 + d < ng) {
+      const float* ps = src + (s0 + d) * stride;
+      const float f = mx == -INFINITY ? 0.f : exp2f(ps[0] - mx);
+      fw[d] = f;
+      L = __builtin_fmaf(ps[1], f, L);
+    }
+    __syncthreads();
+    const int n = min(MERGE_CHUNK, ng - s0);
+    const float* po = src + s0 * stride + 4 + d;
+#pragma unroll 8
+    for (int i = 0; i < n; ++i) o = __builtin_fmaf(fw[i], po[i * stride], o);
   }
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) L = xor_sum(L, s);
+  __syncthreads();
+  if ((d & 63) == 0) red[d >> 6] = L;
+  __syncthreads();
+  L = red[0] + red[1];
   A.out[((size_t)r * A.n_heads + h) * HEAD_DIM + d] = L > 0.f ? o / (L * P_SCALE) : 0.f;
 }
 
@@ -343,7 +446,10 @@ int mk_q8_attn_decode(const uint16_t* Q, const void* pool, int n_pages,
   hipStream_t st = static_cast<hipStream_t>(stream);
   const long long blocks = (long long)n_agents * n_kv * A.max_groups;
   if (blocks > 0x7FFFFFFF) return MK_EINVAL;
-  hipLaunchKernelGGL(q8_attn_kernel, dim3((unsigned)blocks), dim3(ATT_THREADS), 0, st, A);
+  if (A.nqv <= 16)
+    hipLaunchKernelGGL(q8_attn_kernel<1>, dim3((unsigned)blocks), dim3(ATT_THREADS), 0, st, A);
+  else
+    hipLaunchKernelGGL(q8_attn_kernel<2>, dim3((unsigned)blocks), dim3(ATT_THREADS), 0, st, A);
   if (hipGetLastError() != hipSuccess) return MK_EHIP;
   hipLaunchKernelGGL(q8_attn_merge, dim3((unsigned)(n_agents * rows_per_agent * n_heads)),
                      dim3(HEAD_DIM), 0, st, A);
