@@ -80,29 +80,29 @@ __device__ __forceinline__ int agent_len(const AttnArgs& A, int a) {
   return n;
 }
 
-// One page-head's bytes as lane (c, g) holds them: K quants of token c, dims
-// 32u + 8g .. +7 (u = 0..3); K scales of tokens 4g .. 4g+3 (4 blocks each);
-// V quants of dims 16 dt + c, tokens 4g .. 4g+3 (dt = 0..7); V scales of
-// tokens 4g .. 4g+3.
+// One page-head's bytes as lane l = 16 g + c holds them: K quants of token
+// c, dims 32u + 8g .. +7 (u = 0..3); K scales of tokens 4g .. 4g+3 (4 blocks
+// each); V quants of dims 16 dt + c, tokens 4g .. 4g+3 (dt = 0..7); V scales
+// of tokens 4g .. 4g+3. The pool layout puts the quants in four 1 KiB slabs
+// whose 16 bytes at 16 l are exactly lane l's (slab 0: u = 0, 1; slab 1:
+// u = 2, 3; slab 2: dt = 0..3; slab 3: dt = 4..7), and the scales of the
+// lane's four tokens in the 64 bytes at 4096 + 64 g (K then V).
 struct PageRaw {
-  u32x2 kq[4];
+  u32x4 q[4];
   u32x4 ks[2];
-  uint32_t vq[8];
   u32x4 vs[2];
 };
 
 __device__ __forceinline__ void load_page(PageRaw& R, const uint8_t* ph, int c, int g) {
+  const int l = 16 * g + c;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    R.kq[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(ph + c * 128 + 32 * u + 8 * g));
-  R.ks[0] = *reinterpret_cast<const u32x4*>(ph + 2048 + 32 * g);
-  R.ks[1] = *reinterpret_cast<const u32x4*>(ph + 2048 + 32 * g + 16);
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-    R.vq[dt] = __builtin_nontemporal_load(
-        reinterpret_cast<const uint32_t*>(ph + 2176 + (16 * dt + c) * 16 + 4 * g));
-  R.vs[0] = *reinterpret_cast<const u32x4*>(ph + 4224 + 32 * g);
-  R.vs[1] = *reinterpret_cast<const u32x4*>(ph + 4224 + 32 * g + 16);
+  for (int i = 0; i < 4; ++i)
+    R.q[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ph + 1024 * i + 16 * l));
+  const u32x4* sc = reinterpret_cast<const u32x4*>(ph + 4096 + 64 * g);  // shared by 16 lanes
+  R.ks[0] = sc[0];
+  R.ks[1] = sc[1];
+  R.vs[0] = sc[2];
+  R.vs[1] = sc[3];
 }
 
 // binary16 number i (0..15) of a 32-byte scale group
@@ -110,6 +110,9 @@ __device__ __forceinline__ float half_at(const u32x4 (&w)[2], int i) {
   const uint32_t x = w[i >> 3][(i >> 1) & 3];
   return (float)bit_cast_<_Float16>((uint16_t)(x >> (16 * (i & 1))));
 }
+
+// 2^k for the exponent field k of a normal float: exact, no division
+__device__ __forceinline__ float pow2_field(int k) { return __builtin_bit_cast(float, (uint32_t)k << 23); }
 
 // Four int8 numbers (a little-endian word) as exact binary16: each byte,
 // offset by 128, becomes the low mantissa byte of 1024 (binary16 0x6400), and
@@ -179,12 +182,12 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
     return A.pool + ((size_t)pg * A.n_kv + kvh) * PAGE_HEAD_BYTES;
   };
 
-  // running state: per query column the max (log2 units) and this lane's
-  // share of the sum; the outputs in units of 2^12 / sig_run, sig_run the
-  // largest page bound so far
+  // running state: per query column the max (raw score units) and this
+  // lane's share of the sum; the outputs in units of 2^12 / sigma_run,
+  // sigma_run the largest page bound so far
   float m[NQT], lsum[NQT];
   floatx4 acc[NQT][8];
-  float sig_run = 0.f;
+  int ke_run = 0;  // exponent field of sigma_run; 0 before any nonzero V scale
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     m[qt] = -INFINITY;
@@ -203,7 +206,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
       for (int r = 0; r < 4; ++r) pv[qt][r] = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const half4v x = i8x4_to_h4(R.kq[u].x), y = i8x4_to_h4(R.kq[u].y);
+      const half4v x = i8x4_to_h4(R.q[u >> 1][2 * (u & 1)]), y = i8x4_to_h4(R.q[u >> 1][2 * (u & 1) + 1]);
       const half8v ka = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt) {
@@ -215,20 +218,22 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
     }
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
+      // scores stay in raw units (the running max too); the weights are
+      // 2^(qk_scale (s - m)), qk_scale = log2(e) / sqrt(128) > 0
       float mp = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pv[qt][r] = full || tok0 + r < qlen[qt] ? pv[qt][r] * A.qk_scale : -INFINITY;
+        pv[qt][r] = full || tok0 + r < qlen[qt] ? pv[qt][r] : -INFINITY;
         mp = fmaxf(mp, pv[qt][r]);
       }
       mp = xor_max(xor_max(mp, 16), 32);
       const float mn = fmaxf(m[qt], mp);
-      const float ms = mn == -INFINITY ? 0.f : mn;
-      alpha[qt] = exp2f(m[qt] - ms);
+      const float ms = mn == -INFINITY ? 0.f : -mn * A.qk_scale;
+      alpha[qt] = __builtin_amdgcn_exp2f(__builtin_fmaf(m[qt], A.qk_scale, ms));
       float ps = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pv[qt][r] = exp2f(pv[qt][r] - ms);
+        pv[qt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(pv[qt][r], A.qk_scale, ms));
         ps += pv[qt][r];
       }
       lsum[qt] = __builtin_fmaf(lsum[qt], alpha[qt], ps);
@@ -245,29 +250,33 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
     vbits = max(vbits, (uint32_t)__shfl_xor((int)vbits, 16, 64));
     vbits = max(vbits, (uint32_t)__shfl_xor((int)vbits, 32, 64));
     const float vmax = (float)bit_cast_<_Float16>((uint16_t)vbits);
+    // sigma as an exponent field (0: no nonzero scale yet); vmax is a
+    // binary16 value, so 2^-24 <= sigma <= 2^16 and every power below is normal
     const uint32_t vb = __builtin_bit_cast(uint32_t, vmax);
-    const float sig_p = vmax > 0.f ? __builtin_bit_cast(float, (vb + 0x007FFFFFu) & 0xFF800000u) : 0.f;
-    const float sig_new = fmaxf(sig_run, sig_p);
-    bool change = sig_new != sig_run;
+    const int ke_p = vmax > 0.f ? (int)(((vb + 0x007FFFFFu) & 0xFF800000u) >> 23) : 0;
+    const int ke_new = max(ke_run, ke_p);
+    const bool grew = ke_new != ke_run;
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) change |= alpha[qt] != 1.f;
-    if (__builtin_amdgcn_ballot_w64(change) != 0) {  // uniform branch
-      const float ratio = sig_new > 0.f ? sig_run / sig_new : 1.f;
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) {
-        const float f = alpha[qt] * ratio;
+    for (int qt = 0; qt < NQT; ++qt) {
+      if (grew || __builtin_amdgcn_ballot_w64(alpha[qt] != 1.f) != 0) {  // uniform branch
+        const float f = ke_run > 0 ? alpha[qt] * pow2_field(127 + ke_run - ke_new) : 0.f;
         const floatx4 ff = {f, f, f, f};
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) acc[qt][dt] *= ff;
       }
-      sig_run = sig_new;
     }
-    const float bscale = sig_run > 0.f ? P_SCALE / sig_run : 0.f;
+    ke_run = ke_new;
+    // the weights times 2^12 / sigma_run
+    const float bscale = ke_run > 0 ? pow2_field(266 - ke_run) : 0.f;
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[qt][r] *= bscale;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       float vsb[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vsb[r] = half_at(R.vs, 4 * r + b) * bscale;
+      for (int r = 0; r < 4; ++r) vsb[r] = half_at(R.vs, 4 * r + b);
       half4v bh[NQT], bl[NQT];
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt) {
@@ -280,7 +289,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int dt = 2 * b + e;
-        const half4v av = i8x4_to_h4(R.vq[dt]);
+        const half4v av = i8x4_to_h4(R.q[2 + (dt >> 2)][dt & 3]);
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
           acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bh[qt], acc[qt][dt], 0, 0, 0);
@@ -311,12 +320,13 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
   // then one partial per workgroup: (max, sum, 128 outputs x 2^12)
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
-    st_s[wave][qt][lane][0] = m[qt];
+    st_s[wave][qt][lane][0] = m[qt] * A.qk_scale;  // log2 units, as the partials
     st_s[wave][qt][lane][1] = xor_sum(xor_sum(lsum[qt], 16), 32);
   }
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
-    const floatx4 sg = {sig_run, sig_run, sig_run, sig_run};
+    const float sr = ke_run > 0 ? pow2_field(ke_run) : 0.f;
+    const floatx4 sg = {sr, sr, sr, sr};
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc_s[wave][dt][lane] = acc[qt][dt] * sg;
     __syncthreads();

@@ -9,15 +9,21 @@
  * rows_per_agent rows (next token + drafts): row r = a * rows_per_agent + j.
  *
  * KV pool (device, caller-owned): 16-token pages; page p, KV head h is 4352
- * bytes at (p * n_kv + h) * 4352:
- *   K quants [16 tokens][128 dims] int8          bytes    0..2047
- *   K scales [16 tokens][4 blocks] binary16      bytes 2048..2175
- *   V quants [128 dims][16 tokens] int8          bytes 2176..4223
- *   V scales [16 tokens][4 blocks] binary16      bytes 4224..4351
- * Token t's value in dim d is scale[t][d / 32] * quant (q8_0: one binary16
- * scale per 32 values; the quants are kept apart from their scales, and V
- * dim-major, so that every load is aligned and the value product needs no
- * transpose).
+ * bytes at (p * n_kv + h) * 4352. Token t's value in dim d is
+ * scale(t, d / 32) * quant(t, d) (q8_0: one binary16 scale per 32 values,
+ * int8 quants). Byte offsets within the page-head (b = d / 32):
+ *   K quant (t, d)  1024 * (b / 2) + 16 * (16 * ((d % 32) / 8) + t)
+ *                   + 8 * (b % 2) + d % 8
+ *   V quant (t, d)  1024 * (2 + d / 64) + 16 * (16 * (t / 4) + d % 16)
+ *                   + 4 * ((d / 16) % 4) + t % 4
+ *   K scale (t, b)  4096 + 64 * (t / 4) + 2 * (4 * (t % 4) + b)
+ *   V scale (t, b)  4096 + 64 * (t / 4) + 32 + 2 * (4 * (t % 4) + b)
+ * That is, the 4096 quant bytes are four 1 KiB slabs of 64 x 16 bytes, the
+ * 16 bytes at 16 * l of each slab being what lane l of a 64-wide wave feeds
+ * to its matrix-core operands (slabs 0-1: K of token l % 16, slabs 2-3: V
+ * of tokens 4 (l / 16) .. +3); the scales follow in 64-byte groups of four
+ * tokens. A page then arrives as four fully contiguous 16-byte-per-lane
+ * loads plus the scales, and neither product needs a transpose.
  *
  * Row r attends to the first row_len[r] tokens of its agent's sequence;
  * token i of agent a lives in page block_table[a * max_pages + i / 16], slot

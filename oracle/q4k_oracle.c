@@ -276,9 +276,12 @@ void oracle_silu(const double* v, int64_t n, double* out) {
 
 /* ---- decode attention over a paged q8_0 KV pool ----------------------------
  * A page holds 16 tokens; page p, KV head h is 4352 bytes at (p*n_kv + h)*4352:
- * K quants [16][128] int8, K scales [16][4] binary16 (token t, dims 32b..32b+31
- * share scale b), V quants [128][16] int8 (dim-major), V scales [16][4]. A
- * value is scale * quant (q8_0). */
+ * an int8 quant per K and V value and a binary16 scale per token and 32-dim
+ * block b (dims 32b..32b+31 share it), a value being scale * quant (q8_0).
+ * The 4096 quant bytes come first, as four 1 KiB slabs of 64 x 16 bytes, then
+ * 64 bytes of scales per group of four tokens (K scales of tokens 4g..4g+3,
+ * then their V scales, each [token][block]); the offset of every field is
+ * written out in oracle_q8_page. */
 #define ORACLE_PAGE_TOKENS 16
 #define ORACLE_HEAD_DIM 128
 #define ORACLE_PAGE_HEAD_BYTES 4352
@@ -288,11 +291,15 @@ void oracle_q8_page(const uint8_t* ph, double* k, double* v) {
   for (int t = 0; t < ORACLE_PAGE_TOKENS; ++t)
     for (int d = 0; d < ORACLE_HEAD_DIM; ++d) {
       const int b = d / 32;
-      const uint16_t ks = (uint16_t)(ph[2048 + 2 * (4 * t + b)] | (ph[2048 + 2 * (4 * t + b) + 1] << 8));
-      const uint16_t vs = (uint16_t)(ph[4224 + 2 * (4 * t + b)] | (ph[4224 + 2 * (4 * t + b) + 1] << 8));
-      k[t * ORACLE_HEAD_DIM + d] = oracle_f16_to_f64(ks) * (double)(int8_t)ph[t * 128 + d];
-      v[t * ORACLE_HEAD_DIM + d] =
-          oracle_f16_to_f64(vs) * (double)(int8_t)ph[2176 + d * ORACLE_PAGE_TOKENS + t];
+      /* where the page-head keeps each field (the layout of the pool) */
+      const int kq_at = 1024 * (b / 2) + 16 * (16 * ((d % 32) / 8) + t) + 8 * (b % 2) + d % 8;
+      const int vq_at = 1024 * (2 + d / 64) + 16 * (16 * (t / 4) + d % 16) + 4 * ((d / 16) % 4) + t % 4;
+      const int ks_at = 4096 + 64 * (t / 4) + 2 * (4 * (t % 4) + b);
+      const int vs_at = ks_at + 32;
+      const uint16_t ks = (uint16_t)(ph[ks_at] | (ph[ks_at + 1] << 8));
+      const uint16_t vs = (uint16_t)(ph[vs_at] | (ph[vs_at + 1] << 8));
+      k[t * ORACLE_HEAD_DIM + d] = oracle_f16_to_f64(ks) * (double)(int8_t)ph[kq_at];
+      v[t * ORACLE_HEAD_DIM + d] = oracle_f16_to_f64(vs) * (double)(int8_t)ph[vq_at];
     }
 }
 

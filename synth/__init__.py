@@ -172,8 +172,9 @@ TAG_KV = 6     # (seed, TAG_KV, n_pages, n_kv)
 
 
 def q8_pool(seed: int, n_pages: int, n_kv: int) -> np.ndarray:
-    """uint8 [n_pages, n_kv, 4352]: K quants [16][128] int8, K scales [16][4]
-    binary16, V quants [128][16] int8, V scales [16][4] binary16 per page-head."""
+    """uint8 [n_pages, n_kv, 4352]: per page-head the int8 K and V quants of 16
+    tokens x 128 dims in four 1 KiB slabs, then binary16 scales per token and
+    32-dim block in 64-byte groups of four tokens (offsets in synth.c)."""
     out = np.empty((n_pages, n_kv, KV_PAGE_HEAD_BYTES), dtype=np.uint8)
     _load().synth_q8_pool(key(seed, TAG_KV, n_pages, n_kv), n_pages, n_kv, out.ctypes.data)
     return out

@@ -28,16 +28,22 @@
  * nibble) of sub-blocks 4-7.
  *
  * Paged q8_0 KV pool (decode attention): page p, KV head h occupies 4352
- * bytes at (p * n_kv + h) * 4352: K quants [16 tokens][128] int8, K scales
- * [16 tokens][4] binary16, V quants [128 dims][16 tokens] int8 (dim-major),
- * V scales [16 tokens][4] binary16 (one scale per token and 32-dim block, as
- * in q8_0; the quants are stored apart from their scales so that every
- * load is aligned). Quants are uniform bytes; scales are binary16 of
- * |z| * 0.03, z ~ N(0,1). Page-head j (= page * n_kv + head) takes its 4096
- * quant bytes from draws j*512 .. j*512+511 of the stream keyed k ^ A5..A5
- * (8 bytes each, K quants first) and its 128 scales from the Box-Muller
- * pairs of draws j*64 .. j*64+63 of the stream keyed k ^ 5A..5A (K scales
- * first).
+ * bytes at (p * n_kv + h) * 4352, one int8 quant per value and one binary16
+ * scale per token and 32-dim block (as in q8_0), placed as follows (token t,
+ * dim d, block b = d / 32; g = t / 4 or (d % 32) / 8 as stated):
+ *   K quant (t, d): 1024 * (b / 2) + 16 * (16 * ((d % 32) / 8) + t)
+ *                   + 8 * (b % 2) + d % 8
+ *   V quant (t, d): 1024 * (2 + d / 64) + 16 * (16 * (t / 4) + d % 16)
+ *                   + 4 * ((d / 16) % 4) + t % 4
+ *   K scale (t, b): 4096 + 64 * (t / 4) + 2 * (4 * (t % 4) + b)
+ *   V scale (t, b): 4096 + 64 * (t / 4) + 32 + 2 * (4 * (t % 4) + b)
+ * Quants are uniform bytes; scales are binary16 of |z| * 0.03, z ~ N(0,1).
+ * Page-head j (= page * n_kv + head) takes its quant bytes from draws
+ * j*512 .. j*512+511 of the stream keyed k ^ A5..A5 (8 bytes each, little
+ * end first): byte t*128 + d is K quant (t, d), byte 2048 + d*16 + t is V
+ * quant (t, d). Its scales come from the Box-Muller pairs of draws
+ * j*64 .. j*64+63 of the stream keyed k ^ 5A..5A: number 4t + b is K scale
+ * (t, b), number 64 + 4t + b is V scale (t, b).
  *
  * Random source: SplitMix64 (Steele, Lea & Flood, "Fast splittable
  * pseudorandom number generators", OOPSLA 2014). Output i of the stream with
@@ -210,16 +216,24 @@ void synth_q8_pool(uint64_t key, int64_t n_pages, int64_t n_kv, uint8_t* out) {
 #pragma omp parallel for schedule(static)
   for (int64_t j = 0; j < n_pages * n_kv; ++j) {
     uint8_t* ph = out + (size_t)j * 4352;
-    for (int i = 0; i < 512; ++i) {  /* 2048 K quant bytes, then 2048 V quant bytes */
-      const uint64_t w = synth_draw(kq, (uint64_t)j * 512 + (uint64_t)i);
-      uint8_t* dst = i < 256 ? ph + 8 * i : ph + 2176 + 8 * (i - 256);
-      for (int b = 0; b < 8; ++b) dst[b] = (uint8_t)(w >> (8 * b));
+    for (int i = 0; i < 4096; ++i) {  /* 2048 K quant bytes, then 2048 V quant bytes */
+      const uint8_t q = (uint8_t)(synth_draw(kq, (uint64_t)j * 512 + (uint64_t)(i >> 3)) >> (8 * (i & 7)));
+      int off;
+      if (i < 2048) {
+        const int t = i / 128, d = i % 128, b = d / 32;
+        off = 1024 * (b / 2) + 16 * (16 * ((d % 32) / 8) + t) + 8 * (b % 2) + d % 8;
+      } else {
+        const int d = (i - 2048) / 16, t = (i - 2048) % 16;
+        off = 1024 * (2 + d / 64) + 16 * (16 * (t / 4) + d % 16) + 4 * ((d / 16) % 4) + t % 4;
+      }
+      ph[off] = q;
     }
     for (int i = 0; i < 128; ++i) {  /* 64 K scales, then 64 V scales */
       double z0, z1;
       synth_normal_pair(synth_draw(ks, (uint64_t)j * 64 + (uint64_t)(i >> 1)), &z0, &z1);
       const uint16_t sc = synth_f64_to_f16(fabs((i & 1) ? z1 : z0) * 0.03);
-      uint8_t* dst = i < 64 ? ph + 2048 + 2 * i : ph + 4224 + 2 * (i - 64);
+      const int n = i % 64, t = n / 4, b = n % 4;
+      uint8_t* dst = ph + 4096 + 64 * (t / 4) + (i < 64 ? 0 : 32) + 2 * (4 * (t % 4) + b);
       dst[0] = (uint8_t)sc;
       dst[1] = (uint8_t)(sc >> 8);
     }

@@ -90,9 +90,12 @@ def test_large_scales_and_peaked_scores():
     lengths = [500, 77]
     n_pages = 40
     pool, table, row_len, Q = setup(63, lengths, 3, 4, 2, n_pages)
-    scales = pool[:, :, 2048:2176].view(np.float16) * np.float16(40.0)    # K
-    pool[:, :, 2048:2176] = scales.view(np.uint8)
-    vsc = pool[:, :, 4224:4352].view(np.float16) * np.float16(64.0)       # V
-    pool[:, :, 4224:4352] = vsc.view(np.uint8)
-    assert np.all(np.isfinite(pool[:, :, 4224:4352].view(np.float16)))
+    # scales: 64-byte groups of four tokens at 4096, K scales then V scales
+    kat = np.concatenate([np.arange(4096 + 64 * g, 4096 + 64 * g + 32) for g in range(4)])
+    vat = kat + 32
+    def scaled(at, f):
+        return (np.ascontiguousarray(pool[:, :, at]).view(np.float16) * np.float16(f)).view(np.uint8)
+    pool[:, :, kat] = scaled(kat, 40.0)
+    pool[:, :, vat] = scaled(vat, 64.0)
+    assert np.all(np.isfinite(np.ascontiguousarray(pool[:, :, vat]).view(np.float16)))
     check(pool, table, row_len, Q, 3, 2)

@@ -471,22 +471,47 @@ def test_generated_fields_are_uniform():
 
 # --- decode attention over the paged q8_0 pool ---------------------------------
 def _page(kq=None, ks=None, vq=None, vs=None):
-    """Assemble a 4352-byte page-head from fields (no arithmetic)."""
+    """Assemble a 4352-byte page-head from fields [16 tokens][128 dims] (quants)
+    and [16 tokens][4 blocks] (scales), each placed at the offset the pool
+    layout gives it."""
     b = np.zeros(4352, dtype=np.uint8)
-    if kq is not None:
-        b[0:2048] = np.asarray(kq, dtype=np.int8).reshape(16, 128).view(np.uint8).ravel()
-    if ks is not None:
-        b[2048:2176] = np.asarray(ks, dtype=np.float16).reshape(16, 4).view(np.uint8).ravel()
-    if vq is not None:   # given [16 tokens][128 dims], stored dim-major
-        b[2176:4224] = np.asarray(vq, dtype=np.int8).reshape(16, 128).T.copy().view(np.uint8).ravel()
-    if vs is not None:
-        b[4224:4352] = np.asarray(vs, dtype=np.float16).reshape(16, 4).view(np.uint8).ravel()
+    for t in range(16):
+        for d in range(128):
+            blk = d // 32
+            if kq is not None:
+                b[1024 * (blk // 2) + 16 * (16 * ((d % 32) // 8) + t) + 8 * (blk % 2) + d % 8] = \
+                    np.int8(kq[t][d]).view(np.uint8)
+            if vq is not None:
+                b[1024 * (2 + d // 64) + 16 * (16 * (t // 4) + d % 16) + 4 * ((d // 16) % 4) + t % 4] = \
+                    np.int8(vq[t][d]).view(np.uint8)
+        for blk in range(4):
+            at = 4096 + 64 * (t // 4) + 2 * (4 * (t % 4) + blk)
+            if ks is not None:
+                b[at:at + 2] = np.array([ks[t][blk]], dtype=np.float16).view(np.uint8)
+            if vs is not None:
+                b[at + 32:at + 34] = np.array([vs[t][blk]], dtype=np.float16).view(np.uint8)
     return b
 
 
+def test_q8_page_layout_raw_bytes():
+    """Raw bytes at offsets worked out by hand from the layout: K quant
+    (token 3, dim 40) lives at 16 * (16 * 1 + 3) + 8 = 312 with its scale
+    (token 3, block 1) at 4096 + 2 * 13 = 4122; V quant (token 6, dim 77) at
+    1024 * 3 + 16 * (16 * 1 + 13) + 4 * 0 + 2 = 3538 with its scale (token 6,
+    block 2) at 4096 + 64 + 32 + 2 * 10 = 4212."""
+    b = np.zeros(4352, dtype=np.uint8)
+    b[312] = np.int8(-7).view(np.uint8)
+    b[4122:4124] = np.array([0.5], dtype=np.float16).view(np.uint8)
+    b[3538] = np.int8(100).view(np.uint8)
+    b[4212:4214] = np.array([0.125], dtype=np.float16).view(np.uint8)
+    k, v = oracle.q8_page(b)
+    assert k[3, 40] == -3.5 and np.count_nonzero(k) == 1
+    assert v[6, 77] == 12.5 and np.count_nonzero(v) == 1
+
+
 def test_q8_page_decodes_by_hand():
-    """Token t, dim d: K = ks[t][d // 32] * kq[t][d]; V likewise, V quants
-    stored dim-major. A transposed V or a wrong scale block fails."""
+    """Token t, dim d: K = ks[t][d // 32] * kq[t][d]; V likewise. A
+    transposed V or a wrong scale block fails."""
     kq = np.zeros((16, 128), dtype=np.int64)
     kq[3, 40] = -7          # token 3, dim 40: block 1
     kq[15, 127] = 127
