@@ -68,6 +68,34 @@ __device__ __forceinline__ float xor_max(float v, int m) {
 }
 __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m, 64); }
 
+// The max over lanes c, c + 16, c + 32, c + 48 (the four rows of a 16-lane
+// column) in every one of them, with the gfx950 row swaps (VALU, no LDS
+// round trip): swapping two copies of v between odd and even rows, then
+// between the wave's halves, leaves each pair holding complementary rows.
+// (Both outputs of a swap pass through an empty asm: fed one value twice,
+// the compiler may otherwise take them for equal and drop the max.)
+template <bool ROWS16>
+__device__ __forceinline__ void swap_pair(uint32_t v, uint32_t& x, uint32_t& y) {
+  const auto a = ROWS16 ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
+                        : __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  x = a[0];
+  y = a[1];
+  asm volatile("" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ uint32_t col_max_u32(uint32_t v) {
+  uint32_t x, y;
+  swap_pair<true>(v, x, y);
+  swap_pair<false>(max(x, y), x, y);
+  return max(x, y);
+}
+__device__ __forceinline__ float col_max(float v) {
+  uint32_t x, y;
+  swap_pair<true>(__builtin_bit_cast(uint32_t, v), x, y);
+  v = fmaxf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y));
+  swap_pair<false>(__builtin_bit_cast(uint32_t, v), x, y);
+  return fmaxf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y));
+}
+
 // Tokens row r attends to, clamped to what the page table can list.
 __device__ __forceinline__ int row_tokens(const AttnArgs& A, int r) {
   return min(max(A.row_len[r], 0), A.max_pages * PAGE_TOKENS);
@@ -226,7 +254,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
         pv[qt][r] = full || tok0 + r < qlen[qt] ? pv[qt][r] : -INFINITY;
         mp = fmaxf(mp, pv[qt][r]);
       }
-      mp = xor_max(xor_max(mp, 16), 32);
+      mp = col_max(mp);
       const float mn = fmaxf(m[qt], mp);
       const float ms = mn == -INFINITY ? 0.f : -mn * A.qk_scale;
       alpha[qt] = __builtin_amdgcn_exp2f(__builtin_fmaf(m[qt], A.qk_scale, ms));
@@ -247,8 +275,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
       const uint32_t w = R.vs[i >> 2][i & 3] & 0x7FFF7FFFu;
       vbits = max(vbits, max(w & 0xFFFFu, w >> 16));
     }
-    vbits = max(vbits, (uint32_t)__shfl_xor((int)vbits, 16, 64));
-    vbits = max(vbits, (uint32_t)__shfl_xor((int)vbits, 32, 64));
+    vbits = col_max_u32(vbits);
     const float vmax = (float)bit_cast_<_Float16>((uint16_t)vbits);
     // sigma as an exponent field (0: no nonzero scale yet); vmax is a
     // binary16 value, so 2^-24 <= sigma <= 2^16 and every power below is normal
