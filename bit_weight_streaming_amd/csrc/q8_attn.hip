@@ -387,17 +387,21 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
   }
 }
 
-constexpr int MERGE_CHUNK = HEAD_DIM;
+constexpr int MERGE_PARTS = 4;
+constexpr int MERGE_THREADS = MERGE_PARTS * HEAD_DIM;
+constexpr int MERGE_CHUNK = MERGE_THREADS;
 
-// One block per (row, head), one thread per output dim: add the partials of
-// the row's agent and KV head in group order. Each thread first takes the
-// maxima and weights of every 128th group; the weights go through LDS in
-// chunks of 128 groups, and the output sums read a chunk's partials with
-// many loads in flight.
-__global__ void __launch_bounds__(HEAD_DIM) q8_attn_merge(AttnArgs A) {
-  __shared__ float red[2];
+// One block per (row, head): add the partials of the row's agent and KV head.
+// Thread (part, d) sums output dim d over groups part, part + 4, ... of each
+// chunk of 512 groups, the four parts then adding up in fixed order; the
+// group weights exp2(max_g - max) go through LDS a chunk at a time. The
+// order depends only on the agent's group count.
+__global__ void __launch_bounds__(MERGE_THREADS) q8_attn_merge(AttnArgs A) {
+  __shared__ float red[MERGE_THREADS / 64];
   __shared__ float fw[MERGE_CHUNK];
-  const int r = blockIdx.x / A.n_heads, h = blockIdx.x % A.n_heads, d = threadIdx.x;
+  __shared__ float osum[MERGE_PARTS][HEAD_DIM];
+  const int tid = threadIdx.x, d = tid % HEAD_DIM, part = tid / HEAD_DIM;
+  const int r = blockIdx.x / A.n_heads, h = blockIdx.x % A.n_heads;
   const int a = r / A.rows, j = r % A.rows;
   const int kvh = h / A.group, qv = j * A.group + h % A.group;
   const int npages = (agent_len(A, a) + PAGE_TOKENS - 1) / PAGE_TOKENS;
@@ -405,34 +409,41 @@ __global__ void __launch_bounds__(HEAD_DIM) q8_attn_merge(AttnArgs A) {
   const float* src = A.part + (((size_t)a * A.n_kv + kvh) * A.max_groups * MAX_QV + qv) * PART_FLOATS;
   const size_t stride = (size_t)MAX_QV * PART_FLOATS;
   float mx = -INFINITY;
-  for (int s = d; s < ng; s += MERGE_CHUNK) mx = fmaxf(mx, src[s * stride]);
+  for (int s = tid; s < ng; s += MERGE_THREADS) mx = fmaxf(mx, src[s * stride]);
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) mx = xor_max(mx, o);
-  if ((d & 63) == 0) red[d >> 6] = mx;
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
-  mx = fmaxf(red[0], red[1]);
+#pragma unroll
+  for (int w = 0; w < MERGE_THREADS / 64; ++w) mx = fmaxf(mx, red[w]);
   float L = 0.f, o = 0.f;
   for (int s0 = 0; s0 < ng; s0 += MERGE_CHUNK) {
     __syncthreads();  // red and the previous chunk's weights are consumed
-    if (s0 + d < ng) {
-      const float* ps = src + (s0 + d) * stride;
+    if (s0 + tid < ng) {
+      const float* ps = src + (s0 + tid) * stride;
       const float f = mx == -INFINITY ? 0.f : exp2f(ps[0] - mx);
-      fw[d] = f;
+      fw[tid] = f;
       L = __builtin_fmaf(ps[1], f, L);
     }
     __syncthreads();
     const int n = min(MERGE_CHUNK, ng - s0);
     const float* po = src + s0 * stride + 4 + d;
-#pragma unroll 8
-    for (int i = 0; i < n; ++i) o = __builtin_fmaf(fw[i], po[i * stride], o);
+#pragma unroll 4
+    for (int i = part; i < n; i += MERGE_PARTS) o = __builtin_fmaf(fw[i], po[i * stride], o);
   }
 #pragma unroll
   for (int s = 1; s < 64; s <<= 1) L = xor_sum(L, s);
   __syncthreads();
-  if ((d & 63) == 0) red[d >> 6] = L;
+  if ((tid & 63) == 0) red[tid >> 6] = L;
+  osum[part][d] = o;
   __syncthreads();
-  L = red[0] + red[1];
-  A.out[((size_t)r * A.n_heads + h) * HEAD_DIM + d] = L > 0.f ? o / (L * P_SCALE) : 0.f;
+  if (part == 0) {
+    L = 0.f;
+#pragma unroll
+    for (int w = 0; w < MERGE_THREADS / 64; ++w) L += red[w];
+    o = ((osum[0][d] + osum[1][d]) + osum[2][d]) + osum[3][d];
+    A.out[((size_t)r * A.n_heads + h) * HEAD_DIM + d] = L > 0.f ? o / (L * P_SCALE) : 0.f;
+  }
 }
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -489,7 +500,7 @@ int mk_q8_attn_decode(const uint16_t* Q, const void* pool, int n_pages,
     hipLaunchKernelGGL(q8_attn_kernel<2>, dim3((unsigned)blocks), dim3(ATT_THREADS), 0, st, A);
   if (hipGetLastError() != hipSuccess) return MK_EHIP;
   hipLaunchKernelGGL(q8_attn_merge, dim3((unsigned)(n_agents * rows_per_agent * n_heads)),
-                     dim3(HEAD_DIM), 0, st, A);
+                     dim3(MERGE_THREADS), 0, st, A);
   return hipGetLastError() == hipSuccess ? MK_OK : MK_EHIP;
 }
 
