@@ -47,6 +47,7 @@ constexpr int HEAD_DIM = 128;
 constexpr int PAGE_HEAD_BYTES = 4352;
 constexpr int PAGES_PER_WAVE = 16;
 constexpr int PAGES_PER_GROUP = PAGES_PER_WAVE * ATT_WAVES;
+constexpr int TILES_PER_WAVE = 8 / ATT_WAVES;  // output tiles each wave merges
 constexpr int MAX_QV = 32;        // query vectors per (agent, KV head)
 constexpr int PART_FLOATS = 132;  // per query vector: max, sum, 128 outputs, pad
 constexpr float P_SCALE = 4096.f;  // 2^12
@@ -361,14 +362,17 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
 #pragma unroll
     for (int w = 0; w < ATT_WAVES; ++w) mx = fmaxf(mx, st_s[w][qt][lane][0]);
     float L = 0.f;
-    floatx4 o[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    floatx4 o[TILES_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < TILES_PER_WAVE; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < ATT_WAVES; ++w) {
       const float f = mx == -INFINITY ? 0.f : exp2f(st_s[w][qt][lane][0] - mx);
       L = __builtin_fmaf(st_s[w][qt][lane][1], f, L);
       const floatx4 ff = {f, f, f, f};
 #pragma unroll
-      for (int i = 0; i < 2; ++i) o[i] = __builtin_elementwise_fma(ff, acc_s[w][2 * wave + i][lane], o[i]);
+      for (int i = 0; i < TILES_PER_WAVE; ++i)
+        o[i] = __builtin_elementwise_fma(ff, acc_s[w][TILES_PER_WAVE * wave + i][lane], o[i]);
     }
     const int qv = 16 * qt + c;
     if (qv < A.nqv) {
@@ -380,8 +384,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
       }
       // tile dt holds dims 16 dt + 4 g .. +3 of query qv
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        *reinterpret_cast<floatx4*>(dst + 4 + 16 * (2 * wave + i) + 4 * g) = o[i];
+      for (int i = 0; i < TILES_PER_WAVE; ++i)
+        *reinterpret_cast<floatx4*>(dst + 4 + 16 * (TILES_PER_WAVE * wave + i) + 4 * g) = o[i];
     }
     __syncthreads();
   }
