@@ -95,6 +95,10 @@ def _load():
         lib.oracle_dequant_rows.argtypes = [vp, i64, i64, vp]
         lib.oracle_gemm.restype = ctypes.c_int
         lib.oracle_gemm.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+        lib.oracle_q6k_dequant_rows.restype = None
+        lib.oracle_q6k_dequant_rows.argtypes = [vp, i64, i64, vp]
+        lib.oracle_q6k_gemm.restype = ctypes.c_int
+        lib.oracle_q6k_gemm.argtypes = [vp, vp, i64, i64, i64, vp, vp]
         lib.oracle_gemm_std.restype = ctypes.c_int
         lib.oracle_gemm_std.argtypes = [vp, vp, i64, i64, i64, ctypes.c_double, vp, vp]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -189,6 +193,39 @@ def gemm(W: np.ndarray, X: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
                              S.ctypes.data)
     if rc != 0:
         raise RuntimeError(f"oracle_gemm failed ({rc})")
+    return y, S
+
+
+Q6K_BLOCK_BYTES = 210
+
+
+def q6k_dequant_rows(W: np.ndarray, K: int) -> np.ndarray:
+    """Exact float64 weights [nrows, K] of Q6_K rows W (uint8 [nrows, K/256*210])."""
+    W = _c(W, np.uint8)
+    nrows = W.size // (K // QK * Q6K_BLOCK_BYTES)
+    out = np.empty((nrows, K), dtype=np.float64)
+    _load().oracle_q6k_dequant_rows(W.ctypes.data, nrows, K, out.ctypes.data)
+    return out
+
+
+def q6k_gemm(W: np.ndarray, X: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Reference (y, S), both float64 [M, ncols], for the Q6_K rows W of the
+    output columns to check and fp16 activations X [M, K]."""
+    X = np.asarray(X)
+    if X.dtype != np.float16:
+        raise TypeError("X must be float16")
+    M, K = X.shape
+    if K % QK:
+        raise ValueError("K must be a multiple of 256")
+    W = _c(W, np.uint8).reshape(-1, K // QK * Q6K_BLOCK_BYTES)
+    ncols = W.shape[0]
+    xb = _c(X.view(np.uint16), np.uint16)
+    y = np.empty((M, ncols), dtype=np.float64)
+    S = np.empty((M, ncols), dtype=np.float64)
+    rc = _load().oracle_q6k_gemm(W.ctypes.data, xb.ctypes.data, M, ncols, K, y.ctypes.data,
+                                 S.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_q6k_gemm failed ({rc})")
     return y, S
 
 

@@ -154,9 +154,11 @@ void oracle_standardize(const double* v, int64_t M, int64_t N, double eps, doubl
  * product both references below share. Threads split the columns; each
  * column is dequantized once into a private double buffer, then every row m
  * is a plain in-order dot product. */
-static int gemm_f64(const uint8_t* W, const double* xd, int64_t M, int64_t ncols, int64_t K,
-                    double* y, double* S) {
-  int64_t row_bytes = K / ORACLE_QK * ORACLE_BLOCK_BYTES;
+typedef void (*row_decoder)(const uint8_t* row, int64_t K, double* w);
+
+static int gemm_f64_rows(const uint8_t* W, int64_t row_bytes, row_decoder dequant,
+                         const double* xd, int64_t M, int64_t ncols, int64_t K, double* y,
+                         double* S) {
   int err = 0;
 #pragma omp parallel
   {
@@ -168,7 +170,7 @@ static int gemm_f64(const uint8_t* W, const double* xd, int64_t M, int64_t ncols
 #pragma omp for schedule(dynamic, 4)
     for (int64_t n = 0; n < ncols; ++n) {
       if (!w) continue;
-      oracle_dequant_row(W + n * row_bytes, K, w);
+      dequant(W + n * row_bytes, K, w);
       for (int64_t m = 0; m < M; ++m) {
         const double* xm = xd + m * K;
         double acc = 0.0, sabs = 0.0;
@@ -184,6 +186,12 @@ static int gemm_f64(const uint8_t* W, const double* xd, int64_t M, int64_t ncols
     free(w);
   }
   return err;
+}
+
+static int gemm_f64(const uint8_t* W, const double* xd, int64_t M, int64_t ncols, int64_t K,
+                    double* y, double* S) {
+  return gemm_f64_rows(W, K / ORACLE_QK * ORACLE_BLOCK_BYTES, oracle_dequant_row, xd, M, ncols,
+                       K, y, S);
 }
 
 /* Reference GEMM. W holds `ncols` weight rows (the output columns to check),
@@ -272,6 +280,52 @@ int oracle_gemm_rms(const uint8_t* W, const uint16_t* X, int64_t M, int64_t ncol
 /* SiLU of the SwiGLU feed-forward: v * sigmoid(v) = v / (1 + exp(-v)). */
 void oracle_silu(const double* v, int64_t n, double* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = v[i] / (1.0 + exp(-v[i]));
+}
+
+/* ---- Q6_K, the other k-quant of Q4_K_M files --------------------------------
+ * GGUF k-quant type Q6_K: a block of 256 weights in 210 bytes,
+ *   ql[128]  the low 4 bits of the quants,
+ *   qh[64]   the high 2 bits,
+ *   sc[16]   int8 scales, one per run of 16 consecutive weights,
+ *   d        binary16 super-scale (bytes 208-209, little-endian).
+ * Weight k (0..255) lies in half h = k / 128, quarter j = (k % 128) / 32,
+ * place l = k % 32. Its low bits are nibble j / 2 (0 low, 1 high) of
+ * ql[64h + 32 (j % 2) + l], its high bits are bits 2j, 2j+1 of qh[32h + l];
+ * q = low | high << 4 lies in 0..63 and w = d * sc[k / 16] * (q - 32). */
+#define ORACLE_Q6K_BLOCK_BYTES 210
+
+void oracle_q6k_dequant_block(const uint8_t* blk, double* w) {
+  const double d = oracle_f16_to_f64((uint16_t)(blk[208] | (blk[209] << 8)));
+  for (int k = 0; k < ORACLE_QK; ++k) {
+    const int h = k / 128, j = (k % 128) / 32, l = k % 32;
+    const int low = (blk[64 * h + 32 * (j % 2) + l] >> (4 * (j / 2))) & 15;
+    const int high = (blk[128 + 32 * h + l] >> (2 * j)) & 3;
+    const int q = low | (high << 4);
+    w[k] = d * (double)(int8_t)blk[192 + k / 16] * (double)(q - 32);
+  }
+}
+
+void oracle_q6k_dequant_row(const uint8_t* row, int64_t K, double* w) {
+  for (int64_t b = 0; b < K / ORACLE_QK; ++b)
+    oracle_q6k_dequant_block(row + b * ORACLE_Q6K_BLOCK_BYTES, w + b * ORACLE_QK);
+}
+
+void oracle_q6k_dequant_rows(const uint8_t* W, int64_t nrows, int64_t K, double* w) {
+  for (int64_t n = 0; n < nrows; ++n)
+    oracle_q6k_dequant_row(W + n * (K / ORACLE_QK) * ORACLE_Q6K_BLOCK_BYTES, K, w + n * K);
+}
+
+/* Reference GEMM over Q6_K rows: y = x * W^T, S = |x| * |W|^T, as oracle_gemm. */
+int oracle_q6k_gemm(const uint8_t* W, const uint16_t* X, int64_t M, int64_t ncols, int64_t K,
+                    double* y, double* S) {
+  if (K % ORACLE_QK) return -1;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
+  if (!xd) return -2;
+  for (int64_t i = 0; i < M * K; ++i) xd[i] = oracle_f16_to_f64(X[i]);
+  int err = gemm_f64_rows(W, K / ORACLE_QK * ORACLE_Q6K_BLOCK_BYTES, oracle_q6k_dequant_row, xd,
+                          M, ncols, K, y, S);
+  free(xd);
+  return err;
 }
 
 /* ---- decode attention over a paged q8_0 KV pool ----------------------------

@@ -81,6 +81,9 @@ def _load():
         lib.synth_q4k_rows.restype = None
         lib.synth_q4k_rows.argtypes = [u64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_void_p]
+        lib.synth_q6k_rows.restype = None
+        lib.synth_q6k_rows.argtypes = [u64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_void_p]
         lib.synth_q4k_rows_centered.restype = None
         lib.synth_q4k_rows_centered.argtypes = [u64, ctypes.c_int64, ctypes.c_int64,
                                                 ctypes.c_int64, ctypes.c_void_p]
@@ -125,6 +128,22 @@ def q4k_rows(k: int, K: int, n0: int, nrows: int, out: np.ndarray | None = None)
 
 def q4k_matrix(k: int, N: int, K: int) -> np.ndarray:
     return q4k_rows(k, K, 0, N)
+
+
+Q6K_BLOCK_BYTES = 210
+
+
+def q6k_rows(k: int, K: int, n0: int, nrows: int) -> np.ndarray:
+    """Rows [n0, n0+nrows) of the Q6_K matrix of stream k, uint8 [nrows, K/256*210]."""
+    if K % QK:
+        raise ValueError("K must be a multiple of 256")
+    out = np.empty((nrows, K // QK * Q6K_BLOCK_BYTES), dtype=np.uint8)
+    _load().synth_q6k_rows(k, K, n0, nrows, out.ctypes.data)
+    return out
+
+
+def q6k_matrix(k: int, N: int, K: int) -> np.ndarray:
+    return q6k_rows(k, K, 0, N)
 
 
 def q4k_rows_centered(k: int, K: int, n0: int, nrows: int) -> np.ndarray:

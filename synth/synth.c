@@ -210,6 +210,28 @@ void synth_normals(uint64_t key, uint64_t i0, uint64_t n, double* out) {
   }
 }
 
+/* Q6_K rows [n0, n0+nrows) of an N x K matrix (GGUF Q6_K blocks of 210
+ * bytes: ql[128], qh[64], int8 scales[16], binary16 d). Block b (= row * K/256
+ * + block in row) takes bytes 0..207 (quants and scales, uniform) from draws
+ * 27b .. 27b+25 of the stream keyed k ^ 6666..66 (8 bytes each, little end
+ * first), and d = binary16 of |z| * 2^-14 with z the first normal of the
+ * Box-Muller pair of draw 27b + 26. */
+void synth_q6k_rows(uint64_t key, int64_t K, int64_t n0, int64_t nrows, uint8_t* out) {
+  const uint64_t k6 = key ^ 0x6666666666666666ULL;
+  const int64_t nb = K / 256;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < nrows * nb; ++i) {
+    const uint64_t b = (uint64_t)((n0 + i / nb) * nb + i % nb);
+    uint8_t* blk = out + (size_t)i * 210;
+    for (int t = 0; t < 208; ++t) blk[t] = (uint8_t)(synth_draw(k6, 27 * b + (uint64_t)(t >> 3)) >> (8 * (t & 7)));
+    double z0, z1;
+    synth_normal_pair(synth_draw(k6, 27 * b + 26), &z0, &z1);
+    const uint16_t d = synth_f64_to_f16(fabs(z0) * 0x1p-14);
+    blk[208] = (uint8_t)d;
+    blk[209] = (uint8_t)(d >> 8);
+  }
+}
+
 /* Fill n_pages pages of a paged q8_0 KV pool with n_kv heads (layout above). */
 void synth_q8_pool(uint64_t key, int64_t n_pages, int64_t n_kv, uint8_t* out) {
   const uint64_t kq = key ^ 0xA5A5A5A5A5A5A5A5ULL, ks = key ^ 0x5A5A5A5A5A5A5A5AULL;

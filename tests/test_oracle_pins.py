@@ -598,3 +598,86 @@ def test_attn_matches_numpy_with_paging_and_gqa():
             p /= p.sum()
             assert np.allclose(O[r, h], p @ V, rtol=1e-12, atol=1e-14), (r, h)
             assert np.allclose(S[r, h], p @ np.abs(V).max(axis=1), rtol=1e-12, atol=1e-14), (r, h)
+
+
+# --- Q6_K (GGUF k-quant type 14) -----------------------------------------------
+def _q6k_block(d=1.0):
+    b = np.zeros(210, dtype=np.uint8)
+    b[208:210] = np.array([d], dtype=np.float16).view(np.uint8)
+    return b
+
+
+def test_q6k_single_weights_by_hand():
+    """One weight per (half, quarter), its bytes placed by hand: weight 241 is
+    half 1, quarter 3, place 17, so its low nibble is the high nibble of
+    ql[64 + 32 + 17] = ql[113] and its high bits are bits 6-7 of qh[32 + 17],
+    i.e. byte 128 + 49 = 177; its scale is sc[241 // 16] = sc[15], byte 207.
+    Every other weight of a run with a nonzero scale is q = 0, i.e. -32."""
+    b = _q6k_block(0.5)
+    b[113] = 0xA0            # high nibble 10
+    b[177] = 0x80            # bits 6-7 = 2
+    b[207] = np.int8(-3).view(np.uint8)
+    w = oracle.q6k_dequant_rows(b, 256)[0]
+    want = np.zeros(256)
+    want[240:256] = 0.5 * -3 * -32           # q = 0
+    want[241] = 0.5 * -3 * ((10 | 2 << 4) - 32)
+    assert np.array_equal(w, want)
+    # weight 70: half 0, quarter 2, place 6 -> high nibble of ql[6], bits 4-5 of
+    # qh[6] (byte 134), scale sc[4] (byte 196)
+    b = _q6k_block(2.0)
+    b[6] = 0x3F              # low nibble 15 belongs to weight 6, high nibble 3 to weight 70
+    b[134] = 0x30            # bits 4-5 = 3 (weight 70); bits 0-1 = 0 (weight 6)
+    b[196] = 1
+    b[192] = 7
+    w = oracle.q6k_dequant_rows(b, 256)[0]
+    want = np.zeros(256)
+    want[0:16] = 2.0 * 7 * -32
+    want[6] = 2.0 * 7 * (15 - 32)
+    want[64:80] = 2.0 * 1 * -32
+    want[70] = 2.0 * 1 * ((3 | 3 << 4) - 32)
+    assert np.array_equal(w, want)
+    # weight 160: half 1, quarter 1, place 0 -> low nibble of ql[64 + 32] =
+    # ql[96], bits 2-3 of qh[32] (byte 160), scale sc[10] (byte 202)
+    b = _q6k_block(1.0)
+    b[96] = 0x05
+    b[160] = 0x04            # bits 2-3 = 1
+    b[202] = 2
+    w = oracle.q6k_dequant_rows(b, 256)[0]
+    want = np.zeros(256)
+    want[160:176] = 2 * -32.0
+    want[160] = 2 * ((5 | 1 << 4) - 32)
+    assert np.array_equal(w, want)
+
+
+def test_q6k_middle_quant_is_zero_and_extremes():
+    """q = 32 (low 0, high 2) gives 0 whatever the scales; q = 63 and q = 0
+    give 31 and -32 times d * scale."""
+    b = _q6k_block(1.0)
+    b[128:192] = 0xAA        # every high pair = 2
+    b[192:208] = np.arange(1, 17, dtype=np.int8).view(np.uint8)
+    assert np.array_equal(oracle.q6k_dequant_rows(b, 256)[0], np.zeros(256))
+    b[0:128] = 0xFF
+    b[128:192] = 0xFF        # q = 63 everywhere
+    w = oracle.q6k_dequant_rows(b, 256)[0]
+    assert np.array_equal(w, 31.0 * np.repeat(np.arange(1, 17), 16))
+    b[0:192] = 0             # q = 0
+    w = oracle.q6k_dequant_rows(b, 256)[0]
+    assert np.array_equal(w, -32.0 * np.repeat(np.arange(1, 17), 16))
+
+
+def test_q6k_gemm_matches_dequant_and_subnormal_d():
+    """The GEMM is the plain product of the decoded rows (brute force on a
+    tiny case), with a subnormal binary16 d kept exact."""
+    import synth
+    W = synth.q6k_matrix(synth.key(7, 14, 3, 512), 3, 512)
+    W[1, 208:210] = np.array([2.0 ** -20], dtype=np.float16).view(np.uint8)   # subnormal
+    X = synth.f16_normal(synth.key(7, 15, 2, 512), 2 * 512).reshape(2, 512)
+    w = oracle.q6k_dequant_rows(W, 512)
+    assert np.all(np.abs(w[1, :256]) <= 2.0 ** -20 * 128 * 32)
+    y, S = oracle.q6k_gemm(W, X)
+    xd = X.astype(np.float64)
+    for m in range(2):
+        for n in range(3):
+            terms = [w[n, k] * xd[m, k] for k in range(512)]
+            assert abs(y[m, n] - sum(terms)) <= 1e-12 * sum(abs(t) for t in terms)
+            assert abs(S[m, n] - sum(abs(t) for t in terms)) <= 1e-12 * S[m, n]
