@@ -19,7 +19,8 @@ import subprocess
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 LIB_PATH = os.path.join(_HERE, "libmkq4k.so")
-_SOURCES = ["q4k_gemm.hip", "q4k_step.hip", "q4k_repack.hip", "q8_attn.hip", "mk_api.hip"]
+_SOURCES = ["q4k_gemm.hip", "q4k_step.hip", "q4k_repack.hip", "q6k_gemm.hip", "q8_attn.hip",
+            "mk_api.hip"]
 HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-fPIC", "-shared", "-std=c++17",
     # packed fp32 instructions stay off (see the build notes)
@@ -112,6 +113,12 @@ def lib():
         L.mk_q4k_repack.argtypes = [vp, vp, i, i, vp]
         L.mk_q4k_gemm_tiled.restype = i
         L.mk_q4k_gemm_tiled.argtypes = [vp, vp, vp, i, i, i, vp]
+        L.mk_q6k_tiles_bytes.restype = sz
+        L.mk_q6k_tiles_bytes.argtypes = [i, i]
+        L.mk_q6k_repack.restype = i
+        L.mk_q6k_repack.argtypes = [vp, vp, i, i, vp]
+        L.mk_q6k_gemm_tiled.restype = i
+        L.mk_q6k_gemm_tiled.argtypes = [vp, vp, vp, i, i, i, vp]
         if hasattr(L, "mk_q4k_step"):
             L.mk_q4k_step_workspace_bytes.restype = sz
             L.mk_q4k_step_workspace_bytes.argtypes = [ctypes.POINTER(_Layer), i, i]
@@ -226,6 +233,47 @@ def repack(W, N: int, K: int, out=None, stream=None):
     elif out.numel() * out.element_size() < nbytes or not out.is_contiguous():
         raise MkError(MK_EINVAL, "out too small")
     _check(lib().mk_q4k_repack(_ptr(W), _ptr(out), N, K, _stream(stream)))
+    return out
+
+
+Q6K_BLOCK_BYTES = 210
+
+
+def q6k_tiles_bytes(N: int, K: int) -> int:
+    """Bytes of the tile-record form of an N x K Q6_K matrix."""
+    return int(lib().mk_q6k_tiles_bytes(N, K))
+
+
+def q6k_repack(W, N: int, K: int, out=None, stream=None):
+    """Tile-record form (uint8 device tensor) of the Q6_K rows W (device)."""
+    import torch
+    nbytes = q6k_tiles_bytes(N, K)
+    if nbytes == 0:
+        raise MkError(MK_EINVAL, "invalid shape")
+    if W.dtype != torch.uint8 or W.numel() != N * (K // QK) * Q6K_BLOCK_BYTES or not W.is_contiguous():
+        raise MkError(MK_EINVAL, "W must be contiguous uint8 Q6_K rows")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    elif out.numel() * out.element_size() < nbytes or not out.is_contiguous():
+        raise MkError(MK_EINVAL, "out too small")
+    _check(lib().mk_q6k_repack(_ptr(W), _ptr(out), N, K, _stream(stream)))
+    return out
+
+
+def q6k_gemm_tiled(Wt, X, N: int, out=None, stream=None):
+    """Y = X * W^T with the Q6_K matrix W in tile-record form (q6k_repack()); N columns."""
+    import torch
+    if X.dim() != 2 or X.dtype != torch.float16 or not X.is_contiguous():
+        raise MkError(MK_EINVAL, "X must be a contiguous 2-D float16 tensor")
+    M, K = X.shape
+    nbytes = q6k_tiles_bytes(N, K)
+    if nbytes == 0 or Wt.dtype != torch.uint8 or Wt.numel() < nbytes or not Wt.is_contiguous():
+        raise MkError(MK_EINVAL, "Wt must be the contiguous tile-record form of an N x K Q6_K matrix")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    elif out.shape != (M, N) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise MkError(MK_EINVAL, "out must be a contiguous float32 [M, N] tensor")
+    _check(lib().mk_q6k_gemm_tiled(_ptr(Wt), _ptr(X), _ptr(out), M, N, K, _stream(stream)))
     return out
 
 

@@ -1,0 +1,212 @@
+// q6k_gemm.hip - Q6_K weights times M <= 32 stacked binary16 rows.
+//
+// Q6_K is the other k-quant of Q4_K_M model files (GGUF type 14): 256
+// weights in 210 bytes, ql[128] low nibbles, qh[64] high bit pairs, int8
+// scales per run of 16 weights, binary16 d. Weight k of a block (half
+// h = k / 128, quarter j = (k % 128) / 32, place l = k % 32) has low bits
+// nibble j / 2 of ql[64h + 32 (j % 2) + l], high bits 2j..2j+1 of
+// qh[32h + l], q = low | high << 4 and value d * sc[k / 16] * (q - 32).
+//
+// Load-time repack (mk_q6k_repack): 16 rows x one block form a 3360-byte
+// tile record laid out for the MFMA lanes. Lane l = 16 g + c (row c of the
+// tile, lane group g) feeds, for every run r of the block (one 16x16x16
+// MFMA per run), the 4 weights at places 16 (r % 2) + 4 g .. +3 of quarter
+// (r % 8) / 2 of half r / 8; its low-nibble bytes are 8 pieces of 4 bytes
+// (half h, quarter parity, run parity) and its high-bit bytes 4 pieces
+// (half, run parity):
+//   bytes    0..2047  lane l's 32 low-nibble bytes at 32 l
+//   bytes 2048..3071  lane l's 16 high-bit bytes at 2048 + 16 l
+//   bytes 3072..3327  row c's 16 scales at 3072 + 16 c
+//   bytes 3328..3359  row c's d at 3328 + 2 c
+// Rows past N are zero. Records run tile-major: tile t, block b at
+// (t * K/256 + b) * 3360.
+//
+// Product: D = X W^T per run on v_mfma_f32_16x16x16_f16 (A = 16 rows of X,
+// B = the tile's 16 weight rows as exact binary16 q - 32), so lane (c, g)
+// holds output column n = c and rows 4g..4g+3 and adds d[n] * sc[n][r]
+// times its 4 results in fp32. One workgroup of 8 waves per tile; wave w
+// takes blocks w, w + 8, ...; the waves merge in LDS in a fixed order.
+#include <string.h>
+
+#include "mk_q4k.h"
+#include "mk_q6k.h"
+#include "q4k_device.h"
+
+namespace mk {
+
+namespace {
+
+constexpr int Q6_QK = 256;
+constexpr int Q6_BLOCK = 210;
+constexpr int Q6_REC = 3360;  // 16 rows x 210 bytes
+constexpr int Q6_WAVES = 8;
+constexpr int Q6_THREADS = 64 * Q6_WAVES;
+
+// Source byte (within a raw 210-byte block) and row of record byte o.
+__device__ __forceinline__ void q6_rec_source(int o, int& row, int& src) {
+  if (o < 2048) {
+    const int l = o >> 5, p = (o & 31) >> 2, e = o & 3;
+    const int c = l & 15, g = l >> 4, h = p >> 2, jj = (p >> 1) & 1, rr = p & 1;
+    row = c;
+    src = 64 * h + 32 * jj + 16 * rr + 4 * g + e;
+  } else if (o < 3072) {
+    const int o2 = o - 2048, l = o2 >> 4, p = (o2 & 15) >> 2, e = o2 & 3;
+    const int c = l & 15, g = l >> 4, h = p >> 1, rr = p & 1;
+    row = c;
+    src = 128 + 32 * h + 16 * rr + 4 * g + e;
+  } else if (o < 3328) {
+    row = (o - 3072) >> 4;
+    src = 192 + ((o - 3072) & 15);
+  } else {
+    row = (o - 3328) >> 1;
+    src = 208 + ((o - 3328) & 1);
+  }
+}
+
+// One thread per record byte.
+__global__ void __launch_bounds__(256) q6k_repack_kernel(const uint8_t* __restrict__ W,
+                                                         uint8_t* __restrict__ T, int N, int nkb,
+                                                         long long total) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const long long rec = i / Q6_REC;
+  const int o = (int)(i - rec * Q6_REC);
+  const int t = (int)(rec / nkb), kb = (int)(rec - (long long)t * nkb);
+  int row, src;
+  q6_rec_source(o, row, src);
+  const int n = 16 * t + row;
+  T[i] = n < N ? W[((size_t)n * nkb + kb) * Q6_BLOCK + src] : (uint8_t)0;
+}
+
+// Four bytes 0..63 as exact binary16 q - 32 (0x6400 | q is 1024 + q).
+__device__ __forceinline__ half4v q6_to_h4(uint32_t q) {
+  const u32x2 b = {__builtin_amdgcn_perm(0x64646464u, q, 0x04010400u),
+                   __builtin_amdgcn_perm(0x64646464u, q, 0x04030402u)};
+  const _Float16 k = (_Float16)1056.f;
+  return __builtin_bit_cast(half4v, b) - half4v{k, k, k, k};
+}
+
+template <int MT>
+__global__ void __launch_bounds__(Q6_THREADS) q6k_gemm_kernel(const uint8_t* __restrict__ T,
+                                                              const uint16_t* __restrict__ X,
+                                                              float* __restrict__ Y, int M, int N,
+                                                              int K) {
+  __shared__ floatx4 red[Q6_WAVES][MT][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int t = blockIdx.x, nkb = K / Q6_QK;
+  const uint8_t* recs = T + (size_t)t * nkb * Q6_REC;
+
+  floatx4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // A operand rows: m = 16 mt + c (zeros past M)
+  const uint16_t* xr[MT];
+  bool live[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    live[mt] = 16 * mt + c < M;
+    xr[mt] = X + (size_t)(live[mt] ? 16 * mt + c : 0) * K + 4 * g;
+  }
+
+  for (int kb = wave; kb < nkb; kb += Q6_WAVES) {
+    const uint8_t* rec = recs + (size_t)kb * Q6_REC;
+    const u32x4 ql0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + 32 * lane));
+    const u32x4 ql1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + 32 * lane + 16));
+    const u32x4 qh = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + 2048 + 16 * lane));
+    const u32x4 sc = *reinterpret_cast<const u32x4*>(rec + 3072 + 16 * c);
+    const uint32_t dw = *reinterpret_cast<const uint32_t*>(rec + 3328 + 4 * (c >> 1));
+    const float d = (float)bit_cast_<_Float16>((uint16_t)(dw >> (16 * (c & 1))));
+    const uint32_t qlp[8] = {ql0.x, ql0.y, ql0.z, ql0.w, ql1.x, ql1.y, ql1.z, ql1.w};
+    const uint32_t qhp[4] = {qh.x, qh.y, qh.z, qh.w};
+    const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
+    // this block's activations: one base per row tile, the runs at constant
+    // offsets from it (kept from being hoisted out of the loop as 16 pointers)
+    const uint16_t* xb[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      xb[mt] = xr[mt] + (size_t)kb * Q6_QK;
+      asm volatile("" : "+v"(xb[mt]));
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (r == 8) __builtin_amdgcn_sched_barrier(0);  // bounds the activation loads in flight
+      const int h = r >> 3, j = (r & 7) >> 1, rr = r & 1;
+      const uint32_t low = (qlp[4 * h + 2 * (j & 1) + rr] >> (4 * (j >> 1))) & 0x0F0F0F0Fu;
+      const uint32_t high = ((qhp[2 * h + rr] >> (2 * j)) & 0x03030303u) << 4;
+      const half4v wb = q6_to_h4(low | high);
+      const float s = d * (float)(int8_t)(scw[r >> 2] >> (8 * (r & 3)));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x2 xv = live[mt] ? *reinterpret_cast<const u32x2*>(xb[mt] + 16 * r) : u32x2{0u, 0u};
+        const floatx4 p = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4v, xv), wb,
+                                                                 floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const floatx4 ss = {s, s, s, s};
+        acc[mt] = __builtin_elementwise_fma(ss, p, acc[mt]);
+      }
+    }
+  }
+
+  // the waves' partial sums, added in wave order
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
+  __syncthreads();
+  if (wave < MT) {  // wave mt finishes row tile mt
+    const int mt = wave;
+    floatx4 o = red[0][mt][lane];
+#pragma unroll
+    for (int w = 1; w < Q6_WAVES; ++w) o += red[w][mt][lane];
+    const int n = 16 * t + c;
+    if (n < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * mt + 4 * g + i;
+        if (m < M) Y[(size_t)m * N + n] = o[i];
+      }
+    }
+  }
+}
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+}  // namespace mk
+
+extern "C" {
+
+size_t mk_q6k_tiles_bytes(int N, int K) {
+  if (N < 1 || K < mk::Q6_QK || K % mk::Q6_QK) return 0;
+  return (size_t)((N + 15) / 16) * (K / mk::Q6_QK) * mk::Q6_REC;
+}
+
+int mk_q6k_repack(const void* W, void* tiles, int N, int K, void* stream) {
+  using namespace mk;
+  if (!W || !tiles || N < 1 || K < Q6_QK || K % Q6_QK) return MK_EINVAL;
+  if (!al16(tiles)) return MK_EALIGN;
+  const long long total = (long long)mk_q6k_tiles_bytes(N, K);
+  const long long blocks = (total + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return MK_EINVAL;
+  hipLaunchKernelGGL(q6k_repack_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(W),
+                     static_cast<uint8_t*>(tiles), N, K / Q6_QK, total);
+  return hipGetLastError() == hipSuccess ? MK_OK : MK_EHIP;
+}
+
+int mk_q6k_gemm_tiled(const void* tiles, const uint16_t* X, float* Y, int M, int N, int K,
+                      void* stream) {
+  using namespace mk;
+  if (!tiles || !X || !Y || M < 1 || M > 32 || N < 1 || K < Q6_QK || K % Q6_QK) return MK_EINVAL;
+  if (!al16(tiles) || !al16(X) || !al16(Y)) return MK_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)((N + 15) / 16)), block(Q6_THREADS);
+  const uint8_t* T = static_cast<const uint8_t*>(tiles);
+  if (M <= 16)
+    hipLaunchKernelGGL(q6k_gemm_kernel<1>, grid, block, 0, st, T, X, Y, M, N, K);
+  else
+    hipLaunchKernelGGL(q6k_gemm_kernel<2>, grid, block, 0, st, T, X, Y, M, N, K);
+  return hipGetLastError() == hipSuccess ? MK_OK : MK_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+/*
+ * mk_q6k.h - Q6_K weights times stacked binary16 rows (part of
+ * libmkq4k.so; error codes are those of mk_q4k.h).
+ *
+ * Q4_K_M model files (the format the OpenJet post's engine streams, "RTX
+ * 3090 one card, four coding agents") are mostly Q4_K with some tensors in
+ * Q6_K, the GGUF k-quant of 6 bits per weight: a block of 256 weights in
+ * 210 bytes,
+ *   bytes   0..127  ql: low 4 bits of the quants
+ *   bytes 128..191  qh: high 2 bits of the quants
+ *   bytes 192..207  sc: int8 scale of each run of 16 consecutive weights
+ *   bytes 208..209  d: binary16 super-scale, little-endian
+ * Weight k of a block (half h = k / 128, quarter j = (k % 128) / 32, place
+ * l = k % 32) has low bits nibble j / 2 (0: low) of ql[64h + 32 (j % 2) + l]
+ * and high bits 2j..2j+1 of qh[32h + l]; with q = low | high << 4 (0..63)
+ * its value is d * sc[k / 16] * (q - 32). A weight row of K values (K a
+ * multiple of 256) is K / 256 consecutive blocks.
+ *
+ * As for Q4_K, the weights are repacked once at load time into tile records
+ * of 16 rows x one block (3360 bytes, laid out for the matrix-core lanes),
+ * and the product streams those records once per call.
+ *
+ * Precision: the quants enter the matrix cores as exact binary16 q - 32,
+ * the activations as given; each run of 16 products is summed in fp32 and
+ * scaled by d * sc in fp32. Deterministic (fixed summation order for given
+ * N and K, whatever M).
+ */
+#ifndef MK_Q6K_H
+#define MK_Q6K_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MK_Q6K_BLOCK_BYTES 210 /* bytes per block of 256 weights */
+#define MK_Q6K_TILE_BYTES 3360 /* bytes per tile record: 16 rows x one block */
+
+/* Bytes of the tile-record form of an N x K Q6_K matrix: ceil(N / 16) *
+ * (K / 256) * 3360. 0 if N < 1 or K is not a positive multiple of 256. */
+size_t mk_q6k_tiles_bytes(int N, int K);
+
+/* Repack W (device, N rows x K/256 blocks of 210 bytes, row-major, any
+ * alignment) into `tiles` (device, caller-owned, mk_q6k_tiles_bytes(N, K)
+ * bytes, 16-byte aligned); rows past N are zero. Asynchronous on `stream`
+ * (a hipStream_t; NULL = the null stream). Returns MK_OK, MK_EINVAL (null
+ * pointer or bad shape), MK_EALIGN or MK_EHIP. */
+int mk_q6k_repack(const void* W, void* tiles, int N, int K, void* stream);
+
+/* Y = X * W^T for the repacked Q6_K matrix W (N x K): X binary16 [M][K]
+ * row-major, Y fp32 [M][N] row-major (device, caller-owned, 16-byte
+ * aligned), 1 <= M <= 32. Asynchronous on `stream`; no workspace. Returns
+ * MK_OK, MK_EINVAL, MK_EALIGN or MK_EHIP. */
+int mk_q6k_gemm_tiled(const void* tiles, const uint16_t* X, float* Y, int M, int N, int K,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MK_Q6K_H */

@@ -1,0 +1,93 @@
+"""GPU parity of the Q6_K product (mk_q6k_repack + mk_q6k_gemm_tiled) against
+the fp64 oracle, |y - y_ref| <= 1e-4 * S per output, S = sum_k |w x|: every
+output at sizes spanning several tiles with ragged edges, sampled columns at
+the full layer shapes, extreme blocks, and batch invariance (a row's result
+does not depend on the other rows in the call)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import bit_weight_streaming_amd as mk  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def run(W, X, N):
+    Wd = torch.from_numpy(np.ascontiguousarray(W)).to(DEV)
+    Xd = torch.from_numpy(np.ascontiguousarray(X)).to(DEV)
+    T = mk.q6k_repack(Wd, N, X.shape[1])
+    Y = mk.q6k_gemm_tiled(T, Xd, N)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy()
+
+
+def inputs(N, K, M, tag):
+    W = synth.q6k_matrix(synth.key(70 + tag, 14, N, K), N, K)
+    X = synth.f16_normal(synth.key(70 + tag, 15, M, K), M * K).reshape(M, K)
+    return W, X
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 256), (12, 37, 1024), (16, 100, 2304), (17, 48, 512),
+                                   (32, 21, 1280), (5, 333, 4096)])
+def test_q6k_all_outputs(M, N, K):
+    W, X = inputs(N, K, M, tag=M)
+    Y = run(W, X, N)
+    y_ref, S = oracle.q6k_gemm(W, X)
+    ok, worst, nbad = oracle.within_bound(Y.astype(np.float64), y_ref, S)
+    assert ok, f"{nbad} outside the bound, worst {worst:.3e}"
+    print(f"M={M} N={N} K={K}: worst |err|/S = {worst:.3e}")
+
+
+@pytest.mark.parametrize("N,K", [(5120, 17408), (17408, 5120)])
+def test_q6k_full_shapes_sampled(N, K):
+    """The down and gate/up shapes at M = 12, 512 sampled columns (and the
+    first and last) against the oracle."""
+    W, X = inputs(N, K, 12, tag=3)
+    Y = run(W, X, N)
+    cols = np.unique(np.concatenate([np.random.default_rng(9).choice(N, 512, replace=False), [0, N - 1]]))
+    y_ref, S = oracle.q6k_gemm(W[cols], X)
+    ok, worst, nbad = oracle.within_bound(Y[:, cols].astype(np.float64), y_ref, S)
+    assert ok, f"{nbad} outside the bound, worst {worst:.3e}"
+
+
+def test_q6k_extreme_blocks():
+    """Largest binary16 d with scales -128 and 127 and quants 0 and 63, and a
+    subnormal d: still within the bound (no overflow in the fp32 sums)."""
+    N, K, M = 20, 512, 12
+    W, X = inputs(N, K, M, tag=9)
+    blocks = W.reshape(N, K // 256, 210)
+    blocks[0, :, 208:210] = np.array([6.0e4], dtype=np.float16).view(np.uint8).reshape(1, 2)
+    blocks[0, :, 192:208] = np.array([-128, 127] * 8, dtype=np.int8).view(np.uint8)
+    blocks[0, :, 0:192] = 0xFF
+    blocks[1, :, 208:210] = np.array([2.0 ** -24], dtype=np.float16).view(np.uint8).reshape(1, 2)
+    X = (X.astype(np.float32) * np.float32(1e-3)).astype(np.float16)
+    Y = run(W, X, N)
+    y_ref, S = oracle.q6k_gemm(W, X)
+    assert np.all(np.isfinite(Y))
+    ok, worst, nbad = oracle.within_bound(Y.astype(np.float64), y_ref, S)
+    assert ok, f"{nbad} outside the bound, worst {worst:.3e}"
+
+
+def test_q6k_rows_bit_identical_alone_or_stacked():
+    N, K = 64, 2048
+    W, X = inputs(N, K, 12, tag=11)
+    Y = run(W, X, N)
+    for r in (0, 5, 11):
+        one = run(W, X[r:r + 1], N)
+        assert np.array_equal(one.view(np.uint32), Y[r:r + 1].view(np.uint32)), r
+
+
+def test_q6k_rejects_bad_arguments():
+    Wd = torch.zeros(32 * 210, dtype=torch.uint8, device=DEV)
+    T = mk.q6k_repack(Wd, 32, 256)
+    with pytest.raises(mk.MkError) as e:
+        mk.q6k_gemm_tiled(T, torch.zeros((33, 256), dtype=torch.float16, device=DEV), 32)
+    assert e.value.code == mk.MK_EINVAL
