@@ -160,6 +160,47 @@ def gemm_bench(seed: int, reps: int = 60) -> list:
     return out
 
 
+Q6K_CONFIGS = (("down K=17408 N=5120", 12, 5120, 17408), ("gate/up K=5120 N=17408", 12, 17408, 5120))
+Q6K_COPIES = 6
+
+
+def q6k_bench(seed: int, reps: int = 60) -> list:
+    """Time the Q6_K product (mk_q6k_gemm_tiled on tile records) at the layer
+    shapes, HIP events around `reps` back-to-back launches cycling over
+    Q6K_COPIES weight copies (about 440 MB, beyond the last-level cache).
+    Algorithmic bytes: the Q6_K weights (210 B per 256) + X + Y."""
+    import torch
+    import bit_weight_streaming_amd as mk
+    import synth
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    out = []
+    for label, M, N, K in Q6K_CONFIGS:
+        w = torch.from_numpy(synth.q6k_matrix(synth.key(seed, 14, N, K), N, K))
+        tiles = [mk.q6k_repack(w.to(dev), N, K) for _ in range(Q6K_COPIES)]
+        X = torch.from_numpy(synth.activations(seed, M, K)).to(dev)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        for i in range(2 * Q6K_COPIES):
+            mk.q6k_gemm_tiled(tiles[i % Q6K_COPIES], X, N, out=Y)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            mk.q6k_gemm_tiled(tiles[i % Q6K_COPIES], X, N, out=Y)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps * 1e-3
+        wbytes = N * (K // 256) * 210
+        alg = wbytes + M * K * 2 + M * N * 4
+        log(f"q6k {label} M={M}: {t * 1e6:.2f} us, {wbytes / t / 1e9:.1f} GB/s")
+        out.append({"config": label, "M": M, "us": round(t * 1e6, 2),
+                    "weight_GBps": round(wbytes / t / 1e9, 1),
+                    "roofline_frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
+                    "kernel": "q6k_gemm_kernel<1>"})
+        del tiles
+    return out
+
+
 ATTN_CONFIGS = (
     # (label, per-agent cache lengths, rows per agent); 48 query heads over 8
     # KV heads of 128 dims, a shared pool of 8,256 pages (132k tokens)
@@ -288,6 +329,7 @@ def main() -> int:
     ap.add_argument("--gemm-only", action="store_true",
                     help="only the single-matrix GEMM lines (no 64-layer stack)")
     ap.add_argument("--no-attn", action="store_true", help="skip the decode-attention lines")
+    ap.add_argument("--q6k-only", action="store_true", help="only time the Q6_K product")
     ap.add_argument("--attn-only", action="store_true",
                     help="only time decode attention over the 132k-token q8_0 pool")
     ap.add_argument("--walk", choices=("std", "res"), default="std",
@@ -312,6 +354,10 @@ def main() -> int:
     if args.gemm_only:
         torch.cuda.set_device(0)
         print(json.dumps({"gemm": gemm_bench(args.seed)}), flush=True)
+        return 0
+    if args.q6k_only:
+        torch.cuda.set_device(0)
+        print(json.dumps({"q6k": q6k_bench(args.seed)}), flush=True)
         return 0
     if args.attn_only:
         torch.cuda.set_device(0)
@@ -380,9 +426,11 @@ def main() -> int:
         args.no_gemm = args.no_cpu = args.no_attn = True
     if not args.no_gemm:
         gemm = gemm_bench(args.seed)
-    attn = None
+    attn = q6k = None
     if not args.no_attn:
         attn = attn_bench(args.seed)
+    if not args.no_gemm:
+        q6k = q6k_bench(args.seed)
 
     cpu = None
     if not args.no_cpu:
@@ -436,6 +484,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "gemm": gemm,
         "attn": attn,
+        "q6k": q6k,
     }
     print(json.dumps(out), flush=True)
     return 0
