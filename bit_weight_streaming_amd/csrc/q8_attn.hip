@@ -8,8 +8,9 @@
 // listed in a per-agent page table; row j sees the agent's first row_len
 // tokens. Heads are grouped over KV heads (n_heads / n_kv query heads each).
 //
-// Work split: one workgroup of 4 waves per (agent, KV head, group of 64
-// pages); wave w takes 16 consecutive pages of the group. All R x group
+// Work split: one workgroup of 4 waves per (agent, KV head, group of
+// 4 * ppw pages); wave w takes ppw consecutive pages of the group (ppw = 16
+// for page tables of 2048 pages and more, fewer for narrower tables). All R x group
 // query vectors of the (agent, KV head) ride in one wave (up to 32: two
 // 16-column MFMA tiles), so every K and V byte is read once per step.
 //
@@ -45,8 +46,18 @@ constexpr int ATT_THREADS = 64 * ATT_WAVES;
 constexpr int PAGE_TOKENS = 16;
 constexpr int HEAD_DIM = 128;
 constexpr int PAGE_HEAD_BYTES = 4352;
-constexpr int PAGES_PER_WAVE = 16;
-constexpr int PAGES_PER_GROUP = PAGES_PER_WAVE * ATT_WAVES;
+constexpr int MAX_PAGES_PER_WAVE = 16;
+
+// Pages per wave for a page table max_pages wide: 16 from 2048 pages (32k
+// tokens) up, halving below, at least 2, so that short caches still spread
+// over the chip. It depends on the table width only, never on the actual
+// lengths or the number of agents, so a row's summation order does not
+// depend on the other rows of the call.
+__host__ __device__ inline int pages_per_wave(int max_pages) {
+  int ppw = MAX_PAGES_PER_WAVE;
+  while (ppw > 2 && max_pages < 128 * ppw) ppw >>= 1;
+  return ppw;
+}
 constexpr int TILES_PER_WAVE = 8 / ATT_WAVES;  // output tiles each wave merges
 constexpr int MAX_QV = 32;        // query vectors per (agent, KV head)
 constexpr int PART_FLOATS = 132;  // per query vector: max, sum, 128 outputs, pad
@@ -61,6 +72,7 @@ struct AttnArgs {
   float* part;              // [n_agents][n_kv][max_groups][MAX_QV][PART_FLOATS]
   float* out;               // [M][n_heads][128]
   int n_agents, rows, max_pages, n_heads, n_kv, group, nqv, max_groups, n_pages;
+  int ppw;                  // pages per wave; a workgroup's group is 4 * ppw pages
   float qk_scale;           // log2(e) / sqrt(128)
 };
 
@@ -175,9 +187,10 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
   const int a = blockIdx.x / (A.max_groups * A.n_kv);
   const int len_a = agent_len(A, a);
   const int npages = (len_a + PAGE_TOKENS - 1) / PAGE_TOKENS;
-  if (grp * PAGES_PER_GROUP >= npages) return;  // nothing here (uniform per workgroup)
-  const int p0 = grp * PAGES_PER_GROUP + wave * PAGES_PER_WAVE;
-  const int p1 = min(p0 + PAGES_PER_WAVE, npages);
+  const int gpages = ATT_WAVES * A.ppw;
+  if (grp * gpages >= npages) return;  // nothing here (uniform per workgroup)
+  const int p0 = grp * gpages + wave * A.ppw;
+  const int p1 = min(p0 + A.ppw, npages);
 
   // query operands (B of the score MFMA): query vector 16 qt + c, dims
   // 32 u + 8 g .. +7; columns past the agent's query vectors hold zeros and
@@ -205,7 +218,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
   // the wave's page list, one entry per lane, clamped into the pool
   const int32_t* tab = A.table + (size_t)a * A.max_pages;
   int pg_l = 0;
-  if (lane < PAGES_PER_WAVE && p0 + lane < p1) pg_l = min(max(tab[p0 + lane], 0), A.n_pages - 1);
+  if (lane < A.ppw && p0 + lane < p1) pg_l = min(max(tab[p0 + lane], 0), A.n_pages - 1);
   auto page_ptr = [&](int p) {
     const int pg = __builtin_amdgcn_readlane(pg_l, p - p0);
     return A.pool + ((size_t)pg * A.n_kv + kvh) * PAGE_HEAD_BYTES;
@@ -409,7 +422,8 @@ __global__ void __launch_bounds__(MERGE_THREADS) q8_attn_merge(AttnArgs A) {
   const int a = r / A.rows, j = r % A.rows;
   const int kvh = h / A.group, qv = j * A.group + h % A.group;
   const int npages = (agent_len(A, a) + PAGE_TOKENS - 1) / PAGE_TOKENS;
-  const int ng = (npages + PAGES_PER_GROUP - 1) / PAGES_PER_GROUP;
+  const int gpages = ATT_WAVES * A.ppw;
+  const int ng = (npages + gpages - 1) / gpages;
   const float* src = A.part + (((size_t)a * A.n_kv + kvh) * A.max_groups * MAX_QV + qv) * PART_FLOATS;
   const size_t stride = (size_t)MAX_QV * PART_FLOATS;
   float mx = -INFINITY;
@@ -460,7 +474,8 @@ extern "C" {
 
 size_t mk_q8_attn_workspace_bytes(int n_agents, int max_pages, int n_kv) {
   if (n_agents < 1 || max_pages < 1 || n_kv < 1) return 0;
-  const size_t groups = (size_t)(max_pages + mk::PAGES_PER_GROUP - 1) / mk::PAGES_PER_GROUP;
+  const int gpages = mk::ATT_WAVES * mk::pages_per_wave(max_pages);
+  const size_t groups = (size_t)(max_pages + gpages - 1) / gpages;
   return (size_t)n_agents * n_kv * groups * mk::MAX_QV * mk::PART_FLOATS * sizeof(float);
 }
 
@@ -492,7 +507,8 @@ int mk_q8_attn_decode(const uint16_t* Q, const void* pool, int n_pages,
   A.n_kv = n_kv;
   A.group = group;
   A.nqv = rows_per_agent * group;
-  A.max_groups = (max_pages + PAGES_PER_GROUP - 1) / PAGES_PER_GROUP;
+  A.ppw = pages_per_wave(max_pages);
+  A.max_groups = (max_pages + ATT_WAVES * A.ppw - 1) / (ATT_WAVES * A.ppw);
   A.n_pages = n_pages;
   A.qk_scale = (float)(1.4426950408889634 / sqrt((double)HEAD_DIM));
   hipStream_t st = static_cast<hipStream_t>(stream);
