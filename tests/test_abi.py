@@ -124,3 +124,17 @@ def test_attn_rejects_bad_arguments(L):
     assert L.mk_q8_attn_decode(FAKE, FAKE + (1 << 32), 10, FAKE + (2 << 32), FAKE + (4 << 32),
                                4, 3, 8, 48, 8, FAKE + (5 << 32), ws, 16, None) == mk.MK_EWORKSPACE
     assert L.mk_q8_attn_workspace_bytes(4, 8, 8) == 4 * 8 * 1 * 32 * 132 * 4
+
+
+def test_q6k_rejects_bad_arguments(L):
+    T, X, Y = FAKE, FAKE + (1 << 32), FAKE + (2 << 32)
+    assert L.mk_q6k_tiles_bytes(16, 256) == 3360
+    assert L.mk_q6k_tiles_bytes(17, 512) == 2 * 2 * 3360
+    assert L.mk_q6k_tiles_bytes(16, 300) == 0 and L.mk_q6k_tiles_bytes(0, 256) == 0
+    assert L.mk_q6k_gemm_tiled(T, X, Y, 33, 16, 256, None) == mk.MK_EINVAL    # M > 32
+    assert L.mk_q6k_gemm_tiled(T, X, Y, 0, 16, 256, None) == mk.MK_EINVAL
+    assert L.mk_q6k_gemm_tiled(T, X, Y, 4, 16, 200, None) == mk.MK_EINVAL    # K % 256
+    assert L.mk_q6k_gemm_tiled(None, X, Y, 4, 16, 256, None) == mk.MK_EINVAL
+    assert L.mk_q6k_gemm_tiled(T, X + 8, Y, 4, 16, 256, None) == mk.MK_EALIGN
+    assert L.mk_q6k_repack(None, T, 16, 256, None) == mk.MK_EINVAL
+    assert L.mk_q6k_repack(X, T + 4, 16, 256, None) == mk.MK_EALIGN
