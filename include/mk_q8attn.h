@@ -25,7 +25,8 @@
  * tokens. A page then arrives as four fully contiguous 16-byte-per-lane
  * loads plus the scales, and neither product needs a transpose.
  *
- * Row r attends to the first row_len[r] tokens of its agent's sequence;
+ * Row r attends to the first row_len[r] tokens of its agent's sequence
+ * (row_len <= 0: no token, and the row's output is 0, the empty sum);
  * token i of agent a lives in page block_table[a * max_pages + i / 16], slot
  * i % 16. Head h reads KV head h / (n_heads / n_kv). Head dimension 128.
  *   s_i = (q . k_i) / sqrt(128),   O = sum_i softmax(s)_i v_i

@@ -365,7 +365,8 @@ void oracle_q8_page(const uint8_t* ph, double* k, double* v) {
  * and, for the error bound, S = sum_i p_i max_d |v_i[d]|: the size of the
  * values the row attends to, the same for every output dim of the head (a
  * per-element sum of p_i |v_i[d]| could be made of weights far below any
- * finite precision wherever the dominant token's value is 0). */
+ * finite precision wherever the dominant token's value is 0). A row with no
+ * token to attend to (row_len <= 0) gets O = 0 and S = 0: the empty sum. */
 int oracle_q8_attn(const uint16_t* Q, const uint8_t* pool, const int32_t* block_table,
                    const int32_t* row_agent, const int32_t* row_len, int64_t M,
                    int64_t max_pages, int64_t n_heads, int64_t n_kv, double* O, double* S) {
@@ -386,8 +387,12 @@ int oracle_q8_attn(const uint16_t* Q, const uint8_t* pool, const int32_t* block_
       double* o = O + (r * n_heads + h) * ORACLE_HEAD_DIM;
       double* sa = S + (r * n_heads + h) * ORACLE_HEAD_DIM;
       if (!s || !k || !v || n < 1) {
+        if (n < 1) {  /* nothing to attend to: the empty weighted sum, 0 */
+          for (int d = 0; d < ORACLE_HEAD_DIM; ++d) o[d] = sa[d] = 0.0;
+        } else {
 #pragma omp atomic write
-        err = n < 1 ? -1 : -2;
+          err = -2;
+        }
         free(s);
         free(k);
         free(v);

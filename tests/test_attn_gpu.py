@@ -99,3 +99,17 @@ def test_large_scales_and_peaked_scores():
     pool[:, :, vat] = scaled(vat, 64.0)
     assert np.all(np.isfinite(np.ascontiguousarray(pool[:, :, vat]).view(np.float16)))
     check(pool, table, row_len, Q, 3, 2)
+
+
+def test_empty_cache_rows_are_zero():
+    """An agent whose rows attend to no token (length 0, or a negative
+    length, read as 0) gets exact zeros; the other agents' rows are
+    unaffected and match the oracle."""
+    lengths, rows, H, KV = [40, 300, 1], 3, 4, 2
+    n_pages = 30
+    pool, table, row_len, Q = setup(64, lengths, rows, H, KV, n_pages)
+    row_len = row_len.copy()
+    row_len[0:3] = [0, -5, 0]          # agent 0: nothing to attend to
+    O, worst = check(pool, table, row_len, Q, rows, KV)
+    assert np.all(O[0:3] == 0.0)
+    print(f"empty-cache rows: worst |err|/S elsewhere = {worst:.3e}")

@@ -681,3 +681,16 @@ def test_q6k_gemm_matches_dequant_and_subnormal_d():
             terms = [w[n, k] * xd[m, k] for k in range(512)]
             assert abs(y[m, n] - sum(terms)) <= 1e-12 * sum(abs(t) for t in terms)
             assert abs(S[m, n] - sum(abs(t) for t in terms)) <= 1e-12 * S[m, n]
+
+
+def test_attn_empty_rows_are_the_empty_sum():
+    """row_len <= 0: no token to attend to, O = 0 and S = 0 (the empty sum);
+    the other rows are computed as usual."""
+    import synth
+    pool = synth.q8_pool(3, 4, 1)
+    table = np.array([[0, 1], [2, 3]], dtype=np.int32)
+    Q = synth.f16_normal(synth.key(3, 5, 4, 2), 4 * 2 * 128).reshape(4, 2, 128)
+    O, S = oracle.attn_decode(Q, pool, table, np.array([0, 0, 1, 1], dtype=np.int32),
+                              np.array([0, -3, 17, 1], dtype=np.int32), 1)
+    assert np.all(O[:2] == 0) and np.all(S[:2] == 0)
+    assert np.all(S[2:] > 0)
