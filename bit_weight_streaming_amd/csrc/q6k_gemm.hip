@@ -86,21 +86,23 @@ __device__ __forceinline__ half4v q6_to_h4(uint32_t q) {
   return __builtin_bit_cast(half4v, b) - half4v{k, k, k, k};
 }
 
-template <int MT>
+template <int MT, int TN>
 __global__ void __launch_bounds__(Q6_THREADS) q6k_gemm_kernel(const uint8_t* __restrict__ T,
                                                               const uint16_t* __restrict__ X,
                                                               float* __restrict__ Y, int M, int N,
                                                               int K) {
-  __shared__ floatx4 red[Q6_WAVES][MT][64];
+  __shared__ floatx4 red[Q6_WAVES][TN * MT][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
-  const int t = blockIdx.x, nkb = K / Q6_QK;
-  const uint8_t* recs = T + (size_t)t * nkb * Q6_REC;
+  const int t0 = blockIdx.x * TN, nkb = K / Q6_QK;
+  const int n_tiles = (N + 15) / 16;
 
-  floatx4 acc[MT];
+  floatx4 acc[TN][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[tn][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
   // A operand rows: m = 16 mt + c (zeros past M)
   const uint16_t* xr[MT];
   bool live[MT];
@@ -111,53 +113,59 @@ __global__ void __launch_bounds__(Q6_THREADS) q6k_gemm_kernel(const uint8_t* __r
   }
 
   for (int kb = wave; kb < nkb; kb += Q6_WAVES) {
-    const uint8_t* rec = recs + (size_t)kb * Q6_REC;
-    const u32x4 ql0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + 32 * lane));
-    const u32x4 ql1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + 32 * lane + 16));
-    const u32x4 qh = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + 2048 + 16 * lane));
-    const u32x4 sc = *reinterpret_cast<const u32x4*>(rec + 3072 + 16 * c);
-    const uint32_t dw = *reinterpret_cast<const uint32_t*>(rec + 3328 + 4 * (c >> 1));
-    const float d = (float)bit_cast_<_Float16>((uint16_t)(dw >> (16 * (c & 1))));
-    const uint32_t qlp[8] = {ql0.x, ql0.y, ql0.z, ql0.w, ql1.x, ql1.y, ql1.z, ql1.w};
-    const uint32_t qhp[4] = {qh.x, qh.y, qh.z, qh.w};
-    const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
     // this block's activations: one base per row tile, the runs at constant
-    // offsets from it (kept from being hoisted out of the loop as 16 pointers)
-    const uint16_t* xb[MT];
+    // offsets from it; loaded once for the TN weight tiles
+    u32x2 xv[MT][16];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      xb[mt] = xr[mt] + (size_t)kb * Q6_QK;
-      asm volatile("" : "+v"(xb[mt]));
+      const uint16_t* xb = xr[mt] + (size_t)kb * Q6_QK;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        xv[mt][r] = live[mt] ? *reinterpret_cast<const u32x2*>(xb + 16 * r) : u32x2{0u, 0u};
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (r == 8) __builtin_amdgcn_sched_barrier(0);  // bounds the activation loads in flight
-      const int h = r >> 3, j = (r & 7) >> 1, rr = r & 1;
-      const uint32_t low = (qlp[4 * h + 2 * (j & 1) + rr] >> (4 * (j >> 1))) & 0x0F0F0F0Fu;
-      const uint32_t high = ((qhp[2 * h + rr] >> (2 * j)) & 0x03030303u) << 4;
-      const half4v wb = q6_to_h4(low | high);
-      const float s = d * (float)(int8_t)(scw[r >> 2] >> (8 * (r & 3)));
+    for (int tn = 0; tn < TN; ++tn) {
+      const int t = min(t0 + tn, n_tiles - 1);  // a missing last tile reads the one before
+      const uint8_t* rec = T + ((size_t)t * nkb + kb) * Q6_REC;
+      const u32x4 ql0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + 32 * lane));
+      const u32x4 ql1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + 32 * lane + 16));
+      const u32x4 qh = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + 2048 + 16 * lane));
+      const u32x4 sc = *reinterpret_cast<const u32x4*>(rec + 3072 + 16 * c);
+      const uint32_t dw = *reinterpret_cast<const uint32_t*>(rec + 3328 + 4 * (c >> 1));
+      const float d = (float)bit_cast_<_Float16>((uint16_t)(dw >> (16 * (c & 1))));
+      const uint32_t qlp[8] = {ql0.x, ql0.y, ql0.z, ql0.w, ql1.x, ql1.y, ql1.z, ql1.w};
+      const uint32_t qhp[4] = {qh.x, qh.y, qh.z, qh.w};
+      const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const u32x2 xv = live[mt] ? *reinterpret_cast<const u32x2*>(xb[mt] + 16 * r) : u32x2{0u, 0u};
-        const floatx4 p = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4v, xv), wb,
-                                                                 floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        const int h = r >> 3, j = (r & 7) >> 1, rr = r & 1;
+        const uint32_t low = (qlp[4 * h + 2 * (j & 1) + rr] >> (4 * (j >> 1))) & 0x0F0F0F0Fu;
+        const uint32_t high = ((qhp[2 * h + rr] >> (2 * j)) & 0x03030303u) << 4;
+        const half4v wb = q6_to_h4(low | high);
+        const float s = d * (float)(int8_t)(scw[r >> 2] >> (8 * (r & 3)));
         const floatx4 ss = {s, s, s, s};
-        acc[mt] = __builtin_elementwise_fma(ss, p, acc[mt]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const floatx4 p = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4v, xv[mt][r]), wb,
+                                                                   floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          acc[tn][mt] = __builtin_elementwise_fma(ss, p, acc[tn][mt]);
+        }
       }
     }
   }
 
   // the waves' partial sums, added in wave order
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
-  __syncthreads();
-  if (wave < MT) {  // wave mt finishes row tile mt
-    const int mt = wave;
-    floatx4 o = red[0][mt][lane];
+  for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-    for (int w = 1; w < Q6_WAVES; ++w) o += red[w][mt][lane];
-    const int n = 16 * t + c;
+    for (int mt = 0; mt < MT; ++mt) red[wave][tn * MT + mt][lane] = acc[tn][mt];
+  __syncthreads();
+  if (wave < TN * MT) {  // wave tn * MT + mt finishes weight tile tn, row tile mt
+    const int tn = wave / MT, mt = wave % MT;
+    floatx4 o = red[0][wave][lane];
+#pragma unroll
+    for (int w = 1; w < Q6_WAVES; ++w) o += red[w][wave][lane];
+    const int n = 16 * (t0 + tn) + c;
     if (n < N) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -200,12 +208,23 @@ int mk_q6k_gemm_tiled(const void* tiles, const uint16_t* X, float* Y, int M, int
   if (!tiles || !X || !Y || M < 1 || M > 32 || N < 1 || K < Q6_QK || K % Q6_QK) return MK_EINVAL;
   if (!al16(tiles) || !al16(X) || !al16(Y)) return MK_EALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)((N + 15) / 16)), block(Q6_THREADS);
+  const int n_tiles = (N + 15) / 16;
   const uint8_t* T = static_cast<const uint8_t*>(tiles);
-  if (M <= 16)
-    hipLaunchKernelGGL(q6k_gemm_kernel<1>, grid, block, 0, st, T, X, Y, M, N, K);
-  else
-    hipLaunchKernelGGL(q6k_gemm_kernel<2>, grid, block, 0, st, T, X, Y, M, N, K);
+  // two weight tiles per workgroup share the activation loads where that
+  // still leaves 512 workgroups; the choice depends on N only
+  const bool pair = (n_tiles + 1) / 2 >= 512;
+  const dim3 grid((unsigned)(pair ? (n_tiles + 1) / 2 : n_tiles)), block(Q6_THREADS);
+  if (M <= 16) {
+    if (pair)
+      hipLaunchKernelGGL((q6k_gemm_kernel<1, 2>), grid, block, 0, st, T, X, Y, M, N, K);
+    else
+      hipLaunchKernelGGL((q6k_gemm_kernel<1, 1>), grid, block, 0, st, T, X, Y, M, N, K);
+  } else {
+    if (pair)
+      hipLaunchKernelGGL((q6k_gemm_kernel<2, 2>), grid, block, 0, st, T, X, Y, M, N, K);
+    else
+      hipLaunchKernelGGL((q6k_gemm_kernel<2, 1>), grid, block, 0, st, T, X, Y, M, N, K);
+  }
   return hipGetLastError() == hipSuccess ? MK_OK : MK_EHIP;
 }
 

@@ -91,3 +91,15 @@ def test_q6k_rejects_bad_arguments():
     with pytest.raises(mk.MkError) as e:
         mk.q6k_gemm_tiled(T, torch.zeros((33, 256), dtype=torch.float16, device=DEV), 32)
     assert e.value.code == mk.MK_EINVAL
+
+
+def test_q6k_paired_tiles_odd_count():
+    """Enough tiles for two per workgroup (>= 1023), an odd count whose last
+    pair lacks its second tile, and a ragged last tile of 2 rows: every
+    output against the oracle."""
+    N, K, M = 16386, 256, 3
+    W, X = inputs(N, K, M, tag=13)
+    Y = run(W, X, N)
+    y_ref, S = oracle.q6k_gemm(W, X)
+    ok, worst, nbad = oracle.within_bound(Y.astype(np.float64), y_ref, S)
+    assert ok, f"{nbad} outside the bound, worst {worst:.3e}"
