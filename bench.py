@@ -196,7 +196,8 @@ def q6k_bench(seed: int, reps: int = 60) -> list:
         out.append({"config": label, "M": M, "us": round(t * 1e6, 2),
                     "weight_GBps": round(wbytes / t / 1e9, 1),
                     "roofline_frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
-                    "kernel": "q6k_gemm_kernel<1, %d>" % (2 if ((N + 15) // 16 + 1) // 2 >= 512 else 1)})
+                    "kernel": "q6k_gemm_kernel<1, %d>" % (4 if ((N + 15) // 16 + 3) // 4 >= 256 else
+                                                          2 if ((N + 15) // 16 + 1) // 2 >= 512 else 1)})
         del tiles
     return out
 

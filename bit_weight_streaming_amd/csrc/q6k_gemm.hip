@@ -210,12 +210,17 @@ int mk_q6k_gemm_tiled(const void* tiles, const uint16_t* X, float* Y, int M, int
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int n_tiles = (N + 15) / 16;
   const uint8_t* T = static_cast<const uint8_t*>(tiles);
-  // two weight tiles per workgroup share the activation loads where that
-  // still leaves 512 workgroups; the choice depends on N only
+  // several weight tiles per workgroup share the activation loads: four
+  // where that still leaves 256 workgroups (one row tile), two where it
+  // leaves 512; the choice depends on N and the row-tile count only
   const bool pair = (n_tiles + 1) / 2 >= 512;
-  const dim3 grid((unsigned)(pair ? (n_tiles + 1) / 2 : n_tiles)), block(Q6_THREADS);
+  const bool quad = (n_tiles + 3) / 4 >= 256;
+  const dim3 grid((unsigned)(quad && M <= 16 ? (n_tiles + 3) / 4 : pair ? (n_tiles + 1) / 2 : n_tiles)),
+      block(Q6_THREADS);
   if (M <= 16) {
-    if (pair)
+    if (quad)
+      hipLaunchKernelGGL((q6k_gemm_kernel<1, 4>), grid, block, 0, st, T, X, Y, M, N, K);
+    else if (pair)
       hipLaunchKernelGGL((q6k_gemm_kernel<1, 2>), grid, block, 0, st, T, X, Y, M, N, K);
     else
       hipLaunchKernelGGL((q6k_gemm_kernel<1, 1>), grid, block, 0, st, T, X, Y, M, N, K);
