@@ -1,9 +1,12 @@
 // mk_api.hip - the C ABI (include/mk_q4k.h): argument validation, device
 // checks, workspace handling and dispatch to the kernels. Validation happens
 // before any HIP call, so every rejected call touches no device.
+#include <map>
 #include <mutex>
 #include <stdio.h>
 #include <string.h>
+#include <utility>
+#include <vector>
 
 #include "mk_q4k.h"
 #include "q4k_host.h"
@@ -22,12 +25,17 @@ struct DevInfo {
 DevInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
 
-// Library-owned GEMM workspace per device (mk_q4k_gemm only).
+// Library-owned GEMM workspaces (mk_q4k_gemm and mk_q4k_gemm_tiled without
+// a caller workspace), one per (device, stream): calls on one stream are
+// ordered by it, so they can share one. A workspace that is outgrown is not
+// freed (work queued on its stream may still read it; freeing it safely
+// would need a synchronisation): it is kept, unused, until the process ends.
 struct OwnedWs {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
-OwnedWs g_ws[kMaxDevices];
+std::map<std::pair<int, void*>, OwnedWs> g_ws;
+std::vector<void*> g_ws_retired;
 std::mutex g_ws_mu;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -85,23 +93,19 @@ namespace {
 // CU count assumed for workspace sizing when no gfx950 device is current.
 constexpr int kDefaultCus = 256;
 
-// Library-owned workspace of the current device with at least `bytes` bytes.
-int owned_workspace(int dev, size_t bytes, void** out) {
+// Library-owned workspace of (the current device, stream) with at least
+// `bytes` bytes. Sizes start at 64 MiB (every single-matrix plan of the
+// workload fits) and at least double when outgrown, so a stream retires few.
+int owned_workspace(int dev, void* stream, size_t bytes, void** out) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
-  OwnedWs& o = g_ws[dev];
+  OwnedWs& o = g_ws[std::make_pair(dev, stream)];
   if (o.bytes < bytes) {
-    if (o.ptr) {
-      // the old buffer may still be in use by queued work
-      if (hipDeviceSynchronize() != hipSuccess) return MK_EHIP;
-      (void)hipFree(o.ptr);
-      o.ptr = nullptr;
-      o.bytes = 0;
-    }
-    const size_t want = bytes < ((size_t)64 << 20) ? ((size_t)64 << 20) : bytes;
-    if (hipMalloc(&o.ptr, want) != hipSuccess) {
-      o.ptr = nullptr;
-      return MK_EHIP;
-    }
+    size_t want = o.bytes ? 2 * o.bytes : ((size_t)64 << 20);
+    if (want < bytes) want = bytes;
+    void* p = nullptr;
+    if (hipMalloc(&p, want) != hipSuccess) return MK_EHIP;
+    if (o.ptr) g_ws_retired.push_back(o.ptr);
+    o.ptr = p;
     o.bytes = want;
   }
   *out = o.ptr;
@@ -125,7 +129,7 @@ int run_gemm(bool tiled, const void* W, const uint16_t* X, float* Y, int M, int 
   if (!have_dev) return MK_ENODEV;
   void* ws = workspace;
   if (!caller_ws && p.ws_bytes > 0) {
-    rc = owned_workspace(dev, p.ws_bytes, &ws);
+    rc = owned_workspace(dev, stream, p.ws_bytes, &ws);
     if (rc != MK_OK) return rc;
   }
   hipError_t e = mk::gemm_launch(p, tiled, W, X, Y, M, N, K, ws, static_cast<hipStream_t>(stream));

@@ -14,12 +14,17 @@
 //   in 11 bits) through the 0x6400 exponent trick and one packed FMA; eight
 //   MFMA 16x16x32 f16 instructions contract them with the activations:
 //       C_main[m][n] = sum_{k in block} (sc_j(k) * q_k) * x[m][k]
-//   and one MFMA 16x16x16 f16 gives the min term
-//       C_min[m][n] = sum_j m_j * xsum[m][j]      (xsum split in hi+lo fp16)
+//   and one MFMA 16x16x32 f16 gives the min term
+//       C_min[m][n] = sum_j m_j * xsum[m][j]
+//   with each fp32 sub-block sum carried as three binary16 parts,
+//   xsum = 64 a + b + c (see split_xsum), against (64 m_j, m_j, m_j, 0);
 //   then acc[m][n] += d * C_main - dmin * C_min   in fp32.
 // This is the factored form of w = d*sc_j*q - dmin*m_j: every product inside
 // the MFMA is exact (11-bit * 11-bit significands), so the only roundings are
-// fp32 accumulations, far inside the 1e-4 * sum|w x| bound.
+// fp32 accumulations. Their size follows the two terms, d*sc*q*x and
+// dmin*m*x, not their difference w*x: where the two nearly cancel (w close
+// to 0 over a whole sub-block) the error is a small multiple of 2^-24 times
+// sum(|d sc q x| + |dmin m x|), which can exceed 1e-4 * sum|w x|.
 //
 // The k order inside one MFMA is free as long as both operands use it; the
 // nibble extraction yields pairs (k, k+2) per 32-bit lane-half, so the
@@ -43,8 +48,8 @@ constexpr int BLOCK_BYTES = 144;
 // LDS bytes per activation row per super-block (256 binary16 values)
 constexpr int X_BYTES_PER_BLOCK = 512;
 // LDS bytes per activation row per super-block for the sub-block sums
-// (8 sub-blocks x {hi, lo} binary16)
-constexpr int XSUM_BYTES_PER_BLOCK = 32;
+// (8 sub-blocks x {a, b, c, 0} binary16, see split_xsum)
+constexpr int XSUM_BYTES_PER_BLOCK = 64;
 // pad added to each LDS activation row so that the 16 rows read by one
 // ds_read_b128 land on distinct banks
 constexpr int X_ROW_PAD = 16;
@@ -83,7 +88,7 @@ __device__ __forceinline__ half2v small_int_pair(uint32_t v) {
 struct LaneScales {
   half2v sl, nl;  // (sc_lo, sc_lo), (-1024*sc_lo, ...): maps 1024+q -> sc_lo*q
   half2v sh, nh;  // (sc_hi/16, ...), (-64*sc_hi, ...): maps 1024+16q -> sc_hi*q
-  half4v bmin;    // (m_lo, m_lo, m_hi, m_hi): min-term MFMA operand
+  half8v bmin;    // (64 m_lo, m_lo, m_lo, 0, 64 m_hi, m_hi, m_hi, 0): min-term MFMA operand
   float d, dmin;
 };
 
@@ -113,7 +118,8 @@ __device__ __forceinline__ LaneScales lane_scales(const u32x4& h, int g) {
   s.nh = s_hi * half2v{(_Float16)-64.0f, (_Float16)-64.0f};
   const half2v m_lo = small_int_pair(mnp & 0xFFu);
   const half2v m_hi = small_int_pair(mnp >> 8);
-  s.bmin = half4v{m_lo.x, m_lo.y, m_hi.x, m_hi.y};
+  const _Float16 z = (_Float16)0.0f, k64 = (_Float16)64.0f;
+  s.bmin = half8v{m_lo.x * k64, m_lo.x, m_lo.x, z, m_hi.x * k64, m_hi.x, m_hi.x, z};
   const half2v dd = bit_cast_<half2v>(h.x);
   s.d = (float)dd.x;
   s.dmin = (float)dd.y;
@@ -258,11 +264,11 @@ __device__ __forceinline__ void mma_unit(const BlockRegs* r, int g, const char* 
       c1[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, c1[nb], 0, 0, 0);
     }
   }
-  const half4v am = *reinterpret_cast<const half4v*>(xs);
+  const half8v am = *reinterpret_cast<const half8v*>(xs);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     floatx4 cn = {0.f, 0.f, 0.f, 0.f};
-    cn = __builtin_amdgcn_mfma_f32_16x16x16f16(am, s[nb].bmin, cn, 0, 0, 0);
+    cn = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, s[nb].bmin, cn, 0, 0, 0);
     const floatx4 dd = {s[nb].d, s[nb].d, s[nb].d, s[nb].d};
     acc[nb] = __builtin_elementwise_fma(dd, c0[nb], acc[nb]);
     acc[nb] = __builtin_elementwise_fma(dd, c1[nb], acc[nb]);
@@ -355,9 +361,24 @@ __host__ __device__ inline int wave_of_unit(const Assign& a, int x) {
   return w;
 }
 
-// Sub-block sums of the staged activations, split into binary16 hi + lo, for
-// the min-term MFMA: row m, block b, sub-block j at
-// xs_lds + (m * nkb_stride + b) * 32 + 4 * j.
+// An fp32 sub-block sum as three binary16 parts, sum = 64 a + b + c: a is
+// sum / 64 rounded (|sum| <= 32 * 65504 keeps |a| <= 32752, finite), b the
+// rest rounded, c the rest of that. Both subtractions are exact in fp32, so
+// the parts hold the sum to about 33 bits where binary16 is normal, and
+// exactly whenever it is a multiple of 2^-24 smaller than 2^-3 in magnitude
+// (then a = 0 and b, c are exact). The min-term MFMA multiplies them by
+// (64 m, m, m): products of 11- and 12-bit significands, exact in fp32.
+__device__ __forceinline__ half4v split_xsum(float sum) {
+  const _Float16 a = (_Float16)(sum * 0.015625f);
+  const float r = sum - 64.f * (float)a;
+  const _Float16 b = (_Float16)r;
+  const _Float16 c = (_Float16)(r - (float)b);
+  return half4v{a, b, c, (_Float16)0.0f};
+}
+
+// Sub-block sums of the staged activations, as split_xsum parts, for the
+// min-term MFMA: row m, block b, sub-block j at
+// xs_lds + (m * nkb_stride + b) * 64 + 8 * j.
 __device__ __forceinline__ void stage_xsum(int M, int nkb, int nkb_stride, const char* x_lds,
                                            int x_stride, char* xs_lds, int tid,
                                            int nthreads) {
@@ -381,10 +402,8 @@ __device__ __forceinline__ void stage_xsum(int M, int nkb, int nkb_stride, const
         sum += (float)hh.y;
       }
     }
-    const _Float16 hi = (_Float16)sum;
-    const _Float16 lo = (_Float16)(sum - (float)hi);
-    *reinterpret_cast<half2v*>(xs_lds + ((size_t)m * nkb_stride + b) * XSUM_BYTES_PER_BLOCK +
-                               4 * j) = half2v{hi, lo};
+    *reinterpret_cast<half4v*>(xs_lds + ((size_t)m * nkb_stride + b) * XSUM_BYTES_PER_BLOCK +
+                               8 * j) = split_xsum(sum);
   }
 }
 
@@ -418,9 +437,9 @@ __device__ __forceinline__ void mma_unit_mt(const BlockRegs& r, int g, const cha
   const floatx4 nm = {-s.dmin, -s.dmin, -s.dmin, -s.dmin};
 #pragma unroll
   for (int rt = 0; rt < MT; ++rt) {
-    const half4v am = *reinterpret_cast<const half4v*>(xs[rt]);
+    const half8v am = *reinterpret_cast<const half8v*>(xs[rt]);
     floatx4 cn = {0.f, 0.f, 0.f, 0.f};
-    cn = __builtin_amdgcn_mfma_f32_16x16x16f16(am, s.bmin, cn, 0, 0, 0);
+    cn = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, s.bmin, cn, 0, 0, 0);
     acc[rt] = __builtin_elementwise_fma(dd, c0[rt], acc[rt]);
     acc[rt] = __builtin_elementwise_fma(dd, c1[rt], acc[rt]);
     acc[rt] = __builtin_elementwise_fma(nm, cn, acc[rt]);

@@ -72,7 +72,7 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
   for (int rt = 0; rt < MT; ++rt) {
     const int row = min(16 * rt + c, A.M - 1);
     xa[rt] = x_lds + (size_t)row * A.x_stride + g * 128;
-    xs[rt] = xs_lds + (size_t)row * a.nkb * XSUM_BYTES_PER_BLOCK + 8 * g;
+    xs[rt] = xs_lds + (size_t)row * a.nkb * XSUM_BYTES_PER_BLOCK + 16 * g;
   }
   const UnpackConsts k = unpack_consts();
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(A.part, A.part_bytes);

@@ -297,7 +297,7 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
 
 // Stage the binary16 activations of slice a ([M][K] at src, natural order)
 // into LDS in the MFMA order (see q4k_device.h), with the sub-block sums the
-// min term multiplies (each split into binary16 hi + lo). Each thread loads
+// min term multiplies (each as split_xsum's three binary16 parts). Each thread loads
 // up to R 8-wide chunks, all in one round; the four chunks of one 32-value
 // sub-block sit in four consecutive lanes, which add their fp32 chunk sums
 // with two lane exchanges. The row statistics of the whole input (STAT_SLOTS
@@ -356,12 +356,9 @@ __device__ __forceinline__ void stage_rounds(const uint16_t* src, int K, int M, 
     const int gq = kk >> 6, hb = (kk >> 5) & 1, u = (kk >> 3) & 3;
     *reinterpret_cast<u32x4*>(x_lds + (size_t)m * x_stride + b * X_BYTES_PER_BLOCK + gq * 128 +
                               (2 * u + hb) * 16) = o;
-    if ((ch & 3) == 0) {
-      const _Float16 hi = (_Float16)sum;
-      const _Float16 lo = (_Float16)(sum - (float)hi);
-      *reinterpret_cast<half2v*>(xs_lds + ((size_t)m * xs_stride + b) * XSUM_BYTES_PER_BLOCK +
-                                 4 * (kk >> 5)) = half2v{hi, lo};
-    }
+    if ((ch & 3) == 0)
+      *reinterpret_cast<half4v*>(xs_lds + ((size_t)m * xs_stride + b) * XSUM_BYTES_PER_BLOCK +
+                                 8 * (kk >> 5)) = split_xsum(sum);
   }
 #pragma unroll
   for (int i = 0; i < kStatPer; ++i)
@@ -977,7 +974,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
 
       // ---- stream the weights
       const char* xa_lane = x_lds + (size_t)arow * ph.x_stride + g * 128;
-      const char* xs_lane = xs_lds + (size_t)arow * ph.nkb * XSUM_BYTES_PER_BLOCK + 8 * g;
+      const char* xs_lane = xs_lds + (size_t)arow * ph.nkb * XSUM_BYTES_PER_BLOCK + 16 * g;
       if (ph.nm == 2)
         phase_compute<2>(ring, it, ph_s[p], ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, k);
       else

@@ -22,8 +22,11 @@
 //   values  O^T[d][q] += sigma * (Vq^T . B), B[t][q] = p[t][q] * vs[t][b] /
 //           sigma * 2^12 split into binary16 hi + lo (two 16x16x16 MFMAs per
 //           16-dim tile), sigma a power of two at least the page's largest V
-//           scale, so B stays in binary16's normal range; the 2^12 is taken
-//           out at the end.
+//           scale, so B is at most 2^12; the 2^12 is taken out at the end.
+//           The lo part is scaled by 2^13 against quants scaled by 2^-13
+//           (see split_hl); weights too small for hi + lo to hold to 2^-17
+//           get further parts rebased by 2^32 each (see RB_PARTS), only in
+//           waves that hold one.
 // S^T comes out of the score MFMA in exactly the register layout the value
 // MFMA wants for its B operand (4 consecutive tokens of one query per lane),
 // so no transpose is needed.
@@ -166,13 +169,122 @@ __device__ __forceinline__ half4v i8x4_to_h4(uint32_t w) {
   return __builtin_bit_cast(half4v, b) - half4v{k, k, k, k};
 }
 
-// v0, v1 as binary16 hi + lo: hi rounded toward zero, lo = the exact fp32
-// rest, itself rounded toward zero, so |v - hi - lo| < 2^-20 |v| wherever
-// binary16 is normal.
-__device__ __forceinline__ void split2(float v0, float v1, uint32_t& hi, uint32_t& lo) {
+// The value weights enter the matrix cores as two binary16 parts: hi = v
+// rounded toward zero, and lo = the rest times 2^13, rounded toward zero,
+// multiplied by value quants scaled by 2^-13 (q * 2^-13 is exact in
+// binary16 for any int8 q). Both differences are exact in fp32 (each
+// truncation keeps leading bits of its operand), so r = what is left, times
+// 2^13, is exact too. For |v| <= 2^12 the two parts hold v to 2^-17 of
+// itself down to |v| = 2^-18 (FINE): where hi is normal, hi and lo give 11
+// bits each (2^-20); below 2^-14 hi leaves less than 2^-24, which lo holds
+// to 2^-35 (2^-37 once it is subnormal too).
+constexpr float LO_UP = 8192.0f;                // 2^13
+constexpr float LO_DOWN = 1.220703125e-4f;      // 2^-13
+constexpr float FINE = 3.814697265625e-6f;      // 2^-18
+__device__ __forceinline__ void split_hl(float v0, float v1, uint32_t& hi, uint32_t& lo,
+                                         float& r0, float& r1) {
   const auto h = __builtin_amdgcn_cvt_pkrtz(v0, v1);
+  const float d0 = (v0 - (float)h[0]) * LO_UP, d1 = (v1 - (float)h[1]) * LO_UP;
+  const auto l = __builtin_amdgcn_cvt_pkrtz(d0, d1);
   hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v0 - (float)h[0], v1 - (float)h[1]));
+  lo = __builtin_bit_cast(uint32_t, l);
+  r0 = d0 - (float)l[0];
+  r1 = d1 - (float)l[1];
+}
+
+// Weights below FINE (rare: the softmax weights of a row spread over more
+// than about 2^23, or a V scale far below its page's largest) are carried
+// further: what hi + lo leave, rebased by 2^32, becomes the next pair of
+// parts, up to RB_PARTS times, each multiplied into a fresh accumulator and
+// added to the running one times 2^-32 per step. Together they hold every
+// weight down to 2^-114 (of the 2^12 the largest maps to) within 2^-17 of
+// itself; what lies below is under fp32's normal range relative to the
+// largest V scale. A wave runs them only when one of its lanes holds such a
+// weight (a per-token test with the token's least V scale, on the ballot).
+constexpr int RB_PARTS = 3;
+constexpr float RB_NEXT = 524288.0f;             // 2^19: r (units 2^13) to the next part's units 2^32
+constexpr float RB_DOWN = 2.3283064365386963e-10f;  // 2^-32
+
+// O^T += V^T * B for one page: B = the page's value weights pv (already
+// times 2^12 / sigma) times each token's V scale of block b, as split_hl's hi
+// and lo parts; with DEEP (uniform), also the parts that carry weights below
+// FINE, for the blocks where a lane holds one.
+template <int NQT>
+__device__ __forceinline__ void value_blocks(const PageRaw& R, const float (&pv)[NQT][4],
+                                             floatx4 (&acc)[NQT][8], const bool DEEP) {
+  const half4v lod = {(_Float16)LO_DOWN, (_Float16)LO_DOWN, (_Float16)LO_DOWN, (_Float16)LO_DOWN};
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    float vsb[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vsb[r] = half_at(R.vs, 4 * r + b);
+    half4v bh[NQT], bl[NQT];
+    float x[NQT][4];  // DEEP: the next part's values of the weights below FINE, else 0
+    bool more = false;
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      uint32_t h0, h1, l0, l1;
+      float wv[4], rv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wv[r] = pv[qt][r] * vsb[r];
+      split_hl(wv[0], wv[1], h0, l0, rv[0], rv[1]);
+      split_hl(wv[2], wv[3], h1, l1, rv[2], rv[3]);
+      bh[qt] = __builtin_bit_cast(half4v, u32x2{h0, h1});
+      bl[qt] = __builtin_bit_cast(half4v, u32x2{l0, l1});
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[qt][r] = DEEP && fabsf(wv[r]) < FINE ? rv[r] * RB_NEXT : 0.f;
+        more |= x[qt][r] != 0.f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int dt = 2 * b + e;
+      const half4v av = i8x4_to_h4(R.q[2 + (dt >> 2)][dt & 3]);
+      const half4v al = av * lod;  // exact: q * 2^-13
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) {
+        acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bh[qt], acc[qt][dt], 0, 0, 0);
+        acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(al, bl[qt], acc[qt][dt], 0, 0, 0);
+      }
+    }
+    if (!DEEP) continue;
+    // further parts, each rebased by 2^32, into a fresh accumulator added
+    // back times 2^-32 per part
+    float down = RB_DOWN;
+    for (int part = 0; part < RB_PARTS && __builtin_amdgcn_ballot_w64(more) != 0; ++part) {
+      more = false;
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) {
+        uint32_t h0, h1, l0, l1;
+        float rv[4];
+        split_hl(x[qt][0], x[qt][1], h0, l0, rv[0], rv[1]);
+        split_hl(x[qt][2], x[qt][3], h1, l1, rv[2], rv[3]);
+        bh[qt] = __builtin_bit_cast(half4v, u32x2{h0, h1});
+        bl[qt] = __builtin_bit_cast(half4v, u32x2{l0, l1});
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[qt][r] = fabsf(x[qt][r]) < FINE ? rv[r] * RB_NEXT : 0.f;
+          more |= x[qt][r] != 0.f;
+        }
+      }
+      const floatx4 dn = {down, down, down, down};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int dt = 2 * b + e;
+        const half4v av = i8x4_to_h4(R.q[2 + (dt >> 2)][dt & 3]);
+        const half4v al = av * lod;
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+          floatx4 t = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bh[qt],
+                                                             floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_16x16x16f16(al, bl[qt], t, 0, 0, 0);
+          acc[qt][dt] = __builtin_elementwise_fma(dn, t, acc[qt][dt]);
+        }
+      }
+      down *= RB_DOWN;
+    }
+  }
 }
 
 template <int NQT>
@@ -313,31 +425,23 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
     for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) pv[qt][r] *= bscale;
+    // does any lane hold a weight below FINE? (per token, with its least V
+    // scale: conservative where a scale is 0)
+    bool deep = false;
+    {
+      float vsmin[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      float vsb[4];
+      for (int r = 0; r < 4; ++r)
+        vsmin[r] = fminf(fminf(fabsf(half_at(R.vs, 4 * r)), fabsf(half_at(R.vs, 4 * r + 1))),
+                         fminf(fabsf(half_at(R.vs, 4 * r + 2)), fabsf(half_at(R.vs, 4 * r + 3))));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vsb[r] = half_at(R.vs, 4 * r + b);
-      half4v bh[NQT], bl[NQT];
+      for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) {
-        uint32_t h0, h1, l0, l1;
-        split2(pv[qt][0] * vsb[0], pv[qt][1] * vsb[1], h0, l0);
-        split2(pv[qt][2] * vsb[2], pv[qt][3] * vsb[3], h1, l1);
-        bh[qt] = __builtin_bit_cast(half4v, u32x2{h0, h1});
-        bl[qt] = __builtin_bit_cast(half4v, u32x2{l0, l1});
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int dt = 2 * b + e;
-        const half4v av = i8x4_to_h4(R.q[2 + (dt >> 2)][dt & 3]);
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-          acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bh[qt], acc[qt][dt], 0, 0, 0);
-          acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bl[qt], acc[qt][dt], 0, 0, 0);
-        }
-      }
+        for (int r = 0; r < 4; ++r) deep |= pv[qt][r] > 0.f && pv[qt][r] * vsmin[r] < FINE;
     }
+    // the parts for the weights below FINE run only on pages where a lane
+    // holds one (a uniform branch)
+    value_blocks<NQT>(R, pv, acc, __builtin_amdgcn_ballot_w64(deep) != 0);
   };
 
   // two page buffers in registers: the next page's loads are in flight while

@@ -33,11 +33,18 @@ What it computes, and where that comes from:
   identity silu(v) - silu(-v) = v and its limits, and numpy cross-checks.
 * ``q8_page`` / ``attn_decode``: decode attention of stacked rows over a
   paged q8_0 KV pool (each row attends to its agent's first row_len tokens;
-  softmax of q.k / sqrt(128), weighted sum of v), in float64; its bound S is
-  sum_i p_i max_d |v_i[d]| per (row, head). Pinned by
+  softmax of q.k / sqrt(128), weighted sum of v), in float64; its bound S is,
+  per output element, sum_i p_i |v_i[d]| plus a floor of 2^-80 times the
+  largest V scale the row attends to (the edge of fp32's range). Pinned by
   hand-built pages, a single token (O = v), equal keys (O = mean v), two
   tokens in closed form, shift invariance of the scores and a numpy
   cross-check.
+* ``factored_size`` / ``row_moments``: the size of the two terms of the
+  factored weight, sum_k (|d sc q| + |dmin m|) |x|, against which a product
+  that applies d and dmin separately keeps its error where the terms nearly
+  cancel (plus |mean * colsum| and the row scale for a matrix of the walk).
+  Pinned by a hand-worked block, by F == S where no weight's terms have
+  opposite signs, and by F >= S everywhere.
 * ``within_bound``: the acceptance rule ``|y - y_ref| <= tol * S``, and
   ``y == 0`` exactly where ``S == 0``.
 """
@@ -105,10 +112,16 @@ def _load():
         lib.oracle_num_threads.argtypes = []
         lib.oracle_standardize.restype = None
         lib.oracle_standardize.argtypes = [vp, i64, i64, ctypes.c_double, vp]
+        lib.oracle_row_moments.restype = None
+        lib.oracle_row_moments.argtypes = [vp, i64, i64, ctypes.c_double, vp, vp]
+        lib.oracle_factored_size.restype = ctypes.c_int
+        lib.oracle_factored_size.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
         lib.oracle_rms_inv.restype = None
         lib.oracle_rms_inv.argtypes = [vp, i64, i64, ctypes.c_double, vp]
         lib.oracle_gemm_rms.restype = ctypes.c_int
         lib.oracle_gemm_rms.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
+        lib.oracle_q8_vscale_max.restype = ctypes.c_double
+        lib.oracle_q8_vscale_max.argtypes = [vp, ctypes.c_int]
         lib.oracle_q8_page.restype = None
         lib.oracle_q8_page.argtypes = [vp, vp, vp]
         lib.oracle_q8_attn.restype = ctypes.c_int
@@ -305,8 +318,8 @@ def q8_page(ph) -> tuple[np.ndarray, np.ndarray]:
 
 def attn_decode(Q, pool, block_table, row_agent, row_len, n_kv: int):
     """Reference (O, S), float64 [M, n_heads, 128], of decode attention over the
-    paged q8_0 pool for binary16 queries Q [M, n_heads, 128]; S is the size of
-    the attended values, sum_i p_i max_d |v_i[d]|, repeated over the dims."""
+    paged q8_0 pool for binary16 queries Q [M, n_heads, 128]; S[d] is
+    sum_i p_i |v_i[d]| + 2^-80 * (largest V scale of the attended tokens)."""
     Q = np.asarray(Q)
     if Q.dtype != np.float16 or Q.ndim != 3 or Q.shape[2] != 128:
         raise TypeError("Q must be float16 [M, n_heads, 128]")
@@ -335,6 +348,46 @@ def standardize(v: np.ndarray, eps: float = 1e-6) -> np.ndarray:
     return out
 
 
+def row_moments(v: np.ndarray, eps: float = 1e-6) -> tuple[np.ndarray, np.ndarray]:
+    """(mean, 1 / sqrt(variance + eps)) of each row of v [M, N], float64 [M]
+    each; a float16 v is taken at its exact binary16 values."""
+    v = np.asarray(v)
+    if v.dtype == np.float16:
+        v = f16_to_f64(v)
+    v = _c(v, np.float64)
+    M, N = v.shape
+    mean = np.empty(M, dtype=np.float64)
+    inv = np.empty(M, dtype=np.float64)
+    _load().oracle_row_moments(v.ctypes.data, M, N, eps, mean.ctypes.data, inv.ctypes.data)
+    return mean, inv
+
+
+def factored_size(W: np.ndarray, X: np.ndarray, mean=None, r=None) -> np.ndarray:
+    """F [M, ncols] float64: the size of the two terms of the factored Q4_K
+    weight against binary16 X [M, K],
+    r_m * (sum_k (|d sc q| + |dmin m|) |x_mk| + |mean_m * sum_k w_nk|),
+    with mean = 0 and r = 1 by default (a plain product)."""
+    X = np.asarray(X)
+    if X.dtype != np.float16:
+        raise TypeError("X must be float16")
+    M, K = X.shape
+    if K % QK:
+        raise ValueError("K must be a multiple of 256")
+    W = _c(W, np.uint8).reshape(-1, K // QK * BLOCK_BYTES)
+    ncols = W.shape[0]
+    xb = _c(X.view(np.uint16), np.uint16)
+    mean = _c(np.zeros(M) if mean is None else mean, np.float64)
+    r = _c(np.ones(M) if r is None else r, np.float64)
+    if mean.shape != (M,) or r.shape != (M,):
+        raise ValueError("mean and r must have one value per row")
+    F = np.empty((M, ncols), dtype=np.float64)
+    rc = _load().oracle_factored_size(W.ctypes.data, xb.ctypes.data, M, ncols, K,
+                                      mean.ctypes.data, r.ctypes.data, F.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_factored_size failed ({rc})")
+    return F
+
+
 def within_bound(y: np.ndarray, y_ref: np.ndarray, S: np.ndarray, tol: float = TOL):
     """Acceptance rule: |y - y_ref| <= tol * S per element, and y exactly 0 where
     S is 0. Returns (ok, worst |err|/S over S>0, number of failing elements)."""
@@ -346,13 +399,6 @@ def within_bound(y: np.ndarray, y_ref: np.ndarray, S: np.ndarray, tol: float = T
         rel = np.where(zero, 0.0, err / np.where(zero, 1.0, S))
     worst = float(np.max(rel)) if rel.size else 0.0
     return (not bool(bad.any())), worst, int(bad.sum())
-
-
-def f16_spacing(t) -> np.ndarray:
-    """Distance between adjacent binary16 values around |t| (numpy's spacing of
-    the binary16 value nearest to t); the tolerance of the transform check."""
-    t = np.asarray(t, dtype=np.float64)
-    return np.spacing(np.abs(t).astype(np.float16)).astype(np.float64)
 
 
 def num_threads() -> int:

@@ -231,11 +231,10 @@ int oracle_gemm_std(const uint8_t* W, const uint16_t* X, int64_t M, int64_t ncol
   return err;
 }
 
-/* The row-wise standardization every matrix of the layer walk applies to its
- * input:
- *   t[m][n] = (v[m][n] - mean_m) / sqrt(var_m + eps)
- * with mean and (population) variance over the row's N values, in double. */
-void oracle_standardize(const double* v, int64_t M, int64_t N, double eps, double* t) {
+/* Mean and 1 / sqrt(var + eps) of each row of v [M][N], the (population)
+ * variance taken about the mean, in double. */
+void oracle_row_moments(const double* v, int64_t M, int64_t N, double eps, double* mean_out,
+                        double* inv_out) {
   for (int64_t m = 0; m < M; ++m) {
     const double* r = v + m * N;
     double mean = 0.0;
@@ -244,9 +243,74 @@ void oracle_standardize(const double* v, int64_t M, int64_t N, double eps, doubl
     double var = 0.0;
     for (int64_t n = 0; n < N; ++n) var += (r[n] - mean) * (r[n] - mean);
     var /= (double)N;
-    double inv = 1.0 / sqrt(var + eps);
-    for (int64_t n = 0; n < N; ++n) t[m * N + n] = (r[n] - mean) * inv;
+    mean_out[m] = mean;
+    inv_out[m] = 1.0 / sqrt(var + eps);
   }
+}
+
+/* The row-wise standardization every matrix of the layer walk applies to its
+ * input:
+ *   t[m][n] = (v[m][n] - mean_m) / sqrt(var_m + eps)
+ * with mean and (population) variance over the row's N values, in double. */
+void oracle_standardize(const double* v, int64_t M, int64_t N, double eps, double* t) {
+  for (int64_t m = 0; m < M; ++m) {
+    double mean, inv;
+    oracle_row_moments(v + m * N, 1, N, eps, &mean, &inv);
+    for (int64_t n = 0; n < N; ++n) t[m * N + n] = (v[m * N + n] - mean) * inv;
+  }
+}
+
+/* The size of the two terms of the factored weight, against which a product
+ * that multiplies d * sc[j] * q and dmin * m[j] separately (and subtracts)
+ * keeps its error:
+ *   F[m][n] = r[m] * ( sum_k (|d sc[j] q[k]| + |dmin m[j]|) * |x[m][k]|
+ *                      + |mean[m] * sum_k w[n][k]| )
+ * for binary16 X [M][K]; mean and r are per row (mean 0 and r 1 for a plain
+ * product, the input's mean and 1 / sqrt(var + eps) for a matrix of the walk,
+ * whose products are taken with x and standardized after). F >= sum_k
+ * |w x| * r whenever the mean is 0 (|w| <= |d sc q| + |dmin m|), with
+ * equality when no weight's two terms have opposite signs. */
+int oracle_factored_size(const uint8_t* W, const uint16_t* X, int64_t M, int64_t ncols, int64_t K,
+                         const double* mean, const double* r, double* F) {
+  if (K % ORACLE_QK) return -1;
+  const int64_t row_bytes = K / ORACLE_QK * ORACLE_BLOCK_BYTES;
+  int err = 0;
+#pragma omp parallel
+  {
+    double* a = (double*)malloc(sizeof(double) * (size_t)K); /* |d sc q| + |dmin m| */
+    double* xa = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    if (!a || !xa) {
+#pragma omp atomic write
+      err = -2;
+    } else {
+      for (int64_t i = 0; i < M * K; ++i) xa[i] = fabs(oracle_f16_to_f64(X[i]));
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t n = 0; n < ncols; ++n) {
+      if (!a || !xa) continue;
+      const uint8_t* row = W + n * row_bytes;
+      double wsum = 0.0;
+      int sc[8], mn[8], q[256];
+      double d, dmin;
+      for (int64_t kb = 0; kb < K / ORACLE_QK; ++kb) {
+        oracle_decode_block(row + kb * ORACLE_BLOCK_BYTES, &d, &dmin, sc, mn, q);
+        for (int t = 0; t < ORACLE_QK; ++t) {
+          const int j = t / 32;
+          const double main = d * (double)sc[j] * (double)q[t], off = dmin * (double)mn[j];
+          a[kb * ORACLE_QK + t] = fabs(main) + fabs(off);
+          wsum += main - off;
+        }
+      }
+      for (int64_t m = 0; m < M; ++m) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) acc += a[k] * xa[m * K + k];
+        F[m * ncols + n] = r[m] * (acc + fabs(mean[m] * wsum));
+      }
+    }
+    free(a);
+    free(xa);
+  }
+  return err;
 }
 
 /* The residual layer walk: the RMSNorm scale of each row of the fp32
@@ -357,16 +421,37 @@ void oracle_q8_page(const uint8_t* ph, double* k, double* v) {
     }
 }
 
+/* The largest |V scale| of token t (0..15) of a page-head, over its four
+ * 32-dim blocks (scales at the offsets oracle_q8_page reads them from). */
+double oracle_q8_vscale_max(const uint8_t* ph, int t) {
+  double mx = 0.0;
+  for (int b = 0; b < 4; ++b) {
+    const int vs_at = 4096 + 64 * (t / 4) + 2 * (4 * (t % 4) + b) + 32;
+    const double v = fabs(oracle_f16_to_f64((uint16_t)(ph[vs_at] | (ph[vs_at + 1] << 8))));
+    if (v > mx) mx = v;
+  }
+  return mx;
+}
+
+/* The floor of the attention error bound, in units of the largest V scale a
+ * row attends to: 2^-80. A term p_i v_i[d] is held to fp32-like precision
+ * only while its unnormalised weight times its V scale stays above about
+ * fp32's smallest normal number, 2^-126, relative to twice that largest
+ * scale; a term below that is at most 127 * 2^-125 = 2^-118 of it, and up to
+ * 2^18 of them add at most 2^-100, less than the 2^-93.3 that 1e-4 times
+ * 2^-80 allows. */
+#define ORACLE_ATTN_FLOOR 0x1p-80
+
 /* Reference decode attention. Row r of Q [M][n_heads][128] (binary16) belongs
  * to agent row_agent[r] and attends to that agent's first row_len[r] tokens,
  * token i living in page block_table[agent][i / 16], slot i % 16. Head h reads
  * KV head h / (n_heads / n_kv). In double precision:
  *   s_i = (q . k_i) / sqrt(128),  p = softmax(s),  O = sum_i p_i v_i,
- * and, for the error bound, S = sum_i p_i max_d |v_i[d]|: the size of the
- * values the row attends to, the same for every output dim of the head (a
- * per-element sum of p_i |v_i[d]| could be made of weights far below any
- * finite precision wherever the dominant token's value is 0). A row with no
- * token to attend to (row_len <= 0) gets O = 0 and S = 0: the empty sum. */
+ * and, for the error bound, per output element
+ *   S[d] = sum_i p_i |v_i[d]| + 2^-80 * max_i |V scale of token i|,
+ * the sum of the sizes of the terms O[d] adds, plus a floor at the edge of
+ * fp32's range (ORACLE_ATTN_FLOOR). A row with no token to attend to
+ * (row_len <= 0) gets O = 0 and S = 0: the empty sum. */
 int oracle_q8_attn(const uint16_t* Q, const uint8_t* pool, const int32_t* block_table,
                    const int32_t* row_agent, const int32_t* row_len, int64_t M,
                    int64_t max_pages, int64_t n_heads, int64_t n_kv, double* O, double* S) {
@@ -418,22 +503,22 @@ int oracle_q8_attn(const uint16_t* Q, const uint8_t* pool, const int32_t* block_
         s[i] = exp(s[i] - mx);
         z += s[i];
       }
-      double size = 0.0;
-      for (int d = 0; d < ORACLE_HEAD_DIM; ++d) o[d] = 0.0;
+      double vscale = 0.0;
+      for (int d = 0; d < ORACLE_HEAD_DIM; ++d) o[d] = sa[d] = 0.0;
       for (int64_t i = 0; i < n; ++i) {
         const int64_t page = block_table[a * max_pages + i / ORACLE_PAGE_TOKENS];
-        if (i % ORACLE_PAGE_TOKENS == 0)
-          oracle_q8_page(pool + (size_t)(page * n_kv + kvh) * ORACLE_PAGE_HEAD_BYTES, k, v);
+        const uint8_t* ph = pool + (size_t)(page * n_kv + kvh) * ORACLE_PAGE_HEAD_BYTES;
+        if (i % ORACLE_PAGE_TOKENS == 0) oracle_q8_page(ph, k, v);
         const double p = s[i] / z;
         const double* vi = v + (i % ORACLE_PAGE_TOKENS) * ORACLE_HEAD_DIM;
-        double vmax = 0.0;
         for (int d = 0; d < ORACLE_HEAD_DIM; ++d) {
           o[d] += p * vi[d];
-          if (fabs(vi[d]) > vmax) vmax = fabs(vi[d]);
+          sa[d] += p * fabs(vi[d]);
         }
-        size += p * vmax;
+        const double vs = oracle_q8_vscale_max(ph, (int)(i % ORACLE_PAGE_TOKENS));
+        if (vs > vscale) vscale = vs;
       }
-      for (int d = 0; d < ORACLE_HEAD_DIM; ++d) sa[d] = size;
+      for (int d = 0; d < ORACLE_HEAD_DIM; ++d) sa[d] += ORACLE_ATTN_FLOOR * vscale;
       free(s);
       free(k);
       free(v);

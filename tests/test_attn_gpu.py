@@ -1,8 +1,8 @@
 """GPU parity of decode attention over the paged q8_0 KV pool
 (mk_q8_attn_decode) against the fp64 oracle: |O - O_ref| <= 1e-4 * S per
-output element, S = sum_i p_i max_d |v_i[d]| (the size of the values the row
-attends to), plus determinism and the property that a
-row's result does not depend on the other rows in the call."""
+output element, S[d] = sum_i p_i |v_i[d]| + 2^-80 * (largest V scale the row
+attends to: a floor at the edge of fp32's range), plus determinism and the
+property that a row's result does not depend on the other rows in the call."""
 import numpy as np
 import pytest
 
@@ -98,7 +98,42 @@ def test_large_scales_and_peaked_scores():
     pool[:, :, kat] = scaled(kat, 40.0)
     pool[:, :, vat] = scaled(vat, 64.0)
     assert np.all(np.isfinite(np.ascontiguousarray(pool[:, :, vat]).view(np.float16)))
-    check(pool, table, row_len, Q, 3, 2)
+    _, worst = check(pool, table, row_len, Q, 3, 2)
+    print(f"large scales, peaked scores: worst per-element |err|/S = {worst:.3e}")
+
+
+def _kscale_at(t, b):
+    return 4096 + 64 * (t // 4) + 2 * (4 * (t % 4) + b)
+
+
+def test_dominant_tokens_with_zero_values():
+    """Three dominant tokens per agent whose scores stand about 11, 23 and 46
+    nats above the rest, with value quants of 0 in the first 32 or 64 dims:
+    those output dims are made of weights between about 2^-16 and 2^-70 of
+    the largest one, which the value product must carry (rebased parts) to
+    meet the per-element bound."""
+    lengths, rows, H, KV = [300, 200], 3, 4, 2
+    n_pages = 40
+    pool, table, row_len, Q = setup(65, lengths, rows, H, KV, n_pages)
+    Q = np.abs(Q.astype(np.float32)).astype(np.float16)      # every query dim >= 0
+    for a in range(len(lengths)):
+        for t, ksc, zero_dims in ((5, 0.01, 32), (6, 0.02, 32), (7, 0.04, 64)):
+            page, slot = table[a, t // 16], t % 16
+            for h in range(KV):
+                ph = pool[page, h]
+                # K: quant +127 in every dim, one scale for the four blocks
+                for d in range(128):
+                    ph[1024 * ((d // 32) // 2) + 16 * (16 * ((d % 32) // 8) + slot)
+                       + 8 * ((d // 32) % 2) + d % 8] = 127
+                for b in range(4):
+                    ph[_kscale_at(slot, b):_kscale_at(slot, b) + 2] = \
+                        np.array([ksc], dtype=np.float16).view(np.uint8)
+                # V: quant 0 in the first zero_dims dims
+                for d in range(zero_dims):
+                    ph[1024 * (2 + d // 64) + 16 * (16 * (slot // 4) + d % 16)
+                       + 4 * ((d // 16) % 4) + slot % 4] = 0
+    _, worst = check(pool, table, row_len, Q, rows, KV)
+    print(f"dominant tokens with zero values: worst per-element |err|/S = {worst:.3e}")
 
 
 def test_empty_cache_rows_are_zero():

@@ -161,6 +161,68 @@ def test_large_activation_values():
     check(W, X)
 
 
+# --- the min term's sub-block sums and nearly cancelling weights ------------------
+def _big_sum_rows(M, K, seed):
+    """N(0,1) rows with whole 32-value sub-blocks of large values: 2100 (sum
+    67200, past binary16's 65504), -2100, 65504 (the largest finite value, sum
+    2096128) and -30000, at different sub-blocks per row."""
+    X = synth.activations(seed, M, K).astype(np.float32)
+    for m in range(M):
+        for i, v in enumerate((2100.0, -2100.0, 65504.0, -30000.0)):
+            j = (3 * m + 5 * i) % (K // 32)
+            X[m, 32 * j:32 * j + 32] = v
+    return X.astype(np.float16)
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+def test_subblock_sums_beyond_binary16(tiled):
+    """The min term multiplies each 32-value sub-block sum of X; sums past
+    binary16's range must stay finite and exact enough (three binary16 parts)."""
+    M, N, K = 12, 100, 2048
+    W, _ = inputs(N, K, M, tag=17)
+    X = _big_sum_rows(M, K, 17)
+    if tiled:
+        Y = tiled_pair(W, X, N)[1]
+    else:
+        Y = run_gpu(W, X)
+    assert np.all(np.isfinite(Y))
+    _, worst = check(W, X, Y=Y)
+    print(f"large sub-block sums (tiled={tiled}) worst |err|/S = {worst:.3e}")
+
+
+def _cancel_blocks(dmin_bits, n_rows, kb):
+    """d = 1, every scale and min 63, every quant 15: the weight's two terms
+    are 945 and 63 * dmin; dmin = 15 (0x4B80) makes every weight exactly 0,
+    one binary16 step more (0x4B81) makes it -63/128."""
+    return _blocks(0x3C00, dmin_bits, 0xFF, 0xFF, n_rows, kb)
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+def test_cancelling_and_near_cancelling_blocks(tiled):
+    """Columns 0-15 hold weights that are exactly 0 (the two terms of the
+    factored form cancel), 16-31 generated weights, 32-47 weights of -63/128
+    made of two terms of about 945. The factored product keeps its error
+    within 1e-4 of the size of the two terms (F); generated columns also meet
+    1e-4 * sum|w x|."""
+    M, K = 12, 1024
+    gen, _ = inputs(16, K, M, tag=18)
+    W = np.concatenate([_cancel_blocks(0x4B80, 16, K // 256), gen,
+                        _cancel_blocks(0x4B81, 16, K // 256)])
+    X = synth.activations(18, M, K)
+    Y = tiled_pair(W, X, 48)[1] if tiled else run_gpu(W, X)
+    y_ref, S = oracle.gemm(W, X)
+    F = oracle.factored_size(W, X)
+    assert np.all(y_ref[:, :16] == 0) and np.all(S[:, :16] == 0)
+    ok, worst_f, nbad = oracle.within_bound(Y, y_ref, F)
+    assert ok, f"{nbad} outside 1e-4 * F, worst |err|/F = {worst_f:.3e}"
+    ok, worst, nbad = oracle.within_bound(Y[:, 16:32], y_ref[:, 16:32], S[:, 16:32])
+    assert ok, f"generated columns: {nbad} outside the bound, worst {worst:.3e}"
+    with np.errstate(divide="ignore", invalid="ignore"):
+        near = np.max(np.abs(Y[:, 32:] - y_ref[:, 32:]) / S[:, 32:])
+    print(f"cancelling (tiled={tiled}): worst |err|/F {worst_f:.3e}, |y| on w=0 "
+          f"{np.abs(Y[:, :16]).max():.3e}, near-cancelling |err|/S {near:.3e}")
+
+
 # --- properties -----------------------------------------------------------------
 def test_deterministic_run_to_run():
     W, X = inputs(1000, 5120, 12, tag=12)

@@ -305,6 +305,68 @@ def test_standardize_moments_and_small_case():
     assert np.allclose(t.var(axis=1), var / (var + 1e-6), rtol=1e-12)
 
 
+def test_row_moments_closed_form_and_standardize():
+    v = np.array([[1.0, 2.0, 3.0, 4.0], [10.0, 10.0, 10.0, 10.0], [-2.0, 2.0, -2.0, 2.0]])
+    mean, inv = oracle.row_moments(v, eps=1e-6)
+    # population variance: 1.25, 0 and 4
+    assert list(mean) == [2.5, 10.0, 0.0]
+    assert np.allclose(inv, 1.0 / np.sqrt(np.array([1.25, 0.0, 4.0]) + 1e-6), rtol=1e-15, atol=0)
+    t = oracle.standardize(v, eps=1e-6)
+    assert np.array_equal(t, (v - mean[:, None]) * inv[:, None])
+    # binary16 input is taken at its exact values
+    x = np.array([[0.5, -1.5, 3.0, 65504.0]], dtype=np.float16)
+    m16, _ = oracle.row_moments(x)
+    assert m16[0] == (0.5 - 1.5 + 3.0 + 65504.0) / 4
+
+
+def test_factored_size_hand_worked_block():
+    """d = 0.5, dmin = 0.25, every scale 3, min 5 and quant 6: each weight's
+    two terms are d*sc*q = 9 and dmin*m = 1.25 (w = 7.75). Against a row of
+    alternating 1, -2 (sum |x| = 384): F = 10.25 * 384 = 3936 and S = 7.75 *
+    384 = 2976; with a row mean of 0.5 and scale r = 2,
+    F = 2 * (3936 + |0.5 * 7.75 * 256|) = 9856."""
+    blk = make_block(0x3800, 0x3400, pack_scales_from_spec([3] * 8, [5] * 8), [0x66] * 128)
+    W = np.frombuffer(blk, dtype=np.uint8).reshape(1, 144)
+    X = np.tile(np.array([1.0, -2.0], dtype=np.float16), 128).reshape(1, 256)
+    F = oracle.factored_size(W, X)
+    _, S = oracle.gemm(W, X)
+    assert F[0, 0] == 3936.0 and S[0, 0] == 2976.0
+    F2 = oracle.factored_size(W, X, mean=np.array([0.5]), r=np.array([2.0]))
+    assert F2[0, 0] == 9856.0
+
+
+def test_factored_size_cancelling_block():
+    """d = 1, sc = 63, q = 15, dmin = 15, m = 63: the two terms are both 945,
+    so every weight is 0 (S = 0) while F = 1890 * sum |x|."""
+    blk = make_block(0x3C00, 0x4B80, pack_scales_from_spec([63] * 8, [63] * 8), [0xFF] * 128)
+    W = np.frombuffer(blk * 2, dtype=np.uint8).reshape(1, 288)
+    X = synth.activations(21, 3, 512)
+    y, S = oracle.gemm(W, X)
+    assert np.all(y == 0) and np.all(S == 0)
+    F = oracle.factored_size(W, X)
+    assert np.array_equal(F[:, 0], 1890.0 * np.abs(X.astype(np.float64)).sum(axis=1))
+
+
+def test_factored_size_equals_s_without_opposite_terms_and_bounds_it():
+    """Where one of a weight's two terms is 0 (dmin = 0, or q = 0) |w| is the
+    sum of the terms' sizes, so F and S are the same sums of the same
+    products; on generated weights F >= S (|w| <= |d sc q| + |dmin m|)."""
+    N, K, M = 23, 768, 4
+    W = synth.q4k_matrix(synth.key(22, 1), N, K)
+    X = synth.activations(22, M, K)
+    Wb = W.copy().reshape(-1, 144)
+    Wb[:, 2:4] = 0                      # dmin = 0
+    W0 = Wb.reshape(N, -1)
+    assert np.array_equal(oracle.factored_size(W0, X), oracle.gemm(W0, X)[1])
+    Wq = W.copy().reshape(-1, 144)
+    Wq[:, 16:] = 0                      # q = 0: w = -dmin m
+    Wq = Wq.reshape(N, -1)
+    assert np.array_equal(oracle.factored_size(Wq, X), oracle.gemm(Wq, X)[1])
+    F = oracle.factored_size(W, X)
+    S = oracle.gemm(W, X)[1]
+    assert np.all(F >= S) and np.any(F > S)
+
+
 def test_gemm_std_shift_and_scale_invariance():
     """Standardizing the input makes the product independent of a per-row
     offset and of a per-row positive scale (exactly, up to the eps term). The
@@ -531,6 +593,47 @@ def test_q8_page_decodes_by_hand():
     assert np.array_equal(k, want_k) and np.array_equal(v, want_v)
 
 
+def _page_vscales(ph):
+    """[16][4] V scales of a page-head, read from the bytes the layout puts
+    them at: 64-byte groups per four tokens at 4096, K scales [token][block]
+    then V scales."""
+    ph = np.asarray(ph, dtype=np.uint8)
+    out = np.empty((16, 4))
+    for t in range(16):
+        for b in range(4):
+            at = 4096 + 64 * (t // 4) + 2 * (4 * (t % 4) + b) + 32
+            out[t, b] = ph[at:at + 2].copy().view(np.float16)[0]
+    return out
+
+
+def test_attn_bound_per_element_with_floor():
+    """Two tokens: token 0 takes nearly all the weight but its value is 0 in
+    dim 1; token 1 has weight p1 = 1 / (1 + e^delta) and value 8 there. The
+    bound of dim 1 is p1 * 8 (the only term) plus the floor 2^-80 * the
+    largest V scale (0.5): a per-element sum, not the size of the row."""
+    kq = np.zeros((16, 128), dtype=np.int64)
+    kq[0, 0] = 100
+    ks = np.zeros((16, 4))
+    ks[0, 0] = 0.5
+    vq = np.zeros((16, 128), dtype=np.int64)
+    vq[0, 0], vq[1, 1] = 100, 16
+    vs = np.zeros((16, 4))
+    vs[0, 0] = 0.5
+    vs[1, 0] = 0.5
+    pool = _one_page_pool(kq, ks, vq, vs)
+    Q = np.zeros((1, 1, 128), dtype=np.float16)
+    Q[0, 0, 0] = 4.0
+    O, S = oracle.attn_decode(Q, pool, np.zeros((1, 1), np.int32), np.zeros(1, np.int32),
+                              np.array([2], np.int32), 1)
+    delta = 4.0 * 100 * 0.5 / np.sqrt(128.0)
+    p1 = 1.0 / (1.0 + np.exp(delta))
+    assert np.isclose(O[0, 0, 1], p1 * 8.0, rtol=1e-12, atol=0)
+    assert np.isclose(S[0, 0, 1], p1 * 8.0 + 2.0 ** -80 * 0.5, rtol=1e-12, atol=0)
+    assert np.isclose(S[0, 0, 0], (1 - p1) * 50.0 + 2.0 ** -80 * 0.5, rtol=1e-12, atol=0)
+    assert S[0, 0, 2] == 2.0 ** -80 * 0.5        # no term: the floor alone
+    assert O[0, 0, 2] == 0.0
+
+
 def _one_page_pool(kq, ks, vq, vs):
     return _page(kq, ks, vq, vs).reshape(1, 1, 4352)
 
@@ -551,7 +654,9 @@ def test_attn_single_token_and_equal_keys():
     v = vq * 0.125
     for r, n in enumerate(lens):
         assert np.allclose(O[r, 0], v[:n].mean(axis=0), rtol=1e-14, atol=1e-14)
-        assert np.allclose(S[r, 0], np.abs(v[:n]).max(axis=1).mean(), rtol=1e-14, atol=1e-14)
+        # S: the mean of |v| per dim (equal weights), plus 2^-80 * the V scale
+        assert np.allclose(S[r, 0], np.abs(v[:n]).mean(axis=0) + 2.0 ** -80 * 0.125,
+                           rtol=1e-14, atol=0)
     assert np.array_equal(O[0, 0], v[0])
 
 
@@ -597,7 +702,10 @@ def test_attn_matches_numpy_with_paging_and_gqa():
             p = np.exp(s - s.max())
             p /= p.sum()
             assert np.allclose(O[r, h], p @ V, rtol=1e-12, atol=1e-14), (r, h)
-            assert np.allclose(S[r, h], p @ np.abs(V).max(axis=1), rtol=1e-12, atol=1e-14), (r, h)
+            vsmax = max(np.abs(_page_vscales(pool[table[a, i // 16], kvh])[i % 16]).max()
+                        for i in range(rl[r]))
+            assert np.allclose(S[r, h], p @ np.abs(V) + 2.0 ** -80 * vsmax, rtol=1e-12,
+                               atol=0), (r, h)
 
 
 # --- Q6_K (GGUF k-quant type 14) -----------------------------------------------
