@@ -105,6 +105,9 @@ def lib():
         L.mk_q4k_gemm.argtypes = [vp, vp, vp, i, i, i, vp]
         L.mk_q4k_gemm_workspace_bytes.restype = sz
         L.mk_q4k_gemm_workspace_bytes.argtypes = [i, i, i]
+        if hasattr(L, "mk_q4k_gemm_noalloc"):
+            L.mk_q4k_gemm_noalloc.restype = i
+            L.mk_q4k_gemm_noalloc.argtypes = [vp, vp, vp, i, i, i, vp]
         L.mk_q4k_gemm_ws.restype = i
         L.mk_q4k_gemm_ws.argtypes = [vp, vp, vp, i, i, i, vp, sz, vp]
         L.mk_q4k_tiles_bytes.restype = sz
@@ -191,6 +194,27 @@ def gemm(W, X, out=None, stream=None, workspace=None):
         rc = lib().mk_q4k_gemm_ws(_ptr(W), _ptr(X), _ptr(out), M, N, K, _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc)
+    return out
+
+
+def gemm_noalloc(W, X, out=None, stream=None):
+    """Y = X * W^T like gemm(), through mk_q4k_gemm_noalloc: the K-split
+    partials go to the library's static per-GPU scratch array (calls that
+    overlap on one GPU race); shapes that need more than it holds raise
+    MkError(MK_EWORKSPACE)."""
+    import torch
+    if X.dim() != 2 or X.dtype != torch.float16 or not X.is_contiguous():
+        raise MkError(MK_EINVAL, "X must be a contiguous 2-D float16 tensor")
+    M, K = X.shape
+    if K % QK or W.dtype != torch.uint8 or W.numel() % (K // QK * BLOCK_BYTES) \
+            or not W.is_contiguous():
+        raise MkError(MK_EINVAL, "W must be contiguous uint8 Q4_K rows of K/256*144 bytes")
+    N = W.numel() // (K // QK * BLOCK_BYTES)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    elif out.shape != (M, N) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise MkError(MK_EINVAL, "out must be a contiguous float32 [M, N] tensor")
+    _check(lib().mk_q4k_gemm_noalloc(_ptr(W), _ptr(X), _ptr(out), M, N, K, _stream(stream)))
     return out
 
 

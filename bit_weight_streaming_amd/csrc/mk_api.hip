@@ -136,9 +136,60 @@ int run_gemm(bool tiled, const void* W, const uint16_t* X, float* Y, int M, int 
   return e == hipSuccess ? MK_OK : MK_EHIP;
 }
 
+// ---- the GEMM entry point that allocates nothing (mk_q4k_gemm_noalloc)
+//
+// Its K-split partial sums live in a file-scope device array, `scratch`,
+// which every GPU the library runs on holds (one copy per device, at its own
+// address) until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: the device address of each GPU's copy is
+// looked up once per device with hipGetSymbolAddress (with that device
+// current) and only that address is ever handed to kernels.
+static __device__ __align__(256) char scratch[MK_Q4K_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchAddr {
+  int looked_up = 0;
+  void* ptr = nullptr;
+};
+ScratchAddr g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's copy of `scratch`.
+int scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  ScratchAddr& a = g_scratch[dev];
+  if (!a.looked_up) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MK_EHIP;
+    a.ptr = p;
+    a.looked_up = 1;
+  }
+  *out = a.ptr;
+  return MK_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int mk_q4k_gemm_noalloc(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N,
+                        int K, void* stream) {
+  int rc = check_gemm_args(W_blocks, X_fp16, Y_fp32, M, N, K, false);
+  if (rc != MK_OK) return rc;
+  int dev = -1;
+  rc = current_device(&dev);
+  if (rc != MK_OK) return rc;
+  const mk::GemmPlan p = mk::gemm_plan(M, N, K, g_dev[dev].cus);
+  if (!p.ok) return MK_EINVAL;
+  if (p.ws_bytes > (size_t)MK_Q4K_NOALLOC_SCRATCH_BYTES) return MK_EWORKSPACE;
+  void* ws = nullptr;
+  if (p.ws_bytes > 0) {
+    rc = scratch_address(dev, &ws);
+    if (rc != MK_OK) return rc;
+  }
+  hipError_t e =
+      mk::gemm_launch(p, false, W_blocks, X_fp16, Y_fp32, M, N, K, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MK_OK : MK_EHIP;
+}
 
 const char* mk_strerror(int code) {
   switch (code) {

@@ -108,6 +108,25 @@ int mk_q4k_gemm_ws(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, 
                    int K, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * mk_q4k_gemm_noalloc: mk_q4k_gemm for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, kernels and results (bit for bit) as
+ * mk_q4k_gemm; it calls no hipMalloc, hipFree or other allocating routine.
+ * The K-split partial sums go to a device array of
+ * MK_Q4K_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends (enough for every shape of the 27B-class layer
+ * up to 64 rows). A shape whose partials need more returns MK_EWORKSPACE
+ * before anything is enqueued (use mk_q4k_gemm_ws for it). The first call on
+ * a device looks up that device's copy of the array (hipGetSymbolAddress).
+ * All calls on one GPU share the array: calls that overlap in time on one
+ * GPU (different streams, not ordered) race and give wrong results. Its
+ * contents need no initialisation; each call overwrites what it reads.
+ */
+#define MK_Q4K_NOALLOC_SCRATCH_BYTES (24 << 20)
+int mk_q4k_gemm_noalloc(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N,
+                        int K, void* stream);
+
+/*
  * Tile records: a load-time reordering of a Q4_K matrix for the streaming
  * kernels. Every block keeps its 144 bytes; rows are grouped in tiles of 16
  * (rows past N are zero blocks) and for tile t and super-block kb the

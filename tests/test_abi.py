@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
               "mk_q4k_repack", "mk_q4k_tiles_bytes", "mk_q4k_gemm_tiled",
               "mk_q4k_step_workspace_bytes", "mk_q4k_step_status", "mk_strerror",
               "mk_device_info", "mk_q4k_step_res", "mk_q8_attn_decode",
-              "mk_q8_attn_workspace_bytes"):
+              "mk_q8_attn_workspace_bytes", "mk_q4k_gemm_noalloc"):
         assert f in names
 
 
