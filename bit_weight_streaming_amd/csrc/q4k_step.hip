@@ -1331,11 +1331,112 @@ void fill_table(const mk_q4k_layer& L, float* const* y, uint16_t* const* x, DevL
 }
 
 
+// Host walk of everything the kernel indexes for one plan, with the kernel's
+// own work-split functions (assign_split, wave_begin, wave_of_unit) and the
+// record order of its iterator: every weight record, column sum, slice
+// partial, LDS slot, staged element, output element and statistics slot each
+// workgroup and wave touches must lie inside its buffer. Returns the number
+// of accesses that do not.
+long long plan_violations(const mk_q4k_layer& L0, int n_layers, int M, int G) {
+  StepPlan sp;
+  plan_phases(L0, n_layers, M, G, sp);
+  const size_t lds = lds_bytes(sp, M);
+  // plans the launch refuses (MK_EINVAL) are not walked
+  if (!sp.ok || lds + kStaticLds > kLdsLimit) return -1;
+  const mk_q4k_mat* mats[7] = {&L0.q, &L0.k, &L0.v, &L0.o, &L0.gate, &L0.up, &L0.down};
+  long long bad = 0;
+  auto check = [&](bool ok) { bad += ok ? 0 : 1; };
+  for (int p = 0; p < 4; ++p) {
+    const DevPhase& ph = sp.ph[p];
+    check(ph.sk <= G);
+    check((size_t)ph.part_bytes == (size_t)ph.nt * ph.sk * ph.nm * 1024);
+    // the next phase's input width (the finishers' binary16 stores)
+    const int Kn = ph.seg_n[0];
+    for (int w = 0; w < G; ++w) {
+      const Assign a = assign_split(ph.nt, ph.sk, ph.nkb, ph.KB, w, G);
+      check(a.s >= 0 && a.s < ph.sk && a.t0 >= 0 && a.t0 + a.tw <= ph.nt && a.tw <= ph.tw_max);
+      check(a.kb0 >= 0 && a.kb0 + a.nkb <= ph.KB && a.nkb >= 1);
+      // staging: rows m < M, columns of the slice, LDS rows of x_stride bytes
+      check((size_t)(a.kb0 + a.nkb) * QK <= (size_t)ph.K);
+      check((size_t)M * ph.x_stride + (size_t)M * ph.nkb * XSUM_BYTES_PER_BLOCK <=
+            (size_t)ph.lds_contrib);
+      check((size_t)(a.nkb - 1) * X_BYTES_PER_BLOCK + 3 * 128 + 7 * 16 + 16 <=
+            (size_t)ph.x_stride);
+      for (int v = 0; v < SPLIT_WAVES; ++v) {
+        const int ua = wave_begin(a, v), ub = wave_begin(a, v + 1);
+        check(ua >= 0 && ua <= ub && ub <= a.U);
+        // every record the wave loads (the iterator never moves past ub - 1)
+        for (int u = ua; u < ub; ++u) {
+          const int tl = u / a.nkb, b = u % a.nkb, tg = a.t0 + tl;
+          const int seg = (tg >= ph.seg_t0[1]) + (tg >= ph.seg_t0[2]);
+          check(seg < ph.nseg && tg >= ph.seg_t0[seg] && tg < ph.seg_t0[seg + 1]);
+          for (int q = 0; q < ph.nm; ++q) {
+            const mk_q4k_mat& m = *mats[ph.mat0 + seg + q];
+            const size_t rec = ((size_t)(tg - ph.seg_t0[seg]) * ph.KB + a.kb0 + b) * TILE_REC;
+            check(rec + TILE_REC <= (size_t)tiles_of(m.N) * (m.K / QK) * TILE_REC);
+          }
+          // the LDS contribution slot of the tile's part
+          const int first = wave_of_unit(a, tl * a.nkb);
+          check(v >= first && v - first < ph.cmax);
+          const size_t slot = ((size_t)(tl * ph.cmax + (v - first)) * ph.nm + ph.nm - 1) * 1024 + 63 * 16;
+          check(slot + 16 <= (size_t)ph.tw_max * ph.cmax * ph.nm * 1024 &&
+                ph.lds_contrib + slot + 16 <= lds);
+        }
+      }
+      // published slice partials of the workgroup's tiles
+      for (int tl = 0; tl < a.tw; ++tl)
+        check(((size_t)((a.t0 + tl) * ph.sk + a.s) * ph.nm + ph.nm) * 1024 <= ph.part_bytes);
+      // the tiles it finishes: tile t belongs to the workgroup of slice t % sk
+      const int ff = ((a.s - a.t0) % ph.sk + ph.sk) % ph.sk;
+      const int nfin = ff < a.tw ? (a.tw - 1 - ff) / ph.sk + 1 : 0;
+      for (int i = 0; i < nfin; ++i) {
+        const int tg = a.t0 + ff + i * ph.sk;
+        check(tg < a.t0 + a.tw && tg % ph.sk == a.s);
+        check(((size_t)(tg * ph.sk + ph.sk - 1) * ph.nm + ph.nm) * 1024 <= ph.part_bytes);
+        const int seg = (tg >= ph.seg_t0[1]) + (tg >= ph.seg_t0[2]);
+        const int cs_max = (tg - ph.seg_t0[seg]) * 16 + 15;
+        // column sums after the records; outputs and next inputs only below N
+        check(cs_max < tiles_of(ph.seg_n[seg]) * 16);
+        check(ph.cs_off[seg] ==
+              (unsigned)((size_t)tiles_of(ph.seg_n[seg]) * ph.KB * TILE_REC));
+        check(seg > 0 || ph.seg_n[0] <= Kn);
+      }
+    }
+    // every tile has exactly one finisher
+    std::vector<int> fin(ph.nt, 0);
+    for (int w = 0; w < G; ++w) {
+      const Assign a = assign_split(ph.nt, ph.sk, ph.nkb, ph.KB, w, G);
+      const int ff = ((a.s - a.t0) % ph.sk + ph.sk) % ph.sk;
+      for (int tg = a.t0 + ff; tg < a.t0 + a.tw; tg += ph.sk) ++fin[tg];
+    }
+    for (int t = 0; t < ph.nt; ++t) check(fin[t] == 1);
+    // every (tile, slice) unit range is covered by exactly one workgroup
+    std::vector<int> cover((size_t)ph.nt * ph.sk, 0);
+    for (int w = 0; w < G; ++w) {
+      const Assign a = assign_split(ph.nt, ph.sk, ph.nkb, ph.KB, w, G);
+      for (int tl = 0; tl < a.tw; ++tl) ++cover[(size_t)(a.t0 + tl) * ph.sk + a.s];
+    }
+    for (size_t i = 0; i < cover.size(); ++i) check(cover[i] == 1);
+  }
+  // statistics slots of every (layer, phase) input, and the layer table
+  check(sp.stats_off + (size_t)n_layers * 4 * STAT_SLOTS * M * 2 * sizeof(long long) <= sp.sync_end);
+  check(sp.layers_off + (size_t)n_layers * sizeof(DevLayer) <= sp.part_begin);
+  return bad;
+}
+
 }  // namespace
 
 }  // namespace mk
 
 extern "C" {
+
+long long mk_q4k_step_check_plan(const mk_q4k_layer* layer0, int n_layers, int M, int G) {
+  if (mk::check_step_shapes(layer0, 1, M) != MK_OK || n_layers < 1 ||
+      n_layers > mk::STEP_MAX_LAYERS || G < 1 || G > mk::kMaxG)
+    return MK_EINVAL;
+  return mk::plan_violations(*layer0, n_layers, M, G);
+}
+
 
 size_t mk_q4k_step_workspace_bytes(const mk_q4k_layer* layer0, int n_layers, int M) {
   if (mk::check_step_shapes(layer0, 1, M) != MK_OK || n_layers < 1) return 0;

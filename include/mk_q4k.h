@@ -291,6 +291,19 @@ int mk_q4k_step_res(const mk_q4k_layer* layers, const mk_q4k_layer_norm* norms,
                     const mk_q4k_layer_res_io* io, int n_layers, int M, const float* h0,
                     void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * mk_q4k_step_check_plan: host-only self-check of the walk's work split (no
+ * device access). Plans the walk for layer0's shapes, n_layers layers, M rows
+ * and G workgroups, walks every access the kernel's index arithmetic makes
+ * (weight records, column sums, slice partials, LDS slots, staged rows,
+ * finishing tiles, statistics slots) and returns how many fall outside their
+ * buffer, or which tile is finished or covered other than once (0: none);
+ * MK_EINVAL for invalid shapes, -1 when no plan fits (mk_q4k_step then
+ * returns MK_EINVAL without launching).
+ */
+long long mk_q4k_step_check_plan(const mk_q4k_layer* layer0 /* host */, int n_layers, int M,
+                                 int G);
+
 /* Copy the device status word of the last step run in `workspace` to
  * *status_out (MK_OK, MK_ETIMEOUT or MK_ERANGE). Synchronous; call after the
  * step's stream has completed. */

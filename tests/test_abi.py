@@ -138,3 +138,48 @@ def test_q6k_rejects_bad_arguments(L):
     assert L.mk_q6k_gemm_tiled(T, X + 8, Y, 4, 16, 256, None) == mk.MK_EALIGN
     assert L.mk_q6k_repack(None, T, 16, 256, None) == mk.MK_EINVAL
     assert L.mk_q6k_repack(X, T + 4, 16, 256, None) == mk.MK_EALIGN
+
+
+# --- the walk's index arithmetic, checked on the host ---------------------------
+def _layer(shp):
+    lay = mk._Layer()
+    for name in mk.MATRIX_NAMES:
+        N, K = shp[name]
+        m = getattr(lay, name)
+        m.w, m.N, m.K = None, N, K
+    return lay
+
+
+def _plan_violations(L, shp, n_layers, M, G):
+    L.mk_q4k_step_check_plan.restype = ctypes.c_longlong
+    L.mk_q4k_step_check_plan.argtypes = [ctypes.POINTER(mk._Layer), ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int]
+    lay = _layer(shp)
+    return L.mk_q4k_step_check_plan(ctypes.byref(lay), n_layers, M, G)
+
+
+@pytest.mark.parametrize("G", [256, 304, 228, 120, 80])
+def test_step_plan_accesses_stay_in_bounds(L, G):
+    """For every shape the tests and the benchmark walk, at several compute
+    unit counts, every weight record, column sum, slice partial, LDS slot,
+    staged row, finishing tile and statistics slot the kernel's index
+    arithmetic reaches lies inside its buffer, and every tile is covered and
+    finished exactly once (a host walk with the kernel's own split functions)."""
+    from synth.stack import shapes
+    cases = [shapes(), shapes(H=512, Nq=768, Nkv=256, F=1280), shapes(H=768, Nq=512, Nkv=200, F=1024),
+             shapes(H=256, Nq=256, Nkv=16, F=512)]
+    for shp in cases:
+        for M in (1, 5, 12, 16):
+            for n_layers in (1, 3, 64):
+                v = _plan_violations(L, shp, n_layers, M, G)
+                # -1: no plan fits (the launch refuses it); MI355X's 256 CUs fit all
+                assert v == 0 or (v == -1 and G != 256), (shp["q"], shp["gate"], M, n_layers, G, v)
+
+
+def test_step_plan_check_rejects_bad_shapes(L):
+    from synth.stack import shapes
+    bad = shapes()
+    bad["o"] = (5120, 6000)          # o.K != q.N, and not a multiple of 256
+    assert _plan_violations(L, bad, 1, 12, 256) == mk.MK_EINVAL
+    assert _plan_violations(L, shapes(), 1, 17, 256) == mk.MK_EINVAL
+    assert _plan_violations(L, shapes(), 1, 12, 0) == mk.MK_EINVAL
