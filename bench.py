@@ -264,6 +264,120 @@ def attn_bench(seed: int, reps: int = 30) -> list:
     return out
 
 
+TL_NAMES = ("A", "B", "C", "D")
+
+
+def timeline(args) -> int:
+    """Per-boundary breakdown of the walk from the timeline build of the
+    library (libmkq4k_timeline.so: the same kernels storing the wall clock,
+    100 MHz, at five points of every phase of every workgroup). For each phase
+    boundary, times are relative to the last workgroup's compute end of the
+    producing phase; medians over the layers (first and last skipped)."""
+    import numpy as np
+    import torch
+    import bit_weight_streaming_amd as mk
+    mk.LIB_PATH = mk.TIMELINE_LIB_PATH
+    from synth.stack import Stack
+    torch.cuda.set_device(0)
+    cus = json.loads(mk.device_info())["cus"]
+    stack = Stack(args.layers, args.M, seed=args.seed, device="cuda:0")
+    descs = stack.layer_descs()
+    ws = torch.empty(mk.step_workspace_bytes(descs[0], args.layers, args.M), dtype=torch.uint8,
+                     device="cuda:0")
+    off = mk.step_timeline_offset(descs[0], args.layers, args.M)
+    if off < 0:
+        log("the loaded library has no timeline stamps")
+        return 1
+    for _ in range(args.warmup + 1):
+        mk.step(descs, stack.io, stack.x0, stack.x_out, ws, args.M)
+    torch.cuda.synchronize()
+    if mk.step_status(ws) != 0:
+        log(f"device status {mk.step_status(ws)}")
+        return 1
+    L, G = args.layers, cus
+    raw = ws[off:off + L * 4 * G * 64].cpu().numpy().view(np.int64).reshape(L, 4, G, 8)
+    t = raw[..., :5].astype(np.float64) / 100.0   # microseconds
+    START, COMPUTED, PUBLISHED, FINISHED, SEEN = range(5)
+    rows = []
+    layer_us = np.diff(t[:, 3, :, COMPUTED].max(axis=1))
+    for p in range(4):
+        ref = t[:, p, :, COMPUTED].max(axis=1)               # last compute end, per layer
+        med_end = np.median(t[:, p, :, COMPUTED], axis=1)
+        pub = t[:, p, :, PUBLISHED].max(axis=1) - ref
+        fin = t[:, p, :, FINISHED].max(axis=1) - ref
+        seen_med = np.median(t[:, p, :, SEEN], axis=1) - ref
+        seen_max = t[:, p, :, SEEN].max(axis=1) - ref
+        nxt = np.full(L, np.nan)
+        nxt_max = np.full(L, np.nan)
+        if p < 3:
+            nxt = np.median(t[:, p + 1, :, START], axis=1) - ref
+            nxt_max = t[:, p + 1, :, START].max(axis=1) - ref
+        else:
+            nxt[:-1] = np.median(t[1:, 0, :, START], axis=1) - ref[:-1]
+            nxt_max[:-1] = t[1:, 0, :, START].max(axis=1) - ref[:-1]
+        span = np.median(t[:, p, :, COMPUTED] - t[:, p, :, START], axis=1)
+        sel = slice(1, L - 1)
+        rows.append({
+            "boundary": f"{TL_NAMES[p]} -> {TL_NAMES[(p + 1) % 4]}",
+            "compute_span_median_us": round(float(np.median(span[sel])), 2),
+            "compute_end_spread_us": round(float(np.median((ref - med_end)[sel])), 2),
+            "last_partial_published_us": round(float(np.median(pub[sel])), 2),
+            "last_tile_finished_us": round(float(np.median(fin[sel])), 2),
+            "done_seen_median_us": round(float(np.median(seen_med[sel])), 2),
+            "done_seen_last_us": round(float(np.median(seen_max[sel])), 2),
+            "next_compute_start_median_us": round(float(np.nanmedian(nxt[sel])), 2),
+            "next_compute_start_last_us": round(float(np.nanmedian(nxt_max[sel])), 2),
+        })
+    out = {"timeline": {"workload": f"{L} layers, M={args.M}", "workgroups": G,
+                        "layer_us_median": round(float(np.median(layer_us[1:-1])), 2),
+                        "boundaries": rows}}
+    for r in rows:
+        log(f"{r['boundary']}: span {r['compute_span_median_us']} us, end spread "
+            f"{r['compute_end_spread_us']}, published {r['last_partial_published_us']}, finished "
+            f"{r['last_tile_finished_us']}, done seen {r['done_seen_median_us']} (last "
+            f"{r['done_seen_last_us']}), next start {r['next_compute_start_median_us']} (last "
+            f"{r['next_compute_start_last_us']})")
+    log(f"layer: {out['timeline']['layer_us_median']} us (median)")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+CEILING_BYTES = 12 << 30
+CEILING_GRIDS = (256, 512, 1024)
+
+
+def hbm_ceiling(reps: int = 3) -> dict:
+    """The read bandwidth the chip reaches: mk_hbm_read_probe (every byte of a
+    12 GiB buffer read once with 16-byte nontemporal loads, one contiguous
+    share per workgroup) timed with HIP events over `reps` back-to-back
+    launches, for a few grid sizes; the best is the measured ceiling."""
+    import torch
+    import bit_weight_streaming_amd as mk
+    buf = torch.empty(CEILING_BYTES, dtype=torch.uint8, device="cuda:0")
+    out = torch.empty(max(CEILING_GRIDS), dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    best = None
+    per_grid = {}
+    for grid in CEILING_GRIDS:
+        mk.hbm_read_probe(buf, out, grid)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            mk.hbm_read_probe(buf, out, grid)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbs = CEILING_BYTES * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        per_grid[grid] = round(gbs, 1)
+        log(f"read ceiling probe, grid {grid} x 512: {gbs:.1f} GB/s")
+        if best is None or gbs > best[0]:
+            best = (gbs, grid)
+    del buf
+    return {"GBps": round(best[0], 1), "grid": best[1], "bytes": CEILING_BYTES, "reps": reps,
+            "per_grid": per_grid,
+            "kernel": "hbm_read_kernel (16-byte nontemporal loads, contiguous share per workgroup)"}
+
+
 def cpu_baseline(stack, budget_s: float = 20.0) -> dict:
     """Time the fp64 oracle (as it stands) on the same decode step: layers
     chained through binary16 casts as the GPU walks them, each matrix applied
@@ -330,6 +444,12 @@ def main() -> int:
     ap.add_argument("--gemm-only", action="store_true",
                     help="only the single-matrix GEMM lines (no 64-layer stack)")
     ap.add_argument("--no-attn", action="store_true", help="skip the decode-attention lines")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only run the HBM read-ceiling probe (12 GiB, nontemporal 16-byte reads)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling probe")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-boundary time breakdown of the walk from the timeline build "
+                         "(libmkq4k_timeline.so)")
     ap.add_argument("--q6k-only", action="store_true", help="only time the Q6_K product")
     ap.add_argument("--attn-only", action="store_true",
                     help="only time decode attention over the 132k-token q8_0 pool")
@@ -347,6 +467,8 @@ def main() -> int:
 
     if args.copy_calibration:
         return copy_calibration(args.steps)
+    if args.timeline:
+        return timeline(args)
 
     import torch
     import bit_weight_streaming_amd as mk
@@ -363,6 +485,10 @@ def main() -> int:
     if args.attn_only:
         torch.cuda.set_device(0)
         print(json.dumps({"attn": attn_bench(args.seed)}), flush=True)
+        return 0
+    if args.ceiling:
+        torch.cuda.set_device(0)
+        print(json.dumps({"hbm_ceiling": hbm_ceiling()}), flush=True)
         return 0
 
     dev = "cuda:0"
@@ -433,6 +559,10 @@ def main() -> int:
     if not args.no_gemm:
         q6k = q6k_bench(args.seed)
 
+    ceiling = None
+    if not res and not args.no_ceiling:
+        ceiling = hbm_ceiling()
+
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample")
@@ -469,6 +599,8 @@ def main() -> int:
             "parallelism": "1 GPU",
         },
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "hbm_ceiling": ceiling,
+        "pct_of_measured_ceiling": round(100.0 * gbs / ceiling["GBps"], 2) if ceiling else None,
         "row_tokens_per_s": round(args.M / t, 1),
         "roofline": {
             "bound": "hbm",

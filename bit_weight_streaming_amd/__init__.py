@@ -19,8 +19,11 @@ import subprocess
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 LIB_PATH = os.path.join(_HERE, "libmkq4k.so")
+# the same library built with the walk's timeline stamps (a measurement aid,
+# bench.py --timeline); the product path never loads it
+TIMELINE_LIB_PATH = os.path.join(_HERE, "libmkq4k_timeline.so")
 _SOURCES = ["q4k_gemm.hip", "q4k_step.hip", "q4k_repack.hip", "q6k_gemm.hip", "q8_attn.hip",
-            "mk_api.hip"]
+            "hbm_probe.hip", "mk_api.hip"]
 HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-fPIC", "-shared", "-std=c++17",
     # packed fp32 instructions stay off (see the build notes)
@@ -56,12 +59,20 @@ def sources() -> list[str]:
 
 
 def build() -> str:
-    """Compile libmkq4k.so in place for gfx950 with hipcc (runs without a GPU)."""
+    """Compile libmkq4k.so in place for gfx950 with hipcc (runs without a GPU),
+    and libmkq4k_timeline.so, the same sources with the walk's timeline
+    stamps (MK_STEP_TIMELINE=1) for bench.py --timeline."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(_ROOT, "include"), *sources(), "-o", tmp]
-    subprocess.check_call(cmd)
-    os.replace(tmp, LIB_PATH)
+    procs = []
+    for path, extra in ((LIB_PATH, []), (TIMELINE_LIB_PATH, ["-DMK_STEP_TIMELINE=1"])):
+        cmd = [hipcc, *HIPCC_FLAGS, *extra, "-I", os.path.join(_ROOT, "include"), *sources(), "-o",
+               path + ".tmp"]
+        procs.append((subprocess.Popen(cmd), path))
+    for proc, path in procs:
+        if proc.wait() != 0:
+            raise subprocess.CalledProcessError(proc.returncode, "hipcc")
+    for _, path in procs:
+        os.replace(path + ".tmp", path)
     return LIB_PATH
 
 
@@ -105,6 +116,12 @@ def lib():
         L.mk_q4k_gemm.argtypes = [vp, vp, vp, i, i, i, vp]
         L.mk_q4k_gemm_workspace_bytes.restype = sz
         L.mk_q4k_gemm_workspace_bytes.argtypes = [i, i, i]
+        if hasattr(L, "mk_q4k_step_timeline_offset"):
+            L.mk_q4k_step_timeline_offset.restype = ctypes.c_longlong
+            L.mk_q4k_step_timeline_offset.argtypes = [ctypes.POINTER(_Layer), i, i]
+        if hasattr(L, "mk_hbm_read_probe"):
+            L.mk_hbm_read_probe.restype = i
+            L.mk_hbm_read_probe.argtypes = [vp, sz, vp, i, vp]
         if hasattr(L, "mk_q4k_gemm_noalloc"):
             L.mk_q4k_gemm_noalloc.restype = i
             L.mk_q4k_gemm_noalloc.argtypes = [vp, vp, vp, i, i, i, vp]
@@ -195,6 +212,17 @@ def gemm(W, X, out=None, stream=None, workspace=None):
                                   workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc)
     return out
+
+
+def hbm_read_probe(buf, out, grid: int, stream=None):
+    """Read every byte of the device tensor `buf` once (16-byte nontemporal
+    loads, `grid` workgroups of 512 threads, one contiguous share each) and
+    write one XOR word per workgroup into `out` (uint32/int32, >= grid
+    entries): the read bandwidth the chip reaches, for the measured ceiling."""
+    if out.numel() < grid or out.element_size() != 4:
+        raise MkError(MK_EINVAL, "out needs one 32-bit word per workgroup")
+    _check(lib().mk_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out), grid,
+                                   _stream(stream)))
 
 
 def gemm_noalloc(W, X, out=None, stream=None):
@@ -315,6 +343,13 @@ def _layers_struct(layers):
 def step_workspace_bytes(layer0, n_layers: int, M: int) -> int:
     arr = _layers_struct([layer0])
     return int(lib().mk_q4k_step_workspace_bytes(arr, n_layers, M))
+
+
+def step_timeline_offset(layer0, n_layers: int, M: int) -> int:
+    """Byte offset of the walk's timeline stamps in its workspace (a library
+    loaded from TIMELINE_LIB_PATH), or -1 for the product library."""
+    arr = _layers_struct([layer0])
+    return int(lib().mk_q4k_step_timeline_offset(arr, n_layers, M))
 
 
 def step(layers, io, x0, x_out, workspace, M: int, stream=None) -> None:

@@ -17,6 +17,18 @@ constexpr int DONE_CTRS = 64;    // spread of the finished-tile counters
 constexpr int CTR_STRIDE = 32;   // uints between counters (128 bytes)
 constexpr int STEP_MAX_M = 16;   // rows the walk supports (one MFMA row tile)
 
+// Build-time option of the walk (a measurement aid, off in the product
+// library): with MK_STEP_TIMELINE=1 thread 0 of every workgroup stores the
+// wall clock (s_memrealtime, 100 MHz) at five points of each phase of each
+// layer into a region of the workspace (TL_EVENTS slots per (layer, phase,
+// workgroup)): compute start (input staged), compute end, slice partials
+// published, own tiles finished, the phase's done counters seen.
+#ifndef MK_STEP_TIMELINE
+#define MK_STEP_TIMELINE 0
+#endif
+constexpr int TL_EVENTS = 8;  // slots per (layer, phase, workgroup); 5 used
+enum TlEvent { TL_START = 0, TL_COMPUTED = 1, TL_PUBLISHED = 2, TL_FINISHED = 3, TL_DONE_SEEN = 4 };
+
 // Fixed-point scales of the row statistics of a phase input: sum(x) * 2^24
 // (exact for binary16 values) and sum(x^2) * 2^20, accumulated with 64-bit
 // integer atomics, so the totals do not depend on the order in which
@@ -105,6 +117,7 @@ struct StepParams {
                          // the input of phase p of layer l
   size_t status_off;     // int status word
   size_t lds_bytes;
+  size_t tl_off;         // MK_STEP_TIMELINE: [n_layers][4][G][TL_EVENTS] u64 stamps
 };
 
 }  // namespace mk

@@ -59,6 +59,17 @@ constexpr int kStatPer = (STAT_SLOTS * STEP_MAX_M * 2 + STEP_THREADS - 1) / STEP
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Timeline stamp (MK_STEP_TIMELINE builds only): thread 0 stores the wall
+// clock for (layer, phase, workgroup, event).
+__device__ __forceinline__ void tl_stamp(const StepParams& P, int l, int p, int ev) {
+  if constexpr (MK_STEP_TIMELINE) {
+    if (threadIdx.x == 0) {
+      unsigned long long* tl = reinterpret_cast<unsigned long long*>(P.ws + P.tl_off);
+      tl[(((size_t)l * 4 + p) * P.G + blockIdx.x) * TL_EVENTS + ev] = wall_clock64();
+    }
+  }
+}
+
 // Device-coherent (agent-scope) loads of values other workgroups write.
 // The pointers are taken as global-address-space ones: through a generic
 // pointer the access would be a flat one, which also counts against the LDS
@@ -810,9 +821,11 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
   if (tid < STEP_MAX_M)
     mom_s[tid] = tid < P.M ? phase_moments(tot_s, tid, ph) : float2{0.f, 0.f};
   __syncthreads();
+  tl_stamp(P, l, p, TL_PUBLISHED);
   fixup_tiles<NM, MODE>(P, ph, p, l, ltab, a, ffirst, nfin, wst, mom_s, abort_s, tid);
   wait_vm0();
   __syncthreads();
+  tl_stamp(P, l, p, TL_FINISHED);
   if (*abort_s) return false;
   if (tid < nfin) {
     unsigned* done = reinterpret_cast<unsigned*>(P.ws + P.done_off);
@@ -971,6 +984,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
                       (size_t)(l * 4 + p) * STAT_SLOTS * M * 2,
                   tot_s, x_lds, ph.x_stride, xs_lds, ph.nkb, tid);
       __syncthreads();
+      tl_stamp(P, l, p, TL_START);
 
       // ---- stream the weights
       const char* xa_lane = x_lds + (size_t)arow * ph.x_stride + g * 128;
@@ -980,6 +994,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       else
         phase_compute<1>(ring, it, ph_s[p], ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, k);
       __syncthreads();
+      tl_stamp(P, l, p, TL_COMPUTED);
 
       // ---- finish tiles, start the next phase's weight stream, wait until
       //      every tile of this phase is finished
@@ -1000,6 +1015,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
         ring_fill(ring, it, ph_s[pn], ltab[ln].w, a, lane);
       }
       if (!wait_done(P, PH, l, p, &abort_s)) return;
+      tl_stamp(P, l, p, TL_DONE_SEEN);
     }
   }
 
@@ -1043,6 +1059,7 @@ struct StepPlan {
   DevPhase ph[4];
   size_t layers_off, done_off, status_off, start_off, stats_off, sync_end;
   size_t part_begin, part_end;  // slice partial blocks of all phases
+  size_t tl_off;                // MK_STEP_TIMELINE: the stamps (0 otherwise)
   size_t total;
   bool ok = true;  // false: some K slice would get no workgroup
 };
@@ -1168,6 +1185,11 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
     off += align256(pb);
   }
   sp.part_end = off;
+  sp.tl_off = 0;
+  if (MK_STEP_TIMELINE) {
+    sp.tl_off = off;
+    off += align256((size_t)n_layers * 4 * kMaxG * TL_EVENTS * sizeof(unsigned long long));
+  }
   sp.total = off;
 }
 
@@ -1300,6 +1322,7 @@ int launch_walk(const mk_q4k_layer* layers, const std::vector<DevLayer>& table, 
   P.start_off = sp.start_off;
   P.status_off = sp.status_off;
   P.lds_bytes = lds;
+  P.tl_off = sp.tl_off;
   hipLaunchKernelGGL(q4k_step_kernel<MODE>, dim3(G), dim3(STEP_THREADS), lds, st, P);
   e = hipGetLastError();
   return e == hipSuccess ? MK_OK : MK_EHIP;
@@ -1429,6 +1452,14 @@ long long plan_violations(const mk_q4k_layer& L0, int n_layers, int M, int G) {
 }  // namespace mk
 
 extern "C" {
+
+long long mk_q4k_step_timeline_offset(const mk_q4k_layer* layer0, int n_layers, int M) {
+  if (!MK_STEP_TIMELINE) return -1;
+  if (mk::check_step_shapes(layer0, 1, M) != MK_OK || n_layers < 1) return MK_EINVAL;
+  mk::StepPlan sp;
+  mk::plan_phases(*layer0, n_layers, M, mk::kMaxG, sp);
+  return sp.ok ? (long long)sp.tl_off : -1;
+}
 
 long long mk_q4k_step_check_plan(const mk_q4k_layer* layer0, int n_layers, int M, int G) {
   if (mk::check_step_shapes(layer0, 1, M) != MK_OK || n_layers < 1 ||

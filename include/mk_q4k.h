@@ -304,10 +304,32 @@ int mk_q4k_step_res(const mk_q4k_layer* layers, const mk_q4k_layer_norm* norms,
 long long mk_q4k_step_check_plan(const mk_q4k_layer* layer0 /* host */, int n_layers, int M,
                                  int G);
 
+/*
+ * mk_q4k_step_timeline_offset: a measurement aid. In a library built with
+ * MK_STEP_TIMELINE=1 the walks store, per layer l, phase p (0..3) and
+ * workgroup w (G = the device's CU count), eight u64 wall-clock slots
+ * (100 MHz) at byte offset + ((l * 4 + p) * G + w) * 64 of the workspace:
+ * [0] input staged (compute starts), [1] compute ends, [2] slice partials
+ * published, [3] own tiles finished, [4] the phase's done counters seen.
+ * Returns that offset, or -1 in the product library (built without it).
+ */
+long long mk_q4k_step_timeline_offset(const mk_q4k_layer* layer0 /* host */, int n_layers, int M);
+
 /* Copy the device status word of the last step run in `workspace` to
  * *status_out (MK_OK, MK_ETIMEOUT or MK_ERANGE). Synchronous; call after the
  * step's stream has completed. */
 int mk_q4k_step_status(const void* workspace, int* status_out);
+
+/*
+ * mk_hbm_read_probe: a measurement, not part of the product path (the read
+ * ceiling the weight stream is compared with). Reads every whole 16-byte word of
+ * buf[0, bytes) once with nontemporal loads: `grid` workgroups of 512
+ * threads, each streaming one contiguous share with eight loads in flight
+ * per thread, and writes the XOR of what workgroup g read to out[g] (device,
+ * grid words). buf 16-byte aligned (MK_EALIGN); bytes >= 16 and
+ * 1 <= grid <= 65535 (MK_EINVAL). Asynchronous on `stream`.
+ */
+int mk_hbm_read_probe(const void* buf, size_t bytes, uint32_t* out, int grid, void* stream);
 
 /* Static text for a return code (never NULL). */
 const char* mk_strerror(int code);
