@@ -15,7 +15,11 @@ constexpr int STEP_MAX_LAYERS = 128;
 constexpr int STAT_SLOTS = 64;   // spread of the row-statistic atomics
 constexpr int DONE_CTRS = 64;    // spread of the finished-tile counters
 constexpr int CTR_STRIDE = 32;   // uints between counters (128 bytes)
-constexpr int STEP_MAX_M = 16;   // rows the walk supports (one MFMA row tile)
+constexpr int STEP_MAX_M = 16;   // rows one walk takes (one MFMA row tile)
+// Rows a step call takes: more than STEP_MAX_M run as consecutive walks over
+// row groups of STEP_MAX_M (each row's arithmetic is the same in any group).
+constexpr int STEP_MAX_ROWS = 64;
+constexpr int STEP_GROUPS = STEP_MAX_ROWS / STEP_MAX_M;
 
 // Build-time option of the walk (a measurement aid, off in the product
 // library): with MK_STEP_TIMELINE=1 thread 0 of every workgroup stores the

@@ -1025,10 +1025,11 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
 // Zero the counters, status word and statistics, and fill every slice
 // partial piece with words of parity 1 (not yet written in layer 0).
 __global__ void __launch_bounds__(256) q4k_step_clear(uint32_t* p, size_t n, uint32_t* part,
-                                                      size_t npart) {
+                                                      size_t npart, size_t keep0, size_t keep1) {
+  // words [keep0, keep1) keep their value (a later row group keeps the status)
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
+    if (i < keep0 || i >= keep1) p[i] = 0u;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < npart;
        i += (size_t)gridDim.x * blockDim.x)
     part[i] = PART_FILL;
@@ -1175,8 +1176,8 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
   sp.stats_off = off;
   off += align256((size_t)n_layers * 4 * STAT_SLOTS * M * 2 * sizeof(long long));
   sp.sync_end = off;
-  sp.layers_off = off;
-  off += align256((size_t)n_layers * sizeof(DevLayer));
+  sp.layers_off = off;  // one layer table per row group
+  off += align256((size_t)STEP_GROUPS * n_layers * sizeof(DevLayer));
   sp.part_begin = off;
   for (int p = 0; p < 4; ++p) {
     sp.ph[p].part_off = off;
@@ -1212,7 +1213,7 @@ int check_mat(const mk_q4k_mat& m) {
 bool same_shape(const mk_q4k_mat& a, const mk_q4k_mat& b) { return a.N == b.N && a.K == b.K; }
 
 int check_step_shapes(const mk_q4k_layer* layers, int n_layers, int M) {
-  if (!layers || n_layers < 1 || n_layers > STEP_MAX_LAYERS || M < 1 || M > STEP_MAX_M)
+  if (!layers || n_layers < 1 || n_layers > STEP_MAX_LAYERS || M < 1 || M > STEP_MAX_ROWS)
     return MK_EINVAL;
   const mk_q4k_layer& L = layers[0];
   const mk_q4k_mat* m[7] = {&L.q, &L.k, &L.v, &L.o, &L.gate, &L.up, &L.down};
@@ -1239,21 +1240,20 @@ struct TableCache {
   std::vector<DevLayer> table;
   DevPhase phases[4];
 };
-TableCache g_table_cache[64];
+TableCache g_table_cache[64][STEP_GROUPS];  // per device and row group
 std::mutex g_table_mu;
 
 // The part of a step call both walks share: plan, checks, the device layer
 // table (re-sent only when it changed), the clear kernel and the launch.
+// Plan of a walk over M rows (a row group), with the checks made before any
+// work is enqueued: the split, the workspace size, the LDS and occupancy.
 template <int MODE>
-int launch_walk(const mk_q4k_layer* layers, const std::vector<DevLayer>& table, int n_layers,
-                int M, const uint16_t* x0, uint16_t* x_out, const float* h0, void* workspace,
-                size_t ws_bytes, void* stream) {
-  int rc;
+int prepare_walk(const mk_q4k_layer* layers, int n_layers, int M, size_t ws_bytes, StepPlan& sp,
+                 size_t& lds, int& G) {
   int cus = 0;
-  rc = current_gfx950(&cus);
+  const int rc = current_gfx950(&cus);
   if (rc != MK_OK) return rc;
-  const int G = cus < kMaxG ? cus : kMaxG;
-  StepPlan sp;
+  G = cus < kMaxG ? cus : kMaxG;
   plan_phases(layers[0], n_layers, M, G, sp);
   if (!sp.ok) return MK_EINVAL;
   for (int p = 0; p < 4; ++p)
@@ -1264,7 +1264,7 @@ int launch_walk(const mk_q4k_layer* layers, const std::vector<DevLayer>& table, 
     // partial blocks are addressed with 32-bit buffer offsets
     if ((size_t)sp.ph[p].nt * sp.ph[p].sk * sp.ph[p].nm * 1024 >= (1ull << 32)) return MK_EINVAL;
   }
-  const size_t lds = lds_bytes(sp, M);
+  lds = lds_bytes(sp, M);
   if (lds + kStaticLds > kLdsLimit) return MK_EINVAL;
   hipError_t e = hipFuncSetAttribute((const void*)q4k_step_kernel<MODE>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1274,21 +1274,32 @@ int launch_walk(const mk_q4k_layer* layers, const std::vector<DevLayer>& table, 
                                                    STEP_THREADS, lds);
   if (e != hipSuccess) return MK_EHIP;
   if (occ < 1) return MK_EOCCUPANCY;
+  return MK_OK;
+}
 
+// Enqueue one walk (row group `group` of the call, M rows) on the stream:
+// its layer table (copied only when it changed), the clear of the
+// synchronisation words (a later group keeps the status word, so the call
+// reports the first failure of any group) and the persistent kernel.
+template <int MODE>
+int enqueue_walk(const mk_q4k_layer* layers, const std::vector<DevLayer>& table, int n_layers,
+                 int M, const uint16_t* x0, uint16_t* x_out, const float* h0, void* workspace,
+                 const StepPlan& sp, size_t lds, int G, int group, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  // layer table
+  const size_t table_off = sp.layers_off + (size_t)group * n_layers * sizeof(DevLayer);
+  hipError_t e;
   {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MK_EHIP;
     std::lock_guard<std::mutex> lk(g_table_mu);
-    TableCache& tc = g_table_cache[dev];
+    TableCache& tc = g_table_cache[dev][group];
     const bool same = tc.ws == workspace && tc.table.size() == table.size() &&
                       memcmp(tc.table.data(), table.data(), table.size() * sizeof(DevLayer)) == 0 &&
                       memcmp(tc.phases, sp.ph, sizeof(sp.ph)) == 0;
     if (!same) {
       // pageable sources: the calls return once the host buffers have been read
-      e = hipMemcpyAsync(ws + sp.layers_off, table.data(), table.size() * sizeof(DevLayer),
+      e = hipMemcpyAsync(ws + table_off, table.data(), table.size() * sizeof(DevLayer),
                          hipMemcpyHostToDevice, st);
       if (e != hipSuccess) return MK_EHIP;
       tc.ws = workspace;
@@ -1298,10 +1309,12 @@ int launch_walk(const mk_q4k_layer* layers, const std::vector<DevLayer>& table, 
   }
   // clear flags, status, counters and statistics
   const size_t nclear = sp.sync_end / sizeof(uint32_t);
+  const size_t keep0 = group > 0 ? sp.status_off / sizeof(uint32_t) : 0;
+  const size_t keep1 = group > 0 ? keep0 + 1 : 0;
   hipLaunchKernelGGL(q4k_step_clear, dim3(256), dim3(256), 0, st,
                      reinterpret_cast<uint32_t*>(ws), nclear,
                      reinterpret_cast<uint32_t*>(ws + sp.part_begin),
-                     (sp.part_end - sp.part_begin) / sizeof(uint32_t));
+                     (sp.part_end - sp.part_begin) / sizeof(uint32_t), keep0, keep1);
   e = hipGetLastError();
   if (e != hipSuccess) return MK_EHIP;
 
@@ -1316,7 +1329,7 @@ int launch_walk(const mk_q4k_layer* layers, const std::vector<DevLayer>& table, 
   P.x_out = x_out;
   P.h0 = h0;
   P.ws = ws;
-  P.layers_off = sp.layers_off;
+  P.layers_off = table_off;
   P.done_off = sp.done_off;
   P.stats_off = sp.stats_off;
   P.start_off = sp.start_off;
@@ -1326,6 +1339,12 @@ int launch_walk(const mk_q4k_layer* layers, const std::vector<DevLayer>& table, 
   hipLaunchKernelGGL(q4k_step_kernel<MODE>, dim3(G), dim3(STEP_THREADS), lds, st, P);
   e = hipGetLastError();
   return e == hipSuccess ? MK_OK : MK_EHIP;
+}
+
+// Rows [r0, r0 + STEP_MAX_M) of the call: row group r0 / STEP_MAX_M.
+int group_rows(int M, int g) {
+  const int r = M - g * STEP_MAX_M;
+  return r < STEP_MAX_M ? r : STEP_MAX_M;
 }
 
 // Host-side checks of the per-layer weights and outputs both walks share.
@@ -1343,14 +1362,18 @@ int check_layer_io(const mk_q4k_layer* layers, float* const* y, uint16_t* const*
   return MK_OK;
 }
 
-void fill_table(const mk_q4k_layer& L, float* const* y, uint16_t* const* x, DevLayer& t) {
+// A layer's table entry for the rows from r0 on: every [M][width] buffer
+// starts r0 rows in (outputs [M][N]; inputs x[0], x[2] [M][H], x[1] [M][q.N],
+// x[3] [M][gate.N]).
+void fill_table(const mk_q4k_layer& L, float* const* y, uint16_t* const* x, int r0, DevLayer& t) {
   const mk_q4k_mat* m[7] = {&L.q, &L.k, &L.v, &L.o, &L.gate, &L.up, &L.down};
+  const int xw[4] = {L.q.K, L.q.N, L.gate.K, L.gate.N};
   memset(&t, 0, sizeof(t));
   for (int i = 0; i < 7; ++i) {
     t.w[i] = static_cast<const uint8_t*>(m[i]->w);
-    t.y[i] = y[i];
+    t.y[i] = y[i] + (size_t)r0 * m[i]->N;
   }
-  for (int i = 0; i < 4; ++i) t.x[i] = x[i];
+  for (int i = 0; i < 4; ++i) t.x[i] = x[i] + (size_t)r0 * xw[i];
 }
 
 
@@ -1443,7 +1466,7 @@ long long plan_violations(const mk_q4k_layer& L0, int n_layers, int M, int G) {
   }
   // statistics slots of every (layer, phase) input, and the layer table
   check(sp.stats_off + (size_t)n_layers * 4 * STAT_SLOTS * M * 2 * sizeof(long long) <= sp.sync_end);
-  check(sp.layers_off + (size_t)n_layers * sizeof(DevLayer) <= sp.part_begin);
+  check(sp.layers_off + (size_t)STEP_GROUPS * n_layers * sizeof(DevLayer) <= sp.part_begin);
   return bad;
 }
 
@@ -1457,7 +1480,7 @@ long long mk_q4k_step_timeline_offset(const mk_q4k_layer* layer0, int n_layers, 
   if (!MK_STEP_TIMELINE) return -1;
   if (mk::check_step_shapes(layer0, 1, M) != MK_OK || n_layers < 1) return MK_EINVAL;
   mk::StepPlan sp;
-  mk::plan_phases(*layer0, n_layers, M, mk::kMaxG, sp);
+  mk::plan_phases(*layer0, n_layers, mk::group_rows(M, 0), mk::kMaxG, sp);
   return sp.ok ? (long long)sp.tl_off : -1;
 }
 
@@ -1465,14 +1488,21 @@ long long mk_q4k_step_check_plan(const mk_q4k_layer* layer0, int n_layers, int M
   if (mk::check_step_shapes(layer0, 1, M) != MK_OK || n_layers < 1 ||
       n_layers > mk::STEP_MAX_LAYERS || G < 1 || G > mk::kMaxG)
     return MK_EINVAL;
-  return mk::plan_violations(*layer0, n_layers, M, G);
+  // the first row group and the last (the only one that can be smaller)
+  const int last = (M - 1) / mk::STEP_MAX_M;
+  long long bad = mk::plan_violations(*layer0, n_layers, mk::group_rows(M, 0), G);
+  if (bad >= 0 && last > 0) {
+    const long long b2 = mk::plan_violations(*layer0, n_layers, mk::group_rows(M, last), G);
+    bad = b2 < 0 ? b2 : bad + b2;
+  }
+  return bad;
 }
 
 
 size_t mk_q4k_step_workspace_bytes(const mk_q4k_layer* layer0, int n_layers, int M) {
   if (mk::check_step_shapes(layer0, 1, M) != MK_OK || n_layers < 1) return 0;
-  mk::StepPlan sp;
-  mk::plan_phases(*layer0, n_layers, M, mk::kMaxG, sp);
+  mk::StepPlan sp;  // the row groups run one after another in one workspace
+  mk::plan_phases(*layer0, n_layers, mk::group_rows(M, 0), mk::kMaxG, sp);
   return sp.ok ? sp.total : 0;
 }
 
@@ -1485,14 +1515,32 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
   if (rc != MK_OK) return rc;
   if (!io || !x0 || !x_out || !workspace) return MK_EINVAL;
   if (!al16(x0) || !al16(x_out) || !al16(workspace)) return MK_EALIGN;
-  std::vector<DevLayer> table(n_layers);
   for (int l = 0; l < n_layers; ++l) {
     rc = check_layer_io(layers, io[l].y, io[l].x, l);
     if (rc != MK_OK) return rc;
-    fill_table(layers[l], io[l].y, io[l].x, table[l]);
   }
-  return launch_walk<0>(layers, table, n_layers, M, x0, x_out, nullptr, workspace, ws_bytes,
-                        stream);
+  // every row group's plan is checked before any work is enqueued (the
+  // first group has the most rows)
+  StepPlan sp;
+  size_t lds = 0;
+  int G = 0;
+  const int groups = (M + STEP_MAX_M - 1) / STEP_MAX_M;
+  for (int g = groups - 1; g >= 0; --g) {
+    rc = prepare_walk<0>(layers, n_layers, group_rows(M, g), ws_bytes, sp, lds, G);
+    if (rc != MK_OK) return rc;
+  }
+  const int H = layers[0].q.K;
+  std::vector<DevLayer> table(n_layers);
+  for (int g = 0; g < groups; ++g) {
+    const int r0 = g * STEP_MAX_M, Mg = group_rows(M, g);
+    for (int l = 0; l < n_layers; ++l) fill_table(layers[l], io[l].y, io[l].x, r0, table[l]);
+    rc = prepare_walk<0>(layers, n_layers, Mg, ws_bytes, sp, lds, G);
+    if (rc != MK_OK) return rc;
+    rc = enqueue_walk<0>(layers, table, n_layers, Mg, x0 + (size_t)r0 * H, x_out + (size_t)r0 * H,
+                         nullptr, workspace, sp, lds, G, g, stream);
+    if (rc != MK_OK) return rc;
+  }
+  return MK_OK;
 }
 
 int mk_q4k_step_res(const mk_q4k_layer* layers, const mk_q4k_layer_norm* norms,
@@ -1503,7 +1551,6 @@ int mk_q4k_step_res(const mk_q4k_layer* layers, const mk_q4k_layer_norm* norms,
   if (rc != MK_OK) return rc;
   if (!io || !norms || !h0 || !workspace) return MK_EINVAL;
   if (!al16(h0) || !al16(workspace)) return MK_EALIGN;
-  std::vector<DevLayer> table(n_layers);
   for (int l = 0; l < n_layers; ++l) {
     rc = check_layer_io(layers, io[l].y, io[l].x, l);
     if (rc != MK_OK) return rc;
@@ -1511,14 +1558,33 @@ int mk_q4k_step_res(const mk_q4k_layer* layers, const mk_q4k_layer_norm* norms,
     if (!al16(io[l].h_mid) || !al16(io[l].h_out) || !al16(norms[l].attn) ||
         !al16(norms[l].ffn))
       return MK_EALIGN;
-    fill_table(layers[l], io[l].y, io[l].x, table[l]);
-    table[l].h[0] = io[l].h_mid;
-    table[l].h[1] = io[l].h_out;
-    table[l].g[0] = norms[l].attn;
-    table[l].g[1] = norms[l].ffn;
   }
-  return launch_walk<1>(layers, table, n_layers, M, nullptr, nullptr, h0, workspace, ws_bytes,
-                        stream);
+  StepPlan sp;
+  size_t lds = 0;
+  int G = 0;
+  const int groups = (M + STEP_MAX_M - 1) / STEP_MAX_M;
+  for (int g = groups - 1; g >= 0; --g) {
+    rc = prepare_walk<1>(layers, n_layers, group_rows(M, g), ws_bytes, sp, lds, G);
+    if (rc != MK_OK) return rc;
+  }
+  const int H = layers[0].q.K;
+  std::vector<DevLayer> table(n_layers);
+  for (int g = 0; g < groups; ++g) {
+    const int r0 = g * STEP_MAX_M, Mg = group_rows(M, g);
+    for (int l = 0; l < n_layers; ++l) {
+      fill_table(layers[l], io[l].y, io[l].x, r0, table[l]);
+      table[l].h[0] = io[l].h_mid + (size_t)r0 * H;
+      table[l].h[1] = io[l].h_out + (size_t)r0 * H;
+      table[l].g[0] = norms[l].attn;
+      table[l].g[1] = norms[l].ffn;
+    }
+    rc = prepare_walk<1>(layers, n_layers, Mg, ws_bytes, sp, lds, G);
+    if (rc != MK_OK) return rc;
+    rc = enqueue_walk<1>(layers, table, n_layers, Mg, nullptr, nullptr, h0 + (size_t)r0 * H,
+                         workspace, sp, lds, G, g, stream);
+    if (rc != MK_OK) return rc;
+  }
+  return MK_OK;
 }
 
 int mk_q4k_step_status(const void* workspace, int* status_out) {

@@ -195,9 +195,17 @@ int mk_q4k_gemm_tiled(const void* W_tiles, const uint16_t* X_fp16, float* Y_fp32
  * each row's outputs and phase inputs are the same, bit for bit, whether it
  * is walked alone or stacked with other rows (mk_q4k_step_res likewise).
  *
+ * Rows past 16 (a prefill chunk riding with the decode rows; the OpenJet
+ * post, paragraph on keeping it fast with real agents): one walk takes one
+ * MFMA row tile of 16 rows, so a call with M > 16 runs ceil(M / 16) walks one
+ * after another on the stream, rows [16g, 16g + 16) in walk g, each streaming
+ * every weight once. By the invariance above a row's results do not depend
+ * on its group. The workspace of 16 rows serves every M; the status word
+ * keeps the first failure of any group.
+ *
  * Chain rules (checked): q.K = k.K = v.K = gate.K = up.K = down.N = H (the
  * hidden size), o.K = q.N, gate.N = up.N = down.K = F; every K % 256 == 0;
- * every layer has the same shapes. Limits: 1 <= M <= 16 stacked rows,
+ * every layer has the same shapes. Limits: 1 <= M <= 64 stacked rows,
  * 1 <= n_layers <= 128, each matrix's tile-record form under 4 GiB
  * (otherwise MK_EINVAL). Each phase's K range is cut into slices whose input
  * rows fit in on-chip memory; a shape whose plan still does not fit one

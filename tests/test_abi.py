@@ -169,7 +169,7 @@ def test_step_plan_accesses_stay_in_bounds(L, G):
     cases = [shapes(), shapes(H=512, Nq=768, Nkv=256, F=1280), shapes(H=768, Nq=512, Nkv=200, F=1024),
              shapes(H=256, Nq=256, Nkv=16, F=512)]
     for shp in cases:
-        for M in (1, 5, 12, 16):
+        for M in (1, 5, 12, 16, 33, 64):
             for n_layers in (1, 3, 64):
                 v = _plan_violations(L, shp, n_layers, M, G)
                 # -1: no plan fits (the launch refuses it); MI355X's 256 CUs fit all
@@ -181,5 +181,21 @@ def test_step_plan_check_rejects_bad_shapes(L):
     bad = shapes()
     bad["o"] = (5120, 6000)          # o.K != q.N, and not a multiple of 256
     assert _plan_violations(L, bad, 1, 12, 256) == mk.MK_EINVAL
-    assert _plan_violations(L, shapes(), 1, 17, 256) == mk.MK_EINVAL
+    assert _plan_violations(L, shapes(), 1, 65, 256) == mk.MK_EINVAL
+    assert _plan_violations(L, shapes(), 1, 0, 256) == mk.MK_EINVAL
     assert _plan_violations(L, shapes(), 1, 12, 0) == mk.MK_EINVAL
+
+
+def test_step_workspace_is_one_row_group(L):
+    """Rows past 16 run as further walks over row groups of 16, one after
+    another in the same workspace: a call of up to 64 rows needs the
+    workspace of 16 rows, and 65 rows are refused (size 0)."""
+    from synth.stack import shapes
+    L.mk_q4k_step_workspace_bytes.restype = ctypes.c_size_t
+    L.mk_q4k_step_workspace_bytes.argtypes = [ctypes.POINTER(mk._Layer), ctypes.c_int, ctypes.c_int]
+    lay = _layer(shapes())
+    w16 = L.mk_q4k_step_workspace_bytes(ctypes.byref(lay), 64, 16)
+    assert w16 > 0
+    for M in (17, 32, 44, 64):
+        assert L.mk_q4k_step_workspace_bytes(ctypes.byref(lay), 64, M) == w16
+    assert L.mk_q4k_step_workspace_bytes(ctypes.byref(lay), 64, 65) == 0

@@ -92,7 +92,7 @@ SMALL = shapes(H=512, Nq=768, Nkv=256, F=1280)
 RAGGED = shapes(H=768, Nq=512, Nkv=200, F=1024)
 
 
-@pytest.mark.parametrize("M", [12, 1, 5, 16])
+@pytest.mark.parametrize("M", [12, 1, 5, 16, 32, 33, 64])
 def test_small_stack_all_columns(M):
     stack = Stack(3, M, SMALL, seed=M, device=DEV)
     run_step(stack)
@@ -167,6 +167,40 @@ def test_rows_bit_identical_alone_or_stacked():
             for a, b in zip(one.io[l]["y"] + one.io[l]["x"], stack.io[l]["y"] + stack.io[l]["x"]):
                 assert torch.equal(a[0], b[r]), (r, l)
         assert torch.equal(one.x_out[0], stack.x_out[r])
+
+
+def test_decode_rows_stacked_with_a_prefill_chunk():
+    """A mixed step: 12 decode rows (4 agents x 3) stacked with a 32-row
+    prefill chunk of a new prompt, 44 rows in one call (three row groups:
+    the decode rows share the first with 4 prefill rows). Every output and
+    every cast of each part is, bit for bit, what the part gives walked alone
+    (12 rows; 32 rows), and the stacked call matches the oracle."""
+    dec = Stack(2, 12, SMALL, seed=61, device=DEV)
+    pre = Stack(2, 32, SMALL, seed=61, device=DEV)
+    pre.x0.copy_(torch.from_numpy(synth.activations(62, 32, dec.H)).to(DEV))
+    both = Stack(2, 44, SMALL, seed=61, device=DEV)
+    both.x0.copy_(torch.cat([dec.x0, pre.x0]))
+    for s in (dec, pre, both):
+        run_step(s)
+    for l in range(2):
+        for a, b, c in zip(dec.io[l]["y"] + dec.io[l]["x"], pre.io[l]["y"] + pre.io[l]["x"],
+                           both.io[l]["y"] + both.io[l]["x"]):
+            assert torch.equal(c[:12], a), l
+            assert torch.equal(c[12:], b), l
+    assert torch.equal(both.x_out[:12], dec.x_out)
+    assert torch.equal(both.x_out[12:], pre.x_out)
+    check_stack(both)
+    check_out(both)
+
+
+def test_full_size_layers_64_rows():
+    """Two layers of the full 27B-class shapes at M = 64 (four row groups),
+    1024 sampled columns per matrix (all of k and v), every cast in full."""
+    stack = Stack(2, 64, seed=63, device=DEV)
+    run_step(stack)
+    worst = check_stack(stack, ncols=1024, seed=64)
+    check_out(stack)
+    print(f"full-size layers, M=64: worst |err|/S = {worst:.3e}")
 
 
 def test_full_stack_sampled_columns():

@@ -109,7 +109,7 @@ def check_res_stack(stack, check_layers=None, ncols=None, seed=0):
     return worst, off
 
 
-@pytest.mark.parametrize("M", [12, 1, 16])
+@pytest.mark.parametrize("M", [12, 1, 16, 40])
 def test_res_small_stack_all_columns(M):
     stack = ResStack(3, M, SMALL, seed=30 + M, device=DEV)
     run_res(stack)
@@ -144,6 +144,20 @@ def test_res_rows_bit_identical_alone_or_stacked():
             for a, b in zip(one.io[l]["y"] + one.io[l]["x"] + one.io[l]["h"],
                             stack.io[l]["y"] + stack.io[l]["x"] + stack.io[l]["h"]):
                 assert torch.equal(a[0], b[r]), (r, l)
+
+
+def test_res_rows_of_a_later_row_group_bit_identical():
+    """Rows 16.. of a 20-row residual walk (the second row group) against
+    the same rows walked alone."""
+    stack = ResStack(2, 20, SMALL, seed=46, device=DEV)
+    run_res(stack)
+    tail = ResStack(2, 4, SMALL, seed=46, device=DEV)
+    tail.h0.copy_(stack.h0[16:])
+    run_res(tail)
+    for l in range(2):
+        for a, b in zip(tail.io[l]["y"] + tail.io[l]["x"] + tail.io[l]["h"],
+                        stack.io[l]["y"] + stack.io[l]["x"] + stack.io[l]["h"]):
+            assert torch.equal(a, b[16:]), l
 
 
 def test_res_rejects_missing_norm():
