@@ -182,6 +182,38 @@ bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace mk
 
+namespace mk {
+namespace {
+
+// One launch for M <= 32 rows.
+int launch_q6(const uint8_t* T, const uint16_t* X, float* Y, int M, int N, int K, hipStream_t st) {
+  const int n_tiles = (N + 15) / 16;
+  // several weight tiles per workgroup share the activation loads: four
+  // where that still leaves 256 workgroups (one row tile), two where it
+  // leaves 512; the choice depends on N and the row-tile count only
+  const bool pair = (n_tiles + 1) / 2 >= 512;
+  const bool quad = (n_tiles + 3) / 4 >= 256;
+  const dim3 grid((unsigned)(quad && M <= 16 ? (n_tiles + 3) / 4 : pair ? (n_tiles + 1) / 2 : n_tiles)),
+      block(Q6_THREADS);
+  if (M <= 16) {
+    if (quad)
+      hipLaunchKernelGGL((q6k_gemm_kernel<1, 4>), grid, block, 0, st, T, X, Y, M, N, K);
+    else if (pair)
+      hipLaunchKernelGGL((q6k_gemm_kernel<1, 2>), grid, block, 0, st, T, X, Y, M, N, K);
+    else
+      hipLaunchKernelGGL((q6k_gemm_kernel<1, 1>), grid, block, 0, st, T, X, Y, M, N, K);
+  } else {
+    if (pair)
+      hipLaunchKernelGGL((q6k_gemm_kernel<2, 2>), grid, block, 0, st, T, X, Y, M, N, K);
+    else
+      hipLaunchKernelGGL((q6k_gemm_kernel<2, 1>), grid, block, 0, st, T, X, Y, M, N, K);
+  }
+  return hipGetLastError() == hipSuccess ? MK_OK : MK_EHIP;
+}
+
+}  // namespace
+}  // namespace mk
+
 extern "C" {
 
 size_t mk_q6k_tiles_bytes(int N, int K) {
@@ -205,32 +237,19 @@ int mk_q6k_repack(const void* W, void* tiles, int N, int K, void* stream) {
 int mk_q6k_gemm_tiled(const void* tiles, const uint16_t* X, float* Y, int M, int N, int K,
                       void* stream) {
   using namespace mk;
-  if (!tiles || !X || !Y || M < 1 || M > 32 || N < 1 || K < Q6_QK || K % Q6_QK) return MK_EINVAL;
+  if (!tiles || !X || !Y || M < 1 || M > 64 || N < 1 || K < Q6_QK || K % Q6_QK) return MK_EINVAL;
   if (!al16(tiles) || !al16(X) || !al16(Y)) return MK_EALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int n_tiles = (N + 15) / 16;
   const uint8_t* T = static_cast<const uint8_t*>(tiles);
-  // several weight tiles per workgroup share the activation loads: four
-  // where that still leaves 256 workgroups (one row tile), two where it
-  // leaves 512; the choice depends on N and the row-tile count only
-  const bool pair = (n_tiles + 1) / 2 >= 512;
-  const bool quad = (n_tiles + 3) / 4 >= 256;
-  const dim3 grid((unsigned)(quad && M <= 16 ? (n_tiles + 3) / 4 : pair ? (n_tiles + 1) / 2 : n_tiles)),
-      block(Q6_THREADS);
-  if (M <= 16) {
-    if (quad)
-      hipLaunchKernelGGL((q6k_gemm_kernel<1, 4>), grid, block, 0, st, T, X, Y, M, N, K);
-    else if (pair)
-      hipLaunchKernelGGL((q6k_gemm_kernel<1, 2>), grid, block, 0, st, T, X, Y, M, N, K);
-    else
-      hipLaunchKernelGGL((q6k_gemm_kernel<1, 1>), grid, block, 0, st, T, X, Y, M, N, K);
-  } else {
-    if (pair)
-      hipLaunchKernelGGL((q6k_gemm_kernel<2, 2>), grid, block, 0, st, T, X, Y, M, N, K);
-    else
-      hipLaunchKernelGGL((q6k_gemm_kernel<2, 1>), grid, block, 0, st, T, X, Y, M, N, K);
+  // up to 32 rows per launch (two row tiles: more spill registers); rows 32..
+  // in a second launch over the same weights. A row's result does not depend
+  // on the rows beside it, so the split changes no bits.
+  for (int r0 = 0; r0 < M; r0 += 32) {
+    const int m = M - r0 < 32 ? M - r0 : 32;
+    const int rc = launch_q6(T, X + (size_t)r0 * K, Y + (size_t)r0 * N, m, N, K, st);
+    if (rc != MK_OK) return rc;
   }
-  return hipGetLastError() == hipSuccess ? MK_OK : MK_EHIP;
+  return MK_OK;
 }
 
 }  // extern "C"

@@ -51,8 +51,11 @@ int mk_q6k_repack(const void* W, void* tiles, int N, int K, void* stream);
 
 /* Y = X * W^T for the repacked Q6_K matrix W (N x K): X binary16 [M][K]
  * row-major, Y fp32 [M][N] row-major (device, caller-owned, 16-byte
- * aligned), 1 <= M <= 32. Asynchronous on `stream`; no workspace. Returns
- * MK_OK, MK_EINVAL, MK_EALIGN or MK_EHIP. */
+ * aligned), 1 <= M <= 64. One launch takes up to 32 rows (two MFMA row
+ * tiles); rows 32.. go to a second launch over the same weights on the same
+ * stream. A row's result does not depend on the rows beside it, so every
+ * row's bits are the same alone or stacked. Asynchronous on `stream`; no
+ * workspace. Returns MK_OK, MK_EINVAL, MK_EALIGN or MK_EHIP. */
 int mk_q6k_gemm_tiled(const void* tiles, const uint16_t* X, float* Y, int M, int N, int K,
                       void* stream);
 

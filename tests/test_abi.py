@@ -131,7 +131,7 @@ def test_q6k_rejects_bad_arguments(L):
     assert L.mk_q6k_tiles_bytes(16, 256) == 3360
     assert L.mk_q6k_tiles_bytes(17, 512) == 2 * 2 * 3360
     assert L.mk_q6k_tiles_bytes(16, 300) == 0 and L.mk_q6k_tiles_bytes(0, 256) == 0
-    assert L.mk_q6k_gemm_tiled(T, X, Y, 33, 16, 256, None) == mk.MK_EINVAL    # M > 32
+    assert L.mk_q6k_gemm_tiled(T, X, Y, 65, 16, 256, None) == mk.MK_EINVAL    # M > 64
     assert L.mk_q6k_gemm_tiled(T, X, Y, 0, 16, 256, None) == mk.MK_EINVAL
     assert L.mk_q6k_gemm_tiled(T, X, Y, 4, 16, 200, None) == mk.MK_EINVAL    # K % 256
     assert L.mk_q6k_gemm_tiled(None, X, Y, 4, 16, 256, None) == mk.MK_EINVAL

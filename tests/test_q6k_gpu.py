@@ -36,7 +36,8 @@ def inputs(N, K, M, tag):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 256), (12, 37, 1024), (16, 100, 2304), (17, 48, 512),
-                                   (32, 21, 1280), (5, 333, 4096)])
+                                   (32, 21, 1280), (5, 333, 4096), (33, 40, 768), (48, 37, 1024),
+                                   (64, 100, 2304)])
 def test_q6k_all_outputs(M, N, K):
     W, X = inputs(N, K, M, tag=M)
     Y = run(W, X, N)
@@ -85,11 +86,24 @@ def test_q6k_rows_bit_identical_alone_or_stacked():
         assert np.array_equal(one.view(np.uint32), Y[r:r + 1].view(np.uint32)), r
 
 
+def test_q6k_rows_past_32_bit_identical():
+    """64 rows run as two launches of 32 over the same weights: rows 32.. are,
+    bit for bit, what they give alone, and the first 32 what they give as a
+    32-row call."""
+    N, K = 5120, 2048
+    W, X = inputs(N, K, 64, tag=12)
+    Y = run(W, X, N)
+    first = run(W, X[:32], N)
+    rest = run(W, X[32:], N)
+    assert np.array_equal(first.view(np.uint32), Y[:32].view(np.uint32))
+    assert np.array_equal(rest.view(np.uint32), Y[32:].view(np.uint32))
+
+
 def test_q6k_rejects_bad_arguments():
     Wd = torch.zeros(32 * 210, dtype=torch.uint8, device=DEV)
     T = mk.q6k_repack(Wd, 32, 256)
     with pytest.raises(mk.MkError) as e:
-        mk.q6k_gemm_tiled(T, torch.zeros((33, 256), dtype=torch.float16, device=DEV), 32)
+        mk.q6k_gemm_tiled(T, torch.zeros((65, 256), dtype=torch.float16, device=DEV), 32)
     assert e.value.code == mk.MK_EINVAL
 
 
