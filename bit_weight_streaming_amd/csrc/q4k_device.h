@@ -50,6 +50,13 @@ constexpr int X_BYTES_PER_BLOCK = 512;
 // LDS bytes per activation row per super-block for the sub-block sums
 // (8 sub-blocks x {a, b, c, 0} binary16, see split_xsum)
 constexpr int XSUM_BYTES_PER_BLOCK = 64;
+// Bytes after each row's sub-block sums in LDS: the 16 lanes that read one
+// block's sums of 16 rows then hit 16 different bank groups (with a stride of
+// a multiple of 128 bytes they would all hit the same one).
+constexpr int XSUM_ROW_PAD = 16;
+__host__ __device__ constexpr int xsum_row_bytes(int nkb) {
+  return nkb * XSUM_BYTES_PER_BLOCK + XSUM_ROW_PAD;
+}
 // pad added to each LDS activation row so that the 16 rows read by one
 // ds_read_b128 land on distinct banks
 constexpr int X_ROW_PAD = 16;
@@ -378,8 +385,8 @@ __device__ __forceinline__ half4v split_xsum(float sum) {
 
 // Sub-block sums of the staged activations, as split_xsum parts, for the
 // min-term MFMA: row m, block b, sub-block j at
-// xs_lds + (m * nkb_stride + b) * 64 + 8 * j.
-__device__ __forceinline__ void stage_xsum(int M, int nkb, int nkb_stride, const char* x_lds,
+// xs_lds + m * xs_row + b * 64 + 8 * j (xs_row = xsum_row_bytes(nkb)).
+__device__ __forceinline__ void stage_xsum(int M, int nkb, int xs_row, const char* x_lds,
                                            int x_stride, char* xs_lds, int tid,
                                            int nthreads) {
   const int items = M * nkb * 8;
@@ -402,8 +409,8 @@ __device__ __forceinline__ void stage_xsum(int M, int nkb, int nkb_stride, const
         sum += (float)hh.y;
       }
     }
-    *reinterpret_cast<half4v*>(xs_lds + ((size_t)m * nkb_stride + b) * XSUM_BYTES_PER_BLOCK +
-                               8 * j) = split_xsum(sum);
+    *reinterpret_cast<half4v*>(xs_lds + (size_t)m * xs_row + b * XSUM_BYTES_PER_BLOCK + 8 * j) =
+        split_xsum(sum);
   }
 }
 

@@ -72,7 +72,7 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
   for (int rt = 0; rt < MT; ++rt) {
     const int row = min(16 * rt + c, A.M - 1);
     xa[rt] = x_lds + (size_t)row * A.x_stride + g * 128;
-    xs[rt] = xs_lds + (size_t)row * a.nkb * XSUM_BYTES_PER_BLOCK + 16 * g;
+    xs[rt] = xs_lds + (size_t)row * xsum_row_bytes(a.nkb) + 16 * g;
   }
   const UnpackConsts k = unpack_consts();
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(A.part, A.part_bytes);
@@ -124,7 +124,8 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
     if (s < ub - ua) load_next(ring[s]);
   if (a.U > 0) stage_x(A.x, A.K, A.M, a.kb0, a.nkb, x_lds, A.x_stride, tid, GEMM_THREADS);
   __syncthreads();
-  if (a.U > 0) stage_xsum(A.M, a.nkb, a.nkb, x_lds, A.x_stride, xs_lds, tid, GEMM_THREADS);
+  if (a.U > 0)
+    stage_xsum(A.M, a.nkb, xsum_row_bytes(a.nkb), x_lds, A.x_stride, xs_lds, tid, GEMM_THREADS);
   __syncthreads();
 
   // this wave's parts of the tiles it shares (slot 0, slot 1), held until the
@@ -281,7 +282,7 @@ GemmPlan make_plan(int M, int N, int K, int G) {
   const size_t contrib_p = (size_t)SPLIT_WAVES * 2 * mtp * 1024;
   auto x_bytes = [](int rows, int nkb) {
     const size_t b = (size_t)rows * (nkb * X_BYTES_PER_BLOCK + X_ROW_PAD) +
-                     (size_t)rows * nkb * XSUM_BYTES_PER_BLOCK;
+                     (size_t)rows * xsum_row_bytes(nkb);
     return (b + 15) & ~(size_t)15;
   };
   double best = -1.0;

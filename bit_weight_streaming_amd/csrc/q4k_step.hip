@@ -319,7 +319,7 @@ template <int R>
 __device__ __forceinline__ void stage_rounds(const uint16_t* src, int K, int M, const Assign& a,
                                             const long long* st, unsigned long long* tot_s,
                                             char* x_lds, int x_stride, char* xs_lds,
-                                            int xs_stride, int tid) {
+                                            int xs_row, int tid) {
   const int cpr = a.nkb * 32;  // 8-wide chunks per row
   const int items = M * cpr;   // at most STEP_THREADS * R
   // row of chunk index x < 2^16: x * magic / 2^32 (cpr < 2^16)
@@ -368,7 +368,7 @@ __device__ __forceinline__ void stage_rounds(const uint16_t* src, int K, int M, 
     *reinterpret_cast<u32x4*>(x_lds + (size_t)m * x_stride + b * X_BYTES_PER_BLOCK + gq * 128 +
                               (2 * u + hb) * 16) = o;
     if ((ch & 3) == 0)
-      *reinterpret_cast<half4v*>(xs_lds + ((size_t)m * xs_stride + b) * XSUM_BYTES_PER_BLOCK +
+      *reinterpret_cast<half4v*>(xs_lds + (size_t)m * xs_row + b * XSUM_BYTES_PER_BLOCK +
                                  8 * (kk >> 5)) = split_xsum(sum);
   }
 #pragma unroll
@@ -383,11 +383,11 @@ __device__ __forceinline__ void stage_rounds(const uint16_t* src, int K, int M, 
 __device__ __forceinline__ void stage_slice(const uint16_t* src, int K, int M, const Assign& a,
                                             const long long* st, unsigned long long* tot_s,
                                             char* x_lds, int x_stride, char* xs_lds,
-                                            int xs_stride, int tid) {
+                                            int xs_row, int tid) {
   static_assert(kStageRound == 7, "one instantiation per round count");
   const int r = uni((M * a.nkb * 32 + STEP_THREADS - 1) / STEP_THREADS);
 #define MK_STAGE(RR) \
-  stage_rounds<RR>(src, K, M, a, st, tot_s, x_lds, x_stride, xs_lds, xs_stride, tid)
+  stage_rounds<RR>(src, K, M, a, st, tot_s, x_lds, x_stride, xs_lds, xs_row, tid)
   if (r > 5) MK_STAGE(7);
   else if (r > 4) MK_STAGE(5);
   else if (r > 3) MK_STAGE(4);
@@ -982,13 +982,13 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       stage_slice(MODE == 0 && l == 0 && p == 0 ? P.x0 : L->x[p], ph.K, M, a,
                   reinterpret_cast<const long long*>(P.ws + P.stats_off) +
                       (size_t)(l * 4 + p) * STAT_SLOTS * M * 2,
-                  tot_s, x_lds, ph.x_stride, xs_lds, ph.nkb, tid);
+                  tot_s, x_lds, ph.x_stride, xs_lds, xsum_row_bytes(ph.nkb), tid);
       __syncthreads();
       tl_stamp(P, l, p, TL_START);
 
       // ---- stream the weights
       const char* xa_lane = x_lds + (size_t)arow * ph.x_stride + g * 128;
-      const char* xs_lane = xs_lds + (size_t)arow * ph.nkb * XSUM_BYTES_PER_BLOCK + 16 * g;
+      const char* xs_lane = xs_lds + (size_t)arow * xsum_row_bytes(ph.nkb) + 16 * g;
       if (ph.nm == 2)
         phase_compute<2>(ring, it, ph_s[p], ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, k);
       else
@@ -1131,7 +1131,7 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
     for (;;) {
       int nkb = (ph.KB + sk - 1) / sk;
       size_t xb = (size_t)Mp * (nkb * X_BYTES_PER_BLOCK + X_ROW_PAD) +
-                  (size_t)Mp * nkb * XSUM_BYTES_PER_BLOCK;
+                  (size_t)Mp * xsum_row_bytes(nkb);
       const bool one_round = Mp * nkb * 32 <= STEP_THREADS * kStageRound;
       if ((xb <= 96 * 1024 && one_round) || nkb == 1) {
         ph.sk = (ph.KB + nkb - 1) / nkb;
@@ -1159,7 +1159,7 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
     }
     if (ph.tw_max < 1) ph.tw_max = 1;
     {
-      const size_t xb = (size_t)M * ph.x_stride + (size_t)M * ph.nkb * XSUM_BYTES_PER_BLOCK;
+      const size_t xb = (size_t)M * ph.x_stride + (size_t)M * xsum_row_bytes(ph.nkb);
       const size_t c0 = (xb + 15) & ~(size_t)15;
       ph.lds_contrib = (int)c0;
       ph.lds_bytes = (int)(c0 + (size_t)ph.tw_max * ph.cmax * ph.nm * 1024);
@@ -1404,7 +1404,7 @@ long long plan_violations(const mk_q4k_layer& L0, int n_layers, int M, int G) {
       check(a.kb0 >= 0 && a.kb0 + a.nkb <= ph.KB && a.nkb >= 1);
       // staging: rows m < M, columns of the slice, LDS rows of x_stride bytes
       check((size_t)(a.kb0 + a.nkb) * QK <= (size_t)ph.K);
-      check((size_t)M * ph.x_stride + (size_t)M * ph.nkb * XSUM_BYTES_PER_BLOCK <=
+      check((size_t)M * ph.x_stride + (size_t)M * xsum_row_bytes(ph.nkb) <=
             (size_t)ph.lds_contrib);
       check((size_t)(a.nkb - 1) * X_BYTES_PER_BLOCK + 3 * 128 + 7 * 16 + 16 <=
             (size_t)ph.x_stride);
