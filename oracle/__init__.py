@@ -108,6 +108,8 @@ def _load():
         lib.oracle_q6k_gemm.argtypes = [vp, vp, i64, i64, i64, vp, vp]
         lib.oracle_gemm_std.restype = ctypes.c_int
         lib.oracle_gemm_std.argtypes = [vp, vp, i64, i64, i64, ctypes.c_double, vp, vp]
+        lib.oracle_q6k_gemm_std.restype = ctypes.c_int
+        lib.oracle_q6k_gemm_std.argtypes = [vp, vp, i64, i64, i64, ctypes.c_double, vp, vp]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_standardize.restype = None
@@ -261,6 +263,27 @@ def gemm_std(W: np.ndarray, X: np.ndarray, eps: float = 1e-6) -> tuple[np.ndarra
                                  y.ctypes.data, S.ctypes.data)
     if rc != 0:
         raise RuntimeError(f"oracle_gemm_std failed ({rc})")
+    return y, S
+
+
+def q6k_gemm_std(W: np.ndarray, X: np.ndarray, eps: float = 1e-6) -> tuple[np.ndarray, np.ndarray]:
+    """As gemm_std for Q6_K rows W (uint8 [ncols, K/256*210]): the reference of
+    a Q6_K matrix (v or down of a Q4_K_M layer) in the layer walk."""
+    X = np.asarray(X)
+    if X.dtype != np.float16:
+        raise TypeError("X must be float16")
+    M, K = X.shape
+    if K % QK:
+        raise ValueError("K must be a multiple of 256")
+    W = _c(W, np.uint8).reshape(-1, K // QK * Q6K_BLOCK_BYTES)
+    ncols = W.shape[0]
+    xb = _c(X.view(np.uint16), np.uint16)
+    y = np.empty((M, ncols), dtype=np.float64)
+    S = np.empty((M, ncols), dtype=np.float64)
+    rc = _load().oracle_q6k_gemm_std(W.ctypes.data, xb.ctypes.data, M, ncols, K, eps,
+                                     y.ctypes.data, S.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_q6k_gemm_std failed ({rc})")
     return y, S
 
 

@@ -392,6 +392,29 @@ int oracle_q6k_gemm(const uint8_t* W, const uint16_t* X, int64_t M, int64_t ncol
   return err;
 }
 
+/* Reference for a Q6_K matrix of the layer walk (a Q4_K_M file keeps v and
+ * down in Q6_K in some layers): as oracle_gemm_std, the product of the
+ * row-wise standardized binary16 input with the weights, here Q6_K rows
+ * (oracle_q6k_dequant_block), everything in double. */
+int oracle_q6k_gemm_std(const uint8_t* W, const uint16_t* X, int64_t M, int64_t ncols, int64_t K,
+                        double eps, double* y, double* S) {
+  if (K % ORACLE_QK) return -1;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
+  double* t = (double*)malloc(sizeof(double) * (size_t)(M * K));
+  if (!xd || !t) {
+    free(xd);
+    free(t);
+    return -2;
+  }
+  for (int64_t i = 0; i < M * K; ++i) xd[i] = oracle_f16_to_f64(X[i]);
+  oracle_standardize(xd, M, K, eps, t);
+  int err = gemm_f64_rows(W, K / ORACLE_QK * ORACLE_Q6K_BLOCK_BYTES, oracle_q6k_dequant_row, t, M,
+                          ncols, K, y, S);
+  free(xd);
+  free(t);
+  return err;
+}
+
 /* ---- decode attention over a paged q8_0 KV pool ----------------------------
  * A page holds 16 tokens; page p, KV head h is 4352 bytes at (p*n_kv + h)*4352:
  * an int8 quant per K and V value and a binary16 scale per token and 32-dim

@@ -802,3 +802,41 @@ def test_attn_empty_rows_are_the_empty_sum():
                               np.array([0, -3, 17, 1], dtype=np.int32), 1)
     assert np.all(O[:2] == 0) and np.all(S[:2] == 0)
     assert np.all(S[2:] > 0)
+
+
+# --- Q6_K matrices of the layer walk: the standardized product ----------------
+def test_q6k_gemm_std_shift_and_scale_invariance():
+    """As for Q4_K: the Q6_K walk reference depends on the input only through
+    its row-standardized form, so a per-row offset and a positive per-row
+    scale (exact on a coarse binary16 grid) change it only through eps."""
+    M, N, K = 3, 13, 768
+    W = synth.q6k_matrix(synth.key(15, 14, N, K), N, K)
+    rng = np.random.default_rng(15)
+    base = rng.integers(-64, 65, size=(M, K)).astype(np.float64) / 16.0
+    y, S = oracle.q6k_gemm_std(W, base.astype(np.float16))
+    for shift, scale in ((3.0, 1.0), (-5.5, 1.0), (0.0, 2.0), (1.25, 4.0)):
+        X2 = ((base + shift) * scale).astype(np.float16)
+        assert np.array_equal(X2.astype(np.float64), (base + shift) * scale)
+        y2, S2 = oracle.q6k_gemm_std(W, X2)
+        var = base.var(axis=1, keepdims=True)
+        f = np.sqrt((var + 1e-6) / (scale * scale * var + 1e-6)) * scale
+        assert np.all(np.abs(y2 - y * f) <= 1e-12 * S2), (shift, scale)
+        assert np.allclose(S2, S * f, rtol=1e-12), (shift, scale)
+
+
+def test_q6k_gemm_std_alternating_row_and_constant_row():
+    """A row of +s, -s, ... standardizes to +-s / sqrt(s^2 + eps): the product
+    is that factor times the plain Q6_K product of the +-1 row (pinned by the
+    hand-built blocks above); a constant row standardizes to zeros."""
+    M, N, K = 3, 9, 512
+    W = synth.q6k_matrix(synth.key(16, 14, N, K), N, K)
+    z = np.where(np.arange(K) % 2 == 0, 1.0, -1.0)
+    for s in (0.5, 3.0, 1e-3):
+        X = np.stack([z * s, -z * s, np.full(K, 2.5)]).astype(np.float16)
+        sv = float(X.astype(np.float64)[0, 0])
+        y, S = oracle.q6k_gemm_std(W, X)
+        yz, Sz = oracle.q6k_gemm(W, np.stack([z, -z, np.zeros(K)]).astype(np.float16))
+        f = abs(sv) / np.sqrt(sv * sv + 1e-6)
+        assert np.all(np.abs(y[:2] - f * yz[:2]) <= 1e-12 * S[:2] + 1e-300), s
+        assert np.allclose(S[:2], f * Sz[:2], rtol=1e-12), s
+        assert np.all(y[2] == 0.0) and np.all(S[2] == 0.0)
