@@ -76,8 +76,13 @@ def build() -> str:
     return LIB_PATH
 
 
+MK_QTYPE_Q4_K = 12
+MK_QTYPE_Q6_K = 14
+
+
 class _Mat(ctypes.Structure):
-    _fields_ = [("w", ctypes.c_void_p), ("N", ctypes.c_int), ("K", ctypes.c_int)]
+    _fields_ = [("w", ctypes.c_void_p), ("N", ctypes.c_int), ("K", ctypes.c_int),
+                ("type", ctypes.c_int)]
 
 
 class _Layer(ctypes.Structure):
@@ -137,6 +142,10 @@ def lib():
         L.mk_q6k_tiles_bytes.argtypes = [i, i]
         L.mk_q6k_repack.restype = i
         L.mk_q6k_repack.argtypes = [vp, vp, i, i, vp]
+        L.mk_q6k_step_bytes.restype = sz
+        L.mk_q6k_step_bytes.argtypes = [i, i]
+        L.mk_q6k_step_repack.restype = i
+        L.mk_q6k_step_repack.argtypes = [vp, vp, i, i, vp]
         L.mk_q6k_gemm_tiled.restype = i
         L.mk_q6k_gemm_tiled.argtypes = [vp, vp, vp, i, i, i, vp]
         if hasattr(L, "mk_q4k_step"):
@@ -312,6 +321,28 @@ def q6k_repack(W, N: int, K: int, out=None, stream=None):
     return out
 
 
+def q6k_step_bytes(N: int, K: int) -> int:
+    """Bytes of the walk-record form of an N x K Q6_K matrix (records + column sums)."""
+    return int(lib().mk_q6k_step_bytes(N, K))
+
+
+def q6k_step_repack(W, N: int, K: int, out=None, stream=None):
+    """Walk-record form (uint8 device tensor) of the Q6_K rows W (device), for a
+    step matrix of type MK_QTYPE_Q6_K."""
+    import torch
+    nbytes = q6k_step_bytes(N, K)
+    if nbytes == 0:
+        raise MkError(MK_EINVAL, "invalid shape")
+    if W.dtype != torch.uint8 or W.numel() != N * (K // QK) * Q6K_BLOCK_BYTES or not W.is_contiguous():
+        raise MkError(MK_EINVAL, "W must be contiguous uint8 Q6_K rows")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    elif out.numel() * out.element_size() < nbytes or not out.is_contiguous():
+        raise MkError(MK_EINVAL, "out too small")
+    _check(lib().mk_q6k_step_repack(_ptr(W), _ptr(out), N, K, _stream(stream)))
+    return out
+
+
 def q6k_gemm_tiled(Wt, X, N: int, out=None, stream=None):
     """Y = X * W^T with the Q6_K matrix W in tile-record form (q6k_repack()); N columns."""
     import torch
@@ -335,8 +366,10 @@ def _layers_struct(layers):
     arr = (_Layer * len(layers))()
     for i, lay in enumerate(layers):
         for name in MATRIX_NAMES:
-            w, n, k = lay[name]
-            setattr(arr[i], name, _Mat(_ptr(w) if not isinstance(w, int) else w, n, k))
+            # (W, N, K) for a Q4_K matrix, (W, N, K, type) in general
+            w, n, k, *t = lay[name]
+            qt = t[0] if t else MK_QTYPE_Q4_K
+            setattr(arr[i], name, _Mat(_ptr(w) if not isinstance(w, int) else w, n, k, qt))
     return arr
 
 

@@ -454,3 +454,122 @@ __device__ __forceinline__ void mma_unit_mt(const BlockRegs& r, int g, const cha
 }
 
 }  // namespace mk
+
+namespace mk {
+
+// ---- Q6_K matrices inside the decode-step walk
+//
+// Q6_K (the other k-quant a Q4_K_M file holds, for attn_v and ffn_down):
+// 256 weights in 210 bytes per row and block, ql[128] low nibbles, qh[64]
+// high bit pairs, 16 int8 run scales, binary16 d; weight k (half h = k/128,
+// quarter j = (k % 128) / 32, place l = k % 32) has low bits nibble j/2 of
+// ql[64h + 32 (j % 2) + l], high bits 2j..2j+1 of qh[32h + l], q = low |
+// high << 4 and value d * sc[k / 16] * (q - 32).
+//
+// The walk stages its activations once per phase in the MFMA order of the
+// Q4_K product (16x16x32: lane l = 16 g + c takes row c and the 64 weights
+// [64g, 64g+64) of each block), so a Q6_K matrix in the walk is repacked at
+// load time (mk_q6k_step_repack) into records of 16 rows x one block in that
+// same lane order, 3360 bytes (16 x 210, nothing added):
+//   [0, 1024)     lane l: bytes i = 0..15: low nibble = low bits of weight
+//                 64g + i, high nibble = of weight 64g + 32 + i
+//   [1024, 2048)  lane l: the same for weights 64g + 16 + i, 64g + 48 + i
+//   [2048, 3072)  lane l: high bit pairs, 16 bytes: byte 4m + b holds, in
+//                 bits 0-1, 2-3, 4-5 and 6-7, those of weights 64g + 8m + b,
+//                 64g + 32 + 8m + b, 64g + 8m + 4 + b, 64g + 36 + 8m + b
+//   [3072, 3328)  lane l: the int8 scales of runs 4g .. 4g+3 of row c
+//   [3328, 3360)  row c's d at 3328 + 2c
+// followed, after all records, by the column sums like the Q4_K records.
+constexpr int Q6W_REC = 3360;
+
+// A lane's operands of one Q6_K walk record: the quant and high-bit dwords
+// in the registers of a Q4_K ring slot (BlockRegs: h = low bits of quant
+// dwords 0-3, q0 = of 4-7, q1 = high bit pairs, dword m for quant dwords 2m
+// and 2m+1), so that a walk's Q6_K records stream through the same ring;
+// plus the lane's run scales and its row's d.
+struct ScaleRegs6 {
+  uint32_t sc;  // int8 scales of runs 4g .. 4g+3
+  uint32_t d;   // binary16 d of the lane's row (low half)
+};
+
+__device__ __forceinline__ void load_rec6(BlockRegs& r, ScaleRegs6& s, const uint8_t* rec,
+                                          int lane) {
+  typedef __attribute__((address_space(1))) const u32x4 g4;
+  typedef __attribute__((address_space(1))) const uint32_t g1;
+  typedef __attribute__((address_space(1))) const uint16_t gh;
+  const auto g = to_global(rec);
+  r.h = __builtin_nontemporal_load(reinterpret_cast<g4*>(g) + lane);
+  r.q0 = __builtin_nontemporal_load(reinterpret_cast<g4*>(g + 1024) + lane);
+  r.q1 = __builtin_nontemporal_load(reinterpret_cast<g4*>(g + 2048) + lane);
+  s.sc = __builtin_nontemporal_load(reinterpret_cast<g1*>(g + 3072) + lane);
+  s.d = __builtin_nontemporal_load(reinterpret_cast<gh*>(g + 3328) + (lane & 15));
+}
+
+// binary16 (1024 + q) of the bytes (0, 2) and (1, 3) of a dword of 6-bit codes,
+// as two pairs: the MFMA element order 0, 2, 1, 3 within four weights.
+__device__ __forceinline__ void q6_codes_f16(uint32_t q, uint32_t& p02, uint32_t& p13) {
+  p02 = __builtin_amdgcn_perm(0x64646464u, q, 0x04020400u);
+  p13 = __builtin_amdgcn_perm(0x64646464u, q, 0x04030401u);
+}
+
+// B operands (hi and lo parts) of one 16x16x32 MFMA from the 8 weights of
+// quant dwords ve, vo with their high bits already in bits 4-5 of each byte
+// (codes qe, qo): s * (q - 32) for scale pair s, split as hi = fl(s * t)
+// plus lo = s * t - hi (exact with one fused multiply-add: the integers
+// s * t <= 4096 in magnitude leave a rounding error of at most 1), so the two
+// MFMAs together multiply by the exact scaled weight.
+__device__ __forceinline__ void q6_operands(uint32_t qe, uint32_t qo, half2v s, half8v& hi,
+                                            half8v& lo) {
+  uint32_t f[4];
+  q6_codes_f16(qe, f[0], f[1]);
+  q6_codes_f16(qo, f[2], f[3]);
+  const half2v off = {(_Float16)1056.0f, (_Float16)1056.0f};
+  half2v h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2v t = bit_cast_<half2v>(f[i]) - off;  // q - 32, exact
+    h[i] = t * s;
+    l[i] = __builtin_elementwise_fma(t, s, -h[i]);
+  }
+  hi = half8v{h[0].x, h[0].y, h[1].x, h[1].y, h[2].x, h[2].y, h[3].x, h[3].y};
+  lo = half8v{l[0].x, l[0].y, l[1].x, l[1].y, l[2].x, l[2].y, l[3].x, l[3].y};
+}
+
+// One 16-row tile of staged activations (xa: this lane's 128 LDS bytes of
+// the block, as for Q4_K) against one Q6_K walk record: for each step u the
+// lower MFMA takes weights 64g + 8u + (0..7) (run 4g + u/2), the upper
+// 64g + 32 + 8u + (0..7) (run 4g + 2 + u/2); acc += d * (sum of both chains).
+__device__ __forceinline__ void mma_unit6(const BlockRegs& r, const ScaleRegs6& rs,
+                                          const char* xa, floatx4& acc) {
+  half2v sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const _Float16 v = (_Float16)(float)(int)(int8_t)(rs.sc >> (8 * i));
+    sc[i] = half2v{v, v};
+  }
+  floatx4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t ve = u == 0 ? r.h.x : u == 1 ? r.h.z : u == 2 ? r.q0.x : r.q0.z;
+    const uint32_t vo = u == 0 ? r.h.y : u == 1 ? r.h.w : u == 2 ? r.q0.y : r.q0.w;
+    const uint32_t H = u == 0 ? r.q1.x : u == 1 ? r.q1.y : u == 2 ? r.q1.z : r.q1.w;
+    const uint32_t m4 = 0x0F0F0F0Fu, m2 = 0x30303030u;
+    const uint32_t qle = (ve & m4) | ((H << 4) & m2), qlo = (vo & m4) | (H & m2);
+    const uint32_t qhe = ((ve >> 4) & m4) | ((H << 2) & m2), qho = ((vo >> 4) & m4) | ((H >> 2) & m2);
+    const half8v a_lo = *reinterpret_cast<const half8v*>(xa + 32 * u);
+    const half8v a_hi = *reinterpret_cast<const half8v*>(xa + 32 * u + 16);
+    half8v bh, bl;
+    q6_operands(qle, qlo, sc[u >> 1], bh, bl);
+    c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, bh, c0, 0, 0, 0);
+    c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, bl, c0, 0, 0, 0);
+    q6_operands(qhe, qho, sc[2 + (u >> 1)], bh, bl);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, bh, c1, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, bl, c1, 0, 0, 0);
+  }
+  const float d = (float)bit_cast_<_Float16>((uint16_t)rs.d);
+  const floatx4 dd = {d, d, d, d};
+  acc = __builtin_elementwise_fma(dd, c0, acc);
+  acc = __builtin_elementwise_fma(dd, c1, acc);
+}
+
+}  // namespace mk

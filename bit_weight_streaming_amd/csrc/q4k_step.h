@@ -76,6 +76,7 @@ struct DevPhase {
   unsigned part_bytes;
   unsigned cs_off[3];  // byte offset of each segment matrix's column sums
                        // in its tile-record buffer (after the records)
+  unsigned cs_off6[3]; // the same for a Q6_K matrix (its records are larger)
   double inv_k;        // 1 / K (the row statistics of the input run over K)
   int norm;            // what the products of the phase are scaled by per row:
                        // NORM_STD, NORM_RMS or NORM_NONE
@@ -102,6 +103,8 @@ struct DevLayer {
   uint16_t* x[4];
   float* h[2];        // residual walk: fp32 residual after o (h[0]) and after down (h[1])
   const float* g[2];  // residual walk: RMSNorm weights before q/k/v (g[0]) and gate/up (g[1])
+  uint32_t q6;        // bit t: matrix t is in the Q6_K walk-record form (v, down only)
+  uint32_t pad_;
 };
 
 struct StepParams {

@@ -157,26 +157,40 @@ struct Iter {
   int tg;       // tile (phase numbering)
   int seg_end;  // first tile of the next segment
   unsigned stride;  // bytes from one tile's records to the next
+  unsigned rec;     // bytes of one record of the current segment (Q6 walks)
   const uint8_t* base[2];  // record (tg, super-block a.kb0) of each matrix
 };
 
-// The 7 weight pointers of one layer (an LDS copy of the layer table).
-typedef const uint8_t* const* WPtrs;
+// One layer's entry of the layer table (an LDS copy): its 7 weight pointers
+// and which of them are Q6_K.
+typedef const DevLayer* WPtrs;
 
+// Record bytes of matrix mi of layer L: Q4_K tile records, or (in a walk
+// built for Q6_K, Q6) the Q6_K walk records.
+template <bool Q6>
+__device__ __forceinline__ unsigned rec_bytes(WPtrs L, int mi) {
+  if constexpr (Q6) return (uni((int)L->q6) >> mi) & 1 ? (unsigned)Q6W_REC : (unsigned)TILE_REC;
+  return TILE_REC;
+}
+
+template <bool Q6>
 __device__ __forceinline__ void iter_tile(Iter& it, const DevPhase& ph, WPtrs L,
                                           const Assign& a) {
   const int seg = seg_of(ph, it.tg);
-  const size_t off = (size_t)(it.tg - uni(ph.seg_t0[seg])) * it.stride +
-                     (size_t)a.kb0 * TILE_REC;
   const int mi = uni(ph.mat0) + seg;
+  const unsigned rec = rec_bytes<Q6>(L, mi);
+  it.rec = rec;
+  it.stride = (unsigned)uni(ph.KB) * rec;
+  const size_t off = (size_t)(it.tg - uni(ph.seg_t0[seg])) * it.stride + (size_t)a.kb0 * rec;
   it.seg_end = uni(ph.seg_t0[seg + 1]);
-  it.base[0] = uni(L[mi]) + off;
-  it.base[1] = uni(ph.nm) == 2 ? uni(L[mi + 1]) + off : it.base[0];
+  it.base[0] = uni(L->w[mi]) + off;
+  it.base[1] = uni(ph.nm) == 2 ? uni(L->w[mi + 1]) + off : it.base[0];
 }
 
 // Start of a wave's walk from st = (first unit, end unit, tile, super-block)
-// and sp = (matrix of that tile, record offset, first tile of the next
+// and sp = (matrix of that tile, record index in it, first tile of the next
 // segment), all computed once per launch.
+template <bool Q6>
 __device__ __forceinline__ void iter_init(Iter& it, const DevPhase& ph, WPtrs L,
                                           const int4& st, const int4& sp) {
   it.u = uni(st.x);
@@ -184,18 +198,22 @@ __device__ __forceinline__ void iter_init(Iter& it, const DevPhase& ph, WPtrs L,
   it.q = 0;
   it.tg = uni(st.z);
   it.b = uni(st.w);
-  it.stride = (unsigned)uni(ph.KB) * TILE_REC;
-  it.seg_end = uni(sp.z);
   const int mi = uni(sp.x);
-  const unsigned off = (unsigned)uni(sp.y);
-  it.base[0] = uni(L[mi]) + off;
-  it.base[1] = uni(ph.nm) == 2 ? uni(L[mi + 1]) + off : it.base[0];
+  const unsigned rec = rec_bytes<Q6>(L, mi);
+  it.rec = rec;
+  it.stride = (unsigned)uni(ph.KB) * rec;
+  it.seg_end = uni(sp.z);
+  const unsigned off = (unsigned)uni(sp.y) * rec;
+  it.base[0] = uni(L->w[mi]) + off;
+  it.base[1] = uni(ph.nm) == 2 ? uni(L->w[mi + 1]) + off : it.base[0];
 }
 
+template <bool Q6>
 __device__ __forceinline__ const uint8_t* iter_addr(const Iter& it) {
-  return (it.q ? it.base[1] : it.base[0]) + (unsigned)it.b * TILE_REC;
+  return (it.q ? it.base[1] : it.base[0]) + (unsigned)it.b * (Q6 ? it.rec : (unsigned)TILE_REC);
 }
 
+template <bool Q6>
 __device__ __forceinline__ void iter_next(Iter& it, const DevPhase& ph, WPtrs L,
                                           const Assign& a) {
   const int nm = uni(ph.nm);
@@ -212,21 +230,41 @@ __device__ __forceinline__ void iter_next(Iter& it, const DevPhase& ph, WPtrs L,
     it.base[0] += it.stride;
     it.base[1] += it.stride;
   } else {
-    iter_tile(it, ph, L, a);
+    iter_tile<Q6>(it, ph, L, a);
   }
+}
+
+// First unit (of the workgroup's split a) in a Q6_K matrix of layer L in
+// phase ph, or a.U when none: Q6_K is allowed only for v (the last segment of
+// phase A) and down (phase D), so such units are always the split's tail.
+template <bool Q6>
+__device__ __forceinline__ int q6_first_unit(const DevPhase& ph, WPtrs L, const Assign& a) {
+  if constexpr (!Q6) return a.U;
+  const int q6 = uni((int)L->q6);
+  const int m0 = uni(ph.mat0), ns = uni(ph.nseg);
+  for (int s = 0; s < ns; ++s) {
+    if ((q6 >> (m0 + s)) & 1) {
+      const int u = (uni(ph.seg_t0[s]) - a.t0) * a.nkb;
+      return u < 0 ? 0 : (u > a.U ? a.U : u);
+    }
+  }
+  return a.U;
 }
 
 // Issue a phase's first STEP_PD weight records of the wave (fewer if the
 // wave has fewer) into ring slots 0.., before the phase's input is ready.
+template <bool Q6>
 __device__ __forceinline__ void ring_fill(BlockRegs (&ring)[STEP_PD], Iter& it,
                                           const DevPhase& ph, WPtrs L, const Assign& a,
                                           int lane) {
-  const int nrec = (it.ub - it.u) * uni(ph.nm);
+  // Q4_K records only: a wave's Q6_K tail fills its own ring when it gets there
+  const int u6 = q6_first_unit<Q6>(ph, L, a);
+  const int nrec = ((it.ub < u6 ? it.ub : u6) - it.u) * uni(ph.nm);
 #pragma unroll
   for (int s = 0; s < STEP_PD; ++s) {
     if (s < nrec) {
-      load_rec(ring[s], iter_addr(it), lane);
-      iter_next(it, ph, L, a);
+      load_rec(ring[s], iter_addr<Q6>(it), lane);
+      iter_next<Q6>(it, ph, L, a);
     }
   }
 }
@@ -237,7 +275,7 @@ __device__ __forceinline__ void ring_fill(BlockRegs (&ring)[STEP_PD], Iter& it,
 // on); a tile shared with other waves leaves its part in the LDS contribution
 // slot (tile, wave - first wave of the tile). Per lane one floatx4: rows
 // 4*(lane/16)+r, column lane%16.
-template <int NM>
+template <int NM, bool Q6>
 __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& it,
                                               const DevPhase& ph, WPtrs L,
                                               const Assign& a, int wave, int lane,
@@ -245,8 +283,12 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
                                               char* contrib, const UnpackConsts& k) {
   const int g = lane >> 4;
   const int ua = wave_begin(a, wave), ub = wave_begin(a, wave + 1);
-  const int U = (ub - ua) * NM;  // records
-  if (U <= 0) return;
+  // units [ua, u4) are Q4_K, [u4, ub) Q6_K (a Q6_K matrix is always the
+  // phase's tail, and its phase has one record per unit)
+  const int u6 = q6_first_unit<Q6>(ph, L, a);
+  const int u4 = ub < u6 ? ub : (ua > u6 ? ua : u6);
+  const int U = (u4 - ua) * NM;  // Q4_K records
+  if (U <= 0 && (!Q6 || u4 >= ub)) return;
   floatx4 acc[NM];
 #pragma unroll
   for (int q = 0; q < NM; ++q) acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -262,9 +304,9 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
       acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
   };
-  auto consume = [&](int s) {
-    mma_unit<NM>(&ring[s], g, xa_lane + cb * X_BYTES_PER_BLOCK, xs_lane + cb * XSUM_BYTES_PER_BLOCK,
-                 k, acc);
+  // after the product of unit cu: the tile's part goes out when the tile or
+  // the wave's range ends
+  auto advance = [&]() {
     ++cu;
     if (++cb == a.nkb || cu == ub) {
       flush();
@@ -273,6 +315,11 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
         ++ctl;
       }
     }
+  };
+  auto consume = [&](int s) {
+    mma_unit<NM>(&ring[s], g, xa_lane + cb * X_BYTES_PER_BLOCK, xs_lane + cb * XSUM_BYTES_PER_BLOCK,
+                 k, acc);
+    advance();
   };
   // Record r sits in ring slot r % STEP_PD; once consumed, its slot takes
   // record r + STEP_PD, if the wave has one (no load past the range). In the
@@ -285,8 +332,8 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
       consume(s);
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
-        load_rec(ring[s + q], iter_addr(it), lane);
-        iter_next(it, ph, L, a);
+        load_rec(ring[s + q], iter_addr<Q6>(it), lane);
+        iter_next<Q6>(it, ph, L, a);
       }
     }
   }
@@ -298,8 +345,50 @@ __device__ __forceinline__ void phase_compute(BlockRegs (&ring)[STEP_PD], Iter& 
       if (r0 + s + STEP_PD < U) {
 #pragma unroll
         for (int q = 0; q < NM; ++q) {
-          load_rec(ring[s + q], iter_addr(it), lane);
-          iter_next(it, ph, L, a);
+          load_rec(ring[s + q], iter_addr<Q6>(it), lane);
+          iter_next<Q6>(it, ph, L, a);
+        }
+      }
+    }
+  }
+  if constexpr (Q6) {
+    // the Q6_K tail, through the same ring slots (the Q4_K records are all
+    // used), refilled here: the iterator stands at the first Q6_K record
+    // once the Q4_K records are all loaded
+    if constexpr (NM == 1) {
+      const int U6 = ub - u4;
+      if (U6 > 0) {
+        ScaleRegs6 s6[STEP_PD];
+#pragma unroll
+        for (int s = 0; s < STEP_PD; ++s) {
+          if (s < U6) {
+            load_rec6(ring[s], s6[s], iter_addr<Q6>(it), lane);
+            iter_next<Q6>(it, ph, L, a);
+          }
+        }
+        auto consume6 = [&](int s) {
+          mma_unit6(ring[s], s6[s], xa_lane + cb * X_BYTES_PER_BLOCK, acc[0]);
+          advance();
+        };
+        int q0 = 0;
+        for (; q0 + 2 * STEP_PD <= U6; q0 += STEP_PD) {
+#pragma unroll
+          for (int s = 0; s < STEP_PD; ++s) {
+            consume6(s);
+            load_rec6(ring[s], s6[s], iter_addr<Q6>(it), lane);
+            iter_next<Q6>(it, ph, L, a);
+          }
+        }
+        for (; q0 < U6; q0 += STEP_PD) {
+#pragma unroll
+          for (int s = 0; s < STEP_PD; ++s) {
+            if (q0 + s >= U6) break;
+            consume6(s);
+            if (q0 + s + STEP_PD < U6) {
+              load_rec6(ring[s], s6[s], iter_addr<Q6>(it), lane);
+              iter_next<Q6>(it, ph, L, a);
+            }
+          }
         }
       }
     }
@@ -632,10 +721,11 @@ __device__ __forceinline__ void load_colsum(const DevPhase& ph, const DevLayer* 
                                             float* csum) {
   const int seg = __builtin_amdgcn_readfirstlane(seg_of(ph, tg));
   const int cs = (tg - ph.seg_t0[seg]) * 16 + (ln & 15);
+  const int mi = ph.mat0 + seg;
+  const unsigned off = (uni((int)L->q6) >> mi) & 1 ? ph.cs_off6[seg] : ph.cs_off[seg];
 #pragma unroll
   for (int q = 0; q < NM; ++q)
-    csum[q] = to_global(reinterpret_cast<const float*>(L->w[ph.mat0 + seg + q] +
-                                                       ph.cs_off[seg]))[cs];
+    csum[q] = to_global(reinterpret_cast<const float*>(L->w[mi + q] + off))[cs];
 }
 
 // The next phase's input buffer (binary16 [M][Kn]) and the statistics slots
@@ -839,8 +929,10 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
 }  // namespace
 
 // MODE 0: the walk of standardized products between binary16 casts; MODE 1:
-// the residual walk (RMSNorm with weights, residual adds, SiLU * up).
-template <int MODE>
+// the residual walk (RMSNorm with weights, residual adds, SiLU * up). Q6: the
+// walk also reads Q6_K walk records (v and down of the layers that have them);
+// without it the kernel holds no Q6_K code at all.
+template <int MODE, bool Q6>
 __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ DevLayer ltab[STEP_MAX_LAYERS];  // every layer's pointers, read from LDS
@@ -892,9 +984,10 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
     const int seg = (tg >= ph.seg_t0[1]) + (tg >= ph.seg_t0[2]);
     wstart[q][v] = int4{u, ub, tg, u - tl * x.nkb};
     // a wave with no units keeps the phase's first matrix (never read)
+    // (the record index; its size depends on the matrix's type in each layer)
     wseg[q][v] = u < ub ? int4{ph.mat0 + seg,
-                               (int)((unsigned)(tg - ph.seg_t0[seg]) * (unsigned)ph.KB * TILE_REC +
-                                     (unsigned)x.kb0 * TILE_REC),
+                               (int)((unsigned)(tg - ph.seg_t0[seg]) * (unsigned)ph.KB +
+                                     (unsigned)x.kb0),
                                ph.seg_t0[seg + 1], 0}
                         : int4{ph.mat0, 0, ph.nt, 0};
   }
@@ -911,8 +1004,8 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   BlockRegs ring[STEP_PD];
   Iter it;
   Assign a = lds_assign(asg[0]);
-  iter_init(it, ph_s[0], ltab[0].w, wstart[0][wave], wseg[0][wave]);
-  ring_fill(ring, it, ph_s[0], ltab[0].w, a, lane);
+  iter_init<Q6>(it, ph_s[0], &ltab[0], wstart[0][wave], wseg[0][wave]);
+  ring_fill<Q6>(ring, it, ph_s[0], &ltab[0], a, lane);
 
   // ---- layer-0 input: this workgroup's columns of it (MODE 0: a copy of
   //      x0; MODE 1: the cast of h0 times the first norm weight) and their
@@ -990,9 +1083,11 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       const char* xa_lane = x_lds + (size_t)arow * ph.x_stride + g * 128;
       const char* xs_lane = xs_lds + (size_t)arow * xsum_row_bytes(ph.nkb) + 16 * g;
       if (ph.nm == 2)
-        phase_compute<2>(ring, it, ph_s[p], ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, k);
+        phase_compute<2, Q6>(ring, it, ph_s[p], &ltab[l], a, wave, lane, xa_lane, xs_lane,
+                             contrib, k);
       else
-        phase_compute<1>(ring, it, ph_s[p], ltab[l].w, a, wave, lane, xa_lane, xs_lane, contrib, k);
+        phase_compute<1, Q6>(ring, it, ph_s[p], &ltab[l], a, wave, lane, xa_lane, xs_lane,
+                             contrib, k);
       __syncthreads();
       tl_stamp(P, l, p, TL_COMPUTED);
 
@@ -1011,8 +1106,8 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       const int ln = p < 3 ? l : l + 1, pn = p < 3 ? p + 1 : 0;
       if (ln < P.n_layers) {
         a = lds_assign(asg[pn]);
-        iter_init(it, ph_s[pn], ltab[ln].w, wstart[pn][wave], wseg[pn][wave]);
-        ring_fill(ring, it, ph_s[pn], ltab[ln].w, a, lane);
+        iter_init<Q6>(it, ph_s[pn], &ltab[ln], wstart[pn][wave], wseg[pn][wave]);
+        ring_fill<Q6>(ring, it, ph_s[pn], &ltab[ln], a, lane);
       }
       if (!wait_done(P, PH, l, p, &abort_s)) return;
       tl_stamp(P, l, p, TL_DONE_SEEN);
@@ -1119,8 +1214,10 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
     ph.nt = t;
     ph.ncols = c;
     // column sums of segment s's matrix: after its tile records
-    for (int s = 0; s < 3; ++s)
+    for (int s = 0; s < 3; ++s) {
       ph.cs_off[s] = s < nseg ? (unsigned)((size_t)tiles_of(ph.seg_n[s]) * ph.KB * TILE_REC) : 0u;
+      ph.cs_off6[s] = s < nseg ? (unsigned)((size_t)tiles_of(ph.seg_n[s]) * ph.KB * Q6W_REC) : 0u;
+    }
     // K slices: at least 4, more while one slice of activations of the most
     // rows the walk takes (STEP_MAX_M, whatever M is: the slices, and so every
     // summation order, do not depend on the row count, and a row's results
@@ -1231,6 +1328,17 @@ int check_step_shapes(const mk_q4k_layer* layers, int n_layers, int M) {
         !same_shape(B.down, L.down))
       return MK_EINVAL;
   }
+  // block types: Q4_K everywhere, Q6_K allowed for v and down (Q4_K_M files)
+  for (int l = 0; l < n_layers; ++l) {
+    const mk_q4k_layer& B = layers[l];
+    const mk_q4k_mat* q4[5] = {&B.q, &B.k, &B.o, &B.gate, &B.up};
+    for (int i = 0; i < 5; ++i)
+      if (q4[i]->type != 0 && q4[i]->type != MK_QTYPE_Q4_K) return MK_EINVAL;
+    const mk_q4k_mat* q6[2] = {&B.v, &B.down};
+    for (int i = 0; i < 2; ++i)
+      if (q6[i]->type != 0 && q6[i]->type != MK_QTYPE_Q4_K && q6[i]->type != MK_QTYPE_Q6_K)
+        return MK_EINVAL;
+  }
   return MK_OK;
 }
 
@@ -1248,8 +1356,13 @@ std::mutex g_table_mu;
 // Plan of a walk over M rows (a row group), with the checks made before any
 // work is enqueued: the split, the workspace size, the LDS and occupancy.
 template <int MODE>
-int prepare_walk(const mk_q4k_layer* layers, int n_layers, int M, size_t ws_bytes, StepPlan& sp,
-                 size_t& lds, int& G) {
+const void* walk_kernel(bool q6) {
+  return q6 ? (const void*)q4k_step_kernel<MODE, true> : (const void*)q4k_step_kernel<MODE, false>;
+}
+
+template <int MODE>
+int prepare_walk(const mk_q4k_layer* layers, int n_layers, int M, size_t ws_bytes, bool q6,
+                 StepPlan& sp, size_t& lds, int& G) {
   int cus = 0;
   const int rc = current_gfx950(&cus);
   if (rc != MK_OK) return rc;
@@ -1266,12 +1379,11 @@ int prepare_walk(const mk_q4k_layer* layers, int n_layers, int M, size_t ws_byte
   }
   lds = lds_bytes(sp, M);
   if (lds + kStaticLds > kLdsLimit) return MK_EINVAL;
-  hipError_t e = hipFuncSetAttribute((const void*)q4k_step_kernel<MODE>,
+  hipError_t e = hipFuncSetAttribute(walk_kernel<MODE>(q6),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return MK_EHIP;
   int occ = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)q4k_step_kernel<MODE>,
-                                                   STEP_THREADS, lds);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, walk_kernel<MODE>(q6), STEP_THREADS, lds);
   if (e != hipSuccess) return MK_EHIP;
   if (occ < 1) return MK_EOCCUPANCY;
   return MK_OK;
@@ -1284,7 +1396,7 @@ int prepare_walk(const mk_q4k_layer* layers, int n_layers, int M, size_t ws_byte
 template <int MODE>
 int enqueue_walk(const mk_q4k_layer* layers, const std::vector<DevLayer>& table, int n_layers,
                  int M, const uint16_t* x0, uint16_t* x_out, const float* h0, void* workspace,
-                 const StepPlan& sp, size_t lds, int G, int group, void* stream) {
+                 const StepPlan& sp, size_t lds, int G, int group, bool q6, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const size_t table_off = sp.layers_off + (size_t)group * n_layers * sizeof(DevLayer);
@@ -1336,9 +1448,19 @@ int enqueue_walk(const mk_q4k_layer* layers, const std::vector<DevLayer>& table,
   P.status_off = sp.status_off;
   P.lds_bytes = lds;
   P.tl_off = sp.tl_off;
-  hipLaunchKernelGGL(q4k_step_kernel<MODE>, dim3(G), dim3(STEP_THREADS), lds, st, P);
+  if (q6)
+    hipLaunchKernelGGL((q4k_step_kernel<MODE, true>), dim3(G), dim3(STEP_THREADS), lds, st, P);
+  else
+    hipLaunchKernelGGL((q4k_step_kernel<MODE, false>), dim3(G), dim3(STEP_THREADS), lds, st, P);
   e = hipGetLastError();
   return e == hipSuccess ? MK_OK : MK_EHIP;
+}
+
+// Whether any matrix of the walk is Q6_K (then the kernel built for it runs).
+bool any_q6(const mk_q4k_layer* layers, int n_layers) {
+  for (int l = 0; l < n_layers; ++l)
+    if (layers[l].v.type == MK_QTYPE_Q6_K || layers[l].down.type == MK_QTYPE_Q6_K) return true;
+  return false;
 }
 
 // Rows [r0, r0 + STEP_MAX_M) of the call: row group r0 / STEP_MAX_M.
@@ -1372,6 +1494,7 @@ void fill_table(const mk_q4k_layer& L, float* const* y, uint16_t* const* x, int 
   for (int i = 0; i < 7; ++i) {
     t.w[i] = static_cast<const uint8_t*>(m[i]->w);
     t.y[i] = y[i] + (size_t)r0 * m[i]->N;
+    if (m[i]->type == MK_QTYPE_Q6_K) t.q6 |= 1u << i;
   }
   for (int i = 0; i < 4; ++i) t.x[i] = x[i] + (size_t)r0 * xw[i];
 }
@@ -1445,6 +1568,9 @@ long long plan_violations(const mk_q4k_layer& L0, int n_layers, int M, int G) {
         check(cs_max < tiles_of(ph.seg_n[seg]) * 16);
         check(ph.cs_off[seg] ==
               (unsigned)((size_t)tiles_of(ph.seg_n[seg]) * ph.KB * TILE_REC));
+        // the same matrix in the Q6_K walk-record form (v, down)
+        check(ph.cs_off6[seg] ==
+              (unsigned)((size_t)tiles_of(ph.seg_n[seg]) * ph.KB * Q6W_REC));
         check(seg > 0 || ph.seg_n[0] <= Kn);
       }
     }
@@ -1519,6 +1645,7 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
     rc = check_layer_io(layers, io[l].y, io[l].x, l);
     if (rc != MK_OK) return rc;
   }
+  const bool q6 = any_q6(layers, n_layers);
   // every row group's plan is checked before any work is enqueued (the
   // first group has the most rows)
   StepPlan sp;
@@ -1526,7 +1653,7 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
   int G = 0;
   const int groups = (M + STEP_MAX_M - 1) / STEP_MAX_M;
   for (int g = groups - 1; g >= 0; --g) {
-    rc = prepare_walk<0>(layers, n_layers, group_rows(M, g), ws_bytes, sp, lds, G);
+    rc = prepare_walk<0>(layers, n_layers, group_rows(M, g), ws_bytes, q6, sp, lds, G);
     if (rc != MK_OK) return rc;
   }
   const int H = layers[0].q.K;
@@ -1534,10 +1661,10 @@ int mk_q4k_step(const mk_q4k_layer* layers, const mk_q4k_layer_io* io, int n_lay
   for (int g = 0; g < groups; ++g) {
     const int r0 = g * STEP_MAX_M, Mg = group_rows(M, g);
     for (int l = 0; l < n_layers; ++l) fill_table(layers[l], io[l].y, io[l].x, r0, table[l]);
-    rc = prepare_walk<0>(layers, n_layers, Mg, ws_bytes, sp, lds, G);
+    rc = prepare_walk<0>(layers, n_layers, Mg, ws_bytes, q6, sp, lds, G);
     if (rc != MK_OK) return rc;
     rc = enqueue_walk<0>(layers, table, n_layers, Mg, x0 + (size_t)r0 * H, x_out + (size_t)r0 * H,
-                         nullptr, workspace, sp, lds, G, g, stream);
+                         nullptr, workspace, sp, lds, G, g, q6, stream);
     if (rc != MK_OK) return rc;
   }
   return MK_OK;
@@ -1559,12 +1686,13 @@ int mk_q4k_step_res(const mk_q4k_layer* layers, const mk_q4k_layer_norm* norms,
         !al16(norms[l].ffn))
       return MK_EALIGN;
   }
+  const bool q6 = any_q6(layers, n_layers);
   StepPlan sp;
   size_t lds = 0;
   int G = 0;
   const int groups = (M + STEP_MAX_M - 1) / STEP_MAX_M;
   for (int g = groups - 1; g >= 0; --g) {
-    rc = prepare_walk<1>(layers, n_layers, group_rows(M, g), ws_bytes, sp, lds, G);
+    rc = prepare_walk<1>(layers, n_layers, group_rows(M, g), ws_bytes, q6, sp, lds, G);
     if (rc != MK_OK) return rc;
   }
   const int H = layers[0].q.K;
@@ -1578,10 +1706,10 @@ int mk_q4k_step_res(const mk_q4k_layer* layers, const mk_q4k_layer_norm* norms,
       table[l].g[0] = norms[l].attn;
       table[l].g[1] = norms[l].ffn;
     }
-    rc = prepare_walk<1>(layers, n_layers, Mg, ws_bytes, sp, lds, G);
+    rc = prepare_walk<1>(layers, n_layers, Mg, ws_bytes, q6, sp, lds, G);
     if (rc != MK_OK) return rc;
     rc = enqueue_walk<1>(layers, table, n_layers, Mg, nullptr, nullptr, h0 + (size_t)r0 * H,
-                         workspace, sp, lds, G, g, stream);
+                         workspace, sp, lds, G, g, q6, stream);
     if (rc != MK_OK) return rc;
   }
   return MK_OK;

@@ -86,6 +86,90 @@ __device__ __forceinline__ half4v q6_to_h4(uint32_t q) {
   return __builtin_bit_cast(half4v, b) - half4v{k, k, k, k};
 }
 
+// ---- Q6_K matrices for the decode-step walk (record layout in q4k_device.h)
+
+// Low 4 and high 2 bits of weight k of a raw 210-byte Q6_K block.
+__device__ __forceinline__ int q6_low4(const uint8_t* blk, int k) {
+  const int h = k >> 7, j = (k & 127) >> 5, l = k & 31;
+  return (blk[64 * h + 32 * (j & 1) + l] >> (4 * (j >> 1))) & 15;
+}
+__device__ __forceinline__ int q6_high2(const uint8_t* blk, int k) {
+  const int h = k >> 7, j = (k & 127) >> 5, l = k & 31;
+  return (blk[128 + 32 * h + l] >> (2 * j)) & 3;
+}
+
+// One thread per (record, lane): the lane's 16 + 16 + 16 + 4 bytes, and the
+// row's d for lanes 0..15. Rows past N are zero.
+__global__ void __launch_bounds__(256) q6k_step_repack_kernel(const uint8_t* __restrict__ W,
+                                                              uint8_t* __restrict__ T, int N,
+                                                              int nkb, long long nthreads) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nthreads) return;
+  const long long rec = i >> 6;
+  const int l = (int)(i & 63), c = l & 15, g = l >> 4;
+  const int t = (int)(rec / nkb), kb = (int)(rec - (long long)t * nkb);
+  const int n = 16 * t + c;
+  uint8_t* out = T + rec * Q6W_REC;
+  uint8_t qa[16], qb[16], hb[16], sc[4];
+  uint16_t d = 0;
+  if (n < N) {
+    const uint8_t* blk = W + ((size_t)n * nkb + kb) * Q6_BLOCK;
+    const int k0 = 64 * g;
+    for (int b = 0; b < 16; ++b) {
+      qa[b] = (uint8_t)(q6_low4(blk, k0 + b) | (q6_low4(blk, k0 + 32 + b) << 4));
+      qb[b] = (uint8_t)(q6_low4(blk, k0 + 16 + b) | (q6_low4(blk, k0 + 48 + b) << 4));
+    }
+    for (int m = 0; m < 4; ++m)
+      for (int b = 0; b < 4; ++b)
+        hb[4 * m + b] = (uint8_t)(q6_high2(blk, k0 + 8 * m + b) |
+                                  (q6_high2(blk, k0 + 32 + 8 * m + b) << 2) |
+                                  (q6_high2(blk, k0 + 8 * m + 4 + b) << 4) |
+                                  (q6_high2(blk, k0 + 36 + 8 * m + b) << 6));
+    for (int r = 0; r < 4; ++r) sc[r] = blk[192 + 4 * g + r];
+    d = (uint16_t)(blk[208] | (blk[209] << 8));
+  } else {
+    for (int b = 0; b < 16; ++b) qa[b] = qb[b] = hb[b] = 0;
+    for (int r = 0; r < 4; ++r) sc[r] = 0;
+  }
+  for (int b = 0; b < 16; ++b) {
+    out[16 * l + b] = qa[b];
+    out[1024 + 16 * l + b] = qb[b];
+    out[2048 + 16 * l + b] = hb[b];
+  }
+  for (int r = 0; r < 4; ++r) out[3072 + 4 * l + r] = sc[r];
+  if (g == 0) {
+    out[3328 + 2 * c] = (uint8_t)(d & 0xFF);
+    out[3329 + 2 * c] = (uint8_t)(d >> 8);
+  }
+}
+
+// Column sums sum_k w[n][k] of the rows of a Q6_K matrix (zero for the rows
+// that pad the last tile), one thread per row: per block d * sum_r sc[r] *
+// (integer sum of the run's q - 32), exact, added in double; rounded once.
+__global__ void __launch_bounds__(256) q6k_colsum_kernel(const uint8_t* __restrict__ W,
+                                                         float* __restrict__ cs, int N, int Npad,
+                                                         int nkb) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= Npad) return;
+  double acc = 0.0;
+  if (n < N) {
+    for (int kb = 0; kb < nkb; ++kb) {
+      const uint8_t* blk = W + ((size_t)n * nkb + kb) * Q6_BLOCK;
+      long long s = 0;
+      for (int r = 0; r < 16; ++r) {
+        int qs = 0;
+        for (int i = 0; i < 16; ++i) {
+          const int k = 16 * r + i;
+          qs += (q6_low4(blk, k) | (q6_high2(blk, k) << 4)) - 32;
+        }
+        s += (long long)(int8_t)blk[192 + r] * qs;
+      }
+      acc += (double)bit_cast_<_Float16>((uint16_t)(blk[208] | (blk[209] << 8))) * (double)s;
+    }
+  }
+  cs[n] = (float)acc;
+}
+
 template <int MT, int TN>
 __global__ void __launch_bounds__(Q6_THREADS) q6k_gemm_kernel(const uint8_t* __restrict__ T,
                                                               const uint16_t* __restrict__ X,
@@ -250,6 +334,38 @@ int mk_q6k_gemm_tiled(const void* tiles, const uint16_t* X, float* Y, int M, int
     if (rc != MK_OK) return rc;
   }
   return MK_OK;
+}
+
+size_t mk_q6k_step_bytes(int N, int K) {
+  if (N < 1 || K < mk::Q6_QK || K % mk::Q6_QK) return 0;
+  const size_t nt = (size_t)((N + 15) / 16);
+  return nt * (K / mk::Q6_QK) * mk::Q6W_REC + nt * 16 * sizeof(float);
+}
+
+int mk_q6k_step_repack(const void* W, void* out, int N, int K, void* stream) {
+  using namespace mk;
+  if (!W || !out || N < 1 || K < Q6_QK || K % Q6_QK) return MK_EINVAL;
+  if (!al16(out)) return MK_EALIGN;
+  const size_t nt = (size_t)((N + 15) / 16);
+  const size_t rec_bytes = nt * (K / Q6_QK) * Q6W_REC;
+  const size_t in = (size_t)N * (K / Q6_QK) * Q6_BLOCK;
+  const char* a = static_cast<const char*>(W);
+  const char* b = static_cast<const char*>(out);
+  if (a < b + mk_q6k_step_bytes(N, K) && b < a + in) return MK_EINVAL;  // must not overlap
+  const long long nthreads = (long long)(rec_bytes / Q6W_REC) * 64;
+  const long long blocks = (nthreads + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return MK_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(q6k_step_repack_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<const uint8_t*>(W), static_cast<uint8_t*>(out), N, K / Q6_QK,
+                     nthreads);
+  if (hipGetLastError() != hipSuccess) return MK_EHIP;
+  const int npad = (int)(nt * 16);
+  hipLaunchKernelGGL(q6k_colsum_kernel, dim3((unsigned)((npad + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const uint8_t*>(W),
+                     reinterpret_cast<float*>(static_cast<uint8_t*>(out) + rec_bytes), N, npad,
+                     K / Q6_QK);
+  return hipGetLastError() == hipSuccess ? MK_OK : MK_EHIP;
 }
 
 }  // extern "C"

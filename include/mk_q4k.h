@@ -211,10 +211,18 @@ int mk_q4k_gemm_tiled(const void* W_tiles, const uint16_t* X_fp16, float* Y_fp32
  * rows fit in on-chip memory; a shape whose plan still does not fit one
  * workgroup per compute unit returns MK_EOCCUPANCY.
  */
+/* Block types of a step matrix (GGUF type numbers); 0 means Q4_K. */
+#define MK_QTYPE_Q4_K 12
+#define MK_QTYPE_Q6_K 14
+
 typedef struct {
-  const void* w; /* device: the tile-record form (mk_q4k_repack) of the matrix */
+  const void* w; /* device: the record form of the matrix: mk_q4k_repack for
+                    Q4_K, mk_q6k_step_repack (mk_q6k.h) for Q6_K */
   int N;         /* output columns (weight rows)    */
   int K;         /* input width                     */
+  int type;      /* MK_QTYPE_Q4_K (or 0) or MK_QTYPE_Q6_K; Q6_K only for v and
+                    down, the matrices a Q4_K_M file keeps in Q6_K (else
+                    MK_EINVAL); it may differ from layer to layer */
 } mk_q4k_mat;
 
 typedef struct {

@@ -59,6 +59,30 @@ int mk_q6k_repack(const void* W, void* tiles, int N, int K, void* stream);
 int mk_q6k_gemm_tiled(const void* tiles, const uint16_t* X, float* Y, int M, int N, int K,
                       void* stream);
 
+/*
+ * Q6_K matrices inside the decode-step walk (mk_q4k_step): a Q4_K_M file
+ * keeps attn_v and ffn_down (in some or all layers) in Q6_K, and the walk
+ * takes them as they are, in one launch with the Q4_K matrices (the OpenJet
+ * post, paragraph on how parallel decoding works: the whole step in one
+ * persistent kernel).
+ *
+ * mk_q6k_step_bytes: size of the walk's record form of an N x K Q6_K matrix
+ *   (0 for a bad shape): ceil(N/16) * K/256 records of 3360 bytes, then
+ *   ceil(N/16) * 16 fp32 column sums.
+ * mk_q6k_step_repack: write that form of W (device, N rows x K/256 blocks of
+ *   210 bytes, row-major, any alignment) to `out` (device, caller-owned,
+ *   mk_q6k_step_bytes bytes, 16-byte aligned, not overlapping W). Each
+ *   record holds 16 rows x one block in the lane order of the walk's
+ *   activation operands (every byte of the block kept, reordered; rows past N
+ *   zero); the column sums are sum_k w[n][k], exact per block in double,
+ *   rounded once to fp32. Asynchronous on `stream`. Returns MK_OK, MK_EINVAL
+ *   (null pointer, bad shape, overlap), MK_EALIGN or MK_EHIP.
+ * Pass the result as the `w` of a layer's v or down matrix with type
+ * MK_QTYPE_Q6_K (mk_q4k.h).
+ */
+size_t mk_q6k_step_bytes(int N, int K);
+int mk_q6k_step_repack(const void* W, void* out, int N, int K, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,7 +11,10 @@ from __future__ import annotations
 import numpy as np
 
 from . import (LAYER_MATRICES, QK, BLOCK_BYTES, TAG_H0, TAG_NORM, activations, f32_normal, key,
-               q4k_fill_ptr, q4k_fill_ptr_centered, weight_key)
+               q4k_fill_ptr, q4k_fill_ptr_centered, q6k_rows, weight_key)
+
+Q6K_BLOCK_BYTES = 210
+TAG_Q6 = 14  # Q6_K matrices of a stack: (seed, TAG_Q6, layer, matrix index)
 
 MATRIX_ORDER = ("q", "k", "v", "o", "gate", "up", "down")
 
@@ -35,13 +38,17 @@ class Stack:
 
     The weights are kept on the device in the tile-record form the step walk
     reads (made by the library's repack call from the generated rows); the
-    rows themselves can be regenerated on the host with host_rows()."""
+    rows themselves can be regenerated on the host with host_rows(). `q6`
+    lists (layer, name) matrices (name v or down, as in a Q4_K_M file) that
+    are Q6_K instead, kept in the walk's Q6_K record form."""
 
     centered = False  # weight generator: the workload's, or centred (ResStack)
 
-    def __init__(self, n_layers, M, shp=None, seed=0, device="cuda:0"):
+    def __init__(self, n_layers, M, shp=None, seed=0, device="cuda:0", q6=()):
         import torch
         self.torch = torch
+        self.q6 = set(q6)
+        assert all(name in ("v", "down") for _, name in self.q6)
         self.n_layers = n_layers
         self.M = M
         self.shp = dict(shp or MODEL_SHAPES)
@@ -57,6 +64,11 @@ class Stack:
             lay = {}
             for mi, name in enumerate(MATRIX_ORDER):
                 N, K = self.shp[name]
+                if (l, name) in self.q6:
+                    r6 = torch.from_numpy(self.host_rows(l, name, np.arange(N))).to(device)
+                    lay[name] = mk.q6k_step_repack(r6.reshape(-1), N, K)
+                    torch.cuda.synchronize()
+                    continue
                 nbytes = N * (K // QK) * BLOCK_BYTES
                 fill = q4k_fill_ptr_centered if self.centered else q4k_fill_ptr
                 fill(weight_key(seed, l, mi), K, 0, N, pinned.data_ptr())
@@ -78,21 +90,33 @@ class Stack:
             self.io.append({"y": ys, "x": xs})
 
     def layer_descs(self):
-        return [{n: (lay[n], self.shp[n][0], self.shp[n][1]) for n in MATRIX_ORDER}
-                for lay in self.weights]
+        import bit_weight_streaming_amd as mk
+        return [{n: (lay[n], self.shp[n][0], self.shp[n][1],
+                     mk.MK_QTYPE_Q6_K if (l, n) in self.q6 else mk.MK_QTYPE_Q4_K)
+                 for n in MATRIX_ORDER}
+                for l, lay in enumerate(self.weights)]
+
+    def is_q6(self, layer, name):
+        return (layer, name) in self.q6
 
     def host_rows(self, layer, name, rows):
-        """The Q4_K bytes of the given weight rows of one matrix (regenerated)."""
+        """The bytes of the given weight rows of one matrix (regenerated): Q4_K,
+        or Q6_K for the matrices listed in q6."""
         from . import q4k_rows, q4k_rows_centered
         N, K = self.shp[name]
         mi = MATRIX_ORDER.index(name)
+        if (layer, name) in self.q6:
+            full = q6k_rows(key(self.seed, TAG_Q6, layer, mi), K, 0, N)
+            return full[np.asarray(rows)]
         gen = q4k_rows_centered if self.centered else q4k_rows
         full = gen(weight_key(self.seed, layer, mi), K, 0, N)
         return full[np.asarray(rows)]
 
     @property
     def weight_bytes(self):
-        return weight_bytes(self.shp, self.n_layers)
+        q6_extra = sum(self.shp[n][0] * (self.shp[n][1] // QK) * (Q6K_BLOCK_BYTES - BLOCK_BYTES)
+                       for _, n in self.q6)
+        return weight_bytes(self.shp, self.n_layers) + q6_extra
 
 
 def norm_weights(seed, layer, which, H):

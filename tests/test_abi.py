@@ -199,3 +199,26 @@ def test_step_workspace_is_one_row_group(L):
     for M in (17, 32, 44, 64):
         assert L.mk_q4k_step_workspace_bytes(ctypes.byref(lay), 64, M) == w16
     assert L.mk_q4k_step_workspace_bytes(ctypes.byref(lay), 64, 65) == 0
+
+
+def test_step_rejects_q6k_outside_v_and_down(L):
+    """Only v and down may be Q6_K (what a Q4_K_M file keeps in Q6_K)."""
+    from synth.stack import shapes
+    for name in ("q", "k", "o", "gate", "up"):
+        lay = _layer(shapes())
+        getattr(lay, name).type = mk.MK_QTYPE_Q6_K
+        assert L.mk_q4k_step_check_plan(ctypes.byref(lay), 1, 12, 256) == mk.MK_EINVAL, name
+    lay = _layer(shapes())
+    lay.v.type = mk.MK_QTYPE_Q6_K
+    lay.down.type = mk.MK_QTYPE_Q6_K
+    assert L.mk_q4k_step_check_plan(ctypes.byref(lay), 1, 12, 256) == 0
+    lay.down.type = 3                                     # not a supported type
+    assert L.mk_q4k_step_check_plan(ctypes.byref(lay), 1, 12, 256) == mk.MK_EINVAL
+
+
+def test_q6k_step_bytes(L):
+    L.mk_q6k_step_bytes.restype = ctypes.c_size_t
+    L.mk_q6k_step_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+    assert L.mk_q6k_step_bytes(16, 256) == 3360 + 16 * 4
+    assert L.mk_q6k_step_bytes(17, 512) == 2 * 2 * 3360 + 32 * 4
+    assert L.mk_q6k_step_bytes(16, 300) == 0 and L.mk_q6k_step_bytes(0, 256) == 0

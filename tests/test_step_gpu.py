@@ -77,7 +77,8 @@ def check_stack(stack, layers=None, ncols=None, seed=0, skip=()):
             else:
                 cols = np.unique(np.concatenate([rng.choice(N, ncols, replace=False), [0, N - 1]]))
             W = stack.host_rows(l, name, cols)
-            y_ref, S = oracle.gemm_std(W, xs[PHASE_OF[name]])
+            ref = oracle.q6k_gemm_std if stack.is_q6(l, name) else oracle.gemm_std
+            y_ref, S = ref(W, xs[PHASE_OF[name]])
             ok, w, nbad = oracle.within_bound(ys[t][:, cols].astype(np.float64), y_ref, S)
             assert ok, f"layer {l} {name}: {nbad} outside the bound, worst {w:.3e}"
             worst = max(worst, w)
@@ -127,8 +128,8 @@ def test_step_rejects_bad_chain():
     stack = Stack(1, 4, SMALL, seed=1, device=DEV)
     descs = stack.layer_descs()
     bad = [dict(descs[0])]
-    w, N, K = bad[0]["o"]
-    bad[0]["o"] = (w, N, K + 256)           # o.K != q.N
+    w, N, K, t = bad[0]["o"]
+    bad[0]["o"] = (w, N, K + 256, t)        # o.K != q.N
     ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
     with pytest.raises(mk.MkError) as e:
         mk.step(bad, stack.io, stack.x0, stack.x_out, ws, 4)
@@ -283,3 +284,95 @@ def _cancel_block_bytes(dmin_bits):
     b[4:16] = bytes([0xFF] * 12)
     b[16:] = bytes([0xFF] * 128)
     return bytes(b)
+
+
+# --- Q4_K_M layers: v and down in Q6_K in some layers ------------------------
+def test_q6k_walk_records_layout():
+    """The walk's Q6_K records hold, for lane l = c + 16 g of tile t and
+    block b, the low nibbles of weights 64g + i / 64g + 32 + i (bytes 0..15)
+    and 64g + 16 + i / 64g + 48 + i (bytes 1024..), the high bit pairs packed
+    four to a byte, the scales of runs 4g..4g+3 and row c's d, with the
+    column sums after the records (rebuilt here from the block definition)."""
+    N, K = 37, 512
+    W = synth.q6k_matrix(synth.key(81, 14, N, K), N, K)
+    T = mk.q6k_step_repack(torch.from_numpy(W).to(DEV).reshape(-1), N, K).cpu().numpy()
+    nt, KB = (N + 15) // 16, K // 256
+    blocks = W.reshape(N, KB, 210)
+
+    def low4(blk, k):
+        h, j, l = k >> 7, (k & 127) >> 5, k & 31
+        return (int(blk[64 * h + 32 * (j & 1) + l]) >> (4 * (j >> 1))) & 15
+
+    def high2(blk, k):
+        h, j, l = k >> 7, (k & 127) >> 5, k & 31
+        return (int(blk[128 + 32 * h + l]) >> (2 * j)) & 3
+
+    ref = np.zeros(nt * KB * 3360, dtype=np.uint8)
+    for t in range(nt):
+        for b in range(KB):
+            rec = ref[(t * KB + b) * 3360:(t * KB + b + 1) * 3360]
+            for lane in range(64):
+                c, g = lane & 15, lane >> 4
+                n = 16 * t + c
+                if n >= N:
+                    continue
+                blk = blocks[n, b]
+                k0 = 64 * g
+                for i in range(16):
+                    rec[16 * lane + i] = low4(blk, k0 + i) | (low4(blk, k0 + 32 + i) << 4)
+                    rec[1024 + 16 * lane + i] = low4(blk, k0 + 16 + i) | (low4(blk, k0 + 48 + i) << 4)
+                for m in range(4):
+                    for bb in range(4):
+                        rec[2048 + 16 * lane + 4 * m + bb] = (
+                            high2(blk, k0 + 8 * m + bb) | (high2(blk, k0 + 32 + 8 * m + bb) << 2) |
+                            (high2(blk, k0 + 8 * m + 4 + bb) << 4) | (high2(blk, k0 + 36 + 8 * m + bb) << 6))
+                rec[3072 + 4 * lane:3072 + 4 * lane + 4] = blk[192 + 4 * g:192 + 4 * g + 4]
+                rec[3328 + 2 * c:3330 + 2 * c] = blk[208:210]
+    assert np.array_equal(T[:ref.size], ref)
+    cs = T[ref.size:].view(np.float32)
+    w = oracle.q6k_dequant_rows(W, K)
+    want = np.zeros(nt * 16, dtype=np.float32)
+    want[:N] = w.sum(axis=1).astype(np.float32)
+    assert np.array_equal(cs, want)
+
+
+Q6_MIXED = {(0, "v"), (1, "down"), (2, "v"), (2, "down")}
+
+
+@pytest.mark.parametrize("M", [12, 1, 16])
+def test_q6k_mixed_stack_all_columns(M):
+    stack = Stack(3, M, SMALL, seed=71 + M, device=DEV, q6=Q6_MIXED)
+    run_step(stack)
+    worst = check_stack(stack)
+    check_out(stack)
+    print(f"mixed Q4_K/Q6_K, M={M}: worst |err|/S = {worst:.3e}")
+
+
+def test_q6k_mixed_ragged_stack():
+    """v with 200 columns (a ragged last tile) in Q6_K."""
+    stack = Stack(2, 12, RAGGED, seed=74, device=DEV, q6={(0, "v"), (1, "v"), (1, "down")})
+    run_step(stack)
+    check_stack(stack)
+    check_out(stack)
+
+
+def test_q6k_mixed_rows_bit_identical_alone_or_stacked():
+    stack = Stack(3, 12, SMALL, seed=75, device=DEV, q6=Q6_MIXED)
+    run_step(stack)
+    for r in (0, 11):
+        one = Stack(3, 1, SMALL, seed=75, device=DEV, q6=Q6_MIXED)
+        one.x0.copy_(stack.x0[r:r + 1])
+        run_step(one)
+        for l in range(3):
+            for a, b in zip(one.io[l]["y"] + one.io[l]["x"], stack.io[l]["y"] + stack.io[l]["x"]):
+                assert torch.equal(a[0], b[r]), (r, l)
+
+
+def test_q6k_mixed_full_size_layers():
+    """Three layers of the full 27B-class shapes at M = 12, with Q6_K v and
+    down in a Q4_K_M-like pattern; 2048 sampled columns per matrix."""
+    stack = Stack(3, 12, seed=76, device=DEV, q6={(0, "v"), (0, "down"), (2, "v"), (2, "down")})
+    run_step(stack, reps=2)
+    worst = check_stack(stack, ncols=2048, seed=77)
+    check_out(stack)
+    print(f"full-size mixed layers: worst |err|/S = {worst:.3e}")
