@@ -81,8 +81,10 @@ def check_res_stack(stack, check_layers=None, ncols=None, seed=0):
         check_cast(xs[1], ys[0], f"layer {l} cast(q)")
         check_cast(xs[2], h_mid * g_ffn, f"layer {l} cast(h_mid*g_ffn)")
         g, u = ys[4], ys[5]
-        off += check_cast(xs[3], g / (np.float32(1) + np.exp(-g)) * u,
-                          f"layer {l} cast(silu(gate)*up)", steps=1)
+        # exp(-g) may overflow to inf for very negative g: silu's factor is then 0
+        with np.errstate(over="ignore"):
+            silu_u = g / (np.float32(1) + np.exp(-g)) * u
+        off += check_cast(xs[3], silu_u, f"layer {l} cast(silu(gate)*up)", steps=1)
         if l in check_layers:
             r_attn = oracle.rms_inv(h.astype(np.float64))
             r_ffn = oracle.rms_inv(h_mid.astype(np.float64))
@@ -177,3 +179,31 @@ def test_res_full_size_layers_sampled_columns():
     run_res(stack, reps=2)
     worst, off = check_res_stack(stack, check_layers=(0, 7), ncols=4096, seed=4321)
     print(f"full-size residual walk worst |err|/S = {worst:.3e}, silu casts one step off: {off}")
+
+
+class _WorkloadResStack(ResStack):
+    """The residual walk on the benchmark's own weight generator (not centred:
+    the Q4_K blocks of d * sc * q - dmin * m with d, dmin ~ |N(0,1)| 1e-3)."""
+    centered = False
+
+
+def test_res_workload_weights_one_layer():
+    """The residual walk on the workload's (uncentred) Q4_K weights: every
+    output, residual and cast of one layer against the oracle, as for the
+    centred stacks."""
+    stack = _WorkloadResStack(1, 12, SMALL, seed=47, device=DEV)
+    run_res(stack)
+    worst, off = check_res_stack(stack)
+    print(f"workload weights, one layer: worst |err|/S = {worst:.3e}, silu casts one step off: {off}")
+
+
+def test_res_workload_weights_leave_the_range_and_say_so():
+    """A second layer of those weights drives the residual stream past what the
+    row statistics hold (the uncentred weights add a bias every matrix): the
+    walk reports MK_ERANGE in its status word rather than a wrong result."""
+    stack = _WorkloadResStack(2, 12, SMALL, seed=47, device=DEV)
+    descs = stack.layer_descs()
+    ws = torch.empty(mk.step_workspace_bytes(descs[0], 2, 12), dtype=torch.uint8, device=DEV)
+    mk.step_res(descs, stack.io, stack.norms, stack.h0, ws, 12)
+    torch.cuda.synchronize()
+    assert mk.step_status(ws) == mk.MK_ERANGE
