@@ -160,13 +160,16 @@ def gemm_bench(seed: int, reps: int = 60) -> list:
     return out
 
 
-Q6K_CONFIGS = (("down K=17408 N=5120", 12, 5120, 17408), ("gate/up K=5120 N=17408", 12, 17408, 5120))
+Q6K_CONFIGS = (("down K=17408 N=5120", 12, 5120, 17408), ("gate/up K=5120 N=17408", 12, 17408, 5120),
+               ("down K=17408 N=5120", 64, 5120, 17408))
 Q6K_COPIES = 6
 
 
 def q6k_bench(seed: int, reps: int = 60) -> list:
-    """Time the Q6_K product (mk_q6k_gemm_tiled on tile records) at the layer
-    shapes, HIP events around `reps` back-to-back launches cycling over
+    """Time the two Q6_K products at the layer shapes: mk_q6k_gemm_tiled on
+    tile records (M <= 16 here) and mk_q6k_gemm_step, the persistent K-split
+    product on the walk's records (its second launch, the slice reduction,
+    included). HIP events around `reps` back-to-back calls cycling over
     Q6K_COPIES weight copies (about 440 MB, beyond the last-level cache).
     Algorithmic bytes: the Q6_K weights (210 B per 256) + X + Y."""
     import torch
@@ -177,28 +180,33 @@ def q6k_bench(seed: int, reps: int = 60) -> list:
     out = []
     for label, M, N, K in Q6K_CONFIGS:
         w = torch.from_numpy(synth.q6k_matrix(synth.key(seed, 14, N, K), N, K))
-        tiles = [mk.q6k_repack(w.to(dev), N, K) for _ in range(Q6K_COPIES)]
         X = torch.from_numpy(synth.activations(seed, M, K)).to(dev)
         Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        for i in range(2 * Q6K_COPIES):
-            mk.q6k_gemm_tiled(tiles[i % Q6K_COPIES], X, N, out=Y)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(reps):
-            mk.q6k_gemm_tiled(tiles[i % Q6K_COPIES], X, N, out=Y)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / reps * 1e-3
         wbytes = N * (K // 256) * 210
         alg = wbytes + M * K * 2 + M * N * 4
-        log(f"q6k {label} M={M}: {t * 1e6:.2f} us, {wbytes / t / 1e9:.1f} GB/s")
-        out.append({"config": label, "M": M, "us": round(t * 1e6, 2),
-                    "weight_GBps": round(wbytes / t / 1e9, 1),
-                    "roofline_frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
-                    "kernel": "q6k_gemm_kernel<1, %d>" % (4 if ((N + 15) // 16 + 3) // 4 >= 256 else
-                                                          2 if ((N + 15) // 16 + 1) // 2 >= 512 else 1)})
-        del tiles
+        forms = [("step records", lambda wd: mk.q6k_step_repack(wd, N, K), mk.q6k_gemm_step,
+                  "q4k_gemm_kernel<%d, 2> + q4k_gemm_reduce" % ((M + 15) // 16))]
+        if M <= 16:
+            forms.insert(0, ("tile records", lambda wd: mk.q6k_repack(wd, N, K), mk.q6k_gemm_tiled,
+                             "q6k_gemm_kernel<1, %d>" % (4 if ((N + 15) // 16 + 3) // 4 >= 256 else
+                                                         2 if ((N + 15) // 16 + 1) // 2 >= 512 else 1)))
+        for form, repack, gemm, kern in forms:
+            recs = [repack(w.to(dev)) for _ in range(Q6K_COPIES)]
+            for i in range(2 * Q6K_COPIES):
+                gemm(recs[i % Q6K_COPIES], X, N, out=Y)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(reps):
+                gemm(recs[i % Q6K_COPIES], X, N, out=Y)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / reps * 1e-3
+            log(f"q6k {label} M={M} ({form}): {t * 1e6:.2f} us, {wbytes / t / 1e9:.1f} GB/s")
+            out.append({"config": label, "M": M, "form": form, "us": round(t * 1e6, 2),
+                        "weight_GBps": round(wbytes / t / 1e9, 1),
+                        "roofline_frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4), "kernel": kern})
+            del recs
     return out
 
 

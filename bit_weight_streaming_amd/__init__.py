@@ -148,6 +148,8 @@ def lib():
         L.mk_q6k_step_repack.argtypes = [vp, vp, i, i, vp]
         L.mk_q6k_gemm_tiled.restype = i
         L.mk_q6k_gemm_tiled.argtypes = [vp, vp, vp, i, i, i, vp]
+        L.mk_q6k_gemm_step.restype = i
+        L.mk_q6k_gemm_step.argtypes = [vp, vp, vp, i, i, i, vp]
         if hasattr(L, "mk_q4k_step"):
             L.mk_q4k_step_workspace_bytes.restype = sz
             L.mk_q4k_step_workspace_bytes.argtypes = [ctypes.POINTER(_Layer), i, i]
@@ -357,6 +359,24 @@ def q6k_gemm_tiled(Wt, X, N: int, out=None, stream=None):
     elif out.shape != (M, N) or out.dtype != torch.float32 or not out.is_contiguous():
         raise MkError(MK_EINVAL, "out must be a contiguous float32 [M, N] tensor")
     _check(lib().mk_q6k_gemm_tiled(_ptr(Wt), _ptr(X), _ptr(out), M, N, K, _stream(stream)))
+    return out
+
+
+def q6k_gemm_step(Ws, X, N: int, out=None, stream=None):
+    """Y = X * W^T with the Q6_K matrix W in walk-record form (q6k_step_repack());
+    N columns; the persistent K-split product."""
+    import torch
+    if X.dim() != 2 or X.dtype != torch.float16 or not X.is_contiguous():
+        raise MkError(MK_EINVAL, "X must be a contiguous 2-D float16 tensor")
+    M, K = X.shape
+    nbytes = q6k_step_bytes(N, K)
+    if nbytes == 0 or Ws.dtype != torch.uint8 or Ws.numel() < nbytes or not Ws.is_contiguous():
+        raise MkError(MK_EINVAL, "Ws must be the contiguous walk-record form of an N x K Q6_K matrix")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    elif out.shape != (M, N) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise MkError(MK_EINVAL, "out must be a contiguous float32 [M, N] tensor")
+    _check(lib().mk_q6k_gemm_step(_ptr(Ws), _ptr(X), _ptr(out), M, N, K, _stream(stream)))
     return out
 
 

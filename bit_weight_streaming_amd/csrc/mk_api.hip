@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "mk_q4k.h"
+#include "mk_q6k.h"
 #include "q4k_host.h"
 
 namespace {
@@ -59,7 +60,7 @@ int current_device(int* dev_out) {
 }
 
 int check_gemm_args(const void* W, const uint16_t* X, const float* Y, int M, int N, int K,
-                    bool tiled) {
+                    int fmt) {
   if (!W || !X || !Y) return MK_EINVAL;
   if (M < 1 || M > MK_Q4K_MAX_M || N < 1 || K < MK_Q4K_QK || K % MK_Q4K_QK) return MK_EINVAL;
   if ((long long)N * (K / MK_Q4K_QK) > (1LL << 40)) return MK_EINVAL;
@@ -68,8 +69,10 @@ int check_gemm_args(const void* W, const uint16_t* X, const float* Y, int M, int
   const char* y0 = reinterpret_cast<const char*>(Y);
   const char* y1 = y0 + (size_t)M * N * sizeof(float);
   const char* w0 = static_cast<const char*>(W);
-  const char* w1 = w0 + (tiled ? (size_t)((N + 15) / 16) * (K / MK_Q4K_QK) * 16 * MK_Q4K_BLOCK_BYTES
-                               : (size_t)N * (K / MK_Q4K_QK) * MK_Q4K_BLOCK_BYTES);
+  const size_t tiles_kb = (size_t)((N + 15) / 16) * (K / MK_Q4K_QK);
+  const char* w1 = w0 + (fmt == mk::GEMM_Q6W     ? tiles_kb * MK_Q6K_TILE_BYTES
+                         : fmt == mk::GEMM_TILES ? tiles_kb * 16 * MK_Q4K_BLOCK_BYTES
+                                                 : (size_t)N * (K / MK_Q4K_QK) * MK_Q4K_BLOCK_BYTES);
   const char* x0 = reinterpret_cast<const char*>(X);
   const char* x1 = x0 + (size_t)M * K * sizeof(uint16_t);
   if (y0 < w1 && w0 < y1) return MK_EINVAL;
@@ -112,14 +115,14 @@ int owned_workspace(int dev, void* stream, size_t bytes, void** out) {
   return MK_OK;
 }
 
-int run_gemm(bool tiled, const void* W, const uint16_t* X, float* Y, int M, int N, int K,
+int run_gemm(int fmt, const void* W, const uint16_t* X, float* Y, int M, int N, int K,
              void* workspace, size_t ws_bytes, void* stream) {
-  int rc = check_gemm_args(W, X, Y, M, N, K, tiled);
+  int rc = check_gemm_args(W, X, Y, M, N, K, fmt);
   if (rc != MK_OK) return rc;
   // a caller workspace is validated before the device is looked at
   int dev = -1;
   const bool have_dev = current_device(&dev) == MK_OK;
-  const mk::GemmPlan p = mk::gemm_plan(M, N, K, have_dev ? g_dev[dev].cus : kDefaultCus);
+  const mk::GemmPlan p = mk::gemm_plan(M, N, K, have_dev ? g_dev[dev].cus : kDefaultCus, fmt);
   if (!p.ok) return MK_EINVAL;
   const bool caller_ws = workspace != nullptr || ws_bytes != 0;
   if (caller_ws && p.ws_bytes > 0) {
@@ -132,7 +135,7 @@ int run_gemm(bool tiled, const void* W, const uint16_t* X, float* Y, int M, int 
     rc = owned_workspace(dev, stream, p.ws_bytes, &ws);
     if (rc != MK_OK) return rc;
   }
-  hipError_t e = mk::gemm_launch(p, tiled, W, X, Y, M, N, K, ws, static_cast<hipStream_t>(stream));
+  hipError_t e = mk::gemm_launch(p, fmt, W, X, Y, M, N, K, ws, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MK_OK : MK_EHIP;
 }
 
@@ -173,7 +176,7 @@ extern "C" {
 
 int mk_q4k_gemm_noalloc(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N,
                         int K, void* stream) {
-  int rc = check_gemm_args(W_blocks, X_fp16, Y_fp32, M, N, K, false);
+  int rc = check_gemm_args(W_blocks, X_fp16, Y_fp32, M, N, K, mk::GEMM_ROWS);
   if (rc != MK_OK) return rc;
   int dev = -1;
   rc = current_device(&dev);
@@ -233,17 +236,22 @@ size_t mk_q4k_gemm_workspace_bytes(int M, int N, int K) {
 
 int mk_q4k_gemm_ws(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N,
                    int K, void* workspace, size_t ws_bytes, void* stream) {
-  return run_gemm(false, W_blocks, X_fp16, Y_fp32, M, N, K, workspace, ws_bytes, stream);
+  return run_gemm(mk::GEMM_ROWS, W_blocks, X_fp16, Y_fp32, M, N, K, workspace, ws_bytes, stream);
 }
 
 int mk_q4k_gemm(const void* W_blocks, const uint16_t* X_fp16, float* Y_fp32, int M, int N, int K,
                 void* stream) {
-  return run_gemm(false, W_blocks, X_fp16, Y_fp32, M, N, K, nullptr, 0, stream);
+  return run_gemm(mk::GEMM_ROWS, W_blocks, X_fp16, Y_fp32, M, N, K, nullptr, 0, stream);
 }
 
 int mk_q4k_gemm_tiled(const void* W_tiles, const uint16_t* X_fp16, float* Y_fp32, int M, int N,
                       int K, void* stream) {
-  return run_gemm(true, W_tiles, X_fp16, Y_fp32, M, N, K, nullptr, 0, stream);
+  return run_gemm(mk::GEMM_TILES, W_tiles, X_fp16, Y_fp32, M, N, K, nullptr, 0, stream);
+}
+
+int mk_q6k_gemm_step(const void* W_step, const uint16_t* X_fp16, float* Y_fp32, int M, int N,
+                     int K, void* stream) {
+  return run_gemm(mk::GEMM_Q6W, W_step, X_fp16, Y_fp32, M, N, K, nullptr, 0, stream);
 }
 
 }  // extern "C"

@@ -535,19 +535,23 @@ __device__ __forceinline__ void q6_operands(uint32_t qe, uint32_t qo, half2v s, 
   lo = half8v{l[0].x, l[0].y, l[1].x, l[1].y, l[2].x, l[2].y, l[3].x, l[3].y};
 }
 
-// One 16-row tile of staged activations (xa: this lane's 128 LDS bytes of
-// the block, as for Q4_K) against one Q6_K walk record: for each step u the
-// lower MFMA takes weights 64g + 8u + (0..7) (run 4g + u/2), the upper
-// 64g + 32 + 8u + (0..7) (run 4g + 2 + u/2); acc += d * (sum of both chains).
-__device__ __forceinline__ void mma_unit6(const BlockRegs& r, const ScaleRegs6& rs,
-                                          const char* xa, floatx4& acc) {
+// MT 16-row tiles of staged activations (xa[rt]: this lane's 128 LDS bytes of
+// the block in tile rt, as for Q4_K) against one Q6_K walk record: for each
+// step u the lower MFMA takes weights 64g + 8u + (0..7) (run 4g + u/2), the
+// upper 64g + 32 + 8u + (0..7) (run 4g + 2 + u/2); the weight operands are
+// built once for all tiles; acc[rt] += d * (sum of both chains).
+template <int MT>
+__device__ __forceinline__ void mma_unit6_mt(const BlockRegs& r, const ScaleRegs6& rs,
+                                             const char* const* xa, floatx4* acc) {
   half2v sc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const _Float16 v = (_Float16)(float)(int)(int8_t)(rs.sc >> (8 * i));
     sc[i] = half2v{v, v};
   }
-  floatx4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+  floatx4 c0[MT], c1[MT];
+#pragma unroll
+  for (int rt = 0; rt < MT; ++rt) c0[rt] = c1[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const uint32_t ve = u == 0 ? r.h.x : u == 1 ? r.h.z : u == 2 ? r.q0.x : r.q0.z;
@@ -556,20 +560,36 @@ __device__ __forceinline__ void mma_unit6(const BlockRegs& r, const ScaleRegs6& 
     const uint32_t m4 = 0x0F0F0F0Fu, m2 = 0x30303030u;
     const uint32_t qle = (ve & m4) | ((H << 4) & m2), qlo = (vo & m4) | (H & m2);
     const uint32_t qhe = ((ve >> 4) & m4) | ((H << 2) & m2), qho = ((vo >> 4) & m4) | ((H >> 2) & m2);
-    const half8v a_lo = *reinterpret_cast<const half8v*>(xa + 32 * u);
-    const half8v a_hi = *reinterpret_cast<const half8v*>(xa + 32 * u + 16);
     half8v bh, bl;
     q6_operands(qle, qlo, sc[u >> 1], bh, bl);
-    c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, bh, c0, 0, 0, 0);
-    c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, bl, c0, 0, 0, 0);
+#pragma unroll
+    for (int rt = 0; rt < MT; ++rt) {
+      const half8v a_lo = *reinterpret_cast<const half8v*>(xa[rt] + 32 * u);
+      c0[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, bh, c0[rt], 0, 0, 0);
+      c0[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, bl, c0[rt], 0, 0, 0);
+    }
     q6_operands(qhe, qho, sc[2 + (u >> 1)], bh, bl);
-    c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, bh, c1, 0, 0, 0);
-    c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, bl, c1, 0, 0, 0);
+#pragma unroll
+    for (int rt = 0; rt < MT; ++rt) {
+      const half8v a_hi = *reinterpret_cast<const half8v*>(xa[rt] + 32 * u + 16);
+      c1[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, bh, c1[rt], 0, 0, 0);
+      c1[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, bl, c1[rt], 0, 0, 0);
+    }
   }
   const float d = (float)bit_cast_<_Float16>((uint16_t)rs.d);
   const floatx4 dd = {d, d, d, d};
-  acc = __builtin_elementwise_fma(dd, c0, acc);
-  acc = __builtin_elementwise_fma(dd, c1, acc);
+#pragma unroll
+  for (int rt = 0; rt < MT; ++rt) {
+    acc[rt] = __builtin_elementwise_fma(dd, c0[rt], acc[rt]);
+    acc[rt] = __builtin_elementwise_fma(dd, c1[rt], acc[rt]);
+  }
+}
+
+// The walk's case: one row tile.
+__device__ __forceinline__ void mma_unit6(const BlockRegs& r, const ScaleRegs6& rs,
+                                          const char* xa, floatx4& acc) {
+  const char* xas[1] = {xa};
+  mma_unit6_mt<1>(r, rs, xas, &acc);
 }
 
 }  // namespace mk

@@ -20,9 +20,11 @@
 // one, no counters are kept between calls, and no floating-point atomics are
 // used.
 //
-// TILED selects the load-time tile-record layout (mk_q4k_repack: every wave
-// load is one contiguous 1 KiB piece); otherwise the plain row layout is read
-// in place.
+// FMT selects the weights' form: GEMM_ROWS, the plain Q4_K row layout read in
+// place; GEMM_TILES, the load-time Q4_K tile records (mk_q4k_repack: every
+// wave load is one contiguous 1 KiB piece); GEMM_Q6W, Q6_K matrices in the
+// decode step's walk records (mk_q6k_step_repack: 3360 bytes per 16 rows and
+// block, streamed through the same ring with the lane's run scales).
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -51,8 +53,9 @@ struct GemmRing {  // records in flight per wave (what the registers allow)
   static constexpr int PD = MT == 1 ? 6 : 4;
 };
 
-template <int MT, bool TILED>
+template <int MT, int FMT>
 __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
+  constexpr bool Q6 = FMT == GEMM_Q6W;
   constexpr int PD = GemmRing<MT>::PD;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
@@ -101,9 +104,14 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
   const int ua = wave_begin(a, wave), ub = wave_begin(a, wave + 1);
   // next unit to load (the loop below never asks for one past ub)
   int ltl = ua / a.nkb, lb = ua - ltl * a.nkb, lu = ua;
-  auto load_next = [&](BlockRegs& r) {
+  BlockRegs ring[PD];
+  ScaleRegs6 s6[Q6 ? PD : 1];  // Q6_K: the lane's run scales and d of each slot
+  auto load_next = [&](int s) {
+    BlockRegs& r = ring[s];
     const int tg = a.t0 + ltl;
-    if (TILED) {
+    if (Q6) {
+      load_rec6(r, s6[Q6 ? s : 0], A.w + ((size_t)tg * A.KB + a.kb0 + lb) * Q6W_REC, lane);
+    } else if (FMT == GEMM_TILES) {
       load_rec(r, A.w + ((size_t)tg * A.KB + a.kb0 + lb) * TILE_REC, lane);
     } else {
       const int col = min(16 * tg + c, A.N - 1);
@@ -118,15 +126,16 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
     }
   };
   // the first weight records are in flight while the activations are staged
-  BlockRegs ring[PD];
 #pragma unroll
   for (int s = 0; s < PD; ++s)
-    if (s < ub - ua) load_next(ring[s]);
+    if (s < ub - ua) load_next(s);
   if (a.U > 0) stage_x(A.x, A.K, A.M, a.kb0, a.nkb, x_lds, A.x_stride, tid, GEMM_THREADS);
   __syncthreads();
-  if (a.U > 0)
-    stage_xsum(A.M, a.nkb, xsum_row_bytes(a.nkb), x_lds, A.x_stride, xs_lds, tid, GEMM_THREADS);
-  __syncthreads();
+  if (!Q6) {  // the Q4_K min term's sub-block sums (Q6_K has none)
+    if (a.U > 0)
+      stage_xsum(A.M, a.nkb, xsum_row_bytes(a.nkb), x_lds, A.x_stride, xs_lds, tid, GEMM_THREADS);
+    __syncthreads();
+  }
 
   // this wave's parts of the tiles it shares (slot 0, slot 1), held until the
   // stream ends
@@ -156,7 +165,7 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
 #pragma unroll
       for (int rt = 0; rt < MT; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
     };
-    auto consume = [&](const BlockRegs& r) {
+    auto consume = [&](int s) {
       const char* xab[MT];
       const char* xsb[MT];
 #pragma unroll
@@ -164,7 +173,10 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
         xab[rt] = xa[rt] + cb * X_BYTES_PER_BLOCK;
         xsb[rt] = xs[rt] + cb * XSUM_BYTES_PER_BLOCK;
       }
-      mma_unit_mt<MT>(r, g, xab, xsb, k, acc);
+      if constexpr (Q6)
+        mma_unit6_mt<MT>(ring[s], s6[s], xab, acc);
+      else
+        mma_unit_mt<MT>(ring[s], g, xab, xsb, k, acc);
       ++cu;
       if (++cb == a.nkb || cu == ub) {
         flush();
@@ -181,8 +193,8 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
 #pragma unroll
       for (int s = 0; s < PD; ++s) {
         if (r0 + s >= U) break;
-        consume(ring[s]);
-        if (r0 + s + PD < U) load_next(ring[s]);
+        consume(s);
+        if (r0 + s + PD < U) load_next(s);
       }
     }
   }
@@ -258,7 +270,8 @@ namespace {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-GemmPlan make_plan(int M, int N, int K, int G) {
+GemmPlan make_plan(int M, int N, int K, int G, int fmt) {
+  const double rec = fmt == GEMM_Q6W ? (double)Q6W_REC : (double)TILE_REC;
   GemmPlan p;
   p.mt = (M + 15) / 16;
   p.KB = K / QK;
@@ -303,7 +316,7 @@ GemmPlan make_plan(int M, int N, int K, int G) {
     const size_t c1 = c0 > contrib_p ? c0 : contrib_p;
     const bool fits = c1 + 256 <= kGemmLdsLimit;
     const double part = (double)mtp * 1024;
-    const double bytes = (double)umax * TILE_REC + (double)Mp * nkb * X_BYTES_PER_BLOCK +
+    const double bytes = (double)umax * rec + (double)Mp * nkb * X_BYTES_PER_BLOCK +
                          (skr > 1 ? tw_max * part + (double)p.nt * skr * part / G +
                                         (skr + 7) / 8 * 12288.0 + 24576.0
                                   : 0.0);
@@ -329,7 +342,7 @@ GemmPlan make_plan(int M, int N, int K, int G) {
 }
 
 std::mutex g_plan_mu;
-std::map<std::tuple<int, int, int, int>, GemmPlan> g_plans;
+std::map<std::tuple<int, int, int, int, bool>, GemmPlan> g_plans;
 
 // Dynamic LDS each kernel instantiation has been allowed on each device
 // (the attribute is raised only when a plan needs more).
@@ -348,9 +361,9 @@ hipError_t allow_lds(const void* kern, size_t lds) {
   return e;
 }
 
-template <int MT, bool TILED>
+template <int MT, int FMT>
 hipError_t launch(const GemmPlan& p, const GemmArgs& A, hipStream_t st) {
-  auto kern = q4k_gemm_kernel<MT, TILED>;
+  auto kern = q4k_gemm_kernel<MT, FMT>;
   hipError_t e = allow_lds((const void*)kern, p.lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(p.G), dim3(GEMM_THREADS), p.lds, st, A);
@@ -362,30 +375,31 @@ hipError_t launch(const GemmPlan& p, const GemmArgs& A, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool TILED>
+template <int FMT>
 hipError_t launch_mt(const GemmPlan& p, const GemmArgs& A, hipStream_t st) {
   switch (p.mt) {
-    case 1: return launch<1, TILED>(p, A, st);
-    case 2: return launch<2, TILED>(p, A, st);
-    case 3: return launch<3, TILED>(p, A, st);
-    default: return launch<4, TILED>(p, A, st);
+    case 1: return launch<1, FMT>(p, A, st);
+    case 2: return launch<2, FMT>(p, A, st);
+    case 3: return launch<3, FMT>(p, A, st);
+    default: return launch<4, FMT>(p, A, st);
   }
 }
 
 }  // namespace
 
-GemmPlan gemm_plan(int M, int N, int K, int G) {
+GemmPlan gemm_plan(int M, int N, int K, int G, int fmt) {
   std::lock_guard<std::mutex> lk(g_plan_mu);
-  const auto key = std::make_tuple(M, N, K, G);
+  // the row and tile forms cost the same bytes: one plan
+  const auto key = std::make_tuple(M, N, K, G, fmt == GEMM_Q6W);
   auto it = g_plans.find(key);
   if (it != g_plans.end()) return it->second;
-  const GemmPlan p = make_plan(M, N, K, G);
+  const GemmPlan p = make_plan(M, N, K, G, fmt);
   if (g_plans.size() > 4096) g_plans.clear();
   g_plans.emplace(key, p);
   return p;
 }
 
-hipError_t gemm_launch(const GemmPlan& p, bool tiled, const void* W, const uint16_t* X, float* Y,
+hipError_t gemm_launch(const GemmPlan& p, int fmt, const void* W, const uint16_t* X, float* Y,
                        int M, int N, int K, void* ws, hipStream_t st) {
   GemmArgs A;
   A.w = static_cast<const uint8_t*>(W);
@@ -402,7 +416,11 @@ hipError_t gemm_launch(const GemmPlan& p, bool tiled, const void* W, const uint1
   A.nkb = p.nkb;
   A.G = p.G;
   A.x_stride = p.x_stride;
-  return tiled ? launch_mt<true>(p, A, st) : launch_mt<false>(p, A, st);
+  switch (fmt) {
+    case GEMM_TILES: return launch_mt<GEMM_TILES>(p, A, st);
+    case GEMM_Q6W: return launch_mt<GEMM_Q6W>(p, A, st);
+    default: return launch_mt<GEMM_ROWS>(p, A, st);
+  }
 }
 
 }  // namespace mk

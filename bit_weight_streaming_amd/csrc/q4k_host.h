@@ -24,8 +24,12 @@ struct GemmPlan {
   bool ok = false;       // the plan fits the device
 };
 
-GemmPlan gemm_plan(int M, int N, int K, int G);
-hipError_t gemm_launch(const GemmPlan& p, bool tiled, const void* W, const uint16_t* X, float* Y,
+// Weight forms the single-matrix GEMM reads: Q4_K row blocks, Q4_K tile
+// records, Q6_K walk records.
+constexpr int GEMM_ROWS = 0, GEMM_TILES = 1, GEMM_Q6W = 2;
+
+GemmPlan gemm_plan(int M, int N, int K, int G, int fmt = GEMM_ROWS);
+hipError_t gemm_launch(const GemmPlan& p, int fmt, const void* W, const uint16_t* X, float* Y,
                        int M, int N, int K, void* ws, hipStream_t st);
 
 }  // namespace mk

@@ -83,6 +83,24 @@ int mk_q6k_gemm_tiled(const void* tiles, const uint16_t* X, float* Y, int M, int
 size_t mk_q6k_step_bytes(int N, int K);
 int mk_q6k_step_repack(const void* W, void* out, int N, int K, void* stream);
 
+/* Y = X * W^T for a Q6_K matrix W (N x K) in the walk's record form above
+ * (the column sums after the records are not read): X binary16 [M][K]
+ * row-major, Y fp32 [M][N] row-major (device, caller-owned, 16-byte aligned,
+ * Y overlapping neither), 1 <= M <= 64. The persistent product of
+ * mk_q4k_gemm_tiled (mk_q4k.h) on Q6_K records: one workgroup per compute
+ * unit, the K range cut into slices chosen from N, K and the device only
+ * (not M), every record read once per call and multiplied against all M
+ * rows (up to four 16-row MFMA tiles) while it is on chip, a second launch
+ * adding each tile's slice partials in slice order when there are several;
+ * so a row's bits are the same alone or stacked. The arithmetic is the
+ * walk's: each operand d-free s * (q - 32) enters the matrix cores exactly,
+ * as binary16 hi + lo, and each record's products are scaled by d in fp32.
+ * The slice partials go to a library-owned workspace, as for mk_q4k_gemm.
+ * Asynchronous on `stream`. Returns MK_OK, MK_EINVAL, MK_EALIGN, MK_ENODEV
+ * or MK_EHIP. */
+int mk_q6k_gemm_step(const void* W_step, const uint16_t* X, float* Y, int M, int N, int K,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif
