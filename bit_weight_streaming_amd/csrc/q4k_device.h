@@ -245,17 +245,17 @@ __device__ __forceinline__ void unpack_pair_k(uint32_t v0, uint32_t v1, const La
 // One 16-row tile of activations (xa: this lane's 128 LDS bytes of the
 // block, always valid - rows past M read a real row whose results are never
 // stored) against NB weight records of the same super-block; the main term
-// runs as two independent MFMA chains (even and odd 32-weight groups).
+// runs as one MFMA chain over the block's eight 32-weight groups (in the
+// order of the steps u, low then high nibbles), scaled by d once.
 template <int NB>
 __device__ __forceinline__ void mma_unit(const BlockRegs* r, int g, const char* xa,
                                          const char* xs, const UnpackConsts& k, floatx4* acc) {
   LaneScales s[NB];
-  floatx4 c0[NB], c1[NB];
+  floatx4 c0[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     s[nb] = lane_scales(r[nb].h, g);
     c0[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    c1[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -268,7 +268,7 @@ __device__ __forceinline__ void mma_unit(const BlockRegs* r, int g, const char* 
       half8v b_lo, b_hi;
       unpack_pair_k(v0, v1, s[nb], k, b_lo, b_hi);
       c0[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, c0[nb], 0, 0, 0);
-      c1[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, c1[nb], 0, 0, 0);
+      c0[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, c0[nb], 0, 0, 0);
     }
   }
   const half8v am = *reinterpret_cast<const half8v*>(xs);
@@ -278,7 +278,6 @@ __device__ __forceinline__ void mma_unit(const BlockRegs* r, int g, const char* 
     cn = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, s[nb].bmin, cn, 0, 0, 0);
     const floatx4 dd = {s[nb].d, s[nb].d, s[nb].d, s[nb].d};
     acc[nb] = __builtin_elementwise_fma(dd, c0[nb], acc[nb]);
-    acc[nb] = __builtin_elementwise_fma(dd, c1[nb], acc[nb]);
     acc[nb] = __builtin_elementwise_fma(
         floatx4{-s[nb].dmin, -s[nb].dmin, -s[nb].dmin, -s[nb].dmin}, cn, acc[nb]);
   }
@@ -416,16 +415,16 @@ __device__ __forceinline__ void stage_xsum(int M, int nkb, int xs_row, const cha
 
 // Activations of MT 16-row tiles (xa[rt]: this lane's 128 LDS bytes of the
 // block, always valid - rows past M read a real row whose results are never
-// stored) against one weight record; the main term runs as two independent
-// MFMA chains per row tile, the weights are unpacked once for all row tiles.
+// stored) against one weight record; the main term runs as one MFMA chain per
+// row tile (as mma_unit), the weights are unpacked once for all row tiles.
 template <int MT>
 __device__ __forceinline__ void mma_unit_mt(const BlockRegs& r, int g, const char* const* xa,
                                             const char* const* xs, const UnpackConsts& k,
                                             floatx4* acc) {
   const LaneScales s = lane_scales(r.h, g);
-  floatx4 c0[MT], c1[MT];
+  floatx4 c0[MT];
 #pragma unroll
-  for (int rt = 0; rt < MT; ++rt) c0[rt] = c1[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < MT; ++rt) c0[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const uint32_t v0 = u == 0 ? r.q0.x : u == 1 ? r.q0.z : u == 2 ? r.q1.x : r.q1.z;
@@ -437,7 +436,7 @@ __device__ __forceinline__ void mma_unit_mt(const BlockRegs& r, int g, const cha
       const half8v a_lo = *reinterpret_cast<const half8v*>(xa[rt] + 32 * u);
       const half8v a_hi = *reinterpret_cast<const half8v*>(xa[rt] + 32 * u + 16);
       c0[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, c0[rt], 0, 0, 0);
-      c1[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, c1[rt], 0, 0, 0);
+      c0[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, c0[rt], 0, 0, 0);
     }
   }
   const floatx4 dd = {s.d, s.d, s.d, s.d};
@@ -448,7 +447,6 @@ __device__ __forceinline__ void mma_unit_mt(const BlockRegs& r, int g, const cha
     floatx4 cn = {0.f, 0.f, 0.f, 0.f};
     cn = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, s.bmin, cn, 0, 0, 0);
     acc[rt] = __builtin_elementwise_fma(dd, c0[rt], acc[rt]);
-    acc[rt] = __builtin_elementwise_fma(dd, c1[rt], acc[rt]);
     acc[rt] = __builtin_elementwise_fma(nm, cn, acc[rt]);
   }
 }
