@@ -90,50 +90,82 @@ __device__ __forceinline__ half2v small_int_pair(uint32_t v) {
   return bit_cast_<half2v>(u) - half2v{(_Float16)1024.0f, (_Float16)1024.0f};
 }
 
+// Per-lane constants of the weight unpack and of the scale decode, built once
+// per lane (they depend on the lane's group g = lane / 16 only) and kept in
+// VGPRs: the nibble masks and exponent patterns of unpack_pair_k, and the
+// byte selectors of lane_scales.
+struct UnpackConsts {
+  uint32_t mlo, mhi;  // low and high nibble of each byte pair
+  uint32_t orv, orh;  // binary16 exponent patterns: 1024 + q (low), 64 + q (high)
+  uint32_t selA;      // v_perm selector: the scale (min) bytes of sub-blocks 2g, 2g+1
+  uint32_t selB;      // v_perm selector: the bytes holding their top 2 bits (g >= 2)
+  uint32_t mA;        // mask of the first: 6 bits (g < 2) or the low nibble (g >= 2)
+  uint32_t shC;       // shift of the min bytes: 0 (g < 2) or 4 (high nibble, g >= 2)
+};
+
+__device__ __forceinline__ UnpackConsts unpack_consts(int g) {
+  UnpackConsts k;
+  asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(k.mlo));
+  asm volatile("v_mov_b32 %0, 0x00F000F0" : "=v"(k.mhi));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.orv));
+  asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(k.orh));
+  // v_perm bytes: 0-3 pick the second source's bytes, 4-7 the first's, 12
+  // gives zero; results hold two values in bytes 0 and 2
+  const uint32_t z = 0x0C000C00u;
+  if (g < 2) {  // sub-blocks 0..3: 6 bits of scale byte j, min byte j + 4
+    k.selA = z | ((uint32_t)(2 * g + 1) << 16) | (uint32_t)(2 * g);
+    k.selB = 0x0C0C0C0Cu;  // no top bits
+    k.mA = 0x003F003Fu;
+    k.shC = 0;
+  } else {  // sub-blocks 4..7: nibbles of bytes 8..11, top bits in bytes 0..7
+    const uint32_t b0 = 2u * (uint32_t)(g - 2);
+    k.selA = z | ((4u + b0 + 1u) << 16) | (4u + b0);
+    k.selB = z | ((b0 + 1u) << 16) | b0;
+    k.mA = 0x000F000Fu;
+    k.shC = 4;
+  }
+  return k;
+}
+
 // Per-lane scale data of one block for sub-blocks 2g (low nibbles) and 2g+1
 // (high nibbles).
 struct LaneScales {
   half2v sl, nl;  // (sc_lo, sc_lo), (-1024*sc_lo, ...): maps 1024+q -> sc_lo*q
-  half2v sh, nh;  // (sc_hi/16, ...), (-64*sc_hi, ...): maps 1024+16q -> sc_hi*q
-  half8v bmin;    // (64 m_lo, m_lo, m_lo, 0, 64 m_hi, m_hi, m_hi, 0): min-term MFMA operand
+  half2v sh, nh;  // (sc_hi, sc_hi), (-64*sc_hi, ...): maps 64+q -> sc_hi*q
+  half8v bmin;    // (64 m_lo, 64 m_hi, m_lo, m_hi, m_lo, m_hi, 0, 0): min-term MFMA operand
   float d, dmin;
 };
 
-// Unpack the 6-bit scales and mins of sub-blocks 2g, 2g+1 from the header.
-// Sub-blocks 0..3: scale = low 6 bits of scale byte j, min = low 6 bits of
-// byte j+4. Sub-blocks 4..7: low 4 bits in the low/high nibble of byte j+4,
-// top 2 bits in bits 6-7 of byte j-4 (scale) and byte j (min).
-__device__ __forceinline__ LaneScales lane_scales(const u32x4& h, int g) {
-  const uint32_t sh = 16u * (uint32_t)(g & 1);
-  const uint32_t a = h.y >> sh;  // scale bytes 0-3
-  const uint32_t b = h.z >> sh;  // scale bytes 4-7
-  const uint32_t c = h.w >> sh;  // scale bytes 8-11
-  uint32_t scp, mnp;
-  if (g < 2) {
-    scp = a & 0x3F3Fu;
-    mnp = b & 0x3F3Fu;
-  } else {
-    scp = (c & 0x0F0Fu) | ((a >> 2) & 0x3030u);
-    mnp = ((c >> 4) & 0x0F0Fu) | ((b >> 2) & 0x3030u);
-  }
+// The 6-bit scales and mins of sub-blocks 2g, 2g+1 from the block header h
+// (h.x: d, dmin; h.y, h.z, h.w: the 12 scale bytes). Sub-blocks 0..3: scale =
+// low 6 bits of scale byte j, min = of byte j+4. Sub-blocks 4..7: low 4 bits
+// in the low (scale) or high (min) nibble of byte j+4, top 2 bits in bits 6-7
+// of byte j-4 (scale) or byte j (min). Each pair is gathered with byte
+// permutes into the two halves of a dword, ORed with the exponent of 1024 and
+// turned into binary16 (1024 + v) - 1024 = v, exactly.
+__device__ __forceinline__ LaneScales lane_scales(const u32x4& h, const UnpackConsts& k) {
+  const uint32_t e = 0x64006400u;
+  const uint32_t tsc = (__builtin_amdgcn_perm(h.w, h.y, k.selB) >> 2) & 0x00300030u;
+  const uint32_t scp = (__builtin_amdgcn_perm(h.w, h.y, k.selA) & k.mA) | tsc | e;
+  const uint32_t tmn = (__builtin_amdgcn_perm(h.w, h.z, k.selB) >> 2) & 0x00300030u;
+  const uint32_t mnp = ((__builtin_amdgcn_perm(h.w, h.z, k.selA) >> k.shC) & k.mA) | tmn | e;
+  const half2v off = {(_Float16)1024.0f, (_Float16)1024.0f};
+  const half2v sc = bit_cast_<half2v>(scp) - off;  // (sc_lo, sc_hi)
+  const half2v mn = bit_cast_<half2v>(mnp) - off;  // (m_lo, m_hi)
+  const half2v nsc = sc * half2v{(_Float16)-1024.0f, (_Float16)-64.0f};
+  const half2v mn64 = mn * half2v{(_Float16)64.0f, (_Float16)64.0f};
   LaneScales s;
-  const half2v s_lo = small_int_pair(scp & 0xFFu);
-  const half2v s_hi = small_int_pair(scp >> 8);
-  s.sl = s_lo;
-  s.nl = s_lo * half2v{(_Float16)-1024.0f, (_Float16)-1024.0f};
-  s.sh = s_hi * half2v{(_Float16)0.0625f, (_Float16)0.0625f};
-  s.nh = s_hi * half2v{(_Float16)-64.0f, (_Float16)-64.0f};
-  const half2v m_lo = small_int_pair(mnp & 0xFFu);
-  const half2v m_hi = small_int_pair(mnp >> 8);
-  const _Float16 z = (_Float16)0.0f, k64 = (_Float16)64.0f;
-  s.bmin = half8v{m_lo.x * k64, m_lo.x, m_lo.x, z, m_hi.x * k64, m_hi.x, m_hi.x, z};
+  s.sl = half2v{sc.x, sc.x};
+  s.sh = half2v{sc.y, sc.y};
+  s.nl = half2v{nsc.x, nsc.x};
+  s.nh = half2v{nsc.y, nsc.y};
+  const _Float16 z = (_Float16)0.0f;
+  s.bmin = half8v{mn64.x, mn64.y, mn.x, mn.y, mn.x, mn.y, z, z};
   const half2v dd = bit_cast_<half2v>(h.x);
   s.d = (float)dd.x;
   s.dmin = (float)dd.y;
   return s;
 }
-
-
 
 // Stage activations of super-blocks [kb0, kb0+nkb) of the M rows of X
 // ([M][K] binary16, row stride K) into LDS in the MFMA order above (the
@@ -196,28 +228,14 @@ __device__ __forceinline__ void load_rec(BlockRegs& r, const uint8_t* rec, int l
   r.q1 = __builtin_nontemporal_load(g + 80 + lane);
 }
 
-// Nibble masks and the binary16 exponent pattern, materialised once in
-// VGPRs so that every (v & mask) | 0x64006400 is one v_and_or_b32 (gfx9 VOP3
-// takes no literal and one SGPR).
-struct UnpackConsts {
-  uint32_t mlo, mhi, orv;
-};
-
-__device__ __forceinline__ UnpackConsts unpack_consts() {
-  UnpackConsts k;
-  asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(k.mlo));
-  asm volatile("v_mov_b32 %0, 0x00F000F0" : "=v"(k.mhi));
-  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.orv));
-  return k;
-}
-
 // B operands of the two MFMAs fed by quant dwords v0, v1 (8 consecutive
 // weights of sub-block 2g in the low nibbles, of 2g+1 in the high nibbles),
-// k order (0,2,1,3,4,6,5,7): each nibble q becomes the binary16 1024 + q (or
-// 1024 + 16 q for a high nibble) by OR-ing in the exponent pattern, and one
-// packed FMA with (scale, -1024 * scale) (or (scale / 16, -64 * scale))
-// leaves exactly scale * q: every operand and result is exact in binary16.
-// Masks come in registers.
+// k order (0,2,1,3,4,6,5,7): each nibble q becomes the binary16 1024 + q (a
+// low nibble, in mantissa bits 0-3 under the exponent of 1024) or 64 + q (a
+// high nibble, in bits 4-7 under the exponent of 64, whose last place is
+// 1/16) by OR-ing in the exponent pattern, and one packed FMA with (scale,
+// -1024 * scale) or (scale, -64 * scale) leaves exactly scale * q: every
+// operand and result is exact in binary16. Masks come in registers.
 __device__ __forceinline__ void unpack_pair_k(uint32_t v0, uint32_t v1, const LaneScales& s,
                                               const UnpackConsts& k, half8v& b_lo,
                                               half8v& b_hi) {
@@ -226,10 +244,10 @@ __device__ __forceinline__ void unpack_pair_k(uint32_t v0, uint32_t v1, const La
   const half2v l1 = bit_cast_<half2v>((t0 & k.mlo) | k.orv);
   const half2v l2 = bit_cast_<half2v>((v1 & k.mlo) | k.orv);
   const half2v l3 = bit_cast_<half2v>((t1 & k.mlo) | k.orv);
-  const half2v h0 = bit_cast_<half2v>((v0 & k.mhi) | k.orv);
-  const half2v h1 = bit_cast_<half2v>((t0 & k.mhi) | k.orv);
-  const half2v h2 = bit_cast_<half2v>((v1 & k.mhi) | k.orv);
-  const half2v h3 = bit_cast_<half2v>((t1 & k.mhi) | k.orv);
+  const half2v h0 = bit_cast_<half2v>((v0 & k.mhi) | k.orh);
+  const half2v h1 = bit_cast_<half2v>((t0 & k.mhi) | k.orh);
+  const half2v h2 = bit_cast_<half2v>((v1 & k.mhi) | k.orh);
+  const half2v h3 = bit_cast_<half2v>((t1 & k.mhi) | k.orh);
   const half2v L0 = __builtin_elementwise_fma(l0, s.sl, s.nl);
   const half2v L1 = __builtin_elementwise_fma(l1, s.sl, s.nl);
   const half2v L2 = __builtin_elementwise_fma(l2, s.sl, s.nl);
@@ -254,7 +272,7 @@ __device__ __forceinline__ void mma_unit(const BlockRegs* r, int g, const char* 
   floatx4 c0[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    s[nb] = lane_scales(r[nb].h, g);
+    s[nb] = lane_scales(r[nb].h, k);
     c0[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
@@ -382,9 +400,22 @@ __device__ __forceinline__ half4v split_xsum(float sum) {
   return half4v{a, b, c, (_Float16)0.0f};
 }
 
+// Store the split_xsum parts (a, b, c) of sub-block j of a block whose 64 LDS
+// bytes start at blk: the 16 bytes of the pair 2g, 2g+1 (g = j / 2) hold
+// (a_2g, a_2g+1, b_2g, b_2g+1, c_2g, c_2g+1, 0, 0), the order of the min-term
+// MFMA operand (see LaneScales::bmin); the even sub-block also writes the
+// two zeros.
+__device__ __forceinline__ void put_xsum(char* blk, int j, const half4v& p) {
+  _Float16* q = reinterpret_cast<_Float16*>(blk + 16 * (j >> 1)) + (j & 1);
+  q[0] = p[0];
+  q[2] = p[1];
+  q[4] = p[2];
+  if ((j & 1) == 0) *reinterpret_cast<uint32_t*>(blk + 16 * (j >> 1) + 12) = 0u;
+}
+
 // Sub-block sums of the staged activations, as split_xsum parts, for the
-// min-term MFMA: row m, block b, sub-block j at
-// xs_lds + m * xs_row + b * 64 + 8 * j (xs_row = xsum_row_bytes(nkb)).
+// min-term MFMA: row m, block b at xs_lds + m * xs_row + b * 64, in put_xsum's
+// order (xs_row = xsum_row_bytes(nkb)).
 __device__ __forceinline__ void stage_xsum(int M, int nkb, int xs_row, const char* x_lds,
                                            int x_stride, char* xs_lds, int tid,
                                            int nthreads) {
@@ -408,8 +439,7 @@ __device__ __forceinline__ void stage_xsum(int M, int nkb, int xs_row, const cha
         sum += (float)hh.y;
       }
     }
-    *reinterpret_cast<half4v*>(xs_lds + (size_t)m * xs_row + b * XSUM_BYTES_PER_BLOCK + 8 * j) =
-        split_xsum(sum);
+    put_xsum(xs_lds + (size_t)m * xs_row + b * XSUM_BYTES_PER_BLOCK, j, split_xsum(sum));
   }
 }
 
@@ -421,7 +451,7 @@ template <int MT>
 __device__ __forceinline__ void mma_unit_mt(const BlockRegs& r, int g, const char* const* xa,
                                             const char* const* xs, const UnpackConsts& k,
                                             floatx4* acc) {
-  const LaneScales s = lane_scales(r.h, g);
+  const LaneScales s = lane_scales(r.h, k);
   floatx4 c0[MT];
 #pragma unroll
   for (int rt = 0; rt < MT; ++rt) c0[rt] = floatx4{0.f, 0.f, 0.f, 0.f};

@@ -77,7 +77,7 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
     xa[rt] = x_lds + (size_t)row * A.x_stride + g * 128;
     xs[rt] = xs_lds + (size_t)row * xsum_row_bytes(a.nkb) + 16 * g;
   }
-  const UnpackConsts k = unpack_consts();
+  const UnpackConsts k = unpack_consts(g);
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(A.part, A.part_bytes);
 
   // the result of tile tg, row tile rt, lane ln: to Y, or as this slice's partial

@@ -457,8 +457,7 @@ __device__ __forceinline__ void stage_rounds(const uint16_t* src, int K, int M, 
     *reinterpret_cast<u32x4*>(x_lds + (size_t)m * x_stride + b * X_BYTES_PER_BLOCK + gq * 128 +
                               (2 * u + hb) * 16) = o;
     if ((ch & 3) == 0)
-      *reinterpret_cast<half4v*>(xs_lds + (size_t)m * xs_row + b * XSUM_BYTES_PER_BLOCK +
-                                 8 * (kk >> 5)) = split_xsum(sum);
+      put_xsum(xs_lds + (size_t)m * xs_row + b * XSUM_BYTES_PER_BLOCK, kk >> 5, split_xsum(sum));
   }
 #pragma unroll
   for (int i = 0; i < kStatPer; ++i)
@@ -996,7 +995,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
     tot_s[tid] = 0ull;
   }
   __syncthreads();
-  const UnpackConsts k = unpack_consts();
+  const UnpackConsts k = unpack_consts(g);
   // Rows past M read row M-1 (their results are never stored), so every
   // lane's activation reads are unconditional.
   const int arow = c < M ? c : M - 1;
