@@ -270,6 +270,11 @@ namespace {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// The second launch (the slice reduction), priced in bytes through one
+// compute unit's load path: a launch costs a few microseconds of host and
+// queue time, about what 128 KiB take on that path.
+constexpr double kLaunchBytes = 131072.0;
+
 GemmPlan make_plan(int M, int N, int K, int G, int fmt) {
   const double rec = fmt == GEMM_Q6W ? (double)Q6W_REC : (double)TILE_REC;
   GemmPlan p;
@@ -285,7 +290,8 @@ GemmPlan make_plan(int M, int N, int K, int G, int fmt) {
   // partials it stores; with K slices, also one compute unit's share of the
   // partials the reduction reads, 12 KiB for each of its rounds of eight
   // loads (a round trip takes about as long as 12 KiB on that path) and
-  // 24 KiB for the second launch. nkb = 1 is taken when nothing else fits.
+  // kLaunchBytes for the second launch. nkb = 1 is taken when nothing else
+  // fits.
   //
   // The split is chosen for the largest row count a call takes (MK_Q4K_MAX_M),
   // whatever M is: the K slices, and so the order in which every output is
@@ -318,7 +324,7 @@ GemmPlan make_plan(int M, int N, int K, int G, int fmt) {
     const double part = (double)mtp * 1024;
     const double bytes = (double)umax * rec + (double)Mp * nkb * X_BYTES_PER_BLOCK +
                          (skr > 1 ? tw_max * part + (double)p.nt * skr * part / G +
-                                        (skr + 7) / 8 * 12288.0 + 24576.0
+                                        (skr + 7) / 8 * 12288.0 + kLaunchBytes
                                   : 0.0);
     if ((fits && (best < 0 || bytes < best)) || (nkb == 1 && best < 0)) {
       best = bytes;
