@@ -53,7 +53,7 @@ namespace mk {
 namespace {
 
 constexpr unsigned long long kTimeoutTicks = 500000000ull;  // 5 s at 100 MHz
-constexpr int kStageRound = 7;   // staging chunks a thread loads before using them
+constexpr int kStageRound = 10;  // staging chunks a thread loads before using them
 // statistics slot values (STAT_SLOTS x M x 2) each thread reads when staging
 constexpr int kStatPer = (STAT_SLOTS * STEP_MAX_M * 2 + STEP_THREADS - 1) / STEP_THREADS;
 
@@ -472,11 +472,12 @@ __device__ __forceinline__ void stage_slice(const uint16_t* src, int K, int M, c
                                             const long long* st, unsigned long long* tot_s,
                                             char* x_lds, int x_stride, char* xs_lds,
                                             int xs_row, int tid) {
-  static_assert(kStageRound == 7, "one instantiation per round count");
+  static_assert(kStageRound == 10, "one instantiation per round count");
   const int r = uni((M * a.nkb * 32 + STEP_THREADS - 1) / STEP_THREADS);
 #define MK_STAGE(RR) \
   stage_rounds<RR>(src, K, M, a, st, tot_s, x_lds, x_stride, xs_lds, xs_row, tid)
-  if (r > 5) MK_STAGE(7);
+  if (r > 7) MK_STAGE(10);
+  else if (r > 5) MK_STAGE(7);
   else if (r > 4) MK_STAGE(5);
   else if (r > 3) MK_STAGE(4);
   else if (r > 2) MK_STAGE(3);
