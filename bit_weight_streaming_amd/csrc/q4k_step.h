@@ -78,6 +78,8 @@ struct DevPhase {
                        // in its tile-record buffer (after the records)
   unsigned cs_off6[3]; // the same for a Q6_K matrix (its records are larger)
   double inv_k;        // 1 / K (the row statistics of the input run over K)
+  int tab;             // 1: every wave's records fit a record table (the walk's
+                       // branch-free loop); 0: the record iterator walks them
   int norm;            // what the products of the phase are scaled by per row:
                        // NORM_STD, NORM_RMS or NORM_NONE
 };

@@ -269,6 +269,177 @@ __device__ __forceinline__ void ring_fill(BlockRegs (&ring)[STEP_PD], Iter& it,
   }
 }
 
+// A wave's record table of one phase, one entry per lane (so the walk needs
+// no record iterator and its loop no branches). Lane r holds the address of
+// the wave's record r (records past the wave's last repeat it and are never
+// read) and the facts of its unit r: the super-block within the slice, whether
+// the unit starts a tile, and the byte offset of that tile's contribution
+// slot. The walk reads entries with a wave-uniform index (v_readlane). Every
+// unit stores its tile's running sum to the slot, so the tile's last unit
+// leaves the final one there, and a unit that starts a tile starts from zero.
+struct RecTab {
+  uint32_t lo, hi;  // record address
+  uint32_t info;    // super-block (bits 0-3) | starts a tile (bit 4) | slot offset (bits 8-31)
+};
+constexpr int TAB_MAX = 64;  // records (and units) of one wave a table holds
+
+template <bool Q6>
+__device__ __forceinline__ RecTab build_tab(const DevPhase& ph, WPtrs L, const Assign& a,
+                                            int wave, int lane) {
+  const int nm = uni(ph.nm);
+  const int ua = wave_begin(a, wave), ub = wave_begin(a, wave + 1);
+  const int nrec = (ub - ua) * nm;
+  const int nkb = a.nkb > 0 ? a.nkb : 1;
+  RecTab t;
+  {
+    const int r = lane < nrec ? lane : (nrec > 0 ? nrec - 1 : 0);
+    const int u = ua + (nm == 2 ? r >> 1 : r);
+    const int q = nm == 2 ? (r & 1) : 0;
+    const int tl = u / nkb;
+    const int b = u - tl * nkb;
+    const int tg = a.t0 + tl;
+    const int seg = (tg >= ph.seg_t0[1]) + (tg >= ph.seg_t0[2]);
+    const int mi = ph.mat0 + seg + q;
+    const unsigned rec = Q6 && ((L->q6 >> mi) & 1u) ? (unsigned)Q6W_REC : (unsigned)TILE_REC;
+    const unsigned idx = (unsigned)(tg - ph.seg_t0[seg]) * (unsigned)ph.KB + (unsigned)(a.kb0 + b);
+    const unsigned long long p =
+        reinterpret_cast<unsigned long long>(L->w[mi]) + (unsigned long long)idx * rec;
+    t.lo = (uint32_t)p;
+    t.hi = (uint32_t)(p >> 32);
+  }
+  {
+    const int nu = ub - ua;
+    const int u = ua + (lane < nu ? lane : (nu > 0 ? nu - 1 : 0));
+    const int tl = u / nkb;
+    const int b = u - tl * nkb;
+    const unsigned start = (b == 0 || u == ua) ? 1u : 0u;
+    const int first = wave_of_unit(a, tl * nkb);
+    const unsigned slot = (unsigned)((tl * ph.cmax + (wave - first)) * nm) * 1024u;
+    t.info = (unsigned)b | (start << 4) | (slot << 8);
+  }
+  return t;
+}
+
+// (readlane returns an int: each half goes through uint32_t, so that a low
+// word with bit 31 set is not sign-extended into the high one)
+__device__ __forceinline__ const uint8_t* tab_addr(const RecTab& t, int r) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)t.lo, r);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)t.hi, r);
+  return reinterpret_cast<const uint8_t*>(((unsigned long long)hi << 32) | lo);
+}
+
+// The table form of ring_fill.
+template <bool Q6>
+__device__ __forceinline__ void ring_fill_tab(BlockRegs (&ring)[STEP_PD], const RecTab& t,
+                                              const DevPhase& ph, WPtrs L, const Assign& a,
+                                              int wave, int lane) {
+  const int ua = wave_begin(a, wave), ub = wave_begin(a, wave + 1);
+  const int u6 = q6_first_unit<Q6>(ph, L, a);
+  const int nrec = ((ub < u6 ? ub : u6) - ua) * uni(ph.nm);
+#pragma unroll
+  for (int s = 0; s < STEP_PD; ++s)
+    if (s < nrec) load_rec(ring[s], tab_addr(t, s), lane);
+}
+
+// The table form of phase_compute (the same products, sums and contribution
+// slots; the waves' parts of a tile are added in wave order afterwards).
+template <int NM, bool Q6>
+__device__ __forceinline__ void phase_compute_tab(BlockRegs (&ring)[STEP_PD], const RecTab& t,
+                                                  const DevPhase& ph, WPtrs L,
+                                                  const Assign& a, int wave, int lane,
+                                                  const char* xa_lane, const char* xs_lane,
+                                                  char* contrib, const UnpackConsts& k) {
+  const int g = lane >> 4;
+  const int ua = wave_begin(a, wave), ub = wave_begin(a, wave + 1);
+  const int u6 = q6_first_unit<Q6>(ph, L, a);
+  const int u4 = ub < u6 ? ub : (ua > u6 ? ua : u6);
+  const int U = (u4 - ua) * NM;  // Q4_K records
+  if (U <= 0 && (!Q6 || u4 >= ub)) return;
+  floatx4 acc[NM];
+#pragma unroll
+  for (int q = 0; q < NM; ++q) acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+  char* slot_lane = contrib + lane * 16;
+  // unit uu of the wave (uniform): its super-block, a fresh sum at a tile's
+  // first unit, the product, and the running sum to the tile's slot
+  auto unit_info = [&](int uu, int& cb) {
+    const unsigned inf = (uint32_t)__builtin_amdgcn_readlane((int)t.info, uu);
+    cb = (int)(inf & 15u);
+    const bool fresh = (inf & 16u) != 0;  // a select, not a branch
+#pragma unroll
+    for (int q = 0; q < NM; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[q][e] = fresh ? 0.f : acc[q][e];
+    return slot_lane + (inf >> 8);
+  };
+  auto consume = [&](int s, int uu) {
+    int cb;
+    char* sl = unit_info(uu, cb);
+    mma_unit<NM>(&ring[s], g, xa_lane + cb * X_BYTES_PER_BLOCK,
+                 xs_lane + cb * XSUM_BYTES_PER_BLOCK, k, acc);
+#pragma unroll
+    for (int q = 0; q < NM; ++q) *reinterpret_cast<floatx4*>(sl + q * 1024) = acc[q];
+  };
+  // Record r sits in ring slot r % STEP_PD; once consumed, its slot takes
+  // record r + STEP_PD, if the wave has one (no load past the range).
+  int r0 = 0;
+  for (; r0 + 2 * STEP_PD <= U; r0 += STEP_PD) {
+#pragma unroll
+    for (int s = 0; s < STEP_PD; s += NM) {
+      consume(s, (r0 + s) / NM);
+#pragma unroll
+      for (int q = 0; q < NM; ++q) load_rec(ring[s + q], tab_addr(t, r0 + s + q + STEP_PD), lane);
+    }
+  }
+  for (; r0 < U; r0 += STEP_PD) {
+#pragma unroll
+    for (int s = 0; s < STEP_PD; s += NM) {
+      if (r0 + s >= U) break;
+      consume(s, (r0 + s) / NM);
+      if (r0 + s + STEP_PD < U) {
+#pragma unroll
+        for (int q = 0; q < NM; ++q)
+          load_rec(ring[s + q], tab_addr(t, r0 + s + q + STEP_PD), lane);
+      }
+    }
+  }
+  if constexpr (Q6) {
+    // the Q6_K tail (one record per unit), records U.. of the table, through
+    // the same ring slots (the Q4_K records are all used)
+    if constexpr (NM == 1) {
+      const int U6 = ub - u4;
+      if (U6 > 0) {
+        ScaleRegs6 s6[STEP_PD];
+#pragma unroll
+        for (int s = 0; s < STEP_PD; ++s)
+          if (s < U6) load_rec6(ring[s], s6[s], tab_addr(t, U + s), lane);
+        auto consume6 = [&](int s, int uu) {
+          int cb;
+          char* sl = unit_info(uu, cb);
+          mma_unit6(ring[s], s6[s], xa_lane + cb * X_BYTES_PER_BLOCK, acc[0]);
+          *reinterpret_cast<floatx4*>(sl) = acc[0];
+        };
+        int q0 = 0;
+        for (; q0 + 2 * STEP_PD <= U6; q0 += STEP_PD) {
+#pragma unroll
+          for (int s = 0; s < STEP_PD; ++s) {
+            consume6(s, U + q0 + s);
+            load_rec6(ring[s], s6[s], tab_addr(t, U + q0 + s + STEP_PD), lane);
+          }
+        }
+        for (; q0 < U6; q0 += STEP_PD) {
+#pragma unroll
+          for (int s = 0; s < STEP_PD; ++s) {
+            if (q0 + s >= U6) break;
+            consume6(s, U + q0 + s);
+            if (q0 + s + STEP_PD < U6)
+              load_rec6(ring[s], s6[s], tab_addr(t, U + q0 + s + STEP_PD), lane);
+          }
+        }
+      }
+    }
+  }
+}
+
 // Stream the wave's units and multiply them against the staged activations.
 // A tile the wave computes alone goes straight to its slice partial block in
 // the workspace (one 16-byte store per lane, issued while the stream goes
@@ -932,7 +1103,7 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
 // the residual walk (RMSNorm with weights, residual adds, SiLU * up). Q6: the
 // walk also reads Q6_K walk records (v and down of the layers that have them);
 // without it the kernel holds no Q6_K code at all.
-template <int MODE, bool Q6>
+template <int MODE, bool Q6, bool TAB>
 __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ DevLayer ltab[STEP_MAX_LAYERS];  // every layer's pointers, read from LDS
@@ -1003,9 +1174,15 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
 
   BlockRegs ring[STEP_PD];
   Iter it;
+  RecTab tb = {0u, 0u, 0u};
   Assign a = lds_assign(asg[0]);
-  iter_init<Q6>(it, ph_s[0], &ltab[0], wstart[0][wave], wseg[0][wave]);
-  ring_fill<Q6>(ring, it, ph_s[0], &ltab[0], a, lane);
+  if constexpr (TAB) {
+    tb = build_tab<Q6>(ph_s[0], &ltab[0], a, wave, lane);
+    ring_fill_tab<Q6>(ring, tb, ph_s[0], &ltab[0], a, wave, lane);
+  } else {
+    iter_init<Q6>(it, ph_s[0], &ltab[0], wstart[0][wave], wseg[0][wave]);
+    ring_fill<Q6>(ring, it, ph_s[0], &ltab[0], a, lane);
+  }
 
   // ---- layer-0 input: this workgroup's columns of it (MODE 0: a copy of
   //      x0; MODE 1: the cast of h0 times the first norm weight) and their
@@ -1082,12 +1259,21 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       // ---- stream the weights
       const char* xa_lane = x_lds + (size_t)arow * ph.x_stride + g * 128;
       const char* xs_lane = xs_lds + (size_t)arow * xsum_row_bytes(ph.nkb) + 16 * g;
-      if (ph.nm == 2)
-        phase_compute<2, Q6>(ring, it, ph_s[p], &ltab[l], a, wave, lane, xa_lane, xs_lane,
-                             contrib, k);
-      else
-        phase_compute<1, Q6>(ring, it, ph_s[p], &ltab[l], a, wave, lane, xa_lane, xs_lane,
-                             contrib, k);
+      if constexpr (TAB) {
+        if (ph.nm == 2)
+          phase_compute_tab<2, Q6>(ring, tb, ph_s[p], &ltab[l], a, wave, lane, xa_lane, xs_lane,
+                                   contrib, k);
+        else
+          phase_compute_tab<1, Q6>(ring, tb, ph_s[p], &ltab[l], a, wave, lane, xa_lane, xs_lane,
+                                   contrib, k);
+      } else {
+        if (ph.nm == 2)
+          phase_compute<2, Q6>(ring, it, ph_s[p], &ltab[l], a, wave, lane, xa_lane, xs_lane,
+                               contrib, k);
+        else
+          phase_compute<1, Q6>(ring, it, ph_s[p], &ltab[l], a, wave, lane, xa_lane, xs_lane,
+                               contrib, k);
+      }
       __syncthreads();
       tl_stamp(P, l, p, TL_COMPUTED);
 
@@ -1106,8 +1292,13 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       const int ln = p < 3 ? l : l + 1, pn = p < 3 ? p + 1 : 0;
       if (ln < P.n_layers) {
         a = lds_assign(asg[pn]);
-        iter_init<Q6>(it, ph_s[pn], &ltab[ln], wstart[pn][wave], wseg[pn][wave]);
-        ring_fill<Q6>(ring, it, ph_s[pn], &ltab[ln], a, lane);
+        if constexpr (TAB) {
+          tb = build_tab<Q6>(ph_s[pn], &ltab[ln], a, wave, lane);
+          ring_fill_tab<Q6>(ring, tb, ph_s[pn], &ltab[ln], a, wave, lane);
+        } else {
+          iter_init<Q6>(it, ph_s[pn], &ltab[ln], wstart[pn][wave], wseg[pn][wave]);
+          ring_fill<Q6>(ring, it, ph_s[pn], &ltab[ln], a, lane);
+        }
       }
       if (!wait_done(P, PH, l, p, &abort_s)) return;
       tl_stamp(P, l, p, TL_DONE_SEEN);
@@ -1158,6 +1349,7 @@ struct StepPlan {
   size_t tl_off;                // MK_STEP_TIMELINE: the stamps (0 otherwise)
   size_t total;
   bool ok = true;  // false: some K slice would get no workgroup
+  bool tab = false;  // every phase's waves fit a record table (DevPhase::tab)
 };
 
 // Host mirror of the device work split (the same shared functions).
@@ -1255,6 +1447,19 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
       }
     }
     if (ph.tw_max < 1) ph.tw_max = 1;
+    // the record table holds up to TAB_MAX records of a wave, and a unit's
+    // super-block in 4 bits
+    {
+      int maxrec = 0;
+      for (int w = 0; w < G; ++w) {
+        const Assign a = assign_split(ph.nt, ph.sk, ph.nkb, ph.KB, w, G);
+        for (int v = 0; v < SPLIT_WAVES; ++v) {
+          const int r = (wave_begin(a, v + 1) - wave_begin(a, v)) * ph.nm;
+          if (r > maxrec) maxrec = r;
+        }
+      }
+      ph.tab = maxrec <= TAB_MAX && ph.nkb <= 15 ? 1 : 0;
+    }
     {
       const size_t xb = (size_t)M * ph.x_stride + (size_t)M * xsum_row_bytes(ph.nkb);
       const size_t c0 = (xb + 15) & ~(size_t)15;
@@ -1275,6 +1480,7 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
   sp.sync_end = off;
   sp.layers_off = off;  // one layer table per row group
   off += align256((size_t)STEP_GROUPS * n_layers * sizeof(DevLayer));
+  sp.tab = sp.ph[0].tab && sp.ph[1].tab && sp.ph[2].tab && sp.ph[3].tab;
   sp.part_begin = off;
   for (int p = 0; p < 4; ++p) {
     sp.ph[p].part_off = off;
@@ -1355,9 +1561,15 @@ std::mutex g_table_mu;
 // table (re-sent only when it changed), the clear kernel and the launch.
 // Plan of a walk over M rows (a row group), with the checks made before any
 // work is enqueued: the split, the workspace size, the LDS and occupancy.
+// The kernel of a walk: with the Q6_K path or not, and with the record tables
+// (every wave of every phase fits one) or the record iterator.
 template <int MODE>
-const void* walk_kernel(bool q6) {
-  return q6 ? (const void*)q4k_step_kernel<MODE, true> : (const void*)q4k_step_kernel<MODE, false>;
+const void* walk_kernel(bool q6, bool tab) {
+  if (tab)
+    return q6 ? (const void*)q4k_step_kernel<MODE, true, true>
+              : (const void*)q4k_step_kernel<MODE, false, true>;
+  return q6 ? (const void*)q4k_step_kernel<MODE, true, false>
+            : (const void*)q4k_step_kernel<MODE, false, false>;
 }
 
 template <int MODE>
@@ -1379,11 +1591,12 @@ int prepare_walk(const mk_q4k_layer* layers, int n_layers, int M, size_t ws_byte
   }
   lds = lds_bytes(sp, M);
   if (lds + kStaticLds > kLdsLimit) return MK_EINVAL;
-  hipError_t e = hipFuncSetAttribute(walk_kernel<MODE>(q6),
+  hipError_t e = hipFuncSetAttribute(walk_kernel<MODE>(q6, sp.tab),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return MK_EHIP;
   int occ = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, walk_kernel<MODE>(q6), STEP_THREADS, lds);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, walk_kernel<MODE>(q6, sp.tab), STEP_THREADS,
+                                                    lds);
   if (e != hipSuccess) return MK_EHIP;
   if (occ < 1) return MK_EOCCUPANCY;
   return MK_OK;
@@ -1448,10 +1661,10 @@ int enqueue_walk(const mk_q4k_layer* layers, const std::vector<DevLayer>& table,
   P.status_off = sp.status_off;
   P.lds_bytes = lds;
   P.tl_off = sp.tl_off;
-  if (q6)
-    hipLaunchKernelGGL((q4k_step_kernel<MODE, true>), dim3(G), dim3(STEP_THREADS), lds, st, P);
-  else
-    hipLaunchKernelGGL((q4k_step_kernel<MODE, false>), dim3(G), dim3(STEP_THREADS), lds, st, P);
+  const void* kern = walk_kernel<MODE>(q6, sp.tab);
+  void* args[] = {&P};
+  e = hipLaunchKernel(kern, dim3(G), dim3(STEP_THREADS), args, lds, st);
+  if (e != hipSuccess) return MK_EHIP;
   e = hipGetLastError();
   return e == hipSuccess ? MK_OK : MK_EHIP;
 }
@@ -1534,7 +1747,12 @@ long long plan_violations(const mk_q4k_layer& L0, int n_layers, int M, int G) {
       for (int v = 0; v < SPLIT_WAVES; ++v) {
         const int ua = wave_begin(a, v), ub = wave_begin(a, v + 1);
         check(ua >= 0 && ua <= ub && ub <= a.U);
-        // every record the wave loads (the iterator never moves past ub - 1)
+        // a record table holds the wave's records and units, a unit's
+        // super-block in 4 bits and its slot offset in 24
+        if (ph.tab)
+          check((ub - ua) * ph.nm <= TAB_MAX && a.nkb <= 15 &&
+                (size_t)ph.tw_max * ph.cmax * ph.nm * 1024 < ((size_t)1 << 24));
+        // every record the wave loads (the walk never moves past ub - 1)
         for (int u = ua; u < ub; ++u) {
           const int tl = u / a.nkb, b = u % a.nkb, tg = a.t0 + tl;
           const int seg = (tg >= ph.seg_t0[1]) + (tg >= ph.seg_t0[2]);
@@ -1590,6 +1808,7 @@ long long plan_violations(const mk_q4k_layer& L0, int n_layers, int M, int G) {
     }
     for (size_t i = 0; i < cover.size(); ++i) check(cover[i] == 1);
   }
+  check(sp.tab == (sp.ph[0].tab && sp.ph[1].tab && sp.ph[2].tab && sp.ph[3].tab));
   // statistics slots of every (layer, phase) input, and the layer table
   check(sp.stats_off + (size_t)n_layers * 4 * STAT_SLOTS * M * 2 * sizeof(long long) <= sp.sync_end);
   check(sp.layers_off + (size_t)STEP_GROUPS * n_layers * sizeof(DevLayer) <= sp.part_begin);
