@@ -49,8 +49,8 @@ struct GemmArgs {
 };
 
 template <int MT>
-struct GemmRing {  // records in flight per wave (what the registers allow)
-  static constexpr int PD = MT == 1 ? 6 : 4;
+struct GemmRing {  // records in flight per wave (4: six were slower at one row tile)
+  static constexpr int PD = 4;
 };
 
 template <int MT, int FMT>
