@@ -158,6 +158,8 @@ def lib():
                                       vp, vp, vp, sz, vp]
             L.mk_q4k_step_status.restype = i
             L.mk_q4k_step_status.argtypes = [vp, ctypes.POINTER(i)]
+            L.mk_q4k_step_set_walk_form.restype = i
+            L.mk_q4k_step_set_walk_form.argtypes = [i]
         if hasattr(L, "mk_q8_attn_decode"):
             L.mk_q8_attn_workspace_bytes.restype = sz
             L.mk_q8_attn_workspace_bytes.argtypes = [i, i, i]
@@ -476,6 +478,16 @@ def attn_decode(Q, pool, block_table, row_len, rows_per_agent: int, n_kv: int, w
                                  workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc)
     return out
+
+
+MK_WALK_AUTO = 0
+MK_WALK_ITERATOR = 1
+
+
+def step_set_walk_form(form: int) -> None:
+    """Testing aid: MK_WALK_ITERATOR makes later walks use the record iterator
+    instead of the per-wave record tables (same results, bit for bit)."""
+    _check(lib().mk_q4k_step_set_walk_form(int(form)))
 
 
 def step_status(workspace) -> int:

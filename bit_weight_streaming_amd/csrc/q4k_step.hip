@@ -40,6 +40,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -1329,6 +1330,7 @@ namespace mk {
 namespace {
 
 constexpr int kMaxG = 1024;                    // most workgroups (CUs) planned for
+std::atomic<int> g_walk_form{MK_WALK_AUTO};     // mk_q4k_step_set_walk_form
 constexpr size_t kLdsLimit = 160 * 1024;
 // the kernel's static LDS arrays (layer and phase tables, work splits,
 // statistics), with room for alignment
@@ -1581,6 +1583,7 @@ int prepare_walk(const mk_q4k_layer* layers, int n_layers, int M, size_t ws_byte
   G = cus < kMaxG ? cus : kMaxG;
   plan_phases(layers[0], n_layers, M, G, sp);
   if (!sp.ok) return MK_EINVAL;
+  if (g_walk_form.load(std::memory_order_relaxed) == MK_WALK_ITERATOR) sp.tab = false;
   for (int p = 0; p < 4; ++p)
     sp.ph[p].norm = MODE == 0 ? NORM_STD : (p == 0 || p == 2 ? NORM_RMS : NORM_NONE);
   if (ws_bytes < sp.total) return MK_EWORKSPACE;
@@ -1827,6 +1830,12 @@ long long mk_q4k_step_timeline_offset(const mk_q4k_layer* layer0, int n_layers, 
   mk::StepPlan sp;
   mk::plan_phases(*layer0, n_layers, mk::group_rows(M, 0), mk::kMaxG, sp);
   return sp.ok ? (long long)sp.tl_off : -1;
+}
+
+int mk_q4k_step_set_walk_form(int form) {
+  if (form != MK_WALK_AUTO && form != MK_WALK_ITERATOR) return MK_EINVAL;
+  mk::g_walk_form.store(form, std::memory_order_relaxed);
+  return MK_OK;
 }
 
 long long mk_q4k_step_check_plan(const mk_q4k_layer* layer0, int n_layers, int M, int G) {

@@ -321,6 +321,20 @@ long long mk_q4k_step_check_plan(const mk_q4k_layer* layer0 /* host */, int n_la
                                  int G);
 
 /*
+ * mk_q4k_step_set_walk_form: a testing aid for the two forms of the walks'
+ * weight-record walk, which compute the same results bit for bit.
+ * MK_WALK_AUTO (the default): a wave reads its records' addresses from a
+ * per-phase record table held in registers (a branch-free streaming loop)
+ * whenever every wave of every phase has at most 64 records, else it walks
+ * them with the record iterator. MK_WALK_ITERATOR: always the iterator.
+ * Process-wide; applies to step calls made after it returns (a call already
+ * enqueued keeps its form). MK_EINVAL for any other value.
+ */
+#define MK_WALK_AUTO 0
+#define MK_WALK_ITERATOR 1
+int mk_q4k_step_set_walk_form(int form);
+
+/*
  * mk_q4k_step_timeline_offset: a measurement aid. In a library built with
  * MK_STEP_TIMELINE=1 the walks store, per layer l, phase p (0..3) and
  * workgroup w (G = the device's CU count), eight u64 wall-clock slots

@@ -222,3 +222,14 @@ def test_q6k_step_bytes(L):
     assert L.mk_q6k_step_bytes(16, 256) == 3360 + 16 * 4
     assert L.mk_q6k_step_bytes(17, 512) == 2 * 2 * 3360 + 32 * 4
     assert L.mk_q6k_step_bytes(16, 300) == 0 and L.mk_q6k_step_bytes(0, 256) == 0
+
+
+def test_walk_form_switch_on_the_host(L):
+    """The walk-form switch needs no device: it takes the two documented
+    values and refuses others (the GPU tests compare the two forms)."""
+    L.mk_q4k_step_set_walk_form.restype = ctypes.c_int
+    L.mk_q4k_step_set_walk_form.argtypes = [ctypes.c_int]
+    assert L.mk_q4k_step_set_walk_form(2) == mk.MK_EINVAL
+    assert L.mk_q4k_step_set_walk_form(-1) == mk.MK_EINVAL
+    assert L.mk_q4k_step_set_walk_form(mk.MK_WALK_ITERATOR) == 0
+    assert L.mk_q4k_step_set_walk_form(mk.MK_WALK_AUTO) == 0

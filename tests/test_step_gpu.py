@@ -376,3 +376,35 @@ def test_q6k_mixed_full_size_layers():
     worst = check_stack(stack, ncols=2048, seed=77)
     check_out(stack)
     print(f"full-size mixed layers: worst |err|/S = {worst:.3e}")
+
+
+def _outputs(stack):
+    return [t.clone() for io in stack.io for t in io["y"] + io["x"]] + [stack.x_out.clone()]
+
+
+@pytest.mark.parametrize("case", ["small", "ragged", "q6k_mixed"])
+def test_record_tables_and_iterator_agree_bit_for_bit(case):
+    """The two forms of the weight-record walk (per-wave record tables read
+    with readlane, and the record iterator kept for waves with more than 64
+    records) multiply the same records in the same order: every output of
+    the step must be the same, bit for bit, and the iterator form must pass
+    the oracle check as well."""
+    kw = dict(small=(SMALL, ()), ragged=(RAGGED, ()), q6k_mixed=(SMALL, Q6_MIXED))[case]
+    shp, q6 = kw
+    a = Stack(2, 12, shp, seed=90, device=DEV, q6=q6)
+    b = Stack(2, 12, shp, seed=90, device=DEV, q6=q6)
+    run_step(a)
+    try:
+        mk.step_set_walk_form(mk.MK_WALK_ITERATOR)
+        run_step(b)
+    finally:
+        mk.step_set_walk_form(mk.MK_WALK_AUTO)
+    for u, v in zip(_outputs(a), _outputs(b)):
+        assert torch.equal(u, v)
+    check_stack(b)
+
+
+def test_walk_form_rejects_unknown_values():
+    with pytest.raises(mk.MkError) as e:
+        mk.step_set_walk_form(7)
+    assert e.value.code == mk.MK_EINVAL

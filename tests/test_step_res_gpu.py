@@ -207,3 +207,21 @@ def test_res_workload_weights_leave_the_range_and_say_so():
     mk.step_res(descs, stack.io, stack.norms, stack.h0, ws, 12)
     torch.cuda.synchronize()
     assert mk.step_status(ws) == mk.MK_ERANGE
+
+
+def test_res_record_tables_and_iterator_agree_bit_for_bit():
+    """The residual walk in both forms of the weight-record walk (record
+    tables, record iterator): every output, residual and cast the same, bit
+    for bit."""
+    a = ResStack(2, 12, SMALL, seed=48, device=DEV)
+    b = ResStack(2, 12, SMALL, seed=48, device=DEV)
+    run_res(a)
+    try:
+        mk.step_set_walk_form(mk.MK_WALK_ITERATOR)
+        run_res(b)
+    finally:
+        mk.step_set_walk_form(mk.MK_WALK_AUTO)
+    for la, lb in zip(a.io, b.io):
+        for u, v in zip(la["y"] + la["x"] + la["h"], lb["y"] + lb["x"] + lb["h"]):
+            assert torch.equal(u, v)
+    check_res_stack(b)
