@@ -482,11 +482,14 @@ def attn_decode(Q, pool, block_table, row_len, rows_per_agent: int, n_kv: int, w
 
 MK_WALK_AUTO = 0
 MK_WALK_ITERATOR = 1
+MK_WALK_RELOAD_STATS = 2
 
 
 def step_set_walk_form(form: int) -> None:
-    """Testing aid: MK_WALK_ITERATOR makes later walks use the record iterator
-    instead of the per-wave record tables (same results, bit for bit)."""
+    """Testing aid (flags, OR-ed): MK_WALK_ITERATOR makes later walks use the
+    record iterator instead of the per-wave record tables; MK_WALK_RELOAD_STATS
+    makes every phase reload its input statistics at the end of its compute.
+    The results are the same, bit for bit."""
     _check(lib().mk_q4k_step_set_walk_form(int(form)))
 
 

@@ -38,9 +38,20 @@ enum TlEvent { TL_START = 0, TL_COMPUTED = 1, TL_PUBLISHED = 2, TL_FINISHED = 3,
 // integer atomics, so the totals do not depend on the order in which
 // workgroups add them. One contribution (a tile row) must stay below 2^50 in
 // magnitude, which keeps any total of up to 8192 tiles inside 63 bits.
+//
+// Each workgroup sums its contributions in LDS and adds its share S to the
+// word of its slot (workgroup w: slot w % STAT_SLOTS) as 32 S + 1, after it
+// has counted its tiles finished. The low five bits of a word count the
+// shares that are in, so a consumer that staged the words before every share
+// arrived sees it (all words of a phase input count 2 M G shares when
+// complete) and reloads them before it needs the totals. A slot's sum must
+// stay below 2^58 in magnitude: at most STAT_SLOT_TERMS contributions of 2^50
+// per slot, which the plan checks.
 constexpr double STAT_SCALE_SUM = 16777216.0;
 constexpr double STAT_SCALE_SQ = 1048576.0;
 constexpr double STAT_TERM_MAX = 1125899906842624.0;  // 2^50
+constexpr int STAT_CNT_BITS = 5;                      // share count in the low bits
+constexpr int STAT_SLOT_TERMS = 255;                  // 255 * 2^50 < 2^58
 
 // A slice partial carries the parity of its layer in the lowest bit of each
 // word: the producer sets it, the finisher waits until every word of a piece
@@ -127,6 +138,8 @@ struct StepParams {
   size_t status_off;     // int status word
   size_t lds_bytes;
   size_t tl_off;         // MK_STEP_TIMELINE: [n_layers][4][G][TL_EVENTS] u64 stamps
+  int reload;            // testing aid: every phase reloads its input statistics at
+                         // the end of its compute, as when they were staged incomplete
 };
 
 }  // namespace mk

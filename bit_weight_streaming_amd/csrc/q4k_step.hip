@@ -58,6 +58,17 @@ constexpr int kStageRound = 10;  // staging chunks a thread loads before using t
 // statistics slot values (STAT_SLOTS x M x 2) each thread reads when staging
 constexpr int kStatPer = (STAT_SLOTS * STEP_MAX_M * 2 + STEP_THREADS - 1) / STEP_THREADS;
 
+// A statistics word: 32 S + 1 for a share S, its share count, its sum.
+__device__ __forceinline__ long long stat_share(unsigned long long s) {
+  return (long long)((s << STAT_CNT_BITS) + 1u);
+}
+__device__ __forceinline__ int stat_count(long long v) {
+  return (int)(v & ((1 << STAT_CNT_BITS) - 1));
+}
+__device__ __forceinline__ unsigned long long stat_sum(long long v) {
+  return (unsigned long long)(v >> STAT_CNT_BITS);  // arithmetic: exact for negative sums
+}
+
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Timeline stamp (MK_STEP_TIMELINE builds only): thread 0 stores the wall
@@ -580,7 +591,7 @@ template <int R>
 __device__ __forceinline__ void stage_rounds(const uint16_t* src, int K, int M, const Assign& a,
                                             const long long* st, unsigned long long* tot_s,
                                             char* x_lds, int x_stride, char* xs_lds,
-                                            int xs_row, int tid) {
+                                            int xs_row, int* cnt_s, int tid) {
   const int cpr = a.nkb * 32;  // 8-wide chunks per row
   const int items = M * cpr;   // at most STEP_THREADS * R
   // row of chunk index x < 2^16: x * magic / 2^32 (cpr < 2^16)
@@ -631,10 +642,18 @@ __device__ __forceinline__ void stage_rounds(const uint16_t* src, int K, int M, 
     if ((ch & 3) == 0)
       put_xsum(xs_lds + (size_t)m * xs_row + b * XSUM_BYTES_PER_BLOCK, kk >> 5, split_xsum(sum));
   }
+  int cnt = 0;  // shares counted in this thread's words
 #pragma unroll
   for (int i = 0; i < kStatPer; ++i)
-    if (i * STEP_THREADS + uni(tid & ~63) < nv)
-      atomicAdd(&tot_s[(i * STEP_THREADS + tid) % (2 * M)], (unsigned long long)pv[i]);
+    if (i * STEP_THREADS + uni(tid & ~63) < nv) {
+      cnt += stat_count(pv[i]);
+      atomicAdd(&tot_s[(i * STEP_THREADS + tid) % (2 * M)], stat_sum(pv[i]));
+    }
+  // the wave's count (exact in fp32) into the workgroup's
+  const int rs = (int)row_sum16((float)cnt);
+  const int wc = __builtin_amdgcn_readlane(rs, 0) + __builtin_amdgcn_readlane(rs, 16) +
+                 __builtin_amdgcn_readlane(rs, 32) + __builtin_amdgcn_readlane(rs, 48);
+  if ((tid & 63) == 0) atomicAdd(cnt_s, wc);
 }
 
 // Staging with the number of load rounds the slice needs (one per
@@ -643,11 +662,11 @@ __device__ __forceinline__ void stage_rounds(const uint16_t* src, int K, int M, 
 __device__ __forceinline__ void stage_slice(const uint16_t* src, int K, int M, const Assign& a,
                                             const long long* st, unsigned long long* tot_s,
                                             char* x_lds, int x_stride, char* xs_lds,
-                                            int xs_row, int tid) {
+                                            int xs_row, int* cnt_s, int tid) {
   static_assert(kStageRound == 10, "one instantiation per round count");
   const int r = uni((M * a.nkb * 32 + STEP_THREADS - 1) / STEP_THREADS);
 #define MK_STAGE(RR) \
-  stage_rounds<RR>(src, K, M, a, st, tot_s, x_lds, x_stride, xs_lds, xs_row, tid)
+  stage_rounds<RR>(src, K, M, a, st, tot_s, x_lds, x_stride, xs_lds, xs_row, cnt_s, tid)
   if (r > 7) MK_STAGE(10);
   else if (r > 5) MK_STAGE(7);
   else if (r > 4) MK_STAGE(5);
@@ -942,9 +961,6 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
     h_new = uni(h_new);
     gn = uni(gn);
   }
-  const int ln_ = p < 3 ? l : l + 1, pn = p < 3 ? p + 1 : 0;
-  long long* stl = reinterpret_cast<long long*>(P.ws + P.stats_off) +
-                   (size_t)(ln_ * 4 + pn) * STAT_SLOTS * M * 2;
   const int tasks = nfin * 64;
   const unsigned par = (unsigned)l & 1u;
   const unsigned long long t0 = wall_clock64();
@@ -1003,13 +1019,6 @@ __device__ __forceinline__ void fixup_tiles(const StepParams& P, const DevPhase&
     }
     fixup_finish<NM, MODE>(P, ph, p, L, xn, stats, h_new, rc, tg, ln, y, csum, mom_s, wst);
   }
-  __syncthreads();
-  if (stats && tid < 2 * M) {
-    const long long v = (long long)wst[tid];
-    if (v != 0)
-      __hip_atomic_fetch_add(stl + (size_t)(blockIdx.x % STAT_SLOTS) * M * 2 + tid, v,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
 
 // Wait until every workgroup has added its share of the layer-0 input
@@ -1040,6 +1049,35 @@ __device__ __forceinline__ bool wait_start(const StepParams& P, int* abort_s) {
   return *abort_s == 0;
 }
 
+// Statistics of the phase input that were not complete when the slice was
+// staged: wave 0 reloads every word until all shares are in (every word of
+// a slot counts one share per workgroup of the slot, 2 M G in all) and adds
+// them up again into tot_s. Returns false if the walk is aborted.
+__device__ __forceinline__ bool reload_stats(const StepParams& P, const long long* st,
+                                             unsigned long long* tot_s, int lane) {
+  const int M = P.M, nv = STAT_SLOTS * M * 2;
+  const unsigned long long t0 = wall_clock64();
+  for (;;) {
+    if (lane < 2 * STEP_MAX_M) tot_s[lane] = 0ull;
+    int cnt = 0;
+    for (int idx = lane; idx < nv; idx += 64) {
+      const long long v = ld_dev(st + idx);
+      cnt += stat_count(v);
+      atomicAdd(&tot_s[idx % (2 * M)], stat_sum(v));
+    }
+    const int rs = (int)row_sum16((float)cnt);
+    const int wc = __builtin_amdgcn_readlane(rs, 0) + __builtin_amdgcn_readlane(rs, 16) +
+                   __builtin_amdgcn_readlane(rs, 32) + __builtin_amdgcn_readlane(rs, 48);
+    if (wc == 2 * M * P.G) return true;
+    if (ld_dev(reinterpret_cast<const int*>(P.ws + P.status_off)) != 0) return false;
+    if (wall_clock64() - t0 > kTimeoutTicks) {
+      set_status(P, MK_ETIMEOUT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
 // End of a phase in one workgroup: add the wave parts of each tile and
 // publish the tile's slice partial; then, for the tiles this workgroup
 // finishes (tile t is finished by the workgroup of slice t % sk), wait until
@@ -1052,8 +1090,8 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
                                               int l, const DevLayer* ltab, const Assign& a,
                                               int ffirst, int nfin, const char* contrib,
                                               int* abort_s, unsigned long long* wst,
-                                              const unsigned long long* tot_s, float2* mom_s,
-                                              int tid) {
+                                              unsigned long long* tot_s, float2* mom_s,
+                                              int* cnt_s, int tid) {
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.ws + ph.part_off, ph.part_bytes);
   if (tid < 2 * STEP_MAX_M) wst[tid] = 0ull;
   // Every tile's wave parts sit in LDS (slot: tile, wave - first wave of the
@@ -1084,6 +1122,16 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
     mom_s[tid] = tid < P.M ? phase_moments(tot_s, tid, ph) : float2{0.f, 0.f};
   __syncthreads();
   tl_stamp(P, l, p, TL_PUBLISHED);
+  if (ph.norm != NORM_NONE && (*cnt_s != 2 * P.M * P.G || P.reload)) {  // the same in every thread
+    const long long* st = reinterpret_cast<const long long*>(P.ws + P.stats_off) +
+                          (size_t)(l * 4 + p) * STAT_SLOTS * P.M * 2;
+    if (tid < 64 && !reload_stats(P, st, tot_s, tid)) *abort_s = 1;  // wave 0
+    __syncthreads();
+    if (*abort_s) return false;
+    if (tid < STEP_MAX_M)
+      mom_s[tid] = tid < P.M ? phase_moments(tot_s, tid, ph) : float2{0.f, 0.f};
+    __syncthreads();
+  }
   fixup_tiles<NM, MODE>(P, ph, p, l, ltab, a, ffirst, nfin, wst, mom_s, abort_s, tid);
   wait_vm0();
   __syncthreads();
@@ -1093,6 +1141,19 @@ __device__ __forceinline__ bool phase_outputs(const StepParams& P, const DevPhas
     unsigned* done = reinterpret_cast<unsigned*>(P.ws + P.done_off);
     const int tg = a.t0 + ffirst + tid * ph.sk;
     __hip_atomic_fetch_add(done + (size_t)(tg % DONE_CTRS) * CTR_STRIDE, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // the next input's statistics: this workgroup's share of each word, after
+  // the done counters (a consumer that reads a word before every share is in
+  // sees it by the count and reloads at the end of its phase)
+  const bool stats = MODE == 0 ? (p < 3 || l + 1 < P.n_layers)
+                               : (p == 1 || (p == 3 && l + 1 < P.n_layers));
+  if (stats && tid < 2 * P.M) {
+    const int ln = p < 3 ? l : l + 1, pn = p < 3 ? p + 1 : 0;
+    long long* stl = reinterpret_cast<long long*>(P.ws + P.stats_off) +
+                     (size_t)(ln * 4 + pn) * STAT_SLOTS * P.M * 2;
+    __hip_atomic_fetch_add(stl + (size_t)(blockIdx.x % STAT_SLOTS) * P.M * 2 + tid,
+                           stat_share(wst[tid]), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
   }
   return true;
@@ -1120,6 +1181,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
   __shared__ float2 mom_s[STEP_MAX_M];                  // its rows' mean and 1/sigma
   __shared__ unsigned long long wst_s[2 * STEP_MAX_M];  // next input's statistics, being added
   __shared__ int abort_s;
+  __shared__ int cnt_s;  // shares counted in the phase input's statistics words when staged
   const int M = P.M;
   const int w = blockIdx.x;
   const int tid = threadIdx.x;
@@ -1167,6 +1229,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
     wst_s[tid] = 0ull;
     tot_s[tid] = 0ull;
   }
+  if (tid == 0) cnt_s = 0;
   __syncthreads();
   const UnpackConsts k = unpack_consts(g);
   // Rows past M read row M-1 (their results are never stored), so every
@@ -1226,9 +1289,9 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       long long* st0 = reinterpret_cast<long long*>(P.ws + P.stats_off);
       const long long v = (long long)wst_s[tid];
       if (MODE == 0 && !(fabs((double)v) < STAT_TERM_MAX)) set_status(P, MK_ERANGE);
-      if (v != 0)
-        __hip_atomic_fetch_add(st0 + (size_t)(w % STAT_SLOTS) * M * 2 + tid, v, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(st0 + (size_t)(w % STAT_SLOTS) * M * 2 + tid,
+                             stat_share((unsigned long long)v), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
     }
     wait_vm0();
     __syncthreads();
@@ -1253,7 +1316,7 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       stage_slice(MODE == 0 && l == 0 && p == 0 ? P.x0 : L->x[p], ph.K, M, a,
                   reinterpret_cast<const long long*>(P.ws + P.stats_off) +
                       (size_t)(l * 4 + p) * STAT_SLOTS * M * 2,
-                  tot_s, x_lds, ph.x_stride, xs_lds, xsum_row_bytes(ph.nkb), tid);
+                  tot_s, x_lds, ph.x_stride, xs_lds, xsum_row_bytes(ph.nkb), &cnt_s, tid);
       __syncthreads();
       tl_stamp(P, l, p, TL_START);
 
@@ -1283,13 +1346,14 @@ __global__ void __launch_bounds__(STEP_THREADS) q4k_step_kernel(StepParams P) {
       const int ffirst = uni(fin_s[p].x), nfin = uni(fin_s[p].y);
       const bool ok = ph.nm == 2
                           ? phase_outputs<2, MODE>(P, ph, p, l, ltab, a, ffirst, nfin, contrib, &abort_s,
-                                             wst_s, tot_s, mom_s, tid)
+                                             wst_s, tot_s, mom_s, &cnt_s, tid)
                           : phase_outputs<1, MODE>(P, ph, p, l, ltab, a, ffirst, nfin, contrib, &abort_s,
-                                             wst_s, tot_s, mom_s, tid);
+                                             wst_s, tot_s, mom_s, &cnt_s, tid);
       if (!ok) return;
       // the next staging adds the next input's statistics from zero (ordered
       // before its atomics by the barrier that ends wait_done)
       if (tid < 2 * STEP_MAX_M) tot_s[tid] = 0ull;
+      if (tid == 0) cnt_s = 0;
       const int ln = p < 3 ? l : l + 1, pn = p < 3 ? p + 1 : 0;
       if (ln < P.n_layers) {
         a = lds_assign(asg[pn]);
@@ -1352,6 +1416,7 @@ struct StepPlan {
   size_t total;
   bool ok = true;  // false: some K slice would get no workgroup
   bool tab = false;  // every phase's waves fit a record table (DevPhase::tab)
+  bool reload = false;  // MK_WALK_RELOAD_STATS: every phase reloads its input statistics
 };
 
 // Host mirror of the device work split (the same shared functions).
@@ -1483,6 +1548,18 @@ void plan_phases(const mk_q4k_layer& L0, int n_layers, int M, int G, StepPlan& s
   sp.layers_off = off;  // one layer table per row group
   off += align256((size_t)STEP_GROUPS * n_layers * sizeof(DevLayer));
   sp.tab = sp.ph[0].tab && sp.ph[1].tab && sp.ph[2].tab && sp.ph[3].tab;
+  // each statistics slot's sum stays below 2^58 (STAT_SLOT_TERMS terms of
+  // at most 2^50): the slot's workgroups times the tiles one finishes, and
+  // times the layer-0 input columns one adds up (RMS terms, one per value)
+  {
+    const int per_slot = (G + STAT_SLOTS - 1) / STAT_SLOTS;
+    for (int p = 0; p < 4; ++p) {
+      const int nfin = (sp.ph[p].tw_max + sp.ph[p].sk - 1) / sp.ph[p].sk;
+      if ((long long)per_slot * nfin > STAT_SLOT_TERMS) sp.ok = false;
+    }
+    const int H = L0.q.K;
+    if ((long long)per_slot * ((H + G - 1) / G) > STAT_SLOT_TERMS) sp.ok = false;
+  }
   sp.part_begin = off;
   for (int p = 0; p < 4; ++p) {
     sp.ph[p].part_off = off;
@@ -1583,7 +1660,9 @@ int prepare_walk(const mk_q4k_layer* layers, int n_layers, int M, size_t ws_byte
   G = cus < kMaxG ? cus : kMaxG;
   plan_phases(layers[0], n_layers, M, G, sp);
   if (!sp.ok) return MK_EINVAL;
-  if (g_walk_form.load(std::memory_order_relaxed) == MK_WALK_ITERATOR) sp.tab = false;
+  const int form = g_walk_form.load(std::memory_order_relaxed);
+  if (form & MK_WALK_ITERATOR) sp.tab = false;
+  sp.reload = (form & MK_WALK_RELOAD_STATS) != 0;
   for (int p = 0; p < 4; ++p)
     sp.ph[p].norm = MODE == 0 ? NORM_STD : (p == 0 || p == 2 ? NORM_RMS : NORM_NONE);
   if (ws_bytes < sp.total) return MK_EWORKSPACE;
@@ -1664,6 +1743,7 @@ int enqueue_walk(const mk_q4k_layer* layers, const std::vector<DevLayer>& table,
   P.status_off = sp.status_off;
   P.lds_bytes = lds;
   P.tl_off = sp.tl_off;
+  P.reload = sp.reload ? 1 : 0;
   const void* kern = walk_kernel<MODE>(q6, sp.tab);
   void* args[] = {&P};
   e = hipLaunchKernel(kern, dim3(G), dim3(STEP_THREADS), args, lds, st);
@@ -1833,7 +1913,7 @@ long long mk_q4k_step_timeline_offset(const mk_q4k_layer* layer0, int n_layers, 
 }
 
 int mk_q4k_step_set_walk_form(int form) {
-  if (form != MK_WALK_AUTO && form != MK_WALK_ITERATOR) return MK_EINVAL;
+  if ((form & ~(MK_WALK_ITERATOR | MK_WALK_RELOAD_STATS)) != 0) return MK_EINVAL;
   mk::g_walk_form.store(form, std::memory_order_relaxed);
   return MK_OK;
 }

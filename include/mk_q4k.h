@@ -321,17 +321,23 @@ long long mk_q4k_step_check_plan(const mk_q4k_layer* layer0 /* host */, int n_la
                                  int G);
 
 /*
- * mk_q4k_step_set_walk_form: a testing aid for the two forms of the walks'
- * weight-record walk, which compute the same results bit for bit.
- * MK_WALK_AUTO (the default): a wave reads its records' addresses from a
+ * mk_q4k_step_set_walk_form: a testing aid that selects other forms of the
+ * walks, which compute the same results bit for bit. Flags, OR-ed:
+ * MK_WALK_AUTO (0, the default): a wave reads its records' addresses from a
  * per-phase record table held in registers (a branch-free streaming loop)
  * whenever every wave of every phase has at most 64 records, else it walks
- * them with the record iterator. MK_WALK_ITERATOR: always the iterator.
+ * them with the record iterator; a phase reloads the row statistics of its
+ * input at the end of its compute only if some workgroup's share was not yet
+ * added when it staged them.
+ * MK_WALK_ITERATOR: always the record iterator.
+ * MK_WALK_RELOAD_STATS: every phase reloads its input statistics (the path
+ * otherwise taken only when a share arrives late).
  * Process-wide; applies to step calls made after it returns (a call already
- * enqueued keeps its form). MK_EINVAL for any other value.
+ * enqueued keeps its form). MK_EINVAL for any other bit.
  */
 #define MK_WALK_AUTO 0
 #define MK_WALK_ITERATOR 1
+#define MK_WALK_RELOAD_STATS 2
 int mk_q4k_step_set_walk_form(int form);
 
 /*

@@ -225,11 +225,14 @@ def test_q6k_step_bytes(L):
 
 
 def test_walk_form_switch_on_the_host(L):
-    """The walk-form switch needs no device: it takes the two documented
-    values and refuses others (the GPU tests compare the two forms)."""
+    """The walk-form switch needs no device: it takes the documented flags,
+    alone or together, and refuses other bits (the GPU tests compare the
+    forms)."""
     L.mk_q4k_step_set_walk_form.restype = ctypes.c_int
     L.mk_q4k_step_set_walk_form.argtypes = [ctypes.c_int]
-    assert L.mk_q4k_step_set_walk_form(2) == mk.MK_EINVAL
+    assert L.mk_q4k_step_set_walk_form(4) == mk.MK_EINVAL
     assert L.mk_q4k_step_set_walk_form(-1) == mk.MK_EINVAL
     assert L.mk_q4k_step_set_walk_form(mk.MK_WALK_ITERATOR) == 0
+    assert L.mk_q4k_step_set_walk_form(mk.MK_WALK_RELOAD_STATS) == 0
+    assert L.mk_q4k_step_set_walk_form(mk.MK_WALK_ITERATOR | mk.MK_WALK_RELOAD_STATS) == 0
     assert L.mk_q4k_step_set_walk_form(mk.MK_WALK_AUTO) == 0

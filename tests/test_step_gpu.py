@@ -382,20 +382,30 @@ def _outputs(stack):
     return [t.clone() for io in stack.io for t in io["y"] + io["x"]] + [stack.x_out.clone()]
 
 
+WALK_FORMS = {
+    "iterator": mk.MK_WALK_ITERATOR,
+    "reload_stats": mk.MK_WALK_RELOAD_STATS,
+    "iterator_reload_stats": mk.MK_WALK_ITERATOR | mk.MK_WALK_RELOAD_STATS,
+}
+
+
+@pytest.mark.parametrize("form", list(WALK_FORMS))
 @pytest.mark.parametrize("case", ["small", "ragged", "q6k_mixed"])
-def test_record_tables_and_iterator_agree_bit_for_bit(case):
-    """The two forms of the weight-record walk (per-wave record tables read
-    with readlane, and the record iterator kept for waves with more than 64
-    records) multiply the same records in the same order: every output of
-    the step must be the same, bit for bit, and the iterator form must pass
-    the oracle check as well."""
+def test_walk_forms_agree_bit_for_bit(case, form):
+    """The forms of the walk compute the same products in the same order:
+    the weight records read through per-wave record tables or the record
+    iterator (kept for waves with more than 64 records), and the input
+    statistics taken as staged or reloaded at the end of every phase (the
+    path a phase takes when some workgroup's share was not yet in when it
+    staged). Every output of the step must be the same, bit for bit, and the
+    other form must pass the oracle check as well."""
     kw = dict(small=(SMALL, ()), ragged=(RAGGED, ()), q6k_mixed=(SMALL, Q6_MIXED))[case]
     shp, q6 = kw
     a = Stack(2, 12, shp, seed=90, device=DEV, q6=q6)
     b = Stack(2, 12, shp, seed=90, device=DEV, q6=q6)
     run_step(a)
     try:
-        mk.step_set_walk_form(mk.MK_WALK_ITERATOR)
+        mk.step_set_walk_form(WALK_FORMS[form])
         run_step(b)
     finally:
         mk.step_set_walk_form(mk.MK_WALK_AUTO)
@@ -406,5 +416,5 @@ def test_record_tables_and_iterator_agree_bit_for_bit(case):
 
 def test_walk_form_rejects_unknown_values():
     with pytest.raises(mk.MkError) as e:
-        mk.step_set_walk_form(7)
+        mk.step_set_walk_form(4)
     assert e.value.code == mk.MK_EINVAL

@@ -209,15 +209,18 @@ def test_res_workload_weights_leave_the_range_and_say_so():
     assert mk.step_status(ws) == mk.MK_ERANGE
 
 
-def test_res_record_tables_and_iterator_agree_bit_for_bit():
-    """The residual walk in both forms of the weight-record walk (record
-    tables, record iterator): every output, residual and cast the same, bit
-    for bit."""
+@pytest.mark.parametrize("form", ["iterator", "reload_stats"])
+def test_res_walk_forms_agree_bit_for_bit(form):
+    """The residual walk in the other forms of the walk (the record iterator
+    instead of record tables; the normed phases' input statistics reloaded
+    at the end of every phase): every output, residual and cast the same,
+    bit for bit."""
     a = ResStack(2, 12, SMALL, seed=48, device=DEV)
     b = ResStack(2, 12, SMALL, seed=48, device=DEV)
     run_res(a)
     try:
-        mk.step_set_walk_form(mk.MK_WALK_ITERATOR)
+        mk.step_set_walk_form(
+            dict(iterator=mk.MK_WALK_ITERATOR, reload_stats=mk.MK_WALK_RELOAD_STATS)[form])
         run_res(b)
     finally:
         mk.step_set_walk_form(mk.MK_WALK_AUTO)
