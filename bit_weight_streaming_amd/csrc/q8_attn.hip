@@ -14,19 +14,17 @@
 // query vectors of the (agent, KV head) ride in one wave (up to 32: two
 // 16-column MFMA tiles), so every K and V byte is read once per step.
 //
-// Per page (16 tokens), with MFMA (f16 in, fp32 accumulate):
+// Per page (16 tokens), with MFMA (binary16 scores, bfloat16 values, fp32
+// accumulate):
 //   scores  S^T[t][q] = sum_u ks[t][u] * (Kq_u . Q_u)  - four 16x16x32 MFMAs
 //           per query tile, one per 32-dim q8_0 block u, the int8 quants
 //           entering exactly and each block's scale applied to its product;
 //   softmax online over the pages, in the log2 domain, per query column;
 //   values  O^T[d][q] += sigma * (Vq^T . B), B[t][q] = p[t][q] * vs[t][b] /
-//           sigma * 2^12 split into binary16 hi + lo (two 16x16x16 MFMAs per
-//           16-dim tile), sigma a power of two at least the page's largest V
-//           scale, so B is at most 2^12; the 2^12 is taken out at the end.
-//           The lo part is scaled by 2^13 against quants scaled by 2^-13
-//           (see split_hl); weights too small for hi + lo to hold to 2^-17
-//           get further parts rebased by 2^32 each (see RB_PARTS), only in
-//           waves that hold one.
+//           sigma * 2^12 split exactly into three bfloat16 parts (three
+//           16x16x16 MFMAs per 16-dim tile, the quants as bfloat16), sigma a
+//           power of two at least the page's largest V scale, so B is at
+//           most 2^12; the 2^12 is taken out at the end.
 // S^T comes out of the score MFMA in exactly the register layout the value
 // MFMA wants for its B operand (4 consecutive tokens of one query per lane),
 // so no transpose is needed.
@@ -169,120 +167,74 @@ __device__ __forceinline__ half4v i8x4_to_h4(uint32_t w) {
   return __builtin_bit_cast(half4v, b) - half4v{k, k, k, k};
 }
 
-// The value weights enter the matrix cores as two binary16 parts: hi = v
-// rounded toward zero, and lo = the rest times 2^13, rounded toward zero,
-// multiplied by value quants scaled by 2^-13 (q * 2^-13 is exact in
-// binary16 for any int8 q). Both differences are exact in fp32 (each
-// truncation keeps leading bits of its operand), so r = what is left, times
-// 2^13, is exact too. For |v| <= 2^12 the two parts hold v to 2^-17 of
-// itself down to |v| = 2^-18 (FINE): where hi is normal, hi and lo give 11
-// bits each (2^-20); below 2^-14 hi leaves less than 2^-24, which lo holds
-// to 2^-35 (2^-37 once it is subnormal too).
-constexpr float LO_UP = 8192.0f;                // 2^13
-constexpr float LO_DOWN = 1.220703125e-4f;      // 2^-13
-constexpr float FINE = 3.814697265625e-6f;      // 2^-18
-__device__ __forceinline__ void split_hl(float v0, float v1, uint32_t& hi, uint32_t& lo,
-                                         float& r0, float& r1) {
-  const auto h = __builtin_amdgcn_cvt_pkrtz(v0, v1);
-  const float d0 = (v0 - (float)h[0]) * LO_UP, d1 = (v1 - (float)h[1]) * LO_UP;
-  const auto l = __builtin_amdgcn_cvt_pkrtz(d0, d1);
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, l);
-  r0 = d0 - (float)l[0];
-  r1 = d1 - (float)l[1];
+// The value weights enter the matrix cores as three bfloat16 parts, which
+// add up to the fp32 weight exactly: hi = w truncated to bfloat16 (its top
+// 16 bits), r = w - hi (exact in fp32: the low 16 bits of w's significand),
+// mid = r truncated, lo = r - mid (exact, and at most 8 significant bits, so
+// it is a bfloat16 as it stands). bfloat16 keeps fp32's exponent range, so
+// the split holds every weight, however small, down to fp32's normal range,
+// with no rebasing. The value quants enter as bfloat16 too: an int8 is exact.
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+
+// bfloat16 pair {a, b} (a in the low half) of two fp32 numbers whose low 16
+// bits are to be dropped
+__device__ __forceinline__ uint32_t bf_pair(float a, float b) {
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a),
+                               0x07060302u);
+}
+__device__ __forceinline__ float bf_trunc(float v) {
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xFFFF0000u);
+}
+__device__ __forceinline__ void split3(float v0, float v1, uint32_t& hi, uint32_t& mid,
+                                       uint32_t& lo) {
+  hi = bf_pair(v0, v1);
+  const float r0 = v0 - bf_trunc(v0), r1 = v1 - bf_trunc(v1);
+  mid = bf_pair(r0, r1);
+  lo = bf_pair(r0 - bf_trunc(r0), r1 - bf_trunc(r1));
 }
 
-// Weights below FINE (rare: the softmax weights of a row spread over more
-// than about 2^23, or a V scale far below its page's largest) are carried
-// further: what hi + lo leave, rebased by 2^32, becomes the next pair of
-// parts, up to RB_PARTS times, each multiplied into a fresh accumulator and
-// added to the running one times 2^-32 per step. Together they hold every
-// weight down to 2^-114 (of the 2^12 the largest maps to) within 2^-17 of
-// itself; what lies below is under fp32's normal range relative to the
-// largest V scale. A wave runs them only when one of its lanes holds such a
-// weight (a per-token test with the token's least V scale, on the ballot).
-constexpr int RB_PARTS = 3;
-constexpr float RB_NEXT = 524288.0f;             // 2^19: r (units 2^13) to the next part's units 2^32
-constexpr float RB_DOWN = 2.3283064365386963e-10f;  // 2^-32
+// Four int8 numbers (a little-endian word) as exact bfloat16: each converted
+// to fp32 (at most 8 significant bits, so the top 16 bits hold it).
+__device__ __forceinline__ bf16x4 i8x4_to_bf4(uint32_t w) {
+  const float f0 = (float)(int)(int8_t)(w & 0xFFu), f1 = (float)(int)(int8_t)((w >> 8) & 0xFFu);
+  const float f2 = (float)(int)(int8_t)((w >> 16) & 0xFFu), f3 = (float)(int)(int8_t)(w >> 24);
+  return __builtin_bit_cast(bf16x4, u32x2{bf_pair(f0, f1), bf_pair(f2, f3)});
+}
 
 // O^T += V^T * B for one page: B = the page's value weights pv (already
-// times 2^12 / sigma) times each token's V scale of block b, as split_hl's hi
-// and lo parts; with DEEP (uniform), also the parts that carry weights below
-// FINE, for the blocks where a lane holds one.
+// times 2^12 / sigma) times each token's V scale of block b, as split3's
+// three bfloat16 parts, each against the same bfloat16 value quants.
 template <int NQT>
 __device__ __forceinline__ void value_blocks(const PageRaw& R, const float (&pv)[NQT][4],
-                                             floatx4 (&acc)[NQT][8], const bool DEEP) {
-  const half4v lod = {(_Float16)LO_DOWN, (_Float16)LO_DOWN, (_Float16)LO_DOWN, (_Float16)LO_DOWN};
+                                             floatx4 (&acc)[NQT][8]) {
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     float vsb[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) vsb[r] = half_at(R.vs, 4 * r + b);
-    half4v bh[NQT], bl[NQT];
-    float x[NQT][4];  // DEEP: the next part's values of the weights below FINE, else 0
-    bool more = false;
+    bf16x4 bh[NQT], bm[NQT], bl[NQT];
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
-      uint32_t h0, h1, l0, l1;
-      float wv[4], rv[4];
+      uint32_t h0, h1, m0, m1, l0, l1;
+      float wv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) wv[r] = pv[qt][r] * vsb[r];
-      split_hl(wv[0], wv[1], h0, l0, rv[0], rv[1]);
-      split_hl(wv[2], wv[3], h1, l1, rv[2], rv[3]);
-      bh[qt] = __builtin_bit_cast(half4v, u32x2{h0, h1});
-      bl[qt] = __builtin_bit_cast(half4v, u32x2{l0, l1});
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[qt][r] = DEEP && fabsf(wv[r]) < FINE ? rv[r] * RB_NEXT : 0.f;
-        more |= x[qt][r] != 0.f;
-      }
+      split3(wv[0], wv[1], h0, m0, l0);
+      split3(wv[2], wv[3], h1, m1, l1);
+      bh[qt] = __builtin_bit_cast(bf16x4, u32x2{h0, h1});
+      bm[qt] = __builtin_bit_cast(bf16x4, u32x2{m0, m1});
+      bl[qt] = __builtin_bit_cast(bf16x4, u32x2{l0, l1});
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int dt = 2 * b + e;
-      const half4v av = i8x4_to_h4(R.q[2 + (dt >> 2)][dt & 3]);
-      const half4v al = av * lod;  // exact: q * 2^-13
+      const bf16x4 av = i8x4_to_bf4(R.q[2 + (dt >> 2)][dt & 3]);
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt) {
-        acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bh[qt], acc[qt][dt], 0, 0, 0);
-        acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(al, bl[qt], acc[qt][dt], 0, 0, 0);
+        acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bh[qt], acc[qt][dt], 0, 0, 0);
+        acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bm[qt], acc[qt][dt], 0, 0, 0);
+        acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bl[qt], acc[qt][dt], 0, 0, 0);
       }
-    }
-    if (!DEEP) continue;
-    // further parts, each rebased by 2^32, into a fresh accumulator added
-    // back times 2^-32 per part
-    float down = RB_DOWN;
-    for (int part = 0; part < RB_PARTS && __builtin_amdgcn_ballot_w64(more) != 0; ++part) {
-      more = false;
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) {
-        uint32_t h0, h1, l0, l1;
-        float rv[4];
-        split_hl(x[qt][0], x[qt][1], h0, l0, rv[0], rv[1]);
-        split_hl(x[qt][2], x[qt][3], h1, l1, rv[2], rv[3]);
-        bh[qt] = __builtin_bit_cast(half4v, u32x2{h0, h1});
-        bl[qt] = __builtin_bit_cast(half4v, u32x2{l0, l1});
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[qt][r] = fabsf(x[qt][r]) < FINE ? rv[r] * RB_NEXT : 0.f;
-          more |= x[qt][r] != 0.f;
-        }
-      }
-      const floatx4 dn = {down, down, down, down};
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int dt = 2 * b + e;
-        const half4v av = i8x4_to_h4(R.q[2 + (dt >> 2)][dt & 3]);
-        const half4v al = av * lod;
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-          floatx4 t = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bh[qt],
-                                                             floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          t = __builtin_amdgcn_mfma_f32_16x16x16f16(al, bl[qt], t, 0, 0, 0);
-          acc[qt][dt] = __builtin_elementwise_fma(dn, t, acc[qt][dt]);
-        }
-      }
-      down *= RB_DOWN;
     }
   }
 }
@@ -425,23 +377,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) q8_attn_kernel(AttnArgs A) {
     for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) pv[qt][r] *= bscale;
-    // does any lane hold a weight below FINE? (per token, with its least V
-    // scale: conservative where a scale is 0)
-    bool deep = false;
-    {
-      float vsmin[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vsmin[r] = fminf(fminf(fabsf(half_at(R.vs, 4 * r)), fabsf(half_at(R.vs, 4 * r + 1))),
-                         fminf(fabsf(half_at(R.vs, 4 * r + 2)), fabsf(half_at(R.vs, 4 * r + 3))));
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) deep |= pv[qt][r] > 0.f && pv[qt][r] * vsmin[r] < FINE;
-    }
-    // the parts for the weights below FINE run only on pages where a lane
-    // holds one (a uniform branch)
-    value_blocks<NQT>(R, pv, acc, __builtin_amdgcn_ballot_w64(deep) != 0);
+    value_blocks<NQT>(R, pv, acc);
   };
 
   // two page buffers in registers: the next page's loads are in flight while

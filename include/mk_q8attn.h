@@ -32,8 +32,8 @@
  *   s_i = (q . k_i) / sqrt(128),   O = sum_i softmax(s)_i v_i
  * Precision: the int8 quants and binary16 queries enter the products
  * exactly; scores, softmax and sums in fp32; the weights times V scales go
- * to the value product as binary16 parts that hold each of them to 2^-17 of
- * itself down to about fp32's range. Each output element is within
+ * to the value product as three bfloat16 parts that add up to each of them
+ * exactly, down to fp32's normal range. Each output element is within
  * 1e-4 * (sum_i p_i |v_i[d]| + 2^-80 * V_max) of the exact result, V_max
  * the largest V scale the row attends to (the tests check this bound).
  * Deterministic, and each row's result does not depend on the other rows.

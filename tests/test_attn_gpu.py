@@ -110,7 +110,7 @@ def test_dominant_tokens_with_zero_values():
     """Three dominant tokens per agent whose scores stand about 11, 23 and 46
     nats above the rest, with value quants of 0 in the first 32 or 64 dims:
     those output dims are made of weights between about 2^-16 and 2^-70 of
-    the largest one, which the value product must carry (rebased parts) to
+    the largest one, which the value product must carry (its bfloat16 parts keep fp32's range) to
     meet the per-element bound."""
     lengths, rows, H, KV = [300, 200], 3, 4, 2
     n_pages = 40
