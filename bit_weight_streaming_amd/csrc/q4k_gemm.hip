@@ -148,9 +148,8 @@ __global__ void __launch_bounds__(GEMM_THREADS) q4k_gemm_kernel(GemmArgs A) {
     for (int rt = 0; rt < MT; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
     int ctl = ua / a.nkb, cb = ua - ctl * a.nkb, cu = ua;
     auto flush = [&]() {
-      const int first = wave_of_unit(a, ctl * a.nkb);
-      const int last = wave_of_unit(a, (ctl + 1) * a.nkb - 1);
-      if (first == last) {
+      // the tile is this wave's alone when all its units lie in [ua, ub)
+      if (ctl * a.nkb >= ua && (ctl + 1) * a.nkb <= ub) {
 #pragma unroll
         for (int rt = 0; rt < MT; ++rt) put(a.t0 + ctl, lane, acc[rt], rt);
       } else if (ctl * a.nkb < ua) {
