@@ -419,12 +419,16 @@ __device__ __forceinline__ void put_xsum(char* blk, int j, const half4v& p) {
 __device__ __forceinline__ void stage_xsum(int M, int nkb, int xs_row, const char* x_lds,
                                            int x_stride, char* xs_lds, int tid,
                                            int nthreads) {
-  const int items = M * nkb * 8;
+  // eight neighbouring lanes take eight rows of one (block, sub-block): their
+  // reads (row stride = 16 bytes modulo 128) fall on distinct banks
+  const int M8 = (M + 7) & ~7;
+  const int items = M8 * nkb * 8;
   for (int it = tid; it < items; it += nthreads) {
-    const int j = it & 7;
-    const int rest = it >> 3;
-    const int m = rest / nkb;
-    const int b = rest - m * nkb;
+    const int j = (it >> 3) & 7;
+    const int rest = it >> 6;
+    const int b = rest % nkb;
+    const int m = (rest / nkb) * 8 + (it & 7);
+    if (m >= M) continue;
     const int gq = j >> 1, hb = j & 1;
     float sum = 0.f;
 #pragma unroll
